@@ -1,0 +1,235 @@
+/*
+ * octopus_dag.h -- C ABI of the packed-DAG attention library for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * What it computes.  An episode of branching agents is a DAG of branches (Octopus
+ * project page, section "Architecture & Co-Design": a cursor-addressed DAG
+ * G = (V, E_tree, E_mount)).  A branch is created by `fork` and shares its parent's
+ * prefix; `read_thread` mounts a span c_A[s_A:e_A) of another branch into the
+ * reader's attention layers without copying it (primitives table, rows "fork" and
+ * "read_thread").  The trainer packs every branch of a tree into one unpadded 1-D
+ * token stream and runs one block-sparse attention pass over it, forward and
+ * backward, with a shared prefix owned once and reader gradients routed into the
+ * producer's tokens (card "03 · Training"; ia.com.br article, section "Crédito
+ * contrafactual ...").  The serving side decodes cursors whose context is an
+ * ancestor prefix, their own branch and mounted spans, read in place from a page
+ * pool (primitives table; card "02 · Memory": mounts allocate no KV pages).
+ *
+ * Visibility.  For branch b and own offset r, with g(b,r) = start_b + r:
+ *     A(b,r) = H(b) ∪ {g(b,r') : r' < r}
+ *              ∪ {g(p_m,t) : s_m <= t < e_m, for mounts m with reader b, rpos_m <= r}
+ *     H(root) = {},  H(b) = A(parent_b, fork_b)
+ * and packed token i = g(b,r) attends to Ctx(i) = A(b,r) ∪ {i}, each key once.
+ * Attention is ordinary softmax attention restricted to Ctx(i):
+ *     S = scale * Q K^T,  LSE = log sum exp S,  P = exp(S - LSE),  O = P V
+ * with query head h reading KV head h / (Hq / Hkv).
+ *
+ * Positions.  Keys keep the position they were written at; after a mount a reader's
+ * next position is max(p_B, e_A + 1) (card "02 · Memory"; ia.com.br, section
+ * "Memória associativa versus memória de trabalho"), e_A being the span's exclusive
+ * end in positions.  The attention entry points take Q and K already rotated at
+ * these positions; octopus_plan_positions returns them.
+ *
+ * Conventions.
+ *   - Device tensors are row-major and contiguous.  "THD" means [T][H][D].
+ *   - bf16 is IEEE bfloat16 storage with float32 accumulation; outputs are rounded to
+ *     nearest even.  fp32 tensors are float32 throughout.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Device
+ *     work is enqueued asynchronously on it; no entry point synchronises it.
+ *   - The caller owns every device buffer (tensors, plan buffer, workspaces).  The
+ *     library never allocates or frees device memory.  A plan owns host memory only.
+ *   - Return value: OCTOPUS_OK (0) or a negative error code.  On error nothing has
+ *     been enqueued and outputs are untouched; octopus_last_error() returns a
+ *     thread-local message naming the offending row or argument.
+ */
+#ifndef OCTOPUS_DAG_H
+#define OCTOPUS_DAG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* One branch (one `fork`): parent index (-1 for the root, which must be row 0;
+ * every other row's parent has a lower index), fork = offset into the parent's own
+ * tokens at which the child forked (0 <= fork <= parent len), start = where the
+ * branch's own tokens sit in the packed stream, len >= 1 own tokens.  The branch
+ * spans must tile [0, total_tokens) exactly, in any order. */
+typedef struct {
+    int32_t parent, fork, start, len;
+} octopus_branch;
+
+/* One mount (one `read_thread`): the reader, when its own length was rpos
+ * (0 <= rpos <= reader len), mounted the producer's own tokens [s, e)
+ * (0 <= s < e <= producer len, producer != reader).  Reader tokens at own offsets
+ * >= rpos see the span. */
+typedef struct {
+    int32_t reader, rpos, producer, s, e;
+} octopus_mount;
+
+typedef enum { OCTOPUS_BF16 = 0, OCTOPUS_FP32 = 1 } octopus_dtype;
+
+enum {
+    OCTOPUS_OK = 0,
+    OCTOPUS_EINVAL = -1,       /* malformed table or argument */
+    OCTOPUS_ECYCLE = -2,       /* a token's position depends on itself */
+    OCTOPUS_EUNSUPPORTED = -3, /* dtype, head_dim, tile size or GQA ratio not built */
+    OCTOPUS_ENOMEM = -4,       /* host allocation failed */
+    OCTOPUS_EWORKSPACE = -5,   /* caller buffer too small */
+    OCTOPUS_EHIP = -6,         /* a HIP runtime or launch error (message kept) */
+    OCTOPUS_ESTATE = -7        /* plan not uploaded */
+};
+
+typedef struct octopus_plan octopus_plan;
+
+typedef struct {
+    int64_t nnz;          /* visible (query, key) pairs, each key once per query */
+    int64_t n_pairs;      /* listed (query tile, KV tile) pairs */
+    int64_t n_partial;    /* of which carry a bit mask */
+    int32_t total_tokens; /* T */
+    int32_t q_tile;       /* rows per query tile (128) */
+    int32_t kv_tile;      /* keys per KV tile */
+    int32_t n_q_tiles;
+    int32_t n_kv_tiles;
+    int32_t max_q_list;   /* longest KV-tile list of a query tile */
+    int32_t max_kv_list;  /* longest query-tile list of a KV tile */
+    int32_t reserved;
+} octopus_plan_stats;
+
+/* ---------------------------------------------------------------- planning (host) */
+
+/* Validate the tables, compute positions, and build the tile plan: for every
+ * 128-row query tile the ordered list of KV tiles holding a key some row of the
+ * tile sees, each FULL (every row sees every key) or PARTIAL (a per-row bit mask),
+ * the transposed lists (for every KV tile, the query tiles that see it), and
+ * longest-first launch orders.  kv_tile must be 64.  total_tokens must be in
+ * [1, 2^24].  Synchronous and re-entrant; touches no device.
+ * Errors: EINVAL (table rules above), ECYCLE, EUNSUPPORTED, ENOMEM.
+ * On success *out owns the plan; free it with octopus_plan_destroy. */
+int octopus_dag_plan(const octopus_branch* branches, int32_t n_branches,
+                     const octopus_mount* mounts, int32_t n_mounts,
+                     int32_t total_tokens, int32_t kv_tile, octopus_plan** out);
+
+/* Positions of the T packed tokens (host int32[T]). */
+int octopus_plan_positions(const octopus_plan* plan, int32_t* pos_out);
+
+int octopus_plan_stats_get(const octopus_plan* plan, octopus_plan_stats* out);
+
+/* Bytes of the device copy of the plan. */
+size_t octopus_plan_device_bytes(const octopus_plan* plan);
+
+/* Enqueue an asynchronous host-to-device copy of the plan into dev_buf
+ * (caller-owned, >= octopus_plan_device_bytes, 256-byte aligned) on `stream`, and
+ * remember dev_buf for the attention calls.  The plan's host memory must outlive
+ * the copy (synchronise the stream before destroying the plan).
+ * Errors: EINVAL (NULL or misaligned buffer), EWORKSPACE (too small), EHIP. */
+int octopus_plan_upload(octopus_plan* plan, void* dev_buf, size_t bytes, void* stream);
+
+/* Dense visibility bits of rows [row_lo, row_hi), expanded from the tile lists and
+ * masks alone (not from the tables): bits_out is host uint8[(row_hi-row_lo)]
+ * [ceil(T/8)], bit (j % 8) of byte j / 8 of a row set iff the row sees key j. */
+int octopus_plan_export_mask(const octopus_plan* plan, int32_t row_lo, int32_t row_hi,
+                             uint8_t* bits_out);
+
+/* The forward tile lists as the kernels see them: qt_ptr_out int32[n_q_tiles+1],
+ * kv_tile_out and mask_out int32[n_pairs] (mask -1 = FULL, else the PARTIAL mask
+ * index), and, if rows_out is not NULL, the PARTIAL masks as uint64[n_partial][128]
+ * (bit x of row r: row r of the query tile sees key x of the KV tile).  For
+ * inspection and tests. */
+int octopus_plan_export_tiles(const octopus_plan* plan, int32_t* qt_ptr_out,
+                              int32_t* kv_tile_out, int32_t* mask_out, uint64_t* rows_out);
+
+void octopus_plan_destroy(octopus_plan* plan);
+
+/* ---------------------------------------------------------------- attention (device) */
+
+/* Workspace bytes the forward needs (0 today; callers may pass NULL/0). */
+size_t octopus_fwd_workspace_bytes(const octopus_plan* plan, octopus_dtype dtype,
+                                   int32_t Hq, int32_t Hkv, int32_t D);
+
+/* Forward of packed-DAG attention over the uploaded plan.
+ *   q   THD [T][Hq][D], k, v THD [T][Hkv][D]  (dtype; rotated at the plan's positions)
+ *   o   THD [T][Hq][D] (dtype), lse float32 [Hq][T] (natural log) -- both written
+ * Supported: bf16 with D in {64, 128}; fp32 with D in {64, 128}; Hq % Hkv == 0,
+ * Hq / Hkv <= 16.  scale <= 0 selects 1/sqrt(D).
+ * Errors: ESTATE (plan not uploaded), EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP. */
+int octopus_dag_attn_fwd(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
+                         int32_t Hkv, int32_t D, float scale, const void* q,
+                         const void* k, const void* v, void* o, float* lse, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* Workspace bytes the backward needs: float32 [Hq][T] for Delta. */
+size_t octopus_bwd_workspace_bytes(const octopus_plan* plan, octopus_dtype dtype,
+                                   int32_t Hq, int32_t Hkv, int32_t D);
+
+/* Backward of L = sum <dO, O> given the forward's o and lse:
+ *   dq THD [T][Hq][D]; dk, dv THD [T][Hkv][D]  (dtype) -- written, not accumulated.
+ * Every dK/dV row is produced by exactly one work unit (the owner of its KV tile),
+ * summing the queries of every branch that sees it (descendants through the shared
+ * prefix, readers through mounts), so no atomics are used and results do not
+ * depend on scheduling.  Same support and errors as the forward. */
+int octopus_dag_attn_bwd(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
+                         int32_t Hkv, int32_t D, float scale, const void* q,
+                         const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- paged decode */
+
+/* Host helper: turn a DAG of branches held in a page pool into per-cursor segment
+ * lists.  page_ptr (int32[n_branches+1]) / pages (int32[page_ptr[n_branches]]) is
+ * the page table: branch b's own token r lives in page pages[page_ptr[b] + r /
+ * page_size], slot r % page_size.  cursors (int32[n_cursors]) are branch ids whose
+ * last own token is the current query.  For cursor c the segments cover exactly
+ * Ctx of that token (ancestor prefix, own branch, mounted spans, each key once) as
+ * (page, slot_lo, slot_hi) runs in packed-key order.  Mounted keys are read from
+ * the producer's own pages; no page is created.
+ * Two calls: with seg_capacity < needed (e.g. 0) only *n_seg_out is set and the
+ * call returns EWORKSPACE; then with room for *n_seg_out segments it fills
+ * seg_ptr_out (int32[n_cursors+1]) and seg_page/lo/hi_out (int32[n_seg]).
+ * Errors: EINVAL (tables, page ids outside [0, n_pages), short page table),
+ * ECYCLE, EWORKSPACE. */
+int octopus_decode_segments(const octopus_branch* branches, int32_t n_branches,
+                            const octopus_mount* mounts, int32_t n_mounts,
+                            const int32_t* page_ptr, const int32_t* pages,
+                            int32_t page_size, int32_t n_pages, const int32_t* cursors,
+                            int32_t n_cursors, int32_t* seg_ptr_out,
+                            int32_t* seg_page_out, int32_t* seg_lo_out,
+                            int32_t* seg_hi_out, int32_t seg_capacity,
+                            int32_t* n_seg_out);
+
+/* Workspace bytes for octopus_paged_mount_decode: float32 partial states
+ * [B][n_split][Hq][D + 2]. */
+size_t octopus_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t n_split);
+
+/* One-token attention of B cursors over their segments, read in place from the
+ * pools.  q [B][Hq][D]; k_pool, v_pool [n_pages][Hkv][page_size][D] (dtype);
+ * seg_* as produced by octopus_decode_segments, on the device; each cursor's
+ * segments are split into n_split contiguous chunks (1 <= n_split <= 256) whose
+ * partial softmax states are merged by LSE.  Writes o [B][Hq][D] (dtype) and, if
+ * lse is not NULL, float32 [B][Hq].  Segments naming a page outside [0, n_pages)
+ * are skipped.  Supported: bf16, D = 128, page_size = 64, Hq / Hkv <= 8.
+ * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP. */
+int octopus_paged_mount_decode(octopus_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                               int32_t D, int32_t page_size, float scale, const void* q,
+                               const void* k_pool, const void* v_pool, int32_t n_pages,
+                               const int32_t* seg_ptr, const int32_t* seg_page,
+                               const int32_t* seg_lo, const int32_t* seg_hi,
+                               int32_t n_split, void* o, float* lse, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- misc */
+
+/* Message of the last error on this thread ("" if none). */
+const char* octopus_last_error(void);
+
+/* Library version string. */
+const char* octopus_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OCTOPUS_DAG_H */

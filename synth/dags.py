@@ -269,8 +269,8 @@ def decode_workload(seed=5, n_cursors=64, prefix=16384, own_max=32768, max_mount
                     span_max=8192, page_size=64, name="decode64") -> DecodeWorkload:
     """Paged mounted decode: ``n_cursors`` cursors share a ``prefix``-token radix
     prefix; each has its own branch of ``L ~ U{1..own_max}`` tokens (the last one is
-    the current token) and ``U{0..max_mounts}`` mounts of terminal spans of distinct
-    other cursors' branches, span length ``U{1..min(span_max, L_producer)}``, issued
+    the current token) and ``min(U{0..max_mounts}, c)`` mounts of terminal spans of
+    distinct earlier cursors' branches, span length ``U{1..min(span_max, L_producer)}``, issued
     at a reader offset ``U{0..L-1}``.  Physical page ids are a seeded permutation of
     a pool just large enough for every branch's own pages."""
     rng = np.random.default_rng(seed)
@@ -282,9 +282,10 @@ def decode_workload(seed=5, n_cursors=64, prefix=16384, own_max=32768, max_mount
         start += int(L[c])
     rows_m = []
     for c in range(n_cursors):
-        k = int(rng.integers(0, max_mounts + 1))
-        others = np.array([o for o in range(n_cursors) if o != c])
-        prods = rng.choice(others, size=k, replace=False)
+        # Producers are earlier cursors (lower index): a mounted span then never
+        # depends, through positions, on the reader itself.
+        k = min(int(rng.integers(0, max_mounts + 1)), c)
+        prods = rng.choice(c, size=k, replace=False) if k else []
         for p in prods:
             Lp = int(L[p])
             ell = int(rng.integers(1, min(span_max, Lp) + 1))

@@ -1,0 +1,199 @@
+"""CPU tests of the C-ABI library's host side: it loads and exports every declared
+symbol; the planner rejects malformed tables like the oracle does; positions, the
+dense mask expanded from the tile lists, nnz and the FULL/PARTIAL classification
+match the oracle bit for bit; the decode segment builder covers exactly the oracle's
+cursor context with the producers' own pages."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import synth
+import tree_packed_block_amd as tpb
+from oracle import dag as D
+from oracle import decode as DEC
+from oracle.attention import useful_pairs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "octopus_dag.h")).read()
+    declared = set(re.findall(r"\b(octopus_[a-z_]+)\s*\(", header))
+    assert declared == set(tpb.EXPORTS)
+    L = tpb.lib()
+    for name in declared:
+        assert isinstance(getattr(L, name), ctypes._CFuncPtr), name
+    assert b"gfx950" in L.octopus_version()
+
+
+def _plan_code(br, mt, T, kv_tile=64):
+    try:
+        tpb.Plan(br, mt, T, kv_tile)
+        return "OK"
+    except tpb.OctopusError as e:
+        return e.name
+
+
+def test_planner_rejects_what_the_oracle_rejects():
+    ok_b = np.array([[-1, 0, 0, 4], [0, 2, 4, 3]])
+    ok_m = np.array([[1, 1, 0, 0, 2]])
+    assert _plan_code(ok_b, ok_m, 7) == "OK"
+    bad = [
+        (np.array([[0, 0, 0, 4], [0, 2, 4, 3]]), ok_m, 7),
+        (np.array([[-1, 0, 0, 4], [1, 2, 4, 3]]), ok_m, 7),
+        (np.array([[-1, 0, 0, 4], [0, 5, 4, 3]]), ok_m, 7),
+        (np.array([[-1, 0, 0, 4], [0, 2, 4, 0]]), ok_m, 4),
+        (np.array([[-1, 0, 0, 4], [0, 2, 5, 3]]), ok_m, 8),
+        (np.array([[-1, 0, 0, 4], [0, 2, 3, 3]]), ok_m, 6),
+        (ok_b, np.array([[1, 1, 1, 0, 2]]), 7),
+        (ok_b, np.array([[1, 4, 0, 0, 2]]), 7),
+        (ok_b, np.array([[1, 1, 0, 2, 2]]), 7),
+        (ok_b, np.array([[1, 1, 0, 0, 5]]), 7),
+        (ok_b, np.array([[1, 1, 2, 0, 1]]), 7),
+        (ok_b, ok_m, 0),
+    ]
+    for b, m, T in bad:
+        with pytest.raises(D.DagError):
+            D.validate(b, m, T)
+        assert _plan_code(b, m, T) == "EINVAL", (b, m, T)
+    br = np.array([[-1, 0, 0, 4], [0, 4, 4, 6], [0, 4, 10, 6]])
+    assert _plan_code(br, np.array([[1, 0, 2, 0, 5], [2, 0, 1, 0, 5]]), 16) == "ECYCLE"
+    assert _plan_code(ok_b, ok_m, 7, kv_tile=128) == "EUNSUPPORTED"
+
+
+def _check_plan(dag, rows=None):
+    p = tpb.Plan(dag.branches, dag.mounts, dag.T)
+    assert np.array_equal(p.positions(), D.positions(dag.branches, dag.mounts))
+    T = dag.T
+    blocks = rows if rows is not None else [(lo, min(T, lo + 2048)) for lo in range(0, T, 2048)]
+    nnz = 0
+    for lo, hi in blocks:
+        ref = D.mask_rows(dag.branches, dag.mounts, T, lo, hi)
+        got = np.unpackbits(p.export_mask(lo, hi), axis=1, bitorder="little")[:, :T]
+        assert np.array_equal(got.astype(bool), ref), (lo, hi)
+        nnz += int(ref.sum())
+    if rows is None:
+        assert p.stats()["nnz"] == nnz
+    _check_classification(p, dag, blocks)
+    return p
+
+
+def _check_classification(p, dag, blocks):
+    """FULL means every valid row of the query tile sees every key of the KV tile;
+    PARTIAL tiles are neither empty nor full (a ragged last KV tile is always
+    PARTIAL); the lists are strictly increasing."""
+    T = dag.T
+    qt_ptr, kv, mk, rows = p.tiles()
+    qts = sorted({lo // 128 for lo, hi in blocks} | {(hi - 1) // 128 for lo, hi in blocks})
+    for qt in qts:
+        r0, r1 = qt * 128, min(T, qt * 128 + 128)
+        M = D.mask_rows(dag.branches, dag.mounts, T, r0, r1)
+        lst = kv[qt_ptr[qt]:qt_ptr[qt + 1]]
+        assert np.all(np.diff(lst) > 0)
+        seen = set()
+        for t, m in zip(lst, mk[qt_ptr[qt]:qt_ptr[qt + 1]]):
+            k0, k1 = t * 64, min(T, t * 64 + 64)
+            sub = M[:, k0:k1]
+            assert sub.any()
+            if m < 0:
+                assert sub.all() and k1 - k0 == 64
+            else:
+                assert not (sub.all() and k1 - k0 == 64)
+                bits = np.array([[(int(rows[m, r]) >> x) & 1 for x in range(64)]
+                                 for r in range(128)], dtype=bool)
+                assert np.array_equal(bits[: r1 - r0, : k1 - k0], sub)
+                assert not bits[r1 - r0:].any() and not bits[:, k1 - k0:].any()
+            seen.add(int(t))
+        touched = {j // 64 for j in np.flatnonzero(M.any(axis=0))}
+        assert touched == seen
+
+
+@pytest.mark.parametrize("name", ["tiny", "episode_small", "episode_mid", "forked"])
+def test_plan_bit_exact_with_oracle(name):
+    dag, _ = synth.build(name)
+    p = _check_plan(dag)
+    if name == "forked":
+        assert p.stats()["nnz"] == useful_pairs(dag.branches, dag.mounts, dag.T)
+
+
+@pytest.mark.parametrize("name", ["episode131k", "episode262k"])
+def test_plan_bit_exact_with_oracle_sampled_rows(name):
+    """Full-size trees: positions everywhere, the mask on row blocks covering the
+    start, every branch boundary, every mount's reader offset and the end."""
+    dag, _ = synth.build(name)
+    T = dag.T
+    marks = {0, T - 130}
+    for (parent, fork, start, L) in dag.branches:
+        marks |= {max(0, start - 70), start + L // 2}
+    for (reader, rpos, producer, s, e) in dag.mounts:
+        marks.add(max(0, int(dag.branches[reader, 2]) + int(rpos) - 64))
+    rows = sorted((m, min(T, m + 130)) for m in marks)
+    _check_plan(dag, rows=rows)
+
+
+@settings(max_examples=150, deadline=None)
+@given(st.integers(0, 10**9), st.booleans())
+def test_plan_fuzz(seed, acyclic):
+    dag = synth.fuzz_dag(np.random.default_rng(seed), max_len=90, max_branches=7,
+                         max_mounts=5, acyclic=acyclic)
+    try:
+        D.positions(dag.branches, dag.mounts)
+    except D.DagError as e:
+        assert _plan_code(dag.branches, dag.mounts, dag.T) == e.code
+        return
+    _check_plan(dag)
+
+
+# ----------------------------------------------------------------------------- decode
+
+def _check_segments(wl):
+    sp, pg, lo, hi = tpb.decode_segments(wl.dag.branches, wl.dag.mounts, wl.page_ptr,
+                                         wl.pages, wl.page_size, wl.n_pages, wl.cursors)
+    owned = set(wl.pages.tolist())
+    for c, b in enumerate(wl.cursors):
+        idx = DEC.cursor_tokens(wl.dag.branches, wl.dag.mounts, int(b))
+        page, slot = DEC.physical_slots(wl.dag.branches, wl.page_ptr, wl.pages,
+                                        wl.page_size, idx)
+        want = list(zip(page.tolist(), slot.tolist()))
+        got = []
+        for s in range(sp[c], sp[c + 1]):
+            assert 0 <= lo[s] < hi[s] <= wl.page_size
+            assert pg[s] in owned
+            got.extend((int(pg[s]), x) for x in range(lo[s], hi[s]))
+        assert got == want  # same keys, each once, in packed-key order
+    return sp, pg, lo, hi
+
+
+def test_decode_segments_match_oracle_small():
+    wl = synth.decode_workload(seed=5, n_cursors=6, prefix=256, own_max=300, span_max=100,
+                               page_size=16)
+    _check_segments(wl)
+
+
+def test_decode_segments_match_oracle_full_size():
+    wl = synth.decode_workload()
+    sp, pg, lo, hi = _check_segments(wl)
+    # mounts read the producers' pages in place: the pool holds exactly the pages
+    # the branches own, and no segment names any other page
+    assert wl.n_pages == int(wl.page_ptr[-1])
+    assert set(pg.tolist()) <= set(wl.pages.tolist())
+
+
+def test_decode_segments_errors():
+    wl = synth.decode_workload(seed=5, n_cursors=4, prefix=64, own_max=100, page_size=16)
+    bad_pages = wl.pages.copy()
+    bad_pages[0] = wl.n_pages
+    with pytest.raises(tpb.OctopusError) as ei:
+        tpb.decode_segments(wl.dag.branches, wl.dag.mounts, wl.page_ptr, bad_pages, 16,
+                            wl.n_pages, wl.cursors)
+    assert ei.value.name == "EINVAL"
+    short = wl.page_ptr.copy()
+    short[1:] -= 1
+    with pytest.raises(tpb.OctopusError):
+        tpb.decode_segments(wl.dag.branches, wl.dag.mounts, short, wl.pages, 16, wl.n_pages,
+                            wl.cursors)

@@ -1,0 +1,26 @@
+"""Packed-DAG attention for AMD Instinct MI355X (gfx950).
+
+Block-sparse attention over one episode DAG of branches packed into a single
+unpadded token stream (forward and backward), and paged decode of cursors over
+ancestor, own and mounted pages, as described on the Octopus project page (sections
+"Architecture & Co-Design": primitives table, cards "02 · Memory" and
+"03 · Training").  The compute lives in ``liboctopus_dag.so`` (C ABI declared in
+``include/octopus_dag.h``); this package only binds it.
+"""
+
+from ._lib import (  # noqa: F401
+    BF16,
+    FP32,
+    EXPORTS,
+    LIB_PATH,
+    OctopusError,
+    Plan,
+    attn_bwd,
+    attn_fwd,
+    bwd_workspace_bytes,
+    decode_segments,
+    decode_workspace_bytes,
+    default_scale,
+    lib,
+    paged_mount_decode,
+)

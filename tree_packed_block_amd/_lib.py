@@ -1,0 +1,323 @@
+"""ctypes binding of ``liboctopus_dag.so`` (argument marshalling only).
+
+Every step of the path runs inside the library: planning on the host in C++, all
+attention and decode arithmetic in HIP kernels.  PyTorch only supplies device memory
+and the current stream.  If the library is missing the calls raise; there is no
+fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboctopus_dag.so")
+
+OK, EINVAL, ECYCLE, EUNSUPPORTED, ENOMEM, EWORKSPACE, EHIP, ESTATE = 0, -1, -2, -3, -4, -5, -6, -7
+_NAMES = {EINVAL: "EINVAL", ECYCLE: "ECYCLE", EUNSUPPORTED: "EUNSUPPORTED",
+          ENOMEM: "ENOMEM", EWORKSPACE: "EWORKSPACE", EHIP: "EHIP", ESTATE: "ESTATE"}
+BF16, FP32 = 0, 1
+
+# Every symbol include/octopus_dag.h declares.
+EXPORTS = [
+    "octopus_dag_plan", "octopus_plan_positions", "octopus_plan_stats_get",
+    "octopus_plan_device_bytes", "octopus_plan_upload", "octopus_plan_export_mask",
+    "octopus_plan_export_tiles", "octopus_plan_destroy", "octopus_fwd_workspace_bytes", "octopus_dag_attn_fwd",
+    "octopus_bwd_workspace_bytes", "octopus_dag_attn_bwd", "octopus_decode_segments",
+    "octopus_decode_workspace_bytes", "octopus_paged_mount_decode", "octopus_last_error",
+    "octopus_version",
+]
+
+
+class OctopusError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{_NAMES.get(code, code)}: {msg}")
+        self.code = code
+        self.name = _NAMES.get(code, str(code))
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [("nnz", ctypes.c_int64), ("n_pairs", ctypes.c_int64),
+                ("n_partial", ctypes.c_int64), ("total_tokens", ctypes.c_int32),
+                ("q_tile", ctypes.c_int32), ("kv_tile", ctypes.c_int32),
+                ("n_q_tiles", ctypes.c_int32), ("n_kv_tiles", ctypes.c_int32),
+                ("max_q_list", ctypes.c_int32), ("max_kv_list", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+_lib = None
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_vp = ctypes.c_void_p
+
+
+def lib():
+    """Load the library once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    L.octopus_dag_plan.argtypes = [_vp, ctypes.c_int32, _vp, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.POINTER(_vp)]
+    L.octopus_plan_positions.argtypes = [_vp, _i32p]
+    L.octopus_plan_stats_get.argtypes = [_vp, ctypes.POINTER(Stats)]
+    L.octopus_plan_device_bytes.argtypes = [_vp]
+    L.octopus_plan_device_bytes.restype = ctypes.c_size_t
+    L.octopus_plan_upload.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
+    L.octopus_plan_export_mask.argtypes = [_vp, ctypes.c_int32, ctypes.c_int32, _vp]
+    L.octopus_plan_export_tiles.argtypes = [_vp, _vp, _vp, _vp, _vp]
+    L.octopus_plan_destroy.argtypes = [_vp]
+    L.octopus_plan_destroy.restype = None
+    L.octopus_fwd_workspace_bytes.argtypes = [_vp, ctypes.c_int, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_int32]
+    L.octopus_fwd_workspace_bytes.restype = ctypes.c_size_t
+    L.octopus_bwd_workspace_bytes.argtypes = L.octopus_fwd_workspace_bytes.argtypes
+    L.octopus_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.octopus_dag_attn_fwd.argtypes = [_vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_float, _vp, _vp, _vp, _vp, _vp,
+                                       _vp, ctypes.c_size_t, _vp]
+    L.octopus_dag_attn_bwd.argtypes = [_vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_float, _vp, _vp, _vp, _vp, _vp,
+                                       _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.octopus_decode_segments.argtypes = [_vp, ctypes.c_int32, _vp, ctypes.c_int32, _vp, _vp,
+                                          ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int32,
+                                          _vp, _vp, _vp, _vp, ctypes.c_int32, _i32p]
+    L.octopus_decode_workspace_bytes.argtypes = [ctypes.c_int32] * 4
+    L.octopus_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.octopus_paged_mount_decode.argtypes = [ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_float, _vp, _vp, _vp, ctypes.c_int32,
+                                             _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp,
+                                             ctypes.c_size_t, _vp]
+    L.octopus_last_error.restype = ctypes.c_char_p
+    L.octopus_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(rc):
+    if rc != OK:
+        raise OctopusError(rc, lib().octopus_last_error().decode())
+
+
+def _np_ptr(a):
+    return a.ctypes.data_as(_vp)
+
+
+def _tables(branches, mounts):
+    br = np.ascontiguousarray(np.asarray(branches, dtype=np.int32).reshape(-1, 4))
+    mt = np.ascontiguousarray(np.asarray(mounts, dtype=np.int32).reshape(-1, 5))
+    return br, mt
+
+
+# ----------------------------------------------------------------------------- plan
+
+class Plan:
+    """A tile plan of one packed tree (host object; ``upload`` puts a copy on the
+    device in a caller-owned buffer)."""
+
+    def __init__(self, branches, mounts, total_tokens, kv_tile=64):
+        self._h = None
+        br, mt = _tables(branches, mounts)
+        h = _vp()
+        _check(lib().octopus_dag_plan(_np_ptr(br), br.shape[0], _np_ptr(mt), mt.shape[0],
+                                      int(total_tokens), int(kv_tile), ctypes.byref(h)))
+        self._h = h
+        self.T = int(total_tokens)
+        self.dev = None
+
+    def __del__(self):
+        if getattr(self, "_h", None) is not None and _lib is not None:
+            _lib.octopus_plan_destroy(self._h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def positions(self) -> np.ndarray:
+        out = np.empty(self.T, dtype=np.int32)
+        _check(lib().octopus_plan_positions(self._h, out.ctypes.data_as(_i32p)))
+        return out
+
+    def stats(self) -> dict:
+        s = Stats()
+        _check(lib().octopus_plan_stats_get(self._h, ctypes.byref(s)))
+        return {f: getattr(s, f) for f, _ in Stats._fields_ if f != "reserved"}
+
+    def device_bytes(self) -> int:
+        return int(lib().octopus_plan_device_bytes(self._h))
+
+    def export_mask(self, row_lo, row_hi) -> np.ndarray:
+        out = np.zeros((row_hi - row_lo, (self.T + 7) // 8), dtype=np.uint8)
+        _check(lib().octopus_plan_export_mask(self._h, int(row_lo), int(row_hi), _np_ptr(out)))
+        return out
+
+    def tiles(self):
+        """``(qt_ptr, kv_tile, mask, rows)``: the forward tile lists and PARTIAL masks."""
+        st = self.stats()
+        qt_ptr = np.zeros(st["n_q_tiles"] + 1, dtype=np.int32)
+        kv = np.zeros(max(st["n_pairs"], 1), dtype=np.int32)
+        mk = np.zeros(max(st["n_pairs"], 1), dtype=np.int32)
+        rows = np.zeros((max(st["n_partial"], 1), 128), dtype=np.uint64)
+        _check(lib().octopus_plan_export_tiles(self._h, _np_ptr(qt_ptr), _np_ptr(kv),
+                                               _np_ptr(mk), _np_ptr(rows)))
+        n = st["n_pairs"]
+        return qt_ptr, kv[:n], mk[:n], rows[:st["n_partial"]]
+
+    def upload(self, device="cuda", buffer=None):
+        """Copy the plan into ``buffer`` (a uint8 CUDA tensor, allocated here if
+        ``None``) on the current stream and wait for the copy, so the host plan can
+        be freed at any time afterwards."""
+        import torch
+        n = self.device_bytes()
+        if buffer is None:
+            buffer = torch.empty(n, dtype=torch.uint8, device=device)
+        stream = torch.cuda.current_stream(buffer.device)
+        _check(lib().octopus_plan_upload(self._h, _vp(buffer.data_ptr()), buffer.numel(),
+                                         _vp(stream.cuda_stream)))
+        stream.synchronize()
+        self.dev = buffer
+        return self
+
+
+# ----------------------------------------------------------------------------- attention
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return FP32
+    raise OctopusError(EUNSUPPORTED, f"dtype {t.dtype} not supported")
+
+
+def _need(t, shape, dtype, name):
+    if tuple(t.shape) != tuple(shape):
+        raise OctopusError(EINVAL, f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if t.dtype != dtype:
+        raise OctopusError(EINVAL, f"{name}: dtype {t.dtype} != {dtype}")
+    if not t.is_contiguous():
+        raise OctopusError(EINVAL, f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise OctopusError(EINVAL, f"{name} must be a device tensor")
+
+
+def attn_fwd(plan: Plan, q, k, v, scale=None, o=None, lse=None, stream=None):
+    """Packed-DAG attention forward: returns ``(o [T,Hq,D], lse float32 [Hq,T])``."""
+    import torch
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    _need(q, (plan.T, Hq, D), q.dtype, "q")
+    _need(k, (plan.T, Hkv, D), q.dtype, "k")
+    _need(v, (plan.T, Hkv, D), q.dtype, "v")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    _need(o, q.shape, q.dtype, "o")
+    _need(lse, (Hq, T), torch.float32, "lse")
+    s = stream or torch.cuda.current_stream(q.device)
+    _check(lib().octopus_dag_attn_fwd(plan.handle, _dtype_code(q), Hq, Hkv, D,
+                                      float(scale or 0.0), q.data_ptr(), k.data_ptr(),
+                                      v.data_ptr(), o.data_ptr(), lse.data_ptr(), None, 0,
+                                      _vp(s.cuda_stream)))
+    return o, lse
+
+
+def bwd_workspace_bytes(plan: Plan, dtype_code, Hq, Hkv, D) -> int:
+    return int(lib().octopus_bwd_workspace_bytes(plan.handle, dtype_code, Hq, Hkv, D))
+
+
+def attn_bwd(plan: Plan, q, k, v, o, lse, dout, scale=None, dq=None, dk=None, dv=None,
+             ws=None, stream=None):
+    """Packed-DAG attention backward: returns ``(dq, dk, dv)``."""
+    import torch
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    for t, shp, nm in ((q, (plan.T, Hq, D), "q"), (k, (plan.T, Hkv, D), "k"),
+                       (v, (plan.T, Hkv, D), "v"), (o, (plan.T, Hq, D), "o"),
+                       (dout, (plan.T, Hq, D), "dout")):
+        _need(t, shp, q.dtype, nm)
+    _need(lse, (Hq, T), torch.float32, "lse")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    code = _dtype_code(q)
+    need = bwd_workspace_bytes(plan, code, Hq, Hkv, D)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    s = stream or torch.cuda.current_stream(q.device)
+    _check(lib().octopus_dag_attn_bwd(plan.handle, code, Hq, Hkv, D, float(scale or 0.0),
+                                      q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                      lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                                      dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(),
+                                      _vp(s.cuda_stream)))
+    return dq, dk, dv
+
+
+# ----------------------------------------------------------------------------- decode
+
+def decode_segments(branches, mounts, page_ptr, pages, page_size, n_pages, cursors):
+    """Host segment builder: returns int32 arrays ``(seg_ptr, seg_page, seg_lo,
+    seg_hi)``."""
+    br, mt = _tables(branches, mounts)
+    pp = np.ascontiguousarray(page_ptr, dtype=np.int32)
+    pg = np.ascontiguousarray(pages, dtype=np.int32)
+    cur = np.ascontiguousarray(cursors, dtype=np.int32)
+    n = ctypes.c_int32(0)
+    L = lib()
+    args = [_np_ptr(br), br.shape[0], _np_ptr(mt), mt.shape[0], _np_ptr(pp), _np_ptr(pg),
+            int(page_size), int(n_pages), _np_ptr(cur), cur.shape[0]]
+    rc = L.octopus_decode_segments(*args, None, None, None, None, 0, ctypes.byref(n))
+    if rc not in (OK, EWORKSPACE):
+        _check(rc)
+    cap = n.value
+    sp = np.zeros(cur.shape[0] + 1, dtype=np.int32)
+    out = [np.zeros(max(cap, 1), dtype=np.int32) for _ in range(3)]
+    _check(L.octopus_decode_segments(*args, _np_ptr(sp), _np_ptr(out[0]), _np_ptr(out[1]),
+                                     _np_ptr(out[2]), cap, ctypes.byref(n)))
+    return sp, out[0][:cap], out[1][:cap], out[2][:cap]
+
+
+def decode_workspace_bytes(B, Hq, D, n_split) -> int:
+    return int(lib().octopus_decode_workspace_bytes(B, Hq, D, n_split))
+
+
+def paged_mount_decode(q, k_pool, v_pool, seg_ptr, seg_page, seg_lo, seg_hi, n_split=16,
+                       scale=None, o=None, lse=None, ws=None, stream=None):
+    """One-token attention of every cursor over its segments (device int32 tensors).
+    Returns ``(o [B,Hq,D], lse float32 [B,Hq])``."""
+    import torch
+    B, Hq, D = q.shape
+    n_pages, Hkv, page_size, _ = k_pool.shape
+    _need(q, (B, Hq, D), q.dtype, "q")
+    _need(k_pool, (n_pages, Hkv, page_size, D), q.dtype, "k_pool")
+    _need(v_pool, (n_pages, Hkv, page_size, D), q.dtype, "v_pool")
+    for t, nm in ((seg_ptr, "seg_ptr"), (seg_page, "seg_page"), (seg_lo, "seg_lo"),
+                  (seg_hi, "seg_hi")):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise OctopusError(EINVAL, f"{nm} must be a contiguous int32 device tensor")
+    if seg_ptr.numel() != B + 1:
+        raise OctopusError(EINVAL, "seg_ptr must have B + 1 entries")
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    need = decode_workspace_bytes(B, Hq, D, n_split)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    s = stream or torch.cuda.current_stream(q.device)
+    _check(lib().octopus_paged_mount_decode(
+        _dtype_code(q), B, Hq, Hkv, D, page_size, float(scale or 0.0), q.data_ptr(),
+        k_pool.data_ptr(), v_pool.data_ptr(), n_pages, seg_ptr.data_ptr(), seg_page.data_ptr(),
+        seg_lo.data_ptr(), seg_hi.data_ptr(), int(n_split), o.data_ptr(), lse.data_ptr(),
+        ws.data_ptr(), ws.numel(), _vp(s.cuda_stream)))
+    return o, lse
+
+
+def default_scale(D) -> float:
+    return 1.0 / math.sqrt(D)

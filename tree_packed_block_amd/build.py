@@ -1,0 +1,77 @@
+"""Build ``liboctopus_dag.so`` in-tree for gfx950.
+
+HIP sources are compiled with ``hipcc --offload-arch=gfx950`` (packed-fp32 ops
+disabled), host C++ with ``g++`` against the HIP runtime headers, and everything is
+linked into one shared library next to this file.  Objects go to ``_build/`` at the
+repository root.  Always recompiles (the caller decides when to build).
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(HERE, "liboctopus_dag.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+HIP_SOURCES = ["fwd.hip", "bwd.hip", "decode.hip"]
+CXX_SOURCES = ["plan.cpp", "api.cpp"]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
+             "-D__HIP_PLATFORM_AMD__"]
+
+
+def _hipcc():
+    return shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("build step failed:\n" + " ".join(cmd) + "\n" + r.stdout)
+    return r.stdout
+
+
+def build(verbose: bool = False, extra_cxx=(), out=LIB) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    inc = ["-I" + INCLUDE, "-I" + CSRC]
+    jobs = []
+    objs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        jobs.append([_hipcc(), *HIPCC_FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    for src in CXX_SOURCES:
+        obj = os.path.join(BUILD, src.replace(".cpp", ".o"))
+        jobs.append(["g++", *CXX_FLAGS, *extra_cxx, *inc, "-I" + os.path.join(ROCM, "include"),
+                     "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        logs = list(ex.map(_run, jobs))
+    if verbose:
+        for cmd, log in zip(jobs, logs):
+            print(" ".join(cmd))
+            if log.strip():
+                print(log)
+    tmp = out + ".tmp"
+    _run([_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, *extra_cxx,
+          "-o", tmp])
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

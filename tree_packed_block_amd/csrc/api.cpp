@@ -1,0 +1,296 @@
+// C ABI of the packed-DAG attention library (see include/octopus_dag.h).
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "octopus_dag.h"
+#include "plan.h"
+
+struct octopus_plan {
+    octo::Plan p;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, std::string msg) {
+    g_err = std::move(msg);
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return OCTOPUS_OK;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+    return fail(OCTOPUS_EHIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+octo::DevPlan dev_view(const octo::Plan& p) {
+    const unsigned char* base = static_cast<const unsigned char*>(p.dev);
+    octo::DevPlan d;
+    d.T = p.T;
+    d.nQT = p.nQT;
+    d.nKT = p.nKT;
+    d.n_partial = (int32_t)p.n_partial;
+    d.fwd_order = reinterpret_cast<const int32_t*>(base + p.layout.fwd_order);
+    d.qt_ptr = reinterpret_cast<const int32_t*>(base + p.layout.qt_ptr);
+    d.q_pairs = reinterpret_cast<const int2*>(base + p.layout.q_pairs);
+    d.bwd_order = reinterpret_cast<const int32_t*>(base + p.layout.bwd_order);
+    d.kt_ptr = reinterpret_cast<const int32_t*>(base + p.layout.kt_ptr);
+    d.k_pairs = reinterpret_cast<const int2*>(base + p.layout.k_pairs);
+    d.mask_rows = reinterpret_cast<const uint64_t*>(base + p.layout.mask_rows);
+    d.mask_cols = reinterpret_cast<const uint64_t*>(base + p.layout.mask_cols);
+    return d;
+}
+
+// Checks shared by the forward and the backward.
+int check_attn(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq, int32_t Hkv,
+               int32_t D, std::initializer_list<const void*> ptrs) {
+    if (plan == nullptr) return fail(OCTOPUS_EINVAL, "plan is NULL");
+    if (plan->p.dev == nullptr) return fail(OCTOPUS_ESTATE, "plan not uploaded");
+    if (dtype != OCTOPUS_BF16 && dtype != OCTOPUS_FP32)
+        return fail(OCTOPUS_EUNSUPPORTED, "dtype must be bf16 or fp32");
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+        return fail(OCTOPUS_EINVAL, "Hq and Hkv must be positive with Hq % Hkv == 0");
+    if (Hq / Hkv > 16) return fail(OCTOPUS_EUNSUPPORTED, "Hq / Hkv must be <= 16");
+    if (D != 64 && D != 128) return fail(OCTOPUS_EUNSUPPORTED, "head_dim must be 64 or 128");
+    for (const void* p : ptrs) {
+        if (p == nullptr) return fail(OCTOPUS_EINVAL, "a tensor pointer is NULL");
+        if (!aligned(p, 16)) return fail(OCTOPUS_EINVAL, "tensors must be 16-byte aligned");
+    }
+    return OCTOPUS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* octopus_last_error(void) { return g_err.c_str(); }
+
+const char* octopus_version(void) { return "octopus_dag 0.1 (gfx950)"; }
+
+int octopus_dag_plan(const octopus_branch* branches, int32_t n_branches,
+                     const octopus_mount* mounts, int32_t n_mounts, int32_t total_tokens,
+                     int32_t kv_tile, octopus_plan** out) {
+    if (out == nullptr) return fail(OCTOPUS_EINVAL, "out is NULL");
+    *out = nullptr;
+    try {
+        octopus_plan* h = new octopus_plan();
+        std::string err;
+        const int rc = octo::build_plan(branches, n_branches, mounts, n_mounts, total_tokens,
+                                        kv_tile, h->p, err);
+        if (rc != OCTOPUS_OK) {
+            delete h;
+            return fail(rc, err);
+        }
+        *out = h;
+        return ok();
+    } catch (const std::bad_alloc&) {
+        return fail(OCTOPUS_ENOMEM, "host allocation failed while planning");
+    }
+}
+
+int octopus_plan_positions(const octopus_plan* plan, int32_t* pos_out) {
+    if (plan == nullptr || pos_out == nullptr) return fail(OCTOPUS_EINVAL, "NULL argument");
+    for (int32_t i = 0; i < plan->p.T; ++i) pos_out[i] = (int32_t)plan->p.dag.pos[i];
+    return ok();
+}
+
+int octopus_plan_stats_get(const octopus_plan* plan, octopus_plan_stats* out) {
+    if (plan == nullptr || out == nullptr) return fail(OCTOPUS_EINVAL, "NULL argument");
+    const octo::Plan& p = plan->p;
+    out->nnz = p.nnz;
+    out->n_pairs = (int64_t)p.q_pairs.size();
+    out->n_partial = p.n_partial;
+    out->total_tokens = p.T;
+    out->q_tile = p.Bq;
+    out->kv_tile = p.Bk;
+    out->n_q_tiles = p.nQT;
+    out->n_kv_tiles = p.nKT;
+    out->max_q_list = p.max_q_list;
+    out->max_kv_list = p.max_kv_list;
+    out->reserved = 0;
+    return ok();
+}
+
+size_t octopus_plan_device_bytes(const octopus_plan* plan) {
+    return plan ? plan->p.layout.total : 0;
+}
+
+int octopus_plan_upload(octopus_plan* plan, void* dev_buf, size_t bytes, void* stream) {
+    if (plan == nullptr || dev_buf == nullptr) return fail(OCTOPUS_EINVAL, "NULL argument");
+    if (!aligned(dev_buf, 256)) return fail(OCTOPUS_EINVAL, "plan buffer must be 256-byte aligned");
+    if (bytes < plan->p.layout.total)
+        return fail(OCTOPUS_EWORKSPACE, "plan buffer smaller than octopus_plan_device_bytes");
+    const hipError_t e = hipMemcpyAsync(dev_buf, plan->p.blob.data(), plan->p.layout.total,
+                                        hipMemcpyHostToDevice, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "plan upload");
+    plan->p.dev = dev_buf;
+    return ok();
+}
+
+int octopus_plan_export_mask(const octopus_plan* plan, int32_t row_lo, int32_t row_hi,
+                             uint8_t* bits_out) {
+    if (plan == nullptr || bits_out == nullptr) return fail(OCTOPUS_EINVAL, "NULL argument");
+    if (row_lo < 0 || row_hi > plan->p.T || row_lo > row_hi)
+        return fail(OCTOPUS_EINVAL, "row range outside [0, T)");
+    octo::export_mask(plan->p, row_lo, row_hi, bits_out);
+    return ok();
+}
+
+int octopus_plan_export_tiles(const octopus_plan* plan, int32_t* qt_ptr_out,
+                              int32_t* kv_tile_out, int32_t* mask_out, uint64_t* rows_out) {
+    if (plan == nullptr || !qt_ptr_out || !kv_tile_out || !mask_out)
+        return fail(OCTOPUS_EINVAL, "NULL argument");
+    const octo::Plan& p = plan->p;
+    std::copy(p.qt_ptr.begin(), p.qt_ptr.end(), qt_ptr_out);
+    for (size_t i = 0; i < p.q_pairs.size(); ++i) {
+        kv_tile_out[i] = p.q_pairs[i].tile;
+        mask_out[i] = p.q_pairs[i].mask;
+    }
+    if (rows_out) std::copy(p.mask_rows.begin(), p.mask_rows.end(), rows_out);
+    return ok();
+}
+
+void octopus_plan_destroy(octopus_plan* plan) { delete plan; }
+
+size_t octopus_fwd_workspace_bytes(const octopus_plan*, octopus_dtype, int32_t, int32_t,
+                                   int32_t) {
+    return 0;
+}
+
+int octopus_dag_attn_fwd(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
+                         int32_t Hkv, int32_t D, float scale, const void* q, const void* k,
+                         const void* v, void* o, float* lse, void* ws, size_t ws_bytes,
+                         void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    int rc = check_attn(plan, dtype, Hq, Hkv, D, {q, k, v, o, lse});
+    if (rc != OCTOPUS_OK) return rc;
+    if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
+    const octo::DevPlan dp = dev_view(plan->p);
+    hipError_t e = dtype == OCTOPUS_BF16
+                       ? octo::launch_fwd_bf16(dp, Hq, Hkv, D, scale, q, k, v, o, lse,
+                                               (hipStream_t)stream)
+                       : octo::launch_fwd_fp32(dp, Hq, Hkv, D, scale, q, k, v, o, lse,
+                                               (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "forward launch");
+    return ok();
+}
+
+size_t octopus_bwd_workspace_bytes(const octopus_plan* plan, octopus_dtype, int32_t Hq,
+                                   int32_t, int32_t) {
+    if (plan == nullptr || Hq < 1) return 0;
+    return (size_t)Hq * (size_t)plan->p.T * sizeof(float);
+}
+
+int octopus_dag_attn_bwd(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
+                         int32_t Hkv, int32_t D, float scale, const void* q, const void* k,
+                         const void* v, const void* o, const float* lse, const void* dout,
+                         void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                         void* stream) {
+    int rc = check_attn(plan, dtype, Hq, Hkv, D, {q, k, v, o, lse, dout, dq, dk, dv});
+    if (rc != OCTOPUS_OK) return rc;
+    const size_t need = octopus_bwd_workspace_bytes(plan, dtype, Hq, Hkv, D);
+    if (ws == nullptr || ws_bytes < need || !aligned(ws, 16))
+        return fail(OCTOPUS_EWORKSPACE, "backward workspace needs " + std::to_string(need) +
+                                            " bytes, 16-byte aligned");
+    if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
+    const octo::DevPlan dp = dev_view(plan->p);
+    float* delta = static_cast<float*>(ws);
+    hipError_t e = dtype == OCTOPUS_BF16
+                       ? octo::launch_bwd_bf16(dp, Hq, Hkv, D, scale, q, k, v, o, lse, dout,
+                                               dq, dk, dv, delta, (hipStream_t)stream)
+                       : octo::launch_bwd_fp32(dp, Hq, Hkv, D, scale, q, k, v, o, lse, dout,
+                                               dq, dk, dv, delta, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+    return ok();
+}
+
+int octopus_decode_segments(const octopus_branch* branches, int32_t n_branches,
+                            const octopus_mount* mounts, int32_t n_mounts,
+                            const int32_t* page_ptr, const int32_t* pages, int32_t page_size,
+                            int32_t n_pages, const int32_t* cursors, int32_t n_cursors,
+                            int32_t* seg_ptr_out, int32_t* seg_page_out, int32_t* seg_lo_out,
+                            int32_t* seg_hi_out, int32_t seg_capacity, int32_t* n_seg_out) {
+    if (n_seg_out == nullptr) return fail(OCTOPUS_EINVAL, "n_seg_out is NULL");
+    try {
+        if (n_branches < 1 || branches == nullptr) return fail(OCTOPUS_EINVAL, "no branches");
+        int64_t T = 0;
+        for (int32_t b = 0; b < n_branches; ++b) T += branches[b].len > 0 ? branches[b].len : 0;
+        if (T < 1 || T > octo::kMaxTokens) return fail(OCTOPUS_EINVAL, "total tokens out of range");
+        octo::DagInfo dag;
+        std::string err;
+        int rc = octo::load_dag(branches, n_branches, mounts, n_mounts, (int32_t)T, dag, err);
+        if (rc != OCTOPUS_OK) return fail(rc, err);
+        std::vector<int32_t> sp, pg, lo, hi;
+        rc = octo::build_segments(dag, page_ptr, pages, page_size, n_pages, cursors, n_cursors,
+                                  sp, pg, lo, hi, err);
+        if (rc != OCTOPUS_OK) return fail(rc, err);
+        if (pg.size() > (size_t)INT32_MAX) return fail(OCTOPUS_EINVAL, "too many segments");
+        *n_seg_out = (int32_t)pg.size();
+        if (seg_capacity < (int64_t)pg.size())
+            return fail(OCTOPUS_EWORKSPACE, "segment capacity too small; need " +
+                                                std::to_string(pg.size()));
+        if (!seg_ptr_out || !seg_page_out || !seg_lo_out || !seg_hi_out)
+            return fail(OCTOPUS_EINVAL, "NULL output array");
+        std::copy(sp.begin(), sp.end(), seg_ptr_out);
+        std::copy(pg.begin(), pg.end(), seg_page_out);
+        std::copy(lo.begin(), lo.end(), seg_lo_out);
+        std::copy(hi.begin(), hi.end(), seg_hi_out);
+        return ok();
+    } catch (const std::bad_alloc&) {
+        return fail(OCTOPUS_ENOMEM, "host allocation failed while building segments");
+    }
+}
+
+size_t octopus_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t n_split) {
+    if (B < 1 || Hq < 1 || D < 1 || n_split < 1) return 0;
+    return (size_t)B * n_split * Hq * (D + 2) * sizeof(float);
+}
+
+int octopus_paged_mount_decode(octopus_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                               int32_t D, int32_t page_size, float scale, const void* q,
+                               const void* k_pool, const void* v_pool, int32_t n_pages,
+                               const int32_t* seg_ptr, const int32_t* seg_page,
+                               const int32_t* seg_lo, const int32_t* seg_hi, int32_t n_split,
+                               void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+    if (dtype != OCTOPUS_BF16) return fail(OCTOPUS_EUNSUPPORTED, "decode supports bf16 only");
+    if (D != 128) return fail(OCTOPUS_EUNSUPPORTED, "decode supports head_dim 128 only");
+    if (page_size != 64) return fail(OCTOPUS_EUNSUPPORTED, "decode supports page_size 64 only");
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+        return fail(OCTOPUS_EINVAL, "B, Hq, Hkv must be positive with Hq % Hkv == 0");
+    if (Hq / Hkv > 8) return fail(OCTOPUS_EUNSUPPORTED, "Hq / Hkv must be <= 8");
+    if (n_split < 1 || n_split > 256) return fail(OCTOPUS_EINVAL, "n_split must be in [1, 256]");
+    if (n_pages < 0) return fail(OCTOPUS_EINVAL, "n_pages < 0");
+    for (const void* p : {q, k_pool, v_pool, (const void*)o}) {
+        if (p == nullptr) return fail(OCTOPUS_EINVAL, "a tensor pointer is NULL");
+        if (!aligned(p, 16)) return fail(OCTOPUS_EINVAL, "tensors must be 16-byte aligned");
+    }
+    if (!seg_ptr || !seg_page || !seg_lo || !seg_hi)
+        return fail(OCTOPUS_EINVAL, "segment arrays must not be NULL");
+    const size_t need = octopus_decode_workspace_bytes(B, Hq, D, n_split);
+    if (ws == nullptr || ws_bytes < need || !aligned(ws, 16))
+        return fail(OCTOPUS_EWORKSPACE, "decode workspace needs " + std::to_string(need) +
+                                            " bytes, 16-byte aligned");
+    if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
+    hipError_t e = octo::launch_decode_bf16(B, Hq, Hkv, D, page_size, scale, q, k_pool, v_pool,
+                                            n_pages, seg_ptr, seg_page, seg_lo, seg_hi,
+                                            n_split, o, lse, static_cast<float*>(ws),
+                                            (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,483 @@
+// Host-side planner for packed-DAG attention.  See plan.h.
+#include "plan.h"
+
+#include <algorithm>
+#include <cstring>
+#include <numeric>
+
+namespace octo {
+
+namespace {
+
+std::string row_msg(const char* what, long long idx, const char* detail) {
+    return std::string(what) + " " + std::to_string(idx) + ": " + detail;
+}
+
+// Sort and merge intervals in place (adjacent ones are joined).
+void merge(std::vector<Interval>& v) {
+    if (v.empty()) return;
+    std::sort(v.begin(), v.end(),
+              [](const Interval& a, const Interval& b) { return a.lo < b.lo; });
+    size_t w = 0;
+    for (size_t i = 1; i < v.size(); ++i) {
+        if (v[i].lo <= v[w].hi) {
+            v[w].hi = std::max(v[w].hi, v[i].hi);
+        } else {
+            v[++w] = v[i];
+        }
+    }
+    v.resize(w + 1);
+}
+
+int validate(const octopus_branch* br, int32_t nb, const octopus_mount* mt, int32_t nm,
+             int32_t T, std::string& err) {
+    if (nb < 1 || br == nullptr) { err = "no branches"; return OCTOPUS_EINVAL; }
+    if (nm < 0 || (nm > 0 && mt == nullptr)) { err = "bad mount table"; return OCTOPUS_EINVAL; }
+    if (T < 1 || T > kMaxTokens) {
+        err = "total_tokens must be in [1, 2^24]";
+        return OCTOPUS_EINVAL;
+    }
+    for (int32_t b = 0; b < nb; ++b) {
+        const octopus_branch& x = br[b];
+        if (x.len < 1) { err = row_msg("branch", b, "len < 1"); return OCTOPUS_EINVAL; }
+        if (b == 0) {
+            if (x.parent != -1 || x.fork != 0) {
+                err = "branch 0 must be the root (parent -1, fork 0)";
+                return OCTOPUS_EINVAL;
+            }
+        } else {
+            if (x.parent < 0 || x.parent >= b) {
+                err = row_msg("branch", b, "parent must have a lower index");
+                return OCTOPUS_EINVAL;
+            }
+            if (x.fork < 0 || x.fork > br[x.parent].len) {
+                err = row_msg("branch", b, "fork outside the parent");
+                return OCTOPUS_EINVAL;
+            }
+        }
+        if (x.start < 0 || (int64_t)x.start + x.len > T) {
+            err = row_msg("branch", b, "span outside [0, T)");
+            return OCTOPUS_EINVAL;
+        }
+    }
+    // The spans must tile [0, T): sorted by start they are back to back.
+    std::vector<int32_t> ord(nb);
+    std::iota(ord.begin(), ord.end(), 0);
+    std::sort(ord.begin(), ord.end(), [&](int a, int b) { return br[a].start < br[b].start; });
+    int64_t at = 0;
+    for (int32_t b : ord) {
+        if (br[b].start != at) {
+            err = row_msg("branch", b, "branch spans do not tile [0, T) exactly");
+            return OCTOPUS_EINVAL;
+        }
+        at += br[b].len;
+    }
+    if (at != T) { err = "branch spans do not tile [0, T) exactly"; return OCTOPUS_EINVAL; }
+    for (int32_t i = 0; i < nm; ++i) {
+        const octopus_mount& m = mt[i];
+        if (m.reader < 0 || m.reader >= nb || m.producer < 0 || m.producer >= nb) {
+            err = row_msg("mount", i, "branch index out of range");
+            return OCTOPUS_EINVAL;
+        }
+        if (m.reader == m.producer) {
+            err = row_msg("mount", i, "reader == producer");
+            return OCTOPUS_EINVAL;
+        }
+        if (m.rpos < 0 || m.rpos > br[m.reader].len) {
+            err = row_msg("mount", i, "rpos outside the reader");
+            return OCTOPUS_EINVAL;
+        }
+        if (!(0 <= m.s && m.s < m.e && m.e <= br[m.producer].len)) {
+            err = row_msg("mount", i, "span outside the producer");
+            return OCTOPUS_EINVAL;
+        }
+    }
+    return OCTOPUS_OK;
+}
+
+// Positions by an explicit worklist over (branch, offset) requests.  A branch is
+// "open" while it sits on the stack; asking an open branch for an offset it has
+// not reached yet is a dependency cycle.
+int compute_positions(DagInfo& d, std::string& err) {
+    const int32_t nb = (int32_t)d.br.size();
+    std::vector<std::vector<int64_t>> xs(nb);
+    std::vector<size_t> next_mount(nb, 0);
+    std::vector<char> open(nb, 0);
+    struct Req { int32_t b, r; };
+    std::vector<Req> stack;
+    stack.reserve(nb);
+    for (int32_t b0 = 0; b0 < nb; ++b0) {
+        for (auto& x : xs[b0]) (void)x;
+        stack.push_back({b0, d.br[b0].len});
+        open[b0] = 1;
+        while (!stack.empty()) {
+            Req& top = stack.back();
+            const int32_t b = top.b;
+            if ((int64_t)xs[b].size() > top.r) {
+                open[b] = 0;
+                stack.pop_back();
+                continue;
+            }
+            const int32_t k = (int32_t)xs[b].size();
+            const octopus_branch& B = d.br[b];
+            // Dependencies of x_b(k): the parent's position at the fork (k = 0), and the
+            // last mounted key of every mount issued at offset k.
+            Req need{-1, -1};
+            if (k == 0 && B.parent >= 0 && (int64_t)xs[B.parent].size() <= B.fork) {
+                need = {B.parent, B.fork};
+            } else {
+                const auto& ms = d.mounts_of[b];
+                for (size_t i = next_mount[b]; i < ms.size() && d.mt[ms[i]].rpos == k; ++i) {
+                    const octopus_mount& m = d.mt[ms[i]];
+                    if ((int64_t)xs[m.producer].size() <= m.e - 1) {
+                        need = {m.producer, m.e - 1};
+                        break;
+                    }
+                }
+            }
+            if (need.b >= 0) {
+                if (open[need.b]) {
+                    err = "position of branch " + std::to_string(need.b) + " offset " +
+                          std::to_string(need.r) + " depends on itself";
+                    return OCTOPUS_ECYCLE;
+                }
+                open[need.b] = 1;
+                stack.push_back(need);
+                continue;
+            }
+            int64_t v = (k == 0) ? (B.parent < 0 ? 0 : xs[B.parent][B.fork]) : xs[b][k - 1] + 1;
+            const auto& ms = d.mounts_of[b];
+            while (next_mount[b] < ms.size() && d.mt[ms[next_mount[b]]].rpos == k) {
+                const octopus_mount& m = d.mt[ms[next_mount[b]]];
+                // e_A = position of the last mounted key + 1; next = max(p_B, e_A + 1).
+                v = std::max(v, xs[m.producer][m.e - 1] + 2);
+                ++next_mount[b];
+            }
+            xs[b].push_back(v);
+        }
+    }
+    d.pos.assign(d.T, 0);
+    for (int32_t b = 0; b < nb; ++b) {
+        for (int32_t r = 0; r < d.br[b].len; ++r) {
+            if (xs[b][r] > INT32_MAX) {
+                err = "position exceeds int32";
+                return OCTOPUS_EINVAL;
+            }
+            d.pos[d.br[b].start + r] = xs[b][r];
+        }
+    }
+    return OCTOPUS_OK;
+}
+
+}  // namespace
+
+void DagInfo::row_context(int32_t b, int32_t r, std::vector<Interval>& out,
+                          std::vector<Interval>& scratch) const {
+    scratch.assign(inherited[b].begin(), inherited[b].end());
+    const octopus_branch& B = br[b];
+    scratch.push_back({B.start, (int64_t)B.start + r + 1});
+    for (int32_t id : mounts_of[b]) {
+        const octopus_mount& m = mt[id];
+        if (m.rpos > r) break;
+        const int64_t ps = br[m.producer].start;
+        scratch.push_back({ps + m.s, ps + m.e});
+    }
+    merge(scratch);
+    out.swap(scratch);
+}
+
+int32_t DagInfo::owner(int64_t j) const {
+    // order_by_start sorted by start: the last branch whose start <= j.
+    size_t lo = 0, hi = order_by_start.size();
+    while (hi - lo > 1) {
+        size_t mid = (lo + hi) / 2;
+        if (br[order_by_start[mid]].start <= j) lo = mid; else hi = mid;
+    }
+    return order_by_start[lo];
+}
+
+int load_dag(const octopus_branch* br, int32_t nb, const octopus_mount* mt, int32_t nm,
+             int32_t T, DagInfo& d, std::string& err) {
+    int rc = validate(br, nb, mt, nm, T, err);
+    if (rc != OCTOPUS_OK) return rc;
+    d.T = T;
+    d.br.assign(br, br + nb);
+    d.mt.assign(mt, mt + nm);
+    d.mounts_of.assign(nb, {});
+    for (int32_t i = 0; i < nm; ++i) d.mounts_of[mt[i].reader].push_back(i);
+    for (auto& v : d.mounts_of) {
+        std::stable_sort(v.begin(), v.end(),
+                         [&](int32_t a, int32_t b) { return d.mt[a].rpos < d.mt[b].rpos; });
+    }
+    // H(b) = H(parent) ∪ parent's own [0, fork) ∪ parent's mounts issued at rpos <= fork.
+    d.inherited.assign(nb, {});
+    for (int32_t b = 1; b < nb; ++b) {
+        const octopus_branch& B = d.br[b];
+        const octopus_branch& P = d.br[B.parent];
+        std::vector<Interval> h = d.inherited[B.parent];
+        if (B.fork > 0) h.push_back({P.start, (int64_t)P.start + B.fork});
+        for (int32_t id : d.mounts_of[B.parent]) {
+            const octopus_mount& m = d.mt[id];
+            if (m.rpos > B.fork) break;
+            const int64_t ps = d.br[m.producer].start;
+            h.push_back({ps + m.s, ps + m.e});
+        }
+        merge(h);
+        d.inherited[b].swap(h);
+    }
+    d.order_by_start.resize(nb);
+    std::iota(d.order_by_start.begin(), d.order_by_start.end(), 0);
+    std::sort(d.order_by_start.begin(), d.order_by_start.end(),
+              [&](int a, int b) { return d.br[a].start < d.br[b].start; });
+    return compute_positions(d, err);
+}
+
+int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, int32_t nm,
+               int32_t T, int32_t kv_tile, Plan& p, std::string& err) {
+    if (kv_tile != 64) {
+        err = "kv_tile must be 64";
+        return OCTOPUS_EUNSUPPORTED;
+    }
+    int rc = load_dag(br, nb, mt, nm, T, p.dag, err);
+    if (rc != OCTOPUS_OK) return rc;
+    const DagInfo& d = p.dag;
+    const int32_t Bq = kQTile, Bk = kv_tile;
+    p.T = T;
+    p.Bq = Bq;
+    p.Bk = Bk;
+    p.row_words = Bk / 64;
+    p.col_words = Bq / 64;
+    p.nQT = (T + Bq - 1) / Bq;
+    p.nKT = (T + Bk - 1) / Bk;
+    const int32_t nQT = p.nQT, nKT = p.nKT;
+
+    std::vector<int32_t> row_branch(T);
+    for (int32_t b = 0; b < nb; ++b)
+        for (int32_t r = 0; r < d.br[b].len; ++r) row_branch[d.br[b].start + r] = b;
+
+    std::vector<std::vector<Interval>> rows(Bq);
+    std::vector<Interval> scratch;
+    std::vector<int32_t> full_diff(nKT + 1), touch_diff(nKT + 1);
+    std::vector<size_t> cursor(Bq);
+    p.qt_ptr.assign(nQT + 1, 0);
+    p.q_pairs.clear();
+    p.mask_rows.clear();
+    p.nnz = 0;
+    std::vector<uint64_t> words(Bq * p.row_words);
+
+    for (int32_t qt = 0; qt < nQT; ++qt) {
+        const int32_t r0 = qt * Bq;
+        const int32_t nv = std::min(Bq, T - r0);
+        std::fill(full_diff.begin(), full_diff.end(), 0);
+        std::fill(touch_diff.begin(), touch_diff.end(), 0);
+        for (int32_t rr = 0; rr < nv; ++rr) {
+            const int32_t i = r0 + rr;
+            const int32_t b = row_branch[i];
+            d.row_context(b, i - d.br[b].start, rows[rr], scratch);
+            for (const Interval& iv : rows[rr]) {
+                p.nnz += iv.hi - iv.lo;
+                const int64_t t0 = iv.lo / Bk, t1 = (iv.hi + Bk - 1) / Bk;
+                touch_diff[t0] += 1;
+                touch_diff[t1] -= 1;
+                const int64_t f0 = (iv.lo + Bk - 1) / Bk, f1 = iv.hi / Bk;
+                if (f0 < f1) {
+                    full_diff[f0] += 1;
+                    full_diff[f1] -= 1;
+                }
+            }
+            cursor[rr] = 0;
+        }
+        int32_t touch = 0, full = 0;
+        for (int32_t t = 0; t < nKT; ++t) {
+            touch += touch_diff[t];
+            full += full_diff[t];
+            if (touch == 0) continue;
+            if (full == nv) {
+                p.q_pairs.push_back({t, -1});
+                continue;
+            }
+            // PARTIAL: per-row bits of keys [t*Bk, t*Bk + Bk) that the row sees.
+            const int64_t k0 = (int64_t)t * Bk, k1 = k0 + Bk;
+            std::fill(words.begin(), words.end(), 0);
+            for (int32_t rr = 0; rr < nv; ++rr) {
+                const auto& iv = rows[rr];
+                size_t c = cursor[rr];
+                while (c < iv.size() && iv[c].hi <= k0) ++c;
+                cursor[rr] = c;
+                for (size_t j = c; j < iv.size() && iv[j].lo < k1; ++j) {
+                    const int64_t a = std::max(iv[j].lo, k0) - k0;
+                    const int64_t e = std::min(iv[j].hi, k1) - k0;
+                    for (int64_t x = a; x < e; ++x)
+                        words[rr * p.row_words + (x >> 6)] |= 1ull << (x & 63);
+                }
+            }
+            const int32_t idx = (int32_t)(p.mask_rows.size() / (Bq * p.row_words));
+            p.mask_rows.insert(p.mask_rows.end(), words.begin(), words.end());
+            p.q_pairs.push_back({t, idx});
+        }
+        p.qt_ptr[qt + 1] = (int32_t)p.q_pairs.size();
+    }
+    p.n_partial = (int64_t)(p.mask_rows.size() / (Bq * p.row_words));
+
+    // Key-major copy of every PARTIAL mask, for the KV-tile owners of the backward.
+    p.mask_cols.assign(p.n_partial * Bk * p.col_words, 0);
+    for (int64_t m = 0; m < p.n_partial; ++m) {
+        const uint64_t* wr = &p.mask_rows[m * Bq * p.row_words];
+        uint64_t* wc = &p.mask_cols[m * Bk * p.col_words];
+        for (int32_t rr = 0; rr < Bq; ++rr)
+            for (int32_t kk = 0; kk < Bk; ++kk)
+                if ((wr[rr * p.row_words + (kk >> 6)] >> (kk & 63)) & 1)
+                    wc[kk * p.col_words + (rr >> 6)] |= 1ull << (rr & 63);
+    }
+
+    // Transposed lists: for every KV tile, the query tiles that see it, ascending.
+    p.kt_ptr.assign(nKT + 1, 0);
+    for (const TilePair& tp : p.q_pairs) p.kt_ptr[tp.tile + 1] += 1;
+    for (int32_t t = 0; t < nKT; ++t) p.kt_ptr[t + 1] += p.kt_ptr[t];
+    p.k_pairs.assign(p.q_pairs.size(), {0, 0});
+    {
+        std::vector<int32_t> fill(p.kt_ptr.begin(), p.kt_ptr.end() - 1);
+        for (int32_t qt = 0; qt < nQT; ++qt)
+            for (int32_t i = p.qt_ptr[qt]; i < p.qt_ptr[qt + 1]; ++i)
+                p.k_pairs[fill[p.q_pairs[i].tile]++] = {qt, p.q_pairs[i].mask};
+    }
+
+    // Longest-first launch orders (ties by index).
+    p.fwd_order.resize(nQT);
+    std::iota(p.fwd_order.begin(), p.fwd_order.end(), 0);
+    std::stable_sort(p.fwd_order.begin(), p.fwd_order.end(), [&](int a, int b) {
+        return p.qt_ptr[a + 1] - p.qt_ptr[a] > p.qt_ptr[b + 1] - p.qt_ptr[b];
+    });
+    p.bwd_order.resize(nKT);
+    std::iota(p.bwd_order.begin(), p.bwd_order.end(), 0);
+    std::stable_sort(p.bwd_order.begin(), p.bwd_order.end(), [&](int a, int b) {
+        return p.kt_ptr[a + 1] - p.kt_ptr[a] > p.kt_ptr[b + 1] - p.kt_ptr[b];
+    });
+    p.max_q_list = 0;
+    for (int32_t qt = 0; qt < nQT; ++qt)
+        p.max_q_list = std::max(p.max_q_list, p.qt_ptr[qt + 1] - p.qt_ptr[qt]);
+    p.max_kv_list = 0;
+    for (int32_t t = 0; t < nKT; ++t)
+        p.max_kv_list = std::max(p.max_kv_list, p.kt_ptr[t + 1] - p.kt_ptr[t]);
+
+    // Device image: every array 256-byte aligned.
+    DevLayout& L = p.layout;
+    size_t at = 0;
+    auto place = [&](size_t bytes) {
+        size_t off = at;
+        at = (at + bytes + 255) & ~size_t(255);
+        return off;
+    };
+    L.fwd_order = place(p.fwd_order.size() * 4);
+    L.qt_ptr = place(p.qt_ptr.size() * 4);
+    L.q_pairs = place(p.q_pairs.size() * sizeof(TilePair));
+    L.bwd_order = place(p.bwd_order.size() * 4);
+    L.kt_ptr = place(p.kt_ptr.size() * 4);
+    L.k_pairs = place(p.k_pairs.size() * sizeof(TilePair));
+    L.mask_rows = place(p.mask_rows.size() * 8);
+    L.mask_cols = place(p.mask_cols.size() * 8);
+    L.total = std::max<size_t>(at, 256);
+    p.blob.assign(L.total, 0);
+    auto put = [&](size_t off, const void* src, size_t bytes) {
+        if (bytes) std::memcpy(p.blob.data() + off, src, bytes);
+    };
+    put(L.fwd_order, p.fwd_order.data(), p.fwd_order.size() * 4);
+    put(L.qt_ptr, p.qt_ptr.data(), p.qt_ptr.size() * 4);
+    put(L.q_pairs, p.q_pairs.data(), p.q_pairs.size() * sizeof(TilePair));
+    put(L.bwd_order, p.bwd_order.data(), p.bwd_order.size() * 4);
+    put(L.kt_ptr, p.kt_ptr.data(), p.kt_ptr.size() * 4);
+    put(L.k_pairs, p.k_pairs.data(), p.k_pairs.size() * sizeof(TilePair));
+    put(L.mask_rows, p.mask_rows.data(), p.mask_rows.size() * 8);
+    put(L.mask_cols, p.mask_cols.data(), p.mask_cols.size() * 8);
+    return OCTOPUS_OK;
+}
+
+void export_mask(const Plan& p, int32_t lo, int32_t hi, uint8_t* bits) {
+    const size_t row_bytes = (size_t)(p.T + 7) / 8;
+    std::memset(bits, 0, row_bytes * (size_t)(hi - lo));
+    for (int32_t i = lo; i < hi; ++i) {
+        uint8_t* out = bits + (size_t)(i - lo) * row_bytes;
+        const int32_t qt = i / p.Bq, rr = i % p.Bq;
+        for (int32_t k = p.qt_ptr[qt]; k < p.qt_ptr[qt + 1]; ++k) {
+            const TilePair& tp = p.q_pairs[k];
+            const int64_t k0 = (int64_t)tp.tile * p.Bk;
+            for (int32_t x = 0; x < p.Bk; ++x) {
+                const int64_t j = k0 + x;
+                if (j >= p.T) break;
+                bool on;
+                if (tp.mask < 0) {
+                    on = true;
+                } else {
+                    const uint64_t w =
+                        p.mask_rows[((size_t)tp.mask * p.Bq + rr) * p.row_words + (x >> 6)];
+                    on = (w >> (x & 63)) & 1;
+                }
+                if (on) out[j >> 3] |= (uint8_t)(1u << (j & 7));
+            }
+        }
+    }
+}
+
+int build_segments(const DagInfo& d, const int32_t* page_ptr, const int32_t* pages,
+                   int32_t page_size, int32_t n_pages, const int32_t* cursors,
+                   int32_t n_cursors, std::vector<int32_t>& seg_ptr,
+                   std::vector<int32_t>& seg_page, std::vector<int32_t>& seg_lo,
+                   std::vector<int32_t>& seg_hi, std::string& err) {
+    const int32_t nb = (int32_t)d.br.size();
+    if (page_size < 1 || n_pages < 0 || n_cursors < 0 || page_ptr == nullptr ||
+        (n_cursors > 0 && cursors == nullptr)) {
+        err = "bad page table or cursor arguments";
+        return OCTOPUS_EINVAL;
+    }
+    if (page_ptr[0] != 0) { err = "page_ptr[0] must be 0"; return OCTOPUS_EINVAL; }
+    for (int32_t b = 0; b < nb; ++b) {
+        const int64_t need = ((int64_t)d.br[b].len + page_size - 1) / page_size;
+        if (page_ptr[b + 1] - page_ptr[b] < need) {
+            err = row_msg("branch", b, "page table shorter than the branch");
+            return OCTOPUS_EINVAL;
+        }
+        for (int32_t k = page_ptr[b]; k < page_ptr[b] + need; ++k) {
+            if (pages == nullptr || pages[k] < 0 || pages[k] >= n_pages) {
+                err = row_msg("branch", b, "page id outside [0, n_pages)");
+                return OCTOPUS_EINVAL;
+            }
+        }
+    }
+    seg_ptr.assign(n_cursors + 1, 0);
+    seg_page.clear();
+    seg_lo.clear();
+    seg_hi.clear();
+    std::vector<Interval> ctx, scratch;
+    for (int32_t c = 0; c < n_cursors; ++c) {
+        const int32_t b = cursors[c];
+        if (b < 0 || b >= nb) {
+            err = row_msg("cursor", c, "branch id out of range");
+            return OCTOPUS_EINVAL;
+        }
+        d.row_context(b, d.br[b].len - 1, ctx, scratch);
+        for (const Interval& iv : ctx) {
+            int64_t j = iv.lo;
+            while (j < iv.hi) {
+                const int32_t o = d.owner(j);
+                const int64_t ostart = d.br[o].start;
+                const int64_t stop = std::min<int64_t>(iv.hi, ostart + d.br[o].len);
+                int64_t r = j - ostart;
+                const int64_t rend = stop - ostart;
+                while (r < rend) {
+                    const int64_t pi = r / page_size;
+                    const int64_t slot0 = r - pi * page_size;
+                    const int64_t slot1 = std::min<int64_t>(page_size, rend - pi * page_size);
+                    seg_page.push_back(pages[page_ptr[o] + pi]);
+                    seg_lo.push_back((int32_t)slot0);
+                    seg_hi.push_back((int32_t)slot1);
+                    r = (pi + 1) * page_size;
+                }
+                j = stop;
+            }
+        }
+        seg_ptr[c + 1] = (int32_t)seg_page.size();
+    }
+    return OCTOPUS_OK;
+}
+
+}  // namespace octo

@@ -1,0 +1,90 @@
+// Host-side planner for packed-DAG attention (internal interface).
+//
+// Builds, from the branch and mount tables, everything the device kernels need:
+// per 128-row query tile the KV tiles some row sees (FULL or PARTIAL with a per-row
+// bit mask), the transposed lists for the backward's KV-tile owners, and
+// longest-first launch orders.  Visibility follows the fork / read_thread rules of
+// the Octopus project page (primitives table) and positions follow the monotonic
+// jump rule of its card "02 · Memory".
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "octopus_dag.h"
+
+namespace octo {
+
+constexpr int kQTile = 128;
+constexpr int kMaxTokens = 1 << 24;
+
+struct Interval {
+    int64_t lo, hi;  // [lo, hi) in packed indices
+};
+
+// A listed (query tile, KV tile) pair as the kernels read it: 8 bytes.
+struct TilePair {
+    int32_t tile;  // KV tile (forward lists) or query tile (transposed lists)
+    int32_t mask;  // -1 for FULL, else the index of the PARTIAL bit mask
+};
+
+// Validated tables plus the derived per-branch data the planner and the decode
+// segment builder share.
+struct DagInfo {
+    int32_t T = 0;
+    std::vector<octopus_branch> br;
+    std::vector<octopus_mount> mt;
+    std::vector<std::vector<int32_t>> mounts_of;  // per reader: mount ids sorted by rpos
+    std::vector<std::vector<Interval>> inherited;  // H(b), merged
+    std::vector<int32_t> order_by_start;           // branches sorted by start
+    std::vector<int64_t> pos;                      // position of every packed token
+
+    // Ctx(g(b, r)) as sorted, disjoint, non-adjacent intervals (the query included).
+    void row_context(int32_t b, int32_t r, std::vector<Interval>& out,
+                     std::vector<Interval>& scratch) const;
+    // Owning branch of a packed index.
+    int32_t owner(int64_t j) const;
+};
+
+// Returns OCTOPUS_OK or an error code with `err` set.
+int load_dag(const octopus_branch* br, int32_t nb, const octopus_mount* mt, int32_t nm,
+             int32_t T, DagInfo& out, std::string& err);
+
+struct DevLayout {
+    size_t fwd_order = 0, qt_ptr = 0, q_pairs = 0, bwd_order = 0, kt_ptr = 0,
+           k_pairs = 0, mask_rows = 0, mask_cols = 0, total = 0;
+};
+
+struct Plan {
+    DagInfo dag;
+    int32_t T = 0, Bq = kQTile, Bk = 64, nQT = 0, nKT = 0;
+    int32_t row_words = 1;  // uint64 words per row of a PARTIAL mask   (Bk / 64)
+    int32_t col_words = 2;  // uint64 words per key of a PARTIAL mask   (Bq / 64)
+    std::vector<int32_t> fwd_order, qt_ptr;
+    std::vector<TilePair> q_pairs;
+    std::vector<int32_t> bwd_order, kt_ptr;
+    std::vector<TilePair> k_pairs;
+    std::vector<uint64_t> mask_rows;  // [n_partial][Bq][row_words]
+    std::vector<uint64_t> mask_cols;  // [n_partial][Bk][col_words]
+    int64_t nnz = 0, n_partial = 0;
+    int32_t max_q_list = 0, max_kv_list = 0;
+    DevLayout layout;
+    std::vector<unsigned char> blob;  // host image of the device copy
+    void* dev = nullptr;              // caller-owned device copy after upload
+};
+
+int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, int32_t nm,
+               int32_t T, int32_t kv_tile, Plan& out, std::string& err);
+
+// Dense bits of rows [lo, hi) from the tile lists only (see octopus_plan_export_mask).
+void export_mask(const Plan& p, int32_t lo, int32_t hi, uint8_t* bits);
+
+int build_segments(const DagInfo& dag, const int32_t* page_ptr, const int32_t* pages,
+                   int32_t page_size, int32_t n_pages, const int32_t* cursors,
+                   int32_t n_cursors, std::vector<int32_t>& seg_ptr,
+                   std::vector<int32_t>& seg_page, std::vector<int32_t>& seg_lo,
+                   std::vector<int32_t>& seg_hi, std::string& err);
+
+}  // namespace octo
