@@ -201,7 +201,7 @@ int octopus_decode_segments(const octopus_branch* branches, int32_t n_branches,
                             int32_t* n_seg_out);
 
 /* Workspace bytes for octopus_paged_mount_decode: float32 partial states
- * [B][n_split][Hq][D + 2]. */
+ * [B][n_split][Hq][D + 4]. */
 size_t octopus_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t n_split);
 
 /* One-token attention of B cursors over their segments, read in place from the

@@ -1,0 +1,134 @@
+"""GPU parity of paged mounted decode against the float64 oracle (and against the
+packed forward), through the C-ABI library."""
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import attention as A
+from oracle import dag as D
+from oracle import decode as DEC
+from parity import TOL, check_close, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_inputs(wl, Hq=16, Hkv=4, Dh=128, seed=55):
+    rng = np.random.default_rng(seed)
+    return synth.draw_decode_inputs(rng, len(wl.cursors), Hq, Hkv, Dh, wl.n_pages,
+                                    wl.page_size)
+
+
+def _gpu_decode(wl, x, n_split, segs=None):
+    import torch
+    import tree_packed_block_amd as tpb
+    if segs is None:
+        segs = tpb.decode_segments(wl.dag.branches, wl.dag.mounts, wl.page_ptr, wl.pages,
+                                   wl.page_size, wl.n_pages, wl.cursors)
+    sd = [torch.from_numpy(np.ascontiguousarray(s, dtype=np.int32)).cuda() for s in segs]
+    q, kp, vp = dev(x["q"], "bf16"), dev(x["k_pool"], "bf16"), dev(x["v_pool"], "bf16")
+    o, lse = tpb.paged_mount_decode(q, kp, vp, *sd, n_split=n_split)
+    torch.cuda.synchronize()
+    return host(o), host(lse)
+
+
+def _oracle(wl, x):
+    return DEC.decode(x["q"], x["k_pool"], x["v_pool"], wl.dag.branches, wl.dag.mounts,
+                      wl.page_ptr, wl.pages, wl.page_size, wl.cursors)
+
+
+@pytest.mark.parametrize("n_split", [1, 3, 16])
+def test_decode_small(n_split):
+    say(f"case decode small n_split={n_split}")
+    wl = synth.decode_workload(seed=5, n_cursors=6, prefix=256, own_max=300, span_max=100,
+                               page_size=64)
+    x = _decode_inputs(wl)
+    o, lse = _gpu_decode(wl, x, n_split)
+    ro, rl = _oracle(wl, x)
+    check_close(o, ro, TOL["bf16"], "O")
+    check_close(lse, rl, TOL["bf16"], "LSE")
+
+
+def test_decode_full_batch():
+    """64 cursors, 16K shared radix prefix, private branches up to 32K, up to three
+    mounted spans of up to 8K: every cursor against the oracle; the result does not
+    depend on the split count."""
+    say("case decode 64 cursors")
+    wl = synth.decode_workload()
+    x = _decode_inputs(wl)
+    o, lse = _gpu_decode(wl, x, 32)
+    ro, rl = _oracle(wl, x)
+    check_close(o, ro, TOL["bf16"], "O")
+    check_close(lse, rl, TOL["bf16"], "LSE")
+    o2, lse2 = _gpu_decode(wl, x, 128)
+    check_close(o2, ro, TOL["bf16"], "O (128 splits)")
+    check_close(lse2, rl, TOL["bf16"], "LSE (128 splits)")
+
+
+def test_decode_matches_packed_forward():
+    """K/V of a packed tree written into pool pages: decoding the last token of every
+    branch gives the packed forward's row of that token (rollout and packed trainer
+    read the same graph)."""
+    import torch
+    import tree_packed_block_amd as tpb
+    say("case decode vs packed forward")
+    dag, rng = synth.build("episode_small")
+    pos = D.positions(dag.branches, dag.mounts)
+    x = synth.draw_attention_inputs(rng, dag.T, 16, 4, 128, pos, dtype="bf16")
+    n_pages, ptr, pages = synth.dags.assign_pages(dag, 64, np.random.default_rng(9))
+    kp = np.zeros((n_pages, 4, 64, 128), dtype=np.float32)
+    vp = np.zeros_like(kp)
+    for b, (parent, fork, start, L) in enumerate(dag.branches):
+        r = np.arange(L)
+        kp[pages[ptr[b] + r // 64], :, r % 64] = x["k"][start + r]
+        vp[pages[ptr[b] + r // 64], :, r % 64] = x["v"][start + r]
+    last = dag.branches[:, 2] + dag.branches[:, 3] - 1
+    wl = synth.DecodeWorkload(dag, 64, n_pages, ptr, pages,
+                              np.arange(dag.nb, dtype=np.int32))
+    xd = {"q": x["q"][last], "k_pool": kp, "v_pool": vp}
+    od, ld = _gpu_decode(wl, xd, 4)
+    plan = tpb.Plan(dag.branches, dag.mounts, dag.T).upload()
+    of, lf = tpb.attn_fwd(plan, dev(x["q"], "bf16"), dev(x["k"], "bf16"), dev(x["v"], "bf16"))
+    torch.cuda.synchronize()
+    of, lf = host(of)[last], host(lf)[:, last].T
+    ro, rl = A.attn_fwd(x["q"], x["k"], x["v"], dag.branches, dag.mounts)
+    check_close(od, ro[last], TOL["bf16"], "decode O vs oracle")
+    check_close(od, of, TOL["bf16"], "decode O vs packed forward")
+    check_close(ld, lf, TOL["bf16"], "decode LSE vs packed forward")
+
+
+def test_decode_skips_out_of_range_pages():
+    """A segment naming a page outside the pool is skipped (no read)."""
+    say("case decode bad page")
+    import tree_packed_block_amd as tpb
+    wl = synth.decode_workload(seed=5, n_cursors=4, prefix=128, own_max=200, span_max=50,
+                               page_size=64)
+    x = _decode_inputs(wl)
+    sp, pg, lo, hi = tpb.decode_segments(wl.dag.branches, wl.dag.mounts, wl.page_ptr,
+                                         wl.pages, 64, wl.n_pages, wl.cursors)
+    # insert a bogus segment at the front of cursor 0
+    sp2 = sp.copy()
+    sp2[1:] += 1
+    pg2 = np.concatenate([[wl.n_pages + 1000], pg]).astype(np.int32)
+    lo2 = np.concatenate([[0], lo]).astype(np.int32)
+    hi2 = np.concatenate([[64], hi]).astype(np.int32)
+    o1, l1 = _gpu_decode(wl, x, 2, (sp, pg, lo, hi))
+    o2, l2 = _gpu_decode(wl, x, 2, (sp2, pg2, lo2, hi2))
+    check_close(o2, o1, 1e-6, "O with a skipped segment")
+    check_close(l2, l1, 1e-6, "LSE with a skipped segment")
+
+
+def test_decode_argument_errors():
+    import torch
+    import tree_packed_block_amd as tpb
+    q = torch.zeros((2, 16, 128), dtype=torch.bfloat16, device="cuda")
+    kp = torch.zeros((4, 4, 64, 128), dtype=torch.bfloat16, device="cuda")
+    seg = torch.zeros(3, dtype=torch.int32, device="cuda")
+    with pytest.raises(tpb.OctopusError) as ei:
+        tpb.paged_mount_decode(q, kp, kp, seg, seg, seg, seg, n_split=0)
+    assert ei.value.name == "EINVAL"
+    q64 = torch.zeros((2, 16, 64), dtype=torch.bfloat16, device="cuda")
+    kp64 = torch.zeros((4, 4, 64, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(tpb.OctopusError) as ei:
+        tpb.paged_mount_decode(q64, kp64, kp64, seg, seg, seg, seg, n_split=2)
+    assert ei.value.name == "EUNSUPPORTED"

@@ -257,7 +257,7 @@ int octopus_decode_segments(const octopus_branch* branches, int32_t n_branches,
 
 size_t octopus_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t n_split) {
     if (B < 1 || Hq < 1 || D < 1 || n_split < 1) return 0;
-    return (size_t)B * n_split * Hq * (D + 2) * sizeof(float);
+    return (size_t)B * n_split * Hq * (D + 4) * sizeof(float);
 }
 
 int octopus_paged_mount_decode(octopus_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,

@@ -1,14 +1,246 @@
-// Paged mounted decode on gfx950 (kernels follow).
+// Paged mounted decode on gfx950.
+//
+// Serving side of the episode DAG (Octopus project page, primitives table: `fork`
+// shares the parent's radix KV pages, `read_thread` mounts another branch's pages
+// c_A[s_A:e_A) zero-copy, `done` pins finished pages for mounts; card
+// "02 · Memory": a mount allocates no KV pages).  A cursor's current token attends to
+// its ancestor prefix, its own branch and its mounted spans, each read in place from
+// the page of the branch that owns it.  The host turns that context into segments
+// (page, slot_lo, slot_hi); this kernel streams them.
+//
+// Split kernel: every wave64 owns one (cursor, KV head, split) work item, a
+// contiguous run of the cursor's segments, and keeps a partial softmax state.  Per
+// 64-slot page the next page's K and V (2 x 16 KiB contiguous blocks of the pool) are
+// loaded into registers while the current one is computed.  Scores use the forward
+// kernel's transposed form S^T = K q^T (v_mfma_f32_32x32x16_bf16): the G query heads
+// of the KV head are the B operand's columns, so lane l holds head l % 32's scores
+// over 16 slots and the probabilities feed O^T += V^T P^T directly, with V staged
+// transposed in the wave's own LDS region.  Slots outside the segment are zero-filled
+// and masked.  The combine kernel merges the splits of each (cursor, head) by LSE.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace octo {
 
-hipError_t launch_decode_bf16(int, int, int, int, int, float, const void*, const void*,
-                              const void*, int, const int32_t*, const int32_t*,
-                              const int32_t*, const int32_t*, int, void*, float*, float*,
-                              hipStream_t) {
-    return hipErrorNotSupported;
+namespace {
+
+constexpr int kPage = 64;
+constexpr int kWaves = 4;
+
+template <int D>
+struct DecodeSmem {
+    static constexpr int KST = D + 8, VST = kPage + 8;
+    bf16 Ks[kPage * KST];
+    bf16 Vt[D * VST];
+};
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void decode_split_kernel(
+    int B, int Hq, int Hkv, int n_split, float scale_log2, const bf16* __restrict__ Qd,
+    const bf16* __restrict__ Kp, const bf16* __restrict__ Vp, int n_pages,
+    const int32_t* __restrict__ seg_ptr, const int32_t* __restrict__ seg_page,
+    const int32_t* __restrict__ seg_lo, const int32_t* __restrict__ seg_hi,
+    float* __restrict__ partial) {
+    constexpr int KS = D / 16, DB = D / 32, C8 = D / 8;
+    constexpr int KST = DecodeSmem<D>::KST, VST = DecodeSmem<D>::VST;
+    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kWaves * sizeof(DecodeSmem<D>)];
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int item = blockIdx.x * kWaves + w;
+    if (item >= B * Hkv * n_split) return;  // whole wave leaves; no block barriers below
+    DecodeSmem<D>& S = reinterpret_cast<DecodeSmem<D>*>(smem_raw)[w];
+    const int split = item % n_split;
+    const int kvh = (item / n_split) % Hkv;
+    const int c = item / (n_split * Hkv);
+    const int G = Hq / Hkv;
+    const int n = lane & 31, g = lane >> 5;
+
+    const int s0 = seg_ptr[c], s1 = seg_ptr[c + 1];
+    const long long ns = s1 - s0;
+    const int a = s0 + (int)((ns * split) / n_split);
+    const int b = s0 + (int)((ns * (split + 1)) / n_split);
+
+    // B operand: column n is query head kvh*G + n (zero for n >= G).
+    bf16x8 qf[KS];
+    const bool col_ok = n < G;
+    const bf16* qrow = Qd + ((size_t)c * Hq + (size_t)kvh * G + (col_ok ? n : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = col_ok ? ld16(qrow + 16 * ks + 8 * g) : zero8();
+
+    f32x16 o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = zero16();
+    float m = -1e30f, l = 0.f;
+
+    // Loader: lane covers column chunk c8 = lane % C8 of 4-row groups rg.
+    constexpr int RGS = kPage / 4;        // 16 row groups
+    constexpr int LPR = 64 / C8;          // lanes per column pass
+    constexpr int ITEMS = RGS / LPR;      // row groups per lane
+    const int c8 = lane % C8, rg0 = lane / C8;
+    bf16x8 kr[ITEMS][4], vr[ITEMS][4];
+    auto gload = [&](int sg) {
+        const int page = seg_page[sg], lo = seg_lo[sg], hi = seg_hi[sg];
+        const bool ok = page >= 0 && page < n_pages;
+        const size_t base = ((size_t)(ok ? page : 0) * Hkv + kvh) * kPage * D;
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int slot = 4 * (rg0 + LPR * it) + j;
+                if (ok && slot >= lo && slot < hi) {
+                    const size_t off = base + (size_t)slot * D + 8 * c8;
+                    kr[it][j] = ld16(Kp + off);
+                    vr[it][j] = ld16(Vp + off);
+                } else {
+                    kr[it][j] = zero8();
+                    vr[it][j] = zero8();
+                }
+            }
+    };
+    auto lds_put = [&]() {
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+            const int rg = rg0 + LPR * it;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) st16(&S.Ks[(4 * rg + j) * KST + 8 * c8], kr[it][j]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                bf16x4 t;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) t[j] = vr[it][j][e];
+                st8(&S.Vt[(8 * c8 + e) * VST + 4 * rg], t);
+            }
+        }
+    };
+
+    if (a < b) gload(a);
+    for (int sg = a; sg < b; ++sg) {
+        const int lo = seg_lo[sg], hi = seg_hi[sg];
+        const bool ok = seg_page[sg] >= 0 && seg_page[sg] < n_pages;
+        // The wave's previous reads of its LDS region come before these writes, and
+        // these writes before the reads below: one wave's LDS operations stay in order.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        lds_put();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        if (sg + 1 < b) gload(sg + 1);
+
+        f32x16 s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            s[kb] = zero16();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                s[kb] = mfma_32x32x16(ld16(&S.Ks[(kb * 32 + n) * KST + 16 * ks + 8 * g]), qf[ks],
+                                      s[kb]);
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int x = kb * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+                const float t = (ok && x >= lo && x < hi) ? s[kb][j] * scale_log2 : -INFINITY;
+                s[kb][j] = t;
+                mx = fmaxf(mx, t);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(m, mx);
+        const float alpha = fast_exp2(m - mnew);
+        m = mnew;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+        bf16x8 pf[4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float pv = fast_exp2(s[kb][j] - mnew);
+                l += pv;
+                pf[kb * 2 + (j >> 3)][j & 7] = (bf16)pv;
+            }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const bf16* vrow = &S.Vt[(db * 32 + n) * VST + 16 * kk + 4 * g];
+                o[db] = mfma_32x32x16(cat(ld8(vrow), ld8(vrow + 8)), pf[kk], o[db]);
+            }
+    }
+
+    l += __shfl_xor(l, 32);
+    if (col_ok) {
+        const int h = kvh * G + n;
+        float* out = partial + (((size_t)c * n_split + split) * Hq + h) * (D + 4);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                float4 t = make_float4(o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2],
+                                       o[db][4 * q4 + 3]);
+                *reinterpret_cast<float4*>(out + db * 32 + 8 * q4 + 4 * g) = t;
+            }
+        if (g == 0) {
+            out[D] = (a < b && l > 0.f) ? m : -INFINITY;
+            out[D + 1] = l;
+        }
+    }
+}
+
+// Merge the n_split partial states of every (cursor, query head): one wave each.
+// A partial state is D accumulator floats, the running max (log2 units), the running
+// sum, and 2 floats of padding so every state starts 16-byte aligned.
+template <int D>
+__global__ __launch_bounds__(64) void decode_combine_kernel(int B, int Hq, int n_split,
+                                                            const float* __restrict__ partial,
+                                                            bf16* __restrict__ O,
+                                                            float* __restrict__ LSE) {
+    const int c = blockIdx.x / Hq, h = blockIdx.x % Hq;
+    const int lane = threadIdx.x;
+    float M = -INFINITY;
+    for (int sp = 0; sp < n_split; ++sp)
+        M = fmaxf(M, partial[(((size_t)c * n_split + sp) * Hq + h) * (D + 4) + D]);
+    float L = 0.f;
+    float acc[D / 64];
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
+    for (int sp = 0; sp < n_split; ++sp) {
+        const float* p = partial + (((size_t)c * n_split + sp) * Hq + h) * (D + 4);
+        const float ms = p[D];
+        if (ms == -INFINITY) continue;
+        const float wgt = fast_exp2(ms - M);
+        L += wgt * p[D + 1];
+#pragma unroll
+        for (int e = 0; e < D / 64; ++e) acc[e] += wgt * p[lane + 64 * e];
+    }
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e)
+        O[((size_t)c * Hq + h) * D + lane + 64 * e] = (bf16)(acc[e] * inv);
+    if (LSE != nullptr && lane == 0) LSE[(size_t)c * Hq + h] = (M + log2f(L)) * kLn2;
+}
+
+hipError_t launch_decode_bf16(int B, int Hq, int Hkv, int D, int page_size, float scale,
+                              const void* q, const void* k_pool, const void* v_pool,
+                              int n_pages, const int32_t* seg_ptr, const int32_t* seg_page,
+                              const int32_t* seg_lo, const int32_t* seg_hi, int n_split,
+                              void* o, float* lse, float* partial, hipStream_t s) {
+    (void)page_size;
+    (void)D;  // checked by the caller: D == 128, page_size == 64
+    const int items = B * Hkv * n_split;
+    hipLaunchKernelGGL(decode_split_kernel<128>, dim3((items + kWaves - 1) / kWaves),
+                       dim3(64 * kWaves), 0, s, B, Hq, Hkv, n_split, scale * kLog2e,
+                       (const bf16*)q, (const bf16*)k_pool, (const bf16*)v_pool, n_pages,
+                       seg_ptr, seg_page, seg_lo, seg_hi, partial);
+    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(B * Hq), dim3(64), 0, s, B, Hq, n_split,
+                       partial, (bf16*)o, lse);
+    return hipGetLastError();
 }
 
 }  // namespace octo
