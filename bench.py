@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Benchmark of the packed-DAG attention path on one MI355X.
+
+Workload: one episode tree of 262,144 packed tokens (an 8,192-token orchestrator
+prefix, 8 worker branches of 16K-32K tokens water-filled to the exact total, a
+4,096-token orchestrator continuation mounting the terminal spans of 3 workers),
+GQA 16 query / 4 KV heads, head_dim 128, bf16; plus one paged decode batch of 64
+cursors (16K shared radix prefix, private branches up to 32K, 0-3 mounted spans of up
+to 8K, 64-token pages).
+
+One step = the whole hot path over that batch: build the tile plan on the host
+(validation, positions, tile lists) and upload it; forward; backward (Delta, dK/dV
+owner pass, dQ); build the decode segments on the host and upload them; decode.
+Host work for step k+1 overlaps the GPU work of step k (at most two steps in
+flight); inputs are resident in HBM before timing starts.
+
+Printed: one JSON line.  ``value`` is useful (unmasked) fwd+bwd TFLOP/s over the
+whole step, counting 14*D*Hq*nnz FLOP per step (4 forward + 10 backward, one score
+recompute).  ``roofline`` is for the kernel with the longest average duration,
+timed with HIP events on the stream it runs on.  ``cpu_baseline`` is the float64
+oracle on a bounded sample of the same tree, on this host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+METRIC = "packed-DAG attention useful TFLOP/s fwd+bwd @262K tok/tree; % MFMA peak"
+HQ, HKV, HD = 16, 4, 128
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tree_packed_block_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(kernel: str):
+    """HBM bytes per launch measured with rocprofv3 counters for ``kernel``, if the
+    committed record was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    k = rec.get("kernels", {}).get(kernel)
+    if not k or rec.get("source_digest") != source_digest():
+        return None
+    return k.get("fetch_bytes_per_launch", 0) + k.get("write_bytes_per_launch", 0)
+
+
+def cpu_baseline(dag, x, rows_per_part=768):
+    """The float64 oracle (as it stands) on a bounded sample: forward + backward of
+    the last rows of two workers and of the continuation (every row with its whole
+    context)."""
+    import numpy as np
+    from oracle import attention as A
+    from oracle import dag as D
+    br = dag.branches
+    parts = []
+    for b in (1, 2, dag.nb - 1):
+        start, L = int(br[b, 2]), int(br[b, 3])
+        parts.append((start + L - rows_per_part, start + L))
+    ctx = sum(int(D.mask_rows(br, dag.mounts, dag.T, lo, hi).sum()) for lo, hi in parts)
+    t0 = time.perf_counter()
+    A.attn_fwd(x["q"], x["k"], x["v"], br, dag.mounts, rows=parts)
+    A.attn_bwd(x["q"], x["k"], x["v"], x["do"], br, dag.mounts, rows=parts)
+    dt = time.perf_counter() - t0
+    flops = 14.0 * HD * HQ * ctx
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": A.n_workers(), "kind": "oracle",
+            "sample": f"fwd+bwd of {len(parts)}x{rows_per_part} query rows (last rows of "
+                      f"workers 1, 2 and the continuation; {ctx} visible pairs), "
+                      f"float64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--n-split", type=int, default=32, help="decode splits per cursor")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import tree_packed_block_amd as tpb
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ------------------------------------------------------------ workload (untimed)
+    t0 = time.perf_counter()
+    dag, rng = synth.build("episode262k")
+    probe = tpb.Plan(dag.branches, dag.mounts, dag.T)
+    st = probe.stats()
+    pos = probe.positions()
+    x = synth.draw_attention_inputs(rng, dag.T, HQ, HKV, HD, pos, dtype="bf16", std=0.5,
+                                    with_dout=True)
+    t = {k: torch.from_numpy(v).to(device=dev, dtype=torch.bfloat16) for k, v in x.items()}
+    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty((HQ, dag.T), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(tpb.bwd_workspace_bytes(probe, tpb.BF16, HQ, HKV, HD), dtype=torch.uint8,
+                     device=dev)
+    plan_bufs = [torch.empty(probe.device_bytes(), dtype=torch.uint8, device=dev)
+                 for _ in range(2)]
+
+    wl = synth.decode_workload()
+    xd = synth.draw_decode_inputs(np.random.default_rng(55), len(wl.cursors), HQ, HKV, HD,
+                                  wl.n_pages, wl.page_size)
+    qd = torch.from_numpy(xd["q"]).to(device=dev, dtype=torch.bfloat16)
+    kp = torch.from_numpy(xd["k_pool"]).to(device=dev, dtype=torch.bfloat16)
+    vp = torch.from_numpy(xd["v_pool"]).to(device=dev, dtype=torch.bfloat16)
+    seg0 = tpb.decode_segments(wl.dag.branches, wl.dag.mounts, wl.page_ptr, wl.pages,
+                               wl.page_size, wl.n_pages, wl.cursors)
+    n_seg = int(seg0[1].size)
+    B = len(wl.cursors)
+    seg_host = [[torch.empty(n, dtype=torch.int32, pin_memory=True)
+                 for n in (B + 1, n_seg, n_seg, n_seg)] for _ in range(2)]
+    seg_dev = [[torch.empty(n, dtype=torch.int32, device=dev) for n in (B + 1, n_seg, n_seg, n_seg)]
+               for _ in range(2)]
+    od = torch.empty_like(qd)
+    lsed = torch.empty((B, HQ), dtype=torch.float32, device=dev)
+    wsd = torch.empty(tpb.decode_workspace_bytes(B, HQ, HD, args.n_split), dtype=torch.uint8,
+                      device=dev)
+    # unique K/V bytes the decode batch must read (shared prefix and mounted pages once)
+    codes = np.concatenate([int(pg) * wl.page_size + np.arange(lo, hi)
+                            for pg, lo, hi in zip(seg0[1], seg0[2], seg0[3])])
+    n_unique = int(np.unique(codes).size)
+    dec_bytes = (n_unique * HKV * HD * 2 * 2 + qd.numel() * 2 * 2 + lsed.numel() * 4
+                 + (B + 1 + 3 * n_seg) * 4)
+    torch.cuda.synchronize()
+    log(f"setup {time.perf_counter() - t0:.1f} s: T={dag.T} nnz={st['nnz']} "
+        f"pairs={st['n_pairs']} decode segments={n_seg}")
+
+    stream = torch.cuda.current_stream(dev)
+    names = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "decode"]
+
+    def host_prep():
+        plan = tpb.Plan(dag.branches, dag.mounts, dag.T)
+        segs = tpb.decode_segments(wl.dag.branches, wl.dag.mounts, wl.page_ptr, wl.pages,
+                                   wl.page_size, wl.n_pages, wl.cursors)
+        return plan, segs
+
+    def enqueue(i, plan, segs, ev):
+        plan.upload(buffer=plan_bufs[i % 2], sync=False, stream=stream)
+        hs, ds = seg_host[i % 2], seg_dev[i % 2]
+        for h, d, a in zip(hs, ds, segs):
+            h.numpy()[:] = a
+            d.copy_(h, non_blocking=True)
+        ev[0].record(stream)
+        tpb.attn_fwd(plan, q, k, v, o=o, lse=lse)
+        ev[1].record(stream)
+        tpb.attn_bwd_phase("preprocess", plan, q, k, v, o, lse, do, ws)
+        ev[2].record(stream)
+        tpb.attn_bwd_phase("dkdv", plan, q, k, v, o, lse, do, ws, dk=dk, dv=dv)
+        ev[3].record(stream)
+        tpb.attn_bwd_phase("dq", plan, q, k, v, o, lse, do, ws, dq=dq)
+        ev[4].record(stream)
+        tpb.paged_mount_decode(qd, kp, vp, *ds, n_split=args.n_split, o=od, lse=lsed, ws=wsd)
+        ev[5].record(stream)
+
+    def run(n_steps):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_steps)]
+        keep = []
+        nxt = host_prep()
+        for i in range(n_steps):
+            if i >= 2:
+                evs[i - 2][5].synchronize()  # buffers of step i-2 are free again
+            plan, segs = nxt
+            keep.append(plan)
+            enqueue(i, plan, segs, evs[i])
+            if i + 1 < n_steps:
+                nxt = host_prep()  # overlaps the GPU work just enqueued
+        return evs, keep
+
+    for _ in range(max(args.warmup, 0)):
+        run(1)
+    torch.cuda.synchronize()
+
+    # plan time alone (host), for the record
+    tp = time.perf_counter()
+    host_prep()
+    plan_ms = (time.perf_counter() - tp) * 1e3
+
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    evs, keep = run(args.steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    del keep
+
+    per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
+           for j, n in enumerate(names)}
+    ms_per_step = wall * 1e3 / args.steps
+    nnz = st["nnz"]
+    useful = 14.0 * HD * HQ * nnz
+    value = useful / (ms_per_step * 1e-3) / 1e12
+    algo = {
+        "fwd": ("mfma", 4.0 * HD * HQ * nnz),
+        "bwd_dkdv": ("mfma", 8.0 * HD * HQ * nnz),
+        "bwd_dq": ("mfma", 2.0 * HD * HQ * nnz),
+        "bwd_preprocess": ("hbm", 2.0 * dag.T * HQ * HD * 2 + dag.T * HQ * 4),
+        "decode": ("hbm", float(dec_bytes)),
+    }
+    dom = max(per, key=per.get)
+    bound, amount = algo[dom]
+    if bound == "mfma":
+        achieved = amount / (per[dom] * 1e-3) / 1e12
+        peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved = amount / (per[dom] * 1e-3) / 1e9
+        peak, unit = PEAK_HBM_GBS, "GB/s"
+    roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic_record(dom),
+            "kernel": dom, "avg_ms": round(per[dom], 3)}
+
+    breakdown = {}
+    for n in names:
+        b, amt = algo[n]
+        rate = amt / (per[n] * 1e-3)
+        breakdown[n] = {"ms": round(per[n], 3),
+                        ("useful_TFLOP/s" if b == "mfma" else "GB/s"):
+                            round(rate / (1e12 if b == "mfma" else 1e9), 1),
+                        "frac_of_peak": round(rate / (PEAK_BF16_TFLOPS * 1e12 if b == "mfma"
+                                                      else PEAK_HBM_GBS * 1e9), 4)}
+    fb = per["fwd"] + per["bwd_preprocess"] + per["bwd_dkdv"] + per["bwd_dq"]
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "episode tree of 262,144 packed tokens (8,192-token orchestrator "
+                        "prefix, 8 workers 16K-32K water-filled, 4,096-token continuation "
+                        "mounting 3 worker tails), fwd+bwd; plus paged decode of 64 cursors",
+            "tokens_per_tree": dag.T, "q_heads": HQ, "kv_heads": HKV, "head_dim": HD,
+            "nnz": nnz, "tile_pairs": st["n_pairs"], "partial_tiles": st["n_partial"],
+            "decode_cursors": B, "decode_segments": n_seg, "decode_split": args.n_split,
+            "decode_unique_kv_tokens": n_unique, "decode_bytes": dec_bytes,
+        },
+        "roofline": roof,
+        "fwd_bwd_ms": round(fb, 3),
+        "fwd_bwd_useful_TFLOP/s": round(useful / (fb * 1e-3) / 1e12, 2),
+        "fwd_bwd_frac_mfma_peak": round(useful / (fb * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "decode_frac_hbm_peak": breakdown["decode"]["frac_of_peak"],
+        "plan_host_ms": round(plan_ms, 1),
+        "breakdown": breakdown,
+        "device": torch.cuda.get_device_name(dev),
+        "cu_count": torch.cuda.get_device_properties(dev).multi_processor_count,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (float64 oracle on a sample) ...")
+        out["cpu_baseline"] = cpu_baseline(dag, x)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -122,8 +122,10 @@ size_t octopus_plan_device_bytes(const octopus_plan* plan);
 
 /* Enqueue an asynchronous host-to-device copy of the plan into dev_buf
  * (caller-owned, >= octopus_plan_device_bytes, 256-byte aligned) on `stream`, and
- * remember dev_buf for the attention calls.  The plan's host memory must outlive
- * the copy (synchronise the stream before destroying the plan).
+ * remember dev_buf for the attention calls.  The first upload copies the plan into
+ * page-locked host memory owned by the plan (so the copy does not wait for earlier
+ * work on the stream); destroy the plan only after the stream has finished the copy
+ * and every attention call that uses it.
  * Errors: EINVAL (NULL or misaligned buffer), EWORKSPACE (too small), EHIP. */
 int octopus_plan_upload(octopus_plan* plan, void* dev_buf, size_t bytes, void* stream);
 
@@ -175,6 +177,25 @@ int octopus_dag_attn_bwd(const octopus_plan* plan, octopus_dtype dtype, int32_t 
                          const void* k, const void* v, const void* o, const float* lse,
                          const void* dout, void* dq, void* dk, void* dv, void* ws,
                          size_t ws_bytes, void* stream);
+
+/* The same backward as three launches, for callers that time or overlap them.  The
+ * workspace carries Delta from the preprocess to the other two, which are independent
+ * of each other (they may run on two streams once the preprocess has completed).
+ *   preprocess: Delta = rowsum(dO * O) into ws (float32 [Hq][T]);
+ *   dkdv:       dk, dv from q, k, v, lse, dout and Delta (atomics-free owner pass);
+ *   dq:         dq from q, k, v, lse, dout and Delta.
+ * Same support and errors as octopus_dag_attn_bwd. */
+int octopus_dag_attn_bwd_preprocess(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
+                                    int32_t Hkv, int32_t D, const void* o, const void* dout,
+                                    void* ws, size_t ws_bytes, void* stream);
+int octopus_dag_attn_bwd_dkdv(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
+                              int32_t Hkv, int32_t D, float scale, const void* q, const void* k,
+                              const void* v, const float* lse, const void* dout, void* dk,
+                              void* dv, const void* ws, size_t ws_bytes, void* stream);
+int octopus_dag_attn_bwd_dq(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
+                            int32_t Hkv, int32_t D, float scale, const void* q, const void* k,
+                            const void* v, const float* lse, const void* dout, void* dq,
+                            const void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- paged decode */
 

@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     OctopusError,
     Plan,
     attn_bwd,
+    attn_bwd_phase,
     attn_fwd,
     bwd_workspace_bytes,
     decode_segments,

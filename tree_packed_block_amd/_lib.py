@@ -27,7 +27,8 @@ EXPORTS = [
     "octopus_dag_plan", "octopus_plan_positions", "octopus_plan_stats_get",
     "octopus_plan_device_bytes", "octopus_plan_upload", "octopus_plan_export_mask",
     "octopus_plan_export_tiles", "octopus_plan_destroy", "octopus_fwd_workspace_bytes", "octopus_dag_attn_fwd",
-    "octopus_bwd_workspace_bytes", "octopus_dag_attn_bwd", "octopus_decode_segments",
+    "octopus_bwd_workspace_bytes", "octopus_dag_attn_bwd", "octopus_dag_attn_bwd_preprocess",
+    "octopus_dag_attn_bwd_dkdv", "octopus_dag_attn_bwd_dq", "octopus_decode_segments",
     "octopus_decode_workspace_bytes", "octopus_paged_mount_decode", "octopus_last_error",
     "octopus_version",
 ]
@@ -84,6 +85,15 @@ def lib():
     L.octopus_dag_attn_bwd.argtypes = [_vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_float, _vp, _vp, _vp, _vp, _vp,
                                        _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.octopus_dag_attn_bwd_preprocess.argtypes = [_vp, ctypes.c_int, ctypes.c_int32,
+                                                  ctypes.c_int32, ctypes.c_int32, _vp, _vp,
+                                                  _vp, ctypes.c_size_t, _vp]
+    L.octopus_dag_attn_bwd_dkdv.argtypes = [_vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_float, _vp, _vp, _vp, _vp,
+                                            _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.octopus_dag_attn_bwd_dq.argtypes = [_vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_float, _vp, _vp, _vp, _vp,
+                                          _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.octopus_decode_segments.argtypes = [_vp, ctypes.c_int32, _vp, ctypes.c_int32, _vp, _vp,
                                           ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int32,
                                           _vp, _vp, _vp, _vp, ctypes.c_int32, _i32p]
@@ -170,18 +180,20 @@ class Plan:
         n = st["n_pairs"]
         return qt_ptr, kv[:n], mk[:n], rows[:st["n_partial"]]
 
-    def upload(self, device="cuda", buffer=None):
+    def upload(self, device="cuda", buffer=None, sync=True, stream=None):
         """Copy the plan into ``buffer`` (a uint8 CUDA tensor, allocated here if
-        ``None``) on the current stream and wait for the copy, so the host plan can
-        be freed at any time afterwards."""
+        ``None``) on ``stream`` (default: the current stream).  With ``sync`` the call
+        waits for the copy; otherwise keep this object alive until the stream has
+        finished with it."""
         import torch
         n = self.device_bytes()
         if buffer is None:
             buffer = torch.empty(n, dtype=torch.uint8, device=device)
-        stream = torch.cuda.current_stream(buffer.device)
+        stream = stream or torch.cuda.current_stream(buffer.device)
         _check(lib().octopus_plan_upload(self._h, _vp(buffer.data_ptr()), buffer.numel(),
                                          _vp(stream.cuda_stream)))
-        stream.synchronize()
+        if sync:
+            stream.synchronize()
         self.dev = buffer
         return self
 
@@ -259,6 +271,35 @@ def attn_bwd(plan: Plan, q, k, v, o, lse, dout, scale=None, dq=None, dk=None, dv
                                       dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(),
                                       _vp(s.cuda_stream)))
     return dq, dk, dv
+
+
+def attn_bwd_phase(phase, plan: Plan, q, k, v, o, lse, dout, ws, dq=None, dk=None, dv=None,
+                   scale=None, stream=None):
+    """One backward phase: ``"preprocess"`` (Delta into ``ws``), ``"dkdv"`` or
+    ``"dq"``; the output tensors must be given."""
+    import torch
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    code = _dtype_code(q)
+    s = _vp((stream or torch.cuda.current_stream(q.device)).cuda_stream)
+    L = lib()
+    sc = float(scale or 0.0)
+    if phase == "preprocess":
+        rc = L.octopus_dag_attn_bwd_preprocess(plan.handle, code, Hq, Hkv, D, o.data_ptr(),
+                                               dout.data_ptr(), ws.data_ptr(), ws.numel(), s)
+    elif phase == "dkdv":
+        rc = L.octopus_dag_attn_bwd_dkdv(plan.handle, code, Hq, Hkv, D, sc, q.data_ptr(),
+                                         k.data_ptr(), v.data_ptr(), lse.data_ptr(),
+                                         dout.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                         ws.data_ptr(), ws.numel(), s)
+    elif phase == "dq":
+        rc = L.octopus_dag_attn_bwd_dq(plan.handle, code, Hq, Hkv, D, sc, q.data_ptr(),
+                                       k.data_ptr(), v.data_ptr(), lse.data_ptr(),
+                                       dout.data_ptr(), dq.data_ptr(), ws.data_ptr(),
+                                       ws.numel(), s)
+    else:
+        raise ValueError(phase)
+    _check(rc)
 
 
 # ----------------------------------------------------------------------------- decode

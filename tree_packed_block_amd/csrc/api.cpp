@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 #include <new>
 #include <string>
 #include <vector>
@@ -133,7 +134,16 @@ int octopus_plan_upload(octopus_plan* plan, void* dev_buf, size_t bytes, void* s
     if (!aligned(dev_buf, 256)) return fail(OCTOPUS_EINVAL, "plan buffer must be 256-byte aligned");
     if (bytes < plan->p.layout.total)
         return fail(OCTOPUS_EWORKSPACE, "plan buffer smaller than octopus_plan_device_bytes");
-    const hipError_t e = hipMemcpyAsync(dev_buf, plan->p.blob.data(), plan->p.layout.total,
+    // Stage through page-locked memory owned by the plan so the copy is truly
+    // asynchronous (no implicit wait for earlier work on the stream).
+    if (plan->p.pinned == nullptr) {
+        void* h = nullptr;
+        const hipError_t ea = hipHostMalloc(&h, plan->p.layout.total, hipHostMallocDefault);
+        if (ea != hipSuccess) return hip_fail(ea, "plan upload (page-locked staging)");
+        std::memcpy(h, plan->p.blob.data(), plan->p.layout.total);
+        plan->p.pinned = h;
+    }
+    const hipError_t e = hipMemcpyAsync(dev_buf, plan->p.pinned, plan->p.layout.total,
                                         hipMemcpyHostToDevice, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "plan upload");
     plan->p.dev = dev_buf;
@@ -163,7 +173,11 @@ int octopus_plan_export_tiles(const octopus_plan* plan, int32_t* qt_ptr_out,
     return ok();
 }
 
-void octopus_plan_destroy(octopus_plan* plan) { delete plan; }
+void octopus_plan_destroy(octopus_plan* plan) {
+    if (plan == nullptr) return;
+    if (plan->p.pinned != nullptr) (void)hipHostFree(plan->p.pinned);
+    delete plan;
+}
 
 size_t octopus_fwd_workspace_bytes(const octopus_plan*, octopus_dtype, int32_t, int32_t,
                                    int32_t) {
@@ -195,27 +209,82 @@ size_t octopus_bwd_workspace_bytes(const octopus_plan* plan, octopus_dtype, int3
     return (size_t)Hq * (size_t)plan->p.T * sizeof(float);
 }
 
+namespace {
+
+int check_bwd_ws(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq, int32_t Hkv,
+                 int32_t D, void* ws, size_t ws_bytes) {
+    const size_t need = octopus_bwd_workspace_bytes(plan, dtype, Hq, Hkv, D);
+    if (ws == nullptr || ws_bytes < need || !aligned(ws, 16))
+        return fail(OCTOPUS_EWORKSPACE, "backward workspace needs " + std::to_string(need) +
+                                            " bytes, 16-byte aligned");
+    return OCTOPUS_OK;
+}
+
+}  // namespace
+
+int octopus_dag_attn_bwd_preprocess(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
+                                    int32_t Hkv, int32_t D, const void* o, const void* dout,
+                                    void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_attn(plan, dtype, Hq, Hkv, D, {o, dout});
+    if (rc == OCTOPUS_OK) rc = check_bwd_ws(plan, dtype, Hq, Hkv, D, ws, ws_bytes);
+    if (rc != OCTOPUS_OK) return rc;
+    const hipError_t e = octo::launch_bwd_delta(dtype == OCTOPUS_BF16, dev_view(plan->p), Hq, D,
+                                                o, dout, static_cast<float*>(ws),
+                                                (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
+    return ok();
+}
+
+int octopus_dag_attn_bwd_dkdv(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
+                              int32_t Hkv, int32_t D, float scale, const void* q, const void* k,
+                              const void* v, const float* lse, const void* dout, void* dk,
+                              void* dv, const void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_attn(plan, dtype, Hq, Hkv, D, {q, k, v, lse, dout, dk, dv});
+    if (rc == OCTOPUS_OK)
+        rc = check_bwd_ws(plan, dtype, Hq, Hkv, D, const_cast<void*>(ws), ws_bytes);
+    if (rc != OCTOPUS_OK) return rc;
+    if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
+    const hipError_t e = octo::launch_bwd_dkdv(dtype == OCTOPUS_BF16, dev_view(plan->p), Hq, Hkv,
+                                               D, scale, q, k, v, lse, dout,
+                                               static_cast<const float*>(ws), dk, dv,
+                                               (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "backward dK/dV launch");
+    return ok();
+}
+
+int octopus_dag_attn_bwd_dq(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
+                            int32_t Hkv, int32_t D, float scale, const void* q, const void* k,
+                            const void* v, const float* lse, const void* dout, void* dq,
+                            const void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_attn(plan, dtype, Hq, Hkv, D, {q, k, v, lse, dout, dq});
+    if (rc == OCTOPUS_OK)
+        rc = check_bwd_ws(plan, dtype, Hq, Hkv, D, const_cast<void*>(ws), ws_bytes);
+    if (rc != OCTOPUS_OK) return rc;
+    if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
+    const hipError_t e = octo::launch_bwd_dq(dtype == OCTOPUS_BF16, dev_view(plan->p), Hq, Hkv, D,
+                                             scale, q, k, v, lse, dout,
+                                             static_cast<const float*>(ws), dq,
+                                             (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "backward dQ launch");
+    return ok();
+}
+
 int octopus_dag_attn_bwd(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
                          int32_t Hkv, int32_t D, float scale, const void* q, const void* k,
                          const void* v, const void* o, const float* lse, const void* dout,
                          void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
                          void* stream) {
     int rc = check_attn(plan, dtype, Hq, Hkv, D, {q, k, v, o, lse, dout, dq, dk, dv});
+    if (rc == OCTOPUS_OK) rc = check_bwd_ws(plan, dtype, Hq, Hkv, D, ws, ws_bytes);
     if (rc != OCTOPUS_OK) return rc;
-    const size_t need = octopus_bwd_workspace_bytes(plan, dtype, Hq, Hkv, D);
-    if (ws == nullptr || ws_bytes < need || !aligned(ws, 16))
-        return fail(OCTOPUS_EWORKSPACE, "backward workspace needs " + std::to_string(need) +
-                                            " bytes, 16-byte aligned");
-    if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
-    const octo::DevPlan dp = dev_view(plan->p);
-    float* delta = static_cast<float*>(ws);
-    hipError_t e = dtype == OCTOPUS_BF16
-                       ? octo::launch_bwd_bf16(dp, Hq, Hkv, D, scale, q, k, v, o, lse, dout,
-                                               dq, dk, dv, delta, (hipStream_t)stream)
-                       : octo::launch_bwd_fp32(dp, Hq, Hkv, D, scale, q, k, v, o, lse, dout,
-                                               dq, dk, dv, delta, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e, "backward launch");
-    return ok();
+    rc = octopus_dag_attn_bwd_preprocess(plan, dtype, Hq, Hkv, D, o, dout, ws, ws_bytes, stream);
+    if (rc == OCTOPUS_OK)
+        rc = octopus_dag_attn_bwd_dkdv(plan, dtype, Hq, Hkv, D, scale, q, k, v, lse, dout, dk, dv,
+                                       ws, ws_bytes, stream);
+    if (rc == OCTOPUS_OK)
+        rc = octopus_dag_attn_bwd_dq(plan, dtype, Hq, Hkv, D, scale, q, k, v, lse, dout, dq, ws,
+                                     ws_bytes, stream);
+    return rc;
 }
 
 int octopus_decode_segments(const octopus_branch* branches, int32_t n_branches,

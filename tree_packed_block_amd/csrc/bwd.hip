@@ -527,57 +527,78 @@ __global__ __launch_bounds__(64) void dkdv_fp32_kernel(DevPlan P, int Hq, int Hk
 
 // ------------------------------------------------------------------ launchers
 
-template <int D>
-static hipError_t bwd_bf16(const DevPlan& p, int Hq, int Hkv, float scale, const void* q,
-                           const void* k, const void* v, const void* o, const float* lse,
-                           const void* dout, void* dq, void* dk, void* dv, float* delta,
-                           hipStream_t s) {
+hipError_t launch_bwd_delta(bool bf16_, const DevPlan& p, int Hq, int D, const void* o,
+                            const void* dout, float* delta, hipStream_t s) {
     const long long pairs = (long long)p.T * Hq;
-    const int per_block = 256 / (D / 8);
-    hipLaunchKernelGGL(delta_bf16_kernel<D>, dim3((unsigned)((pairs + per_block - 1) / per_block)),
-                       dim3(256), 0, s, p.T, Hq, (const bf16*)o, (const bf16*)dout, delta);
-    const float sl2 = scale * kLog2e;
-    const int G = Hq / Hkv;
-    hipLaunchKernelGGL(dkdv_bf16_kernel<D>, dim3(xcd_grid((p.nKT + 3) / 4 * Hkv, 4)), dim3(256), 0,
-                       s, p, Hq, Hkv, scale, sl2, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, (const bf16*)dout, lse, delta, (bf16*)dk, (bf16*)dv);
-    hipLaunchKernelGGL(dq_bf16_kernel<D>, dim3(xcd_grid(p.nQT * Hkv, G)), dim3(256), 0, s, p, Hq,
-                       Hkv, scale, sl2, (const bf16*)q, (const bf16*)k, (const bf16*)v,
-                       (const bf16*)dout, lse, delta, (bf16*)dq);
+    if (bf16_) {
+        const int per_block = 256 / (D / 8);
+        const dim3 grid((unsigned)((pairs + per_block - 1) / per_block));
+        if (D == 128)
+            hipLaunchKernelGGL(delta_bf16_kernel<128>, grid, dim3(256), 0, s, p.T, Hq,
+                               (const bf16*)o, (const bf16*)dout, delta);
+        else
+            hipLaunchKernelGGL(delta_bf16_kernel<64>, grid, dim3(256), 0, s, p.T, Hq,
+                               (const bf16*)o, (const bf16*)dout, delta);
+    } else {
+        const dim3 grid((unsigned)((pairs + 255) / 256));
+        if (D == 128)
+            hipLaunchKernelGGL(delta_fp32_kernel<128>, grid, dim3(256), 0, s, p.T, Hq,
+                               (const float*)o, (const float*)dout, delta);
+        else
+            hipLaunchKernelGGL(delta_fp32_kernel<64>, grid, dim3(256), 0, s, p.T, Hq,
+                               (const float*)o, (const float*)dout, delta);
+    }
     return hipGetLastError();
 }
 
 template <int D>
-static hipError_t bwd_fp32(const DevPlan& p, int Hq, int Hkv, float scale, const void* q,
-                           const void* k, const void* v, const void* o, const float* lse,
-                           const void* dout, void* dq, void* dk, void* dv, float* delta,
+static void dkdv_launch(bool bf16_, const DevPlan& p, int Hq, int Hkv, float scale,
+                        const void* q, const void* k, const void* v, const float* lse,
+                        const void* dout, const float* delta, void* dk, void* dv, hipStream_t s) {
+    if (bf16_)
+        hipLaunchKernelGGL(dkdv_bf16_kernel<D>, dim3(xcd_grid((p.nKT + 3) / 4 * Hkv, 4)),
+                           dim3(256), 0, s, p, Hq, Hkv, scale, scale * kLog2e, (const bf16*)q,
+                           (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse, delta,
+                           (bf16*)dk, (bf16*)dv);
+    else
+        hipLaunchKernelGGL(dkdv_fp32_kernel<D>, dim3(p.nKT * Hkv), dim3(64), 0, s, p, Hq, Hkv,
+                           scale, (const float*)q, (const float*)k, (const float*)v,
+                           (const float*)dout, lse, delta, (float*)dk, (float*)dv);
+}
+
+hipError_t launch_bwd_dkdv(bool bf16_, const DevPlan& p, int Hq, int Hkv, int D, float scale,
+                           const void* q, const void* k, const void* v, const float* lse,
+                           const void* dout, const float* delta, void* dk, void* dv,
                            hipStream_t s) {
-    const long long pairs = (long long)p.T * Hq;
-    hipLaunchKernelGGL(delta_fp32_kernel<D>, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0,
-                       s, p.T, Hq, (const float*)o, (const float*)dout, delta);
-    hipLaunchKernelGGL(dkdv_fp32_kernel<D>, dim3(p.nKT * Hkv), dim3(64), 0, s, p, Hq, Hkv, scale,
-                       (const float*)q, (const float*)k, (const float*)v, (const float*)dout,
-                       lse, delta, (float*)dk, (float*)dv);
-    hipLaunchKernelGGL(dq_fp32_kernel<D>, dim3(p.nQT * Hq), dim3(kBq), 0, s, p, Hq, Hkv, scale,
-                       (const float*)q, (const float*)k, (const float*)v, (const float*)dout,
-                       lse, delta, (float*)dq);
+    if (D == 128)
+        dkdv_launch<128>(bf16_, p, Hq, Hkv, scale, q, k, v, lse, dout, delta, dk, dv, s);
+    else
+        dkdv_launch<64>(bf16_, p, Hq, Hkv, scale, q, k, v, lse, dout, delta, dk, dv, s);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_bf16(const DevPlan& p, int Hq, int Hkv, int D, float scale,
-                           const void* q, const void* k, const void* v, const void* o,
-                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                           float* delta, hipStream_t s) {
-    return D == 128 ? bwd_bf16<128>(p, Hq, Hkv, scale, q, k, v, o, lse, dout, dq, dk, dv, delta, s)
-                    : bwd_bf16<64>(p, Hq, Hkv, scale, q, k, v, o, lse, dout, dq, dk, dv, delta, s);
+template <int D>
+static void dq_launch(bool bf16_, const DevPlan& p, int Hq, int Hkv, float scale, const void* q,
+                      const void* k, const void* v, const float* lse, const void* dout,
+                      const float* delta, void* dq, hipStream_t s) {
+    if (bf16_)
+        hipLaunchKernelGGL(dq_bf16_kernel<D>, dim3(xcd_grid(p.nQT * Hkv, Hq / Hkv)), dim3(256), 0,
+                           s, p, Hq, Hkv, scale, scale * kLog2e, (const bf16*)q, (const bf16*)k,
+                           (const bf16*)v, (const bf16*)dout, lse, delta, (bf16*)dq);
+    else
+        hipLaunchKernelGGL(dq_fp32_kernel<D>, dim3(p.nQT * Hq), dim3(kBq), 0, s, p, Hq, Hkv,
+                           scale, (const float*)q, (const float*)k, (const float*)v,
+                           (const float*)dout, lse, delta, (float*)dq);
 }
 
-hipError_t launch_bwd_fp32(const DevPlan& p, int Hq, int Hkv, int D, float scale,
-                           const void* q, const void* k, const void* v, const void* o,
-                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                           float* delta, hipStream_t s) {
-    return D == 128 ? bwd_fp32<128>(p, Hq, Hkv, scale, q, k, v, o, lse, dout, dq, dk, dv, delta, s)
-                    : bwd_fp32<64>(p, Hq, Hkv, scale, q, k, v, o, lse, dout, dq, dk, dv, delta, s);
+hipError_t launch_bwd_dq(bool bf16_, const DevPlan& p, int Hq, int Hkv, int D, float scale,
+                         const void* q, const void* k, const void* v, const float* lse,
+                         const void* dout, const float* delta, void* dq, hipStream_t s) {
+    if (D == 128)
+        dq_launch<128>(bf16_, p, Hq, Hkv, scale, q, k, v, lse, dout, delta, dq, s);
+    else
+        dq_launch<64>(bf16_, p, Hq, Hkv, scale, q, k, v, lse, dout, delta, dq, s);
+    return hipGetLastError();
 }
 
 }  // namespace octo

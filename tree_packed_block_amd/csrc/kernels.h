@@ -29,14 +29,16 @@ hipError_t launch_fwd_bf16(const DevPlan& p, int Hq, int Hkv, int D, float scale
 hipError_t launch_fwd_fp32(const DevPlan& p, int Hq, int Hkv, int D, float scale,
                            const void* q, const void* k, const void* v, void* o, float* lse,
                            hipStream_t s);
-hipError_t launch_bwd_bf16(const DevPlan& p, int Hq, int Hkv, int D, float scale,
-                           const void* q, const void* k, const void* v, const void* o,
-                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                           float* delta, hipStream_t s);
-hipError_t launch_bwd_fp32(const DevPlan& p, int Hq, int Hkv, int D, float scale,
-                           const void* q, const void* k, const void* v, const void* o,
-                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                           float* delta, hipStream_t s);
+// Backward phases.  `bf16` selects the MFMA kernels, otherwise float32.
+hipError_t launch_bwd_delta(bool bf16, const DevPlan& p, int Hq, int D, const void* o,
+                            const void* dout, float* delta, hipStream_t s);
+hipError_t launch_bwd_dkdv(bool bf16, const DevPlan& p, int Hq, int Hkv, int D, float scale,
+                           const void* q, const void* k, const void* v, const float* lse,
+                           const void* dout, const float* delta, void* dk, void* dv,
+                           hipStream_t s);
+hipError_t launch_bwd_dq(bool bf16, const DevPlan& p, int Hq, int Hkv, int D, float scale,
+                         const void* q, const void* k, const void* v, const float* lse,
+                         const void* dout, const float* delta, void* dq, hipStream_t s);
 hipError_t launch_decode_bf16(int B, int Hq, int Hkv, int D, int page_size, float scale,
                               const void* q, const void* k_pool, const void* v_pool,
                               int n_pages, const int32_t* seg_ptr, const int32_t* seg_page,

@@ -73,6 +73,7 @@ struct Plan {
     DevLayout layout;
     std::vector<unsigned char> blob;  // host image of the device copy
     void* dev = nullptr;              // caller-owned device copy after upload
+    void* pinned = nullptr;           // page-locked copy of `blob` used by uploads
 };
 
 int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, int32_t nm,
