@@ -162,7 +162,8 @@ int octopus_dag_attn_fwd(const octopus_plan* plan, octopus_dtype dtype, int32_t 
                          const void* k, const void* v, void* o, float* lse, void* ws,
                          size_t ws_bytes, void* stream);
 
-/* Workspace bytes the backward needs: float32 [Hq][T] for Delta. */
+/* Workspace bytes the backward needs: float32 [2][Hq][Tp] (LSE * log2(e) and Delta),
+ * Tp = T rounded up to a multiple of 128. */
 size_t octopus_bwd_workspace_bytes(const octopus_plan* plan, octopus_dtype dtype,
                                    int32_t Hq, int32_t Hkv, int32_t D);
 
@@ -179,23 +180,24 @@ int octopus_dag_attn_bwd(const octopus_plan* plan, octopus_dtype dtype, int32_t 
                          size_t ws_bytes, void* stream);
 
 /* The same backward as three launches, for callers that time or overlap them.  The
- * workspace carries Delta from the preprocess to the other two, which are independent
- * of each other (they may run on two streams once the preprocess has completed).
- *   preprocess: Delta = rowsum(dO * O) into ws (float32 [Hq][T]);
- *   dkdv:       dk, dv from q, k, v, lse, dout and Delta (atomics-free owner pass);
- *   dq:         dq from q, k, v, lse, dout and Delta.
+ * workspace carries LSE and Delta from the preprocess to the other two, which are
+ * independent of each other (they may run on two streams once the preprocess has
+ * completed).
+ *   preprocess: Delta = rowsum(dO * O), and LSE * log2(e), into ws;
+ *   dkdv:       dk, dv from q, k, v, dout and ws (atomics-free owner pass);
+ *   dq:         dq from q, k, v, dout and ws.
  * Same support and errors as octopus_dag_attn_bwd. */
 int octopus_dag_attn_bwd_preprocess(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
-                                    int32_t Hkv, int32_t D, const void* o, const void* dout,
-                                    void* ws, size_t ws_bytes, void* stream);
+                                    int32_t Hkv, int32_t D, const void* o, const float* lse,
+                                    const void* dout, void* ws, size_t ws_bytes, void* stream);
 int octopus_dag_attn_bwd_dkdv(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
                               int32_t Hkv, int32_t D, float scale, const void* q, const void* k,
-                              const void* v, const float* lse, const void* dout, void* dk,
-                              void* dv, const void* ws, size_t ws_bytes, void* stream);
+                              const void* v, const void* dout, void* dk, void* dv,
+                              const void* ws, size_t ws_bytes, void* stream);
 int octopus_dag_attn_bwd_dq(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
                             int32_t Hkv, int32_t D, float scale, const void* q, const void* k,
-                            const void* v, const float* lse, const void* dout, void* dq,
-                            const void* ws, size_t ws_bytes, void* stream);
+                            const void* v, const void* dout, void* dq, const void* ws,
+                            size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- paged decode */
 

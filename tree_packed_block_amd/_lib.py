@@ -87,13 +87,13 @@ def lib():
                                        _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.octopus_dag_attn_bwd_preprocess.argtypes = [_vp, ctypes.c_int, ctypes.c_int32,
                                                   ctypes.c_int32, ctypes.c_int32, _vp, _vp,
-                                                  _vp, ctypes.c_size_t, _vp]
+                                                  _vp, _vp, ctypes.c_size_t, _vp]
     L.octopus_dag_attn_bwd_dkdv.argtypes = [_vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_float, _vp, _vp, _vp, _vp,
-                                            _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+                                            _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.octopus_dag_attn_bwd_dq.argtypes = [_vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_int32, ctypes.c_float, _vp, _vp, _vp, _vp,
-                                          _vp, _vp, _vp, ctypes.c_size_t, _vp]
+                                          _vp, _vp, ctypes.c_size_t, _vp]
     L.octopus_decode_segments.argtypes = [_vp, ctypes.c_int32, _vp, ctypes.c_int32, _vp, _vp,
                                           ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int32,
                                           _vp, _vp, _vp, _vp, ctypes.c_int32, _i32p]
@@ -286,17 +286,17 @@ def attn_bwd_phase(phase, plan: Plan, q, k, v, o, lse, dout, ws, dq=None, dk=Non
     sc = float(scale or 0.0)
     if phase == "preprocess":
         rc = L.octopus_dag_attn_bwd_preprocess(plan.handle, code, Hq, Hkv, D, o.data_ptr(),
-                                               dout.data_ptr(), ws.data_ptr(), ws.numel(), s)
+                                               lse.data_ptr(), dout.data_ptr(), ws.data_ptr(),
+                                               ws.numel(), s)
     elif phase == "dkdv":
         rc = L.octopus_dag_attn_bwd_dkdv(plan.handle, code, Hq, Hkv, D, sc, q.data_ptr(),
-                                         k.data_ptr(), v.data_ptr(), lse.data_ptr(),
-                                         dout.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                                         ws.data_ptr(), ws.numel(), s)
+                                         k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                                         dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
+                                         ws.numel(), s)
     elif phase == "dq":
         rc = L.octopus_dag_attn_bwd_dq(plan.handle, code, Hq, Hkv, D, sc, q.data_ptr(),
-                                       k.data_ptr(), v.data_ptr(), lse.data_ptr(),
-                                       dout.data_ptr(), dq.data_ptr(), ws.data_ptr(),
-                                       ws.numel(), s)
+                                       k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                                       dq.data_ptr(), ws.data_ptr(), ws.numel(), s)
     else:
         raise ValueError(phase)
     _check(rc)

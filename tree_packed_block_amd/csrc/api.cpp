@@ -52,6 +52,11 @@ octo::DevPlan dev_view(const octo::Plan& p) {
     d.k_pairs = reinterpret_cast<const int2*>(base + p.layout.k_pairs);
     d.mask_rows = reinterpret_cast<const uint64_t*>(base + p.layout.mask_rows);
     d.mask_cols = reinterpret_cast<const uint64_t*>(base + p.layout.mask_cols);
+    d.nKB = p.nKB;
+    d.pad = 0;
+    d.blk_order = reinterpret_cast<const int32_t*>(base + p.layout.blk_order);
+    d.blk_ptr = reinterpret_cast<const int32_t*>(base + p.layout.blk_ptr);
+    d.blk_entries = reinterpret_cast<const int4*>(base + p.layout.blk_entries);
     return d;
 }
 
@@ -169,7 +174,9 @@ int octopus_plan_export_tiles(const octopus_plan* plan, int32_t* qt_ptr_out,
         kv_tile_out[i] = p.q_pairs[i].tile;
         mask_out[i] = p.q_pairs[i].mask;
     }
-    if (rows_out) std::copy(p.mask_rows.begin(), p.mask_rows.end(), rows_out);
+    if (rows_out)
+        std::copy(p.mask_rows.begin(), p.mask_rows.begin() + p.n_partial * p.Bq * p.row_words,
+                  rows_out);
     return ok();
 }
 
@@ -206,7 +213,7 @@ int octopus_dag_attn_fwd(const octopus_plan* plan, octopus_dtype dtype, int32_t 
 size_t octopus_bwd_workspace_bytes(const octopus_plan* plan, octopus_dtype, int32_t Hq,
                                    int32_t, int32_t) {
     if (plan == nullptr || Hq < 1) return 0;
-    return (size_t)Hq * (size_t)plan->p.T * sizeof(float);
+    return octo::bwd_workspace_floats(plan->p.T, Hq) * sizeof(float);
 }
 
 namespace {
@@ -223,29 +230,29 @@ int check_bwd_ws(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq, int3
 }  // namespace
 
 int octopus_dag_attn_bwd_preprocess(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
-                                    int32_t Hkv, int32_t D, const void* o, const void* dout,
-                                    void* ws, size_t ws_bytes, void* stream) {
-    int rc = check_attn(plan, dtype, Hq, Hkv, D, {o, dout});
+                                    int32_t Hkv, int32_t D, const void* o, const float* lse,
+                                    const void* dout, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_attn(plan, dtype, Hq, Hkv, D, {o, lse, dout});
     if (rc == OCTOPUS_OK) rc = check_bwd_ws(plan, dtype, Hq, Hkv, D, ws, ws_bytes);
     if (rc != OCTOPUS_OK) return rc;
-    const hipError_t e = octo::launch_bwd_delta(dtype == OCTOPUS_BF16, dev_view(plan->p), Hq, D,
-                                                o, dout, static_cast<float*>(ws),
-                                                (hipStream_t)stream);
+    const hipError_t e =
+        octo::launch_bwd_preprocess(dtype == OCTOPUS_BF16, dev_view(plan->p), Hq, D, o, dout, lse,
+                                    static_cast<float*>(ws), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
     return ok();
 }
 
 int octopus_dag_attn_bwd_dkdv(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
                               int32_t Hkv, int32_t D, float scale, const void* q, const void* k,
-                              const void* v, const float* lse, const void* dout, void* dk,
-                              void* dv, const void* ws, size_t ws_bytes, void* stream) {
-    int rc = check_attn(plan, dtype, Hq, Hkv, D, {q, k, v, lse, dout, dk, dv});
+                              const void* v, const void* dout, void* dk, void* dv,
+                              const void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_attn(plan, dtype, Hq, Hkv, D, {q, k, v, dout, dk, dv});
     if (rc == OCTOPUS_OK)
         rc = check_bwd_ws(plan, dtype, Hq, Hkv, D, const_cast<void*>(ws), ws_bytes);
     if (rc != OCTOPUS_OK) return rc;
     if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
     const hipError_t e = octo::launch_bwd_dkdv(dtype == OCTOPUS_BF16, dev_view(plan->p), Hq, Hkv,
-                                               D, scale, q, k, v, lse, dout,
+                                               D, scale, q, k, v, dout,
                                                static_cast<const float*>(ws), dk, dv,
                                                (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "backward dK/dV launch");
@@ -254,17 +261,16 @@ int octopus_dag_attn_bwd_dkdv(const octopus_plan* plan, octopus_dtype dtype, int
 
 int octopus_dag_attn_bwd_dq(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
                             int32_t Hkv, int32_t D, float scale, const void* q, const void* k,
-                            const void* v, const float* lse, const void* dout, void* dq,
-                            const void* ws, size_t ws_bytes, void* stream) {
-    int rc = check_attn(plan, dtype, Hq, Hkv, D, {q, k, v, lse, dout, dq});
+                            const void* v, const void* dout, void* dq, const void* ws,
+                            size_t ws_bytes, void* stream) {
+    int rc = check_attn(plan, dtype, Hq, Hkv, D, {q, k, v, dout, dq});
     if (rc == OCTOPUS_OK)
         rc = check_bwd_ws(plan, dtype, Hq, Hkv, D, const_cast<void*>(ws), ws_bytes);
     if (rc != OCTOPUS_OK) return rc;
     if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
     const hipError_t e = octo::launch_bwd_dq(dtype == OCTOPUS_BF16, dev_view(plan->p), Hq, Hkv, D,
-                                             scale, q, k, v, lse, dout,
-                                             static_cast<const float*>(ws), dq,
-                                             (hipStream_t)stream);
+                                             scale, q, k, v, dout, static_cast<const float*>(ws),
+                                             dq, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "backward dQ launch");
     return ok();
 }
@@ -277,12 +283,13 @@ int octopus_dag_attn_bwd(const octopus_plan* plan, octopus_dtype dtype, int32_t 
     int rc = check_attn(plan, dtype, Hq, Hkv, D, {q, k, v, o, lse, dout, dq, dk, dv});
     if (rc == OCTOPUS_OK) rc = check_bwd_ws(plan, dtype, Hq, Hkv, D, ws, ws_bytes);
     if (rc != OCTOPUS_OK) return rc;
-    rc = octopus_dag_attn_bwd_preprocess(plan, dtype, Hq, Hkv, D, o, dout, ws, ws_bytes, stream);
+    rc = octopus_dag_attn_bwd_preprocess(plan, dtype, Hq, Hkv, D, o, lse, dout, ws, ws_bytes,
+                                         stream);
     if (rc == OCTOPUS_OK)
-        rc = octopus_dag_attn_bwd_dkdv(plan, dtype, Hq, Hkv, D, scale, q, k, v, lse, dout, dk, dv,
-                                       ws, ws_bytes, stream);
+        rc = octopus_dag_attn_bwd_dkdv(plan, dtype, Hq, Hkv, D, scale, q, k, v, dout, dk, dv, ws,
+                                       ws_bytes, stream);
     if (rc == OCTOPUS_OK)
-        rc = octopus_dag_attn_bwd_dq(plan, dtype, Hq, Hkv, D, scale, q, k, v, lse, dout, dq, ws,
+        rc = octopus_dag_attn_bwd_dq(plan, dtype, Hq, Hkv, D, scale, q, k, v, dout, dq, ws,
                                      ws_bytes, stream);
     return rc;
 }

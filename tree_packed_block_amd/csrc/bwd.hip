@@ -24,18 +24,28 @@
 
 namespace octo {
 
-// ------------------------------------------------------------------ Delta
+// ------------------------------------------------------------------ preprocess
+//
+// Workspace (float32): LSE2[Hq][Tp] = LSE * log2(e) and Delta[Hq][Tp], Tp = T rounded
+// up to a multiple of the 128-row query tile.  Rows >= T hold LSE2 = +inf and
+// Delta = 0, so a padded row gets P = 0 and dS = 0 with no per-row test, and every
+// 64-row run of a query tile is in bounds and 16-byte aligned.
+
+__host__ __device__ inline int padded_rows(int T) { return (T + kBq - 1) / kBq * kBq; }
 
 template <int D>
-__global__ __launch_bounds__(256) void delta_bf16_kernel(int T, int Hq, const bf16* __restrict__ O,
-                                                         const bf16* __restrict__ dO,
-                                                         float* __restrict__ Delta) {
+__global__ __launch_bounds__(256) void preprocess_bf16_kernel(int T, int Tp, int Hq,
+                                                              const bf16* __restrict__ O,
+                                                              const bf16* __restrict__ dO,
+                                                              const float* __restrict__ LSE,
+                                                              float* __restrict__ ws) {
     constexpr int L = D / 8;  // lanes per (row, head)
     const long long pair = ((long long)blockIdx.x * blockDim.x + threadIdx.x) / L;
     const int sub = threadIdx.x % L;
-    const bool valid = pair < (long long)T * Hq;
+    const bool valid = pair < (long long)Tp * Hq;
+    const int row = (int)(pair / Hq), h = (int)(pair % Hq);
     float acc = 0.f;
-    if (valid) {
+    if (valid && row < T) {
         const bf16x8 a = ld16(O + pair * D + 8 * sub);
         const bf16x8 b = ld16(dO + pair * D + 8 * sub);
 #pragma unroll
@@ -44,68 +54,79 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(int T, int Hq, const bf
 #pragma unroll
     for (int off = L / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, L);
     if (valid && sub == 0) {
-        const int row = (int)(pair / Hq), h = (int)(pair % Hq);
-        Delta[(size_t)h * T + row] = acc;
+        ws[(size_t)h * Tp + row] = row < T ? LSE[(size_t)h * T + row] * kLog2e : INFINITY;
+        ws[(size_t)Hq * Tp + (size_t)h * Tp + row] = acc;
     }
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void delta_fp32_kernel(int T, int Hq, const float* __restrict__ O,
-                                                         const float* __restrict__ dO,
-                                                         float* __restrict__ Delta) {
+__global__ __launch_bounds__(256) void preprocess_fp32_kernel(int T, int Tp, int Hq,
+                                                              const float* __restrict__ O,
+                                                              const float* __restrict__ dO,
+                                                              const float* __restrict__ LSE,
+                                                              float* __restrict__ ws) {
     const long long pair = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (pair >= (long long)T * Hq) return;
-    float acc = 0.f;
-    for (int d = 0; d < D; ++d) acc = fmaf(O[pair * D + d], dO[pair * D + d], acc);
+    if (pair >= (long long)Tp * Hq) return;
     const int row = (int)(pair / Hq), h = (int)(pair % Hq);
-    Delta[(size_t)h * T + row] = acc;
+    float acc = 0.f;
+    if (row < T)
+        for (int d = 0; d < D; ++d) acc = fmaf(O[pair * D + d], dO[pair * D + d], acc);
+    ws[(size_t)h * Tp + row] = row < T ? LSE[(size_t)h * T + row] * kLog2e : INFINITY;
+    ws[(size_t)Hq * Tp + (size_t)h * Tp + row] = acc;
 }
 
 // ------------------------------------------------------------------ dK / dV (bf16)
 //
-// Workgroup = (KV tile, KV head), 4 wave64s: wave w owns keys 32*(w&1) .. +32 of the
-// tile and, for each 64-row chunk of a query tile, query rows 32*(w>>1) .. +32 of
-// the chunk.  S = Q K^T is computed with K as the register-resident B operand so a
-// lane holds one key column: P and dS then serve directly as B operands of
-// dV^T += dO^T P and dK^T += Q^T dS, with Q and dO staged in LDS both row-major (A
-// of S and dP) and transposed (A of dV^T and dK^T).  The two waves sharing a key
-// half add their partial sums through LDS at the end.
+// Workgroup = (128-key block = KV tiles 2b and 2b+1, KV head), 4 wave64s; wave w owns
+// keys 32w .. 32w+31 of the block (tile 2b for w < 2).  The workgroup walks the
+// block's merged list of query tiles; for every entry, every query head of the group
+// and each 64-row half of the query tile, the Q and dO rows (and their LSE2/Delta) are
+// copied global -> LDS asynchronously (three stages in flight) and all four waves
+// consume them: S = Q K^T and dP = dO V^T with K and V register-resident B operands, so
+// a lane owns one key column; P and dS then serve directly as B operands of
+// dV^T += dO^T P and dK^T += Q^T dS, whose A operands are read transposed straight
+// from the row-major Q and dO tiles (ds_read_b64_tr_b16).  Every dK/dV row has one
+// writer; there are no atomics and no cross-wave reduction.
 
 template <int D>
-struct DkdvSmem {
-    static constexpr int RST = D + 8, TST = 64 + 8;
-    bf16 Qs[64 * RST];
-    bf16 dOs[64 * RST];
-    bf16 Qt[D * TST];
-    bf16 dOt[D * TST];
-    float Ls[64];
-    float Ds[64];
+struct DkdvCfg {
+    static constexpr int ROWB = D * 2;                   // bytes per row
+    static constexpr int MAT = 64 * ROWB;                // one 64-row Q or dO chunk
+    static constexpr int NDMA = MAT / (16 * 256);        // copies per thread per matrix
+    static constexpr int LSE_OFF = 2 * MAT;              // LSE2[64], then Delta[64]
+    static constexpr int MASK_OFF = LSE_OFF + 512;       // per wave: 32 keys x 2 words
+    static constexpr int STAGE = MASK_OFF + 4 * 512;
+    static constexpr int NST = 3;                        // stages in flight
+    static constexpr int PER_STAGE = 2 * NDMA + 2;       // copies per wave per stage
 };
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
     DevPlan P, int Hq, int Hkv, float scale, float scale_log2, const bf16* __restrict__ Q,
     const bf16* __restrict__ K, const bf16* __restrict__ V, const bf16* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ Delta, bf16* __restrict__ dK,
-    bf16* __restrict__ dV) {
-    constexpr int KS = D / 16, DB = D / 32, C8 = D / 8, NLOAD = 16 * C8;
-    constexpr int RST = DkdvSmem<D>::RST, TST = DkdvSmem<D>::TST;
-    constexpr int M = 4;  // consecutive KV tiles of one KV head placed on one XCD
-    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[sizeof(DkdvSmem<D>)];
-    DkdvSmem<D>& S = *reinterpret_cast<DkdvSmem<D>*>(smem_raw);
+    const float* __restrict__ ws, bf16* __restrict__ dK, bf16* __restrict__ dV) {
+    using C = DkdvCfg<D>;
+    constexpr int KS = D / 16, DB = D / 32, CPR = D / 8;
+    constexpr int M = 4;  // consecutive blocks of one KV head dealt to one XCD
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[C::NST * C::STAGE];
 
     int grp, mm;
-    if (!xcd_group(blockIdx.x, M, (P.nKT + M - 1) / M * Hkv, grp, mm)) return;
+    if (!xcd_group(blockIdx.x, M, (P.nKB + M - 1) / M * Hkv, grp, mm)) return;
     const int rank = (grp / Hkv) * M + mm;
-    if (rank >= P.nKT) return;
+    if (rank >= P.nKB) return;
     const int kvh = grp % Hkv;
-    const int kt = P.bwd_order[rank];
+    const int kb = ld_const(P.blk_order + rank);
 
-    const int T = P.T, G = Hq / Hkv;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int n = lane & 31, g = lane >> 5, kh = w & 1, qh = w >> 1;
-    const int key = kt * kBk + 32 * kh + n;
+    const int T = P.T, G = Hq / Hkv, Tp = padded_rows(T);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int n = lane & 31, g = lane >> 5;
+    const int key = kb * 128 + 32 * w + n;
+    const bool hi_tile = w >= 2;
     const size_t qstride = (size_t)Hq * D, kvstride = (size_t)Hkv * D;
+    const float* LSE2 = ws;
+    const float* DEL = ws + (size_t)Hq * Tp;
+    const unsigned smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
     bf16x8 kf[KS], vf[KS];
 #pragma unroll
@@ -114,6 +135,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
         kf[ks] = key < T ? ld16(K + off) : zero8();
         vf[ks] = key < T ? ld16(V + off) : zero8();
     }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        settle(kf[ks]);
+        settle(vf[ks]);
+    }
     f32x16 dk[DB], dv[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -121,119 +147,114 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
         dv[db] = zero16();
     }
 
-    const int p0 = P.kt_ptr[kt], p1 = P.kt_ptr[kt + 1];
-    const int n_it = (p1 - p0) * G * 2;  // (query tile, head, 64-row chunk)
+    const int e0 = ld_const(P.blk_ptr + kb), e1 = ld_const(P.blk_ptr + kb + 1);
+    const int n_it = (e1 - e0) * G * 2;  // (entry, head, 64-row half)
 
-    const bool loader = tid < NLOAD;
-    const int c8 = tid % C8, rg = tid / C8;
-    bf16x8 qr[4], dr[4];
-    float lr = 0.f;
-    auto gload = [&](int it) {
-        const int pi = p0 + it / (2 * G);
+    // Issue the asynchronous copies of iteration `it` into stage buffer `st`: the 64
+    // rows of Q and dO, their LSE2 and Delta, and this wave's 32 key-major mask words
+    // (the all-ones mask when the tile is FULL or not seen).
+    auto issue = [&](int it, int st) {
+        const int e = e0 + it / (2 * G);
         const int hh = (it >> 1) % G, c = it & 1;
         const int h = kvh * G + hh;
-        const int row0 = P.k_pairs[pi].x * kBq + c * 64;
+        const int4 ent = ld_const(P.blk_entries + e);
+        const int row0 = ent.x * kBq + c * 64;
+        const unsigned base = smem_base + st * C::STAGE;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = row0 + 4 * rg + j;
-            if (loader && r < T) {
-                const size_t off = (size_t)r * qstride + (size_t)h * D + 8 * c8;
-                qr[j] = ld16(Q + off);
-                dr[j] = ld16(dO + off);
-            } else {
-                qr[j] = zero8();
-                dr[j] = zero8();
-            }
+        for (int i = 0; i < C::NDMA; ++i) {
+            const int L = i * 256 + tid;
+            const int rho = L / CPR, slot = L % CPR;
+            const int chunk = swz<D>(rho, slot);  // the XOR swizzle is its own inverse
+            const int r = min(row0 + rho, T - 1);
+            const size_t off = (size_t)r * qstride + (size_t)h * D + 8 * chunk;
+            dma16(Q + off, base + (i * 256 + w * 64) * 16);
+            dma16(dO + off, base + C::MAT + (i * 256 + w * 64) * 16);
         }
-        if (tid < 64) {
-            const int r = row0 + tid;
-            lr = r < T ? LSE[(size_t)h * T + r] * kLog2e : INFINITY;
-        } else if (tid < 128) {
-            const int r = row0 + tid - 64;
-            lr = r < T ? Delta[(size_t)h * T + r] : 0.f;
+        if (lane < 8) {  // 32 pieces of 16 bytes, 8 per wave
+            const int u = 8 * w + lane;
+            const float* src = (u < 16 ? LSE2 : DEL) + (size_t)h * Tp + row0 + 4 * (u & 15);
+            dma16(src, base + C::LSE_OFF + 8 * w * 16);
         }
-    };
-    auto lds_put = [&]() {
-        if (loader) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                st16(&S.Qs[(4 * rg + j) * RST + 8 * c8], qr[j]);
-                st16(&S.dOs[(4 * rg + j) * RST + 8 * c8], dr[j]);
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                bf16x4 a, b;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    a[j] = qr[j][e];
-                    b[j] = dr[j][e];
-                }
-                st8(&S.Qt[(8 * c8 + e) * TST + 4 * rg], a);
-                st8(&S.dOt[(8 * c8 + e) * TST + 4 * rg], b);
-            }
+        if (lane < 32) {
+            int m = hi_tile ? ent.z : ent.y;
+            if (m < 0) m = P.n_partial;
+            dma16(P.mask_cols + ((size_t)m * kBk + 32 * (w & 1) + lane) * 2,
+                  base + C::MASK_OFF + w * 512);
         }
-        if (tid < 64) S.Ls[tid] = lr;
-        else if (tid < 128) S.Ds[tid - 64] = lr;
     };
 
-    if (n_it > 0) gload(0);
+    if (n_it > 0) issue(0, 0);
+    if (n_it > 1) issue(1, 1);
     for (int it = 0; it < n_it; ++it) {
-        const int pi = p0 + it / (2 * G);
-        const int c = it & 1;
-        const int mask = P.k_pairs[pi].y;
-        __syncthreads();
-        lds_put();
-        __syncthreads();
-        if (it + 1 < n_it) gload(it + 1);
+        if (it + 1 < n_it) wait_vmem<C::PER_STAGE>();
+        else wait_vmem<0>();
+        barrier();
+        if (it + 2 < n_it) issue(it + 2, (it + 2) % C::NST);
+        const int4 ent = ld_const(P.blk_entries + e0 + it / (2 * G));
+        if ((hi_tile ? ent.z : ent.y) == -2) continue;  // tile not seen by this query tile
 
-        // S and dP for 32 query rows x this wave's 32 keys.
-        f32x16 s = zero16(), dp = zero16();
+        const int c = it & 1;
+        const unsigned char* base = smem + (it % C::NST) * C::STAGE;
+        const unsigned char* Qs = base;
+        const unsigned char* Ds = base + C::MAT;
+        const float* Ls = reinterpret_cast<const float*>(base + C::LSE_OFF);
+        const float* Dl = Ls + 64;
+        const uint64_t bits =
+            *reinterpret_cast<const uint64_t*>(base + C::MASK_OFF + w * 512 + n * 16 + 8 * c);
+
+        f32x16 s[2], dp[2];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 aq = ld16(&S.Qs[(32 * qh + n) * RST + 16 * ks + 8 * g]);
-            const bf16x8 ad = ld16(&S.dOs[(32 * qh + n) * RST + 16 * ks + 8 * g]);
-            s = mfma_32x32x16(aq, kf[ks], s);
-            dp = mfma_32x32x16(ad, vf[ks], dp);
+        for (int qb = 0; qb < 2; ++qb) {
+            s[qb] = zero16();
+            dp[qb] = zero16();
+            const int row = 32 * qb + n;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int off = tile_off<D>(row, 2 * ks + g);
+                s[qb] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(Qs + off), kf[ks], s[qb]);
+                dp[qb] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(Ds + off), vf[ks], dp[qb]);
+            }
         }
-        uint64_t bits = ~0ull;
-        if (mask >= 0) bits = P.mask_cols[((size_t)mask * kBk + 32 * kh + n) * 2 + c];
-        bf16x8 pb[2], sb[2];
+        bf16x8 pb[4], sb[4];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int qrow = 32 * qh + 8 * (j >> 2) + 4 * g + (j & 3);  // row in the chunk
-            float p = fast_exp2(s[j] * scale_log2 - S.Ls[qrow]);
-            if (!((bits >> qrow) & 1ull)) p = 0.f;
-            const float ds = p * (dp[j] - S.Ds[qrow]);
-            pb[j >> 3][j & 7] = (bf16)p;
-            sb[j >> 3][j & 7] = (bf16)ds;
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS over 2 k-steps of 16 query rows.
+        for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int r4 = 32 * qb + 8 * q4 + 4 * g;  // rows r4 .. r4+3 of the chunk
+                const float4 l4 = *reinterpret_cast<const float4*>(Ls + r4);
+                const float4 d4 = *reinterpret_cast<const float4*>(Dl + r4);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+                const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const int j = 4 * q4 + e2;
+                    float pv = fast_exp2(s[qb][j] * scale_log2 - lv[e2]);
+                    if (!((bits >> (r4 + e2)) & 1ull)) pv = 0.f;
+                    pb[2 * qb + (j >> 3)][j & 7] = (bf16)pv;
+                    sb[2 * qb + (j >> 3)][j & 7] = (bf16)(pv * (dp[qb][j] - dl[e2]));
+                }
+            }
+        // dV^T += dO^T P and dK^T += Q^T dS over 4 k-steps of 16 rows.  The lane's 8
+        // rows in k-step qs are 16qs + 4g + {0..3} and 16qs + 8 + 4g + {0..3}.
+        const int r_in = lane & 15;
+        const int dh = (lane >> 4) & 1;
+#pragma unroll
+        for (int qs = 0; qs < 4; ++qs) {
+            const int rowa = 16 * qs + 4 * g + (r_in >> 2);
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const int off = (db * 32 + n) * TST + 32 * qh + 16 * st + 4 * g;
-                const bf16x8 ao = cat(ld8(&S.dOt[off]), ld8(&S.dOt[off + 8]));
-                const bf16x8 aq = cat(ld8(&S.Qt[off]), ld8(&S.Qt[off + 8]));
-                dv[db] = mfma_32x32x16(ao, pb[st], dv[db]);
-                dk[db] = mfma_32x32x16(aq, sb[st], dk[db]);
+                const int col = db * 32 + 16 * dh + 4 * (r_in & 3);
+                const int oa = tile_off<D>(rowa, col >> 3) + (col & 7) * 2;
+                const int ob = tile_off<D>(rowa + 8, col >> 3) + (col & 7) * 2;
+                const bf16x8 ado = cat(ld8_tr(Ds + oa), ld8_tr(Ds + ob));
+                const bf16x8 aq = cat(ld8_tr(Qs + oa), ld8_tr(Qs + ob));
+                dv[db] = mfma_32x32x16(ado, pb[qs], dv[db]);
+                dk[db] = mfma_32x32x16(aq, sb[qs], dk[db]);
             }
+        }
     }
 
-    // Sum the two query halves: waves with qh = 1 hand their partials to qh = 0.
-    __syncthreads();
-    float* red = reinterpret_cast<float*>(smem_raw);  // [kh][2][DB*16][64]
-    if (qh == 1) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                red[((kh * 2 + 0) * DB * 16 + db * 16 + j) * 64 + lane] = dk[db][j];
-                red[((kh * 2 + 1) * DB * 16 + db * 16 + j) * 64 + lane] = dv[db][j];
-            }
-    }
-    __syncthreads();
-    if (qh == 0 && key < T) {
+    if (key < T) {
         bf16* krow = dK + (size_t)key * kvstride + (size_t)kvh * D;
         bf16* vrow = dV + (size_t)key * kvstride + (size_t)kvh * D;
 #pragma unroll
@@ -242,10 +263,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
             for (int q4 = 0; q4 < 4; ++q4) {
                 bf16x4 a, b;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = 4 * q4 + e;
-                    a[e] = (bf16)(scale * (dk[db][j] + red[((kh * 2 + 0) * DB * 16 + db * 16 + j) * 64 + lane]));
-                    b[e] = (bf16)(dv[db][j] + red[((kh * 2 + 1) * DB * 16 + db * 16 + j) * 64 + lane]);
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    a[e2] = (bf16)(scale * dk[db][4 * q4 + e2]);
+                    b[e2] = (bf16)dv[db][4 * q4 + e2];
                 }
                 st8(krow + db * 32 + 8 * q4 + 4 * g, a);
                 st8(vrow + db * 32 + 8 * q4 + 4 * g, b);
@@ -271,7 +291,7 @@ template <int D>
 __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(
     DevPlan P, int Hq, int Hkv, float scale, float scale_log2, const bf16* __restrict__ Q,
     const bf16* __restrict__ K, const bf16* __restrict__ V, const bf16* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ Delta, bf16* __restrict__ dQ) {
+    const float* __restrict__ ws, bf16* __restrict__ dQ) {
     constexpr int KS = D / 16, DB = D / 32, C8 = D / 8, NLOAD = 16 * C8;
     constexpr int RST = DqSmem<D>::RST, TST = DqSmem<D>::TST;
     __shared__ __attribute__((aligned(16))) unsigned char smem_raw[sizeof(DqSmem<D>)];
@@ -298,8 +318,9 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(
         qf[ks] = row < T ? ld16(Q + off) : zero8();
         df[ks] = row < T ? ld16(dO + off) : zero8();
     }
-    const float lse2 = row < T ? LSE[(size_t)h * T + row] * kLog2e : INFINITY;
-    const float dlt = row < T ? Delta[(size_t)h * T + row] : 0.f;
+    const int Tp = padded_rows(T);
+    const float lse2 = ws[(size_t)h * Tp + row];
+    const float dlt = ws[(size_t)Hq * Tp + (size_t)h * Tp + row];
     f32x16 dq[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) dq[db] = zero16();
@@ -401,8 +422,7 @@ __global__ __launch_bounds__(128) void dq_fp32_kernel(DevPlan P, int Hq, int Hkv
                                                       const float* __restrict__ K,
                                                       const float* __restrict__ V,
                                                       const float* __restrict__ dO,
-                                                      const float* __restrict__ LSE,
-                                                      const float* __restrict__ Delta,
+                                                      const float* __restrict__ ws,
                                                       float* __restrict__ dQ) {
     constexpr int HALF = 32;
     __shared__ float Ksh[HALF][D];
@@ -420,8 +440,10 @@ __global__ __launch_bounds__(128) void dq_fp32_kernel(DevPlan P, int Hq, int Hkv
         d[x] = row < T ? dO[row * qstride + (size_t)h * D + x] : 0.f;
         acc[x] = 0.f;
     }
-    const float lse = row < T ? LSE[(size_t)h * T + row] : INFINITY;
-    const float dlt = row < T ? Delta[(size_t)h * T + row] : 0.f;
+    const int Tp = padded_rows(T);
+    const float lse2 = ws[(size_t)h * Tp + row];
+    const float dlt = ws[(size_t)Hq * Tp + (size_t)h * Tp + row];
+    const float sl2 = scale * kLog2e;
     for (int pi = P.qt_ptr[qt]; pi < P.qt_ptr[qt + 1]; ++pi) {
         const int2 pr = P.q_pairs[pi];
         const uint64_t bits = pr.y >= 0 ? P.mask_rows[(size_t)pr.y * kBq + rr] : ~0ull;
@@ -441,7 +463,7 @@ __global__ __launch_bounds__(128) void dq_fp32_kernel(DevPlan P, int Hq, int Hkv
                     sc = fmaf(q[x], Ksh[kk][x], sc);
                     dp = fmaf(d[x], Vsh[kk][x], dp);
                 }
-                const float p = expf(sc * scale - lse);
+                const float p = exp2f(sc * sl2 - lse2);
                 const float ds = p * (dp - dlt);
                 for (int x = 0; x < D; ++x) acc[x] = fmaf(ds, Ksh[kk][x], acc[x]);
             }
@@ -457,8 +479,7 @@ __global__ __launch_bounds__(64) void dkdv_fp32_kernel(DevPlan P, int Hq, int Hk
                                                        const float* __restrict__ K,
                                                        const float* __restrict__ V,
                                                        const float* __restrict__ dO,
-                                                       const float* __restrict__ LSE,
-                                                       const float* __restrict__ Delta,
+                                                       const float* __restrict__ ws,
                                                        float* __restrict__ dK,
                                                        float* __restrict__ dV) {
     constexpr int CH = 32;
@@ -468,7 +489,8 @@ __global__ __launch_bounds__(64) void dkdv_fp32_kernel(DevPlan P, int Hq, int Hk
     const int kt = P.bwd_order[blockIdx.x / Hkv];
     const int kvh = blockIdx.x % Hkv;
     const int G = Hq / Hkv;
-    const int T = P.T;
+    const int T = P.T, Tp = padded_rows(T);
+    const float sl2 = scale * kLog2e;
     const int kk = threadIdx.x;
     const int key = kt * kBk + kk;
     const size_t qstride = (size_t)Hq * D, kvstride = (size_t)Hkv * D;
@@ -494,8 +516,8 @@ __global__ __launch_bounds__(64) void dkdv_fp32_kernel(DevPlan P, int Hq, int Hk
                 }
                 if (threadIdx.x < CH) {
                     const int row = row0 + threadIdx.x;
-                    Lsh[threadIdx.x] = row < T ? LSE[(size_t)h * T + row] : INFINITY;
-                    Tsh[threadIdx.x] = row < T ? Delta[(size_t)h * T + row] : 0.f;
+                    Lsh[threadIdx.x] = ws[(size_t)h * Tp + row];
+                    Tsh[threadIdx.x] = ws[(size_t)Hq * Tp + (size_t)h * Tp + row];
                 }
                 __syncthreads();
                 const uint64_t bits =
@@ -508,7 +530,7 @@ __global__ __launch_bounds__(64) void dkdv_fp32_kernel(DevPlan P, int Hq, int Hk
                         sc = fmaf(Qsh[r][x], k[x], sc);
                         dp = fmaf(Dsh[r][x], v[x], dp);
                     }
-                    const float p = expf(sc * scale - Lsh[r]);
+                    const float p = exp2f(sc * sl2 - Lsh[r]);
                     const float ds = p * (dp - Tsh[r]);
                     for (int x = 0; x < D; ++x) {
                         dv[x] = fmaf(p, Dsh[r][x], dv[x]);
@@ -527,77 +549,75 @@ __global__ __launch_bounds__(64) void dkdv_fp32_kernel(DevPlan P, int Hq, int Hk
 
 // ------------------------------------------------------------------ launchers
 
-hipError_t launch_bwd_delta(bool bf16_, const DevPlan& p, int Hq, int D, const void* o,
-                            const void* dout, float* delta, hipStream_t s) {
-    const long long pairs = (long long)p.T * Hq;
+size_t bwd_workspace_floats(int T, int Hq) { return (size_t)2 * Hq * padded_rows(T); }
+
+hipError_t launch_bwd_preprocess(bool bf16_, const DevPlan& p, int Hq, int D, const void* o,
+                                 const void* dout, const float* lse, float* ws, hipStream_t s) {
+    const int Tp = padded_rows(p.T);
+    const long long pairs = (long long)Tp * Hq;
     if (bf16_) {
         const int per_block = 256 / (D / 8);
         const dim3 grid((unsigned)((pairs + per_block - 1) / per_block));
         if (D == 128)
-            hipLaunchKernelGGL(delta_bf16_kernel<128>, grid, dim3(256), 0, s, p.T, Hq,
-                               (const bf16*)o, (const bf16*)dout, delta);
+            hipLaunchKernelGGL(preprocess_bf16_kernel<128>, grid, dim3(256), 0, s, p.T, Tp, Hq,
+                               (const bf16*)o, (const bf16*)dout, lse, ws);
         else
-            hipLaunchKernelGGL(delta_bf16_kernel<64>, grid, dim3(256), 0, s, p.T, Hq,
-                               (const bf16*)o, (const bf16*)dout, delta);
+            hipLaunchKernelGGL(preprocess_bf16_kernel<64>, grid, dim3(256), 0, s, p.T, Tp, Hq,
+                               (const bf16*)o, (const bf16*)dout, lse, ws);
     } else {
         const dim3 grid((unsigned)((pairs + 255) / 256));
         if (D == 128)
-            hipLaunchKernelGGL(delta_fp32_kernel<128>, grid, dim3(256), 0, s, p.T, Hq,
-                               (const float*)o, (const float*)dout, delta);
+            hipLaunchKernelGGL(preprocess_fp32_kernel<128>, grid, dim3(256), 0, s, p.T, Tp, Hq,
+                               (const float*)o, (const float*)dout, lse, ws);
         else
-            hipLaunchKernelGGL(delta_fp32_kernel<64>, grid, dim3(256), 0, s, p.T, Hq,
-                               (const float*)o, (const float*)dout, delta);
+            hipLaunchKernelGGL(preprocess_fp32_kernel<64>, grid, dim3(256), 0, s, p.T, Tp, Hq,
+                               (const float*)o, (const float*)dout, lse, ws);
     }
     return hipGetLastError();
 }
 
 template <int D>
 static void dkdv_launch(bool bf16_, const DevPlan& p, int Hq, int Hkv, float scale,
-                        const void* q, const void* k, const void* v, const float* lse,
-                        const void* dout, const float* delta, void* dk, void* dv, hipStream_t s) {
+                        const void* q, const void* k, const void* v, const void* dout,
+                        const float* ws, void* dk, void* dv, hipStream_t s) {
     if (bf16_)
-        hipLaunchKernelGGL(dkdv_bf16_kernel<D>, dim3(xcd_grid((p.nKT + 3) / 4 * Hkv, 4)),
+        hipLaunchKernelGGL(dkdv_bf16_kernel<D>, dim3(xcd_grid((p.nKB + 3) / 4 * Hkv, 4)),
                            dim3(256), 0, s, p, Hq, Hkv, scale, scale * kLog2e, (const bf16*)q,
-                           (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse, delta,
-                           (bf16*)dk, (bf16*)dv);
+                           (const bf16*)k, (const bf16*)v, (const bf16*)dout, ws, (bf16*)dk,
+                           (bf16*)dv);
     else
         hipLaunchKernelGGL(dkdv_fp32_kernel<D>, dim3(p.nKT * Hkv), dim3(64), 0, s, p, Hq, Hkv,
                            scale, (const float*)q, (const float*)k, (const float*)v,
-                           (const float*)dout, lse, delta, (float*)dk, (float*)dv);
+                           (const float*)dout, ws, (float*)dk, (float*)dv);
 }
 
 hipError_t launch_bwd_dkdv(bool bf16_, const DevPlan& p, int Hq, int Hkv, int D, float scale,
-                           const void* q, const void* k, const void* v, const float* lse,
-                           const void* dout, const float* delta, void* dk, void* dv,
-                           hipStream_t s) {
-    if (D == 128)
-        dkdv_launch<128>(bf16_, p, Hq, Hkv, scale, q, k, v, lse, dout, delta, dk, dv, s);
-    else
-        dkdv_launch<64>(bf16_, p, Hq, Hkv, scale, q, k, v, lse, dout, delta, dk, dv, s);
+                           const void* q, const void* k, const void* v, const void* dout,
+                           const float* ws, void* dk, void* dv, hipStream_t s) {
+    if (D == 128) dkdv_launch<128>(bf16_, p, Hq, Hkv, scale, q, k, v, dout, ws, dk, dv, s);
+    else dkdv_launch<64>(bf16_, p, Hq, Hkv, scale, q, k, v, dout, ws, dk, dv, s);
     return hipGetLastError();
 }
 
 template <int D>
 static void dq_launch(bool bf16_, const DevPlan& p, int Hq, int Hkv, float scale, const void* q,
-                      const void* k, const void* v, const float* lse, const void* dout,
-                      const float* delta, void* dq, hipStream_t s) {
+                      const void* k, const void* v, const void* dout, const float* ws, void* dq,
+                      hipStream_t s) {
     if (bf16_)
         hipLaunchKernelGGL(dq_bf16_kernel<D>, dim3(xcd_grid(p.nQT * Hkv, Hq / Hkv)), dim3(256), 0,
                            s, p, Hq, Hkv, scale, scale * kLog2e, (const bf16*)q, (const bf16*)k,
-                           (const bf16*)v, (const bf16*)dout, lse, delta, (bf16*)dq);
+                           (const bf16*)v, (const bf16*)dout, ws, (bf16*)dq);
     else
         hipLaunchKernelGGL(dq_fp32_kernel<D>, dim3(p.nQT * Hq), dim3(kBq), 0, s, p, Hq, Hkv,
                            scale, (const float*)q, (const float*)k, (const float*)v,
-                           (const float*)dout, lse, delta, (float*)dq);
+                           (const float*)dout, ws, (float*)dq);
 }
 
 hipError_t launch_bwd_dq(bool bf16_, const DevPlan& p, int Hq, int Hkv, int D, float scale,
-                         const void* q, const void* k, const void* v, const float* lse,
-                         const void* dout, const float* delta, void* dq, hipStream_t s) {
-    if (D == 128)
-        dq_launch<128>(bf16_, p, Hq, Hkv, scale, q, k, v, lse, dout, delta, dq, s);
-    else
-        dq_launch<64>(bf16_, p, Hq, Hkv, scale, q, k, v, lse, dout, delta, dq, s);
+                         const void* q, const void* k, const void* v, const void* dout,
+                         const float* ws, void* dq, hipStream_t s) {
+    if (D == 128) dq_launch<128>(bf16_, p, Hq, Hkv, scale, q, k, v, dout, ws, dq, s);
+    else dq_launch<64>(bf16_, p, Hq, Hkv, scale, q, k, v, dout, ws, dq, s);
     return hipGetLastError();
 }
 

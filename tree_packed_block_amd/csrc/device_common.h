@@ -47,6 +47,27 @@ __device__ __forceinline__ f32x16 zero16() {
     return z;
 }
 
+// Load through the constant address space: plan metadata is never written while a
+// kernel runs, and with a wave-uniform address this becomes a scalar load (tracked
+// by lgkmcnt, so it never waits behind the asynchronous LDS copies counted by vmcnt).
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return *(const __attribute__((address_space(4))) T*)(p);
+#else
+    return *p;
+#endif
+}
+__device__ __forceinline__ int4 ld_const(const int4* p) {
+    typedef __attribute__((ext_vector_type(4))) int i32x4;
+    const i32x4 v = ld_const(reinterpret_cast<const i32x4*>(p));
+    return make_int4(v[0], v[1], v[2], v[3]);
+}
+
+// Make the compiler wait here for a register loaded from memory (so later loops do not
+// re-check it against outstanding asynchronous copies).
+__device__ __forceinline__ void settle(const bf16x8& v) { asm volatile("" ::"v"(v)); }
+
 // 2^x on the hardware exponential unit (exact 0 for -inf).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -67,5 +88,62 @@ __device__ __forceinline__ bool xcd_group(int bid, int members, int n_groups, in
 }
 
 inline int xcd_grid(int n_groups, int members) { return (n_groups + 7) / 8 * 8 * members; }
+
+// ---------------------------------------------------------------- LDS staging
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)(p);
+}
+
+// Asynchronous 16-byte copy global -> LDS (global_load_lds_dwordx4): lane i's 16 bytes
+// land at LDS byte address lds_wave_base + 16 * i (M0); lds_wave_base must be the same
+// for every lane of the wave.  Issued as inline assembly so the compiler neither
+// inserts waits for it nor reorders LDS accesses around it: completion is tracked
+// with explicit vmcnt waits, and the copy becomes visible to other waves after the
+// issuing wave has waited and a barrier has passed.
+__device__ __forceinline__ void dma16(const void* g, unsigned lds_wave_base) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_wave_base))
+                 : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding (they
+// complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier without the implied memory fence of __syncthreads (which would
+// drain every outstanding load, prefetches included).  LDS written by regular stores
+// must be waited for (lgkmcnt) by the writer before it.
+__device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
+
+// Transposed 8-byte LDS read (ds_read_b64_tr_b16).  In every group of 16 lanes,
+// lane i receives element i % 4 of the 8-byte rows addressed by lanes 4j + i / 4,
+// j = 0..3.  Addressing lane r at X[k0 + r / 4][c0 + 4 * (r % 4)] of a row-major
+// 16-bit matrix therefore gives lane i the four values X[k0 + j][c0 + i].
+__device__ __forceinline__ bf16x4 ld8_tr(const void* lds_addr) {
+    typedef __attribute__((ext_vector_type(4))) short s16x4;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(lds_addr));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+// 16-byte slot holding chunk `chunk` (8 elements) of row `row` in a row-major LDS tile
+// of 16-bit elements with D columns, XOR-swizzled so that 16 lanes reading the same
+// chunk of 16 consecutive rows, and 16 lanes reading 4 consecutive rows in transposed
+// fashion, hit distinct banks.
+template <int D>
+__device__ __forceinline__ int swz(int row, int chunk) {
+    if constexpr (D == 128) return chunk ^ ((2 * (row & 7)) | ((row >> 3) & 1));
+    else return chunk ^ ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int chunk) {  // byte offset
+    return row * (D * 2) + swz<D>(row, chunk) * 16;
+}
 
 }  // namespace octo

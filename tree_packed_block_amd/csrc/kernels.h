@@ -9,7 +9,7 @@ namespace octo {
 
 // Device view of an uploaded plan (see plan.h for how the host builds it).
 struct DevPlan {
-    int32_t T, nQT, nKT, n_partial;
+    int32_t T, nQT, nKT, n_partial;  // mask index n_partial is all ones (FULL)
     const int32_t* fwd_order;   // [nQT] query tiles, longest list first
     const int32_t* qt_ptr;      // [nQT+1]
     const int2* q_pairs;        // [n_pairs] {kv_tile, mask (-1 = FULL)}
@@ -18,6 +18,11 @@ struct DevPlan {
     const int2* k_pairs;        // [n_pairs] {q_tile, mask}
     const uint64_t* mask_rows;  // [n_partial][128]   bit x of row r: row sees key x
     const uint64_t* mask_cols;  // [n_partial][64][2] bit r of key x: row r sees key x
+    int32_t nKB, pad;           // 128-key blocks
+    const int32_t* blk_order;   // [nKB] blocks, longest list first
+    const int32_t* blk_ptr;     // [nKB+1]
+    const int4* blk_entries;    // {q_tile, mask of tile 2b, mask of tile 2b+1, 0};
+                                // mask -1 FULL, -2 not seen, else PARTIAL index
 };
 
 constexpr int kBq = 128;  // query rows per tile
@@ -29,16 +34,18 @@ hipError_t launch_fwd_bf16(const DevPlan& p, int Hq, int Hkv, int D, float scale
 hipError_t launch_fwd_fp32(const DevPlan& p, int Hq, int Hkv, int D, float scale,
                            const void* q, const void* k, const void* v, void* o, float* lse,
                            hipStream_t s);
-// Backward phases.  `bf16` selects the MFMA kernels, otherwise float32.
-hipError_t launch_bwd_delta(bool bf16, const DevPlan& p, int Hq, int D, const void* o,
-                            const void* dout, float* delta, hipStream_t s);
+// Backward phases.  `bf16` selects the MFMA kernels, otherwise float32.  The
+// workspace holds LSE * log2(e) and Delta, float32 [2][Hq][Tp], Tp = T rounded up to
+// a multiple of 128 (padding rows: +inf and 0).
+size_t bwd_workspace_floats(int T, int Hq);
+hipError_t launch_bwd_preprocess(bool bf16, const DevPlan& p, int Hq, int D, const void* o,
+                                 const void* dout, const float* lse, float* ws, hipStream_t s);
 hipError_t launch_bwd_dkdv(bool bf16, const DevPlan& p, int Hq, int Hkv, int D, float scale,
-                           const void* q, const void* k, const void* v, const float* lse,
-                           const void* dout, const float* delta, void* dk, void* dv,
-                           hipStream_t s);
+                           const void* q, const void* k, const void* v, const void* dout,
+                           const float* ws, void* dk, void* dv, hipStream_t s);
 hipError_t launch_bwd_dq(bool bf16, const DevPlan& p, int Hq, int Hkv, int D, float scale,
-                         const void* q, const void* k, const void* v, const float* lse,
-                         const void* dout, const float* delta, void* dq, hipStream_t s);
+                         const void* q, const void* k, const void* v, const void* dout,
+                         const float* ws, void* dq, hipStream_t s);
 hipError_t launch_decode_bf16(int B, int Hq, int Hkv, int D, int page_size, float scale,
                               const void* q, const void* k_pool, const void* v_pool,
                               int n_pages, const int32_t* seg_ptr, const int32_t* seg_page,

@@ -2,6 +2,7 @@
 #include "plan.h"
 
 #include <algorithm>
+#include <climits>
 #include <cstring>
 #include <numeric>
 
@@ -107,7 +108,6 @@ int compute_positions(DagInfo& d, std::string& err) {
     std::vector<Req> stack;
     stack.reserve(nb);
     for (int32_t b0 = 0; b0 < nb; ++b0) {
-        for (auto& x : xs[b0]) (void)x;
         stack.push_back({b0, d.br[b0].len});
         open[b0] = 1;
         while (!stack.empty()) {
@@ -319,8 +319,12 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     }
     p.n_partial = (int64_t)(p.mask_rows.size() / (Bq * p.row_words));
 
+    // One extra all-ones mask (index n_partial) that kernels may use for FULL tiles.
+    p.mask_rows.insert(p.mask_rows.end(), (size_t)Bq * p.row_words, ~0ull);
+
     // Key-major copy of every PARTIAL mask, for the KV-tile owners of the backward.
-    p.mask_cols.assign(p.n_partial * Bk * p.col_words, 0);
+    p.mask_cols.assign((p.n_partial + 1) * Bk * p.col_words, 0);
+    std::fill(p.mask_cols.begin() + p.n_partial * Bk * p.col_words, p.mask_cols.end(), ~0ull);
     for (int64_t m = 0; m < p.n_partial; ++m) {
         const uint64_t* wr = &p.mask_rows[m * Bq * p.row_words];
         uint64_t* wc = &p.mask_cols[m * Bk * p.col_words];
@@ -353,6 +357,31 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     std::stable_sort(p.bwd_order.begin(), p.bwd_order.end(), [&](int a, int b) {
         return p.kt_ptr[a + 1] - p.kt_ptr[a] > p.kt_ptr[b + 1] - p.kt_ptr[b];
     });
+    // 128-key blocks: merge the transposed lists of tiles 2b and 2b+1.
+    p.nKB = (nKT + 1) / 2;
+    p.blk_ptr.assign(p.nKB + 1, 0);
+    p.blk_entries.clear();
+    for (int32_t b = 0; b < p.nKB; ++b) {
+        const int32_t t0 = 2 * b, t1 = 2 * b + 1;
+        int32_t i0 = p.kt_ptr[t0], e0 = p.kt_ptr[t0 + 1];
+        int32_t i1 = t1 < nKT ? p.kt_ptr[t1] : 0, e1 = t1 < nKT ? p.kt_ptr[t1 + 1] : 0;
+        while (i0 < e0 || i1 < e1) {
+            const int32_t q0 = i0 < e0 ? p.k_pairs[i0].tile : INT32_MAX;
+            const int32_t q1 = i1 < e1 ? p.k_pairs[i1].tile : INT32_MAX;
+            const int32_t qt = std::min(q0, q1);
+            BlockEntry be{qt, -2, -2, 0};
+            if (q0 == qt) be.mask0 = p.k_pairs[i0++].mask;
+            if (q1 == qt) be.mask1 = p.k_pairs[i1++].mask;
+            p.blk_entries.push_back(be);
+        }
+        p.blk_ptr[b + 1] = (int32_t)p.blk_entries.size();
+    }
+    p.blk_order.resize(p.nKB);
+    std::iota(p.blk_order.begin(), p.blk_order.end(), 0);
+    std::stable_sort(p.blk_order.begin(), p.blk_order.end(), [&](int a, int b) {
+        return p.blk_ptr[a + 1] - p.blk_ptr[a] > p.blk_ptr[b + 1] - p.blk_ptr[b];
+    });
+
     p.max_q_list = 0;
     for (int32_t qt = 0; qt < nQT; ++qt)
         p.max_q_list = std::max(p.max_q_list, p.qt_ptr[qt + 1] - p.qt_ptr[qt]);
@@ -376,6 +405,9 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     L.k_pairs = place(p.k_pairs.size() * sizeof(TilePair));
     L.mask_rows = place(p.mask_rows.size() * 8);
     L.mask_cols = place(p.mask_cols.size() * 8);
+    L.blk_order = place(p.blk_order.size() * 4);
+    L.blk_ptr = place(p.blk_ptr.size() * 4);
+    L.blk_entries = place(p.blk_entries.size() * sizeof(BlockEntry));
     L.total = std::max<size_t>(at, 256);
     p.blob.assign(L.total, 0);
     auto put = [&](size_t off, const void* src, size_t bytes) {
@@ -389,6 +421,9 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     put(L.k_pairs, p.k_pairs.data(), p.k_pairs.size() * sizeof(TilePair));
     put(L.mask_rows, p.mask_rows.data(), p.mask_rows.size() * 8);
     put(L.mask_cols, p.mask_cols.data(), p.mask_cols.size() * 8);
+    put(L.blk_order, p.blk_order.data(), p.blk_order.size() * 4);
+    put(L.blk_ptr, p.blk_ptr.data(), p.blk_ptr.size() * 4);
+    put(L.blk_entries, p.blk_entries.data(), p.blk_entries.size() * sizeof(BlockEntry));
     return OCTOPUS_OK;
 }
 

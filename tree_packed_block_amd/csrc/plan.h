@@ -52,9 +52,17 @@ struct DagInfo {
 int load_dag(const octopus_branch* br, int32_t nb, const octopus_mount* mt, int32_t nm,
              int32_t T, DagInfo& out, std::string& err);
 
+// One entry of a 128-key block's list: a query tile and, for each of the block's two
+// 64-key tiles, -1 (FULL), -2 (the tile is not seen by this query tile) or the
+// index of its PARTIAL mask.
+struct BlockEntry {
+    int32_t qt, mask0, mask1, pad;
+};
+
 struct DevLayout {
     size_t fwd_order = 0, qt_ptr = 0, q_pairs = 0, bwd_order = 0, kt_ptr = 0,
-           k_pairs = 0, mask_rows = 0, mask_cols = 0, total = 0;
+           k_pairs = 0, mask_rows = 0, mask_cols = 0, blk_order = 0, blk_ptr = 0,
+           blk_entries = 0, total = 0;
 };
 
 struct Plan {
@@ -66,6 +74,9 @@ struct Plan {
     std::vector<TilePair> q_pairs;
     std::vector<int32_t> bwd_order, kt_ptr;
     std::vector<TilePair> k_pairs;
+    int32_t nKB = 0;                      // 128-key blocks (pairs of KV tiles)
+    std::vector<int32_t> blk_order, blk_ptr;
+    std::vector<BlockEntry> blk_entries;  // merged transposed lists of each block
     std::vector<uint64_t> mask_rows;  // [n_partial][Bq][row_words]
     std::vector<uint64_t> mask_cols;  // [n_partial][Bk][col_words]
     int64_t nnz = 0, n_partial = 0;
