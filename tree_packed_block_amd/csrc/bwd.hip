@@ -17,10 +17,11 @@
 //      mounts), for every query head of the group.  Each dK/dV row is written by its
 //      owner only, so there are no atomics and the result does not depend on the
 //      schedule;
-//   3. dQ: one workgroup per (query tile, query head), like the forward.
+//   3. dQ: one workgroup per query tile and pair of query heads, like the forward.
 // Scores are recomputed from LSE in both 2 and 3.
 #include "device_common.h"
 #include "kernels.h"
+#include "kvstage.h"
 
 namespace octo {
 
@@ -275,41 +276,37 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
 
 // ------------------------------------------------------------------ dQ (bf16)
 //
-// Workgroup = (query tile, query head), wave w owns 32 query rows; like the forward,
-// S^T = K Q^T and dP^T = V dO^T put one query per lane, and dS^T is the B operand of
-// dQ^T += K^T dS^T with K staged transposed in LDS.
+// Workgroup = one query tile for HPW query heads of one KV group, wave = 32 query rows;
+// like the forward, S^T = K Q^T and dP^T = V dO^T put one query per lane, and dS^T is
+// the B operand of dQ^T += K^T dS^T, whose A operand is read transposed from the same
+// row-major K tile.  K/V tiles and row masks arrive through three asynchronous stages.
 
-template <int D>
-struct DqSmem {
-    static constexpr int RST = D + 8, TST = 64 + 8;
-    bf16 Ks[64 * RST];
-    bf16 Vs[64 * RST];
-    bf16 Kt[D * TST];
-};
-
-template <int D>
-__global__ __launch_bounds__(256, 1) void dq_bf16_kernel(
+template <int D, int HPW>
+__global__ __launch_bounds__(256 * HPW, 1) void dq_bf16_kernel(
     DevPlan P, int Hq, int Hkv, float scale, float scale_log2, const bf16* __restrict__ Q,
     const bf16* __restrict__ K, const bf16* __restrict__ V, const bf16* __restrict__ dO,
     const float* __restrict__ ws, bf16* __restrict__ dQ) {
-    constexpr int KS = D / 16, DB = D / 32, C8 = D / 8, NLOAD = 16 * C8;
-    constexpr int RST = DqSmem<D>::RST, TST = DqSmem<D>::TST;
-    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[sizeof(DqSmem<D>)];
-    DqSmem<D>& S = *reinterpret_cast<DqSmem<D>*>(smem_raw);
+    using S = KvStage<D>;
+    constexpr int NTHR = 256 * HPW;
+    constexpr int KS = D / 16, DB = D / 32;
+    constexpr int PER_STAGE = 2 * (S::MAT / (16 * NTHR)) + 1;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[S::NST * S::BYTES];
 
     const int G = Hq / Hkv;
-    int grp, hh;
-    if (!xcd_group(blockIdx.x, G, P.nQT * Hkv, grp, hh)) return;
-    const int qt = P.fwd_order[grp / Hkv];
+    int grp, hp;
+    if (!xcd_group(blockIdx.x, G / HPW, P.nQT * Hkv, grp, hp)) return;
+    const int qt = ld_const(P.fwd_order + grp / Hkv);
     const int kvh = grp % Hkv;
-    const int h = kvh * G + hh;
 
-    const int T = P.T;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = kvh * G + hp * HPW + (w >> 2);
     const int n = lane & 31, g = lane >> 5;
-    const int rr = w * 32 + n;
+    const int T = P.T, Tp = padded_rows(T);
+    const int rr = (w & 3) * 32 + n;
     const int row = qt * kBq + rr;
     const size_t qstride = (size_t)Hq * D, kvstride = (size_t)Hkv * D;
+    const unsigned smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
     bf16x8 qf[KS], df[KS];
 #pragma unroll
@@ -318,86 +315,67 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(
         qf[ks] = row < T ? ld16(Q + off) : zero8();
         df[ks] = row < T ? ld16(dO + off) : zero8();
     }
-    const int Tp = padded_rows(T);
     const float lse2 = ws[(size_t)h * Tp + row];
     const float dlt = ws[(size_t)Hq * Tp + (size_t)h * Tp + row];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        settle(qf[ks]);
+        settle(df[ks]);
+    }
+    asm volatile("" ::"v"(lse2), "v"(dlt));
     f32x16 dq[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) dq[db] = zero16();
 
-    const bool loader = tid < NLOAD;
-    const int c8 = tid % C8, rg = tid / C8;
-    bf16x8 kr[4], vr[4];
-    auto gload = [&](int kt) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int key = kt * kBk + 4 * rg + j;
-            if (loader && key < T) {
-                const size_t off = (size_t)key * kvstride + (size_t)kvh * D + 8 * c8;
-                kr[j] = ld16(K + off);
-                vr[j] = ld16(V + off);
-            } else {
-                kr[j] = zero8();
-                vr[j] = zero8();
-            }
-        }
+    const int p0 = ld_const(P.qt_ptr + qt), p1 = ld_const(P.qt_ptr + qt + 1);
+    const int n_it = p1 - p0;
+    auto issue = [&](int it) {
+        const int2 pr = ld_const(P.q_pairs + p0 + it);
+        issue_kv_stage<D, NTHR>(smem_base + (it % S::NST) * S::BYTES, K, V, P.mask_rows, pr.x,
+                                pr.y >= 0 ? pr.y : P.n_partial, T, kvh, kvstride, tid, w, lane);
     };
-    auto lds_put = [&]() {
-        if (!loader) return;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            st16(&S.Ks[(4 * rg + j) * RST + 8 * c8], kr[j]);
-            st16(&S.Vs[(4 * rg + j) * RST + 8 * c8], vr[j]);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            bf16x4 a;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) a[j] = kr[j][e];
-            st8(&S.Kt[(8 * c8 + e) * TST + 4 * rg], a);
-        }
-    };
+    if (n_it > 0) issue(0);
+    if (n_it > 1) issue(1);
+    const int r_in = lane & 15, dh = (lane >> 4) & 1;
+    for (int it = 0; it < n_it; ++it) {
+        if (it + 1 < n_it) wait_vmem<PER_STAGE>();
+        else wait_vmem<0>();
+        barrier();
+        if (it + 2 < n_it) issue(it + 2);
+        const unsigned char* base = smem + (it % S::NST) * S::BYTES;
+        const unsigned char* Ks = base;
+        const unsigned char* Vs = base + S::MAT;
+        const uint64_t bits = *reinterpret_cast<const uint64_t*>(base + S::MASK_OFF + rr * 8);
 
-    const int p0 = P.qt_ptr[qt], p1 = P.qt_ptr[qt + 1];
-    if (p0 < p1) gload(P.q_pairs[p0].x);
-    for (int pi = p0; pi < p1; ++pi) {
-        const int2 pr = P.q_pairs[pi];
-        __syncthreads();
-        lds_put();
-        __syncthreads();
-        if (pi + 1 < p1) gload(P.q_pairs[pi + 1].x);
-
-        f32x16 s[2], dp[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = zero16();
-            dp[kb] = zero16();
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 ak = ld16(&S.Ks[(kb * 32 + n) * RST + 16 * ks + 8 * g]);
-                const bf16x8 av = ld16(&S.Vs[(kb * 32 + n) * RST + 16 * ks + 8 * g]);
-                s[kb] = mfma_32x32x16(ak, qf[ks], s[kb]);
-                dp[kb] = mfma_32x32x16(av, df[ks], dp[kb]);
-            }
-        }
-        const uint64_t bits = pr.y >= 0 ? P.mask_rows[(size_t)pr.y * kBq + rr] : ~0ull;
         bf16x8 sb[4];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) {  // one 32-key block at a time (register pressure)
+            f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int off = tile_off<D>(kb * 32 + n, 2 * ks + g);
+                s = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(Ks + off), qf[ks], s);
+                dp = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(Vs + off), df[ks], dp);
+            }
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const int x = kb * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-                float p = fast_exp2(s[kb][j] * scale_log2 - lse2);
+                float p = fast_exp2(s[j] * scale_log2 - lse2);
                 if (!((bits >> x) & 1ull)) p = 0.f;
-                sb[kb * 2 + (j >> 3)][j & 7] = (bf16)(p * (dp[kb][j] - dlt));
+                sb[kb * 2 + (j >> 3)][j & 7] = (bf16)(p * (dp[j] - dlt));
             }
+        }
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+        for (int kk = 0; kk < 4; ++kk) {
+            const int rowa = 16 * kk + 4 * g + (r_in >> 2);
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const bf16* krow = &S.Kt[(db * 32 + n) * TST + 16 * kk + 4 * g];
-                dq[db] = mfma_32x32x16(cat(ld8(krow), ld8(krow + 8)), sb[kk], dq[db]);
+                const int col = db * 32 + 16 * dh + 4 * (r_in & 3);
+                const bf16x8 a = cat(ld8_tr(Ks + tile_off<D>(rowa, col >> 3) + (col & 7) * 2),
+                                     ld8_tr(Ks + tile_off<D>(rowa + 8, col >> 3) + (col & 7) * 2));
+                dq[db] = mfma_32x32x16(a, sb[kk], dq[db]);
             }
+        }
     }
 
     if (row < T) {
@@ -599,18 +577,30 @@ hipError_t launch_bwd_dkdv(bool bf16_, const DevPlan& p, int Hq, int Hkv, int D,
     return hipGetLastError();
 }
 
+template <int D, int HPW>
+static void dq_bf16_launch(const DevPlan& p, int Hq, int Hkv, float scale, const void* q,
+                           const void* k, const void* v, const void* dout, const float* ws,
+                           void* dq, hipStream_t s) {
+    hipLaunchKernelGGL((dq_bf16_kernel<D, HPW>), dim3(xcd_grid(p.nQT * Hkv, Hq / Hkv / HPW)),
+                       dim3(256 * HPW), 0, s, p, Hq, Hkv, scale, scale * kLog2e, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (const bf16*)dout, ws, (bf16*)dq);
+}
+
 template <int D>
 static void dq_launch(bool bf16_, const DevPlan& p, int Hq, int Hkv, float scale, const void* q,
                       const void* k, const void* v, const void* dout, const float* ws, void* dq,
                       hipStream_t s) {
-    if (bf16_)
-        hipLaunchKernelGGL(dq_bf16_kernel<D>, dim3(xcd_grid(p.nQT * Hkv, Hq / Hkv)), dim3(256), 0,
-                           s, p, Hq, Hkv, scale, scale * kLog2e, (const bf16*)q, (const bf16*)k,
-                           (const bf16*)v, (const bf16*)dout, ws, (bf16*)dq);
-    else
+    if (bf16_) {
+        // Two heads per workgroup do not fit the register file at D = 128.
+        if (D == 64 && (Hq / Hkv) % 2 == 0)
+            dq_bf16_launch<D, 2>(p, Hq, Hkv, scale, q, k, v, dout, ws, dq, s);
+        else
+            dq_bf16_launch<D, 1>(p, Hq, Hkv, scale, q, k, v, dout, ws, dq, s);
+    } else {
         hipLaunchKernelGGL(dq_fp32_kernel<D>, dim3(p.nQT * Hq), dim3(kBq), 0, s, p, Hq, Hkv,
                            scale, (const float*)q, (const float*)k, (const float*)v,
                            (const float*)dout, ws, (float*)dq);
+    }
 }
 
 hipError_t launch_bwd_dq(bool bf16_, const DevPlan& p, int Hq, int Hkv, int D, float scale,

@@ -7,98 +7,82 @@
 // some row sees (FULL, or PARTIAL with a per-row bit mask); this kernel walks that
 // list with an online softmax.
 //
-// bf16 kernel: one workgroup = one (query tile, query head); four wave64s, each
-// owning 32 query rows.  Scores are computed transposed, S^T = K Q^T, with
-// v_mfma_f32_32x32x16_bf16 so that every lane holds one query column: the row max
-// and row sum are in-lane plus one exchange with lane ^ 32, and the probabilities
-// come out of the accumulator already laid out as the B operand of O^T = V^T P^T.
-// K is staged row-major in LDS (A operand of S^T), V transposed (A operand of O^T);
-// the next tile's global loads are issued before the current tile's MFMAs.  The
-// G = Hq/Hkv query heads reading one KV head are launched adjacently on one XCD so
-// their shared K/V tiles hit the same L2.
+// bf16 kernel: one workgroup = one query tile for HPW query heads of one KV group
+// (HPW = 2 when the group size is even), 4 wave64s per head, each owning 32 query
+// rows.  Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 so
+// that every lane holds one query column: the row max and row sum are in-lane plus
+// one exchange with lane ^ 32, and the probabilities come out of the accumulator
+// already laid out as the B operand of O^T = V^T P^T.  K and V tiles are copied
+// global -> LDS asynchronously (three stages in flight, XOR-swizzled rows) together
+// with the query tile's row masks; V^T operands are read with ds_read_b64_tr_b16.
+// Workgroups of one KV group are launched adjacently on one XCD so their shared K/V
+// tiles hit the same L2.
 #include "device_common.h"
 #include "kernels.h"
+#include "kvstage.h"
 
 namespace octo {
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
+// Forward.  HPW query heads (of one KV group) per workgroup, 4 waves per head, each
+// wave owning 32 query rows.
+template <int D, int HPW>
+__global__ __launch_bounds__(256 * HPW, 1) void fwd_bf16_kernel(
     DevPlan P, int Hq, int Hkv, float scale_log2, const bf16* __restrict__ Q,
     const bf16* __restrict__ K, const bf16* __restrict__ V, bf16* __restrict__ O,
     float* __restrict__ LSE) {
-    constexpr int KS = D / 16;   // MFMA k-steps over the head dimension
-    constexpr int DB = D / 32;   // 32-row blocks of O^T
-    constexpr int KST = D + 8;   // LDS row stride of K (elements), padded
-    constexpr int VST = kBk + 8; // LDS row stride of V^T
-    constexpr int C8 = D / 8;    // 16-byte chunks per K/V row
-    constexpr int NLOAD = (kBk / 4) * C8;  // loader items: 4 rows x 8 columns each
-    __shared__ __attribute__((aligned(16))) bf16 Ks[kBk * KST];
-    __shared__ __attribute__((aligned(16))) bf16 Vt[D * VST];
+    using S = KvStage<D>;
+    constexpr int NTHR = 256 * HPW;
+    constexpr int KS = D / 16, DB = D / 32;
+    constexpr int PER_STAGE = 2 * (S::MAT / (16 * NTHR)) + 1;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[S::NST * S::BYTES];
 
     const int G = Hq / Hkv;
-    int grp, hh;
-    if (!xcd_group(blockIdx.x, G, P.nQT * Hkv, grp, hh)) return;
-    const int qt = P.fwd_order[grp / Hkv];
+    int grp, hp;
+    if (!xcd_group(blockIdx.x, G / HPW, P.nQT * Hkv, grp, hp)) return;
+    const int qt = ld_const(P.fwd_order + grp / Hkv);
     const int kvh = grp % Hkv;
-    const int h = kvh * G + hh;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = kvh * G + hp * HPW + (w >> 2);
     const int n = lane & 31, g = lane >> 5;
     const int T = P.T;
-    const int rr = w * 32 + n;       // row inside the query tile
-    const int row = qt * kBq + rr;   // packed query row of this lane
+    const int rr = (w & 3) * 32 + n;  // row inside the query tile
+    const int row = qt * kBq + rr;
     const size_t qstride = (size_t)Hq * D, kvstride = (size_t)Hkv * D;
+    const unsigned smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
     bf16x8 qf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
         qf[ks] = row < T ? ld16(Q + row * qstride + (size_t)h * D + 16 * ks + 8 * g) : zero8();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) settle(qf[ks]);
 
     f32x16 o[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = zero16();
     float m = -1e30f, l = 0.f;
 
-    const bool loader = tid < NLOAD;
-    const int c8 = tid % C8, rg = tid / C8;
-    bf16x8 kr[4], vr[4];
-    auto gload = [&](int kt) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int key = kt * kBk + 4 * rg + j;
-            if (loader && key < T) {
-                const size_t off = (size_t)key * kvstride + (size_t)kvh * D + 8 * c8;
-                kr[j] = ld16(K + off);
-                vr[j] = ld16(V + off);
-            } else {
-                kr[j] = zero8();
-                vr[j] = zero8();
-            }
-        }
+    const int p0 = ld_const(P.qt_ptr + qt), p1 = ld_const(P.qt_ptr + qt + 1);
+    const int n_it = p1 - p0;
+    auto issue = [&](int it) {
+        const int2 pr = ld_const(P.q_pairs + p0 + it);
+        issue_kv_stage<D, NTHR>(smem_base + (it % S::NST) * S::BYTES, K, V, P.mask_rows, pr.x,
+                                pr.y >= 0 ? pr.y : P.n_partial, T, kvh, kvstride, tid, w, lane);
     };
-    auto lds_put = [&]() {
-        if (!loader) return;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) st16(&Ks[(4 * rg + j) * KST + 8 * c8], kr[j]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            bf16x4 t;
-            t[0] = vr[0][e];
-            t[1] = vr[1][e];
-            t[2] = vr[2][e];
-            t[3] = vr[3][e];
-            st8(&Vt[(8 * c8 + e) * VST + 4 * rg], t);
-        }
-    };
-
-    const int p0 = P.qt_ptr[qt], p1 = P.qt_ptr[qt + 1];
-    if (p0 < p1) gload(P.q_pairs[p0].x);
-    for (int pi = p0; pi < p1; ++pi) {
-        const int2 pr = P.q_pairs[pi];
-        __syncthreads();
-        lds_put();
-        __syncthreads();
-        if (pi + 1 < p1) gload(P.q_pairs[pi + 1].x);
+    if (n_it > 0) issue(0);
+    if (n_it > 1) issue(1);
+    const int r_in = lane & 15, dh = (lane >> 4) & 1;
+    for (int it = 0; it < n_it; ++it) {
+        if (it + 1 < n_it) wait_vmem<PER_STAGE>();
+        else wait_vmem<0>();
+        barrier();
+        if (it + 2 < n_it) issue(it + 2);
+        const unsigned char* base = smem + (it % S::NST) * S::BYTES;
+        const unsigned char* Ks = base;
+        const unsigned char* Vs = base + S::MAT;
+        const uint64_t bits = *reinterpret_cast<const uint64_t*>(base + S::MASK_OFF + rr * 8);
 
         // S^T (64 keys x 32 queries) = K Q^T, two 32-key blocks.
         f32x16 s[2];
@@ -106,29 +90,20 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
         for (int kb = 0; kb < 2; ++kb) {
             s[kb] = zero16();
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a = ld16(&Ks[(kb * 32 + n) * KST + 16 * ks + 8 * g]);
-                s[kb] = mfma_32x32x16(a, qf[ks], s[kb]);
-            }
+            for (int ks = 0; ks < KS; ++ks)
+                s[kb] = mfma_32x32x16(
+                    *reinterpret_cast<const bf16x8*>(Ks + tile_off<D>(kb * 32 + n, 2 * ks + g)),
+                    qf[ks], s[kb]);
         }
-        if (pr.y >= 0) {
-            const uint64_t bits = P.mask_rows[(size_t)pr.y * kBq + rr];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int x = kb * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-                    if (!((bits >> x) & 1ull)) s[kb][j] = -INFINITY;
-                }
-        }
-        // Online softmax in the log2 domain.
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                s[kb][j] *= scale_log2;
-                mx = fmaxf(mx, s[kb][j]);
+                const int x = kb * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+                const float t = ((bits >> x) & 1ull) ? s[kb][j] * scale_log2 : -INFINITY;
+                s[kb][j] = t;
+                mx = fmaxf(mx, t);
             }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float mnew = fmaxf(m, mx);
@@ -148,17 +123,19 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
                 l += pv;
                 pf[kb * 2 + (j >> 3)][j & 7] = (bf16)pv;
             }
-        // O^T (D x 32 queries) += V^T P^T over 4 k-steps of 16 keys.  The lane's 8 keys
-        // of k-step kk are 16kk + 4g + {0..3} and 16kk + 8 + 4g + {0..3}, matching the
-        // rows its accumulator holds.
+        // O^T += V^T P^T over 4 k-steps of 16 keys; the lane's 8 keys in k-step kk are
+        // 16kk + 4g + {0..3} and 16kk + 8 + 4g + {0..3}, read transposed from V.
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+        for (int kk = 0; kk < 4; ++kk) {
+            const int rowa = 16 * kk + 4 * g + (r_in >> 2);
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const bf16* vrow = &Vt[(db * 32 + n) * VST + 16 * kk + 4 * g];
-                const bf16x8 a = cat(ld8(vrow), ld8(vrow + 8));
+                const int col = db * 32 + 16 * dh + 4 * (r_in & 3);
+                const bf16x8 a = cat(ld8_tr(Vs + tile_off<D>(rowa, col >> 3) + (col & 7) * 2),
+                                     ld8_tr(Vs + tile_off<D>(rowa + 8, col >> 3) + (col & 7) * 2));
                 o[db] = mfma_32x32x16(a, pf[kk], o[db]);
             }
+        }
     }
 
     l += __shfl_xor(l, 32);
@@ -236,18 +213,27 @@ __global__ __launch_bounds__(128) void fwd_fp32_kernel(DevPlan P, int Hq, int Hk
     }
 }
 
+template <int D, int HPW>
+static void fwd_bf16_launch(const DevPlan& p, int Hq, int Hkv, float sl2, const void* q,
+                            const void* k, const void* v, void* o, float* lse, hipStream_t s) {
+    const int G = Hq / Hkv;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, HPW>), dim3(xcd_grid(p.nQT * Hkv, G / HPW)),
+                       dim3(256 * HPW), 0, s, p, Hq, Hkv, sl2, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, (bf16*)o, lse);
+}
+
 hipError_t launch_fwd_bf16(const DevPlan& p, int Hq, int Hkv, int D, float scale,
                            const void* q, const void* k, const void* v, void* o, float* lse,
                            hipStream_t s) {
-    const int G = Hq / Hkv;
-    dim3 grid(xcd_grid(p.nQT * Hkv, G)), block(256);
     const float sl2 = scale * kLog2e;
-    if (D == 128)
-        hipLaunchKernelGGL(fwd_bf16_kernel<128>, grid, block, 0, s, p, Hq, Hkv, sl2,
-                           (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse);
-    else
-        hipLaunchKernelGGL(fwd_bf16_kernel<64>, grid, block, 0, s, p, Hq, Hkv, sl2,
-                           (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse);
+    const bool pair = (Hq / Hkv) % 2 == 0;
+    if (D == 128) {
+        if (pair) fwd_bf16_launch<128, 2>(p, Hq, Hkv, sl2, q, k, v, o, lse, s);
+        else fwd_bf16_launch<128, 1>(p, Hq, Hkv, sl2, q, k, v, o, lse, s);
+    } else {
+        if (pair) fwd_bf16_launch<64, 2>(p, Hq, Hkv, sl2, q, k, v, o, lse, s);
+        else fwd_bf16_launch<64, 1>(p, Hq, Hkv, sl2, q, k, v, o, lse, s);
+    }
     return hipGetLastError();
 }
 
