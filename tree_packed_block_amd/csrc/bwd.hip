@@ -89,16 +89,21 @@ __global__ __launch_bounds__(256) void preprocess_fp32_kernel(int T, int Tp, int
 // from the row-major Q and dO tiles (ds_read_b64_tr_b16).  Every dK/dV row has one
 // writer; there are no atomics and no cross-wave reduction.
 
+// LDS layout of the dK/dV stages, stage-major by kind: [Q x 3][dO x 3][LSE2/Delta x 3]
+// [key-major mask words x 3], so lane reads are a register plus an immediate.
 template <int D>
-struct DkdvCfg {
-    static constexpr int ROWB = D * 2;                   // bytes per row
-    static constexpr int MAT = 64 * ROWB;                // one 64-row Q or dO chunk
-    static constexpr int NDMA = MAT / (16 * 256);        // copies per thread per matrix
-    static constexpr int LSE_OFF = 2 * MAT;              // LSE2[64], then Delta[64]
-    static constexpr int MASK_OFF = LSE_OFF + 512;       // per wave: 32 keys x 2 words
-    static constexpr int STAGE = MASK_OFF + 4 * 512;
-    static constexpr int NST = 3;                        // stages in flight
-    static constexpr int PER_STAGE = 2 * NDMA + 2;       // copies per wave per stage
+struct DkdvLayout {
+    static constexpr int ROWB = D * 2;               // bytes per row
+    static constexpr int MAT = 64 * ROWB;            // one 64-row Q or dO chunk
+    static constexpr int NST = 3;                    // stages in flight
+    static constexpr int NDMA = MAT / (16 * 256);    // copies per thread per matrix
+    static constexpr int Q0 = 0;
+    static constexpr int D0 = NST * MAT;
+    static constexpr int L0 = 2 * NST * MAT;         // LSE2[64] then Delta[64] per stage
+    static constexpr int M0 = L0 + NST * 512;        // per wave: 32 keys x 2 words
+    static constexpr int MASKB = 4 * 512;
+    static constexpr int BYTES = M0 + NST * MASKB;
+    static constexpr int PER_STAGE = 2 * NDMA + 2;   // copies per wave per stage
 };
 
 template <int D>
@@ -106,10 +111,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
     DevPlan P, int Hq, int Hkv, float scale, float scale_log2, const bf16* __restrict__ Q,
     const bf16* __restrict__ K, const bf16* __restrict__ V, const bf16* __restrict__ dO,
     const float* __restrict__ ws, bf16* __restrict__ dK, bf16* __restrict__ dV) {
-    using C = DkdvCfg<D>;
+    using C = DkdvLayout<D>;
     constexpr int KS = D / 16, DB = D / 32, CPR = D / 8;
     constexpr int M = 4;  // consecutive blocks of one KV head dealt to one XCD
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[C::NST * C::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[C::BYTES];
 
     int grp, mm;
     if (!xcd_group(blockIdx.x, M, (P.nKB + M - 1) / M * Hkv, grp, mm)) return;
@@ -148,111 +153,126 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
         dv[db] = zero16();
     }
 
+    // Per-lane LDS offsets: row n (+32 per query block) chunk 2ks+g of Q and dO, and
+    // the transposed reads (rows 4g + r/4 (+8), +16 per k-step) of both.
+    const int r_in = lane & 15, dh = (lane >> 4) & 1;
+    int oq[KS], od[KS], oqt[DB][2], odt[DB][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        oq[ks] = C::Q0 + n * C::ROWB + (((2 * ks + g) ^ swz_key<D>(n)) * 16);
+        od[ks] = oq[ks] - C::Q0 + C::D0;
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int r = 4 * g + (r_in >> 2) + 8 * hf;
+            const int chunk = 4 * db + 2 * dh + ((r_in & 3) >> 1);
+            const int o2 = r * C::ROWB + ((chunk ^ swz_key<D>(r)) * 16) + 8 * (r_in & 1);
+            oqt[db][hf] = C::Q0 + o2;
+            odt[db][hf] = C::D0 + o2;
+        }
+    const int ol = C::L0 + 16 * g;                      // LSE2 rows 4g.. of each 8-row group
+    const int om = C::M0 + w * 512 + n * 16;            // this key's two mask words
+
     const int e0 = ld_const(P.blk_ptr + kb), e1 = ld_const(P.blk_ptr + kb + 1);
     const int n_it = (e1 - e0) * G * 2;  // (entry, head, 64-row half)
 
-    // Issue the asynchronous copies of iteration `it` into stage buffer `st`: the 64
-    // rows of Q and dO, their LSE2 and Delta, and this wave's 32 key-major mask words
-    // (the all-ones mask when the tile is FULL or not seen).
-    auto issue = [&](int it, int st) {
+    // Copies of iteration `it` into stage ST: the 64 rows of Q and dO, their LSE2 and
+    // Delta, and this wave's 32 key-major mask words (all ones when FULL or unseen).
+    auto issue = [&](auto st_c, int it) {
+        constexpr int ST = decltype(st_c)::value;
         const int e = e0 + it / (2 * G);
         const int hh = (it >> 1) % G, c = it & 1;
         const int h = kvh * G + hh;
         const int4 ent = ld_const(P.blk_entries + e);
         const int row0 = ent.x * kBq + c * 64;
-        const unsigned base = smem_base + st * C::STAGE;
 #pragma unroll
         for (int i = 0; i < C::NDMA; ++i) {
-            const int L = i * 256 + tid;
-            const int rho = L / CPR, slot = L % CPR;
+            const int li = i * 256 + tid;
+            const int rho = li / CPR, slot = li % CPR;
             const int chunk = swz<D>(rho, slot);  // the XOR swizzle is its own inverse
             const int r = min(row0 + rho, T - 1);
             const size_t off = (size_t)r * qstride + (size_t)h * D + 8 * chunk;
-            dma16(Q + off, base + (i * 256 + w * 64) * 16);
-            dma16(dO + off, base + C::MAT + (i * 256 + w * 64) * 16);
+            dma16(Q + off, smem_base + C::Q0 + ST * C::MAT + (i * 256 + w * 64) * 16);
+            dma16(dO + off, smem_base + C::D0 + ST * C::MAT + (i * 256 + w * 64) * 16);
         }
         if (lane < 8) {  // 32 pieces of 16 bytes, 8 per wave
             const int u = 8 * w + lane;
             const float* src = (u < 16 ? LSE2 : DEL) + (size_t)h * Tp + row0 + 4 * (u & 15);
-            dma16(src, base + C::LSE_OFF + 8 * w * 16);
+            dma16(src, smem_base + C::L0 + ST * 512 + 8 * w * 16);
         }
         if (lane < 32) {
-            int m = hi_tile ? ent.z : ent.y;
-            if (m < 0) m = P.n_partial;
-            dma16(P.mask_cols + ((size_t)m * kBk + 32 * (w & 1) + lane) * 2,
-                  base + C::MASK_OFF + w * 512);
+            int mk = hi_tile ? ent.z : ent.y;
+            if (mk < 0) mk = P.n_partial;
+            dma16(P.mask_cols + ((size_t)mk * kBk + 32 * (w & 1) + lane) * 2,
+                  smem_base + C::M0 + ST * C::MASKB + w * 512);
         }
     };
 
-    if (n_it > 0) issue(0, 0);
-    if (n_it > 1) issue(1, 1);
-    for (int it = 0; it < n_it; ++it) {
+    auto step = [&](auto st_c, int it) {
+        constexpr int ST = decltype(st_c)::value;
         if (it + 1 < n_it) wait_vmem<C::PER_STAGE>();
         else wait_vmem<0>();
         barrier();
-        if (it + 2 < n_it) issue(it + 2, (it + 2) % C::NST);
+        if (it + 2 < n_it) issue(ic<(ST + 2) % 3>{}, it + 2);
         const int4 ent = ld_const(P.blk_entries + e0 + it / (2 * G));
-        if ((hi_tile ? ent.z : ent.y) == -2) continue;  // tile not seen by this query tile
-
+        const int mk = hi_tile ? ent.z : ent.y;
+        if (mk == -2) return;  // this wave's tile is not seen by the query tile
+        const bool partial = mk >= 0;
         const int c = it & 1;
-        const unsigned char* base = smem + (it % C::NST) * C::STAGE;
-        const unsigned char* Qs = base;
-        const unsigned char* Ds = base + C::MAT;
-        const float* Ls = reinterpret_cast<const float*>(base + C::LSE_OFF);
-        const float* Dl = Ls + 64;
-        const uint64_t bits =
-            *reinterpret_cast<const uint64_t*>(base + C::MASK_OFF + w * 512 + n * 16 + 8 * c);
+        uint64_t bits = ~0ull;
+        if (partial)
+            bits = *reinterpret_cast<const uint64_t*>(smem + om + ST * C::MASKB + 8 * c);
 
-        f32x16 s[2], dp[2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            s[qb] = zero16();
-            dp[qb] = zero16();
-            const int row = 32 * qb + n;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int off = tile_off<D>(row, 2 * ks + g);
-                s[qb] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(Qs + off), kf[ks], s[qb]);
-                dp[qb] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(Ds + off), vf[ks], dp[qb]);
-            }
-        }
         bf16x8 pb[4], sb[4];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < 2; ++qb) {
+            f32x16 sc = zero16(), dp = zero16();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int imm = ST * C::MAT + qb * 32 * C::ROWB;
+                sc = mfma_32x32x16(lds16(smem, oq[ks], imm), kf[ks], sc);
+                dp = mfma_32x32x16(lds16(smem, od[ks], imm), vf[ks], dp);
+            }
+            const uint32_t bw = (uint32_t)(bits >> (32 * qb + 4 * g));
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                const int r4 = 32 * qb + 8 * q4 + 4 * g;  // rows r4 .. r4+3 of the chunk
-                const float4 l4 = *reinterpret_cast<const float4*>(Ls + r4);
-                const float4 d4 = *reinterpret_cast<const float4*>(Dl + r4);
+                const int imm = ST * 512 + (32 * qb + 8 * q4) * 4;  // rows 32qb+8q4+4g..+3
+                const float4 l4 = *reinterpret_cast<const float4*>(smem + ol + imm);
+                const float4 d4 = *reinterpret_cast<const float4*>(smem + ol + imm + 256);
                 const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
                 const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
                 for (int e2 = 0; e2 < 4; ++e2) {
                     const int j = 4 * q4 + e2;
-                    float pv = fast_exp2(s[qb][j] * scale_log2 - lv[e2]);
-                    if (!((bits >> (r4 + e2)) & 1ull)) pv = 0.f;
+                    float pv = fast_exp2(fmaf(sc[j], scale_log2, -lv[e2]));
+                    if (partial && !((bw >> (8 * q4 + e2)) & 1u)) pv = 0.f;
                     pb[2 * qb + (j >> 3)][j & 7] = (bf16)pv;
-                    sb[2 * qb + (j >> 3)][j & 7] = (bf16)(pv * (dp[qb][j] - dl[e2]));
+                    sb[2 * qb + (j >> 3)][j & 7] = (bf16)(pv * (dp[j] - dl[e2]));
                 }
             }
+        }
         // dV^T += dO^T P and dK^T += Q^T dS over 4 k-steps of 16 rows.  The lane's 8
         // rows in k-step qs are 16qs + 4g + {0..3} and 16qs + 8 + 4g + {0..3}.
-        const int r_in = lane & 15;
-        const int dh = (lane >> 4) & 1;
 #pragma unroll
-        for (int qs = 0; qs < 4; ++qs) {
-            const int rowa = 16 * qs + 4 * g + (r_in >> 2);
+        for (int qs = 0; qs < 4; ++qs)
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const int col = db * 32 + 16 * dh + 4 * (r_in & 3);
-                const int oa = tile_off<D>(rowa, col >> 3) + (col & 7) * 2;
-                const int ob = tile_off<D>(rowa + 8, col >> 3) + (col & 7) * 2;
-                const bf16x8 ado = cat(ld8_tr(Ds + oa), ld8_tr(Ds + ob));
-                const bf16x8 aq = cat(ld8_tr(Qs + oa), ld8_tr(Qs + ob));
+                const int imm = ST * C::MAT + 16 * qs * C::ROWB;
+                const bf16x8 ado = cat(lds8_tr(smem, odt[db][0], imm), lds8_tr(smem, odt[db][1], imm));
+                const bf16x8 aq = cat(lds8_tr(smem, oqt[db][0], imm), lds8_tr(smem, oqt[db][1], imm));
                 dv[db] = mfma_32x32x16(ado, pb[qs], dv[db]);
                 dk[db] = mfma_32x32x16(aq, sb[qs], dk[db]);
             }
-        }
+    };
+
+    if (n_it > 0) issue(ic<0>{}, 0);
+    if (n_it > 1) issue(ic<1>{}, 1);
+    for (int it = 0; it < n_it; it += 3) {
+        step(ic<0>{}, it);
+        if (it + 1 < n_it) step(ic<1>{}, it + 1);
+        if (it + 2 < n_it) step(ic<2>{}, it + 2);
     }
 
     if (key < T) {
@@ -286,11 +306,11 @@ __global__ __launch_bounds__(256 * HPW, 1) void dq_bf16_kernel(
     DevPlan P, int Hq, int Hkv, float scale, float scale_log2, const bf16* __restrict__ Q,
     const bf16* __restrict__ K, const bf16* __restrict__ V, const bf16* __restrict__ dO,
     const float* __restrict__ ws, bf16* __restrict__ dQ) {
-    using S = KvStage<D>;
+    using L = KvLayout<D>;
     constexpr int NTHR = 256 * HPW;
     constexpr int KS = D / 16, DB = D / 32;
-    constexpr int PER_STAGE = 2 * (S::MAT / (16 * NTHR)) + 1;
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[S::NST * S::BYTES];
+    constexpr int PER_STAGE = 2 * (L::MAT / (16 * NTHR)) + 1;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[L::BYTES];
 
     const int G = Hq / Hkv;
     int grp, hp;
@@ -323,59 +343,71 @@ __global__ __launch_bounds__(256 * HPW, 1) void dq_bf16_kernel(
         settle(df[ks]);
     }
     asm volatile("" ::"v"(lse2), "v"(dlt));
+
+    KvOffsets<D> off;
+    off.init(lane);
+    int offv[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) offv[ks] = off.k[ks] - L::K0 + L::V0;
+    const int off_mask = L::M0 + rr * 8;
+
     f32x16 dq[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) dq[db] = zero16();
 
     const int p0 = ld_const(P.qt_ptr + qt), p1 = ld_const(P.qt_ptr + qt + 1);
     const int n_it = p1 - p0;
-    auto issue = [&](int it) {
+    auto issue = [&](auto st_c, int it) {
         const int2 pr = ld_const(P.q_pairs + p0 + it);
-        issue_kv_stage<D, NTHR>(smem_base + (it % S::NST) * S::BYTES, K, V, P.mask_rows, pr.x,
-                                pr.y >= 0 ? pr.y : P.n_partial, T, kvh, kvstride, tid, w, lane);
+        issue_kv_stage<D, NTHR, decltype(st_c)::value>(smem_base, K, V, P.mask_rows, pr.x,
+                                                        pr.y >= 0 ? pr.y : P.n_partial, T, kvh,
+                                                        kvstride, tid, w, lane);
     };
-    if (n_it > 0) issue(0);
-    if (n_it > 1) issue(1);
-    const int r_in = lane & 15, dh = (lane >> 4) & 1;
-    for (int it = 0; it < n_it; ++it) {
+    auto step = [&](auto st_c, int it) {
+        constexpr int ST = decltype(st_c)::value;
         if (it + 1 < n_it) wait_vmem<PER_STAGE>();
         else wait_vmem<0>();
         barrier();
-        if (it + 2 < n_it) issue(it + 2);
-        const unsigned char* base = smem + (it % S::NST) * S::BYTES;
-        const unsigned char* Ks = base;
-        const unsigned char* Vs = base + S::MAT;
-        const uint64_t bits = *reinterpret_cast<const uint64_t*>(base + S::MASK_OFF + rr * 8);
+        if (it + 2 < n_it) issue(ic<(ST + 2) % 3>{}, it + 2);
+        const bool partial = ld_const(P.q_pairs + p0 + it).y >= 0;
+        uint64_t bits = ~0ull;
+        if (partial) bits = *reinterpret_cast<const uint64_t*>(smem + off_mask + ST * L::MASKB);
 
         bf16x8 sb[4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {  // one 32-key block at a time (register pressure)
-            f32x16 s = zero16(), dp = zero16();
+            f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const int off = tile_off<D>(kb * 32 + n, 2 * ks + g);
-                s = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(Ks + off), qf[ks], s);
-                dp = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(Vs + off), df[ks], dp);
+                const int imm = ST * L::MAT + kb * 32 * L::ROWB;
+                sc = mfma_32x32x16(lds16(smem, off.k[ks], imm), qf[ks], sc);
+                dp = mfma_32x32x16(lds16(smem, offv[ks], imm), df[ks], dp);
             }
+            const uint32_t bw = (uint32_t)(bits >> (32 * kb + 4 * g));
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const int x = kb * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-                float p = fast_exp2(s[j] * scale_log2 - lse2);
-                if (!((bits >> x) & 1ull)) p = 0.f;
+                float p = fast_exp2(fmaf(sc[j], scale_log2, -lse2));
+                if (partial && !((bw >> (8 * (j >> 2) + (j & 3))) & 1u)) p = 0.f;
                 sb[kb * 2 + (j >> 3)][j & 7] = (bf16)(p * (dp[j] - dlt));
             }
         }
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int rowa = 16 * kk + 4 * g + (r_in >> 2);
+        for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const int col = db * 32 + 16 * dh + 4 * (r_in & 3);
-                const bf16x8 a = cat(ld8_tr(Ks + tile_off<D>(rowa, col >> 3) + (col & 7) * 2),
-                                     ld8_tr(Ks + tile_off<D>(rowa + 8, col >> 3) + (col & 7) * 2));
+                const int imm = ST * L::MAT + 16 * kk * L::ROWB;
+                const bf16x8 a = cat(lds8_tr(smem, off.kt[db][0], imm),
+                                     lds8_tr(smem, off.kt[db][1], imm));
                 dq[db] = mfma_32x32x16(a, sb[kk], dq[db]);
             }
-        }
+    };
+
+    if (n_it > 0) issue(ic<0>{}, 0);
+    if (n_it > 1) issue(ic<1>{}, 1);
+    for (int it = 0; it < n_it; it += 3) {
+        step(ic<0>{}, it);
+        if (it + 1 < n_it) step(ic<1>{}, it + 1);
+        if (it + 2 < n_it) step(ic<2>{}, it + 2);
     }
 
     if (row < T) {
@@ -591,8 +623,7 @@ static void dq_launch(bool bf16_, const DevPlan& p, int Hq, int Hkv, float scale
                       const void* k, const void* v, const void* dout, const float* ws, void* dq,
                       hipStream_t s) {
     if (bf16_) {
-        // Two heads per workgroup do not fit the register file at D = 128.
-        if (D == 64 && (Hq / Hkv) % 2 == 0)
+        if ((Hq / Hkv) % 2 == 0)
             dq_bf16_launch<D, 2>(p, Hq, Hkv, scale, q, k, v, dout, ws, dq, s);
         else
             dq_bf16_launch<D, 1>(p, Hq, Hkv, scale, q, k, v, dout, ws, dq, s);

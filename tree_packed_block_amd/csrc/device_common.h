@@ -133,13 +133,17 @@ __device__ __forceinline__ bf16x4 ld8_tr(const void* lds_addr) {
 }
 
 // 16-byte slot holding chunk `chunk` (8 elements) of row `row` in a row-major LDS tile
-// of 16-bit elements with D columns, XOR-swizzled so that 16 lanes reading the same
-// chunk of 16 consecutive rows, and 16 lanes reading 4 consecutive rows in transposed
-// fashion, hit distinct banks.
+// of 16-bit elements with D columns, XOR-swizzled by a function of the row's low bits
+// so that (a) 16 lanes reading the same chunk of 16 consecutive rows and (b) 16 lanes
+// reading 4 chunks of 4 consecutive rows (the transposed reads) hit distinct banks.
+template <int D>
+__host__ __device__ constexpr int swz_key(int row) {
+    if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
 template <int D>
 __device__ __forceinline__ int swz(int row, int chunk) {
-    if constexpr (D == 128) return chunk ^ ((2 * (row & 7)) | ((row >> 3) & 1));
-    else return chunk ^ ((row >> 1) & 7);
+    return chunk ^ swz_key<D>(row);
 }
 template <int D>
 __device__ __forceinline__ int tile_off(int row, int chunk) {  // byte offset

@@ -30,11 +30,15 @@ __global__ __launch_bounds__(256 * HPW, 1) void fwd_bf16_kernel(
     DevPlan P, int Hq, int Hkv, float scale_log2, const bf16* __restrict__ Q,
     const bf16* __restrict__ K, const bf16* __restrict__ V, bf16* __restrict__ O,
     float* __restrict__ LSE) {
-    using S = KvStage<D>;
+    using L = KvLayout<D>;
     constexpr int NTHR = 256 * HPW;
     constexpr int KS = D / 16, DB = D / 32;
-    constexpr int PER_STAGE = 2 * (S::MAT / (16 * NTHR)) + 1;
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[S::NST * S::BYTES];
+    constexpr int PER_STAGE = 2 * (L::MAT / (16 * NTHR)) + 1;
+    // A row's running max moves only when a tile exceeds it by more than 2^8 (log2
+    // units): probabilities stay below 256, and the final division by the running sum
+    // makes the result independent of where the max was taken.
+    constexpr float kLazy = 8.f;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[L::BYTES];
 
     const int G = Hq / Hkv;
     int grp, hp;
@@ -59,6 +63,10 @@ __global__ __launch_bounds__(256 * HPW, 1) void fwd_bf16_kernel(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) settle(qf[ks]);
 
+    KvOffsets<D> off;
+    off.init(lane);
+    const int off_mask = L::M0 + rr * 8;
+
     f32x16 o[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = zero16();
@@ -66,76 +74,82 @@ __global__ __launch_bounds__(256 * HPW, 1) void fwd_bf16_kernel(
 
     const int p0 = ld_const(P.qt_ptr + qt), p1 = ld_const(P.qt_ptr + qt + 1);
     const int n_it = p1 - p0;
-    auto issue = [&](int it) {
+    auto issue = [&](auto st_c, int it) {
         const int2 pr = ld_const(P.q_pairs + p0 + it);
-        issue_kv_stage<D, NTHR>(smem_base + (it % S::NST) * S::BYTES, K, V, P.mask_rows, pr.x,
-                                pr.y >= 0 ? pr.y : P.n_partial, T, kvh, kvstride, tid, w, lane);
+        issue_kv_stage<D, NTHR, decltype(st_c)::value>(smem_base, K, V, P.mask_rows, pr.x,
+                                                        pr.y >= 0 ? pr.y : P.n_partial, T, kvh,
+                                                        kvstride, tid, w, lane);
     };
-    if (n_it > 0) issue(0);
-    if (n_it > 1) issue(1);
-    const int r_in = lane & 15, dh = (lane >> 4) & 1;
-    for (int it = 0; it < n_it; ++it) {
+
+    auto step = [&](auto st_c, int it) {
+        constexpr int ST = decltype(st_c)::value;
         if (it + 1 < n_it) wait_vmem<PER_STAGE>();
         else wait_vmem<0>();
         barrier();
-        if (it + 2 < n_it) issue(it + 2);
-        const unsigned char* base = smem + (it % S::NST) * S::BYTES;
-        const unsigned char* Ks = base;
-        const unsigned char* Vs = base + S::MAT;
-        const uint64_t bits = *reinterpret_cast<const uint64_t*>(base + S::MASK_OFF + rr * 8);
+        if (it + 2 < n_it) issue(ic<(ST + 2) % 3>{}, it + 2);
+        const bool partial = ld_const(P.q_pairs + p0 + it).y >= 0;
 
         // S^T (64 keys x 32 queries) = K Q^T, two 32-key blocks.
         f32x16 s[2];
+        s[0] = zero16();
+        s[1] = zero16();
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = zero16();
+        for (int ks = 0; ks < KS; ++ks) {
+            s[0] = mfma_32x32x16(lds16(smem, off.k[ks], ST * L::MAT), qf[ks], s[0]);
+            s[1] = mfma_32x32x16(lds16(smem, off.k[ks], ST * L::MAT + 32 * L::ROWB), qf[ks], s[1]);
+        }
+        if (partial) {
+            const uint64_t bits =
+                *reinterpret_cast<const uint64_t*>(smem + off_mask + ST * L::MASKB);
+            const uint32_t b0 = (uint32_t)(bits >> (4 * g)), b1 = (uint32_t)(bits >> (32 + 4 * g));
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                s[kb] = mfma_32x32x16(
-                    *reinterpret_cast<const bf16x8*>(Ks + tile_off<D>(kb * 32 + n, 2 * ks + g)),
-                    qf[ks], s[kb]);
+            for (int j = 0; j < 16; ++j) {
+                const int x = 8 * (j >> 2) + (j & 3);
+                if (!((b0 >> x) & 1u)) s[0][j] = -INFINITY;
+                if (!((b1 >> x) & 1u)) s[1][j] = -INFINITY;
+            }
         }
         float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fmaxf(s[0][j], s[1][j]));
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+        if (__any(mx > m + kLazy)) {
+            const float mnew = fmaxf(m, mx);
+            const float alpha = fast_exp2(m - mnew);
+            m = mnew;
+            l *= alpha;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int x = kb * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-                const float t = ((bits >> x) & 1ull) ? s[kb][j] * scale_log2 : -INFINITY;
-                s[kb][j] = t;
-                mx = fmaxf(mx, t);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m, mx);
-        const float alpha = fast_exp2(m - mnew);
-        m = mnew;
-        l *= alpha;
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+                for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+        }
         bf16x8 pf[4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const float pv = fast_exp2(s[kb][j] - mnew);
+                const float pv = fast_exp2(fmaf(s[kb][j], scale_log2, -m));
                 l += pv;
                 pf[kb * 2 + (j >> 3)][j & 7] = (bf16)pv;
             }
         // O^T += V^T P^T over 4 k-steps of 16 keys; the lane's 8 keys in k-step kk are
         // 16kk + 4g + {0..3} and 16kk + 8 + 4g + {0..3}, read transposed from V.
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int rowa = 16 * kk + 4 * g + (r_in >> 2);
+        for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const int col = db * 32 + 16 * dh + 4 * (r_in & 3);
-                const bf16x8 a = cat(ld8_tr(Vs + tile_off<D>(rowa, col >> 3) + (col & 7) * 2),
-                                     ld8_tr(Vs + tile_off<D>(rowa + 8, col >> 3) + (col & 7) * 2));
+                const bf16x8 a = cat(lds8_tr(smem, off.vt[db][0], ST * L::MAT + 16 * kk * L::ROWB),
+                                     lds8_tr(smem, off.vt[db][1], ST * L::MAT + 16 * kk * L::ROWB));
                 o[db] = mfma_32x32x16(a, pf[kk], o[db]);
             }
-        }
+    };
+
+    if (n_it > 0) issue(ic<0>{}, 0);
+    if (n_it > 1) issue(ic<1>{}, 1);
+    for (int it = 0; it < n_it; it += 3) {
+        step(ic<0>{}, it);
+        if (it + 1 < n_it) step(ic<1>{}, it + 1);
+        if (it + 2 < n_it) step(ic<2>{}, it + 2);
     }
 
     l += __shfl_xor(l, 32);

@@ -1,46 +1,92 @@
 // K/V tile staging shared by the forward and dQ kernels (internal).
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
 namespace octo {
 
-// Stage layout shared by the forward and dQ kernels: one 64-key K tile, the V tile,
-// and the 128 row-mask words of the query tile (the all-ones mask when FULL).
+// LDS layout of the three stages, stage-major by kind so that every offset a lane
+// reads is a per-lane register plus a compile-time immediate below 64 KiB:
+// [K tile x 3][V tile x 3][row-mask words x 3].
 template <int D>
-struct KvStage {
-    static constexpr int MAT = 64 * D * 2;
-    static constexpr int MASK_OFF = 2 * MAT;
-    static constexpr int BYTES = MASK_OFF + 128 * 8;
-    static constexpr int NST = 3;
+struct KvLayout {
+    static constexpr int ROWB = D * 2;         // bytes per row
+    static constexpr int MAT = 64 * ROWB;      // one 64-key tile
+    static constexpr int NST = 3;              // stages in flight
+    static constexpr int K0 = 0;
+    static constexpr int V0 = NST * MAT;
+    static constexpr int M0 = 2 * NST * MAT;
+    static constexpr int MASKB = kBq * 8;      // 128 row words
+    static constexpr int BYTES = M0 + NST * MASKB;
 };
 
-// Copy K/V tile `kt` and the mask of pair `m` into the stage at LDS byte address
-// `base`: 64 rows of K and V (16 KiB each at D = 128, XOR-swizzled rows) and 1 KiB of
-// mask words.  Every wave issues the same number of copies: per thread
-// 2 * (64 * D * 2 / 16 / threads) + 1.
-template <int D, int NTHR>
-__device__ __forceinline__ void issue_kv_stage(unsigned base, const bf16* K, const bf16* V,
+template <int V>
+using ic = std::integral_constant<int, V>;
+
+// Copy K/V tile `kt` and the row masks of mask `m` into stage ST: 64 rows of K and V
+// (XOR-swizzled) and 1 KiB of mask words.  Every wave issues the same number of
+// copies: 2 * (64 * D * 2 / 16 / NTHR) + 1 per thread.
+template <int D, int NTHR, int ST>
+__device__ __forceinline__ void issue_kv_stage(unsigned smem_base, const bf16* K, const bf16* V,
                                                const uint64_t* mask_rows, int kt, int m, int T,
                                                int kvh, size_t kvstride, int tid, int w,
                                                int lane) {
+    using L = KvLayout<D>;
     constexpr int CPR = D / 8;
-    constexpr int NDMA = KvStage<D>::MAT / (16 * NTHR);
+    constexpr int NDMA = L::MAT / (16 * NTHR);
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
-        const int L = i * NTHR + tid;
-        const int rho = L / CPR, slot = L % CPR;
-        const int chunk = swz<D>(rho, slot);
+        const int li = i * NTHR + tid;
+        const int rho = li / CPR, slot = li % CPR;
+        const int chunk = swz<D>(rho, slot);  // the XOR swizzle is its own inverse
         const int key = min(kt * kBk + rho, T - 1);
         const size_t off = (size_t)key * kvstride + (size_t)kvh * D + 8 * chunk;
-        dma16(K + off, base + (i * NTHR + w * 64) * 16);
-        dma16(V + off, base + KvStage<D>::MAT + (i * NTHR + w * 64) * 16);
+        dma16(K + off, smem_base + L::K0 + ST * L::MAT + (i * NTHR + w * 64) * 16);
+        dma16(V + off, smem_base + L::V0 + ST * L::MAT + (i * NTHR + w * 64) * 16);
     }
     constexpr int LANES = 64 / (NTHR / 64);  // 16-byte pieces per wave for 1 KiB
     if (lane < LANES)
         dma16(mask_rows + (size_t)m * kBq + 2 * (w * LANES + lane),
-              base + KvStage<D>::MASK_OFF + w * LANES * 16);
+              smem_base + L::M0 + ST * L::MASKB + w * LANES * 16);
+}
+
+// Per-lane byte offsets (relative to the LDS base) of the operands a wave reads from
+// one stage, for query rows owned as S^T = K Q^T columns (lane n = l % 32, g = l / 32).
+template <int D>
+struct KvOffsets {
+    static constexpr int KS = D / 16, DB = D / 32;
+    int k[KS];      // A operand of S^T (row n, chunk 2ks+g); +32 rows: + 32 * ROWB
+    int kt[DB][2];  // transposed A operand from the K tile; +16 rows per k-step
+    int vt[DB][2];  // the same from the V tile
+    __device__ __forceinline__ void init(int lane) {
+        using L = KvLayout<D>;
+        const int n = lane & 31, g = lane >> 5, r_in = lane & 15, dh = (lane >> 4) & 1;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            k[ks] = L::K0 + n * L::ROWB + (((2 * ks + g) ^ swz_key<D>(n)) * 16);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int row = 4 * g + (r_in >> 2) + 8 * hf;
+                const int chunk = 4 * db + 2 * dh + ((r_in & 3) >> 1);
+                const int off = row * L::ROWB + ((chunk ^ swz_key<D>(row)) * 16) + 8 * (r_in & 1);
+                kt[db][hf] = L::K0 + off;
+                vt[db][hf] = L::V0 + off;
+            }
+    }
+};
+
+// LDS reads at a per-lane offset plus a constant (folded into the instruction's
+// immediate offset once loops are unrolled).
+__device__ __forceinline__ bf16x8 lds16(const unsigned char* smem, int lane_off, int imm) {
+    return *reinterpret_cast<const bf16x8*>(smem + lane_off + imm);
+}
+__device__ __forceinline__ bf16x4 lds8_tr(const unsigned char* smem, int lane_off, int imm) {
+    return ld8_tr(smem + lane_off + imm);
 }
 
 }  // namespace octo
