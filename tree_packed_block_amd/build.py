@@ -30,6 +30,8 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+# Per-source code-generation options.
+HIP_FILE_FLAGS: dict = {}
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
              "-D__HIP_PLATFORM_AMD__"]
 
@@ -45,19 +47,21 @@ def _run(cmd):
     return r.stdout
 
 
-def build(verbose: bool = False, extra_cxx=(), out=LIB) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    inc = ["-I" + INCLUDE, "-I" + CSRC]
+def build(verbose: bool = False, extra_cxx=(), out=LIB, extra_hip=(), csrc=CSRC,
+          build_dir=BUILD) -> str:
+    os.makedirs(build_dir, exist_ok=True)
+    inc = ["-I" + INCLUDE, "-I" + csrc]
     jobs = []
     objs = []
     for src in HIP_SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        jobs.append([_hipcc(), *HIPCC_FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
+        jobs.append([_hipcc(), *HIPCC_FLAGS, *HIP_FILE_FLAGS.get(src, ()), *extra_hip, *inc,
+                     "-c", os.path.join(csrc, src), "-o", obj])
         objs.append(obj)
     for src in CXX_SOURCES:
-        obj = os.path.join(BUILD, src.replace(".cpp", ".o"))
+        obj = os.path.join(build_dir, src.replace(".cpp", ".o"))
         jobs.append(["g++", *CXX_FLAGS, *extra_cxx, *inc, "-I" + os.path.join(ROCM, "include"),
-                     "-c", os.path.join(CSRC, src), "-o", obj])
+                     "-c", os.path.join(csrc, src), "-o", obj])
         objs.append(obj)
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         logs = list(ex.map(_run, jobs))

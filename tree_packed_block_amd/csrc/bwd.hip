@@ -78,19 +78,26 @@ __global__ __launch_bounds__(256) void preprocess_fp32_kernel(int T, int Tp, int
 
 // ------------------------------------------------------------------ dK / dV (bf16)
 //
-// Workgroup = (128-key block = KV tiles 2b and 2b+1, KV head), 4 wave64s; wave w owns
-// keys 32w .. 32w+31 of the block (tile 2b for w < 2).  The workgroup walks the
-// block's merged list of query tiles; for every entry, every query head of the group
-// and each 64-row half of the query tile, the Q and dO rows (and their LSE2/Delta) are
-// copied global -> LDS asynchronously (three stages in flight) and all four waves
-// consume them: S = Q K^T and dP = dO V^T with K and V register-resident B operands, so
-// a lane owns one key column; P and dS then serve directly as B operands of
-// dV^T += dO^T P and dK^T += Q^T dS, whose A operands are read transposed straight
-// from the row-major Q and dO tiles (ds_read_b64_tr_b16).  Every dK/dV row has one
-// writer; there are no atomics and no cross-wave reduction.
+// Workgroup = (128-key block = KV tiles 2b and 2b+1, KV head), 4 wave64s in two pairs;
+// pair p owns the 64 keys of tile 2b+p, and inside a pair wave 0 accumulates dK and
+// wave 1 dV for all 64 keys.  The workgroup walks the block's merged list of query
+// tiles; for every entry, every query head of the group and each 64-row half of the
+// query tile, the Q and dO rows (and their LSE2/Delta) are copied global -> LDS
+// asynchronously (three stages in flight).  In a pair each wave takes 32 of the 64
+// rows: S = Q K^T and dP = dO V^T for its rows against the pair's 64 keys (K and V are
+// register-resident B operands, so a lane owns one key column per 32-key block), then
+// P and dS.  The dK wave hands its P rows to the dV wave and receives the dV wave's dS
+// rows through LDS, after which dV^T += dO^T P and dK^T += Q^T dS run over all 64 rows
+// with A operands read transposed from the row-major tiles (ds_read_b64_tr_b16).  Each
+// A operand read from LDS thus feeds two MFMAs (two 32-key blocks), which halves LDS
+// traffic per MFMA against one wave per 32 keys.  The row terms enter the MFMA as one
+// extra k-step: a lane's own row value (-LSE2/(scale log2 e) for S, -Delta for dP) is
+// split into three bf16 parts that multiply a column of ones, so the accumulators come
+// out as S - LSE/scale and dP - Delta without any per-element loads.  Every dK/dV row
+// has one writer; there are no atomics.
 
 // LDS layout of the dK/dV stages, stage-major by kind: [Q x 3][dO x 3][LSE2/Delta x 3]
-// [key-major mask words x 3], so lane reads are a register plus an immediate.
+// [key-major mask words x 3], then one 4 KiB hand-over buffer per wave.
 template <int D>
 struct DkdvLayout {
     static constexpr int ROWB = D * 2;               // bytes per row
@@ -100,89 +107,119 @@ struct DkdvLayout {
     static constexpr int Q0 = 0;
     static constexpr int D0 = NST * MAT;
     static constexpr int L0 = 2 * NST * MAT;         // LSE2[64] then Delta[64] per stage
-    static constexpr int M0 = L0 + NST * 512;        // per wave: 32 keys x 2 words
+    static constexpr int M0 = L0 + NST * 512;        // 2 tiles x 64 keys x 2 words
     static constexpr int MASKB = 4 * 512;
-    static constexpr int BYTES = M0 + NST * MASKB;
+    static constexpr int X0 = M0 + NST * MASKB;      // hand-over: 4 B operands per wave
+    static constexpr int BYTES = X0 + 4 * 4096;
     static constexpr int PER_STAGE = 2 * NDMA + 2;   // copies per wave per stage
 };
 
-template <int D>
-__global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
-    DevPlan P, int Hq, int Hkv, float scale, float scale_log2, const bf16* __restrict__ Q,
-    const bf16* __restrict__ K, const bf16* __restrict__ V, const bf16* __restrict__ dO,
-    const float* __restrict__ ws, bf16* __restrict__ dK, bf16* __restrict__ dV) {
+// x as the sum of three bf16 values (the error is below 2^-24 |x|), in slots 0..2 of
+// an MFMA operand; lanes of the upper half (k values 8..15) carry zeros.
+__device__ __forceinline__ bf16x8 split3(float x, bool on) {
+    x = on ? fmaxf(x, -1e30f) : 0.f;  // a padded row's -inf becomes a finite -1e30
+    const bf16 h = (bf16)x;
+    const float r1 = x - (float)h;
+    const bf16 m = (bf16)r1;
+    const bf16 l = (bf16)(r1 - (float)m);
+    bf16x8 v = zero8();
+    v[0] = h;
+    v[1] = m;
+    v[2] = l;
+    return v;
+}
+
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// One wave of a dK/dV workgroup.  ROLE 0 accumulates dK (and hands P to its partner),
+// ROLE 1 accumulates dV (and hands dS over).  Both roles run the same sequence of
+// barriers.
+template <int D, int ROLE>
+__device__ __forceinline__ void dkdv_wave(const DevPlan& P, int Hq, int Hkv, int kb, int kvh,
+                                          float scale, float scale_log2,
+                                          const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                                          const bf16* __restrict__ V, const bf16* __restrict__ dO,
+                                          const float* __restrict__ ws, bf16* __restrict__ out,
+                                          unsigned char* smem) {
     using C = DkdvLayout<D>;
     constexpr int KS = D / 16, DB = D / 32, CPR = D / 8;
-    constexpr int M = 4;  // consecutive blocks of one KV head dealt to one XCD
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[C::BYTES];
-
-    int grp, mm;
-    if (!xcd_group(blockIdx.x, M, (P.nKB + M - 1) / M * Hkv, grp, mm)) return;
-    const int rank = (grp / Hkv) * M + mm;
-    if (rank >= P.nKB) return;
-    const int kvh = grp % Hkv;
-    const int kb = ld_const(P.blk_order + rank);
-
     const int T = P.T, G = Hq / Hkv, Tp = padded_rows(T);
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int pr = w >> 1;                                    // pair = KV tile 2kb+pr
     const int n = lane & 31, g = lane >> 5;
-    const int key = kb * 128 + 32 * w + n;
-    const bool hi_tile = w >= 2;
+    const int key0 = kb * 128 + 64 * pr + n;                  // + 32 per key block
     const size_t qstride = (size_t)Hq * D, kvstride = (size_t)Hkv * D;
     const float* LSE2 = ws;
     const float* DEL = ws + (size_t)Hq * Tp;
     const unsigned smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+    const float inv_sl2 = 1.f / scale_log2;
 
-    bf16x8 kf[KS], vf[KS];
+    // K enters the scores pre-multiplied by scale * log2(e) (rounded to bf16), so the
+    // S accumulator is directly the exponent of P.
+    bf16x8 kf[2][KS], vf[2][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const size_t off = (size_t)key * kvstride + (size_t)kvh * D + 16 * ks + 8 * g;
-        kf[ks] = key < T ? ld16(K + off) : zero8();
-        vf[ks] = key < T ? ld16(V + off) : zero8();
-    }
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        settle(kf[ks]);
-        settle(vf[ks]);
-    }
-    f32x16 dk[DB], dv[DB];
+        for (int ks = 0; ks < KS; ++ks) {
+            const int key = key0 + 32 * kk;
+            const size_t off = (size_t)key * kvstride + (size_t)kvh * D + 16 * ks + 8 * g;
+            const bf16x8 kr = key < T ? ld16(K + off) : zero8();
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-        dk[db] = zero16();
-        dv[db] = zero16();
-    }
+            for (int e = 0; e < 8; ++e) kf[kk][ks][e] = (bf16)((float)kr[e] * scale_log2);
+            vf[kk][ks] = key < T ? ld16(V + off) : zero8();
+        }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            settle(kf[kk][ks]);
+            park(vf[kk][ks]);
+        }
+    bf16x8 ones = zero8();
+    if (g == 0) ones[0] = ones[1] = ones[2] = (bf16)1.f;
 
-    // Per-lane LDS offsets: row n (+32 per query block) chunk 2ks+g of Q and dO, and
-    // the transposed reads (rows 4g + r/4 (+8), +16 per k-step) of both.
+    f32x16 acc[2][DB];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[kk][db] = zero16();
+
+    // Per-lane LDS offsets.  Row-major reads: row n of this wave's 32 rows, chunk 2ks+g
+    // (the wave's +32 rows and the stage go into the immediate).  Transposed reads:
+    // rows 4g + r/4 (+8) of each 16-row k-step of Q (ROLE 0) or dO (ROLE 1).
     const int r_in = lane & 15, dh = (lane >> 4) & 1;
-    int oq[KS], od[KS], oqt[DB][2], odt[DB][2];
+    int oq[KS], ot[DB][2];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < KS; ++ks)
         oq[ks] = C::Q0 + n * C::ROWB + (((2 * ks + g) ^ swz_key<D>(n)) * 16);
-        od[ks] = oq[ks] - C::Q0 + C::D0;
-    }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const int r = 4 * g + (r_in >> 2) + 8 * hf;
             const int chunk = 4 * db + 2 * dh + ((r_in & 3) >> 1);
-            const int o2 = r * C::ROWB + ((chunk ^ swz_key<D>(r)) * 16) + 8 * (r_in & 1);
-            oqt[db][hf] = C::Q0 + o2;
-            odt[db][hf] = C::D0 + o2;
+            ot[db][hf] = (ROLE == 0 ? C::Q0 : C::D0) + r * C::ROWB +
+                         ((chunk ^ swz_key<D>(r)) * 16) + 8 * (r_in & 1);
         }
-    const int ol = C::L0 + 16 * g;                      // LSE2 rows 4g.. of each 8-row group
-    const int om = C::M0 + w * 512 + n * 16;            // this key's two mask words
+    const int ol = C::L0 + (32 * ROLE + n) * 4;          // this lane's row: LSE2, +256 Delta
+    const int om = C::M0 + pr * 1024 + n * 16 + 4 * ROLE; // + 512 kk + 8 c: 32 mask bits
+    const int ox = C::X0 + w * 4096 + lane * 16;          // own hand-over slots
+    const int ox_in = C::X0 + (w ^ 1) * 4096 + lane * 16; // partner's
 
     const int e0 = ld_const(P.blk_ptr + kb), e1 = ld_const(P.blk_ptr + kb + 1);
     const int n_it = (e1 - e0) * G * 2;  // (entry, head, 64-row half)
+    if (n_it == 0) return;
+    const int n_run = (n_it + 2) / 3 * 3;  // iterations run: whole rounds of 3 stages
 
     // Copies of iteration `it` into stage ST: the 64 rows of Q and dO, their LSE2 and
-    // Delta, and this wave's 32 key-major mask words (all ones when FULL or unseen).
+    // Delta, and this wave's 32 key-major mask words (the all-ones mask for a FULL tile,
+    // the all-zeros one for a tile the query tile does not see and for the padding
+    // iterations it >= n_it, which repeat the last entry and so contribute nothing).
     auto issue = [&](auto st_c, int it) {
         constexpr int ST = decltype(st_c)::value;
-        const int e = e0 + it / (2 * G);
+        const bool pad = it >= n_it;
+        const int e = min(e0 + it / (2 * G), e1 - 1);
         const int hh = (it >> 1) % G, c = it & 1;
         const int h = kvh * G + hh;
         const int4 ent = ld_const(P.blk_entries + e);
@@ -203,103 +240,172 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
             dma16(src, smem_base + C::L0 + ST * 512 + 8 * w * 16);
         }
         if (lane < 32) {
-            int mk = hi_tile ? ent.z : ent.y;
-            if (mk < 0) mk = P.n_partial;
+            int mk = pr ? ent.z : ent.y;
+            mk = pad || mk == -2 ? P.n_partial + 1 : (mk == -1 ? P.n_partial : mk);
             dma16(P.mask_cols + ((size_t)mk * kBk + 32 * (w & 1) + lane) * 2,
                   smem_base + C::M0 + ST * C::MASKB + w * 512);
         }
     };
 
+    // One iteration: S, dP, P and dS for this wave's 32 rows, the hand-over, then dV or
+    // dK over all 64 rows.
     auto step = [&](auto st_c, int it) {
         constexpr int ST = decltype(st_c)::value;
-        if (it + 1 < n_it) wait_vmem<C::PER_STAGE>();
-        else wait_vmem<0>();
+        wait_vmem<C::PER_STAGE>();
+        wait_lds();
         barrier();
-        if (it + 2 < n_it) issue(ic<(ST + 2) % 3>{}, it + 2);
-        const int4 ent = ld_const(P.blk_entries + e0 + it / (2 * G));
-        const int mk = hi_tile ? ent.z : ent.y;
-        if (mk == -2) return;  // this wave's tile is not seen by the query tile
-        const bool partial = mk >= 0;
+        issue(ic<(ST + 2) % 3>{}, it + 2);
+        const int4 ent = ld_const(P.blk_entries + min(e0 + it / (2 * G), e1 - 1));
+        const int mk = pr ? ent.z : ent.y;
+        const bool masked = mk != -1 || it >= n_it;  // PARTIAL, unseen or padding
         const int c = it & 1;
-        uint64_t bits = ~0ull;
-        if (partial)
-            bits = *reinterpret_cast<const uint64_t*>(smem + om + ST * C::MASKB + 8 * c);
 
-        bf16x8 pb[4], sb[4];
+        const float l2 = *reinterpret_cast<const float*>(smem + ol + ST * 512);
+        const float dl = *reinterpret_cast<const float*>(smem + ol + ST * 512 + 256);
+        const bf16x8 xl = split3(-l2, g == 0);
+        const bf16x8 xd = split3(-dl, g == 0);
+        // A operands: all eight Q k-steps are read first, the dO k-steps one per pair
+        // of S MFMAs, so the reads run ahead of the MFMAs that consume them.
+        bf16x8 aq[KS], ad[KS];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            f32x16 sc = zero16(), dp = zero16();
+        for (int ks = 0; ks < KS; ++ks)
+            aq[ks] = lds16(smem, oq[ks], ST * C::MAT + ROLE * 32 * C::ROWB);
+        f32x16 sc[2], dp[2];
+        // S (exponent of P: scale log2e Q K^T - LSE2), then dP - Delta.
+        sc[0] = sc[1] = mfma_32x32x16(xl, ones, zero16());
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int imm = ST * C::MAT + qb * 32 * C::ROWB;
-                sc = mfma_32x32x16(lds16(smem, oq[ks], imm), kf[ks], sc);
-                dp = mfma_32x32x16(lds16(smem, od[ks], imm), vf[ks], dp);
-            }
-            const uint32_t bw = (uint32_t)(bits >> (32 * qb + 4 * g));
+        for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int imm = ST * 512 + (32 * qb + 8 * q4) * 4;  // rows 32qb+8q4+4g..+3
-                const float4 l4 = *reinterpret_cast<const float4*>(smem + ol + imm);
-                const float4 d4 = *reinterpret_cast<const float4*>(smem + ol + imm + 256);
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-                const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
+            for (int kk = 0; kk < 2; ++kk) sc[kk] = mfma_32x32x16(aq[ks], kf[kk][ks], sc[kk]);
+            ad[ks] = lds16(smem, oq[ks] - C::Q0 + C::D0, ST * C::MAT + ROLE * 32 * C::ROWB);
+        }
+        dp[0] = dp[1] = mfma_32x32x16(xd, ones, zero16());
 #pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    const int j = 4 * q4 + e2;
-                    float pv = fast_exp2(fmaf(sc[j], scale_log2, -lv[e2]));
-                    if (partial && !((bw >> (8 * q4 + e2)) & 1u)) pv = 0.f;
-                    pb[2 * qb + (j >> 3)][j & 7] = (bf16)pv;
-                    sb[2 * qb + (j >> 3)][j & 7] = (bf16)(pv * (dp[j] - dl[e2]));
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) dp[kk] = mfma_32x32x16(ad[ks], vf[kk][ks], dp[kk]);
+        __builtin_amdgcn_sched_group_barrier(0x100, KS + 2, 0);  // LSE2, Delta, Q reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        // keep: the B operand this wave uses itself (dS for dK, P for dV); give: the
+        // partner's.  Index [kk][ql]: 32-key block, 16-row k-step of this wave's rows;
+        // slot e of lane (n, g) is row 16 ql + 4g + e (e < 4) or 16 ql + 8 + 4g + e - 4.
+        bf16x8 keep[2][2], give[2][2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float pv = fast_exp2(sc[kk][j]);
+                const float dsv = pv * dp[kk][j];
+                if constexpr (ROLE == 0) {
+                    keep[kk][j >> 3][j & 7] = (bf16)dsv;
+                    give[kk][j >> 3][j & 7] = (bf16)pv;
+                } else {
+                    keep[kk][j >> 3][j & 7] = (bf16)pv;
+                    give[kk][j >> 3][j & 7] = (bf16)dsv;
                 }
             }
+        if (__builtin_expect(masked, 0)) {  // wave-uniform and rare: clear P and dS where
+            asm volatile("");                  // the mask is 0 (a real branch, not selects)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const uint32_t mb = *reinterpret_cast<const uint32_t*>(
+                                        smem + om + ST * C::MASKB + 512 * kk + 8 * c) >> (4 * g);
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    if (!((mb >> (8 * (j >> 2) + (j & 3))) & 1u)) {
+                        keep[kk][j >> 3][j & 7] = (bf16)0.f;
+                        give[kk][j >> 3][j & 7] = (bf16)0.f;
+                    }
+            }
         }
-        // dV^T += dO^T P and dK^T += Q^T dS over 4 k-steps of 16 rows.  The lane's 8
-        // rows in k-step qs are 16qs + 4g + {0..3} and 16qs + 8 + 4g + {0..3}.
 #pragma unroll
-        for (int qs = 0; qs < 4; ++qs)
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int imm = ST * C::MAT + 16 * qs * C::ROWB;
-                const bf16x8 ado = cat(lds8_tr(smem, odt[db][0], imm), lds8_tr(smem, odt[db][1], imm));
-                const bf16x8 aq = cat(lds8_tr(smem, oqt[db][0], imm), lds8_tr(smem, oqt[db][1], imm));
-                dv[db] = mfma_32x32x16(ado, pb[qs], dv[db]);
-                dk[db] = mfma_32x32x16(aq, sb[qs], dk[db]);
+            for (int ql = 0; ql < 2; ++ql)
+                *reinterpret_cast<bf16x8*>(smem + ox + (2 * kk + ql) * 1024) = give[kk][ql];
+        // The A operands of the partner's rows are read before the hand-over barrier.
+        bf16x8 ap[DB][2];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int ql = 0; ql < 2; ++ql) {
+                const int imm = ST * C::MAT + (32 * (1 - ROLE) + 16 * ql) * C::ROWB;
+                ap[db][ql] = cat(lds8_tr(smem, ot[db][0], imm), lds8_tr(smem, ot[db][1], imm));
+            }
+        // This wave's own 32 rows while the partner finishes its hand-over.
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int ql = 0; ql < 2; ++ql) {
+                const int imm = ST * C::MAT + (32 * ROLE + 16 * ql) * C::ROWB;
+                const bf16x8 a = cat(lds8_tr(smem, ot[db][0], imm), lds8_tr(smem, ot[db][1], imm));
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    acc[kk][db] = mfma_32x32x16(a, keep[kk][ql], acc[kk][db]);
+            }
+        wait_lds();
+        barrier();
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int ql = 0; ql < 2; ++ql) {
+                const bf16x8 part = lds16(smem, ox_in, (2 * kk + ql) * 1024);
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    acc[kk][db] = mfma_32x32x16(ap[db][ql], part, acc[kk][db]);
             }
     };
 
-    if (n_it > 0) issue(ic<0>{}, 0);
-    if (n_it > 1) issue(ic<1>{}, 1);
-    for (int it = 0; it < n_it; it += 3) {
+    issue(ic<0>{}, 0);
+    issue(ic<1>{}, 1);
+    for (int it = 0; it < n_run; it += 3) {
         step(ic<0>{}, it);
-        if (it + 1 < n_it) step(ic<1>{}, it + 1);
-        if (it + 2 < n_it) step(ic<2>{}, it + 2);
+        step(ic<1>{}, it + 1);
+        step(ic<2>{}, it + 2);
     }
+    wait_vmem<0>();  // the trailing copies land before the workgroup's LDS is released
 
-    if (key < T) {
-        bf16* krow = dK + (size_t)key * kvstride + (size_t)kvh * D;
-        bf16* vrow = dV + (size_t)key * kvstride + (size_t)kvh * D;
+    const float os = ROLE == 0 ? scale : 1.f;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const int key = key0 + 32 * kk;
+        if (key >= T) continue;
+        bf16* row = out + (size_t)key * kvstride + (size_t)kvh * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                bf16x4 a, b;
+                bf16x4 a;
 #pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    a[e2] = (bf16)(scale * dk[db][4 * q4 + e2]);
-                    b[e2] = (bf16)dv[db][4 * q4 + e2];
-                }
-                st8(krow + db * 32 + 8 * q4 + 4 * g, a);
-                st8(vrow + db * 32 + 8 * q4 + 4 * g, b);
+                for (int e2 = 0; e2 < 4; ++e2) a[e2] = (bf16)(os * acc[kk][db][4 * q4 + e2]);
+                st8(row + db * 32 + 8 * q4 + 4 * g, a);
             }
     }
 }
 
-// ------------------------------------------------------------------ dQ (bf16)
-//
-// Workgroup = one query tile for HPW query heads of one KV group, wave = 32 query rows;
-// like the forward, S^T = K Q^T and dP^T = V dO^T put one query per lane, and dS^T is
-// the B operand of dQ^T += K^T dS^T, whose A operand is read transposed from the same
-// row-major K tile.  K/V tiles and row masks arrive through three asynchronous stages.
+template <int D>
+__global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
+    DevPlan P, int Hq, int Hkv, float scale, float scale_log2, const bf16* __restrict__ Q,
+    const bf16* __restrict__ K, const bf16* __restrict__ V, const bf16* __restrict__ dO,
+    const float* __restrict__ ws, bf16* __restrict__ dK, bf16* __restrict__ dV) {
+    constexpr int M = 4;  // consecutive blocks of one KV head dealt to one XCD
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[DkdvLayout<D>::BYTES];
+    int grp, mm;
+    if (!xcd_group(blockIdx.x, M, (P.nKB + M - 1) / M * Hkv, grp, mm)) return;
+    const int rank = (grp / Hkv) * M + mm;
+    if (rank >= P.nKB) return;
+    const int kvh = grp % Hkv;
+    const int kb = ld_const(P.blk_order + rank);
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1)
+        dkdv_wave<D, 1>(P, Hq, Hkv, kb, kvh, scale, scale_log2, Q, K, V, dO, ws, dV, smem);
+    else
+        dkdv_wave<D, 0>(P, Hq, Hkv, kb, kvh, scale, scale_log2, Q, K, V, dO, ws, dK, smem);
+}
 
 template <int D, int HPW>
 __global__ __launch_bounds__(256 * HPW, 1) void dq_bf16_kernel(

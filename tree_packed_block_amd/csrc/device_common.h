@@ -68,6 +68,11 @@ __device__ __forceinline__ int4 ld_const(const int4* p) {
 // re-check it against outstanding asynchronous copies).
 __device__ __forceinline__ void settle(const bf16x8& v) { asm volatile("" ::"v"(v)); }
 
+// Wait for v and move it to accumulation registers: MFMA reads its A and B operands
+// from either register file, and a loop-invariant operand kept there leaves the
+// architectural registers free for staging LDS reads ahead of the MFMAs.
+__device__ __forceinline__ void park(bf16x8& v) { asm volatile("" : "+a"(v)); }
+
 // 2^x on the hardware exponential unit (exact 0 for -inf).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -118,8 +123,13 @@ __device__ __forceinline__ void wait_vmem() {
 
 // Workgroup barrier without the implied memory fence of __syncthreads (which would
 // drain every outstanding load, prefetches included).  LDS written by regular stores
-// must be waited for (lgkmcnt) by the writer before it.
-__device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
+// must be waited for (lgkmcnt) by the writer before it.  The empty asm statements keep
+// the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // Transposed 8-byte LDS read (ds_read_b64_tr_b16).  In every group of 16 lanes,
 // lane i receives element i % 4 of the 8-byte rows addressed by lanes 4j + i / 4,

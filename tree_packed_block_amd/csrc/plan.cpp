@@ -322,9 +322,12 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     // One extra all-ones mask (index n_partial) that kernels may use for FULL tiles.
     p.mask_rows.insert(p.mask_rows.end(), (size_t)Bq * p.row_words, ~0ull);
 
-    // Key-major copy of every PARTIAL mask, for the KV-tile owners of the backward.
-    p.mask_cols.assign((p.n_partial + 1) * Bk * p.col_words, 0);
-    std::fill(p.mask_cols.begin() + p.n_partial * Bk * p.col_words, p.mask_cols.end(), ~0ull);
+    // Key-major copy of every PARTIAL mask, for the KV-tile owners of the backward, then
+    // an all-ones mask (index n_partial, FULL) and an all-zeros one (n_partial + 1, a
+    // tile that the query tile does not see).
+    p.mask_cols.assign((p.n_partial + 2) * Bk * p.col_words, 0);
+    std::fill(p.mask_cols.begin() + p.n_partial * Bk * p.col_words,
+              p.mask_cols.begin() + (p.n_partial + 1) * Bk * p.col_words, ~0ull);
     for (int64_t m = 0; m < p.n_partial; ++m) {
         const uint64_t* wr = &p.mask_rows[m * Bq * p.row_words];
         uint64_t* wc = &p.mask_cols[m * Bk * p.col_words];
