@@ -93,6 +93,54 @@ def cpu_baseline(dag, x, rows_per_part=768):
                       f"float64, {dt:.1f} s"}
 
 
+KERNEL_KEYS = (("fwd_bf16_kernel", "fwd"), ("preprocess_bf16_kernel", "bwd_preprocess"),
+               ("dkdv_bf16_kernel", "bwd_dkdv"), ("dq_bf16_kernel", "bwd_dq"),
+               ("decode_split_kernel", "decode"), ("decode_combine_kernel", "decode"))
+CALIBRATION_BYTES = 1 << 30  # the --calibrate-copy transfer
+
+
+def _counter_per_dispatch(csv_path: str, counter: str):
+    """{kernel name: [value per dispatch]} for one counter of a rocprofv3 CSV."""
+    import csv
+    out = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            out.setdefault(r["Kernel_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+            out[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {k: list(v.values()) for k, v in out.items()}
+
+
+def write_traffic(fetch_csv: str, write_csv: str) -> dict:
+    """profiles/traffic.json from two rocprofv3 --pmc runs of ``bench.py --calibrate-copy``
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch).  Each counter is scaled so that the
+    1 GiB device copy reads and writes exactly 1 GiB; values are averaged per launch of
+    each kernel of the step (decode = split + combine)."""
+    rec = {"source_digest": source_digest(), "kernels": {}, "calibration": {}}
+    for counter, path, field in (("FETCH_SIZE", fetch_csv, "fetch_bytes_per_launch"),
+                                 ("WRITE_SIZE", write_csv, "write_bytes_per_launch")):
+        per = _counter_per_dispatch(path, counter)
+        copies = [v for name, vals in per.items() if "copyBuffer" in name for v in vals]
+        if not copies:
+            raise SystemExit(f"{path}: no copy kernel to calibrate {counter} against")
+        factor = CALIBRATION_BYTES / (max(copies) * 1024.0)
+        rec["calibration"][counter] = {"copy_kib": max(copies), "bytes_per_kib": factor}
+        sums = {}
+        for name, vals in per.items():
+            for sub, key in KERNEL_KEYS:
+                if sub in name:
+                    avg = sum(vals) / len(vals) * 1024.0 * factor
+                    sums[key] = sums.get(key, 0.0) + avg
+        for key, v in sums.items():
+            rec["kernels"].setdefault(key, {})[field] = round(v)
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,7 +150,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (reference for HBM counters)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="only write profiles/traffic.json from two rocprofv3 counter CSVs")
     args = ap.parse_args()
+    if args.write_traffic:
+        print(json.dumps(write_traffic(*args.write_traffic), sort_keys=True))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)

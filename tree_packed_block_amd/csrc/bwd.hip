@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void preprocess_fp32_kernel(int T, int Tp, int
 // has one writer; there are no atomics.
 
 // LDS layout of the dK/dV stages, stage-major by kind: [Q x 3][dO x 3][LSE2/Delta x 3]
-// [key-major mask words x 3], then one 4 KiB hand-over buffer per wave.
+// [key-major mask words x 3], then two sets of 4 KiB hand-over buffers, one per wave.
 template <int D>
 struct DkdvLayout {
     static constexpr int ROWB = D * 2;               // bytes per row
@@ -109,8 +109,9 @@ struct DkdvLayout {
     static constexpr int L0 = 2 * NST * MAT;         // LSE2[64] then Delta[64] per stage
     static constexpr int M0 = L0 + NST * 512;        // 2 tiles x 64 keys x 2 words
     static constexpr int MASKB = 4 * 512;
-    static constexpr int X0 = M0 + NST * MASKB;      // hand-over: 4 B operands per wave
-    static constexpr int BYTES = X0 + 4 * 4096;
+    static constexpr int X0 = M0 + NST * MASKB;      // hand-over: 4 B operands per wave,
+    static constexpr int XB = 4 * 4096;              // two buffers by iteration parity
+    static constexpr int BYTES = X0 + 2 * XB;
     static constexpr int PER_STAGE = 2 * NDMA + 2;   // copies per wave per stage
 };
 
@@ -216,10 +217,12 @@ __device__ __forceinline__ void dkdv_wave(const DevPlan& P, int Hq, int Hkv, int
     // Delta, and this wave's 32 key-major mask words (the all-ones mask for a FULL tile,
     // the all-zeros one for a tile the query tile does not see and for the padding
     // iterations it >= n_it, which repeat the last entry and so contribute nothing).
+    // The entries are walked from the last query tile down: the key blocks of one branch
+    // then start on the same query tiles together and share them in L2.
     auto issue = [&](auto st_c, int it) {
         constexpr int ST = decltype(st_c)::value;
         const bool pad = it >= n_it;
-        const int e = min(e0 + it / (2 * G), e1 - 1);
+        const int e = max(e1 - 1 - it / (2 * G), e0);
         const int hh = (it >> 1) % G, c = it & 1;
         const int h = kvh * G + hh;
         const int4 ent = ld_const(P.blk_entries + e);
@@ -247,18 +250,42 @@ __device__ __forceinline__ void dkdv_wave(const DevPlan& P, int Hq, int Hkv, int
         }
     };
 
-    // One iteration: S, dP, P and dS for this wave's 32 rows, the hand-over, then dV or
-    // dK over all 64 rows.
+    // The wave's MFMAs over the partner's rows of one iteration run in the next one,
+    // interleaved with that iteration's softmax: `ap` carries their A operands (read
+    // before the barrier that ends the iteration) and the partner's B operands come
+    // from the hand-over buffer of that iteration's parity.
+    bf16x8 ap[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) ap[db][0] = ap[db][1] = zero8();
+#pragma unroll
+    for (int i = 0; i < 2 * 4; ++i)  // both hand-over buffers start as zeros
+        *reinterpret_cast<bf16x8*>(smem + ox + (i >> 2) * C::XB + (i & 3) * 1024) = zero8();
+
+    auto partner_mfmas = [&](int xoff) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int ql = 0; ql < 2; ++ql) {
+                const bf16x8 part = lds16(smem, ox_in + xoff, (2 * kk + ql) * 1024);
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    acc[kk][db] = mfma_32x32x16(ap[db][ql], part, acc[kk][db]);
+            }
+    };
+
+    // One iteration: S, dP, P and dS for this wave's 32 rows; the previous iteration's
+    // partner rows; the hand-over; dV or dK over this wave's own rows.
     auto step = [&](auto st_c, int it) {
         constexpr int ST = decltype(st_c)::value;
         wait_vmem<C::PER_STAGE>();
         wait_lds();
         barrier();
         issue(ic<(ST + 2) % 3>{}, it + 2);
-        const int4 ent = ld_const(P.blk_entries + min(e0 + it / (2 * G), e1 - 1));
+        const int4 ent = ld_const(P.blk_entries + max(e1 - 1 - it / (2 * G), e0));
         const int mk = pr ? ent.z : ent.y;
         const bool masked = mk != -1 || it >= n_it;  // PARTIAL, unseen or padding
         const int c = it & 1;
+        const int xcur = (it & 1) * C::XB, xprev = C::XB - xcur;
 
         const float l2 = *reinterpret_cast<const float*>(smem + ol + ST * 512);
         const float dl = *reinterpret_cast<const float*>(smem + ol + ST * 512 + 256);
@@ -291,6 +318,8 @@ __device__ __forceinline__ void dkdv_wave(const DevPlan& P, int Hq, int Hkv, int
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+        // The previous iteration's partner rows, overlapping the softmax below.
+        partner_mfmas(xprev);
         // keep: the B operand this wave uses itself (dS for dK, P for dV); give: the
         // partner's.  Index [kk][ql]: 32-key block, 16-row k-step of this wave's rows;
         // slot e of lane (n, g) is row 16 ql + 4g + e (e < 4) or 16 ql + 8 + 4g + e - 4.
@@ -327,9 +356,8 @@ __device__ __forceinline__ void dkdv_wave(const DevPlan& P, int Hq, int Hkv, int
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int ql = 0; ql < 2; ++ql)
-                *reinterpret_cast<bf16x8*>(smem + ox + (2 * kk + ql) * 1024) = give[kk][ql];
-        // The A operands of the partner's rows are read before the hand-over barrier.
-        bf16x8 ap[DB][2];
+                *reinterpret_cast<bf16x8*>(smem + ox + xcur + (2 * kk + ql) * 1024) = give[kk][ql];
+        // A operands of the partner's rows, for the next iteration.
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -337,7 +365,7 @@ __device__ __forceinline__ void dkdv_wave(const DevPlan& P, int Hq, int Hkv, int
                 const int imm = ST * C::MAT + (32 * (1 - ROLE) + 16 * ql) * C::ROWB;
                 ap[db][ql] = cat(lds8_tr(smem, ot[db][0], imm), lds8_tr(smem, ot[db][1], imm));
             }
-        // This wave's own 32 rows while the partner finishes its hand-over.
+        // This wave's own 32 rows.
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -348,17 +376,6 @@ __device__ __forceinline__ void dkdv_wave(const DevPlan& P, int Hq, int Hkv, int
                 for (int kk = 0; kk < 2; ++kk)
                     acc[kk][db] = mfma_32x32x16(a, keep[kk][ql], acc[kk][db]);
             }
-        wait_lds();
-        barrier();
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int ql = 0; ql < 2; ++ql) {
-                const bf16x8 part = lds16(smem, ox_in, (2 * kk + ql) * 1024);
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-                    acc[kk][db] = mfma_32x32x16(ap[db][ql], part, acc[kk][db]);
-            }
     };
 
     issue(ic<0>{}, 0);
@@ -368,6 +385,9 @@ __device__ __forceinline__ void dkdv_wave(const DevPlan& P, int Hq, int Hkv, int
         step(ic<1>{}, it + 1);
         step(ic<2>{}, it + 2);
     }
+    wait_lds();
+    barrier();
+    partner_mfmas(((n_run - 1) & 1) * C::XB);
     wait_vmem<0>();  // the trailing copies land before the workgroup's LDS is released
 
     const float os = ROLE == 0 ? scale : 1.f;
