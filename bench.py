@@ -193,6 +193,8 @@ def main():
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(tpb.bwd_workspace_bytes(probe, tpb.BF16, HQ, HKV, HD), dtype=torch.uint8,
                      device=dev)
+    wsf = torch.empty(tpb.fwd_workspace_bytes(probe, tpb.BF16, HQ, HKV, HD), dtype=torch.uint8,
+                      device=dev)
     plan_bufs = [torch.empty(probe.device_bytes(), dtype=torch.uint8, device=dev)
                  for _ in range(2)]
 
@@ -240,7 +242,7 @@ def main():
             h.numpy()[:] = a
             d.copy_(h, non_blocking=True)
         ev[0].record(stream)
-        tpb.attn_fwd(plan, q, k, v, o=o, lse=lse)
+        tpb.attn_fwd(plan, q, k, v, o=o, lse=lse, ws=wsf)
         ev[1].record(stream)
         tpb.attn_bwd_phase("preprocess", plan, q, k, v, o, lse, do, ws)
         ev[2].record(stream)

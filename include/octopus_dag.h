@@ -147,7 +147,11 @@ void octopus_plan_destroy(octopus_plan* plan);
 
 /* ---------------------------------------------------------------- attention (device) */
 
-/* Workspace bytes the forward needs (0 today; callers may pass NULL/0). */
+/* Workspace bytes the forward needs: for bf16, a copy of V re-laid per 64-key tile
+ * (bf16 [Hkv][n_kv_tiles][8][D][8], keys transposed so that every V^T operand of the
+ * MFMAs is one contiguous 16-byte read), written by the forward itself; 0 for fp32
+ * (callers may then pass NULL/0).  Caller-owned device memory, 16-byte aligned; its
+ * contents need not survive between calls. */
 size_t octopus_fwd_workspace_bytes(const octopus_plan* plan, octopus_dtype dtype,
                                    int32_t Hq, int32_t Hkv, int32_t D);
 

@@ -90,3 +90,16 @@ def test_fwd_error_paths():
     with pytest.raises(tpb.OctopusError) as ei:
         tpb.attn_fwd(plan, bad, bad, bad)
     assert ei.value.name == "EUNSUPPORTED"
+
+
+def test_fwd_workspace_error():
+    import torch
+    import tree_packed_block_amd as tpb
+    dag, x = workload("tiny", 2, 1, 64, "bf16", 1.0)
+    plan = tpb.Plan(dag.branches, dag.mounts, dag.T).upload()
+    t = {k: dev(v, "bf16") for k, v in x.items()}
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(tpb.OctopusError) as ei:
+        tpb.attn_fwd(plan, t["q"], t["k"], t["v"], ws=small)
+    assert ei.value.name == "EWORKSPACE"
+

@@ -197,3 +197,21 @@ def test_decode_segments_errors():
     with pytest.raises(tpb.OctopusError):
         tpb.decode_segments(wl.dag.branches, wl.dag.mounts, short, wl.pages, 16, wl.n_pages,
                             wl.cursors)
+
+
+def test_workspace_sizes():
+    """Forward: bf16 V re-laid per 64-key tile; backward: LSE2/Delta float32 rows padded
+    to 128."""
+    import tree_packed_block_amd as tpb
+    dag = synth.build("forked")[0]
+    plan = tpb.Plan(dag.branches, dag.mounts, dag.T)
+    n_kt = -(-dag.T // 64)
+    tp = -(-dag.T // 128) * 128
+    for hq, hkv, d in ((4, 2, 64), (16, 4, 128)):
+        tiles = hkv * n_kt * 64 * d * 2
+        assert tpb.fwd_workspace_bytes(plan, tpb.BF16, hq, hkv, d) == tiles
+        assert tpb.fwd_workspace_bytes(plan, tpb.FP32, hq, hkv, d) == 0
+        floats = 2 * hq * tp * 4
+        assert tpb.bwd_workspace_bytes(plan, tpb.FP32, hq, hkv, d) == floats
+        assert tpb.bwd_workspace_bytes(plan, tpb.BF16, hq, hkv, d) == floats
+

@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     decode_segments,
     decode_workspace_bytes,
     default_scale,
+    fwd_workspace_bytes,
     lib,
     paged_mount_decode,
 )

@@ -220,8 +220,13 @@ def _need(t, shape, dtype, name):
         raise OctopusError(EINVAL, f"{name} must be a device tensor")
 
 
-def attn_fwd(plan: Plan, q, k, v, scale=None, o=None, lse=None, stream=None):
-    """Packed-DAG attention forward: returns ``(o [T,Hq,D], lse float32 [Hq,T])``."""
+def fwd_workspace_bytes(plan: Plan, dtype_code, Hq, Hkv, D) -> int:
+    return int(lib().octopus_fwd_workspace_bytes(plan.handle, dtype_code, Hq, Hkv, D))
+
+
+def attn_fwd(plan: Plan, q, k, v, scale=None, o=None, lse=None, ws=None, stream=None):
+    """Packed-DAG attention forward: returns ``(o [T,Hq,D], lse float32 [Hq,T])``.
+    ``ws`` (uint8 device tensor of fwd_workspace_bytes) is allocated when not given."""
     import torch
     T, Hq, D = q.shape
     Hkv = k.shape[1]
@@ -234,11 +239,15 @@ def attn_fwd(plan: Plan, q, k, v, scale=None, o=None, lse=None, stream=None):
         lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
     _need(o, q.shape, q.dtype, "o")
     _need(lse, (Hq, T), torch.float32, "lse")
+    code = _dtype_code(q)
+    if ws is None:
+        need = fwd_workspace_bytes(plan, code, Hq, Hkv, D)
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
     s = stream or torch.cuda.current_stream(q.device)
-    _check(lib().octopus_dag_attn_fwd(plan.handle, _dtype_code(q), Hq, Hkv, D,
-                                      float(scale or 0.0), q.data_ptr(), k.data_ptr(),
-                                      v.data_ptr(), o.data_ptr(), lse.data_ptr(), None, 0,
-                                      _vp(s.cuda_stream)))
+    _check(lib().octopus_dag_attn_fwd(plan.handle, code, Hq, Hkv, D, float(scale or 0.0),
+                                      q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                      lse.data_ptr(), None if ws is None else ws.data_ptr(),
+                                      0 if ws is None else ws.numel(), _vp(s.cuda_stream)))
     return o, lse
 
 

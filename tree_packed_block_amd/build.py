@@ -30,8 +30,9 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
-# Per-source code-generation options.
-HIP_FILE_FLAGS: dict = {}
+# Per-source code-generation options.  The kernels never produce NaN on purpose, so
+# fmaxf need not quiet NaN operands (that costs one extra instruction per maximum).
+HIP_FILE_FLAGS: dict = {"fwd.hip": ["-fno-honor-nans"]}
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
              "-D__HIP_PLATFORM_AMD__"]
 

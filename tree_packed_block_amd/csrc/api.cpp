@@ -186,26 +186,33 @@ void octopus_plan_destroy(octopus_plan* plan) {
     delete plan;
 }
 
-size_t octopus_fwd_workspace_bytes(const octopus_plan*, octopus_dtype, int32_t, int32_t,
-                                   int32_t) {
-    return 0;
+size_t octopus_fwd_workspace_bytes(const octopus_plan* plan, octopus_dtype dtype, int32_t,
+                                   int32_t Hkv, int32_t D) {
+    if (plan == nullptr || dtype != OCTOPUS_BF16 || Hkv < 1 || (D != 64 && D != 128)) return 0;
+    return octo::tiles_t_bytes(plan->p.nKT, Hkv, D);
 }
 
 int octopus_dag_attn_fwd(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
                          int32_t Hkv, int32_t D, float scale, const void* q, const void* k,
                          const void* v, void* o, float* lse, void* ws, size_t ws_bytes,
                          void* stream) {
-    (void)ws;
-    (void)ws_bytes;
     int rc = check_attn(plan, dtype, Hq, Hkv, D, {q, k, v, o, lse});
     if (rc != OCTOPUS_OK) return rc;
+    const size_t need = octopus_fwd_workspace_bytes(plan, dtype, Hq, Hkv, D);
+    if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned(ws, 16)))
+        return fail(OCTOPUS_EWORKSPACE, "forward workspace needs " + std::to_string(need) +
+                                            " bytes, 16-byte aligned");
     if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
     const octo::DevPlan dp = dev_view(plan->p);
-    hipError_t e = dtype == OCTOPUS_BF16
-                       ? octo::launch_fwd_bf16(dp, Hq, Hkv, D, scale, q, k, v, o, lse,
-                                               (hipStream_t)stream)
-                       : octo::launch_fwd_fp32(dp, Hq, Hkv, D, scale, q, k, v, o, lse,
-                                               (hipStream_t)stream);
+    hipError_t e;
+    if (dtype == OCTOPUS_BF16) {
+        e = octo::launch_tiles_t(dp.T, dp.nKT, Hkv, D, v, ws, (hipStream_t)stream);
+        if (e == hipSuccess)
+            e = octo::launch_fwd_bf16(dp, Hq, Hkv, D, scale, q, k, ws, o, lse,
+                                      (hipStream_t)stream);
+    } else {
+        e = octo::launch_fwd_fp32(dp, Hq, Hkv, D, scale, q, k, v, o, lse, (hipStream_t)stream);
+    }
     if (e != hipSuccess) return hip_fail(e, "forward launch");
     return ok();
 }
@@ -269,8 +276,9 @@ int octopus_dag_attn_bwd_dq(const octopus_plan* plan, octopus_dtype dtype, int32
     if (rc != OCTOPUS_OK) return rc;
     if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
     const hipError_t e = octo::launch_bwd_dq(dtype == OCTOPUS_BF16, dev_view(plan->p), Hq, Hkv, D,
-                                             scale, q, k, v, dout, static_cast<const float*>(ws),
-                                             dq, (hipStream_t)stream);
+                                             scale, q, k, v, dout,
+                                             static_cast<float*>(const_cast<void*>(ws)), dq,
+                                             (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "backward dQ launch");
     return ok();
 }

@@ -484,10 +484,11 @@ __global__ __launch_bounds__(256 * HPW, 1) void dq_bf16_kernel(
     const int p0 = ld_const(P.qt_ptr + qt), p1 = ld_const(P.qt_ptr + qt + 1);
     const int n_it = p1 - p0;
     auto issue = [&](auto st_c, int it) {
+        constexpr int ST = decltype(st_c)::value;
         const int2 pr = ld_const(P.q_pairs + p0 + it);
-        issue_kv_stage<D, NTHR, decltype(st_c)::value>(smem_base, K, V, P.mask_rows, pr.x,
-                                                        pr.y >= 0 ? pr.y : P.n_partial, T, kvh,
-                                                        kvstride, tid, w, lane);
+        issue_kv_stage<D, NTHR, ST>(smem_base, K, V, P.mask_rows, pr.x,
+                                    pr.y >= 0 ? pr.y : P.n_partial, T, kvh, kvstride, tid, w,
+                                    lane);
     };
     auto step = [&](auto st_c, int it) {
         constexpr int ST = decltype(st_c)::value;
@@ -496,8 +497,6 @@ __global__ __launch_bounds__(256 * HPW, 1) void dq_bf16_kernel(
         barrier();
         if (it + 2 < n_it) issue(ic<(ST + 2) % 3>{}, it + 2);
         const bool partial = ld_const(P.q_pairs + p0 + it).y >= 0;
-        uint64_t bits = ~0ull;
-        if (partial) bits = *reinterpret_cast<const uint64_t*>(smem + off_mask + ST * L::MASKB);
 
         bf16x8 sb[4];
 #pragma unroll
@@ -509,12 +508,23 @@ __global__ __launch_bounds__(256 * HPW, 1) void dq_bf16_kernel(
                 sc = mfma_32x32x16(lds16(smem, off.k[ks], imm), qf[ks], sc);
                 dp = mfma_32x32x16(lds16(smem, offv[ks], imm), df[ks], dp);
             }
-            const uint32_t bw = (uint32_t)(bits >> (32 * kb + 4 * g));
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                float p = fast_exp2(fmaf(sc[j], scale_log2, -lse2));
-                if (partial && !((bw >> (8 * (j >> 2) + (j & 3))) & 1u)) p = 0.f;
+                const float p = fast_exp2(fmaf(sc[j], scale_log2, -lse2));
                 sb[kb * 2 + (j >> 3)][j & 7] = (bf16)(p * (dp[j] - dlt));
+            }
+        }
+        if (__builtin_expect(partial, 0)) {  // wave-uniform and rare: clear dS where the
+            asm volatile("");                   // mask is 0 (a real branch, not selects)
+            const uint64_t bits =
+                *reinterpret_cast<const uint64_t*>(smem + off_mask + ST * L::MASKB);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const uint32_t bw = (uint32_t)(bits >> (32 * kb + 4 * g));
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    if (!((bw >> (8 * (j >> 2) + (j & 3))) & 1u))
+                        sb[kb * 2 + (j >> 3)][j & 7] = (bf16)0.f;
             }
         }
 #pragma unroll
@@ -687,6 +697,7 @@ __global__ __launch_bounds__(64) void dkdv_fp32_kernel(DevPlan P, int Hq, int Hk
 
 size_t bwd_workspace_floats(int T, int Hq) { return (size_t)2 * Hq * padded_rows(T); }
 
+
 hipError_t launch_bwd_preprocess(bool bf16_, const DevPlan& p, int Hq, int D, const void* o,
                                  const void* dout, const float* lse, float* ws, hipStream_t s) {
     const int Tp = padded_rows(p.T);
@@ -736,36 +747,35 @@ hipError_t launch_bwd_dkdv(bool bf16_, const DevPlan& p, int Hq, int Hkv, int D,
 }
 
 template <int D, int HPW>
-static void dq_bf16_launch(const DevPlan& p, int Hq, int Hkv, float scale, const void* q,
-                           const void* k, const void* v, const void* dout, const float* ws,
-                           void* dq, hipStream_t s) {
+static hipError_t dq_bf16_launch(const DevPlan& p, int Hq, int Hkv, float scale, const void* q,
+                                 const void* k, const void* v, const void* dout, float* ws,
+                                 void* dq, hipStream_t s) {
     hipLaunchKernelGGL((dq_bf16_kernel<D, HPW>), dim3(xcd_grid(p.nQT * Hkv, Hq / Hkv / HPW)),
                        dim3(256 * HPW), 0, s, p, Hq, Hkv, scale, scale * kLog2e, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, (const bf16*)dout, ws, (bf16*)dq);
+    return hipGetLastError();
 }
 
 template <int D>
-static void dq_launch(bool bf16_, const DevPlan& p, int Hq, int Hkv, float scale, const void* q,
-                      const void* k, const void* v, const void* dout, const float* ws, void* dq,
-                      hipStream_t s) {
+static hipError_t dq_launch(bool bf16_, const DevPlan& p, int Hq, int Hkv, float scale,
+                            const void* q, const void* k, const void* v, const void* dout,
+                            float* ws, void* dq, hipStream_t s) {
     if (bf16_) {
         if ((Hq / Hkv) % 2 == 0)
-            dq_bf16_launch<D, 2>(p, Hq, Hkv, scale, q, k, v, dout, ws, dq, s);
-        else
-            dq_bf16_launch<D, 1>(p, Hq, Hkv, scale, q, k, v, dout, ws, dq, s);
-    } else {
-        hipLaunchKernelGGL(dq_fp32_kernel<D>, dim3(p.nQT * Hq), dim3(kBq), 0, s, p, Hq, Hkv,
-                           scale, (const float*)q, (const float*)k, (const float*)v,
-                           (const float*)dout, ws, (float*)dq);
+            return dq_bf16_launch<D, 2>(p, Hq, Hkv, scale, q, k, v, dout, ws, dq, s);
+        return dq_bf16_launch<D, 1>(p, Hq, Hkv, scale, q, k, v, dout, ws, dq, s);
     }
+    hipLaunchKernelGGL(dq_fp32_kernel<D>, dim3(p.nQT * Hq), dim3(kBq), 0, s, p, Hq, Hkv, scale,
+                       (const float*)q, (const float*)k, (const float*)v, (const float*)dout,
+                       ws, (float*)dq);
+    return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq(bool bf16_, const DevPlan& p, int Hq, int Hkv, int D, float scale,
                          const void* q, const void* k, const void* v, const void* dout,
-                         const float* ws, void* dq, hipStream_t s) {
-    if (D == 128) dq_launch<128>(bf16_, p, Hq, Hkv, scale, q, k, v, dout, ws, dq, s);
-    else dq_launch<64>(bf16_, p, Hq, Hkv, scale, q, k, v, dout, ws, dq, s);
-    return hipGetLastError();
+                         float* ws, void* dq, hipStream_t s) {
+    if (D == 128) return dq_launch<128>(bf16_, p, Hq, Hkv, scale, q, k, v, dout, ws, dq, s);
+    return dq_launch<64>(bf16_, p, Hq, Hkv, scale, q, k, v, dout, ws, dq, s);
 }
 
 }  // namespace octo

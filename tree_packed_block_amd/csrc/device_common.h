@@ -76,6 +76,15 @@ __device__ __forceinline__ void park(bf16x8& v) { asm volatile("" : "+a"(v)); }
 // 2^x on the hardware exponential unit (exact 0 for -inf).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// acc + the sum of the 8 bf16 values of v (v_dot2 against ones, two per instruction).
+__device__ __forceinline__ float row_sum8(bf16x8 v, float acc) {
+    const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), ones, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), ones, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), ones, acc, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), ones, acc, false);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

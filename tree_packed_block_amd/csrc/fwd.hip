@@ -12,9 +12,10 @@
 // rows.  Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 so
 // that every lane holds one query column: the row max and row sum are in-lane plus
 // one exchange with lane ^ 32, and the probabilities come out of the accumulator
-// already laid out as the B operand of O^T = V^T P^T.  K and V tiles are copied
-// global -> LDS asynchronously (three stages in flight, XOR-swizzled rows) together
-// with the query tile's row masks; V^T operands are read with ds_read_b64_tr_b16.
+// already laid out as the B operand of O^T = V^T P^T.  K tiles (XOR-swizzled rows) and
+// V tiles re-laid by tiles_t_kernel (so every V^T operand is one 16-byte LDS read) are
+// copied global -> LDS asynchronously, three stages in flight, together with the query
+// tile's row masks.
 // Workgroups of one KV group are launched adjacently on one XCD so their shared K/V
 // tiles hit the same L2.
 #include "device_common.h"
@@ -25,10 +26,49 @@ namespace octo {
 
 // Forward.  HPW query heads (of one KV group) per workgroup, 4 waves per head, each
 // wave owning 32 query rows.
+// One workgroup per (64-key tile, KV head): the tile's 64 x D block of src, read
+// row by row, written out in the tiles_t order (see kernels.h).
+template <int D>
+__global__ __launch_bounds__(256) void tiles_t_kernel(int T, int nKT, int Hkv,
+                                                      const bf16* __restrict__ src,
+                                                      bf16* __restrict__ dst) {
+    constexpr int RS = D + 8;  // padded LDS row, elements
+    __shared__ __attribute__((aligned(16))) bf16 tile[64 * RS];
+    const int kt = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
+    for (int i = threadIdx.x; i < 64 * D / 8; i += 256) {
+        const int r = i / (D / 8), c8 = i % (D / 8);
+        const int key = kt * kBk + r;
+        const bf16x8 v = key < T ? ld16(src + ((size_t)key * Hkv + kvh) * D + 8 * c8) : zero8();
+        st16(tile + r * RS + 8 * c8, v);
+    }
+    __syncthreads();
+    bf16* out = dst + ((size_t)kvh * nKT + kt) * (64 * D);
+    for (int u = threadIdx.x; u < 8 * D; u += 256) {  // u = chunk * D + row
+        const int c = u / D, d = u % D;
+        bf16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = tile[(16 * (c >> 1) + kperm(8 * (c & 1) + e)) * RS + d];
+        st16(out + (size_t)u * 8, v);
+    }
+}
+
+size_t tiles_t_bytes(int nKT, int Hkv, int D) { return (size_t)Hkv * nKT * 64 * D * 2; }
+
+hipError_t launch_tiles_t(int T, int nKT, int Hkv, int D, const void* src, void* dst,
+                          hipStream_t s) {
+    if (D == 128)
+        hipLaunchKernelGGL(tiles_t_kernel<128>, dim3(nKT * Hkv), dim3(256), 0, s, T, nKT, Hkv,
+                           (const bf16*)src, (bf16*)dst);
+    else
+        hipLaunchKernelGGL(tiles_t_kernel<64>, dim3(nKT * Hkv), dim3(256), 0, s, T, nKT, Hkv,
+                           (const bf16*)src, (bf16*)dst);
+    return hipGetLastError();
+}
+
 template <int D, int HPW>
 __global__ __launch_bounds__(256 * HPW, 1) void fwd_bf16_kernel(
     DevPlan P, int Hq, int Hkv, float scale_log2, const bf16* __restrict__ Q,
-    const bf16* __restrict__ K, const bf16* __restrict__ V, bf16* __restrict__ O,
+    const bf16* __restrict__ K, const bf16* __restrict__ VX, bf16* __restrict__ O,
     float* __restrict__ LSE) {
     using L = KvLayout<D>;
     constexpr int NTHR = 256 * HPW;
@@ -66,6 +106,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void fwd_bf16_kernel(
     KvOffsets<D> off;
     off.init(lane);
     const int off_mask = L::M0 + rr * 8;
+    const int ovx = L::V0 + tile_t_lane<D>(lane);  // V^T operands (tiles_t layout)
 
     f32x16 o[DB];
 #pragma unroll
@@ -75,10 +116,12 @@ __global__ __launch_bounds__(256 * HPW, 1) void fwd_bf16_kernel(
     const int p0 = ld_const(P.qt_ptr + qt), p1 = ld_const(P.qt_ptr + qt + 1);
     const int n_it = p1 - p0;
     auto issue = [&](auto st_c, int it) {
+        constexpr int ST = decltype(st_c)::value;
         const int2 pr = ld_const(P.q_pairs + p0 + it);
-        issue_kv_stage<D, NTHR, decltype(st_c)::value>(smem_base, K, V, P.mask_rows, pr.x,
-                                                        pr.y >= 0 ? pr.y : P.n_partial, T, kvh,
-                                                        kvstride, tid, w, lane);
+        issue_kv_stage<D, NTHR, ST, false>(smem_base, K, nullptr, P.mask_rows, pr.x,
+                                           pr.y >= 0 ? pr.y : P.n_partial, T, kvh, kvstride, tid,
+                                           w, lane);
+        issue_tile_t<D, NTHR>(smem_base, L::V0 + ST * L::MAT, VX, P.nKT, kvh, pr.x, tid, w);
     };
 
     auto step = [&](auto st_c, int it) {
@@ -111,7 +154,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void fwd_bf16_kernel(
         }
         float mx = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fmaxf(s[0][j], s[1][j]));
+        for (int j = 0; j < 16; ++j) mx = fmaxf(fmaxf(mx, s[0][j]), s[1][j]);  // v_max3
         mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
         if (__any(mx > m + kLazy)) {
             const float mnew = fmaxf(m, mx);
@@ -127,21 +170,19 @@ __global__ __launch_bounds__(256 * HPW, 1) void fwd_bf16_kernel(
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const float pv = fast_exp2(fmaf(s[kb][j], scale_log2, -m));
-                l += pv;
-                pf[kb * 2 + (j >> 3)][j & 7] = (bf16)pv;
-            }
+            for (int j = 0; j < 16; ++j)
+                pf[kb * 2 + (j >> 3)][j & 7] = (bf16)fast_exp2(fmaf(s[kb][j], scale_log2, -m));
+        // Row sum of the bf16 probabilities that enter O, two per instruction.
+#pragma unroll
+        for (int i = 0; i < 4; ++i) l = row_sum8(pf[i], l);
         // O^T += V^T P^T over 4 k-steps of 16 keys; the lane's 8 keys in k-step kk are
-        // 16kk + 4g + {0..3} and 16kk + 8 + 4g + {0..3}, read transposed from V.
+        // 16kk + 4g + {0..3} and 16kk + 8 + 4g + {0..3}, contiguous in the V tile.
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const bf16x8 a = cat(lds8_tr(smem, off.vt[db][0], ST * L::MAT + 16 * kk * L::ROWB),
-                                     lds8_tr(smem, off.vt[db][1], ST * L::MAT + 16 * kk * L::ROWB));
-                o[db] = mfma_32x32x16(a, pf[kk], o[db]);
-            }
+            for (int db = 0; db < DB; ++db)
+                o[db] = mfma_32x32x16(lds16(smem, ovx, ST * L::MAT + tile_t_imm<D>(kk, db)),
+                                      pf[kk], o[db]);
     };
 
     if (n_it > 0) issue(ic<0>{}, 0);
@@ -229,24 +270,24 @@ __global__ __launch_bounds__(128) void fwd_fp32_kernel(DevPlan P, int Hq, int Hk
 
 template <int D, int HPW>
 static void fwd_bf16_launch(const DevPlan& p, int Hq, int Hkv, float sl2, const void* q,
-                            const void* k, const void* v, void* o, float* lse, hipStream_t s) {
+                            const void* k, const void* vx, void* o, float* lse, hipStream_t s) {
     const int G = Hq / Hkv;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, HPW>), dim3(xcd_grid(p.nQT * Hkv, G / HPW)),
                        dim3(256 * HPW), 0, s, p, Hq, Hkv, sl2, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, (bf16*)o, lse);
+                       (const bf16*)vx, (bf16*)o, lse);
 }
 
 hipError_t launch_fwd_bf16(const DevPlan& p, int Hq, int Hkv, int D, float scale,
-                           const void* q, const void* k, const void* v, void* o, float* lse,
+                           const void* q, const void* k, const void* vx, void* o, float* lse,
                            hipStream_t s) {
     const float sl2 = scale * kLog2e;
     const bool pair = (Hq / Hkv) % 2 == 0;
     if (D == 128) {
-        if (pair) fwd_bf16_launch<128, 2>(p, Hq, Hkv, sl2, q, k, v, o, lse, s);
-        else fwd_bf16_launch<128, 1>(p, Hq, Hkv, sl2, q, k, v, o, lse, s);
+        if (pair) fwd_bf16_launch<128, 2>(p, Hq, Hkv, sl2, q, k, vx, o, lse, s);
+        else fwd_bf16_launch<128, 1>(p, Hq, Hkv, sl2, q, k, vx, o, lse, s);
     } else {
-        if (pair) fwd_bf16_launch<64, 2>(p, Hq, Hkv, sl2, q, k, v, o, lse, s);
-        else fwd_bf16_launch<64, 1>(p, Hq, Hkv, sl2, q, k, v, o, lse, s);
+        if (pair) fwd_bf16_launch<64, 2>(p, Hq, Hkv, sl2, q, k, vx, o, lse, s);
+        else fwd_bf16_launch<64, 1>(p, Hq, Hkv, sl2, q, k, vx, o, lse, s);
     }
     return hipGetLastError();
 }

@@ -29,8 +29,19 @@ struct DevPlan {
 constexpr int kBq = 128;  // query rows per tile
 constexpr int kBk = 64;   // keys per KV tile
 
+// V re-laid per 64-key tile so that the forward's MFMA operands which contract over
+// keys (V^T) are plain 16-byte LDS reads: bf16
+// [Hkv][nKT][8 chunks][D][8].  Element e of chunk c of tile t, row d, is key
+// 64 t + 16 (c / 2) + kperm(8 (c % 2) + e) of row d (zero past T); kperm swaps bits 2
+// and 3 of a key's index in its 16-key group, matching the key order of the
+// probabilities held by an MFMA lane.
+size_t tiles_t_bytes(int nKT, int Hkv, int D);
+hipError_t launch_tiles_t(int T, int nKT, int Hkv, int D, const void* src, void* dst,
+                          hipStream_t s);
+
+// The bf16 forward reads V through `vx` (tiles_t layout, filled by the caller).
 hipError_t launch_fwd_bf16(const DevPlan& p, int Hq, int Hkv, int D, float scale,
-                           const void* q, const void* k, const void* v, void* o, float* lse,
+                           const void* q, const void* k, const void* vx, void* o, float* lse,
                            hipStream_t s);
 hipError_t launch_fwd_fp32(const DevPlan& p, int Hq, int Hkv, int D, float scale,
                            const void* q, const void* k, const void* v, void* o, float* lse,
@@ -46,7 +57,7 @@ hipError_t launch_bwd_dkdv(bool bf16, const DevPlan& p, int Hq, int Hkv, int D, 
                            const float* ws, void* dk, void* dv, hipStream_t s);
 hipError_t launch_bwd_dq(bool bf16, const DevPlan& p, int Hq, int Hkv, int D, float scale,
                          const void* q, const void* k, const void* v, const void* dout,
-                         const float* ws, void* dq, hipStream_t s);
+                         float* ws, void* dq, hipStream_t s);
 hipError_t launch_decode_bf16(int B, int Hq, int Hkv, int D, int page_size, float scale,
                               const void* q, const void* k_pool, const void* v_pool,
                               int n_pages, const int32_t* seg_ptr, const int32_t* seg_page,

@@ -26,15 +26,44 @@ struct KvLayout {
 template <int V>
 using ic = std::integral_constant<int, V>;
 
+// Position p of a 16-key group in the tiles_t layout holds key kperm(p) (an
+// involution): lane half g of an MFMA holds keys 4g..4g+3 and 8+4g..8+4g+3 of each
+// 16-key step, which become the contiguous positions 8g..8g+7.
+__host__ __device__ constexpr int kperm(int p) { return (p & 3) | ((p & 4) << 1) | ((p & 8) >> 1); }
+
+// Copy tile `kt` of a tiles_t array (one contiguous block of 64 * D bf16) into the LDS
+// region at byte `lds_off`, NDMA copies of 16 bytes per thread, in order.
+template <int D, int NTHR>
+__device__ __forceinline__ void issue_tile_t(unsigned smem_base, unsigned lds_off,
+                                             const bf16* X, int nKT, int kvh, int kt, int tid,
+                                             int w) {
+    constexpr int NDMA = 64 * D * 2 / (16 * NTHR);
+    const bf16* src = X + ((size_t)kvh * nKT + kt) * (64 * D);
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i)
+        dma16(src + 8 * (i * NTHR + tid), smem_base + lds_off + (i * NTHR + w * 64) * 16);
+}
+
+// Per-lane byte offset, inside a tiles_t tile in LDS, of the A operand that covers
+// rows d = 32 db + n (lane n = l % 32) and k-step kk (16 keys): chunk 2kk + g, so
+// lane base n * 16 + g * D * 16 plus the immediate tile_t_imm(kk, db).
+template <int D>
+__device__ __forceinline__ int tile_t_lane(int lane) {
+    return (lane & 31) * 16 + (lane >> 5) * D * 16;
+}
+template <int D>
+__host__ __device__ constexpr int tile_t_imm(int kk, int db) {
+    return kk * 2 * D * 16 + db * 32 * 16;
+}
+
 // Copy K/V tile `kt` and the row masks of mask `m` into stage ST: 64 rows of K and V
 // (XOR-swizzled) and 1 KiB of mask words.  Every wave issues the same number of
 // copies: 2 * (64 * D * 2 / 16 / NTHR) + 1 per thread.
-template <int D, int NTHR, int ST>
+template <int D, int NTHR, int ST, bool WITH_V = true, typename L = KvLayout<D>>
 __device__ __forceinline__ void issue_kv_stage(unsigned smem_base, const bf16* K, const bf16* V,
                                                const uint64_t* mask_rows, int kt, int m, int T,
                                                int kvh, size_t kvstride, int tid, int w,
                                                int lane) {
-    using L = KvLayout<D>;
     constexpr int CPR = D / 8;
     constexpr int NDMA = L::MAT / (16 * NTHR);
 #pragma unroll
@@ -45,7 +74,8 @@ __device__ __forceinline__ void issue_kv_stage(unsigned smem_base, const bf16* K
         const int key = min(kt * kBk + rho, T - 1);
         const size_t off = (size_t)key * kvstride + (size_t)kvh * D + 8 * chunk;
         dma16(K + off, smem_base + L::K0 + ST * L::MAT + (i * NTHR + w * 64) * 16);
-        dma16(V + off, smem_base + L::V0 + ST * L::MAT + (i * NTHR + w * 64) * 16);
+        if constexpr (WITH_V)
+            dma16(V + off, smem_base + L::V0 + ST * L::MAT + (i * NTHR + w * 64) * 16);
     }
     constexpr int LANES = 64 / (NTHR / 64);  // 16-byte pieces per wave for 1 KiB
     if (lane < LANES)
@@ -60,7 +90,6 @@ struct KvOffsets {
     static constexpr int KS = D / 16, DB = D / 32;
     int k[KS];      // A operand of S^T (row n, chunk 2ks+g); +32 rows: + 32 * ROWB
     int kt[DB][2];  // transposed A operand from the K tile; +16 rows per k-step
-    int vt[DB][2];  // the same from the V tile
     __device__ __forceinline__ void init(int lane) {
         using L = KvLayout<D>;
         const int n = lane & 31, g = lane >> 5, r_in = lane & 15, dh = (lane >> 4) & 1;
@@ -75,7 +104,6 @@ struct KvOffsets {
                 const int chunk = 4 * db + 2 * dh + ((r_in & 3) >> 1);
                 const int off = row * L::ROWB + ((chunk ^ swz_key<D>(row)) * 16) + 8 * (r_in & 1);
                 kt[db][hf] = L::K0 + off;
-                vt[db][hf] = L::V0 + off;
             }
     }
 };
