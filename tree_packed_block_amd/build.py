@@ -32,7 +32,7 @@ HIPCC_FLAGS = [
 ]
 # Per-source code-generation options.  The kernels never produce NaN on purpose, so
 # fmaxf need not quiet NaN operands (that costs one extra instruction per maximum).
-HIP_FILE_FLAGS: dict = {"fwd.hip": ["-fno-honor-nans"]}
+HIP_FILE_FLAGS: dict = {"fwd.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"]}
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
              "-D__HIP_PLATFORM_AMD__"]
 

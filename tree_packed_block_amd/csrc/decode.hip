@@ -148,14 +148,20 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(
                 mx = fmaxf(mx, t);
             }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m, mx);
-        const float alpha = fast_exp2(m - mnew);
-        m = mnew;
-        l *= alpha;
+        // The running max moves only when a page exceeds it by more than 2^8 (log2
+        // units); the final division by the running sum makes the result independent
+        // of where it was taken.
+        if (__any(mx > m + 8.f)) {
+            const float mnew = fmaxf(m, mx);
+            const float alpha = fast_exp2(m - mnew);
+            m = mnew;
+            l *= alpha;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+                for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+        }
+        const float mnew = m;
         bf16x8 pf[4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
