@@ -93,7 +93,8 @@ def cpu_baseline(dag, x, rows_per_part=768):
                       f"float64, {dt:.1f} s"}
 
 
-KERNEL_KEYS = (("fwd_bf16_kernel", "fwd"), ("preprocess_bf16_kernel", "bwd_preprocess"),
+KERNEL_KEYS = (("fwd_bf16_kernel", "fwd"), ("tiles_t_kernel", "fwd"),
+               ("preprocess_bf16_kernel", "bwd_preprocess"),
                ("dkdv_bf16_kernel", "bwd_dkdv"), ("dq_bf16_kernel", "bwd_dq"),
                ("decode_split_kernel", "decode"), ("decode_combine_kernel", "decode"))
 CALIBRATION_BYTES = 1 << 30  # the --calibrate-copy transfer
