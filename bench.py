@@ -12,7 +12,8 @@ One step = the whole hot path over that batch: build the tile plan on the host
 (validation, positions, tile lists) and upload it; forward; backward (Delta, dK/dV
 owner pass, dQ); build the decode segments on the host and upload them; decode.
 Host work for step k+1 overlaps the GPU work of step k (at most two steps in
-flight); inputs are resident in HBM before timing starts.
+flight; the first timed step's host work overlaps the last warm-up step); inputs are
+resident in HBM before timing starts.
 
 Printed: one JSON line.  ``value`` is useful (unmasked) fwd+bwd TFLOP/s over the
 whole step, counting 14*D*Hq*nnz FLOP per step (4 forward + 10 backward, one score
@@ -254,10 +255,12 @@ def main():
         tpb.paged_mount_decode(qd, kp, vp, *ds, n_split=args.n_split, o=od, lse=lsed, ws=wsd)
         ev[5].record(stream)
 
-    def run(n_steps):
+    def run(n_steps, first):
+        """Enqueue n_steps steps; `first` is the host work of the first one, done while
+        the previous GPU work ran (as every later step's is, inside this loop)."""
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_steps)]
         keep = []
-        nxt = host_prep()
+        nxt = first
         for i in range(n_steps):
             if i >= 2:
                 evs[i - 2][5].synchronize()  # buffers of step i-2 are free again
@@ -269,7 +272,8 @@ def main():
         return evs, keep
 
     for _ in range(max(args.warmup, 0)):
-        run(1)
+        run(1, host_prep())
+    first = host_prep()  # in a stream of steps this overlaps the last warm-up step
     torch.cuda.synchronize()
 
     # plan time alone (host), for the record
@@ -279,7 +283,7 @@ def main():
 
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    evs, keep = run(args.steps)
+    evs, keep = run(args.steps, first)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     del keep

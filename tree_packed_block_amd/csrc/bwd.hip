@@ -454,21 +454,30 @@ __global__ __launch_bounds__(256 * HPW, 1) void dq_bf16_kernel(
     const size_t qstride = (size_t)Hq * D, kvstride = (size_t)Hkv * D;
     const unsigned smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
+    // Q enters the scores pre-multiplied by scale * log2(e) (rounded to bf16), and the
+    // row terms as one extra MFMA k-step (this lane's -LSE2 or -Delta in three bf16
+    // parts against a row of ones), so the accumulators come out as the exponent of P
+    // and as dP - Delta.
     bf16x8 qf[KS], df[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         const size_t off = (size_t)row * qstride + (size_t)h * D + 16 * ks + 8 * g;
-        qf[ks] = row < T ? ld16(Q + off) : zero8();
+        const bf16x8 qr = row < T ? ld16(Q + off) : zero8();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[ks][e] = (bf16)((float)qr[e] * scale_log2);
         df[ks] = row < T ? ld16(dO + off) : zero8();
     }
-    const float lse2 = ws[(size_t)h * Tp + row];
-    const float dlt = ws[(size_t)Hq * Tp + (size_t)h * Tp + row];
+    const bf16x8 xl = split3(-ws[(size_t)h * Tp + row], g == 0);
+    const bf16x8 xd = split3(-ws[(size_t)Hq * Tp + (size_t)h * Tp + row], g == 0);
+    bf16x8 ones = zero8();
+    if (g == 0) ones[0] = ones[1] = ones[2] = (bf16)1.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         settle(qf[ks]);
         settle(df[ks]);
     }
-    asm volatile("" ::"v"(lse2), "v"(dlt));
+    settle(xl);
+    settle(xd);
 
     KvOffsets<D> off;
     off.init(lane);
@@ -501,7 +510,8 @@ __global__ __launch_bounds__(256 * HPW, 1) void dq_bf16_kernel(
         bf16x8 sb[4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {  // one 32-key block at a time (register pressure)
-            f32x16 sc = zero16(), dp = zero16();
+            f32x16 sc = mfma_32x32x16(ones, xl, zero16());
+            f32x16 dp = mfma_32x32x16(ones, xd, zero16());
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int imm = ST * L::MAT + kb * 32 * L::ROWB;
@@ -509,10 +519,8 @@ __global__ __launch_bounds__(256 * HPW, 1) void dq_bf16_kernel(
                 dp = mfma_32x32x16(lds16(smem, offv[ks], imm), df[ks], dp);
             }
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const float p = fast_exp2(fmaf(sc[j], scale_log2, -lse2));
-                sb[kb * 2 + (j >> 3)][j & 7] = (bf16)(p * (dp[j] - dlt));
-            }
+            for (int j = 0; j < 16; ++j)
+                sb[kb * 2 + (j >> 3)][j & 7] = (bf16)(fast_exp2(sc[j]) * dp[j]);
         }
         if (__builtin_expect(partial, 0)) {  // wave-uniform and rare: clear dS where the
             asm volatile("");                   // mask is 0 (a real branch, not selects)
