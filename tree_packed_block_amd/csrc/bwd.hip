@@ -211,6 +211,10 @@ __device__ __forceinline__ void dkdv_wave(const DevPlan& P, int Hq, int Hkv, int
     const int e0 = ld_const(P.blk_ptr + kb), e1 = ld_const(P.blk_ptr + kb + 1);
     const int n_it = (e1 - e0) * G * 2;  // (entry, head, 64-row half)
     if (n_it == 0) return;
+    TileDma<D, 256> dm;  // per-lane offsets of the copies
+    dm.init(tid, qstride);
+    const unsigned off_ld = (unsigned)((4 * ((8 * w + (lane & 7)) & 15)) * 4);
+    const unsigned off_mk = (unsigned)((32 * (w & 1) + (lane & 31)) * 16);
     const int n_run = (n_it + 2) / 3 * 3;  // iterations run: whole rounds of 3 stages
 
     // Copies of iteration `it` into stage ST: the 64 rows of Q and dO, their LSE2 and
@@ -227,26 +231,16 @@ __device__ __forceinline__ void dkdv_wave(const DevPlan& P, int Hq, int Hkv, int
         const int h = kvh * G + hh;
         const int4 ent = ld_const(P.blk_entries + e);
         const int row0 = ent.x * kBq + c * 64;
-#pragma unroll
-        for (int i = 0; i < C::NDMA; ++i) {
-            const int li = i * 256 + tid;
-            const int rho = li / CPR, slot = li % CPR;
-            const int chunk = swz<D>(rho, slot);  // the XOR swizzle is its own inverse
-            const int r = min(row0 + rho, T - 1);
-            const size_t off = (size_t)r * qstride + (size_t)h * D + 8 * chunk;
-            dma16(Q + off, smem_base + C::Q0 + ST * C::MAT + (i * 256 + w * 64) * 16);
-            dma16(dO + off, smem_base + C::D0 + ST * C::MAT + (i * 256 + w * 64) * 16);
-        }
-        if (lane < 8) {  // 32 pieces of 16 bytes, 8 per wave
-            const int u = 8 * w + lane;
-            const float* src = (u < 16 ? LSE2 : DEL) + (size_t)h * Tp + row0 + 4 * (u & 15);
-            dma16(src, smem_base + C::L0 + ST * 512 + 8 * w * 16);
-        }
+        issue_rows<D, 256>(smem_base, C::Q0 + ST * C::MAT, Q, row0, T, h, qstride, dm, tid, w);
+        issue_rows<D, 256>(smem_base, C::D0 + ST * C::MAT, dO, row0, T, h, qstride, dm, tid, w);
+        if (lane < 8)  // 32 pieces of 16 bytes, 8 per wave: LSE2 (waves 0, 1), Delta (2, 3)
+            dma16_s((w < 2 ? LSE2 : DEL) + (size_t)h * Tp + row0, off_ld,
+                    smem_base + C::L0 + ST * 512 + 8 * w * 16);
         if (lane < 32) {
             int mk = pr ? ent.z : ent.y;
             mk = pad || mk == -2 ? P.n_partial + 1 : (mk == -1 ? P.n_partial : mk);
-            dma16(P.mask_cols + ((size_t)mk * kBk + 32 * (w & 1) + lane) * 2,
-                  smem_base + C::M0 + ST * C::MASKB + w * 512);
+            dma16_s(P.mask_cols + (size_t)mk * kBk * 2, off_mk,
+                    smem_base + C::M0 + ST * C::MASKB + w * 512);
         }
     };
 
@@ -485,6 +479,8 @@ __global__ __launch_bounds__(256 * HPW, 1) void dq_bf16_kernel(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) offv[ks] = off.k[ks] - L::K0 + L::V0;
     const int off_mask = L::M0 + rr * 8;
+    TileDma<D, NTHR> dm;
+    dm.init(tid, kvstride);
 
     f32x16 dq[DB];
 #pragma unroll
@@ -496,8 +492,8 @@ __global__ __launch_bounds__(256 * HPW, 1) void dq_bf16_kernel(
         constexpr int ST = decltype(st_c)::value;
         const int2 pr = ld_const(P.q_pairs + p0 + it);
         issue_kv_stage<D, NTHR, ST>(smem_base, K, V, P.mask_rows, pr.x,
-                                    pr.y >= 0 ? pr.y : P.n_partial, T, kvh, kvstride, tid, w,
-                                    lane);
+                                    pr.y >= 0 ? pr.y : P.n_partial, T, kvh, kvstride, dm, tid,
+                                    w, lane);
     };
     auto step = [&](auto st_c, int it) {
         constexpr int ST = decltype(st_c)::value;

@@ -123,6 +123,15 @@ __device__ __forceinline__ void dma16(const void* g, unsigned lds_wave_base) {
                  : "memory", "m0");
 }
 
+// The same copy from a wave-uniform base address plus a per-lane 32-bit byte offset:
+// the per-lane part is computed once, the base on the scalar unit.
+__device__ __forceinline__ void dma16_s(const void* sbase, unsigned voff, unsigned lds_wave_base) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_wave_base))
+                 : "memory", "m0");
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding (they
 // complete in issue order).
 template <int N>

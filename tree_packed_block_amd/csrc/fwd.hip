@@ -107,6 +107,8 @@ __global__ __launch_bounds__(256 * HPW, 1) void fwd_bf16_kernel(
     off.init(lane);
     const int off_mask = L::M0 + rr * 8;
     const int ovx = L::V0 + tile_t_lane<D>(lane);  // V^T operands (tiles_t layout)
+    TileDma<D, NTHR> dm;
+    dm.init(tid, kvstride);
 
     f32x16 o[DB];
 #pragma unroll
@@ -119,8 +121,8 @@ __global__ __launch_bounds__(256 * HPW, 1) void fwd_bf16_kernel(
         constexpr int ST = decltype(st_c)::value;
         const int2 pr = ld_const(P.q_pairs + p0 + it);
         issue_kv_stage<D, NTHR, ST, false>(smem_base, K, nullptr, P.mask_rows, pr.x,
-                                           pr.y >= 0 ? pr.y : P.n_partial, T, kvh, kvstride, tid,
-                                           w, lane);
+                                           pr.y >= 0 ? pr.y : P.n_partial, T, kvh, kvstride, dm,
+                                           tid, w, lane);
         issue_tile_t<D, NTHR>(smem_base, L::V0 + ST * L::MAT, VX, P.nKT, kvh, pr.x, tid, w);
     };
 

@@ -41,7 +41,8 @@ __device__ __forceinline__ void issue_tile_t(unsigned smem_base, unsigned lds_of
     const bf16* src = X + ((size_t)kvh * nKT + kt) * (64 * D);
 #pragma unroll
     for (int i = 0; i < NDMA; ++i)
-        dma16(src + 8 * (i * NTHR + tid), smem_base + lds_off + (i * NTHR + w * 64) * 16);
+        dma16_s(src, (unsigned)((i * NTHR + tid) * 16),
+                smem_base + lds_off + (i * NTHR + w * 64) * 16);
 }
 
 // Per-lane byte offset, inside a tiles_t tile in LDS, of the A operand that covers
@@ -59,28 +60,64 @@ __host__ __device__ constexpr int tile_t_imm(int kk, int db) {
 // Copy K/V tile `kt` and the row masks of mask `m` into stage ST: 64 rows of K and V
 // (XOR-swizzled) and 1 KiB of mask words.  Every wave issues the same number of
 // copies: 2 * (64 * D * 2 / 16 / NTHR) + 1 per thread.
+// Per-lane byte offsets of the copies of one 64-row tile of a [rows][heads][D] tensor
+// (row stride `stride` elements), relative to the tile's first row and head: copy i of
+// thread t moves row (i * NTHR + t) / (D / 8), XOR-swizzled chunk, into LDS position
+// i * NTHR + t.
+template <int D, int NTHR>
+struct TileDma {
+    static constexpr int NDMA = 64 * D * 2 / (16 * NTHR);
+    unsigned off[NDMA];
+    __device__ __forceinline__ void init(int tid, size_t stride) {
+        constexpr int CPR = D / 8;
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) {
+            const int li = i * NTHR + tid;
+            const int rho = li / CPR, slot = li % CPR;
+            off[i] = (unsigned)(((size_t)rho * stride + 8 * swz<D>(rho, slot)) * 2);
+        }
+    }
+};
+
+// Copy rows row0 .. row0 + 63 (head `head`) of X into the LDS region at byte `lds_off`:
+// from a scalar base when the whole tile lies below T, else row by row with the rows
+// clamped to T - 1 (they are masked out by the caller).
+template <int D, int NTHR>
+__device__ __forceinline__ void issue_rows(unsigned smem_base, unsigned lds_off, const bf16* X,
+                                           int row0, int T, int head, size_t stride,
+                                           const TileDma<D, NTHR>& dm, int tid, int w) {
+    constexpr int CPR = D / 8;
+    if (row0 + 64 <= T) {
+        const bf16* base = X + (size_t)row0 * stride + (size_t)head * D;
+#pragma unroll
+        for (int i = 0; i < dm.NDMA; ++i)
+            dma16_s(base, dm.off[i], smem_base + lds_off + (i * NTHR + w * 64) * 16);
+    } else {
+#pragma unroll
+        for (int i = 0; i < dm.NDMA; ++i) {
+            const int li = i * NTHR + tid;
+            const int rho = li / CPR, slot = li % CPR;
+            const int r = min(row0 + rho, T - 1);
+            dma16(X + (size_t)r * stride + (size_t)head * D + 8 * swz<D>(rho, slot),
+                  smem_base + lds_off + (i * NTHR + w * 64) * 16);
+        }
+    }
+}
+
 template <int D, int NTHR, int ST, bool WITH_V = true, typename L = KvLayout<D>>
 __device__ __forceinline__ void issue_kv_stage(unsigned smem_base, const bf16* K, const bf16* V,
                                                const uint64_t* mask_rows, int kt, int m, int T,
-                                               int kvh, size_t kvstride, int tid, int w,
+                                               int kvh, size_t kvstride,
+                                               const TileDma<D, NTHR>& dm, int tid, int w,
                                                int lane) {
-    constexpr int CPR = D / 8;
-    constexpr int NDMA = L::MAT / (16 * NTHR);
-#pragma unroll
-    for (int i = 0; i < NDMA; ++i) {
-        const int li = i * NTHR + tid;
-        const int rho = li / CPR, slot = li % CPR;
-        const int chunk = swz<D>(rho, slot);  // the XOR swizzle is its own inverse
-        const int key = min(kt * kBk + rho, T - 1);
-        const size_t off = (size_t)key * kvstride + (size_t)kvh * D + 8 * chunk;
-        dma16(K + off, smem_base + L::K0 + ST * L::MAT + (i * NTHR + w * 64) * 16);
-        if constexpr (WITH_V)
-            dma16(V + off, smem_base + L::V0 + ST * L::MAT + (i * NTHR + w * 64) * 16);
-    }
+    issue_rows<D, NTHR>(smem_base, L::K0 + ST * L::MAT, K, kt * kBk, T, kvh, kvstride, dm, tid, w);
+    if constexpr (WITH_V)
+        issue_rows<D, NTHR>(smem_base, L::V0 + ST * L::MAT, V, kt * kBk, T, kvh, kvstride, dm, tid,
+                            w);
     constexpr int LANES = 64 / (NTHR / 64);  // 16-byte pieces per wave for 1 KiB
     if (lane < LANES)
-        dma16(mask_rows + (size_t)m * kBq + 2 * (w * LANES + lane),
-              smem_base + L::M0 + ST * L::MASKB + w * LANES * 16);
+        dma16_s(mask_rows + (size_t)m * kBq, (unsigned)((w * LANES + lane) * 16),
+                smem_base + L::M0 + ST * L::MASKB + w * LANES * 16);
 }
 
 // Per-lane byte offsets (relative to the LDS base) of the operands a wave reads from
