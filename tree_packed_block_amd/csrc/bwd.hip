@@ -130,7 +130,6 @@ __device__ __forceinline__ bf16x8 split3(float x, bool on) {
     return v;
 }
 
-__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // One wave of a dK/dV workgroup.  ROLE 0 accumulates dK (and hands P to its partner),
 // ROLE 1 accumulates dV (and hands dS over).  Both roles run the same sequence of

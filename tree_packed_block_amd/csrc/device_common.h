@@ -126,9 +126,16 @@ __device__ __forceinline__ void dma16(const void* g, unsigned lds_wave_base) {
 // The same copy from a wave-uniform base address plus a per-lane 32-bit byte offset:
 // the per-lane part is computed once, the base on the scalar unit.
 __device__ __forceinline__ void dma16_s(const void* sbase, unsigned voff, unsigned lds_wave_base) {
+    // The base is wave-uniform by contract; reading it through readfirstlane keeps it in
+    // scalar registers even where the compiler computed it in vector registers.
+    // (readfirstlane returns a signed int: widen through unsigned, never sign-extend.)
+    const uint64_t b = reinterpret_cast<uint64_t>(sbase);
+    const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
+    const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)b);
+    const uint64_t sb = (hi << 32) | lo;
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_wave_base))
+                 : "v"(voff), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds_wave_base))
                  : "memory", "m0");
 }
 
@@ -138,6 +145,9 @@ template <int N>
 __device__ __forceinline__ void wait_vmem() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+
+// Wait until this wave's LDS (and scalar memory) operations have completed.
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Workgroup barrier without the implied memory fence of __syncthreads (which would
 // drain every outstanding load, prefetches included).  LDS written by regular stores

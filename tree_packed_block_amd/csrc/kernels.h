@@ -16,7 +16,8 @@ struct DevPlan {
     const int32_t* bwd_order;   // [nKT] KV tiles, longest list first
     const int32_t* kt_ptr;      // [nKT+1]
     const int2* k_pairs;        // [n_pairs] {q_tile, mask}
-    const uint64_t* mask_rows;  // [n_partial][128]   bit x of row r: row sees key x
+    const uint64_t* mask_rows;  // [n_partial + 1][128] bit x of row r: row sees key x
+                                // (n_partial: all ones)
     const uint64_t* mask_cols;  // [n_partial + 2][64][2] bit r of key x: row r sees key x
                                 // (n_partial: all ones, n_partial + 1: all zeros)
     int32_t nKB, pad;           // 128-key blocks
