@@ -70,6 +70,20 @@ def test_bwd_fuzz_bf16(seed):
     _full_case(dag, x, "bf16")
 
 
+# Head layouts beyond the common 16/4: an odd group (one head per wave group in dQ),
+# one query head per KV head, the largest group, and head_dim 64 with an odd group.
+HEAD_CASES = [(3, 1, 128), (2, 2, 128), (16, 1, 128), (6, 2, 64), (8, 8, 64)]
+
+
+@pytest.mark.parametrize("seed", range(2))
+@pytest.mark.parametrize("Hq,Hkv,Dh", HEAD_CASES)
+def test_bwd_fuzz_heads_bf16(Hq, Hkv, Dh, seed):
+    say(f"case bwd fuzz heads Hq={Hq} Hkv={Hkv} D={Dh} seed={seed}")
+    dag, x = fuzz_workload(100 + seed, Hq, Hkv, Dh, max_len=300, max_branches=7,
+                           max_mounts=5)
+    _full_case(dag, x, "bf16")
+
+
 def _key_samples(dag, width=64):
     """Keys whose every reader is cheap to enumerate: the last ``width`` keys of
     every non-root branch.  Their readers are the branch's own later rows and, for

@@ -61,6 +61,23 @@ def test_fwd_fuzz_bf16(seed):
     check_close(lse, rl, TOL["bf16"], "LSE")
 
 
+# Head layouts beyond the common 16/4: an odd group (one head per wave group), one
+# query head per KV head, the largest group, and head_dim 64 with an odd group.
+HEAD_CASES = [(3, 1, 128), (2, 2, 128), (16, 1, 128), (6, 2, 64), (8, 8, 64)]
+
+
+@pytest.mark.parametrize("seed", range(2))
+@pytest.mark.parametrize("Hq,Hkv,Dh", HEAD_CASES)
+def test_fwd_fuzz_heads_bf16(Hq, Hkv, Dh, seed):
+    say(f"case fwd fuzz heads Hq={Hq} Hkv={Hkv} D={Dh} seed={seed}")
+    dag, x = fuzz_workload(100 + seed, Hq, Hkv, Dh, max_len=300, max_branches=7,
+                           max_mounts=5)
+    o, lse = _run_fwd(dag, x, "bf16")
+    ro, rl = A.attn_fwd(x["q"], x["k"], x["v"], dag.branches, dag.mounts)
+    check_close(o, ro, TOL["bf16"], "O")
+    check_close(lse, rl, TOL["bf16"], "LSE")
+
+
 @pytest.mark.parametrize("name", ["episode131k", "episode262k"])
 def test_fwd_full_size_sampled_rows(name):
     """The full tree through the same launch as the benchmark; the oracle computes
