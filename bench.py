@@ -46,9 +46,13 @@ def log(*a):
 
 
 def source_digest() -> str:
+    """Digest of the device code: the HIP kernel sources and the headers they include
+    (host planning and argument checking are left out)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tree_packed_block_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    device = [n for n in os.listdir(csrc)
+              if n.endswith(".hip") or n in ("device_common.h", "kvstage.h", "kernels.h")]
+    for name in sorted(device):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
