@@ -15,6 +15,9 @@ Host work for step k+1 overlaps the GPU work of step k (at most two steps in
 flight; the first timed step's host work overlaps the last warm-up step); inputs are
 resident in HBM before timing starts.
 
+``--workload forest1m`` packs four such trees into one stream and one plan (forest
+batching); the default is the single tree.
+
 Printed: one JSON line.  ``value`` is useful (unmasked) fwd+bwd TFLOP/s over the
 whole step, counting 14*D*Hq*nnz FLOP per step (4 forward + 10 backward, one score
 recompute).  ``roofline`` is for the kernel with the longest average duration,
@@ -41,6 +44,16 @@ METRIC = "packed-DAG attention useful TFLOP/s fwd+bwd @262K tok/tree; % MFMA pea
 HQ, HKV, HD = 16, 4, 128
 
 
+WORKLOADS = {
+    "episode262k": "episode tree of 262,144 packed tokens (8,192-token orchestrator prefix, "
+                   "8 workers 16K-32K water-filled, 4,096-token continuation mounting 3 "
+                   "worker tails), fwd+bwd; plus paged decode of 64 cursors",
+    "forest1m": "forest of 4 episode trees of 262,144 packed tokens each (1,048,576 tokens "
+                "in one plan; each tree as in the single-tree workload), fwd+bwd; plus "
+                "paged decode of 64 cursors",
+}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -59,9 +72,9 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_record(kernel: str):
+def traffic_record(kernel: str, workload: str):
     """HBM bytes per launch measured with rocprofv3 counters for ``kernel``, if the
-    committed record was taken on the current kernel sources."""
+    committed record was taken on the current kernel sources and the same workload."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -69,6 +82,8 @@ def traffic_record(kernel: str):
         rec = json.load(f)
     k = rec.get("kernels", {}).get(kernel)
     if not k or rec.get("source_digest") != source_digest():
+        return None
+    if rec.get("workload") != workload:
         return None
     return k.get("fetch_bytes_per_launch", 0) + k.get("write_bytes_per_launch", 0)
 
@@ -118,12 +133,13 @@ def _counter_per_dispatch(csv_path: str, counter: str):
     return {k: list(v.values()) for k, v in out.items()}
 
 
-def write_traffic(fetch_csv: str, write_csv: str) -> dict:
+def write_traffic(fetch_csv: str, write_csv: str, workload: str) -> dict:
     """profiles/traffic.json from two rocprofv3 --pmc runs of ``bench.py --calibrate-copy``
     (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch).  Each counter is scaled so that the
     1 GiB device copy reads and writes exactly 1 GiB; values are averaged per launch of
     each kernel of the step (decode = split + combine)."""
-    rec = {"source_digest": source_digest(), "kernels": {}, "calibration": {}}
+    rec = {"source_digest": source_digest(), "workload": workload, "kernels": {},
+           "calibration": {}}
     for counter, path, field in (("FETCH_SIZE", fetch_csv, "fetch_bytes_per_launch"),
                                  ("WRITE_SIZE", write_csv, "write_bytes_per_launch")):
         per = _counter_per_dispatch(path, counter)
@@ -153,6 +169,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--n-split", type=int, default=32, help="decode splits per cursor")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="episode262k",
+                    help="the packed stream of the fwd+bwd part of the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (reference for HBM counters)")
@@ -160,7 +178,7 @@ def main():
                     help="only write profiles/traffic.json from two rocprofv3 counter CSVs")
     args = ap.parse_args()
     if args.write_traffic:
-        print(json.dumps(write_traffic(*args.write_traffic), sort_keys=True))
+        print(json.dumps(write_traffic(*args.write_traffic, args.workload), sort_keys=True))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -186,7 +204,7 @@ def main():
 
     # ------------------------------------------------------------ workload (untimed)
     t0 = time.perf_counter()
-    dag, rng = synth.build("episode262k")
+    dag, rng = synth.build(args.workload)
     probe = tpb.Plan(dag.branches, dag.mounts, dag.T)
     st = probe.stats()
     pos = probe.positions()
@@ -314,7 +332,7 @@ def main():
         achieved = amount / (per[dom] * 1e-3) / 1e9
         peak, unit = PEAK_HBM_GBS, "GB/s"
     roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": traffic_record(dom),
+            "frac": round(achieved / peak, 4), "traffic": traffic_record(dom, args.workload),
             "kernel": dom, "avg_ms": round(per[dom], 3)}
 
     breakdown = {}
@@ -341,10 +359,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "episode tree of 262,144 packed tokens (8,192-token orchestrator "
-                        "prefix, 8 workers 16K-32K water-filled, 4,096-token continuation "
-                        "mounting 3 worker tails), fwd+bwd; plus paged decode of 64 cursors",
-            "tokens_per_tree": dag.T, "q_heads": HQ, "kv_heads": HKV, "head_dim": HD,
+            "workload": WORKLOADS[args.workload],
+            "tokens": dag.T, "trees": int((dag.branches[:, 0] < 0).sum()),
+            "q_heads": HQ, "kv_heads": HKV, "head_dim": HD,
             "nnz": nnz, "tile_pairs": st["n_pairs"], "partial_tiles": st["n_partial"],
             "decode_cursors": B, "decode_segments": n_seg, "decode_split": args.n_split,
             "decode_unique_kv_tokens": n_unique, "decode_bytes": dec_bytes,

@@ -18,7 +18,7 @@
  * Visibility.  For branch b and own offset r, with g(b,r) = start_b + r:
  *     A(b,r) = H(b) ∪ {g(b,r') : r' < r}
  *              ∪ {g(p_m,t) : s_m <= t < e_m, for mounts m with reader b, rpos_m <= r}
- *     H(root) = {},  H(b) = A(parent_b, fork_b)
+ *     H(root) = {} for every root,  H(b) = A(parent_b, fork_b)
  * and packed token i = g(b,r) attends to Ctx(i) = A(b,r) ∪ {i}, each key once.
  * Attention is ordinary softmax attention restricted to Ctx(i):
  *     S = scale * Q K^T,  LSE = log sum exp S,  P = exp(S - LSE),  O = P V
@@ -52,19 +52,22 @@
 extern "C" {
 #endif
 
-/* One branch (one `fork`): parent index (-1 for the root, which must be row 0;
- * every other row's parent has a lower index), fork = offset into the parent's own
- * tokens at which the child forked (0 <= fork <= parent len), start = where the
+/* One branch (one `fork`): parent index, or -1 for a root (fork 0; row 0 is always a
+ * root; every other row's parent has a lower index), fork = offset into the parent's
+ * own tokens at which the child forked (0 <= fork <= parent len), start = where the
  * branch's own tokens sit in the packed stream, len >= 1 own tokens.  The branch
- * spans must tile [0, total_tokens) exactly, in any order. */
+ * spans must tile [0, total_tokens) exactly, in any order.  Several roots make a
+ * forest: independent episode trees packed into one stream and one plan, no token
+ * seeing another tree (the trainer's step batches several trees; card "03 ·
+ * Training"); each tree's positions start at 0. */
 typedef struct {
     int32_t parent, fork, start, len;
 } octopus_branch;
 
 /* One mount (one `read_thread`): the reader, when its own length was rpos
  * (0 <= rpos <= reader len), mounted the producer's own tokens [s, e)
- * (0 <= s < e <= producer len, producer != reader).  Reader tokens at own offsets
- * >= rpos see the span. */
+ * (0 <= s < e <= producer len, producer != reader, both in the same tree).  Reader
+ * tokens at own offsets >= rpos see the span. */
 typedef struct {
     int32_t reader, rpos, producer, s, e;
 } octopus_mount;

@@ -54,25 +54,33 @@ def _rows(branches, mounts):
 
 
 def validate(branches, mounts, T: int) -> None:
-    """Reject malformed tables (``DagError('EINVAL')``): exactly one root in row 0;
-    every other row's parent has a lower index; ``0 <= fork <= len(parent)``;
-    ``len >= 1``; the branch spans tile ``[0, T)`` without gap or overlap; every
-    mount has ``reader != producer``, ``0 <= rpos <= len(reader)`` and
-    ``0 <= s < e <= len(producer)``."""
+    """Reject malformed tables (``DagError('EINVAL')``): row 0 is a root
+    (``parent = -1``, ``fork = 0``); any later row is a root too or has a parent of
+    lower index with ``0 <= fork <= len(parent)``; ``len >= 1``; the branch spans
+    tile ``[0, T)`` without gap or overlap; every mount has ``reader != producer``,
+    both in the same tree, ``0 <= rpos <= len(reader)`` and
+    ``0 <= s < e <= len(producer)``.
+
+    Several roots are a forest: independent trees packed into one stream (a training
+    step batches several episodes, card "03 · Training").  Reading: nothing in one
+    tree sees another, so a mount across trees is rejected."""
     br, mt = _rows(branches, mounts)
     if len(br) < 1:
         raise DagError("EINVAL", "no branches")
+    tree = []
     for b, (parent, fork, start, length) in enumerate(br):
         if length < 1:
             raise DagError("EINVAL", f"branch {b}: len < 1")
-        if b == 0:
-            if parent != -1 or fork != 0:
-                raise DagError("EINVAL", "branch 0 must be the root (parent -1, fork 0)")
+        if parent == -1:
+            if fork != 0:
+                raise DagError("EINVAL", f"branch {b}: a root must have fork 0")
+            tree.append(b)
         else:
             if not 0 <= parent < b:
-                raise DagError("EINVAL", f"branch {b}: parent must have a lower index")
+                raise DagError("EINVAL", f"branch {b}: parent must be -1 or a lower index")
             if not 0 <= fork <= br[parent][3]:
                 raise DagError("EINVAL", f"branch {b}: fork outside the parent")
+            tree.append(tree[parent])
     covered = np.zeros(T, dtype=np.int64)
     for b, (_, _, start, length) in enumerate(br):
         if start < 0 or start + length > T:
@@ -89,6 +97,8 @@ def validate(branches, mounts, T: int) -> None:
             raise DagError("EINVAL", f"mount {i}: rpos outside the reader")
         if not 0 <= s < e <= br[producer][3]:
             raise DagError("EINVAL", f"mount {i}: span outside the producer")
+        if tree[reader] != tree[producer]:
+            raise DagError("EINVAL", f"mount {i}: producer belongs to another tree")
 
 
 # --------------------------------------------------------------------------------------

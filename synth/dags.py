@@ -147,12 +147,43 @@ def episode(rng: np.random.Generator, total=262144, prefix=8192, n_workers=8,
     return Dag(name, b, m, total)
 
 
+def forest(trees, rng: np.random.Generator | None = None, name="forest") -> Dag:
+    """Several trees in one packed stream: the rows of every tree, parents and mount
+    branch indices shifted by the rows before it.  Without ``rng`` the trees are
+    packed one after another, each in its own order; with ``rng`` the branch spans of
+    all trees are packed in one random interleaved order."""
+    rows_b, rows_m, base = [], [], 0
+    for t in trees:
+        for (parent, fork, start, L) in t.branches:
+            rows_b.append([int(parent) + base if parent >= 0 else -1, int(fork), int(start),
+                           int(L)])
+        for (reader, rpos, producer, s, e) in t.mounts:
+            rows_m.append([int(reader) + base, int(rpos), int(producer) + base, int(s),
+                           int(e)])
+        base += t.nb
+    if rng is None:
+        off = 0
+        i = 0
+        for t in trees:
+            for _ in range(t.nb):
+                rows_b[i][2] += off
+                i += 1
+            off += t.T
+    else:
+        s = 0
+        for b in rng.permutation(len(rows_b)):
+            rows_b[int(b)][2] = s
+            s += rows_b[int(b)][3]
+    b, m = _tables(rows_b, rows_m)
+    return Dag(name, b, m, int(sum(t.T for t in trees)))
+
+
 def build(name: str, seed: int | None = None):
     """Return ``(dag, rng)`` for a named workload; ``rng`` is left positioned after
     the structure draws so the tensors can be drawn from it next (structure, then Q,
     K, V, then dO)."""
     defaults = {"tiny": 1, "forked": 2, "episode262k": 3, "episode131k": 3,
-                "episode_small": 7, "episode_mid": 11}
+                "episode_small": 7, "episode_mid": 11, "forest_small": 13, "forest1m": 17}
     if seed is None:
         seed = defaults[name]
     rng = np.random.default_rng(seed)
@@ -172,6 +203,18 @@ def build(name: str, seed: int | None = None):
     if name == "episode_mid":
         return episode(rng, total=12345, prefix=1037, n_workers=6, wmin=900, wmax=2048,
                        cont=611, n_mounts=3, smin=100, smax=700, name=name), rng
+    if name == "forest_small":
+        # Three small episodes of different totals, branch spans interleaved.
+        trees = [episode(rng, total=tot, prefix=pre, n_workers=nw, wmin=150, wmax=700,
+                         cont=cont, n_mounts=2, smin=20, smax=150, name=name)
+                 for tot, pre, nw, cont in ((3000, 300, 5, 229), (2077, 129, 3, 301),
+                                            (1111, 65, 2, 97))]
+        return forest(trees, rng, name=name), rng
+    if name == "forest1m":
+        # Four 262,144-token episodes of the headline shape, packed one after another
+        # (the trainer's step holds about a million owned tokens).
+        trees = [episode(rng, name=name) for _ in range(4)]
+        return forest(trees, name=name), rng
     raise KeyError(name)
 
 

@@ -25,7 +25,7 @@ def say(*a):
     sys.stdout.flush()
 
 
-@functools.lru_cache(maxsize=4)
+@functools.lru_cache(maxsize=2)
 def workload(name, Hq=16, Hkv=4, Dh=128, dtype="bf16", std=0.5, with_dout=False, seed=None):
     """``(dag, inputs)``: the named DAG and Q/K/V (and dO) drawn from the same
     generator, Q and K rotated at the oracle's positions."""

@@ -63,6 +63,14 @@ def test_bwd_episode_mid_bf16():
     _full_case(dag, x, "bf16")
 
 
+def test_bwd_forest_small_bf16():
+    """Three trees, branch spans interleaved in the stream: one plan, one launch per
+    phase."""
+    say("case bwd forest_small bf16 16/4 D=128")
+    dag, x = workload("forest_small", 16, 4, 128, "bf16", 0.5, with_dout=True)
+    _full_case(dag, x, "bf16")
+
+
 @pytest.mark.parametrize("seed", range(8))
 def test_bwd_fuzz_bf16(seed):
     say(f"case bwd fuzz seed={seed}")
@@ -112,7 +120,7 @@ def _merge(ranges):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["episode131k", "episode262k"])
+@pytest.mark.parametrize("name", ["episode131k", "episode262k", "forest1m"])
 def test_bwd_full_size_sampled(name):
     """The full tree through the benchmark's launches.  The oracle computes dQ on
     sampled query rows, and dK/dV of sampled keys from every query that sees them

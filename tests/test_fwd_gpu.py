@@ -51,6 +51,11 @@ def test_fwd_forked_bf16():
     _full_case("forked", "bf16", 16, 4, 128)
 
 
+def test_fwd_forest_small_bf16():
+    """Three trees, branch spans interleaved in the stream: one plan, one launch."""
+    _full_case("forest_small", "bf16", 16, 4, 128)
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_fwd_fuzz_bf16(seed):
     say(f"case fwd fuzz seed={seed}")
@@ -78,7 +83,7 @@ def test_fwd_fuzz_heads_bf16(Hq, Hkv, Dh, seed):
     check_close(lse, rl, TOL["bf16"], "LSE")
 
 
-@pytest.mark.parametrize("name", ["episode131k", "episode262k"])
+@pytest.mark.parametrize("name", ["episode131k", "episode262k", "forest1m"])
 def test_fwd_full_size_sampled_rows(name):
     """The full tree through the same launch as the benchmark; the oracle computes
     sampled row ranges (boundaries, mounts, ends) one by one."""

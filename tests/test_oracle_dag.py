@@ -119,6 +119,8 @@ def test_validate_errors():
         (ok_b, np.array([[1, 1, 0, 2, 2]]), 7),  # empty span
         (ok_b, np.array([[1, 1, 0, 0, 5]]), 7),  # span past the producer
         (ok_b, np.array([[1, 1, 2, 0, 1]]), 7),  # producer index out of range
+        (np.array([[-1, 0, 0, 4], [-1, 2, 4, 3]]), ok_m, 7),  # second root forked
+        (np.array([[-1, 0, 0, 4], [-1, 0, 4, 3]]), ok_m, 7),  # mount across trees
     ]
     for b, m, T in bad:
         with pytest.raises(D.DagError) as ei:

@@ -56,6 +56,8 @@ def test_planner_rejects_what_the_oracle_rejects():
         (ok_b, np.array([[1, 1, 0, 0, 5]]), 7),
         (ok_b, np.array([[1, 1, 2, 0, 1]]), 7),
         (ok_b, ok_m, 0),
+        (np.array([[-1, 0, 0, 4], [-1, 2, 4, 3]]), ok_m, 7),
+        (np.array([[-1, 0, 0, 4], [-1, 0, 4, 3]]), ok_m, 7),
     ]
     for b, m, T in bad:
         with pytest.raises(D.DagError):

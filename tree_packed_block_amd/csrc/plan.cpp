@@ -38,23 +38,28 @@ int validate(const octopus_branch* br, int32_t nb, const octopus_mount* mt, int3
         err = "total_tokens must be in [1, 2^24]";
         return OCTOPUS_EINVAL;
     }
+    // tree[b]: the root row of b's tree.  Every row with parent -1 starts a tree of
+    // its own (a forest packs several episodes into one stream); row 0 is one.
+    std::vector<int32_t> tree(nb);
     for (int32_t b = 0; b < nb; ++b) {
         const octopus_branch& x = br[b];
         if (x.len < 1) { err = row_msg("branch", b, "len < 1"); return OCTOPUS_EINVAL; }
-        if (b == 0) {
-            if (x.parent != -1 || x.fork != 0) {
-                err = "branch 0 must be the root (parent -1, fork 0)";
+        if (x.parent == -1) {
+            if (x.fork != 0) {
+                err = row_msg("branch", b, "a root must have fork 0");
                 return OCTOPUS_EINVAL;
             }
+            tree[b] = b;
         } else {
             if (x.parent < 0 || x.parent >= b) {
-                err = row_msg("branch", b, "parent must have a lower index");
+                err = row_msg("branch", b, "parent must be -1 or a lower index");
                 return OCTOPUS_EINVAL;
             }
             if (x.fork < 0 || x.fork > br[x.parent].len) {
                 err = row_msg("branch", b, "fork outside the parent");
                 return OCTOPUS_EINVAL;
             }
+            tree[b] = tree[x.parent];
         }
         if (x.start < 0 || (int64_t)x.start + x.len > T) {
             err = row_msg("branch", b, "span outside [0, T)");
@@ -90,6 +95,10 @@ int validate(const octopus_branch* br, int32_t nb, const octopus_mount* mt, int3
         }
         if (!(0 <= m.s && m.s < m.e && m.e <= br[m.producer].len)) {
             err = row_msg("mount", i, "span outside the producer");
+            return OCTOPUS_EINVAL;
+        }
+        if (tree[m.reader] != tree[m.producer]) {
+            err = row_msg("mount", i, "producer belongs to another tree");
             return OCTOPUS_EINVAL;
         }
     }
@@ -209,10 +218,13 @@ int load_dag(const octopus_branch* br, int32_t nb, const octopus_mount* mt, int3
         std::stable_sort(v.begin(), v.end(),
                          [&](int32_t a, int32_t b) { return d.mt[a].rpos < d.mt[b].rpos; });
     }
+    d.tree.resize(nb);
+    for (int32_t b = 0; b < nb; ++b) d.tree[b] = br[b].parent < 0 ? b : d.tree[br[b].parent];
     // H(b) = H(parent) ∪ parent's own [0, fork) ∪ parent's mounts issued at rpos <= fork.
     d.inherited.assign(nb, {});
     for (int32_t b = 1; b < nb; ++b) {
         const octopus_branch& B = d.br[b];
+        if (B.parent < 0) continue;  // the root of another tree: H = {}
         const octopus_branch& P = d.br[B.parent];
         std::vector<Interval> h = d.inherited[B.parent];
         if (B.fork > 0) h.push_back({P.start, (int64_t)P.start + B.fork});
@@ -349,17 +361,24 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
                 p.k_pairs[fill[p.q_pairs[i].tile]++] = {qt, p.q_pairs[i].mask};
     }
 
-    // Longest-first launch orders (ties by index).
-    p.fwd_order.resize(nQT);
-    std::iota(p.fwd_order.begin(), p.fwd_order.end(), 0);
-    std::stable_sort(p.fwd_order.begin(), p.fwd_order.end(), [&](int a, int b) {
-        return p.qt_ptr[a + 1] - p.qt_ptr[a] > p.qt_ptr[b + 1] - p.qt_ptr[b];
-    });
-    p.bwd_order.resize(nKT);
-    std::iota(p.bwd_order.begin(), p.bwd_order.end(), 0);
-    std::stable_sort(p.bwd_order.begin(), p.bwd_order.end(), [&](int a, int b) {
-        return p.kt_ptr[a + 1] - p.kt_ptr[a] > p.kt_ptr[b + 1] - p.kt_ptr[b];
-    });
+    // Launch orders: tree by tree (in the order of their root rows), longest list first
+    // inside a tree, ties by index.  A tile belongs to the tree of its first token.  One
+    // tree at a time keeps the K/V and Q/dO that concurrently running workgroups read
+    // as small as for a single tree; only the last tree's shortest tiles form the tail.
+    auto tree_of = [&](int64_t j) { return d.tree[row_branch[j]]; };
+    auto order = [&](std::vector<int32_t>& ord, int32_t n, const std::vector<int32_t>& ptr,
+                     int32_t rows_per) {
+        std::vector<int32_t> tr(n);
+        for (int32_t i = 0; i < n; ++i) tr[i] = tree_of((int64_t)i * rows_per);
+        ord.resize(n);
+        std::iota(ord.begin(), ord.end(), 0);
+        std::stable_sort(ord.begin(), ord.end(), [&](int a, int b) {
+            if (tr[a] != tr[b]) return tr[a] < tr[b];
+            return ptr[a + 1] - ptr[a] > ptr[b + 1] - ptr[b];
+        });
+    };
+    order(p.fwd_order, nQT, p.qt_ptr, Bq);
+    order(p.bwd_order, nKT, p.kt_ptr, Bk);
     // 128-key blocks: merge the transposed lists of tiles 2b and 2b+1.
     p.nKB = (nKT + 1) / 2;
     p.blk_ptr.assign(p.nKB + 1, 0);
@@ -379,11 +398,7 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
         }
         p.blk_ptr[b + 1] = (int32_t)p.blk_entries.size();
     }
-    p.blk_order.resize(p.nKB);
-    std::iota(p.blk_order.begin(), p.blk_order.end(), 0);
-    std::stable_sort(p.blk_order.begin(), p.blk_order.end(), [&](int a, int b) {
-        return p.blk_ptr[a + 1] - p.blk_ptr[a] > p.blk_ptr[b + 1] - p.blk_ptr[b];
-    });
+    order(p.blk_order, p.nKB, p.blk_ptr, 2 * Bk);
 
     p.max_q_list = 0;
     for (int32_t qt = 0; qt < nQT; ++qt)

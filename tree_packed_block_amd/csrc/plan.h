@@ -39,6 +39,7 @@ struct DagInfo {
     std::vector<std::vector<int32_t>> mounts_of;  // per reader: mount ids sorted by rpos
     std::vector<std::vector<Interval>> inherited;  // H(b), merged
     std::vector<int32_t> order_by_start;           // branches sorted by start
+    std::vector<int32_t> tree;                     // root row of every branch's tree
     std::vector<int64_t> pos;                      // position of every packed token
 
     // Ctx(g(b, r)) as sorted, disjoint, non-adjacent intervals (the query included).
