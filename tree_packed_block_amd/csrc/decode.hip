@@ -14,9 +14,12 @@
 // loaded into registers while the current one is computed.  Scores use the forward
 // kernel's transposed form S^T = K q^T (v_mfma_f32_32x32x16_bf16): the G query heads
 // of the KV head are the B operand's columns, so lane l holds head l % 32's scores
-// over 16 slots and the probabilities feed O^T += V^T P^T directly, with V staged
-// transposed in the wave's own LDS region.  Slots outside the segment are zero-filled
-// and masked.  The combine kernel merges the splits of each (cursor, head) by LSE.
+// over 16 slots and the probabilities feed O^T += V^T P^T directly.  K and V are
+// staged row-major in the wave's own LDS region, 16-byte chunks XOR-swizzled per row
+// so that the row writes, the row reads of K and the transposed reads of V
+// (ds_read_b64_tr_b16, giving the V^T operand) all hit distinct banks.  Slots outside
+// the segment are zero-filled and masked.  The combine kernel merges the splits of
+// each (cursor, head) by LSE.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -29,9 +32,9 @@ constexpr int kWaves = 4;
 
 template <int D>
 struct DecodeSmem {
-    static constexpr int KST = D + 8, VST = kPage + 8;
-    bf16 Ks[kPage * KST];
-    bf16 Vt[D * VST];
+    static constexpr int MAT = kPage * D * 2;  // bytes of one page-head block
+    unsigned char Ks[MAT];
+    unsigned char Vs[MAT];
 };
 
 }  // namespace
@@ -43,8 +46,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(
     const int32_t* __restrict__ seg_ptr, const int32_t* __restrict__ seg_page,
     const int32_t* __restrict__ seg_lo, const int32_t* __restrict__ seg_hi,
     float* __restrict__ partial) {
-    constexpr int KS = D / 16, DB = D / 32, C8 = D / 8;
-    constexpr int KST = DecodeSmem<D>::KST, VST = DecodeSmem<D>::VST;
+    constexpr int KS = D / 16, DB = D / 32, C8 = D / 8, ROWB = D * 2;
     __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kWaves * sizeof(DecodeSmem<D>)];
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -56,6 +58,23 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(
     const int c = item / (n_split * Hkv);
     const int G = Hq / Hkv;
     const int n = lane & 31, g = lane >> 5;
+    // Per-lane LDS byte offsets: K rows (A operand of S^T: row n, chunk 2ks + g; + 32
+    // rows for the second key block) and transposed V reads (rows 4g + r/4 (+8) of
+    // each 16-slot k-step, columns 32db + 16(l/16 % 2) + 4(r % 4), r = l % 16).
+    int ok_[KS], ov_[DB][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ok_[ks] = n * ROWB + swz<D>(n, 2 * ks + g) * 16;
+    {
+        const int r_in = lane & 15, dh = (lane >> 4) & 1;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int row = 4 * g + (r_in >> 2) + 8 * hf;
+                const int chunk = 4 * db + 2 * dh + ((r_in & 3) >> 1);
+                ov_[db][hf] = row * ROWB + swz<D>(row, chunk) * 16 + 8 * (r_in & 1);
+            }
+    }
 
     const int s0 = seg_ptr[c], s1 = seg_ptr[c + 1];
     const long long ns = s1 - s0;
@@ -104,13 +123,10 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(
         for (int it = 0; it < ITEMS; ++it) {
             const int rg = rg0 + LPR * it;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) st16(&S.Ks[(4 * rg + j) * KST + 8 * c8], kr[it][j]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                bf16x4 t;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) t[j] = vr[it][j][e];
-                st8(&S.Vt[(8 * c8 + e) * VST + 4 * rg], t);
+            for (int j = 0; j < 4; ++j) {
+                const int off = tile_off<D>(4 * rg + j, c8);
+                *reinterpret_cast<bf16x8*>(S.Ks + off) = kr[it][j];
+                *reinterpret_cast<bf16x8*>(S.Vs + off) = vr[it][j];
             }
         }
     };
@@ -134,8 +150,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(
             s[kb] = zero16();
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                s[kb] = mfma_32x32x16(ld16(&S.Ks[(kb * 32 + n) * KST + 16 * ks + 8 * g]), qf[ks],
-                                      s[kb]);
+                s[kb] = mfma_32x32x16(lds16(S.Ks, ok_[ks], kb * 32 * ROWB), qf[ks], s[kb]);
         }
         float mx = -INFINITY;
 #pragma unroll
@@ -175,8 +190,9 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const bf16* vrow = &S.Vt[(db * 32 + n) * VST + 16 * kk + 4 * g];
-                o[db] = mfma_32x32x16(cat(ld8(vrow), ld8(vrow + 8)), pf[kk], o[db]);
+                const bf16x8 a = cat(lds8_tr(S.Vs, ov_[db][0], 16 * kk * ROWB),
+                                     lds8_tr(S.Vs, ov_[db][1], 16 * kk * ROWB));
+                o[db] = mfma_32x32x16(a, pf[kk], o[db]);
             }
     }
 

@@ -170,6 +170,15 @@ __device__ __forceinline__ bf16x4 ld8_tr(const void* lds_addr) {
     return __builtin_bit_cast(bf16x4, v);
 }
 
+// LDS reads at a per-lane offset plus a constant (folded into the instruction's
+// immediate offset once loops are unrolled).
+__device__ __forceinline__ bf16x8 lds16(const unsigned char* smem, int lane_off, int imm) {
+    return *reinterpret_cast<const bf16x8*>(smem + lane_off + imm);
+}
+__device__ __forceinline__ bf16x4 lds8_tr(const unsigned char* smem, int lane_off, int imm) {
+    return ld8_tr(smem + lane_off + imm);
+}
+
 // 16-byte slot holding chunk `chunk` (8 elements) of row `row` in a row-major LDS tile
 // of 16-bit elements with D columns, XOR-swizzled by a function of the row's low bits
 // so that (a) 16 lanes reading the same chunk of 16 consecutive rows and (b) 16 lanes

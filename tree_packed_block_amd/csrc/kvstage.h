@@ -145,13 +145,5 @@ struct KvOffsets {
     }
 };
 
-// LDS reads at a per-lane offset plus a constant (folded into the instruction's
-// immediate offset once loops are unrolled).
-__device__ __forceinline__ bf16x8 lds16(const unsigned char* smem, int lane_off, int imm) {
-    return *reinterpret_cast<const bf16x8*>(smem + lane_off + imm);
-}
-__device__ __forceinline__ bf16x4 lds8_tr(const unsigned char* smem, int lane_off, int imm) {
-    return ld8_tr(smem + lane_off + imm);
-}
 
 }  // namespace octo
