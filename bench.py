@@ -228,14 +228,16 @@ def main():
     qd = torch.from_numpy(xd["q"]).to(device=dev, dtype=torch.bfloat16)
     kp = torch.from_numpy(xd["k_pool"]).to(device=dev, dtype=torch.bfloat16)
     vp = torch.from_numpy(xd["v_pool"]).to(device=dev, dtype=torch.bfloat16)
+    # Shared lists: the 16,384-token prefix all cursors inherit is one list, read once
+    # per block of cursors.
     seg0 = tpb.decode_segments(wl.dag.branches, wl.dag.mounts, wl.page_ptr, wl.pages,
-                               wl.page_size, wl.n_pages, wl.cursors)
+                               wl.page_size, wl.n_pages, wl.cursors, share=True)
     n_seg = int(seg0[1].size)
     B = len(wl.cursors)
-    seg_host = [[torch.empty(n, dtype=torch.int32, pin_memory=True)
-                 for n in (B + 1, n_seg, n_seg, n_seg)] for _ in range(2)]
-    seg_dev = [[torch.empty(n, dtype=torch.int32, device=dev) for n in (B + 1, n_seg, n_seg, n_seg)]
-               for _ in range(2)]
+    sizes = [int(a.size) for a in seg0]
+    seg_host = [[torch.empty(n, dtype=torch.int32, pin_memory=True) for n in sizes]
+                for _ in range(2)]
+    seg_dev = [[torch.empty(n, dtype=torch.int32, device=dev) for n in sizes] for _ in range(2)]
     od = torch.empty_like(qd)
     lsed = torch.empty((B, HQ), dtype=torch.float32, device=dev)
     wsd = torch.empty(tpb.decode_workspace_bytes(B, HQ, HD, args.n_split), dtype=torch.uint8,
@@ -245,7 +247,7 @@ def main():
                             for pg, lo, hi in zip(seg0[1], seg0[2], seg0[3])])
     n_unique = int(np.unique(codes).size)
     dec_bytes = (n_unique * HKV * HD * 2 * 2 + qd.numel() * 2 * 2 + lsed.numel() * 4
-                 + (B + 1 + 3 * n_seg) * 4)
+                 + sum(sizes) * 4)
     torch.cuda.synchronize()
     log(f"setup {time.perf_counter() - t0:.1f} s: T={dag.T} nnz={st['nnz']} "
         f"pairs={st['n_pairs']} decode segments={n_seg}")
@@ -256,7 +258,7 @@ def main():
     def host_prep():
         plan = tpb.Plan(dag.branches, dag.mounts, dag.T)
         segs = tpb.decode_segments(wl.dag.branches, wl.dag.mounts, wl.page_ptr, wl.pages,
-                                   wl.page_size, wl.n_pages, wl.cursors)
+                                   wl.page_size, wl.n_pages, wl.cursors, share=True)
         return plan, segs
 
     def enqueue(i, plan, segs, ev):

@@ -212,43 +212,59 @@ int octopus_dag_attn_bwd_dq(const octopus_plan* plan, octopus_dtype dtype, int32
  * lists.  page_ptr (int32[n_branches+1]) / pages (int32[page_ptr[n_branches]]) is
  * the page table: branch b's own token r lives in page pages[page_ptr[b] + r /
  * page_size], slot r % page_size.  cursors (int32[n_cursors]) are branch ids whose
- * last own token is the current query.  For cursor c the segments cover exactly
- * Ctx of that token (ancestor prefix, own branch, mounted spans, each key once) as
- * (page, slot_lo, slot_hi) runs in packed-key order.  Mounted keys are read from
- * the producer's own pages; no page is created.
- * Two calls: with seg_capacity < needed (e.g. 0) only *n_seg_out is set and the
- * call returns EWORKSPACE; then with room for *n_seg_out segments it fills
- * seg_ptr_out (int32[n_cursors+1]) and seg_page/lo/hi_out (int32[n_seg]).
- * Errors: EINVAL (tables, page ids outside [0, n_pages), short page table),
- * ECYCLE, EWORKSPACE. */
+ * last own token is the current query.  Segments are (page, slot_lo, slot_hi) runs;
+ * mounted keys are read from the producer's own pages; no page is created.
+ *
+ * share = 0: list c (c < n_cursors) covers exactly Ctx of cursor c's token (ancestor
+ * prefix, own branch, mounted spans, each key once), in packed-key order; n_groups is
+ * not written and the group arrays may be NULL.
+ * share != 0: the cursors are grouped by the (parent, fork) of their branches; all
+ * cursors of a group inherit the same context H (the shared radix prefix; primitives
+ * table, `fork`).  List c then covers Ctx minus H, and list n_cursors + g the H of group
+ * g; grp_ptr_out (int32[n_groups+1]) / grp_cur_out (int32[n_cursors]) list the cursors
+ * of every group, each cursor in exactly one group (a group with an empty H has an
+ * empty list).  The decode reads a shared list once per block of cursors instead of
+ * once per cursor.
+ *
+ * Two calls: with seg_capacity < needed (e.g. 0) only *n_seg_out (and *n_groups_out)
+ * are set and the call returns EWORKSPACE; then with room for *n_seg_out segments it
+ * fills seg_ptr_out (int32[n_cursors + n_groups + 1]; size it 2 n_cursors + 1 when
+ * sharing), seg_page/lo/hi_out (int32[n_seg]) and the group arrays.
+ * Errors: EINVAL (tables, page ids outside [0, n_pages), short page table, NULL
+ * outputs), ECYCLE, EWORKSPACE. */
 int octopus_decode_segments(const octopus_branch* branches, int32_t n_branches,
                             const octopus_mount* mounts, int32_t n_mounts,
                             const int32_t* page_ptr, const int32_t* pages,
                             int32_t page_size, int32_t n_pages, const int32_t* cursors,
-                            int32_t n_cursors, int32_t* seg_ptr_out,
+                            int32_t n_cursors, int32_t share, int32_t* seg_ptr_out,
                             int32_t* seg_page_out, int32_t* seg_lo_out,
                             int32_t* seg_hi_out, int32_t seg_capacity,
-                            int32_t* n_seg_out);
+                            int32_t* n_seg_out, int32_t* grp_ptr_out, int32_t* grp_cur_out,
+                            int32_t* n_groups_out);
 
 /* Workspace bytes for octopus_paged_mount_decode: float32 partial states
- * [B][n_split][Hq][D + 4]. */
+ * [B][2 n_split][Hq][D + 4] (own and shared lists). */
 size_t octopus_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t n_split);
 
 /* One-token attention of B cursors over their segments, read in place from the
  * pools.  q [B][Hq][D]; k_pool, v_pool [n_pages][Hkv][page_size][D] (dtype);
- * seg_* as produced by octopus_decode_segments, on the device; each cursor's
- * segments are split into n_split contiguous chunks (1 <= n_split <= 256) whose
- * partial softmax states are merged by LSE.  Writes o [B][Hq][D] (dtype) and, if
- * lse is not NULL, float32 [B][Hq].  Segments naming a page outside [0, n_pages)
- * are skipped.  Supported: bf16, D = 128, page_size = 64, Hq / Hkv <= 8.
+ * seg_* and, with n_groups > 0, grp_ptr / grp_cur as produced by
+ * octopus_decode_segments (n_groups = 0: share = 0 lists, group arrays ignored), on
+ * the device.  Every list is split into n_split contiguous chunks (1 <= n_split <=
+ * 256); the partial softmax states of a cursor's own chunks and of its group's shared
+ * chunks are merged by LSE.  Writes o [B][Hq][D] (dtype) and, if lse is not NULL,
+ * float32 [B][Hq].  Segments naming a page outside [0, n_pages) are skipped; group
+ * entries naming no cursor in [0, B) are ignored.  Supported: bf16, D = 128,
+ * page_size = 64, Hq / Hkv <= 8.
  * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP. */
 int octopus_paged_mount_decode(octopus_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
                                int32_t D, int32_t page_size, float scale, const void* q,
                                const void* k_pool, const void* v_pool, int32_t n_pages,
                                const int32_t* seg_ptr, const int32_t* seg_page,
                                const int32_t* seg_lo, const int32_t* seg_hi,
-                               int32_t n_split, void* o, float* lse, void* ws,
-                               size_t ws_bytes, void* stream);
+                               int32_t n_groups, const int32_t* grp_ptr,
+                               const int32_t* grp_cur, int32_t n_split, void* o, float* lse,
+                               void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- misc */
 

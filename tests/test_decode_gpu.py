@@ -19,12 +19,14 @@ def _decode_inputs(wl, Hq=16, Hkv=4, Dh=128, seed=55):
                                     wl.page_size)
 
 
-def _gpu_decode(wl, x, n_split, segs=None):
+def _gpu_decode(wl, x, n_split, segs=None, share=False):
+    """Through the C ABI; with ``share``, the inherited context of every group of cursors
+    is a list of its own, read once per block of cursors."""
     import torch
     import tree_packed_block_amd as tpb
     if segs is None:
         segs = tpb.decode_segments(wl.dag.branches, wl.dag.mounts, wl.page_ptr, wl.pages,
-                                   wl.page_size, wl.n_pages, wl.cursors)
+                                   wl.page_size, wl.n_pages, wl.cursors, share=share)
     sd = [torch.from_numpy(np.ascontiguousarray(s, dtype=np.int32)).cuda() for s in segs]
     q, kp, vp = dev(x["q"], "bf16"), dev(x["k_pool"], "bf16"), dev(x["v_pool"], "bf16")
     o, lse = tpb.paged_mount_decode(q, kp, vp, *sd, n_split=n_split)
@@ -37,13 +39,14 @@ def _oracle(wl, x):
                       wl.page_ptr, wl.pages, wl.page_size, wl.cursors)
 
 
+@pytest.mark.parametrize("share", [False, True])
 @pytest.mark.parametrize("n_split", [1, 3, 16])
-def test_decode_small(n_split):
-    say(f"case decode small n_split={n_split}")
+def test_decode_small(n_split, share):
+    say(f"case decode small n_split={n_split} share={share}")
     wl = synth.decode_workload(seed=5, n_cursors=6, prefix=256, own_max=300, span_max=100,
                                page_size=64)
     x = _decode_inputs(wl)
-    o, lse = _gpu_decode(wl, x, n_split)
+    o, lse = _gpu_decode(wl, x, n_split, share=share)
     ro, rl = _oracle(wl, x)
     check_close(o, ro, TOL["bf16"], "O")
     check_close(lse, rl, TOL["bf16"], "LSE")
@@ -63,6 +66,9 @@ def test_decode_full_batch():
     o2, lse2 = _gpu_decode(wl, x, 128)
     check_close(o2, ro, TOL["bf16"], "O (128 splits)")
     check_close(lse2, rl, TOL["bf16"], "LSE (128 splits)")
+    o3, lse3 = _gpu_decode(wl, x, 32, share=True)
+    check_close(o3, ro, TOL["bf16"], "O (shared prefix list)")
+    check_close(lse3, rl, TOL["bf16"], "LSE (shared prefix list)")
 
 
 def test_decode_matches_packed_forward():
@@ -87,6 +93,9 @@ def test_decode_matches_packed_forward():
                               np.arange(dag.nb, dtype=np.int32))
     xd = {"q": x["q"][last], "k_pool": kp, "v_pool": vp}
     od, ld = _gpu_decode(wl, xd, 4)
+    os_, ls_ = _gpu_decode(wl, xd, 4, share=True)
+    check_close(os_, od, TOL["bf16"], "decode O, shared lists vs whole lists")
+    check_close(ls_, ld, TOL["bf16"], "decode LSE, shared lists vs whole lists")
     plan = tpb.Plan(dag.branches, dag.mounts, dag.T).upload()
     of, lf = tpb.attn_fwd(plan, dev(x["q"], "bf16"), dev(x["k"], "bf16"), dev(x["v"], "bf16"))
     torch.cuda.synchronize()

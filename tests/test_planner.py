@@ -186,6 +186,59 @@ def test_decode_segments_match_oracle_full_size():
     assert set(pg.tolist()) <= set(wl.pages.tolist())
 
 
+def _check_shared_segments(wl):
+    """With sharing: groups partition the cursors, every group's cursors fork from one
+    (parent, fork), and a cursor's own list plus its group's list hold exactly its
+    context, each key once."""
+    B = len(wl.cursors)
+    sp, pg, lo, hi, gp, gc = tpb.decode_segments(wl.dag.branches, wl.dag.mounts,
+                                                 wl.page_ptr, wl.pages, wl.page_size,
+                                                 wl.n_pages, wl.cursors, share=True)
+    n_groups = len(gp) - 1
+    assert len(sp) == B + n_groups + 1 and gp[0] == 0 and gp[-1] == B
+    assert sorted(gc.tolist()) == list(range(B))
+    br = wl.dag.branches
+    shared = 0
+    for g in range(n_groups):
+        members = gc[gp[g]:gp[g + 1]]
+        assert len(members) >= 1
+        keys = {(int(br[wl.cursors[c], 0]), int(br[wl.cursors[c], 1]) if br[wl.cursors[c], 0] >= 0 else 0)
+                for c in members}
+        assert len(keys) == 1
+        gl = B + g
+        group_keys = [(int(pg[s]), x) for s in range(sp[gl], sp[gl + 1])
+                      for x in range(lo[s], hi[s])]
+        shared += len(group_keys)
+        for c in members:
+            b = int(wl.cursors[c])
+            idx = DEC.cursor_tokens(br, wl.dag.mounts, b)
+            page, slot = DEC.physical_slots(br, wl.page_ptr, wl.pages, wl.page_size, idx)
+            want = sorted(zip(page.tolist(), slot.tolist()))
+            own = [(int(pg[s]), x) for s in range(sp[c], sp[c + 1]) for x in range(lo[s], hi[s])]
+            assert sorted(own + group_keys) == want
+    return n_groups, shared
+
+
+def test_decode_shared_segments_full_size():
+    """64 cursors forked at the end of one 16,384-token prefix: one group whose list is
+    the prefix (256 pages of 64 slots), read once instead of 64 times."""
+    wl = synth.decode_workload()
+    n_groups, shared = _check_shared_segments(wl)
+    assert n_groups == 1 and shared == 16384
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_decode_shared_segments_fuzz(seed):
+    """Random forks (several groups, nested ones) and mounts that overlap what the
+    reader inherits; every branch is a cursor."""
+    rng = np.random.default_rng(seed)
+    dag = synth.fuzz_dag(rng, max_len=70, max_branches=7, max_mounts=5)
+    n_pages, ptr, pages = synth.dags.assign_pages(dag, 16, rng)
+    wl = synth.DecodeWorkload(dag, 16, n_pages, ptr, pages,
+                              np.arange(dag.nb, dtype=np.int32))
+    _check_shared_segments(wl)
+
+
 def test_decode_segments_errors():
     wl = synth.decode_workload(seed=5, n_cursors=4, prefix=64, own_max=100, page_size=16)
     bad_pages = wl.pages.copy()

@@ -96,14 +96,16 @@ def lib():
                                           _vp, _vp, ctypes.c_size_t, _vp]
     L.octopus_decode_segments.argtypes = [_vp, ctypes.c_int32, _vp, ctypes.c_int32, _vp, _vp,
                                           ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int32,
-                                          _vp, _vp, _vp, _vp, ctypes.c_int32, _i32p]
+                                          ctypes.c_int32, _vp, _vp, _vp, _vp, ctypes.c_int32,
+                                          _i32p, _vp, _vp, _i32p]
     L.octopus_decode_workspace_bytes.argtypes = [ctypes.c_int32] * 4
     L.octopus_decode_workspace_bytes.restype = ctypes.c_size_t
     L.octopus_paged_mount_decode.argtypes = [ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                              ctypes.c_float, _vp, _vp, _vp, ctypes.c_int32,
-                                             _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp,
-                                             ctypes.c_size_t, _vp]
+                                             _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp,
+                                             ctypes.c_int32, _vp, _vp, _vp, ctypes.c_size_t,
+                                             _vp]
     L.octopus_last_error.restype = ctypes.c_char_p
     L.octopus_version.restype = ctypes.c_char_p
     _lib = L
@@ -313,35 +315,50 @@ def attn_bwd_phase(phase, plan: Plan, q, k, v, o, lse, dout, ws, dq=None, dk=Non
 
 # ----------------------------------------------------------------------------- decode
 
-def decode_segments(branches, mounts, page_ptr, pages, page_size, n_pages, cursors):
-    """Host segment builder: returns int32 arrays ``(seg_ptr, seg_page, seg_lo,
-    seg_hi)``."""
+def decode_segments(branches, mounts, page_ptr, pages, page_size, n_pages, cursors,
+                    share=False):
+    """Host segment builder.  Returns int32 arrays ``(seg_ptr, seg_page, seg_lo,
+    seg_hi)`` with one list per cursor (its whole context); with ``share``, also
+    ``(grp_ptr, grp_cur)``: each cursor's list then holds only what it does not inherit,
+    followed by one list per group of cursors forked from the same (parent, fork) with
+    the context they all inherit (``seg_ptr`` has ``B + n_groups + 1`` entries)."""
     br, mt = _tables(branches, mounts)
     pp = np.ascontiguousarray(page_ptr, dtype=np.int32)
     pg = np.ascontiguousarray(pages, dtype=np.int32)
     cur = np.ascontiguousarray(cursors, dtype=np.int32)
+    B = cur.shape[0]
     n = ctypes.c_int32(0)
+    ng = ctypes.c_int32(0)
     L = lib()
     args = [_np_ptr(br), br.shape[0], _np_ptr(mt), mt.shape[0], _np_ptr(pp), _np_ptr(pg),
-            int(page_size), int(n_pages), _np_ptr(cur), cur.shape[0]]
-    rc = L.octopus_decode_segments(*args, None, None, None, None, 0, ctypes.byref(n))
+            int(page_size), int(n_pages), _np_ptr(cur), B, 1 if share else 0]
+    rc = L.octopus_decode_segments(*args, None, None, None, None, 0, ctypes.byref(n), None,
+                                   None, ctypes.byref(ng))
     if rc not in (OK, EWORKSPACE):
         _check(rc)
     cap = n.value
-    sp = np.zeros(cur.shape[0] + 1, dtype=np.int32)
+    sp = np.zeros(2 * B + 1, dtype=np.int32)
+    gp = np.zeros(B + 1, dtype=np.int32)
+    gc = np.zeros(max(B, 1), dtype=np.int32)
     out = [np.zeros(max(cap, 1), dtype=np.int32) for _ in range(3)]
     _check(L.octopus_decode_segments(*args, _np_ptr(sp), _np_ptr(out[0]), _np_ptr(out[1]),
-                                     _np_ptr(out[2]), cap, ctypes.byref(n)))
-    return sp, out[0][:cap], out[1][:cap], out[2][:cap]
+                                     _np_ptr(out[2]), cap, ctypes.byref(n), _np_ptr(gp),
+                                     _np_ptr(gc), ctypes.byref(ng)))
+    segs = (out[0][:cap], out[1][:cap], out[2][:cap])
+    if not share:
+        return (sp[:B + 1],) + segs
+    return (sp[:B + ng.value + 1],) + segs + (gp[:ng.value + 1], gc[:B])
 
 
 def decode_workspace_bytes(B, Hq, D, n_split) -> int:
     return int(lib().octopus_decode_workspace_bytes(B, Hq, D, n_split))
 
 
-def paged_mount_decode(q, k_pool, v_pool, seg_ptr, seg_page, seg_lo, seg_hi, n_split=16,
-                       scale=None, o=None, lse=None, ws=None, stream=None):
-    """One-token attention of every cursor over its segments (device int32 tensors).
+def paged_mount_decode(q, k_pool, v_pool, seg_ptr, seg_page, seg_lo, seg_hi, grp_ptr=None,
+                       grp_cur=None, n_split=16, scale=None, o=None, lse=None, ws=None,
+                       stream=None):
+    """One-token attention of every cursor over its segments (device int32 tensors, as
+    ``decode_segments`` returns them; ``grp_ptr``/``grp_cur`` with ``share``).
     Returns ``(o [B,Hq,D], lse float32 [B,Hq])``."""
     import torch
     B, Hq, D = q.shape
@@ -349,23 +366,34 @@ def paged_mount_decode(q, k_pool, v_pool, seg_ptr, seg_page, seg_lo, seg_hi, n_s
     _need(q, (B, Hq, D), q.dtype, "q")
     _need(k_pool, (n_pages, Hkv, page_size, D), q.dtype, "k_pool")
     _need(v_pool, (n_pages, Hkv, page_size, D), q.dtype, "v_pool")
-    for t, nm in ((seg_ptr, "seg_ptr"), (seg_page, "seg_page"), (seg_lo, "seg_lo"),
-                  (seg_hi, "seg_hi")):
+    arrays = [(seg_ptr, "seg_ptr"), (seg_page, "seg_page"), (seg_lo, "seg_lo"),
+              (seg_hi, "seg_hi")]
+    if (grp_ptr is None) != (grp_cur is None):
+        raise OctopusError(EINVAL, "grp_ptr and grp_cur go together")
+    n_groups = 0
+    if grp_ptr is not None:
+        arrays += [(grp_ptr, "grp_ptr"), (grp_cur, "grp_cur")]
+        n_groups = grp_ptr.numel() - 1
+        if grp_cur.numel() != B:
+            raise OctopusError(EINVAL, "grp_cur must have B entries")
+    for t, nm in arrays:
         if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
             raise OctopusError(EINVAL, f"{nm} must be a contiguous int32 device tensor")
-    if seg_ptr.numel() != B + 1:
-        raise OctopusError(EINVAL, "seg_ptr must have B + 1 entries")
+    if seg_ptr.numel() != B + n_groups + 1:
+        raise OctopusError(EINVAL, "seg_ptr must have B + n_groups + 1 entries")
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
     need = decode_workspace_bytes(B, Hq, D, n_split)
     if ws is None:
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     s = stream or torch.cuda.current_stream(q.device)
+    gp = grp_ptr.data_ptr() if grp_ptr is not None else None
+    gc = grp_cur.data_ptr() if grp_cur is not None else None
     _check(lib().octopus_paged_mount_decode(
         _dtype_code(q), B, Hq, Hkv, D, page_size, float(scale or 0.0), q.data_ptr(),
         k_pool.data_ptr(), v_pool.data_ptr(), n_pages, seg_ptr.data_ptr(), seg_page.data_ptr(),
-        seg_lo.data_ptr(), seg_hi.data_ptr(), int(n_split), o.data_ptr(), lse.data_ptr(),
-        ws.data_ptr(), ws.numel(), _vp(s.cuda_stream)))
+        seg_lo.data_ptr(), seg_hi.data_ptr(), n_groups, gp, gc, int(n_split), o.data_ptr(),
+        lse.data_ptr(), ws.data_ptr(), ws.numel(), _vp(s.cuda_stream)))
     return o, lse
 
 

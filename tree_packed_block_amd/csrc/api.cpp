@@ -306,9 +306,12 @@ int octopus_decode_segments(const octopus_branch* branches, int32_t n_branches,
                             const octopus_mount* mounts, int32_t n_mounts,
                             const int32_t* page_ptr, const int32_t* pages, int32_t page_size,
                             int32_t n_pages, const int32_t* cursors, int32_t n_cursors,
-                            int32_t* seg_ptr_out, int32_t* seg_page_out, int32_t* seg_lo_out,
-                            int32_t* seg_hi_out, int32_t seg_capacity, int32_t* n_seg_out) {
+                            int32_t share, int32_t* seg_ptr_out, int32_t* seg_page_out,
+                            int32_t* seg_lo_out, int32_t* seg_hi_out, int32_t seg_capacity,
+                            int32_t* n_seg_out, int32_t* grp_ptr_out, int32_t* grp_cur_out,
+                            int32_t* n_groups_out) {
     if (n_seg_out == nullptr) return fail(OCTOPUS_EINVAL, "n_seg_out is NULL");
+    if (share && n_groups_out == nullptr) return fail(OCTOPUS_EINVAL, "n_groups_out is NULL");
     try {
         if (n_branches < 1 || branches == nullptr) return fail(OCTOPUS_EINVAL, "no branches");
         int64_t T = 0;
@@ -318,21 +321,28 @@ int octopus_decode_segments(const octopus_branch* branches, int32_t n_branches,
         std::string err;
         int rc = octo::load_dag(branches, n_branches, mounts, n_mounts, (int32_t)T, dag, err);
         if (rc != OCTOPUS_OK) return fail(rc, err);
-        std::vector<int32_t> sp, pg, lo, hi;
+        std::vector<int32_t> sp, pg, lo, hi, gp, gc;
         rc = octo::build_segments(dag, page_ptr, pages, page_size, n_pages, cursors, n_cursors,
-                                  sp, pg, lo, hi, err);
+                                  share != 0, sp, pg, lo, hi, gp, gc, err);
         if (rc != OCTOPUS_OK) return fail(rc, err);
         if (pg.size() > (size_t)INT32_MAX) return fail(OCTOPUS_EINVAL, "too many segments");
         *n_seg_out = (int32_t)pg.size();
+        if (share) *n_groups_out = (int32_t)gp.size() - 1;
         if (seg_capacity < (int64_t)pg.size())
             return fail(OCTOPUS_EWORKSPACE, "segment capacity too small; need " +
                                                 std::to_string(pg.size()));
         if (!seg_ptr_out || !seg_page_out || !seg_lo_out || !seg_hi_out)
             return fail(OCTOPUS_EINVAL, "NULL output array");
+        if (share && (!grp_ptr_out || !grp_cur_out))
+            return fail(OCTOPUS_EINVAL, "NULL group output array");
         std::copy(sp.begin(), sp.end(), seg_ptr_out);
         std::copy(pg.begin(), pg.end(), seg_page_out);
         std::copy(lo.begin(), lo.end(), seg_lo_out);
         std::copy(hi.begin(), hi.end(), seg_hi_out);
+        if (share) {
+            std::copy(gp.begin(), gp.end(), grp_ptr_out);
+            std::copy(gc.begin(), gc.end(), grp_cur_out);
+        }
         return ok();
     } catch (const std::bad_alloc&) {
         return fail(OCTOPUS_ENOMEM, "host allocation failed while building segments");
@@ -341,14 +351,15 @@ int octopus_decode_segments(const octopus_branch* branches, int32_t n_branches,
 
 size_t octopus_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t n_split) {
     if (B < 1 || Hq < 1 || D < 1 || n_split < 1) return 0;
-    return (size_t)B * n_split * Hq * (D + 4) * sizeof(float);
+    return (size_t)B * 2 * n_split * Hq * (D + 4) * sizeof(float);
 }
 
 int octopus_paged_mount_decode(octopus_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
                                int32_t D, int32_t page_size, float scale, const void* q,
                                const void* k_pool, const void* v_pool, int32_t n_pages,
                                const int32_t* seg_ptr, const int32_t* seg_page,
-                               const int32_t* seg_lo, const int32_t* seg_hi, int32_t n_split,
+                               const int32_t* seg_lo, const int32_t* seg_hi, int32_t n_groups,
+                               const int32_t* grp_ptr, const int32_t* grp_cur, int32_t n_split,
                                void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
     if (dtype != OCTOPUS_BF16) return fail(OCTOPUS_EUNSUPPORTED, "decode supports bf16 only");
     if (D != 128) return fail(OCTOPUS_EUNSUPPORTED, "decode supports head_dim 128 only");
@@ -364,6 +375,9 @@ int octopus_paged_mount_decode(octopus_dtype dtype, int32_t B, int32_t Hq, int32
     }
     if (!seg_ptr || !seg_page || !seg_lo || !seg_hi)
         return fail(OCTOPUS_EINVAL, "segment arrays must not be NULL");
+    if (n_groups < 0 || n_groups > B) return fail(OCTOPUS_EINVAL, "n_groups must be in [0, B]");
+    if (n_groups > 0 && (!grp_ptr || !grp_cur))
+        return fail(OCTOPUS_EINVAL, "group arrays must not be NULL");
     const size_t need = octopus_decode_workspace_bytes(B, Hq, D, n_split);
     if (ws == nullptr || ws_bytes < need || !aligned(ws, 16))
         return fail(OCTOPUS_EWORKSPACE, "decode workspace needs " + std::to_string(need) +
@@ -371,8 +385,8 @@ int octopus_paged_mount_decode(octopus_dtype dtype, int32_t B, int32_t Hq, int32
     if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
     hipError_t e = octo::launch_decode_bf16(B, Hq, Hkv, D, page_size, scale, q, k_pool, v_pool,
                                             n_pages, seg_ptr, seg_page, seg_lo, seg_hi,
-                                            n_split, o, lse, static_cast<float*>(ws),
-                                            (hipStream_t)stream);
+                                            n_groups, grp_ptr, grp_cur, n_split, o, lse,
+                                            static_cast<float*>(ws), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return ok();
 }

@@ -39,12 +39,20 @@ struct DecodeSmem {
 
 }  // namespace
 
-template <int D>
+// Work items (one wave each): without GROUP, (cursor c, KV head, split) over c's own
+// segment list c.  With GROUP, (position p in grp_cur, KV head, split) over the shared
+// list B + gi of the group gi that holds p; only positions at the start of a block of
+// 32 / G cursors of the group work, and the MFMA's 32 query columns are those cursors'
+// G heads, so the group's pages are read once per block of cursors.  Split `split`
+// writes partial state slot `split` (own lists) or n_split + split (shared lists) of
+// each of its columns' (cursor, head).
+template <int D, bool GROUP>
 __global__ __launch_bounds__(256, 1) void decode_split_kernel(
-    int B, int Hq, int Hkv, int n_split, float scale_log2, const bf16* __restrict__ Qd,
-    const bf16* __restrict__ Kp, const bf16* __restrict__ Vp, int n_pages,
-    const int32_t* __restrict__ seg_ptr, const int32_t* __restrict__ seg_page,
-    const int32_t* __restrict__ seg_lo, const int32_t* __restrict__ seg_hi,
+    int B, int Hq, int Hkv, int n_split, int n_slots, float scale_log2,
+    const bf16* __restrict__ Qd, const bf16* __restrict__ Kp, const bf16* __restrict__ Vp,
+    int n_pages, const int32_t* __restrict__ seg_ptr, const int32_t* __restrict__ seg_page,
+    const int32_t* __restrict__ seg_lo, const int32_t* __restrict__ seg_hi, int n_groups,
+    const int32_t* __restrict__ grp_ptr, const int32_t* __restrict__ grp_cur,
     float* __restrict__ partial) {
     constexpr int KS = D / 16, DB = D / 32, C8 = D / 8, ROWB = D * 2;
     __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kWaves * sizeof(DecodeSmem<D>)];
@@ -58,6 +66,27 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(
     const int c = item / (n_split * Hkv);
     const int G = Hq / Hkv;
     const int n = lane & 31, g = lane >> 5;
+    int list = c, cursor = c, head = kvh * G + n;
+    bool col_ok = n < G;
+    if constexpr (GROUP) {
+        int lo_g = 0, hi_g = n_groups;  // the group gi with grp_ptr[gi] <= c < grp_ptr[gi+1]
+        while (hi_g - lo_g > 1) {
+            const int mid = (lo_g + hi_g) >> 1;
+            if (grp_ptr[mid] <= c) lo_g = mid; else hi_g = mid;
+        }
+        const int g0 = grp_ptr[lo_g], g1 = grp_ptr[lo_g + 1];
+        const int cpb = 32 / G;  // cursors per block of columns
+        if ((c - g0) % cpb != 0) return;
+        list = B + lo_g;
+        const int pos = c + n / G;
+        col_ok = n < cpb * G && pos < g1 && pos < B;
+        cursor = col_ok ? grp_cur[pos] : 0;
+        if (cursor < 0 || cursor >= B) {  // not a cursor: the column stays empty
+            col_ok = false;
+            cursor = 0;
+        }
+        head = kvh * G + n % G;
+    }
     // Per-lane LDS byte offsets: K rows (A operand of S^T: row n, chunk 2ks + g; + 32
     // rows for the second key block) and transposed V reads (rows 4g + r/4 (+8) of
     // each 16-slot k-step, columns 32db + 16(l/16 % 2) + 4(r % 4), r = l % 16).
@@ -76,15 +105,14 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(
             }
     }
 
-    const int s0 = seg_ptr[c], s1 = seg_ptr[c + 1];
+    const int s0 = seg_ptr[list], s1 = seg_ptr[list + 1];
     const long long ns = s1 - s0;
     const int a = s0 + (int)((ns * split) / n_split);
     const int b = s0 + (int)((ns * (split + 1)) / n_split);
 
-    // B operand: column n is query head kvh*G + n (zero for n >= G).
+    // B operand: column n is query (cursor, head) (zero where col_ok is false).
     bf16x8 qf[KS];
-    const bool col_ok = n < G;
-    const bf16* qrow = Qd + ((size_t)c * Hq + (size_t)kvh * G + (col_ok ? n : 0)) * D;
+    const bf16* qrow = Qd + ((size_t)cursor * Hq + (col_ok ? head : 0)) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = col_ok ? ld16(qrow + 16 * ks + 8 * g) : zero8();
 
@@ -198,8 +226,8 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(
 
     l += __shfl_xor(l, 32);
     if (col_ok) {
-        const int h = kvh * G + n;
-        float* out = partial + (((size_t)c * n_split + split) * Hq + h) * (D + 4);
+        const int slot = GROUP ? n_split + split : split;
+        float* out = partial + (((size_t)cursor * n_slots + slot) * Hq + head) * (D + 4);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -215,25 +243,25 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(
     }
 }
 
-// Merge the n_split partial states of every (cursor, query head): one wave each.
+// Merge the n_slots partial states of every (cursor, query head): one wave each.
 // A partial state is D accumulator floats, the running max (log2 units), the running
 // sum, and 2 floats of padding so every state starts 16-byte aligned.
 template <int D>
-__global__ __launch_bounds__(64) void decode_combine_kernel(int B, int Hq, int n_split,
+__global__ __launch_bounds__(64) void decode_combine_kernel(int B, int Hq, int n_slots,
                                                             const float* __restrict__ partial,
                                                             bf16* __restrict__ O,
                                                             float* __restrict__ LSE) {
     const int c = blockIdx.x / Hq, h = blockIdx.x % Hq;
     const int lane = threadIdx.x;
     float M = -INFINITY;
-    for (int sp = 0; sp < n_split; ++sp)
-        M = fmaxf(M, partial[(((size_t)c * n_split + sp) * Hq + h) * (D + 4) + D]);
+    for (int sp = 0; sp < n_slots; ++sp)
+        M = fmaxf(M, partial[(((size_t)c * n_slots + sp) * Hq + h) * (D + 4) + D]);
     float L = 0.f;
     float acc[D / 64];
 #pragma unroll
     for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
-    for (int sp = 0; sp < n_split; ++sp) {
-        const float* p = partial + (((size_t)c * n_split + sp) * Hq + h) * (D + 4);
+    for (int sp = 0; sp < n_slots; ++sp) {
+        const float* p = partial + (((size_t)c * n_slots + sp) * Hq + h) * (D + 4);
         const float ms = p[D];
         if (ms == -INFINITY) continue;
         const float wgt = fast_exp2(ms - M);
@@ -251,16 +279,23 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(int B, int Hq, int n
 hipError_t launch_decode_bf16(int B, int Hq, int Hkv, int D, int page_size, float scale,
                               const void* q, const void* k_pool, const void* v_pool,
                               int n_pages, const int32_t* seg_ptr, const int32_t* seg_page,
-                              const int32_t* seg_lo, const int32_t* seg_hi, int n_split,
+                              const int32_t* seg_lo, const int32_t* seg_hi, int n_groups,
+                              const int32_t* grp_ptr, const int32_t* grp_cur, int n_split,
                               void* o, float* lse, float* partial, hipStream_t s) {
     (void)page_size;
     (void)D;  // checked by the caller: D == 128, page_size == 64
-    const int items = B * Hkv * n_split;
-    hipLaunchKernelGGL(decode_split_kernel<128>, dim3((items + kWaves - 1) / kWaves),
-                       dim3(64 * kWaves), 0, s, B, Hq, Hkv, n_split, scale * kLog2e,
-                       (const bf16*)q, (const bf16*)k_pool, (const bf16*)v_pool, n_pages,
-                       seg_ptr, seg_page, seg_lo, seg_hi, partial);
-    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(B * Hq), dim3(64), 0, s, B, Hq, n_split,
+    const int n_slots = n_groups > 0 ? 2 * n_split : n_split;
+    const dim3 grid((B * Hkv * n_split + kWaves - 1) / kWaves), block(64 * kWaves);
+    hipLaunchKernelGGL((decode_split_kernel<128, false>), grid, block, 0, s, B, Hq, Hkv, n_split,
+                       n_slots, scale * kLog2e, (const bf16*)q, (const bf16*)k_pool,
+                       (const bf16*)v_pool, n_pages, seg_ptr, seg_page, seg_lo, seg_hi, n_groups,
+                       grp_ptr, grp_cur, partial);
+    if (n_groups > 0)
+        hipLaunchKernelGGL((decode_split_kernel<128, true>), grid, block, 0, s, B, Hq, Hkv,
+                           n_split, n_slots, scale * kLog2e, (const bf16*)q, (const bf16*)k_pool,
+                           (const bf16*)v_pool, n_pages, seg_ptr, seg_page, seg_lo, seg_hi,
+                           n_groups, grp_ptr, grp_cur, partial);
+    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(B * Hq), dim3(64), 0, s, B, Hq, n_slots,
                        partial, (bf16*)o, lse);
     return hipGetLastError();
 }

@@ -59,10 +59,13 @@ hipError_t launch_bwd_dkdv(bool bf16, const DevPlan& p, int Hq, int Hkv, int D, 
 hipError_t launch_bwd_dq(bool bf16, const DevPlan& p, int Hq, int Hkv, int D, float scale,
                          const void* q, const void* k, const void* v, const void* dout,
                          float* ws, void* dq, hipStream_t s);
+// Decode: per-cursor segment lists 0..B-1, then (n_groups > 0) one shared list per group
+// of cursors (grp_ptr / grp_cur).  partial: float32 [B][2 n_split][Hq][D + 4].
 hipError_t launch_decode_bf16(int B, int Hq, int Hkv, int D, int page_size, float scale,
                               const void* q, const void* k_pool, const void* v_pool,
                               int n_pages, const int32_t* seg_ptr, const int32_t* seg_page,
-                              const int32_t* seg_lo, const int32_t* seg_hi, int n_split,
+                              const int32_t* seg_lo, const int32_t* seg_hi, int n_groups,
+                              const int32_t* grp_ptr, const int32_t* grp_cur, int n_split,
                               void* o, float* lse, float* partial, hipStream_t s);
 
 }  // namespace octo

@@ -2,6 +2,7 @@
 #include "plan.h"
 
 #include <algorithm>
+#include <map>
 #include <climits>
 #include <cstring>
 #include <numeric>
@@ -473,9 +474,10 @@ void export_mask(const Plan& p, int32_t lo, int32_t hi, uint8_t* bits) {
 
 int build_segments(const DagInfo& d, const int32_t* page_ptr, const int32_t* pages,
                    int32_t page_size, int32_t n_pages, const int32_t* cursors,
-                   int32_t n_cursors, std::vector<int32_t>& seg_ptr,
+                   int32_t n_cursors, bool share, std::vector<int32_t>& seg_ptr,
                    std::vector<int32_t>& seg_page, std::vector<int32_t>& seg_lo,
-                   std::vector<int32_t>& seg_hi, std::string& err) {
+                   std::vector<int32_t>& seg_hi, std::vector<int32_t>& grp_ptr,
+                   std::vector<int32_t>& grp_cur, std::string& err) {
     const int32_t nb = (int32_t)d.br.size();
     if (page_size < 1 || n_pages < 0 || n_cursors < 0 || page_ptr == nullptr ||
         (n_cursors > 0 && cursors == nullptr)) {
@@ -496,19 +498,21 @@ int build_segments(const DagInfo& d, const int32_t* page_ptr, const int32_t* pag
             }
         }
     }
-    seg_ptr.assign(n_cursors + 1, 0);
-    seg_page.clear();
-    seg_lo.clear();
-    seg_hi.clear();
-    std::vector<Interval> ctx, scratch;
     for (int32_t c = 0; c < n_cursors; ++c) {
-        const int32_t b = cursors[c];
-        if (b < 0 || b >= nb) {
+        if (cursors[c] < 0 || cursors[c] >= nb) {
             err = row_msg("cursor", c, "branch id out of range");
             return OCTOPUS_EINVAL;
         }
-        d.row_context(b, d.br[b].len - 1, ctx, scratch);
-        for (const Interval& iv : ctx) {
+    }
+    seg_ptr.assign(1, 0);
+    seg_page.clear();
+    seg_lo.clear();
+    seg_hi.clear();
+    grp_ptr.clear();
+    grp_cur.clear();
+    // One segment per (owning branch, page) run of the intervals, in order.
+    auto emit = [&](const std::vector<Interval>& ivs) {
+        for (const Interval& iv : ivs) {
             int64_t j = iv.lo;
             while (j < iv.hi) {
                 const int32_t o = d.owner(j);
@@ -528,7 +532,57 @@ int build_segments(const DagInfo& d, const int32_t* page_ptr, const int32_t* pag
                 j = stop;
             }
         }
-        seg_ptr[c + 1] = (int32_t)seg_page.size();
+        seg_ptr.push_back((int32_t)seg_page.size());
+    };
+    std::vector<Interval> ctx, scratch, rest;
+    for (int32_t c = 0; c < n_cursors; ++c) {
+        const int32_t b = cursors[c];
+        d.row_context(b, d.br[b].len - 1, ctx, scratch);
+        if (!share) {
+            emit(ctx);
+            continue;
+        }
+        // ctx minus H(b): both sorted and disjoint, and H(b) lies inside ctx.
+        const std::vector<Interval>& h = d.inherited[b];
+        rest.clear();
+        size_t k = 0;
+        for (const Interval& iv : ctx) {
+            int64_t lo = iv.lo;
+            while (k < h.size() && h[k].hi <= lo) ++k;
+            size_t t = k;
+            while (lo < iv.hi) {
+                if (t < h.size() && h[t].lo < iv.hi) {
+                    if (h[t].lo > lo) rest.push_back({lo, h[t].lo});
+                    lo = std::max(lo, (int64_t)h[t].hi);
+                    ++t;
+                } else {
+                    rest.push_back({lo, iv.hi});
+                    lo = iv.hi;
+                }
+            }
+        }
+        emit(rest);
+    }
+    if (share) {
+        // Groups: cursors forked from the same (parent, fork) inherit the same context.
+        std::map<std::pair<int32_t, int32_t>, int32_t> gid;
+        std::vector<std::vector<int32_t>> members;
+        for (int32_t c = 0; c < n_cursors; ++c) {
+            const octopus_branch& B = d.br[cursors[c]];
+            const auto key = std::make_pair(B.parent, B.parent < 0 ? 0 : B.fork);
+            auto it = gid.find(key);
+            if (it == gid.end()) {
+                it = gid.emplace(key, (int32_t)members.size()).first;
+                members.emplace_back();
+            }
+            members[it->second].push_back(c);
+        }
+        grp_ptr.assign(1, 0);
+        for (const auto& m : members) {
+            emit(d.inherited[cursors[m[0]]]);
+            grp_cur.insert(grp_cur.end(), m.begin(), m.end());
+            grp_ptr.push_back((int32_t)grp_cur.size());
+        }
     }
     return OCTOPUS_OK;
 }

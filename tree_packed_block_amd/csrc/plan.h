@@ -94,10 +94,15 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
 // Dense bits of rows [lo, hi) from the tile lists only (see octopus_plan_export_mask).
 void export_mask(const Plan& p, int32_t lo, int32_t hi, uint8_t* bits);
 
+// Decode segments of every cursor (see octopus_decode_segments).  With `share`, each
+// cursor's list holds only what it does not inherit, and the inherited context of every
+// group of cursors forked from the same (parent, fork) follows as one list per group;
+// grp_ptr / grp_cur list the cursors of each group.
 int build_segments(const DagInfo& dag, const int32_t* page_ptr, const int32_t* pages,
                    int32_t page_size, int32_t n_pages, const int32_t* cursors,
-                   int32_t n_cursors, std::vector<int32_t>& seg_ptr,
+                   int32_t n_cursors, bool share, std::vector<int32_t>& seg_ptr,
                    std::vector<int32_t>& seg_page, std::vector<int32_t>& seg_lo,
-                   std::vector<int32_t>& seg_hi, std::string& err);
+                   std::vector<int32_t>& seg_hi, std::vector<int32_t>& grp_ptr,
+                   std::vector<int32_t>& grp_cur, std::string& err);
 
 }  // namespace octo
