@@ -29,6 +29,13 @@ namespace {
 
 constexpr int kPage = 64;
 constexpr int kWaves = 4;
+// Word 3 of a raw buffer resource on gfx9-family chips (32-bit data format, no swizzle).
+constexpr int kBufferWord3 = 0x00020000;
+
+// A segment is read only if its page is in the pool and its slot range is well formed.
+__device__ __forceinline__ bool seg_ok(int page, int lo, int hi, int n_pages) {
+    return page >= 0 && page < n_pages && lo >= 0 && lo < hi && hi <= kPage;
+}
 
 template <int D>
 struct DecodeSmem {
@@ -39,14 +46,14 @@ struct DecodeSmem {
 
 }  // namespace
 
-// Work items (one wave each): without GROUP, (cursor c, KV head, split) over c's own
-// segment list c.  With GROUP, (position p in grp_cur, KV head, split) over the shared
-// list B + gi of the group gi that holds p; only positions at the start of a block of
-// 32 / G cursors of the group work, and the MFMA's 32 query columns are those cursors'
-// G heads, so the group's pages are read once per block of cursors.  Split `split`
-// writes partial state slot `split` (own lists) or n_split + split (shared lists) of
-// each of its columns' (cursor, head).
-template <int D, bool GROUP>
+// Work items (one wave each).  Own items: (cursor c, KV head, split) over c's own
+// segment list c.  Group items (with n_groups > 0, launched first in the same grid):
+// (position p in grp_cur, KV head, split) over the shared list B + gi of the group gi
+// that holds p; only positions at the start of a block of 32 / G cursors of the group
+// work, and the MFMA's 32 query columns are those cursors' G heads, so the group's pages
+// are read once per block of cursors.  Split `split` writes partial state slot `split`
+// (own lists) or n_split + split (shared lists) of each of its columns' (cursor, head).
+template <int D>
 __global__ __launch_bounds__(256, 1) void decode_split_kernel(
     int B, int Hq, int Hkv, int n_split, int n_slots, float scale_log2,
     const bf16* __restrict__ Qd, const bf16* __restrict__ Kp, const bf16* __restrict__ Vp,
@@ -57,9 +64,13 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(
     constexpr int KS = D / 16, DB = D / 32, C8 = D / 8, ROWB = D * 2;
     __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kWaves * sizeof(DecodeSmem<D>)];
 
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int item = blockIdx.x * kWaves + w;
-    if (item >= B * Hkv * n_split) return;  // whole wave leaves; no block barriers below
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int per = B * Hkv * n_split;  // items of each kind
+    int item = blockIdx.x * kWaves + w;
+    if (item >= (n_groups > 0 ? 2 * per : per)) return;  // whole wave leaves; no block barriers below
+    const bool grp = n_groups > 0 && item < per;  // wave-uniform
+    if (n_groups > 0 && !grp) item -= per;
     DecodeSmem<D>& S = reinterpret_cast<DecodeSmem<D>*>(smem_raw)[w];
     const int split = item % n_split;
     const int kvh = (item / n_split) % Hkv;
@@ -68,7 +79,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(
     const int n = lane & 31, g = lane >> 5;
     int list = c, cursor = c, head = kvh * G + n;
     bool col_ok = n < G;
-    if constexpr (GROUP) {
+    if (grp) {
         int lo_g = 0, hi_g = n_groups;  // the group gi with grp_ptr[gi] <= c < grp_ptr[gi+1]
         while (hi_g - lo_g > 1) {
             const int mid = (lo_g + hi_g) >> 1;
@@ -127,23 +138,35 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(
     constexpr int ITEMS = RGS / LPR;      // row groups per lane
     const int c8 = lane % C8, rg0 = lane / C8;
     bf16x8 kr[ITEMS][4], vr[ITEMS][4];
+    // Byte offset (within a page-head block) of the first row this lane copies in pass
+    // `it`; its rows are 4 (rg0 + LPR it) + j, j = 0..3, chunk c8.
+    unsigned loff[ITEMS];
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) loff[it] = (unsigned)(4 * (rg0 + LPR * it) * ROWB + 16 * c8);
+    // Raw buffer loads through a resource that spans exactly slots [lo, hi) of the
+    // page-head block: slots outside it read as zero with no branch, and nothing outside
+    // the block is ever read (a segment that is not valid gets an empty resource).
+    // Offsets are relative to slot lo; below it they wrap to huge values, which are out
+    // of range too.
     auto gload = [&](int sg) {
         const int page = seg_page[sg], lo = seg_lo[sg], hi = seg_hi[sg];
-        const bool ok = page >= 0 && page < n_pages;
-        const size_t base = ((size_t)(ok ? page : 0) * Hkv + kvh) * kPage * D;
+        const bool ok = seg_ok(page, lo, hi, n_pages);
+        const size_t blk = (((size_t)(ok ? page : 0) * Hkv + kvh) * kPage + (ok ? lo : 0)) * ROWB;
+        const int bytes = ok ? (hi - lo) * ROWB : 0;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<unsigned char*>(reinterpret_cast<const unsigned char*>(Kp) + blk), 0, bytes,
+            kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<unsigned char*>(reinterpret_cast<const unsigned char*>(Vp) + blk), 0, bytes,
+            kBufferWord3);
+        const unsigned sub = (unsigned)((ok ? lo : 0) * ROWB);
 #pragma unroll
         for (int it = 0; it < ITEMS; ++it)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int slot = 4 * (rg0 + LPR * it) + j;
-                if (ok && slot >= lo && slot < hi) {
-                    const size_t off = base + (size_t)slot * D + 8 * c8;
-                    kr[it][j] = ld16(Kp + off);
-                    vr[it][j] = ld16(Vp + off);
-                } else {
-                    kr[it][j] = zero8();
-                    vr[it][j] = zero8();
-                }
+                const int off = (int)(loff[it] + (unsigned)(j * ROWB) - sub);
+                kr[it][j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+                vr[it][j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
             }
     };
     auto lds_put = [&]() {
@@ -162,7 +185,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(
     if (a < b) gload(a);
     for (int sg = a; sg < b; ++sg) {
         const int lo = seg_lo[sg], hi = seg_hi[sg];
-        const bool ok = seg_page[sg] >= 0 && seg_page[sg] < n_pages;
+        const bool ok = seg_ok(seg_page[sg], lo, hi, n_pages);
         // The wave's previous reads of its LDS region come before these writes, and
         // these writes before the reads below: one wave's LDS operations stay in order.
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -226,7 +249,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(
 
     l += __shfl_xor(l, 32);
     if (col_ok) {
-        const int slot = GROUP ? n_split + split : split;
+        const int slot = grp ? n_split + split : split;
         float* out = partial + (((size_t)cursor * n_slots + slot) * Hq + head) * (D + 4);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -245,7 +268,9 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(
 
 // Merge the n_slots partial states of every (cursor, query head): one wave each.
 // A partial state is D accumulator floats, the running max (log2 units), the running
-// sum, and 2 floats of padding so every state starts 16-byte aligned.
+// sum, and 2 floats of padding so every state starts 16-byte aligned.  Every slot is
+// written by the split pass (an empty one as max -inf, sum 0, zero accumulator), so
+// the lanes read 64 slots' maxima at once and the accumulation needs no branch.
 template <int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(int B, int Hq, int n_slots,
                                                             const float* __restrict__ partial,
@@ -253,22 +278,44 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(int B, int Hq, int n
                                                             float* __restrict__ LSE) {
     const int c = blockIdx.x / Hq, h = blockIdx.x % Hq;
     const int lane = threadIdx.x;
+    const size_t sstride = (size_t)Hq * (D + 4);  // floats between consecutive slots
+    const float* base = partial + ((size_t)c * n_slots * Hq + h) * (D + 4);
     float M = -INFINITY;
-    for (int sp = 0; sp < n_slots; ++sp)
-        M = fmaxf(M, partial[(((size_t)c * n_slots + sp) * Hq + h) * (D + 4) + D]);
+    for (int j = lane; j < n_slots; j += 64) M = fmaxf(M, base[j * sstride + D]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     float L = 0.f;
     float acc[D / 64];
 #pragma unroll
     for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
-    for (int sp = 0; sp < n_slots; ++sp) {
-        const float* p = partial + (((size_t)c * n_slots + sp) * Hq + h) * (D + 4);
-        const float ms = p[D];
-        if (ms == -INFINITY) continue;
-        const float wgt = fast_exp2(ms - M);
-        L += wgt * p[D + 1];
+    for (int j0 = 0; j0 < n_slots; j0 += 64) {
+        const int j = j0 + lane;
+        float wj = 0.f;
+        if (j < n_slots) {
+            const float mj = base[j * sstride + D];
+            wj = mj == -INFINITY ? 0.f : fast_exp2(mj - M);
+            L += wj * base[j * sstride + D + 1];
+        }
+        const int nj = min(64, n_slots - j0);
+        int t = 0;
+        for (; t + 8 <= nj; t += 8) {
 #pragma unroll
-        for (int e = 0; e < D / 64; ++e) acc[e] += wgt * p[lane + 64 * e];
+            for (int u = 0; u < 8; ++u) {
+                const float w = __shfl(wj, t + u);
+                const float* p = base + (size_t)(j0 + t + u) * sstride;
+#pragma unroll
+                for (int e = 0; e < D / 64; ++e) acc[e] += w * p[lane + 64 * e];
+            }
+        }
+        for (; t < nj; ++t) {
+            const float w = __shfl(wj, t);
+            const float* p = base + (size_t)(j0 + t) * sstride;
+#pragma unroll
+            for (int e = 0; e < D / 64; ++e) acc[e] += w * p[lane + 64 * e];
+        }
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
     const float inv = 1.f / L;
 #pragma unroll
     for (int e = 0; e < D / 64; ++e)
@@ -285,16 +332,11 @@ hipError_t launch_decode_bf16(int B, int Hq, int Hkv, int D, int page_size, floa
     (void)page_size;
     (void)D;  // checked by the caller: D == 128, page_size == 64
     const int n_slots = n_groups > 0 ? 2 * n_split : n_split;
-    const dim3 grid((B * Hkv * n_split + kWaves - 1) / kWaves), block(64 * kWaves);
-    hipLaunchKernelGGL((decode_split_kernel<128, false>), grid, block, 0, s, B, Hq, Hkv, n_split,
-                       n_slots, scale * kLog2e, (const bf16*)q, (const bf16*)k_pool,
-                       (const bf16*)v_pool, n_pages, seg_ptr, seg_page, seg_lo, seg_hi, n_groups,
-                       grp_ptr, grp_cur, partial);
-    if (n_groups > 0)
-        hipLaunchKernelGGL((decode_split_kernel<128, true>), grid, block, 0, s, B, Hq, Hkv,
-                           n_split, n_slots, scale * kLog2e, (const bf16*)q, (const bf16*)k_pool,
-                           (const bf16*)v_pool, n_pages, seg_ptr, seg_page, seg_lo, seg_hi,
-                           n_groups, grp_ptr, grp_cur, partial);
+    const int items = (n_groups > 0 ? 2 : 1) * B * Hkv * n_split;
+    hipLaunchKernelGGL(decode_split_kernel<128>, dim3((items + kWaves - 1) / kWaves),
+                       dim3(64 * kWaves), 0, s, B, Hq, Hkv, n_split, n_slots, scale * kLog2e,
+                       (const bf16*)q, (const bf16*)k_pool, (const bf16*)v_pool, n_pages, seg_ptr,
+                       seg_page, seg_lo, seg_hi, n_groups, grp_ptr, grp_cur, partial);
     hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(B * Hq), dim3(64), 0, s, B, Hq, n_slots,
                        partial, (bf16*)o, lse);
     return hipGetLastError();
