@@ -47,7 +47,9 @@ struct DecodeSmem {
 }  // namespace
 
 // Work items (one wave each).  Own items: (cursor c, KV head, split) over c's own
-// segment list c.  Group items (with n_groups > 0, launched first in the same grid):
+// segment list c; the 4 waves of a workgroup take consecutive splits of one (cursor,
+// head), which keeps their lengths alike.  Group items (with n_groups > 0, after the
+// own items in the same grid):
 // (position p in grp_cur, KV head, split) over the shared list B + gi of the group gi
 // that holds p; only positions at the start of a block of 32 / G cursors of the group
 // work, and the MFMA's 32 query columns are those cursors' G heads, so the group's pages
@@ -69,8 +71,8 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(
     const int per = B * Hkv * n_split;  // items of each kind
     int item = blockIdx.x * kWaves + w;
     if (item >= (n_groups > 0 ? 2 * per : per)) return;  // whole wave leaves; no block barriers below
-    const bool grp = n_groups > 0 && item < per;  // wave-uniform
-    if (n_groups > 0 && !grp) item -= per;
+    const bool grp = n_groups > 0 && item >= per;  // wave-uniform
+    if (grp) item -= per;
     DecodeSmem<D>& S = reinterpret_cast<DecodeSmem<D>*>(smem_raw)[w];
     const int split = item % n_split;
     const int kvh = (item / n_split) % Hkv;
