@@ -13,6 +13,12 @@ physical page of the branch that owns it:
 
 Pools are ``[n_pages, Hkv, page_size, D]``; queries ``[B, Hq, D]`` are the current
 tokens' (already rotated) queries.
+
+Extend (prefill of several new tokens per cursor, the step that appends a turn's delta
+to a cursor whose earlier context is already in pages): cursor ``c`` adds its branch's
+last ``m_c`` own tokens, already written to its pages; each of them attends to ``Ctx``
+of its own packed index, so the new tokens see each other causally, and a span mounted
+at a reader offset inside the new tokens is seen from that offset on.
 """
 
 from __future__ import annotations
@@ -79,3 +85,42 @@ def unique_tokens(branches, mounts, cursors) -> int:
     for b in np.asarray(cursors):
         seen[cursor_tokens(branches, mounts, int(b))] = True
     return int(seen.sum())
+
+
+def extend(q, k_pool, v_pool, branches, mounts, page_ptr, pages, page_size, cursors, q_ptr,
+           scale=None):
+    """Attention of the new tokens of every cursor.  ``q_ptr`` (``[B+1]``) delimits the
+    rows of ``q`` (``[n_rows, Hq, D]``) that belong to each cursor: rows
+    ``q_ptr[c] .. q_ptr[c+1]-1`` are the last ``m_c = q_ptr[c+1] - q_ptr[c]`` own tokens
+    of branch ``cursors[c]``, in order.  Returns ``O`` float64 ``[n_rows, Hq, D]`` and
+    ``LSE`` float64 ``[n_rows, Hq]``."""
+    n_rows, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    br = np.asarray(branches).reshape(-1, 4)
+    T = int(br[:, 3].sum())
+    owner = dagmod.branch_of(br, T)
+    O = np.zeros((n_rows, Hq, D))
+    LSE = np.zeros((n_rows, Hq))
+    for c, b in enumerate(np.asarray(cursors)):
+        r0, r1 = int(q_ptr[c]), int(q_ptr[c + 1])
+        m = r1 - r0
+        if m == 0:
+            continue
+        start, L = int(br[b, 2]), int(br[b, 3])
+        rows = dagmod.mask_rows(branches, mounts, T, start + L - m, start + L)  # [m, T]
+        for j in range(m):
+            idx = np.flatnonzero(rows[j])
+            page, slot = physical_slots(br, page_ptr, pages, page_size, idx, owner)
+            K = k_pool[page, :, slot, :].astype(np.float64)
+            V = v_pool[page, :, slot, :].astype(np.float64)
+            for h in range(Hq):
+                kk = h // G
+                s_ = scale * (K[:, kk, :] @ q[r0 + j, h].astype(np.float64))
+                mx = s_.max()
+                p = np.exp(s_ - mx)
+                l = p.sum()
+                O[r0 + j, h] = (p @ V[:, kk, :]) / l
+                LSE[r0 + j, h] = mx + np.log(l)
+    return O, LSE
