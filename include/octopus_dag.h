@@ -266,6 +266,49 @@ int octopus_paged_mount_decode(octopus_dtype dtype, int32_t B, int32_t Hq, int32
                                const int32_t* grp_cur, int32_t n_split, void* o, float* lse,
                                void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- paged extend */
+
+/* Host helper for extend (prefill of several new tokens per cursor: a continuation
+ * sends only its new tokens, ia.com.br article, section on O(|Δm|) deltas).  Cursor c's
+ * new tokens are the last n_new[c] own tokens of branch cursors[c] (1 <= n_new[c] <=
+ * branch length), already written to its pages.  The segments of cursor c cover the
+ * context of its last token, each (page, slot_lo, slot_hi) with a threshold thr: a new
+ * token at own offset r sees slot x of the segment iff r >= thr (inherited keys: 0; a
+ * mounted span: the mount's rpos) or, where causal is 1 (the cursor's own pages), iff
+ * r >= thr + x - slot_lo.  A key reachable in several ways gets the smallest threshold,
+ * and each key appears once.  Segments are sorted by thr within a cursor.
+ * first_off_out (int32[n_cursors]) receives each cursor's first new token's own offset.
+ * Two calls as for octopus_decode_segments: seg_ptr_out int32[n_cursors+1],
+ * seg_page/lo/hi/thr/causal_out int32[n_seg].
+ * Errors: EINVAL (tables, page table, n_new out of range), ECYCLE, EWORKSPACE. */
+int octopus_extend_segments(const octopus_branch* branches, int32_t n_branches,
+                            const octopus_mount* mounts, int32_t n_mounts,
+                            const int32_t* page_ptr, const int32_t* pages, int32_t page_size,
+                            int32_t n_pages, const int32_t* cursors, int32_t n_cursors,
+                            const int32_t* n_new, int32_t* seg_ptr_out, int32_t* seg_page_out,
+                            int32_t* seg_lo_out, int32_t* seg_hi_out, int32_t* seg_thr_out,
+                            int32_t* seg_causal_out, int32_t seg_capacity, int32_t* n_seg_out,
+                            int32_t* first_off_out);
+
+/* Attention of every cursor's new tokens over their context, read in place from the
+ * pools: q [n_rows][Hq][D] (dtype) with q_ptr (int32[B+1], device) delimiting cursor c's
+ * rows q_ptr[c] .. q_ptr[c+1]-1 (its new tokens in order, at most max_new of them);
+ * first_off and seg_* as produced by octopus_extend_segments, on the device; k_pool,
+ * v_pool [n_pages][Hkv][page_size][D].  Writes o [n_rows][Hq][D] (dtype) and lse
+ * float32 [n_rows][Hq].  Needs no workspace.  Index arrays that do not come from
+ * octopus_extend_segments give undefined values (never a read outside the pools: a
+ * segment naming a page outside [0, n_pages) reads page 0 and is masked).
+ * Supported: bf16, D = 128, page_size = 64, Hq / Hkv <= 16.
+ * Errors: EINVAL, EUNSUPPORTED, EHIP. */
+int octopus_paged_mount_extend(octopus_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                               int32_t D, int32_t page_size, float scale, const void* q,
+                               const void* k_pool, const void* v_pool, int32_t n_pages,
+                               const int32_t* q_ptr, int32_t max_new, const int32_t* first_off,
+                               const int32_t* seg_ptr, const int32_t* seg_page,
+                               const int32_t* seg_lo, const int32_t* seg_hi,
+                               const int32_t* seg_thr, const int32_t* seg_causal, void* o,
+                               float* lse, void* stream);
+
 /* ---------------------------------------------------------------- misc */
 
 /* Message of the last error on this thread ("" if none). */

@@ -88,12 +88,13 @@ def unique_tokens(branches, mounts, cursors) -> int:
 
 
 def extend(q, k_pool, v_pool, branches, mounts, page_ptr, pages, page_size, cursors, q_ptr,
-           scale=None):
+           scale=None, only=None):
     """Attention of the new tokens of every cursor.  ``q_ptr`` (``[B+1]``) delimits the
     rows of ``q`` (``[n_rows, Hq, D]``) that belong to each cursor: rows
     ``q_ptr[c] .. q_ptr[c+1]-1`` are the last ``m_c = q_ptr[c+1] - q_ptr[c]`` own tokens
     of branch ``cursors[c]``, in order.  Returns ``O`` float64 ``[n_rows, Hq, D]`` and
-    ``LSE`` float64 ``[n_rows, Hq]``."""
+    ``LSE`` float64 ``[n_rows, Hq]``.  With ``only`` (a set of row indices), only those
+    rows are computed; the others are left zero."""
     n_rows, Hq, D = q.shape
     Hkv = k_pool.shape[1]
     G = Hq // Hkv
@@ -109,9 +110,11 @@ def extend(q, k_pool, v_pool, branches, mounts, page_ptr, pages, page_size, curs
         if m == 0:
             continue
         start, L = int(br[b, 2]), int(br[b, 3])
-        rows = dagmod.mask_rows(branches, mounts, T, start + L - m, start + L)  # [m, T]
         for j in range(m):
-            idx = np.flatnonzero(rows[j])
+            if only is not None and r0 + j not in only:
+                continue
+            i = start + L - m + j  # packed index of this new token
+            idx = np.flatnonzero(dagmod.mask_rows(branches, mounts, T, i, i + 1)[0])
             page, slot = physical_slots(br, page_ptr, pages, page_size, idx, owner)
             K = k_pool[page, :, slot, :].astype(np.float64)
             V = v_pool[page, :, slot, :].astype(np.float64)

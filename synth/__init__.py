@@ -12,11 +12,12 @@ primitives table): isolated branches of at most 32K own tokens, up to 262K packe
 tokens per tree, a handful of lateral read_thread mounts per episode.
 """
 
-from .dags import Dag, DecodeWorkload, build, fuzz_dag, decode_workload  # noqa: F401
+from .dags import Dag, DecodeWorkload, build, fuzz_dag, decode_workload, extend_workload  # noqa: F401
 from .tensors import (  # noqa: F401
     round_bf16,
     bf16_bits,
     rope_rotate,
     draw_attention_inputs,
     draw_decode_inputs,
+    draw_extend_inputs,
 )

@@ -339,3 +339,14 @@ def decode_workload(seed=5, n_cursors=64, prefix=16384, own_max=32768, max_mount
     n_pages, ptr, pages = assign_pages(dag, page_size, rng)
     cursors = np.arange(1, n_cursors + 1, dtype=np.int32)
     return DecodeWorkload(dag, page_size, n_pages, ptr, pages, cursors)
+
+
+def extend_workload(seed=5, new_min=256, new_max=2048, **kw):
+    """The paged decode batch of ``decode_workload`` with every cursor appending a turn:
+    its branch's last ``min(L, U{new_min..new_max})`` tokens are new.  Returns
+    ``(workload, n_new)``."""
+    wl = decode_workload(seed=seed, **kw)
+    rng = np.random.default_rng(seed + 1000)
+    L = wl.dag.branches[wl.cursors, 3]
+    n_new = np.minimum(L, rng.integers(new_min, new_max + 1, size=len(L))).astype(np.int32)
+    return wl, n_new

@@ -91,3 +91,17 @@ def draw_decode_inputs(rng: np.random.Generator, B: int, Hq: int, Hkv: int, D: i
     if dtype == "bf16":
         q, kp, vp = round_bf16(q), round_bf16(kp), round_bf16(vp)
     return {"q": q, "k_pool": kp, "v_pool": vp}
+
+
+def draw_extend_inputs(rng: np.random.Generator, n_rows: int, Hq: int, Hkv: int, D: int,
+                       n_pages: int, page_size: int, std: float = 0.5,
+                       dtype: str = "bf16"):
+    """Extend queries ``[n_rows,Hq,D]`` (the new tokens of all cursors, cursor by cursor)
+    and K/V pools ``[n_pages,Hkv,page_size,D]``, i.i.d. N(0, std^2), rounded to
+    ``dtype``."""
+    q = _normal(rng, (n_rows, Hq, D), std)
+    kp = _normal(rng, (n_pages, Hkv, page_size, D), std)
+    vp = _normal(rng, (n_pages, Hkv, page_size, D), std)
+    if dtype == "bf16":
+        q, kp, vp = round_bf16(q), round_bf16(kp), round_bf16(vp)
+    return {"q": q, "k_pool": kp, "v_pool": vp}

@@ -239,6 +239,63 @@ def test_decode_shared_segments_fuzz(seed):
     _check_shared_segments(wl)
 
 
+def _check_extend_segments(wl, n_new):
+    """For every new token (own offset r) of every cursor, the slots the thresholds
+    admit are exactly the oracle's context of that token, each key once; thresholds are
+    sorted within a cursor; first_off is the first new token's offset."""
+    sp, pg, lo, hi, thr, causal, first = tpb.extend_segments(
+        wl.dag.branches, wl.dag.mounts, wl.page_ptr, wl.pages, wl.page_size, wl.n_pages,
+        wl.cursors, n_new)
+    br = wl.dag.branches
+    T = int(br[:, 3].sum())
+    for c, b in enumerate(wl.cursors):
+        start, L = int(br[b, 2]), int(br[b, 3])
+        m = int(n_new[c])
+        assert first[c] == L - m
+        seg = range(sp[c], sp[c + 1])
+        assert all(thr[s] <= thr[s + 1] for s in list(seg)[:-1])
+        keys = [(int(pg[s]), x) for s in seg for x in range(lo[s], hi[s])]
+        assert len(keys) == len(set(keys))
+        rows = D.mask_rows(br, wl.dag.mounts, T, start + L - m, start + L)
+        for j in range(m):
+            r = L - m + j
+            got = sorted((int(pg[s]), x) for s in seg for x in range(lo[s], hi[s])
+                         if r >= thr[s] + (x - lo[s] if causal[s] else 0))
+            page, slot = DEC.physical_slots(br, wl.page_ptr, wl.pages, wl.page_size,
+                                            np.flatnonzero(rows[j]))
+            assert got == sorted(zip(page.tolist(), slot.tolist())), (c, j)
+
+
+def test_extend_segments_match_oracle_small():
+    wl = synth.decode_workload(seed=5, n_cursors=6, prefix=256, own_max=300, span_max=100,
+                               page_size=16)
+    rng = np.random.default_rng(3)
+    L = wl.dag.branches[wl.cursors, 3]
+    _check_extend_segments(wl, np.minimum(L, rng.integers(1, 90, size=len(L))))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_extend_segments_fuzz(seed):
+    """Every branch a cursor, mounts issued inside the new tokens, spans that overlap
+    what the reader inherits."""
+    rng = np.random.default_rng(40 + seed)
+    dag = synth.fuzz_dag(rng, max_len=70, max_branches=7, max_mounts=6)
+    n_pages, ptr, pages = synth.dags.assign_pages(dag, 16, rng)
+    wl = synth.DecodeWorkload(dag, 16, n_pages, ptr, pages, np.arange(dag.nb, dtype=np.int32))
+    n_new = np.array([int(rng.integers(1, L + 1)) for L in dag.branches[:, 3]])
+    _check_extend_segments(wl, n_new)
+
+
+def test_extend_segments_errors():
+    wl = synth.decode_workload(seed=5, n_cursors=4, prefix=64, own_max=100, page_size=16)
+    L = wl.dag.branches[wl.cursors, 3]
+    for bad in (np.zeros_like(L), L + 1):
+        with pytest.raises(tpb.OctopusError) as ei:
+            tpb.extend_segments(wl.dag.branches, wl.dag.mounts, wl.page_ptr, wl.pages, 16,
+                                wl.n_pages, wl.cursors, bad)
+        assert ei.value.name == "EINVAL"
+
+
 def test_decode_segments_errors():
     wl = synth.decode_workload(seed=5, n_cursors=4, prefix=64, own_max=100, page_size=16)
     bad_pages = wl.pages.copy()

@@ -21,8 +21,10 @@ from ._lib import (  # noqa: F401
     bwd_workspace_bytes,
     decode_segments,
     decode_workspace_bytes,
+    extend_segments,
     default_scale,
     fwd_workspace_bytes,
     lib,
     paged_mount_decode,
+    paged_mount_extend,
 )

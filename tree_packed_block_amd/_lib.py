@@ -29,8 +29,8 @@ EXPORTS = [
     "octopus_plan_export_tiles", "octopus_plan_destroy", "octopus_fwd_workspace_bytes", "octopus_dag_attn_fwd",
     "octopus_bwd_workspace_bytes", "octopus_dag_attn_bwd", "octopus_dag_attn_bwd_preprocess",
     "octopus_dag_attn_bwd_dkdv", "octopus_dag_attn_bwd_dq", "octopus_decode_segments",
-    "octopus_decode_workspace_bytes", "octopus_paged_mount_decode", "octopus_last_error",
-    "octopus_version",
+    "octopus_decode_workspace_bytes", "octopus_paged_mount_decode", "octopus_extend_segments",
+    "octopus_paged_mount_extend", "octopus_last_error", "octopus_version",
 ]
 
 
@@ -106,6 +106,15 @@ def lib():
                                              _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp,
                                              ctypes.c_int32, _vp, _vp, _vp, ctypes.c_size_t,
                                              _vp]
+    L.octopus_extend_segments.argtypes = [_vp, ctypes.c_int32, _vp, ctypes.c_int32, _vp, _vp,
+                                          ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int32,
+                                          _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
+                                          _i32p, _vp]
+    L.octopus_paged_mount_extend.argtypes = [ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_float, _vp, _vp, _vp, ctypes.c_int32,
+                                             _vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                             _vp, _vp, _vp, _vp]
     L.octopus_last_error.restype = ctypes.c_char_p
     L.octopus_version.restype = ctypes.c_char_p
     _lib = L
@@ -394,6 +403,69 @@ def paged_mount_decode(q, k_pool, v_pool, seg_ptr, seg_page, seg_lo, seg_hi, grp
         k_pool.data_ptr(), v_pool.data_ptr(), n_pages, seg_ptr.data_ptr(), seg_page.data_ptr(),
         seg_lo.data_ptr(), seg_hi.data_ptr(), n_groups, gp, gc, int(n_split), o.data_ptr(),
         lse.data_ptr(), ws.data_ptr(), ws.numel(), _vp(s.cuda_stream)))
+    return o, lse
+
+
+# ----------------------------------------------------------------------------- extend
+
+def extend_segments(branches, mounts, page_ptr, pages, page_size, n_pages, cursors, n_new):
+    """Host segment builder for extend: returns int32 arrays ``(seg_ptr, seg_page, seg_lo,
+    seg_hi, seg_thr, seg_causal, first_off)``."""
+    br, mt = _tables(branches, mounts)
+    pp = np.ascontiguousarray(page_ptr, dtype=np.int32)
+    pg = np.ascontiguousarray(pages, dtype=np.int32)
+    cur = np.ascontiguousarray(cursors, dtype=np.int32)
+    nn = np.ascontiguousarray(n_new, dtype=np.int32)
+    B = cur.shape[0]
+    if nn.shape != (B,):
+        raise OctopusError(EINVAL, "n_new must have one entry per cursor")
+    n = ctypes.c_int32(0)
+    L = lib()
+    args = [_np_ptr(br), br.shape[0], _np_ptr(mt), mt.shape[0], _np_ptr(pp), _np_ptr(pg),
+            int(page_size), int(n_pages), _np_ptr(cur), B, _np_ptr(nn)]
+    rc = L.octopus_extend_segments(*args, None, None, None, None, None, None, 0,
+                                   ctypes.byref(n), None)
+    if rc not in (OK, EWORKSPACE):
+        _check(rc)
+    cap = n.value
+    sp = np.zeros(B + 1, dtype=np.int32)
+    fo = np.zeros(max(B, 1), dtype=np.int32)
+    out = [np.zeros(max(cap, 1), dtype=np.int32) for _ in range(5)]
+    _check(L.octopus_extend_segments(*args, _np_ptr(sp), *[_np_ptr(a) for a in out], cap,
+                                     ctypes.byref(n), _np_ptr(fo)))
+    return (sp,) + tuple(a[:cap] for a in out) + (fo[:B],)
+
+
+def paged_mount_extend(q, k_pool, v_pool, q_ptr, max_new, first_off, seg_ptr, seg_page,
+                       seg_lo, seg_hi, seg_thr, seg_causal, scale=None, o=None, lse=None,
+                       stream=None):
+    """Attention of every cursor's new tokens (rows ``q_ptr[c] .. q_ptr[c+1]-1`` of
+    ``q [n_rows, Hq, D]``, at most ``max_new`` per cursor) over their paged context;
+    index arrays are contiguous int32 device tensors as ``extend_segments`` returns
+    them.  Returns ``(o [n_rows, Hq, D], lse float32 [n_rows, Hq])``."""
+    import torch
+    n_rows, Hq, D = q.shape
+    n_pages, Hkv, page_size, _ = k_pool.shape
+    _need(q, (n_rows, Hq, D), q.dtype, "q")
+    _need(k_pool, (n_pages, Hkv, page_size, D), q.dtype, "k_pool")
+    _need(v_pool, (n_pages, Hkv, page_size, D), q.dtype, "v_pool")
+    for t, nm in ((q_ptr, "q_ptr"), (first_off, "first_off"), (seg_ptr, "seg_ptr"),
+                  (seg_page, "seg_page"), (seg_lo, "seg_lo"), (seg_hi, "seg_hi"),
+                  (seg_thr, "seg_thr"), (seg_causal, "seg_causal")):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise OctopusError(EINVAL, f"{nm} must be a contiguous int32 device tensor")
+    B = q_ptr.numel() - 1
+    if first_off.numel() != B or seg_ptr.numel() != B + 1:
+        raise OctopusError(EINVAL, "first_off and seg_ptr must match q_ptr's cursor count")
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((n_rows, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    s = stream or torch.cuda.current_stream(q.device)
+    _check(lib().octopus_paged_mount_extend(
+        _dtype_code(q), B, Hq, Hkv, D, page_size, float(scale or 0.0), q.data_ptr(),
+        k_pool.data_ptr(), v_pool.data_ptr(), n_pages, q_ptr.data_ptr(), int(max_new),
+        first_off.data_ptr(), seg_ptr.data_ptr(), seg_page.data_ptr(), seg_lo.data_ptr(),
+        seg_hi.data_ptr(), seg_thr.data_ptr(), seg_causal.data_ptr(), o.data_ptr(),
+        lse.data_ptr(), _vp(s.cuda_stream)))
     return o, lse
 
 

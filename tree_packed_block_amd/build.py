@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liboctopus_dag.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-HIP_SOURCES = ["fwd.hip", "bwd.hip", "decode.hip"]
+HIP_SOURCES = ["fwd.hip", "bwd.hip", "decode.hip", "extend.hip"]
 CXX_SOURCES = ["plan.cpp", "api.cpp"]
 
 HIPCC_FLAGS = [
@@ -32,7 +32,8 @@ HIPCC_FLAGS = [
 ]
 # Per-source code-generation options.  The kernels never produce NaN on purpose, so
 # fmaxf need not quiet NaN operands (that costs one extra instruction per maximum).
-HIP_FILE_FLAGS: dict = {"fwd.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"]}
+HIP_FILE_FLAGS: dict = {"fwd.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"],
+                        "extend.hip": ["-fno-honor-nans"]}
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
              "-D__HIP_PLATFORM_AMD__"]
 

@@ -349,6 +349,81 @@ int octopus_decode_segments(const octopus_branch* branches, int32_t n_branches,
     }
 }
 
+int octopus_extend_segments(const octopus_branch* branches, int32_t n_branches,
+                            const octopus_mount* mounts, int32_t n_mounts,
+                            const int32_t* page_ptr, const int32_t* pages, int32_t page_size,
+                            int32_t n_pages, const int32_t* cursors, int32_t n_cursors,
+                            const int32_t* n_new, int32_t* seg_ptr_out, int32_t* seg_page_out,
+                            int32_t* seg_lo_out, int32_t* seg_hi_out, int32_t* seg_thr_out,
+                            int32_t* seg_causal_out, int32_t seg_capacity, int32_t* n_seg_out,
+                            int32_t* first_off_out) {
+    if (n_seg_out == nullptr) return fail(OCTOPUS_EINVAL, "n_seg_out is NULL");
+    try {
+        if (n_branches < 1 || branches == nullptr) return fail(OCTOPUS_EINVAL, "no branches");
+        int64_t T = 0;
+        for (int32_t b = 0; b < n_branches; ++b) T += branches[b].len > 0 ? branches[b].len : 0;
+        if (T < 1 || T > octo::kMaxTokens) return fail(OCTOPUS_EINVAL, "total tokens out of range");
+        octo::DagInfo dag;
+        std::string err;
+        int rc = octo::load_dag(branches, n_branches, mounts, n_mounts, (int32_t)T, dag, err);
+        if (rc != OCTOPUS_OK) return fail(rc, err);
+        std::vector<int32_t> sp, pg, lo, hi, th, ca, fo;
+        rc = octo::build_extend_segments(dag, page_ptr, pages, page_size, n_pages, cursors,
+                                         n_cursors, n_new, sp, pg, lo, hi, th, ca, fo, err);
+        if (rc != OCTOPUS_OK) return fail(rc, err);
+        if (pg.size() > (size_t)INT32_MAX) return fail(OCTOPUS_EINVAL, "too many segments");
+        *n_seg_out = (int32_t)pg.size();
+        if (seg_capacity < (int64_t)pg.size())
+            return fail(OCTOPUS_EWORKSPACE, "segment capacity too small; need " +
+                                                std::to_string(pg.size()));
+        if (!seg_ptr_out || !seg_page_out || !seg_lo_out || !seg_hi_out || !seg_thr_out ||
+            !seg_causal_out || !first_off_out)
+            return fail(OCTOPUS_EINVAL, "NULL output array");
+        std::copy(sp.begin(), sp.end(), seg_ptr_out);
+        std::copy(pg.begin(), pg.end(), seg_page_out);
+        std::copy(lo.begin(), lo.end(), seg_lo_out);
+        std::copy(hi.begin(), hi.end(), seg_hi_out);
+        std::copy(th.begin(), th.end(), seg_thr_out);
+        std::copy(ca.begin(), ca.end(), seg_causal_out);
+        std::copy(fo.begin(), fo.end(), first_off_out);
+        return ok();
+    } catch (const std::bad_alloc&) {
+        return fail(OCTOPUS_ENOMEM, "host allocation failed while building segments");
+    }
+}
+
+int octopus_paged_mount_extend(octopus_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                               int32_t D, int32_t page_size, float scale, const void* q,
+                               const void* k_pool, const void* v_pool, int32_t n_pages,
+                               const int32_t* q_ptr, int32_t max_new, const int32_t* first_off,
+                               const int32_t* seg_ptr, const int32_t* seg_page,
+                               const int32_t* seg_lo, const int32_t* seg_hi,
+                               const int32_t* seg_thr, const int32_t* seg_causal, void* o,
+                               float* lse, void* stream) {
+    if (dtype != OCTOPUS_BF16) return fail(OCTOPUS_EUNSUPPORTED, "extend supports bf16 only");
+    if (D != 128) return fail(OCTOPUS_EUNSUPPORTED, "extend supports head_dim 128 only");
+    if (page_size != 64) return fail(OCTOPUS_EUNSUPPORTED, "extend supports page_size 64 only");
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+        return fail(OCTOPUS_EINVAL, "B, Hq, Hkv must be positive with Hq % Hkv == 0");
+    if (Hq / Hkv > 16) return fail(OCTOPUS_EUNSUPPORTED, "Hq / Hkv must be <= 16");
+    if (max_new < 1) return fail(OCTOPUS_EINVAL, "max_new must be >= 1");
+    if (n_pages < 1) return fail(OCTOPUS_EINVAL, "n_pages must be >= 1");
+    for (const void* p : {q, k_pool, v_pool, (const void*)o, (const void*)lse}) {
+        if (p == nullptr) return fail(OCTOPUS_EINVAL, "a tensor pointer is NULL");
+        if (!aligned(p, 16)) return fail(OCTOPUS_EINVAL, "tensors must be 16-byte aligned");
+    }
+    if (!q_ptr || !first_off || !seg_ptr || !seg_page || !seg_lo || !seg_hi || !seg_thr ||
+        !seg_causal)
+        return fail(OCTOPUS_EINVAL, "index arrays must not be NULL");
+    if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
+    hipError_t e = octo::launch_extend_bf16(B, Hq, Hkv, D, scale, q, k_pool, v_pool, n_pages,
+                                            q_ptr, max_new, first_off, seg_ptr, seg_page, seg_lo,
+                                            seg_hi, seg_thr, seg_causal, o, lse,
+                                            (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "extend launch");
+    return ok();
+}
+
 size_t octopus_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t n_split) {
     if (B < 1 || Hq < 1 || D < 1 || n_split < 1) return 0;
     return (size_t)B * 2 * n_split * Hq * (D + 4) * sizeof(float);

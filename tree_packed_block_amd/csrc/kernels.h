@@ -68,4 +68,14 @@ hipError_t launch_decode_bf16(int B, int Hq, int Hkv, int D, int page_size, floa
                               const int32_t* grp_ptr, const int32_t* grp_cur, int n_split,
                               void* o, float* lse, float* partial, hipStream_t s);
 
+// Extend: rows q_ptr[c] .. q_ptr[c+1]-1 of q are cursor c's new tokens (own offsets
+// first_off[c] + j); segments as built by build_extend_segments.  max_new >= every m_c.
+hipError_t launch_extend_bf16(int B, int Hq, int Hkv, int D, float scale, const void* q,
+                              const void* k_pool, const void* v_pool, int n_pages,
+                              const int32_t* q_ptr, int max_new, const int32_t* first_off,
+                              const int32_t* seg_ptr, const int32_t* seg_page,
+                              const int32_t* seg_lo, const int32_t* seg_hi,
+                              const int32_t* seg_thr, const int32_t* seg_causal, void* o,
+                              float* lse, hipStream_t s);
+
 }  // namespace octo

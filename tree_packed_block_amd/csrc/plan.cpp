@@ -472,12 +472,10 @@ void export_mask(const Plan& p, int32_t lo, int32_t hi, uint8_t* bits) {
     }
 }
 
-int build_segments(const DagInfo& d, const int32_t* page_ptr, const int32_t* pages,
-                   int32_t page_size, int32_t n_pages, const int32_t* cursors,
-                   int32_t n_cursors, bool share, std::vector<int32_t>& seg_ptr,
-                   std::vector<int32_t>& seg_page, std::vector<int32_t>& seg_lo,
-                   std::vector<int32_t>& seg_hi, std::vector<int32_t>& grp_ptr,
-                   std::vector<int32_t>& grp_cur, std::string& err) {
+// Shared checks of the page table and the cursor list.
+static int check_pages(const DagInfo& d, const int32_t* page_ptr, const int32_t* pages,
+                       int32_t page_size, int32_t n_pages, const int32_t* cursors,
+                       int32_t n_cursors, std::string& err) {
     const int32_t nb = (int32_t)d.br.size();
     if (page_size < 1 || n_pages < 0 || n_cursors < 0 || page_ptr == nullptr ||
         (n_cursors > 0 && cursors == nullptr)) {
@@ -504,6 +502,17 @@ int build_segments(const DagInfo& d, const int32_t* page_ptr, const int32_t* pag
             return OCTOPUS_EINVAL;
         }
     }
+    return OCTOPUS_OK;
+}
+
+int build_segments(const DagInfo& d, const int32_t* page_ptr, const int32_t* pages,
+                   int32_t page_size, int32_t n_pages, const int32_t* cursors,
+                   int32_t n_cursors, bool share, std::vector<int32_t>& seg_ptr,
+                   std::vector<int32_t>& seg_page, std::vector<int32_t>& seg_lo,
+                   std::vector<int32_t>& seg_hi, std::vector<int32_t>& grp_ptr,
+                   std::vector<int32_t>& grp_cur, std::string& err) {
+    const int rc = check_pages(d, page_ptr, pages, page_size, n_pages, cursors, n_cursors, err);
+    if (rc != OCTOPUS_OK) return rc;
     seg_ptr.assign(1, 0);
     seg_page.clear();
     seg_lo.clear();
@@ -583,6 +592,107 @@ int build_segments(const DagInfo& d, const int32_t* page_ptr, const int32_t* pag
             grp_cur.insert(grp_cur.end(), m.begin(), m.end());
             grp_ptr.push_back((int32_t)grp_cur.size());
         }
+    }
+    return OCTOPUS_OK;
+}
+
+int build_extend_segments(const DagInfo& d, const int32_t* page_ptr, const int32_t* pages,
+                          int32_t page_size, int32_t n_pages, const int32_t* cursors,
+                          int32_t n_cursors, const int32_t* n_new, std::vector<int32_t>& seg_ptr,
+                          std::vector<int32_t>& seg_page, std::vector<int32_t>& seg_lo,
+                          std::vector<int32_t>& seg_hi, std::vector<int32_t>& seg_thr,
+                          std::vector<int32_t>& seg_causal, std::vector<int32_t>& first_off,
+                          std::string& err) {
+    int rc = check_pages(d, page_ptr, pages, page_size, n_pages, cursors, n_cursors, err);
+    if (rc != OCTOPUS_OK) return rc;
+    if (n_cursors > 0 && n_new == nullptr) { err = "n_new is NULL"; return OCTOPUS_EINVAL; }
+    for (int32_t c = 0; c < n_cursors; ++c) {
+        if (n_new[c] < 1 || n_new[c] > d.br[cursors[c]].len) {
+            err = row_msg("cursor", c, "new-token count outside [1, branch length]");
+            return OCTOPUS_EINVAL;
+        }
+    }
+    seg_ptr.assign(1, 0);
+    seg_page.clear();
+    seg_lo.clear();
+    seg_hi.clear();
+    seg_thr.clear();
+    seg_causal.clear();
+    first_off.assign(n_cursors, 0);
+    struct Seg { int32_t page, lo, hi, thr, causal; };
+    std::vector<Seg> segs;
+    struct Piece { int64_t lo, hi; int32_t thr; };
+    std::vector<Piece> pieces, resolved;
+    std::vector<int64_t> cuts;
+    for (int32_t c = 0; c < n_cursors; ++c) {
+        const int32_t b = cursors[c];
+        const octopus_branch& B = d.br[b];
+        const int32_t L = B.len;
+        first_off[c] = L - n_new[c];
+        // Keys that are not b's own tokens, each with the smallest own offset from which
+        // b sees it: 0 for what b inherits, rpos for a mounted span (mounts issued after
+        // b's last token are seen by none of its tokens).
+        pieces.clear();
+        for (const Interval& iv : d.inherited[b]) pieces.push_back({iv.lo, iv.hi, 0});
+        for (int32_t id : d.mounts_of[b]) {
+            const octopus_mount& m = d.mt[id];
+            if (m.rpos > L - 1) continue;
+            const int64_t ps = d.br[m.producer].start;
+            pieces.push_back({ps + m.s, ps + m.e, m.rpos});
+        }
+        cuts.clear();
+        for (const Piece& p : pieces) {
+            cuts.push_back(p.lo);
+            cuts.push_back(p.hi);
+        }
+        std::sort(cuts.begin(), cuts.end());
+        cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
+        resolved.clear();
+        for (size_t k = 0; k + 1 < cuts.size(); ++k) {
+            int32_t thr = INT32_MAX;
+            for (const Piece& p : pieces)
+                if (p.lo <= cuts[k] && cuts[k + 1] <= p.hi) thr = std::min(thr, p.thr);
+            if (thr == INT32_MAX) continue;
+            if (!resolved.empty() && resolved.back().hi == cuts[k] && resolved.back().thr == thr)
+                resolved.back().hi = cuts[k + 1];
+            else
+                resolved.push_back({cuts[k], cuts[k + 1], thr});
+        }
+        segs.clear();
+        for (const Piece& p : resolved) {
+            int64_t j = p.lo;
+            while (j < p.hi) {
+                const int32_t o = d.owner(j);
+                const int64_t ostart = d.br[o].start;
+                const int64_t stop = std::min<int64_t>(p.hi, ostart + d.br[o].len);
+                int64_t r = j - ostart;
+                const int64_t rend = stop - ostart;
+                while (r < rend) {
+                    const int64_t pi = r / page_size;
+                    const int64_t slot0 = r - pi * page_size;
+                    const int64_t slot1 = std::min<int64_t>(page_size, rend - pi * page_size);
+                    segs.push_back({pages[page_ptr[o] + pi], (int32_t)slot0, (int32_t)slot1,
+                                    p.thr, 0});
+                    r = (pi + 1) * page_size;
+                }
+                j = stop;
+            }
+        }
+        // b's own tokens: own offset t is seen by new tokens at offsets >= t.
+        for (int64_t pi = 0; pi * page_size < L; ++pi) {
+            const int32_t hi = (int32_t)std::min<int64_t>(page_size, L - pi * page_size);
+            segs.push_back({pages[page_ptr[b] + pi], 0, hi, (int32_t)(pi * page_size), 1});
+        }
+        std::stable_sort(segs.begin(), segs.end(),
+                         [](const Seg& x, const Seg& y) { return x.thr < y.thr; });
+        for (const Seg& sg : segs) {
+            seg_page.push_back(sg.page);
+            seg_lo.push_back(sg.lo);
+            seg_hi.push_back(sg.hi);
+            seg_thr.push_back(sg.thr);
+            seg_causal.push_back(sg.causal);
+        }
+        seg_ptr.push_back((int32_t)seg_page.size());
     }
     return OCTOPUS_OK;
 }

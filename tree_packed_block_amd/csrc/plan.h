@@ -105,4 +105,16 @@ int build_segments(const DagInfo& dag, const int32_t* page_ptr, const int32_t* p
                    std::vector<int32_t>& seg_hi, std::vector<int32_t>& grp_ptr,
                    std::vector<int32_t>& grp_cur, std::string& err);
 
+// Extend segments (see octopus_extend_segments): for cursor c, the segments of the
+// context of its last token, each with the smallest own offset of a new token that sees
+// it (thr; for own-token segments, `causal`: slot x needs offset thr + x - lo), sorted by
+// that threshold; first_off[c] is the own offset of c's first new token.
+int build_extend_segments(const DagInfo& dag, const int32_t* page_ptr, const int32_t* pages,
+                          int32_t page_size, int32_t n_pages, const int32_t* cursors,
+                          int32_t n_cursors, const int32_t* n_new, std::vector<int32_t>& seg_ptr,
+                          std::vector<int32_t>& seg_page, std::vector<int32_t>& seg_lo,
+                          std::vector<int32_t>& seg_hi, std::vector<int32_t>& seg_thr,
+                          std::vector<int32_t>& seg_causal, std::vector<int32_t>& first_off,
+                          std::string& err);
+
 }  // namespace octo
