@@ -113,7 +113,26 @@ def cpu_baseline(dag, x, rows_per_part=768):
                       f"float64, {dt:.1f} s"}
 
 
+def extend_pairs(segs, n_new, branches, cursors) -> int:
+    """Visible (new token, key) pairs of an extend batch, from its threshold segments: a
+    token at own offset r sees the keys whose threshold is <= r."""
+    import numpy as np
+    sp, pg, lo, hi, thr, causal, first = segs
+    total = 0
+    for c, b in enumerate(cursors):
+        L, m = int(branches[b, 3]), int(n_new[c])
+        keys = []
+        for s in range(sp[c], sp[c + 1]):
+            n = int(hi[s] - lo[s])
+            keys.append(np.full(n, thr[s]) + (np.arange(n) if causal[s] else 0))
+        kt = np.sort(np.concatenate(keys))
+        r = np.arange(L - m, L)
+        total += int(np.searchsorted(kt, r, side="right").sum())
+    return total
+
+
 KERNEL_KEYS = (("fwd_bf16_kernel", "fwd"), ("tiles_t_kernel", "fwd"),
+               ("extend_bf16_kernel", "extend"),
                ("preprocess_bf16_kernel", "bwd_preprocess"),
                ("dkdv_bf16_kernel", "bwd_dkdv"), ("dq_bf16_kernel", "bwd_dq"),
                ("decode_split_kernel", "decode"), ("decode_combine_kernel", "decode"))
@@ -378,6 +397,43 @@ def main():
         "device": torch.cuda.get_device_name(dev),
         "cu_count": torch.cuda.get_device_properties(dev).multi_processor_count,
     }
+    # Extend, on its own clock (not part of the step): every cursor of the decode batch
+    # appends a turn of 256-2048 new tokens over its paged context (the same pools).
+    wl_e, n_new = synth.extend_workload()
+    segs_e = tpb.extend_segments(wl_e.dag.branches, wl_e.dag.mounts, wl_e.page_ptr,
+                                 wl_e.pages, wl_e.page_size, wl_e.n_pages, wl_e.cursors, n_new)
+    pairs_e = extend_pairs(segs_e, n_new, wl_e.dag.branches, wl_e.cursors)
+    rows_e = int(n_new.sum())
+    qe = (torch.from_numpy(np.random.default_rng(77).standard_normal((rows_e, HQ, HD),
+                                                                      dtype=np.float32))
+          * 0.5).to(device=dev, dtype=torch.bfloat16)
+    ie = [torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+          for a in (np.concatenate([[0], np.cumsum(n_new)]), segs_e[6]) + segs_e[:6]]
+    oe = torch.empty_like(qe)
+    lsee = torch.empty((rows_e, HQ), dtype=torch.float32, device=dev)
+
+    def run_extend():
+        tpb.paged_mount_extend(qe, kp, vp, ie[0], int(n_new.max()), ie[1], *ie[2:], o=oe,
+                               lse=lsee)
+
+    for _ in range(2):
+        run_extend()
+    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    ev_e[0].record(stream)
+    for j in range(5):
+        run_extend()
+        ev_e[j + 1].record(stream)
+    torch.cuda.synchronize()
+    ms_e = float(np.median([ev_e[j].elapsed_time(ev_e[j + 1]) for j in range(5)]))
+    rate_e = 4.0 * HD * HQ * pairs_e / (ms_e * 1e-3)
+    out["breakdown"]["extend"] = {"ms": round(ms_e, 3),
+                                  "useful_TFLOP/s": round(rate_e / 1e12, 1),
+                                  "frac_of_peak": round(rate_e / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    out["extend"] = {"workload": "64 cursors of the decode batch each appending 256-2048 "
+                                 "new tokens (causal among them) over their paged context",
+                     "new_tokens": rows_e, "pairs": pairs_e, "timed": "own clock, not in "
+                     "the step"}
+
     if not args.no_cpu_baseline:
         log("cpu baseline (float64 oracle on a sample) ...")
         out["cpu_baseline"] = cpu_baseline(dag, x)

@@ -327,3 +327,22 @@ def test_workspace_sizes():
         assert tpb.bwd_workspace_bytes(plan, tpb.FP32, hq, hkv, d) == floats
         assert tpb.bwd_workspace_bytes(plan, tpb.BF16, hq, hkv, d) == floats
 
+
+
+def test_extend_pair_count_matches_oracle():
+    """The benchmark's count of visible (new token, key) pairs equals the oracle's mask
+    row sums."""
+    import bench
+    wl = synth.decode_workload(seed=5, n_cursors=6, prefix=256, own_max=300, span_max=100,
+                               page_size=16)
+    L = wl.dag.branches[wl.cursors, 3]
+    n_new = np.minimum(L, np.random.default_rng(4).integers(1, 200, size=len(L)))
+    segs = tpb.extend_segments(wl.dag.branches, wl.dag.mounts, wl.page_ptr, wl.pages, 16,
+                               wl.n_pages, wl.cursors, n_new)
+    br = wl.dag.branches
+    T = int(br[:, 3].sum())
+    want = 0
+    for c, b in enumerate(wl.cursors):
+        end = int(br[b, 2] + br[b, 3])
+        want += int(D.mask_rows(br, wl.dag.mounts, T, end - int(n_new[c]), end).sum())
+    assert bench.extend_pairs(segs, n_new, br, wl.cursors) == want
