@@ -206,6 +206,48 @@ int octopus_dag_attn_bwd_dq(const octopus_plan* plan, octopus_dtype dtype, int32
                             const void* v, const void* dout, void* dq, const void* ws,
                             size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- rotary positions */
+
+/* Positions only (host): int32[total_tokens] as octopus_plan_positions returns them, with
+ * no tile plan built (for serving, where queries are rotated at their cursor's
+ * positions).  Errors: EINVAL, ECYCLE, ENOMEM. */
+int octopus_dag_positions(const octopus_branch* branches, int32_t n_branches,
+                          const octopus_mount* mounts, int32_t n_mounts, int32_t total_tokens,
+                          int32_t* pos_out);
+
+/* Rotary embedding on the device (rotate-half): row r of x [rows][H][D] has its pairs
+ * (x_i, x_{i+D/2}) turned by pos[r] * rope_base^(-2i/D) (by the opposite angle if
+ * inverse), written to out (may equal x).  pos: device int32[rows].  Mounted keys keep
+ * the position they were written at, so paged keys are stored rotated once, at their
+ * producer's positions (card "02 · Memory": rotation-free mounts).
+ * Supported: bf16 and fp32, D in {64, 128}.  Errors: EINVAL, EUNSUPPORTED, EHIP. */
+int octopus_rope(octopus_dtype dtype, int32_t rows, int32_t H, int32_t D, float rope_base,
+                 int32_t inverse, const int32_t* pos, const void* x, void* out, void* stream);
+
+/* Extra workspace bytes of the RoPE variants below: rotated copies of Q and K. */
+size_t octopus_rope_workspace_bytes(const octopus_plan* plan, octopus_dtype dtype,
+                                    int32_t Hq, int32_t Hkv, int32_t D);
+
+/* octopus_dag_attn_fwd with Q and K given unrotated: both are turned at the plan's
+ * positions (rope_base > 1) into the front of the workspace, then the forward runs on
+ * them.  ws: 256-byte aligned, octopus_rope_workspace_bytes + octopus_fwd_workspace_bytes
+ * bytes, the rotated copies first.  Errors as octopus_dag_attn_fwd. */
+int octopus_dag_attn_fwd_rope(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
+                              int32_t Hkv, int32_t D, float scale, float rope_base,
+                              const void* q, const void* k, const void* v, void* o, float* lse,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* octopus_dag_attn_bwd with Q and K given unrotated: gradients are taken with respect to
+ * the rotated copies and dQ, dK are then turned back in place (the rotation is
+ * orthogonal), so they are the gradients with respect to the unrotated inputs.  ws as
+ * for the forward, with octopus_bwd_workspace_bytes after the rotated copies.
+ * Errors as octopus_dag_attn_bwd. */
+int octopus_dag_attn_bwd_rope(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
+                              int32_t Hkv, int32_t D, float scale, float rope_base,
+                              const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                              void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- paged decode */
 
 /* Host helper: turn a DAG of branches held in a page pool into per-cursor segment

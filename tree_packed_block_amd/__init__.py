@@ -18,6 +18,11 @@ from ._lib import (  # noqa: F401
     attn_bwd,
     attn_bwd_phase,
     attn_fwd,
+    attn_fwd_rope,
+    attn_bwd_rope,
+    dag_positions,
+    rope,
+    rope_workspace_bytes,
     bwd_workspace_bytes,
     decode_segments,
     decode_workspace_bytes,

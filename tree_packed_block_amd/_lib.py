@@ -30,7 +30,9 @@ EXPORTS = [
     "octopus_bwd_workspace_bytes", "octopus_dag_attn_bwd", "octopus_dag_attn_bwd_preprocess",
     "octopus_dag_attn_bwd_dkdv", "octopus_dag_attn_bwd_dq", "octopus_decode_segments",
     "octopus_decode_workspace_bytes", "octopus_paged_mount_decode", "octopus_extend_segments",
-    "octopus_paged_mount_extend", "octopus_last_error", "octopus_version",
+    "octopus_paged_mount_extend", "octopus_dag_positions", "octopus_rope",
+    "octopus_rope_workspace_bytes", "octopus_dag_attn_fwd_rope", "octopus_dag_attn_bwd_rope",
+    "octopus_last_error", "octopus_version",
 ]
 
 
@@ -115,6 +117,20 @@ def lib():
                                              ctypes.c_float, _vp, _vp, _vp, ctypes.c_int32,
                                              _vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp,
                                              _vp, _vp, _vp, _vp]
+    L.octopus_dag_positions.argtypes = [_vp, ctypes.c_int32, _vp, ctypes.c_int32,
+                                        ctypes.c_int32, _vp]
+    L.octopus_rope.argtypes = [ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                               ctypes.c_float, ctypes.c_int32, _vp, _vp, _vp, _vp]
+    L.octopus_rope_workspace_bytes.argtypes = [_vp, ctypes.c_int, ctypes.c_int32,
+                                               ctypes.c_int32, ctypes.c_int32]
+    L.octopus_rope_workspace_bytes.restype = ctypes.c_size_t
+    L.octopus_dag_attn_fwd_rope.argtypes = [_vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_float, ctypes.c_float,
+                                            _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.octopus_dag_attn_bwd_rope.argtypes = [_vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_float, ctypes.c_float,
+                                            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                            ctypes.c_size_t, _vp]
     L.octopus_last_error.restype = ctypes.c_char_p
     L.octopus_version.restype = ctypes.c_char_p
     _lib = L
@@ -320,6 +336,90 @@ def attn_bwd_phase(phase, plan: Plan, q, k, v, o, lse, dout, ws, dq=None, dk=Non
     else:
         raise ValueError(phase)
     _check(rc)
+
+
+# ----------------------------------------------------------------------------- rope
+
+def dag_positions(branches, mounts, total_tokens) -> np.ndarray:
+    """Positions of the packed tokens (host int32), no tile plan built."""
+    br, mt = _tables(branches, mounts)
+    out = np.zeros(max(int(total_tokens), 1), dtype=np.int32)
+    _check(lib().octopus_dag_positions(_np_ptr(br), br.shape[0], _np_ptr(mt), mt.shape[0],
+                                       int(total_tokens), _np_ptr(out)))
+    return out[:int(total_tokens)]
+
+
+def rope(x, pos, base=10000.0, inverse=False, out=None, stream=None):
+    """Rotate-half RoPE of ``x [rows, H, D]`` (device) at ``pos`` (device int32
+    ``[rows]``); ``out`` may be ``x``."""
+    import torch
+    rows, H, D = x.shape
+    if not (x.is_cuda and x.is_contiguous()):
+        raise OctopusError(EINVAL, "x must be a contiguous device tensor")
+    if pos.dtype != torch.int32 or not pos.is_cuda or pos.numel() != rows:
+        raise OctopusError(EINVAL, "pos must be a device int32 tensor with one entry per row")
+    out = torch.empty_like(x) if out is None else out
+    _need(out, x.shape, x.dtype, "out")
+    s = stream or torch.cuda.current_stream(x.device)
+    _check(lib().octopus_rope(_dtype_code(x), rows, H, D, float(base), 1 if inverse else 0,
+                              pos.data_ptr(), x.data_ptr(), out.data_ptr(), _vp(s.cuda_stream)))
+    return out
+
+
+def rope_workspace_bytes(plan: Plan, dtype_code, Hq, Hkv, D) -> int:
+    return int(lib().octopus_rope_workspace_bytes(plan.handle, dtype_code, Hq, Hkv, D))
+
+
+def attn_fwd_rope(plan: Plan, q, k, v, base=10000.0, scale=None, o=None, lse=None, ws=None,
+                  stream=None):
+    """Forward with unrotated Q and K, turned at the plan's positions first."""
+    import torch
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    _need(q, (plan.T, Hq, D), q.dtype, "q")
+    _need(k, (plan.T, Hkv, D), q.dtype, "k")
+    _need(v, (plan.T, Hkv, D), q.dtype, "v")
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device) if lse is None else lse
+    code = _dtype_code(q)
+    if ws is None:
+        need = rope_workspace_bytes(plan, code, Hq, Hkv, D) + fwd_workspace_bytes(plan, code,
+                                                                                Hq, Hkv, D)
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    s = stream or torch.cuda.current_stream(q.device)
+    _check(lib().octopus_dag_attn_fwd_rope(plan.handle, code, Hq, Hkv, D, float(scale or 0.0),
+                                           float(base), q.data_ptr(), k.data_ptr(),
+                                           v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                           ws.data_ptr(), ws.numel(), _vp(s.cuda_stream)))
+    return o, lse
+
+
+def attn_bwd_rope(plan: Plan, q, k, v, o, lse, dout, base=10000.0, scale=None, dq=None,
+                  dk=None, dv=None, ws=None, stream=None):
+    """Backward with unrotated Q and K: returns gradients with respect to them."""
+    import torch
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    for t, shp, nm in ((q, (plan.T, Hq, D), "q"), (k, (plan.T, Hkv, D), "k"),
+                       (v, (plan.T, Hkv, D), "v"), (o, (plan.T, Hq, D), "o"),
+                       (dout, (plan.T, Hq, D), "dout")):
+        _need(t, shp, q.dtype, nm)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    code = _dtype_code(q)
+    if ws is None:
+        need = rope_workspace_bytes(plan, code, Hq, Hkv, D) + bwd_workspace_bytes(plan, code,
+                                                                                Hq, Hkv, D)
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    s = stream or torch.cuda.current_stream(q.device)
+    _check(lib().octopus_dag_attn_bwd_rope(plan.handle, code, Hq, Hkv, D, float(scale or 0.0),
+                                           float(base), q.data_ptr(), k.data_ptr(),
+                                           v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                           dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                           dv.data_ptr(), ws.data_ptr(), ws.numel(),
+                                           _vp(s.cuda_stream)))
+    return dq, dk, dv
 
 
 # ----------------------------------------------------------------------------- decode

@@ -57,6 +57,7 @@ octo::DevPlan dev_view(const octo::Plan& p) {
     d.blk_order = reinterpret_cast<const int32_t*>(base + p.layout.blk_order);
     d.blk_ptr = reinterpret_cast<const int32_t*>(base + p.layout.blk_ptr);
     d.blk_entries = reinterpret_cast<const int4*>(base + p.layout.blk_entries);
+    d.pos = reinterpret_cast<const int32_t*>(base + p.layout.pos);
     return d;
 }
 
@@ -217,6 +218,56 @@ int octopus_dag_attn_fwd(const octopus_plan* plan, octopus_dtype dtype, int32_t 
     return ok();
 }
 
+namespace {
+
+size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Rotated copies of Q and K at the front of a RoPE workspace.
+size_t rope_part(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq, int32_t Hkv,
+                 int32_t D) {
+    const size_t es = dtype == OCTOPUS_BF16 ? 2 : 4;
+    const size_t T = (size_t)plan->p.T;
+    return round256(T * Hq * D * es) + round256(T * Hkv * D * es);
+}
+
+}  // namespace
+
+size_t octopus_rope_workspace_bytes(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
+                                    int32_t Hkv, int32_t D) {
+    if (plan == nullptr || Hq < 1 || Hkv < 1 || (D != 64 && D != 128) ||
+        (dtype != OCTOPUS_BF16 && dtype != OCTOPUS_FP32))
+        return 0;
+    return rope_part(plan, dtype, Hq, Hkv, D);
+}
+
+int octopus_dag_attn_fwd_rope(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
+                              int32_t Hkv, int32_t D, float scale, float rope_base,
+                              const void* q, const void* k, const void* v, void* o, float* lse,
+                              void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_attn(plan, dtype, Hq, Hkv, D, {q, k, v, o, lse});
+    if (rc != OCTOPUS_OK) return rc;
+    if (!(rope_base > 1.f)) return fail(OCTOPUS_EINVAL, "rope_base must be > 1");
+    const size_t head = rope_part(plan, dtype, Hq, Hkv, D);
+    const size_t need = head + octopus_fwd_workspace_bytes(plan, dtype, Hq, Hkv, D);
+    if (ws == nullptr || ws_bytes < need || !aligned(ws, 256))
+        return fail(OCTOPUS_EWORKSPACE, "forward (rope) workspace needs " +
+                                            std::to_string(need) + " bytes, 256-byte aligned");
+    unsigned char* w = static_cast<unsigned char*>(ws);
+    const size_t es = dtype == OCTOPUS_BF16 ? 2 : 4;
+    void* qr = w;
+    void* kr = w + round256((size_t)plan->p.T * Hq * D * es);
+    const octo::DevPlan dp = dev_view(plan->p);
+    const bool b16 = dtype == OCTOPUS_BF16;
+    hipError_t e = octo::launch_rope(b16, dp.T, Hq, D, rope_base, false, dp.pos, q, qr,
+                                     (hipStream_t)stream);
+    if (e == hipSuccess)
+        e = octo::launch_rope(b16, dp.T, Hkv, D, rope_base, false, dp.pos, k, kr,
+                              (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "rope launch");
+    return octopus_dag_attn_fwd(plan, dtype, Hq, Hkv, D, scale, qr, kr, v, o, lse, w + head,
+                                ws_bytes - head, stream);
+}
+
 size_t octopus_bwd_workspace_bytes(const octopus_plan* plan, octopus_dtype, int32_t Hq,
                                    int32_t, int32_t) {
     if (plan == nullptr || Hq < 1) return 0;
@@ -302,6 +353,39 @@ int octopus_dag_attn_bwd(const octopus_plan* plan, octopus_dtype dtype, int32_t 
     return rc;
 }
 
+int octopus_dag_attn_bwd_rope(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
+                              int32_t Hkv, int32_t D, float scale, float rope_base,
+                              const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                              void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_attn(plan, dtype, Hq, Hkv, D, {q, k, v, o, lse, dout, dq, dk, dv});
+    if (rc != OCTOPUS_OK) return rc;
+    if (!(rope_base > 1.f)) return fail(OCTOPUS_EINVAL, "rope_base must be > 1");
+    const size_t head = rope_part(plan, dtype, Hq, Hkv, D);
+    const size_t need = head + octopus_bwd_workspace_bytes(plan, dtype, Hq, Hkv, D);
+    if (ws == nullptr || ws_bytes < need || !aligned(ws, 256))
+        return fail(OCTOPUS_EWORKSPACE, "backward (rope) workspace needs " +
+                                            std::to_string(need) + " bytes, 256-byte aligned");
+    unsigned char* w = static_cast<unsigned char*>(ws);
+    const size_t es = dtype == OCTOPUS_BF16 ? 2 : 4;
+    void* qr = w;
+    void* kr = w + round256((size_t)plan->p.T * Hq * D * es);
+    const octo::DevPlan dp = dev_view(plan->p);
+    const bool b16 = dtype == OCTOPUS_BF16;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = octo::launch_rope(b16, dp.T, Hq, D, rope_base, false, dp.pos, q, qr, st);
+    if (e == hipSuccess) e = octo::launch_rope(b16, dp.T, Hkv, D, rope_base, false, dp.pos, k, kr, st);
+    if (e != hipSuccess) return hip_fail(e, "rope launch");
+    // Gradients with respect to the rotated Q and K, then turned back in place.
+    rc = octopus_dag_attn_bwd(plan, dtype, Hq, Hkv, D, scale, qr, kr, v, o, lse, dout, dq, dk,
+                              dv, w + head, ws_bytes - head, stream);
+    if (rc != OCTOPUS_OK) return rc;
+    e = octo::launch_rope(b16, dp.T, Hq, D, rope_base, true, dp.pos, dq, dq, st);
+    if (e == hipSuccess) e = octo::launch_rope(b16, dp.T, Hkv, D, rope_base, true, dp.pos, dk, dk, st);
+    if (e != hipSuccess) return hip_fail(e, "rope launch");
+    return ok();
+}
+
 int octopus_decode_segments(const octopus_branch* branches, int32_t n_branches,
                             const octopus_mount* mounts, int32_t n_mounts,
                             const int32_t* page_ptr, const int32_t* pages, int32_t page_size,
@@ -347,6 +431,37 @@ int octopus_decode_segments(const octopus_branch* branches, int32_t n_branches,
     } catch (const std::bad_alloc&) {
         return fail(OCTOPUS_ENOMEM, "host allocation failed while building segments");
     }
+}
+
+int octopus_dag_positions(const octopus_branch* branches, int32_t n_branches,
+                          const octopus_mount* mounts, int32_t n_mounts, int32_t total_tokens,
+                          int32_t* pos_out) {
+    if (pos_out == nullptr) return fail(OCTOPUS_EINVAL, "pos_out is NULL");
+    try {
+        octo::DagInfo dag;
+        std::string err;
+        const int rc = octo::load_dag(branches, n_branches, mounts, n_mounts, total_tokens, dag,
+                                      err);
+        if (rc != OCTOPUS_OK) return fail(rc, err);
+        for (int32_t i = 0; i < total_tokens; ++i) pos_out[i] = (int32_t)dag.pos[i];
+        return ok();
+    } catch (const std::bad_alloc&) {
+        return fail(OCTOPUS_ENOMEM, "host allocation failed while computing positions");
+    }
+}
+
+int octopus_rope(octopus_dtype dtype, int32_t rows, int32_t H, int32_t D, float rope_base,
+                 int32_t inverse, const int32_t* pos, const void* x, void* out, void* stream) {
+    if (dtype != OCTOPUS_BF16 && dtype != OCTOPUS_FP32)
+        return fail(OCTOPUS_EUNSUPPORTED, "dtype must be bf16 or fp32");
+    if (D != 64 && D != 128) return fail(OCTOPUS_EUNSUPPORTED, "head_dim must be 64 or 128");
+    if (rows < 0 || H < 1) return fail(OCTOPUS_EINVAL, "rows must be >= 0 and H >= 1");
+    if (!(rope_base > 1.f)) return fail(OCTOPUS_EINVAL, "rope_base must be > 1");
+    if (rows > 0 && (!pos || !x || !out)) return fail(OCTOPUS_EINVAL, "NULL pointer");
+    const hipError_t e = octo::launch_rope(dtype == OCTOPUS_BF16, rows, H, D, rope_base,
+                                           inverse != 0, pos, x, out, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "rope launch");
+    return ok();
 }
 
 int octopus_extend_segments(const octopus_branch* branches, int32_t n_branches,

@@ -25,6 +25,7 @@ struct DevPlan {
     const int32_t* blk_ptr;     // [nKB+1]
     const int4* blk_entries;    // {q_tile, mask of tile 2b, mask of tile 2b+1, 0};
                                 // mask -1 FULL, -2 not seen, else PARTIAL index
+    const int32_t* pos;         // [T] position of every packed token
 };
 
 constexpr int kBq = 128;  // query rows per tile
@@ -67,6 +68,12 @@ hipError_t launch_decode_bf16(int B, int Hq, int Hkv, int D, int page_size, floa
                               const int32_t* seg_lo, const int32_t* seg_hi, int n_groups,
                               const int32_t* grp_ptr, const int32_t* grp_cur, int n_split,
                               void* o, float* lse, float* partial, hipStream_t s);
+
+// Rotary embedding in place or out of place: x is [rows][H][D] (bf16 if `bf16`, else
+// float32); row r turns by pos[r] * base^(-2i/D) on pairs (i, i + D/2), by the opposite
+// angle if `inverse`.  out may equal x.
+hipError_t launch_rope(bool bf16, int rows, int H, int D, float base, bool inverse,
+                       const int32_t* pos, const void* x, void* out, hipStream_t s);
 
 // Extend: rows q_ptr[c] .. q_ptr[c+1]-1 of q are cursor c's new tokens (own offsets
 // first_off[c] + j); segments as built by build_extend_segments.  max_new >= every m_c.

@@ -427,6 +427,7 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     L.blk_order = place(p.blk_order.size() * 4);
     L.blk_ptr = place(p.blk_ptr.size() * 4);
     L.blk_entries = place(p.blk_entries.size() * sizeof(BlockEntry));
+    L.pos = place((size_t)T * 4);
     L.total = std::max<size_t>(at, 256);
     p.blob.assign(L.total, 0);
     auto put = [&](size_t off, const void* src, size_t bytes) {
@@ -443,6 +444,10 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     put(L.blk_order, p.blk_order.data(), p.blk_order.size() * 4);
     put(L.blk_ptr, p.blk_ptr.data(), p.blk_ptr.size() * 4);
     put(L.blk_entries, p.blk_entries.data(), p.blk_entries.size() * sizeof(BlockEntry));
+    {
+        int32_t* pos = reinterpret_cast<int32_t*>(p.blob.data() + L.pos);
+        for (int32_t i = 0; i < T; ++i) pos[i] = (int32_t)d.pos[i];
+    }
     return OCTOPUS_OK;
 }
 

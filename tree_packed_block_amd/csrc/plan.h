@@ -63,7 +63,7 @@ struct BlockEntry {
 struct DevLayout {
     size_t fwd_order = 0, qt_ptr = 0, q_pairs = 0, bwd_order = 0, kt_ptr = 0,
            k_pairs = 0, mask_rows = 0, mask_cols = 0, blk_order = 0, blk_ptr = 0,
-           blk_entries = 0, total = 0;
+           blk_entries = 0, pos = 0, total = 0;
 };
 
 struct Plan {
