@@ -434,6 +434,31 @@ def main():
                      "new_tokens": rows_e, "pairs": pairs_e, "timed": "own clock, not in "
                      "the step"}
 
+    # The RoPE pass of the RoPE entry points, on its own clock: Q and K turned at the
+    # plan's positions in one launch (the forward runs it once, the backward once more
+    # and once in reverse on dQ, dK).
+    wsr = torch.empty(tpb.rope_workspace_bytes(probe, tpb.BF16, HQ, HKV, HD)
+                      + tpb.fwd_workspace_bytes(probe, tpb.BF16, HQ, HKV, HD),
+                      dtype=torch.uint8, device=dev)
+    plan_r = tpb.Plan(dag.branches, dag.mounts, dag.T).upload()
+    o_r, lse_r = torch.empty_like(q), torch.empty_like(lse)
+
+    def run_rope():
+        tpb.attn_fwd_rope(plan_r, q, k, v, o=o_r, lse=lse_r, ws=wsr)
+
+    run_rope()
+    ev_r = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev_r[0].record(stream)
+    for j in range(3):
+        run_rope()
+        ev_r[j + 1].record(stream)
+    torch.cuda.synchronize()
+    ms_r = float(np.median([ev_r[j].elapsed_time(ev_r[j + 1]) for j in range(3)]))
+    out["breakdown"]["fwd_rope"] = {
+        "ms": round(ms_r, 3), "rope_overhead_ms": round(ms_r - per["fwd"], 3),
+        "note": "forward with unrotated Q, K: the RoPE pass (Q and K turned at the plan's "
+                "positions, one launch) plus the same forward"}
+
     if not args.no_cpu_baseline:
         log("cpu baseline (float64 oracle on a sample) ...")
         out["cpu_baseline"] = cpu_baseline(dag, x)

@@ -258,11 +258,8 @@ int octopus_dag_attn_fwd_rope(const octopus_plan* plan, octopus_dtype dtype, int
     void* kr = w + round256((size_t)plan->p.T * Hq * D * es);
     const octo::DevPlan dp = dev_view(plan->p);
     const bool b16 = dtype == OCTOPUS_BF16;
-    hipError_t e = octo::launch_rope(b16, dp.T, Hq, D, rope_base, false, dp.pos, q, qr,
-                                     (hipStream_t)stream);
-    if (e == hipSuccess)
-        e = octo::launch_rope(b16, dp.T, Hkv, D, rope_base, false, dp.pos, k, kr,
-                              (hipStream_t)stream);
+    const hipError_t e = octo::launch_rope2(b16, dp.T, D, rope_base, false, dp.pos, Hq, q, qr,
+                                            Hkv, k, kr, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "rope launch");
     return octopus_dag_attn_fwd(plan, dtype, Hq, Hkv, D, scale, qr, kr, v, o, lse, w + head,
                                 ws_bytes - head, stream);
@@ -373,15 +370,14 @@ int octopus_dag_attn_bwd_rope(const octopus_plan* plan, octopus_dtype dtype, int
     const octo::DevPlan dp = dev_view(plan->p);
     const bool b16 = dtype == OCTOPUS_BF16;
     hipStream_t st = (hipStream_t)stream;
-    hipError_t e = octo::launch_rope(b16, dp.T, Hq, D, rope_base, false, dp.pos, q, qr, st);
-    if (e == hipSuccess) e = octo::launch_rope(b16, dp.T, Hkv, D, rope_base, false, dp.pos, k, kr, st);
+    hipError_t e = octo::launch_rope2(b16, dp.T, D, rope_base, false, dp.pos, Hq, q, qr, Hkv, k,
+                                      kr, st);
     if (e != hipSuccess) return hip_fail(e, "rope launch");
     // Gradients with respect to the rotated Q and K, then turned back in place.
     rc = octopus_dag_attn_bwd(plan, dtype, Hq, Hkv, D, scale, qr, kr, v, o, lse, dout, dq, dk,
                               dv, w + head, ws_bytes - head, stream);
     if (rc != OCTOPUS_OK) return rc;
-    e = octo::launch_rope(b16, dp.T, Hq, D, rope_base, true, dp.pos, dq, dq, st);
-    if (e == hipSuccess) e = octo::launch_rope(b16, dp.T, Hkv, D, rope_base, true, dp.pos, dk, dk, st);
+    e = octo::launch_rope2(b16, dp.T, D, rope_base, true, dp.pos, Hq, dq, dq, Hkv, dk, dk, st);
     if (e != hipSuccess) return hip_fail(e, "rope launch");
     return ok();
 }

@@ -74,6 +74,11 @@ hipError_t launch_decode_bf16(int B, int Hq, int Hkv, int D, int page_size, floa
 // angle if `inverse`.  out may equal x.
 hipError_t launch_rope(bool bf16, int rows, int H, int D, float base, bool inverse,
                        const int32_t* pos, const void* x, void* out, hipStream_t s);
+// The same for two tensors sharing the rows' positions in one pass (x2/out2 with H2
+// heads; x2 may be NULL).
+hipError_t launch_rope2(bool bf16, int rows, int D, float base, bool inverse,
+                        const int32_t* pos, int H, const void* x, void* out, int H2,
+                        const void* x2, void* out2, hipStream_t s);
 
 // Extend: rows q_ptr[c] .. q_ptr[c+1]-1 of q are cursor c's new tokens (own offsets
 // first_off[c] + j); segments as built by build_extend_segments.  max_new >= every m_c.
