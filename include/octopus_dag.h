@@ -248,6 +248,29 @@ int octopus_dag_attn_bwd_rope(const octopus_plan* plan, octopus_dtype dtype, int
                               const float* lse, const void* dout, void* dq, void* dk, void* dv,
                               void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- recurrent scan */
+
+/* Workspace bytes of octopus_gated_delta_scan: float32 fork checkpoints
+ * [n_slots][H][Dv][Dk], one slot per distinct (parent, fork offset) of the plan. */
+size_t octopus_gdn_workspace_bytes(const octopus_plan* plan, int32_t H, int32_t Dk,
+                                   int32_t Dv);
+
+/* Branch-aware gated delta-rule scan (the recurrent layers of a hybrid backbone, Gated
+ * DeltaNet; Octopus project page, primitives table: `fork` clones the parent's recurrent
+ * checkpoint, mounted spans bypass the recurrent layers).  Per head, state S (Dv x Dk):
+ *     S_t = alpha_t (S_{t-1} - beta_t (S_{t-1} k_t) k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t,
+ * over each branch's own tokens in order, a root from S = 0, a child from its parent's
+ * state just before the parent's own token `fork`; mounts are ignored.
+ * q, k [T][H][Dk], v, o [T][H][Dv] (dtype); alpha, beta float32 [T][H] (device).
+ * The plan must be uploaded.  Levels of the tree run one launch each, in order.
+ * Supported: bf16, Dk = Dv = 128.  Errors: EINVAL, ESTATE, EUNSUPPORTED, EWORKSPACE,
+ * EHIP. */
+int octopus_gated_delta_scan(const octopus_plan* plan, octopus_dtype dtype, int32_t H,
+                             int32_t Dk, int32_t Dv, const void* q, const void* k,
+                             const void* v, const float* alpha, const float* beta, void* o,
+                             void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- paged decode */
 
 /* Host helper: turn a DAG of branches held in a page pool into per-cursor segment

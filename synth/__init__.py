@@ -20,4 +20,5 @@ from .tensors import (  # noqa: F401
     draw_attention_inputs,
     draw_decode_inputs,
     draw_extend_inputs,
+    draw_scan_inputs,
 )

@@ -105,3 +105,21 @@ def draw_extend_inputs(rng: np.random.Generator, n_rows: int, Hq: int, Hkv: int,
     if dtype == "bf16":
         q, kp, vp = round_bf16(q), round_bf16(kp), round_bf16(vp)
     return {"q": q, "k_pool": kp, "v_pool": vp}
+
+
+def draw_scan_inputs(rng: np.random.Generator, T: int, H: int, D: int = 128,
+                     dtype: str = "bf16"):
+    """Recurrent-layer inputs: q and k unit vectors per (token, head) (the layer
+    normalises them before the scan), v ~ N(0, 0.25), gates alpha in [0.9, 1) and step
+    sizes beta in [0.05, 0.95), float32."""
+    q = rng.standard_normal((T, H, D))
+    k = rng.standard_normal((T, H, D))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = 0.5 * rng.standard_normal((T, H, D))
+    alpha = rng.uniform(0.9, 1.0, size=(T, H)).astype(np.float32)
+    beta = rng.uniform(0.05, 0.95, size=(T, H)).astype(np.float32)
+    q, k, v = (x.astype(np.float32) for x in (q, k, v))
+    if dtype == "bf16":
+        q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
+    return {"q": q, "k": k, "v": v, "alpha": alpha, "beta": beta}

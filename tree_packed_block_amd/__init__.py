@@ -27,6 +27,8 @@ from ._lib import (  # noqa: F401
     decode_segments,
     decode_workspace_bytes,
     extend_segments,
+    gated_delta_scan,
+    gdn_workspace_bytes,
     default_scale,
     fwd_workspace_bytes,
     lib,

@@ -32,7 +32,8 @@ EXPORTS = [
     "octopus_decode_workspace_bytes", "octopus_paged_mount_decode", "octopus_extend_segments",
     "octopus_paged_mount_extend", "octopus_dag_positions", "octopus_rope",
     "octopus_rope_workspace_bytes", "octopus_dag_attn_fwd_rope", "octopus_dag_attn_bwd_rope",
-    "octopus_last_error", "octopus_version",
+    "octopus_gdn_workspace_bytes", "octopus_gated_delta_scan", "octopus_last_error",
+    "octopus_version",
 ]
 
 
@@ -131,6 +132,12 @@ def lib():
                                             ctypes.c_int32, ctypes.c_float, ctypes.c_float,
                                             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                             ctypes.c_size_t, _vp]
+    L.octopus_gdn_workspace_bytes.argtypes = [_vp, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32]
+    L.octopus_gdn_workspace_bytes.restype = ctypes.c_size_t
+    L.octopus_gated_delta_scan.argtypes = [_vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                           ctypes.c_size_t, _vp]
     L.octopus_last_error.restype = ctypes.c_char_p
     L.octopus_version.restype = ctypes.c_char_p
     _lib = L
@@ -420,6 +427,35 @@ def attn_bwd_rope(plan: Plan, q, k, v, o, lse, dout, base=10000.0, scale=None, d
                                            dv.data_ptr(), ws.data_ptr(), ws.numel(),
                                            _vp(s.cuda_stream)))
     return dq, dk, dv
+
+
+# ----------------------------------------------------------------------------- scan
+
+def gdn_workspace_bytes(plan: Plan, H, Dk=128, Dv=128) -> int:
+    return int(lib().octopus_gdn_workspace_bytes(plan.handle, H, Dk, Dv))
+
+
+def gated_delta_scan(plan: Plan, q, k, v, alpha, beta, o=None, ws=None, stream=None):
+    """Branch-aware gated delta-rule scan: ``q, k [T,H,Dk]``, ``v [T,H,Dv]`` bf16,
+    ``alpha, beta`` float32 ``[T,H]``; returns ``o [T,H,Dv]``."""
+    import torch
+    T, H, Dk = q.shape
+    Dv = v.shape[2]
+    _need(q, (plan.T, H, Dk), q.dtype, "q")
+    _need(k, (plan.T, H, Dk), q.dtype, "k")
+    _need(v, (plan.T, H, Dv), q.dtype, "v")
+    _need(alpha, (plan.T, H), torch.float32, "alpha")
+    _need(beta, (plan.T, H), torch.float32, "beta")
+    o = torch.empty_like(v) if o is None else o
+    if ws is None:
+        ws = torch.empty(max(gdn_workspace_bytes(plan, H, Dk, Dv), 16), dtype=torch.uint8,
+                         device=q.device)
+    s = stream or torch.cuda.current_stream(q.device)
+    _check(lib().octopus_gated_delta_scan(plan.handle, _dtype_code(q), H, Dk, Dv, q.data_ptr(),
+                                          k.data_ptr(), v.data_ptr(), alpha.data_ptr(),
+                                          beta.data_ptr(), o.data_ptr(), ws.data_ptr(),
+                                          ws.numel(), _vp(s.cuda_stream)))
+    return o
 
 
 # ----------------------------------------------------------------------------- decode

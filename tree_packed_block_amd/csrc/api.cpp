@@ -58,6 +58,13 @@ octo::DevPlan dev_view(const octo::Plan& p) {
     d.blk_ptr = reinterpret_cast<const int32_t*>(base + p.layout.blk_ptr);
     d.blk_entries = reinterpret_cast<const int4*>(base + p.layout.blk_entries);
     d.pos = reinterpret_cast<const int32_t*>(base + p.layout.pos);
+    d.sc_start = reinterpret_cast<const int32_t*>(base + p.layout.sc_start);
+    d.sc_len = reinterpret_cast<const int32_t*>(base + p.layout.sc_len);
+    d.sc_init = reinterpret_cast<const int32_t*>(base + p.layout.sc_init);
+    d.sc_ck_ptr = reinterpret_cast<const int32_t*>(base + p.layout.sc_ck_ptr);
+    d.sc_ck_off = reinterpret_cast<const int32_t*>(base + p.layout.sc_ck_off);
+    d.sc_ck_slot = reinterpret_cast<const int32_t*>(base + p.layout.sc_ck_slot);
+    d.sc_level_br = reinterpret_cast<const int32_t*>(base + p.layout.sc_level_br);
     return d;
 }
 
@@ -457,6 +464,40 @@ int octopus_rope(octopus_dtype dtype, int32_t rows, int32_t H, int32_t D, float 
     const hipError_t e = octo::launch_rope(dtype == OCTOPUS_BF16, rows, H, D, rope_base,
                                            inverse != 0, pos, x, out, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "rope launch");
+    return ok();
+}
+
+size_t octopus_gdn_workspace_bytes(const octopus_plan* plan, int32_t H, int32_t Dk,
+                                   int32_t Dv) {
+    if (plan == nullptr || H < 1 || Dk != 128 || Dv != 128) return 0;
+    return (size_t)std::max(plan->p.n_slots, 1) * H * Dv * Dk * sizeof(float);
+}
+
+int octopus_gated_delta_scan(const octopus_plan* plan, octopus_dtype dtype, int32_t H,
+                             int32_t Dk, int32_t Dv, const void* q, const void* k,
+                             const void* v, const float* alpha, const float* beta, void* o,
+                             void* ws, size_t ws_bytes, void* stream) {
+    if (plan == nullptr) return fail(OCTOPUS_EINVAL, "plan is NULL");
+    if (plan->p.dev == nullptr) return fail(OCTOPUS_ESTATE, "plan not uploaded");
+    if (dtype != OCTOPUS_BF16) return fail(OCTOPUS_EUNSUPPORTED, "the scan supports bf16 only");
+    if (Dk != 128 || Dv != 128) return fail(OCTOPUS_EUNSUPPORTED, "the scan supports Dk = Dv = 128");
+    if (H < 1) return fail(OCTOPUS_EINVAL, "H must be >= 1");
+    for (const void* p : {q, k, v, (const void*)alpha, (const void*)beta, (const void*)o}) {
+        if (p == nullptr) return fail(OCTOPUS_EINVAL, "a tensor pointer is NULL");
+        if (!aligned(p, 16)) return fail(OCTOPUS_EINVAL, "tensors must be 16-byte aligned");
+    }
+    const size_t need = octopus_gdn_workspace_bytes(plan, H, Dk, Dv);
+    if (ws == nullptr || ws_bytes < need || !aligned(ws, 16))
+        return fail(OCTOPUS_EWORKSPACE, "scan workspace needs " + std::to_string(need) +
+                                            " bytes, 16-byte aligned");
+    const octo::DevPlan dp = dev_view(plan->p);
+    const std::vector<int32_t>& lp = plan->p.level_ptr;
+    for (size_t l = 0; l + 1 < lp.size(); ++l) {
+        const hipError_t e = octo::launch_gdn_scan(dp, lp[l], lp[l + 1] - lp[l], H, q, k, v,
+                                                   alpha, beta, o, static_cast<float*>(ws),
+                                                   (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "scan launch");
+    }
     return ok();
 }
 

@@ -26,6 +26,11 @@ struct DevPlan {
     const int4* blk_entries;    // {q_tile, mask of tile 2b, mask of tile 2b+1, 0};
                                 // mask -1 FULL, -2 not seen, else PARTIAL index
     const int32_t* pos;         // [T] position of every packed token
+    // Recurrent scan (per branch): own tokens [start, start + len), initial checkpoint
+    // slot (-1: zero state), checkpoints to save (CSR over branches: own offset, slot),
+    // branches grouped by depth.
+    const int32_t *sc_start, *sc_len, *sc_init, *sc_ck_ptr, *sc_ck_off, *sc_ck_slot,
+        *sc_level_br;
 };
 
 constexpr int kBq = 128;  // query rows per tile
@@ -79,6 +84,13 @@ hipError_t launch_rope(bool bf16, int rows, int H, int D, float base, bool inver
 hipError_t launch_rope2(bool bf16, int rows, int D, float base, bool inverse,
                         const int32_t* pos, int H, const void* x, void* out, int H2,
                         const void* x2, void* out2, hipStream_t s);
+
+// Gated delta-rule scan of the branches level_br[l0 .. l0 + n_br): q, k [T][H][128] and
+// v [T][H][128] bf16, alpha, beta float32 [T][H]; o [T][H][128] bf16; states: float32
+// checkpoint slots [n_slots][H][128][128] (row = value index).
+hipError_t launch_gdn_scan(const DevPlan& p, int l0, int n_br, int H, const void* q,
+                           const void* k, const void* v, const float* alpha,
+                           const float* beta, void* o, float* states, hipStream_t s);
 
 // Extend: rows q_ptr[c] .. q_ptr[c+1]-1 of q are cursor c's new tokens (own offsets
 // first_off[c] + j); segments as built by build_extend_segments.  max_new >= every m_c.

@@ -408,6 +408,50 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     for (int32_t t = 0; t < nKT; ++t)
         p.max_kv_list = std::max(p.max_kv_list, p.kt_ptr[t + 1] - p.kt_ptr[t]);
 
+    // Recurrent scan metadata: one checkpoint slot per distinct (parent, fork offset);
+    // levels by depth so that a level's branches start from states the previous levels
+    // saved.
+    {
+        std::map<std::pair<int32_t, int32_t>, int32_t> slot;
+        p.sc_init.assign(nb, -1);
+        std::vector<std::vector<std::pair<int32_t, int32_t>>> cks(nb);
+        for (int32_t b = 0; b < nb; ++b) {
+            const octopus_branch& B = d.br[b];
+            if (B.parent < 0) continue;
+            const auto key = std::make_pair(B.parent, B.fork);
+            auto it = slot.find(key);
+            if (it == slot.end()) {
+                it = slot.emplace(key, (int32_t)slot.size()).first;
+                cks[B.parent].push_back({B.fork, it->second});
+            }
+            p.sc_init[b] = it->second;
+        }
+        p.n_slots = (int32_t)slot.size();
+        p.sc_ck_ptr.assign(1, 0);
+        p.sc_ck_off.clear();
+        p.sc_ck_slot.clear();
+        for (int32_t b = 0; b < nb; ++b) {
+            std::sort(cks[b].begin(), cks[b].end());
+            for (const auto& c : cks[b]) {
+                p.sc_ck_off.push_back(c.first);
+                p.sc_ck_slot.push_back(c.second);
+            }
+            p.sc_ck_ptr.push_back((int32_t)p.sc_ck_off.size());
+        }
+        std::vector<int32_t> depth(nb, 0);
+        int32_t max_depth = 0;
+        for (int32_t b = 0; b < nb; ++b) {
+            if (d.br[b].parent >= 0) depth[b] = depth[d.br[b].parent] + 1;
+            max_depth = std::max(max_depth, depth[b]);
+        }
+        p.level_ptr.assign(max_depth + 2, 0);
+        for (int32_t b = 0; b < nb; ++b) p.level_ptr[depth[b] + 1] += 1;
+        for (int32_t l = 0; l <= max_depth; ++l) p.level_ptr[l + 1] += p.level_ptr[l];
+        p.level_br.assign(nb, 0);
+        std::vector<int32_t> fill(p.level_ptr.begin(), p.level_ptr.end() - 1);
+        for (int32_t b = 0; b < nb; ++b) p.level_br[fill[depth[b]]++] = b;
+    }
+
     // Device image: every array 256-byte aligned.
     DevLayout& L = p.layout;
     size_t at = 0;
@@ -428,6 +472,13 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     L.blk_ptr = place(p.blk_ptr.size() * 4);
     L.blk_entries = place(p.blk_entries.size() * sizeof(BlockEntry));
     L.pos = place((size_t)T * 4);
+    L.sc_start = place((size_t)nb * 4);
+    L.sc_len = place((size_t)nb * 4);
+    L.sc_init = place((size_t)nb * 4);
+    L.sc_ck_ptr = place(p.sc_ck_ptr.size() * 4);
+    L.sc_ck_off = place(std::max<size_t>(p.sc_ck_off.size(), 1) * 4);
+    L.sc_ck_slot = place(std::max<size_t>(p.sc_ck_slot.size(), 1) * 4);
+    L.sc_level_br = place((size_t)nb * 4);
     L.total = std::max<size_t>(at, 256);
     p.blob.assign(L.total, 0);
     auto put = [&](size_t off, const void* src, size_t bytes) {
@@ -447,7 +498,18 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     {
         int32_t* pos = reinterpret_cast<int32_t*>(p.blob.data() + L.pos);
         for (int32_t i = 0; i < T; ++i) pos[i] = (int32_t)d.pos[i];
+        int32_t* st = reinterpret_cast<int32_t*>(p.blob.data() + L.sc_start);
+        int32_t* ln = reinterpret_cast<int32_t*>(p.blob.data() + L.sc_len);
+        for (int32_t b = 0; b < nb; ++b) {
+            st[b] = d.br[b].start;
+            ln[b] = d.br[b].len;
+        }
     }
+    put(L.sc_init, p.sc_init.data(), p.sc_init.size() * 4);
+    put(L.sc_ck_ptr, p.sc_ck_ptr.data(), p.sc_ck_ptr.size() * 4);
+    put(L.sc_ck_off, p.sc_ck_off.data(), p.sc_ck_off.size() * 4);
+    put(L.sc_ck_slot, p.sc_ck_slot.data(), p.sc_ck_slot.size() * 4);
+    put(L.sc_level_br, p.level_br.data(), p.level_br.size() * 4);
     return OCTOPUS_OK;
 }
 

@@ -63,7 +63,8 @@ struct BlockEntry {
 struct DevLayout {
     size_t fwd_order = 0, qt_ptr = 0, q_pairs = 0, bwd_order = 0, kt_ptr = 0,
            k_pairs = 0, mask_rows = 0, mask_cols = 0, blk_order = 0, blk_ptr = 0,
-           blk_entries = 0, pos = 0, total = 0;
+           blk_entries = 0, pos = 0, sc_start = 0, sc_len = 0, sc_init = 0, sc_ck_ptr = 0,
+           sc_ck_off = 0, sc_ck_slot = 0, sc_level_br = 0, total = 0;
 };
 
 struct Plan {
@@ -82,6 +83,11 @@ struct Plan {
     std::vector<uint64_t> mask_cols;  // [n_partial][Bk][col_words]
     int64_t nnz = 0, n_partial = 0;
     int32_t max_q_list = 0, max_kv_list = 0;
+    // Recurrent scan: branches grouped by depth (level_ptr over level_br); a branch
+    // starts from checkpoint slot sc_init (-1: zero state) and saves its state before own
+    // token sc_ck_off[j] into slot sc_ck_slot[j] (its children's fork points).
+    std::vector<int32_t> sc_init, sc_ck_ptr, sc_ck_off, sc_ck_slot, level_ptr, level_br;
+    int32_t n_slots = 0;
     DevLayout layout;
     std::vector<unsigned char> blob;  // host image of the device copy
     void* dev = nullptr;              // caller-owned device copy after upload
