@@ -459,6 +459,36 @@ def main():
         "note": "forward with unrotated Q, K: the RoPE pass (Q and K turned at the plan's "
                 "positions, one launch) plus the same forward"}
 
+    # Recurrent-layer scan over the same tree, on its own clock: 16 heads of 128 x 128
+    # gated delta-rule state, each branch from its parent's fork checkpoint.
+    H_s = 16
+    xs = synth.draw_scan_inputs(np.random.default_rng(21), dag.T, H_s)
+    ts = {n: torch.from_numpy(a).to(dev) for n, a in xs.items()}
+    for n in ("q", "k", "v"):
+        ts[n] = ts[n].to(torch.bfloat16)
+    os_ = torch.empty_like(ts["v"])
+    wss = torch.empty(max(tpb.gdn_workspace_bytes(probe, H_s), 16), dtype=torch.uint8,
+                      device=dev)
+    plan_s = tpb.Plan(dag.branches, dag.mounts, dag.T).upload()
+
+    def run_scan():
+        tpb.gated_delta_scan(plan_s, ts["q"], ts["k"], ts["v"], ts["alpha"], ts["beta"],
+                             o=os_, ws=wss)
+
+    run_scan()
+    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev_s[0].record(stream)
+    for j in range(3):
+        run_scan()
+        ev_s[j + 1].record(stream)
+    torch.cuda.synchronize()
+    ms_s = float(np.median([ev_s[j].elapsed_time(ev_s[j + 1]) for j in range(3)]))
+    flops_s = 6.0 * 128 * 128 * H_s * dag.T
+    out["breakdown"]["gdn_scan"] = {
+        "ms": round(ms_s, 3), "GFLOP/s": round(flops_s / (ms_s * 1e-3) / 1e9, 1),
+        "note": "16 heads, 128x128 state, 6*Dk*Dv FLOP per token-head; sequential along "
+                "each branch (critical path: root + longest worker)"}
+
     if not args.no_cpu_baseline:
         log("cpu baseline (float64 oracle on a sample) ...")
         out["cpu_baseline"] = cpu_baseline(dag, x)
