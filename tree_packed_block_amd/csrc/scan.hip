@@ -108,6 +108,8 @@ __global__ __launch_bounds__(kThreads) void gdn_scan_kernel(DevPlan P, int l0, i
     const int n_chunks = (len + kChunk - 1) / kChunk;
     constexpr int KQ_PER = TILE / 16 / kThreads;  // k (and q) pieces per thread
     constexpr int VP = VT / 16;                   // v pieces in all
+    static_assert(KQ_PER * kThreads * 16 == TILE, "k and q tiles split evenly over threads");
+    static_assert(VP % 64 == 0 && VP <= kThreads, "the v slice is copied by whole waves");
     float ab = 0.f;
     auto issue = [&](int c, int st) {
         const int last = len - 1 - c * kChunk;  // last valid token within the chunk
