@@ -135,7 +135,8 @@ KERNEL_KEYS = (("fwd_bf16_kernel", "fwd"), ("tiles_t_kernel", "fwd"),
                ("extend_bf16_kernel", "extend"),
                ("preprocess_bf16_kernel", "bwd_preprocess"),
                ("dkdv_bf16_kernel", "bwd_dkdv"), ("dq_bf16_kernel", "bwd_dq"),
-               ("decode_split_kernel", "decode"), ("decode_combine_kernel", "decode"))
+               ("decode_split_kernel", "decode"), ("decode_combine_kernel", "decode"),
+               ("rope_kernel", "rope"), ("gdn_scan_kernel", "gdn_scan"))
 CALIBRATION_BYTES = 1 << 30  # the --calibrate-copy transfer
 
 
