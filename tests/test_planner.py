@@ -346,3 +346,57 @@ def test_extend_pair_count_matches_oracle():
         end = int(br[b, 2] + br[b, 3])
         want += int(D.mask_rows(br, wl.dag.mounts, T, end - int(n_new[c]), end).sum())
     assert bench.extend_pairs(segs, n_new, br, wl.cursors) == want
+
+
+def _code(rc):
+    names = {0: "OK", -1: "EINVAL", -2: "ECYCLE", -3: "EUNSUPPORTED", -4: "ENOMEM",
+             -5: "EWORKSPACE", -6: "EHIP", -7: "ESTATE"}
+    return names[rc]
+
+
+def test_new_entry_points_reject_bad_arguments_before_any_launch():
+    """Errors the RoPE, extend and scan entry points detect on the host (no device
+    memory is touched): unsupported head sizes and dtypes, bad counts, NULL pointers, a
+    plan that was never uploaded."""
+    L = tpb.lib()
+    dag, _ = synth.build("tiny")
+    p = tpb.Plan(dag.branches, dag.mounts, dag.T)
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call fails first
+    # RoPE pass
+    assert _code(L.octopus_rope(tpb.BF16, 4, 2, 96, 10000.0, 0, fake, fake, fake, None)) == "EUNSUPPORTED"
+    assert _code(L.octopus_rope(tpb.BF16, 4, 2, 128, 1.0, 0, fake, fake, fake, None)) == "EINVAL"
+    assert _code(L.octopus_rope(tpb.BF16, 4, 2, 128, 10000.0, 0, None, fake, fake, None)) == "EINVAL"
+    assert _code(L.octopus_rope(7, 4, 2, 128, 10000.0, 0, fake, fake, fake, None)) == "EUNSUPPORTED"
+    # RoPE attention entry points on a plan that was never uploaded
+    assert _code(L.octopus_dag_attn_fwd_rope(p.handle, tpb.BF16, 4, 2, 128, 0.0, 10000.0, fake,
+                                             fake, fake, fake, fake, fake, 1 << 30, None)) == "ESTATE"
+    assert _code(L.octopus_dag_attn_bwd_rope(p.handle, tpb.BF16, 4, 2, 128, 0.0, 10000.0, fake,
+                                             fake, fake, fake, fake, fake, fake, fake, fake,
+                                             fake, 1 << 30, None)) == "ESTATE"
+    # recurrent scan
+    assert _code(L.octopus_gated_delta_scan(p.handle, tpb.BF16, 2, 128, 128, fake, fake, fake,
+                                            fake, fake, fake, fake, 1 << 30, None)) == "ESTATE"
+    assert tpb.lib().octopus_gdn_workspace_bytes(p.handle, 2, 64, 128) == 0
+    # both children fork from the root at offset 256: one checkpoint slot
+    assert tpb.gdn_workspace_bytes(p, 2) == 1 * 2 * 128 * 128 * 4
+    # extend
+    assert _code(L.octopus_paged_mount_extend(tpb.BF16, 1, 16, 4, 64, 64, 0.0, fake, fake, fake,
+                                              4, fake, 1, fake, fake, fake, fake, fake, fake,
+                                              fake, fake, fake, None)) == "EUNSUPPORTED"
+    assert _code(L.octopus_paged_mount_extend(tpb.BF16, 1, 16, 4, 128, 64, 0.0, fake, fake, fake,
+                                              4, fake, 0, fake, fake, fake, fake, fake, fake,
+                                              fake, fake, fake, None)) == "EINVAL"
+    assert _code(L.octopus_paged_mount_extend(tpb.BF16, 1, 16, 4, 128, 32, 0.0, fake, fake, fake,
+                                              4, fake, 1, fake, fake, fake, fake, fake, fake,
+                                              fake, fake, fake, None)) == "EUNSUPPORTED"
+
+
+def test_positions_without_a_plan_match_the_oracle():
+    for name in ("tiny", "episode_mid", "forest_small"):
+        dag, _ = synth.build(name)
+        assert np.array_equal(tpb.dag_positions(dag.branches, dag.mounts, dag.T),
+                              D.positions(dag.branches, dag.mounts))
+    br = np.array([[-1, 0, 0, 4], [0, 4, 4, 6], [0, 4, 10, 6]])
+    with pytest.raises(tpb.OctopusError) as ei:
+        tpb.dag_positions(br, np.array([[1, 0, 2, 0, 5], [2, 0, 1, 0, 5]]), 16)
+    assert ei.value.name == "ECYCLE"
