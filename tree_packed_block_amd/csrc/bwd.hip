@@ -477,7 +477,6 @@ __global__ __launch_bounds__(256 * HPW, 1) void dq_bf16_kernel(
     int offv[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) offv[ks] = off.k[ks] - L::K0 + L::V0;
-    const int off_mask = L::M0 + rr * 8;
     TileDma<D, NTHR> dm;
     dm.init(tid, kvstride);
 
@@ -502,9 +501,10 @@ __global__ __launch_bounds__(256 * HPW, 1) void dq_bf16_kernel(
         if (it + 2 < n_it) issue(ic<(ST + 2) % 3>{}, it + 2);
         const bool partial = ld_const(P.q_pairs + p0 + it).y >= 0;
 
-        bf16x8 sb[4];
+        // One 32-key block at a time: S and dP, dS, then its two k-steps of
+        // dQ^T += K^T dS^T, whose MFMAs overlap the next block's softmax.
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {  // one 32-key block at a time (register pressure)
+        for (int kb = 0; kb < 2; ++kb) {
             f32x16 sc = mfma_32x32x16(ones, xl, zero16());
             f32x16 dp = mfma_32x32x16(ones, xd, zero16());
 #pragma unroll
@@ -513,32 +513,33 @@ __global__ __launch_bounds__(256 * HPW, 1) void dq_bf16_kernel(
                 sc = mfma_32x32x16(lds16(smem, off.k[ks], imm), qf[ks], sc);
                 dp = mfma_32x32x16(lds16(smem, offv[ks], imm), df[ks], dp);
             }
+            bf16x8 sb[2];
 #pragma unroll
             for (int j = 0; j < 16; ++j)
-                sb[kb * 2 + (j >> 3)][j & 7] = (bf16)(fast_exp2(sc[j]) * dp[j]);
-        }
-        if (__builtin_expect(partial, 0)) {  // wave-uniform and rare: clear dS where the
-            asm volatile("");                   // mask is 0 (a real branch, not selects)
-            const uint64_t bits =
-                *reinterpret_cast<const uint64_t*>(smem + off_mask + ST * L::MASKB);
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const uint32_t bw = (uint32_t)(bits >> (32 * kb + 4 * g));
+                sb[j >> 3][j & 7] = (bf16)(fast_exp2(sc[j]) * dp[j]);
+            if (__builtin_expect(partial, 0)) {  // wave-uniform and rare: clear dS where
+                asm volatile("");                   // the mask is 0 (a real branch)
+                // The row's mask word, addressed from the lane id afresh (the opaque
+                // copy keeps the address from being hoisted and held across the loop).
+                int lid = __lane_id();
+                asm volatile("" : "+v"(lid));
+                const int om = L::M0 + ((w & 3) * 32 + (lid & 31)) * 8;
+                const uint32_t bw = *reinterpret_cast<const uint32_t*>(
+                                        smem + om + ST * L::MASKB + 4 * kb) >> (4 * g);
 #pragma unroll
                 for (int j = 0; j < 16; ++j)
-                    if (!((bw >> (8 * (j >> 2) + (j & 3))) & 1u))
-                        sb[kb * 2 + (j >> 3)][j & 7] = (bf16)0.f;
+                    if (!((bw >> (8 * (j >> 2) + (j & 3))) & 1u)) sb[j >> 3][j & 7] = (bf16)0.f;
             }
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const int imm = ST * L::MAT + 16 * (2 * kb + k2) * L::ROWB;
+                    const bf16x8 a = cat(lds8_tr(smem, off.kt[db][0], imm),
+                                         lds8_tr(smem, off.kt[db][1], imm));
+                    dq[db] = mfma_32x32x16(a, sb[k2], dq[db]);
+                }
         }
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int imm = ST * L::MAT + 16 * kk * L::ROWB;
-                const bf16x8 a = cat(lds8_tr(smem, off.kt[db][0], imm),
-                                     lds8_tr(smem, off.kt[db][1], imm));
-                dq[db] = mfma_32x32x16(a, sb[kk], dq[db]);
-            }
     };
 
     if (n_it > 0) issue(ic<0>{}, 0);
