@@ -58,10 +58,18 @@ __device__ __forceinline__ T ld_const(const T* p) {
     return *p;
 #endif
 }
+// The HIP vector structs are loaded as plain vectors: a struct load is split into
+// scalar fields on the original (global) pointer, which would make it a vector-memory
+// load and so a wait on every outstanding copy.
 __device__ __forceinline__ int4 ld_const(const int4* p) {
     typedef __attribute__((ext_vector_type(4))) int i32x4;
     const i32x4 v = ld_const(reinterpret_cast<const i32x4*>(p));
     return make_int4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ int2 ld_const(const int2* p) {
+    typedef __attribute__((ext_vector_type(2))) int i32x2;
+    const i32x2 v = ld_const(reinterpret_cast<const i32x2*>(p));
+    return make_int2(v[0], v[1]);
 }
 
 // Make the compiler wait here for a register loaded from memory (so later loops do not
