@@ -143,6 +143,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void fwd_bf16_kernel(
             s[0] = mfma_32x32x16(lds16(smem, off.k[ks], ST * L::MAT), qf[ks], s[0]);
             s[1] = mfma_32x32x16(lds16(smem, off.k[ks], ST * L::MAT + 32 * L::ROWB), qf[ks], s[1]);
         }
+        lead_reads<2 * KS>();
         if (partial) {
             const uint64_t bits =
                 *reinterpret_cast<const uint64_t*>(smem + off_mask + ST * L::MASKB);
@@ -185,6 +186,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void fwd_bf16_kernel(
             for (int db = 0; db < DB; ++db)
                 o[db] = mfma_32x32x16(lds16(smem, ovx, ST * L::MAT + tile_t_imm<D>(kk, db)),
                                       pf[kk], o[db]);
+        lead_reads<4 * DB>();
     };
 
     if (n_it > 0) issue(ic<0>{}, 0);

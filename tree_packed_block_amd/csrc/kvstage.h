@@ -57,6 +57,21 @@ __host__ __device__ constexpr int tile_t_imm(int kk, int db) {
     return kk * 2 * D * 16 + db * 32 * 16;
 }
 
+// Order the N LDS reads and N MFMAs of one basic block so that the reads run AHEAD
+// operands in front of the MFMAs that consume them (left alone, the scheduler keeps
+// only two in flight and each MFMA pair waits out a full LDS latency).
+template <int N, int AHEAD = 6>
+__device__ __forceinline__ void lead_reads() {
+    constexpr int A = N < AHEAD ? N : AHEAD;
+    __builtin_amdgcn_sched_group_barrier(0x100, A, 0);  // DS reads
+#pragma unroll
+    for (int i = 0; i < N - A; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
+}
+
 // Copy K/V tile `kt` and the row masks of mask `m` into stage ST: 64 rows of K and V
 // (XOR-swizzled) and 1 KiB of mask words.  Every wave issues the same number of
 // copies: 2 * (64 * D * 2 / 16 / NTHR) + 1 per thread.
