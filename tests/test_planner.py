@@ -400,3 +400,16 @@ def test_positions_without_a_plan_match_the_oracle():
     with pytest.raises(tpb.OctopusError) as ei:
         tpb.dag_positions(br, np.array([[1, 0, 2, 0, 5], [2, 0, 1, 0, 5]]), 16)
     assert ei.value.name == "ECYCLE"
+
+
+def test_plan_upload_rejects_a_host_or_mistyped_buffer():
+    """The plan image goes to a caller-owned device buffer; a host tensor or one of
+    another element type is refused before any copy is issued."""
+    import torch
+    dag = synth.build("tiny")[0]
+    p = tpb.Plan(dag.branches, dag.mounts, dag.T)
+    n = p.device_bytes()
+    for buf in (torch.empty(n, dtype=torch.uint8), torch.empty(n, dtype=torch.float32)):
+        with pytest.raises(tpb.OctopusError):
+            p.upload(buffer=buf)
+    assert p.dev is None

@@ -223,6 +223,8 @@ class Plan:
         n = self.device_bytes()
         if buffer is None:
             buffer = torch.empty(n, dtype=torch.uint8, device=device)
+        if buffer.dtype != torch.uint8 or not buffer.is_cuda or not buffer.is_contiguous():
+            raise OctopusError(EINVAL, "plan buffer must be a contiguous uint8 device tensor")
         stream = stream or torch.cuda.current_stream(buffer.device)
         _check(lib().octopus_plan_upload(self._h, _vp(buffer.data_ptr()), buffer.numel(),
                                          _vp(stream.cuda_stream)))

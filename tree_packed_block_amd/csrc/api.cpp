@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <memory>
 #include <new>
 #include <string>
 #include <vector>
@@ -100,15 +101,12 @@ int octopus_dag_plan(const octopus_branch* branches, int32_t n_branches,
     if (out == nullptr) return fail(OCTOPUS_EINVAL, "out is NULL");
     *out = nullptr;
     try {
-        octopus_plan* h = new octopus_plan();
+        std::unique_ptr<octopus_plan> h(new octopus_plan());  // freed on every error path
         std::string err;
         const int rc = octo::build_plan(branches, n_branches, mounts, n_mounts, total_tokens,
                                         kv_tile, h->p, err);
-        if (rc != OCTOPUS_OK) {
-            delete h;
-            return fail(rc, err);
-        }
-        *out = h;
+        if (rc != OCTOPUS_OK) return fail(rc, err);
+        *out = h.release();
         return ok();
     } catch (const std::bad_alloc&) {
         return fail(OCTOPUS_ENOMEM, "host allocation failed while planning");
