@@ -413,3 +413,27 @@ def test_plan_upload_rejects_a_host_or_mistyped_buffer():
         with pytest.raises(tpb.OctopusError):
             p.upload(buffer=buf)
     assert p.dev is None
+
+
+def test_plan_at_the_token_limit():
+    """2^24 tokens (the planner's limit) as a forest of 4,096 causal trees of 4,096 tokens:
+    the plan is built in seconds (its cost follows the listed pairs, not query tiles x KV
+    tiles), with the closed-form counts: nnz = n L (L + 1) / 2, 2j + 2 KV tiles for query
+    tile j of a tree, two of them PARTIAL (the diagonal); one token more is refused."""
+    import time
+    n, L = 4096, 4096
+    br = np.array([[-1, 0, i * L, L] for i in range(n)], dtype=np.int32)
+    t0 = time.time()
+    p = tpb.Plan(br, np.zeros((0, 5), np.int32), n * L)
+    took = time.time() - t0
+    st = p.stats()
+    assert st["nnz"] == n * L * (L + 1) // 2
+    assert st["n_pairs"] == n * sum(2 * j + 2 for j in range(L // 128))
+    assert st["n_partial"] == n * 2 * (L // 128)
+    pos = p.positions()
+    assert np.array_equal(pos[:L], np.arange(L)) and np.array_equal(pos[-L:], np.arange(L))
+    assert took < 120, took
+    del p
+    with pytest.raises(tpb.OctopusError):
+        tpb.Plan(np.array([[-1, 0, 0, n * L + 1]], np.int32), np.zeros((0, 5), np.int32),
+                 n * L + 1)

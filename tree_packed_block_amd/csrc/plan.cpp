@@ -270,7 +270,12 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
 
     std::vector<std::vector<Interval>> rows(Bq);
     std::vector<Interval> scratch;
-    std::vector<int32_t> full_diff(nKT + 1), touch_diff(nKT + 1);
+    // Difference arrays over KV tiles, cleared entry by entry after each query tile; only
+    // the tile ranges some row touches are swept, so planning costs O(rows x intervals +
+    // listed pairs) rather than O(query tiles x KV tiles) (a forest of many trees would
+    // otherwise sweep every tile of every tree for every query tile).
+    std::vector<int32_t> full_diff(nKT + 1, 0), touch_diff(nKT + 1, 0);
+    std::vector<std::pair<int64_t, int64_t>> spans;  // touched tile ranges [t0, t1)
     std::vector<size_t> cursor(Bq);
     p.qt_ptr.assign(nQT + 1, 0);
     p.q_pairs.clear();
@@ -281,8 +286,7 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     for (int32_t qt = 0; qt < nQT; ++qt) {
         const int32_t r0 = qt * Bq;
         const int32_t nv = std::min(Bq, T - r0);
-        std::fill(full_diff.begin(), full_diff.end(), 0);
-        std::fill(touch_diff.begin(), touch_diff.end(), 0);
+        spans.clear();
         for (int32_t rr = 0; rr < nv; ++rr) {
             const int32_t i = r0 + rr;
             const int32_t b = row_branch[i];
@@ -292,6 +296,7 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
                 const int64_t t0 = iv.lo / Bk, t1 = (iv.hi + Bk - 1) / Bk;
                 touch_diff[t0] += 1;
                 touch_diff[t1] -= 1;
+                spans.push_back({t0, t1});
                 const int64_t f0 = (iv.lo + Bk - 1) / Bk, f1 = iv.hi / Bk;
                 if (f0 < f1) {
                     full_diff[f0] += 1;
@@ -300,33 +305,54 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
             }
             cursor[rr] = 0;
         }
-        int32_t touch = 0, full = 0;
-        for (int32_t t = 0; t < nKT; ++t) {
-            touch += touch_diff[t];
-            full += full_diff[t];
-            if (touch == 0) continue;
-            if (full == nv) {
-                p.q_pairs.push_back({t, -1});
-                continue;
-            }
-            // PARTIAL: per-row bits of keys [t*Bk, t*Bk + Bk) that the row sees.
-            const int64_t k0 = (int64_t)t * Bk, k1 = k0 + Bk;
-            std::fill(words.begin(), words.end(), 0);
-            for (int32_t rr = 0; rr < nv; ++rr) {
-                const auto& iv = rows[rr];
-                size_t c = cursor[rr];
-                while (c < iv.size() && iv[c].hi <= k0) ++c;
-                cursor[rr] = c;
-                for (size_t j = c; j < iv.size() && iv[j].lo < k1; ++j) {
-                    const int64_t a = std::max(iv[j].lo, k0) - k0;
-                    const int64_t e = std::min(iv[j].hi, k1) - k0;
-                    for (int64_t x = a; x < e; ++x)
-                        words[rr * p.row_words + (x >> 6)] |= 1ull << (x & 63);
+        // Merge the touched ranges; every interval starts and ends inside one merged
+        // range, so the running sums are 0 at the start of each.
+        std::sort(spans.begin(), spans.end());
+        size_t n_sp = 0;
+        for (size_t j = 0; j < spans.size(); ++j) {
+            if (n_sp > 0 && spans[j].first <= spans[n_sp - 1].second)
+                spans[n_sp - 1].second = std::max(spans[n_sp - 1].second, spans[j].second);
+            else
+                spans[n_sp++] = spans[j];
+        }
+        for (size_t sp = 0; sp < n_sp; ++sp) {
+            int32_t touch = 0, full = 0;
+            for (int32_t t = (int32_t)spans[sp].first; t < (int32_t)spans[sp].second; ++t) {
+                touch += touch_diff[t];
+                full += full_diff[t];
+                if (touch == 0) continue;
+                if (full == nv) {
+                    p.q_pairs.push_back({t, -1});
+                    continue;
                 }
+                // PARTIAL: per-row bits of keys [t*Bk, t*Bk + Bk) that the row sees.
+                const int64_t k0 = (int64_t)t * Bk, k1 = k0 + Bk;
+                std::fill(words.begin(), words.end(), 0);
+                for (int32_t rr = 0; rr < nv; ++rr) {
+                    const auto& iv = rows[rr];
+                    size_t c = cursor[rr];
+                    while (c < iv.size() && iv[c].hi <= k0) ++c;
+                    cursor[rr] = c;
+                    for (size_t j = c; j < iv.size() && iv[j].lo < k1; ++j) {
+                        const int64_t a = std::max(iv[j].lo, k0) - k0;
+                        const int64_t e = std::min(iv[j].hi, k1) - k0;
+                        for (int64_t x = a; x < e; ++x)
+                            words[rr * p.row_words + (x >> 6)] |= 1ull << (x & 63);
+                    }
+                }
+                const int32_t idx = (int32_t)(p.mask_rows.size() / (Bq * p.row_words));
+                p.mask_rows.insert(p.mask_rows.end(), words.begin(), words.end());
+                p.q_pairs.push_back({t, idx});
             }
-            const int32_t idx = (int32_t)(p.mask_rows.size() / (Bq * p.row_words));
-            p.mask_rows.insert(p.mask_rows.end(), words.begin(), words.end());
-            p.q_pairs.push_back({t, idx});
+        }
+        // Clear the entries this query tile set.
+        for (int32_t rr = 0; rr < nv; ++rr) {
+            for (const Interval& iv : rows[rr]) {
+                touch_diff[iv.lo / Bk] = 0;
+                touch_diff[(iv.hi + Bk - 1) / Bk] = 0;
+                full_diff[(iv.lo + Bk - 1) / Bk] = 0;
+                full_diff[iv.hi / Bk] = 0;
+            }
         }
         p.qt_ptr[qt + 1] = (int32_t)p.q_pairs.size();
     }
