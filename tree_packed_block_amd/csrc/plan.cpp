@@ -15,6 +15,30 @@ std::string row_msg(const char* what, long long idx, const char* detail) {
     return std::string(what) + " " + std::to_string(idx) + ": " + detail;
 }
 
+// Set bits [a, e) of a little-endian bit string held in 64-bit words.
+void set_bits(uint64_t* w, int64_t a, int64_t e) {
+    while (a < e) {
+        const int64_t wi = a >> 6, b0 = a & 63;
+        const int64_t b1 = std::min<int64_t>(64, b0 + (e - a));
+        const uint64_t hi = b1 == 64 ? ~0ull : ((1ull << b1) - 1);
+        w[wi] |= hi & ~((1ull << b0) - 1);
+        a += b1 - b0;
+    }
+}
+
+// In place: word c gets bit r = bit c of word r (a 64 x 64 bit matrix, bit c of word r
+// being entry (r, c)), by swapping ever smaller off-diagonal blocks.
+void transpose64(uint64_t a[64]) {
+    uint64_t m = 0x00000000FFFFFFFFull;
+    for (int j = 32; j != 0; j >>= 1, m ^= (m << j)) {
+        for (int k = 0; k < 64; k = ((k | j) + 1) & ~j) {
+            const uint64_t t = ((a[k] >> j) ^ a[k | j]) & m;
+            a[k] ^= t << j;
+            a[k | j] ^= t;
+        }
+    }
+}
+
 // Sort and merge intervals in place (adjacent ones are joined).
 void merge(std::vector<Interval>& v) {
     if (v.empty()) return;
@@ -336,8 +360,7 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
                     for (size_t j = c; j < iv.size() && iv[j].lo < k1; ++j) {
                         const int64_t a = std::max(iv[j].lo, k0) - k0;
                         const int64_t e = std::min(iv[j].hi, k1) - k0;
-                        for (int64_t x = a; x < e; ++x)
-                            words[rr * p.row_words + (x >> 6)] |= 1ull << (x & 63);
+                        set_bits(&words[rr * p.row_words], a, e);
                     }
                 }
                 const int32_t idx = (int32_t)(p.mask_rows.size() / (Bq * p.row_words));
@@ -370,6 +393,15 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     for (int64_t m = 0; m < p.n_partial; ++m) {
         const uint64_t* wr = &p.mask_rows[m * Bq * p.row_words];
         uint64_t* wc = &p.mask_cols[m * Bk * p.col_words];
+        if (Bk == 64) {  // one word per row: transpose 64-row blocks as bit matrices
+            for (int32_t hf = 0; hf < Bq / 64; ++hf) {
+                uint64_t blk[64];
+                std::copy(wr + 64 * hf, wr + 64 * hf + 64, blk);
+                transpose64(blk);
+                for (int32_t kk = 0; kk < 64; ++kk) wc[kk * p.col_words + hf] = blk[kk];
+            }
+            continue;
+        }
         for (int32_t rr = 0; rr < Bq; ++rr)
             for (int32_t kk = 0; kk < Bk; ++kk)
                 if ((wr[rr * p.row_words + (kk >> 6)] >> (kk & 63)) & 1)
