@@ -300,6 +300,7 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     // otherwise sweep every tile of every tree for every query tile).
     std::vector<int32_t> full_diff(nKT + 1, 0), touch_diff(nKT + 1, 0);
     std::vector<std::pair<int64_t, int64_t>> spans;  // touched tile ranges [t0, t1)
+    std::vector<std::pair<int64_t, int64_t>> row_sp, prev_sp;  // one row's ranges
     std::vector<size_t> cursor(Bq);
     p.qt_ptr.assign(nQT + 1, 0);
     p.q_pairs.clear();
@@ -311,16 +312,44 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
         const int32_t r0 = qt * Bq;
         const int32_t nv = std::min(Bq, T - r0);
         spans.clear();
+        prev_sp.clear();
         for (int32_t rr = 0; rr < nv; ++rr) {
             const int32_t i = r0 + rr;
             const int32_t b = row_branch[i];
-            d.row_context(b, i - d.br[b].start, rows[rr], scratch);
+            const int32_t r = i - d.br[b].start;
+            // Ctx(b, r) = Ctx(b, r - 1) + the own token i (never already in it: a branch
+            // does not mount itself) + the spans mounted at rpos = r.  Without such a
+            // mount the previous row's intervals are copied and the one ending at i
+            // grows by one key (joining the next interval if that starts at i + 1).
+            bool inc = rr > 0 && r > 0 && row_branch[i - 1] == b;
+            if (inc)
+                for (int32_t id : d.mounts_of[b])
+                    if (d.mt[id].rpos == r) { inc = false; break; }
+            if (inc) {
+                std::vector<Interval>& cur = rows[rr];
+                cur = rows[rr - 1];
+                for (size_t j = 0; j < cur.size(); ++j) {
+                    if (cur[j].hi != i) continue;
+                    cur[j].hi = (int64_t)i + 1;
+                    if (j + 1 < cur.size() && cur[j + 1].lo == (int64_t)i + 1) {
+                        cur[j].hi = cur[j + 1].hi;
+                        cur.erase(cur.begin() + (j + 1));
+                    }
+                    break;
+                }
+            } else {
+                d.row_context(b, r, rows[rr], scratch);
+            }
+            row_sp.clear();
             for (const Interval& iv : rows[rr]) {
                 p.nnz += iv.hi - iv.lo;
                 const int64_t t0 = iv.lo / Bk, t1 = (iv.hi + Bk - 1) / Bk;
                 touch_diff[t0] += 1;
                 touch_diff[t1] -= 1;
-                spans.push_back({t0, t1});
+                // Neighbouring rows mostly repeat their ranges; keep each range once.
+                row_sp.push_back({t0, t1});
+                if (std::find(prev_sp.begin(), prev_sp.end(), row_sp.back()) == prev_sp.end())
+                    spans.push_back({t0, t1});
                 const int64_t f0 = (iv.lo + Bk - 1) / Bk, f1 = iv.hi / Bk;
                 if (f0 < f1) {
                     full_diff[f0] += 1;
@@ -328,6 +357,7 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
                 }
             }
             cursor[rr] = 0;
+            prev_sp.swap(row_sp);
         }
         // Merge the touched ranges; every interval starts and ends inside one merged
         // range, so the running sums are 0 at the start of each.
