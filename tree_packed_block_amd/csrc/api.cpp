@@ -404,7 +404,8 @@ int octopus_decode_segments(const octopus_branch* branches, int32_t n_branches,
         if (T < 1 || T > octo::kMaxTokens) return fail(OCTOPUS_EINVAL, "total tokens out of range");
         octo::DagInfo dag;
         std::string err;
-        int rc = octo::load_dag(branches, n_branches, mounts, n_mounts, (int32_t)T, dag, err);
+        int rc = octo::load_dag(branches, n_branches, mounts, n_mounts, (int32_t)T, dag, err,
+                                false);
         if (rc != OCTOPUS_OK) return fail(rc, err);
         std::vector<int32_t> sp, pg, lo, hi, gp, gc;
         rc = octo::build_segments(dag, page_ptr, pages, page_size, n_pages, cursors, n_cursors,
@@ -515,7 +516,8 @@ int octopus_extend_segments(const octopus_branch* branches, int32_t n_branches,
         if (T < 1 || T > octo::kMaxTokens) return fail(OCTOPUS_EINVAL, "total tokens out of range");
         octo::DagInfo dag;
         std::string err;
-        int rc = octo::load_dag(branches, n_branches, mounts, n_mounts, (int32_t)T, dag, err);
+        int rc = octo::load_dag(branches, n_branches, mounts, n_mounts, (int32_t)T, dag, err,
+                                false);
         if (rc != OCTOPUS_OK) return fail(rc, err);
         std::vector<int32_t> sp, pg, lo, hi, th, ca, fo;
         rc = octo::build_extend_segments(dag, page_ptr, pages, page_size, n_pages, cursors,

@@ -132,10 +132,25 @@ int validate(const octopus_branch* br, int32_t nb, const octopus_mount* mt, int3
 
 // Positions by an explicit worklist over (branch, offset) requests.  A branch is
 // "open" while it sits on the stack; asking an open branch for an offset it has
-// not reached yet is a dependency cycle.
-int compute_positions(DagInfo& d, std::string& err) {
+// not reached yet is a dependency cycle.  Along a branch a position only moves by
+// one per token except at a mount offset, so each branch's positions are kept as runs
+// (first offset, its position) and computed run by run: the cost follows the branches
+// and mounts, not the tokens (the dense positions are written only when asked for).
+int compute_positions(DagInfo& d, bool fill, std::string& err) {
     const int32_t nb = (int32_t)d.br.size();
-    std::vector<std::vector<int64_t>> xs(nb);
+    struct Run { int32_t k; int64_t v; };
+    std::vector<std::vector<Run>> runs(nb);
+    std::vector<int32_t> done(nb, 0);  // offsets 0 .. done - 1 are known
+    // Position of branch b's offset k (k < done[b]).
+    auto at = [&](int32_t b, int32_t k) -> int64_t {
+        const std::vector<Run>& rs = runs[b];
+        size_t lo = 0, hi = rs.size();
+        while (hi - lo > 1) {
+            const size_t mid = (lo + hi) / 2;
+            if (rs[mid].k <= k) lo = mid; else hi = mid;
+        }
+        return rs[lo].v + (k - rs[lo].k);
+    };
     std::vector<size_t> next_mount(nb, 0);
     std::vector<char> open(nb, 0);
     struct Req { int32_t b, r; };
@@ -147,23 +162,23 @@ int compute_positions(DagInfo& d, std::string& err) {
         while (!stack.empty()) {
             Req& top = stack.back();
             const int32_t b = top.b;
-            if ((int64_t)xs[b].size() > top.r) {
+            if (done[b] > top.r) {
                 open[b] = 0;
                 stack.pop_back();
                 continue;
             }
-            const int32_t k = (int32_t)xs[b].size();
+            const int32_t k = done[b];
             const octopus_branch& B = d.br[b];
             // Dependencies of x_b(k): the parent's position at the fork (k = 0), and the
             // last mounted key of every mount issued at offset k.
             Req need{-1, -1};
-            if (k == 0 && B.parent >= 0 && (int64_t)xs[B.parent].size() <= B.fork) {
+            if (k == 0 && B.parent >= 0 && done[B.parent] <= B.fork) {
                 need = {B.parent, B.fork};
             } else {
                 const auto& ms = d.mounts_of[b];
                 for (size_t i = next_mount[b]; i < ms.size() && d.mt[ms[i]].rpos == k; ++i) {
                     const octopus_mount& m = d.mt[ms[i]];
-                    if ((int64_t)xs[m.producer].size() <= m.e - 1) {
+                    if (done[m.producer] <= m.e - 1) {
                         need = {m.producer, m.e - 1};
                         break;
                     }
@@ -179,25 +194,34 @@ int compute_positions(DagInfo& d, std::string& err) {
                 stack.push_back(need);
                 continue;
             }
-            int64_t v = (k == 0) ? (B.parent < 0 ? 0 : xs[B.parent][B.fork]) : xs[b][k - 1] + 1;
+            int64_t v = (k == 0) ? (B.parent < 0 ? 0 : at(B.parent, B.fork)) : at(b, k - 1) + 1;
             const auto& ms = d.mounts_of[b];
             while (next_mount[b] < ms.size() && d.mt[ms[next_mount[b]]].rpos == k) {
                 const octopus_mount& m = d.mt[ms[next_mount[b]]];
                 // e_A = position of the last mounted key + 1; next = max(p_B, e_A + 1).
-                v = std::max(v, xs[m.producer][m.e - 1] + 2);
+                v = std::max(v, at(m.producer, m.e - 1) + 2);
                 ++next_mount[b];
             }
-            xs[b].push_back(v);
+            if (k == 0 || v != at(b, k - 1) + 1) runs[b].push_back({k, v});
+            // Up to the branch's next mount offset nothing else moves a position: the
+            // run continues by one per token (and depends on nothing).
+            done[b] = (next_mount[b] < ms.size() ? d.mt[ms[next_mount[b]]].rpos - 1 : B.len) + 1;
         }
     }
+    for (int32_t b = 0; b < nb; ++b) {  // positions increase along a branch
+        if (d.br[b].len > 0 && at(b, d.br[b].len - 1) > INT32_MAX) {
+            err = "position exceeds int32";
+            return OCTOPUS_EINVAL;
+        }
+    }
+    if (!fill) return OCTOPUS_OK;
     d.pos.assign(d.T, 0);
     for (int32_t b = 0; b < nb; ++b) {
-        for (int32_t r = 0; r < d.br[b].len; ++r) {
-            if (xs[b][r] > INT32_MAX) {
-                err = "position exceeds int32";
-                return OCTOPUS_EINVAL;
-            }
-            d.pos[d.br[b].start + r] = xs[b][r];
+        const std::vector<Run>& rs = runs[b];
+        for (size_t j = 0; j < rs.size(); ++j) {
+            const int32_t k1 = j + 1 < rs.size() ? rs[j + 1].k : d.br[b].len;
+            for (int32_t k = rs[j].k; k < std::min(k1, d.br[b].len); ++k)
+                d.pos[(size_t)d.br[b].start + k] = rs[j].v + (k - rs[j].k);
         }
     }
     return OCTOPUS_OK;
@@ -231,7 +255,7 @@ int32_t DagInfo::owner(int64_t j) const {
 }
 
 int load_dag(const octopus_branch* br, int32_t nb, const octopus_mount* mt, int32_t nm,
-             int32_t T, DagInfo& d, std::string& err) {
+             int32_t T, DagInfo& d, std::string& err, bool with_positions) {
     int rc = validate(br, nb, mt, nm, T, err);
     if (rc != OCTOPUS_OK) return rc;
     d.T = T;
@@ -266,7 +290,7 @@ int load_dag(const octopus_branch* br, int32_t nb, const octopus_mount* mt, int3
     std::iota(d.order_by_start.begin(), d.order_by_start.end(), 0);
     std::sort(d.order_by_start.begin(), d.order_by_start.end(),
               [&](int a, int b) { return d.br[a].start < d.br[b].start; });
-    return compute_positions(d, err);
+    return compute_positions(d, with_positions, err);
 }
 
 int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, int32_t nm,

@@ -49,9 +49,11 @@ struct DagInfo {
     int32_t owner(int64_t j) const;
 };
 
-// Returns OCTOPUS_OK or an error code with `err` set.
+// Returns OCTOPUS_OK or an error code with `err` set.  Positions are always computed
+// (their dependency cycles are errors); with_positions = false leaves `pos` empty for
+// callers that need only visibility (the decode and extend segment builders).
 int load_dag(const octopus_branch* br, int32_t nb, const octopus_mount* mt, int32_t nm,
-             int32_t T, DagInfo& out, std::string& err);
+             int32_t T, DagInfo& out, std::string& err, bool with_positions = true);
 
 // One entry of a 128-key block's list: a query tile and, for each of the block's two
 // 64-key tiles, -1 (FULL), -2 (the tile is not seen by this query tile) or the
