@@ -192,6 +192,8 @@ def main():
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="episode262k",
                     help="the packed stream of the fwd+bwd part of the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cache-resident", action="store_true",
+                    help="skip the cache-resident decode leg (for profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (reference for HBM counters)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -440,36 +442,42 @@ def main():
     # pool of 2,048 pages, so that all K/V (256 MiB) can stay in the 256 MB MALL.  This is
     # a cache-resident timing, not an HBM measurement (the headline decode uses a pool
     # that holds every branch's own pages).
-    n_small = 2048
+    # Skipped in profiling runs (--calibrate-copy, --no-cache-resident), whose per-kernel
+    # figures would otherwise average this leg's decode launches with the HBM ones.
+    n_small = 0 if args.calibrate_copy or args.no_cache_resident else 2048
     rng_c = np.random.default_rng(56)
-    pages_c = rng_c.integers(0, n_small, size=len(wl.pages)).astype(np.int32)
-    segs_c = tpb.decode_segments(wl.dag.branches, wl.dag.mounts, wl.page_ptr, pages_c,
-                                 wl.page_size, n_small, wl.cursors, share=True)
-    sd_c = [torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev) for a in segs_c]
-    kc = (torch.randn((n_small, HKV, wl.page_size, HD), device=dev) * 0.5).to(torch.bfloat16)
-    vc = (torch.randn((n_small, HKV, wl.page_size, HD), device=dev) * 0.5).to(torch.bfloat16)
-    slots_c = int((segs_c[3] - segs_c[2]).astype(np.int64).sum())
+    if n_small:
+        pages_c = rng_c.integers(0, n_small, size=len(wl.pages)).astype(np.int32)
+        segs_c = tpb.decode_segments(wl.dag.branches, wl.dag.mounts, wl.page_ptr, pages_c,
+                                     wl.page_size, n_small, wl.cursors, share=True)
+        sd_c = [torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+                for a in segs_c]
+        shape_c = (n_small, HKV, wl.page_size, HD)
+        kc = (torch.randn(shape_c, device=dev) * 0.5).to(torch.bfloat16)
+        vc = (torch.randn(shape_c, device=dev) * 0.5).to(torch.bfloat16)
+        slots_c = int((segs_c[3] - segs_c[2]).astype(np.int64).sum())
 
-    def run_dec_c():
-        tpb.paged_mount_decode(qd, kc, vc, *sd_c, n_split=args.n_split, o=od, lse=lsed, ws=wsd)
+        def run_dec_c():
+            tpb.paged_mount_decode(qd, kc, vc, *sd_c, n_split=args.n_split, o=od, lse=lsed,
+                                   ws=wsd)
 
-    for _ in range(3):
-        run_dec_c()
-    ev_c = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
-    ev_c[0].record(stream)
-    for j in range(20):
-        run_dec_c()
-        ev_c[j + 1].record(stream)
-    torch.cuda.synchronize()
-    ms_c = float(np.median([ev_c[j].elapsed_time(ev_c[j + 1]) for j in range(20)]))
-    bytes_c = slots_c * HKV * HD * 2 * 2
-    out["breakdown"]["decode_cache_resident"] = {
-        "ms": round(ms_c, 3), "streamed_GB/s": round(bytes_c / (ms_c * 1e-3) / 1e9, 1),
-        "note": "same 64 cursors and segments over a 2,048-page (131,072-token) pool, pages "
-                "drawn with replacement: K/V fit in the MALL; streamed bytes = K and V of every "
-                "listed slot, each list counted once (a shared list is read once per block of "
-                "8 cursors); not an HBM figure"}
-    del kc, vc
+        for _ in range(3):
+            run_dec_c()
+        ev_c = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
+        ev_c[0].record(stream)
+        for j in range(20):
+            run_dec_c()
+            ev_c[j + 1].record(stream)
+        torch.cuda.synchronize()
+        ms_c = float(np.median([ev_c[j].elapsed_time(ev_c[j + 1]) for j in range(20)]))
+        bytes_c = slots_c * HKV * HD * 2 * 2
+        out["breakdown"]["decode_cache_resident"] = {
+            "ms": round(ms_c, 3), "streamed_GB/s": round(bytes_c / (ms_c * 1e-3) / 1e9, 1),
+            "note": "same 64 cursors and segments over a 2,048-page (131,072-token) pool, "
+                    "pages drawn with replacement: K/V fit in the MALL; streamed bytes = K and "
+                    "V of every listed slot, each list counted once (a shared list is read "
+                    "once per block of 8 cursors); not an HBM figure"}
+        del kc, vc
 
     # The RoPE pass of the RoPE entry points, on its own clock: Q and K turned at the
     # plan's positions in one launch (the forward runs it once, the backward once more
