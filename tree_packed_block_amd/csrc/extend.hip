@@ -175,6 +175,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void extend_bf16_kernel(
             s[0] = mfma_32x32x16(lds16(smem, ok_[ks], ST * L::MAT), qf[ks], s[0]);
             s[1] = mfma_32x32x16(lds16(smem, ok_[ks], ST * L::MAT + 32 * ROWB), qf[ks], s[1]);
         }
+        lead_reads<2 * KS>();
         // Every new token of the tile sees the whole page unless it is partial or its
         // threshold reaches past the tile's first token.
         const bool whole = ok && lo == 0 && hi == kSlots && r_min >= thr + (causal ? kSlots - 1 : 0);
@@ -221,6 +222,14 @@ __global__ __launch_bounds__(256 * HPW, 1) void extend_bf16_kernel(
                                       lds8_tr(smem, ov_[db][1], ST * L::MAT + 16 * kk * ROWB));
                 o[db] = mfma_32x32x16(va, pf[kk], o[db]);
             }
+        // Two transposed reads per MFMA operand: keep six operands' reads ahead.
+        __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+        for (int i = 0; i < 4 * DB - 6; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
     };
 
     if (n_it > 0) issue(ic<0>{}, 0);
