@@ -283,12 +283,30 @@ def main():
                                    wl.page_size, wl.n_pages, wl.cursors, share=True)
         return plan, segs
 
-    def enqueue(i, plan, segs, ev):
-        plan.upload(buffer=plan_bufs[i % 2], sync=False, stream=stream)
+    # Uploads of a step's plan and segments run on a copy stream of their own (default
+    # priority), issued as soon as the host has built them, i.e. while the previous step's
+    # kernels run; the step's first kernel waits for them, and a buffer pair is reused
+    # only after the step that last read it has finished.
+    copy_stream = torch.cuda.Stream(device=dev)
+    up_done = [torch.cuda.Event() for _ in range(2)]
+    bufs_free = [torch.cuda.Event() for _ in range(2)]
+    for e in bufs_free:
+        e.record(stream)
+
+    def stage(i, plan, segs):
+        up_done[i % 2].synchronize()  # the host staging buffers' previous copies are done
+        copy_stream.wait_event(bufs_free[i % 2])
+        plan.upload(buffer=plan_bufs[i % 2], sync=False, stream=copy_stream)
         hs, ds = seg_host[i % 2], seg_dev[i % 2]
-        for h, d, a in zip(hs, ds, segs):
-            h.numpy()[:] = a
-            d.copy_(h, non_blocking=True)
+        with torch.cuda.stream(copy_stream):
+            for h, d, a in zip(hs, ds, segs):
+                h.numpy()[:] = a
+                d.copy_(h, non_blocking=True)
+        up_done[i % 2].record(copy_stream)
+
+    def enqueue(i, plan, segs, ev):
+        ds = seg_dev[i % 2]
+        stream.wait_event(up_done[i % 2])
         ev[0].record(stream)
         tpb.attn_fwd(plan, q, k, v, o=o, lse=lse, ws=wsf)
         ev[1].record(stream)
@@ -300,21 +318,22 @@ def main():
         ev[4].record(stream)
         tpb.paged_mount_decode(qd, kp, vp, *ds, n_split=args.n_split, o=od, lse=lsed, ws=wsd)
         ev[5].record(stream)
+        bufs_free[i % 2].record(stream)
 
     def run(n_steps, first):
         """Enqueue n_steps steps; `first` is the host work of the first one, done while
         the previous GPU work ran (as every later step's is, inside this loop)."""
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_steps)]
         keep = []
-        nxt = first
+        plan, segs = first
+        keep.append(plan)
+        stage(0, plan, segs)
         for i in range(n_steps):
-            if i >= 2:
-                evs[i - 2][5].synchronize()  # buffers of step i-2 are free again
-            plan, segs = nxt
-            keep.append(plan)
-            enqueue(i, plan, segs, evs[i])
+            enqueue(i, keep[i], segs, evs[i])
             if i + 1 < n_steps:
-                nxt = host_prep()  # overlaps the GPU work just enqueued
+                plan, segs = host_prep()  # overlaps the GPU work just enqueued
+                keep.append(plan)
+                stage(i + 1, plan, segs)
         return evs, keep
 
     for _ in range(max(args.warmup, 0)):
