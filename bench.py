@@ -59,9 +59,13 @@ def log(*a):
 
 
 def source_digest() -> str:
-    """Digest of the device code: the HIP kernel sources and the headers they include
-    (host planning and argument checking are left out)."""
+    """Digest of the device code: the HIP kernel sources, the headers they include and
+    the options they are compiled with (host planning and argument checking are left
+    out)."""
+    from tree_packed_block_amd import build as _b
+
     h = hashlib.sha256()
+    h.update(json.dumps([_b.HIPCC_FLAGS, sorted(_b.HIP_FILE_FLAGS.items())]).encode())
     csrc = os.path.join(ROOT, "tree_packed_block_amd", "csrc")
     device = [n for n in os.listdir(csrc)
               if n.endswith(".hip") or n in ("device_common.h", "kvstage.h", "kernels.h")]
