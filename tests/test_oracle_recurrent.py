@@ -1,7 +1,9 @@
-"""Pins of the recurrent-scan oracle: every branch equals the plain recurrence run from
-zero over its flattened root-to-branch token path (an independent formulation of the
-fork checkpoints), the delta rule stores and retrieves values under orthonormal keys,
-beta = 0 keeps the inherited state, alpha gates it, and mounts change nothing."""
+"""Pins of the recurrent-scan oracle: hand-derived outputs of one and two tokens with
+gates strictly between 0 and 1 (which fix where alpha and beta enter the update), every
+branch equals the plain recurrence run from zero over its flattened root-to-branch token
+path (an independent formulation of the fork checkpoints), the delta rule stores and
+retrieves values under orthonormal keys, beta = 0 keeps the inherited state, alpha gates
+it, and mounts change nothing."""
 
 import numpy as np
 
@@ -31,6 +33,41 @@ def _plain(q, k, v, a, b):
                 + b[t, h] * np.outer(v[t, h], k[t, h])
             o[t, h] = S @ q[t, h]
     return o
+
+
+def _two_tokens(k1, k2, v1, v2, q1, q2, a1, a2, b1, b2):
+    T = 2
+    q = np.array([q1, q2], dtype=np.float64).reshape(T, 1, -1)
+    k = np.array([k1, k2], dtype=np.float64).reshape(T, 1, -1)
+    v = np.array([v1, v2], dtype=np.float64).reshape(T, 1, -1)
+    a = np.array([[a1], [a2]], dtype=np.float64)
+    b = np.array([[b1], [b2]], dtype=np.float64)
+    o, _ = RC.scan(q, k, v, a, b, np.array([[-1, 0, 0, T]]))
+    return o[:, 0]
+
+
+def test_gated_delta_rule_hand_derived():
+    """Worked by hand from S_t = a_t (S_{t-1} - b_t (S_{t-1} k_t) k_t^T) + b_t v_t k_t^T,
+    o_t = S_t q_t, from S_0 = 0, with unit keys k1 = (0.6, 0.8).
+
+    One token: S_1 = b1 v1 k1^T whatever a1 is, so o_1 = b1 (k1.q1) v1
+      = 0.5 * 2.2 * (2, -1) = (2.2, -1.1) for q1 = (1, 2).
+    Second key orthogonal, k2 = (-0.8, 0.6): S_1 k2 = 0, so
+      o_2 = a2 b1 (k1.q2) v1 + b2 (k2.q2) v2 = 0.5*0.5*1.4*(2, -1) + 0.25*(-0.2)*(1, 3)
+          = (0.65, -0.5) for q2 = (1, 1).
+      (The gate on the write term instead would give (1.375, -0.775).)
+    Same key twice, k2 = k1: S_1 k1 = b1 v1, so S_2 = (a2 b1 (1 - b2) v1 + b2 v2) k1^T and
+      o_2 = 1.4 * (0.1875*(2, -1) + 0.25*(1, 3)) = (0.875, 0.7875).
+      (The erase term outside the gate, a2 S_1 - b2 (S_1 k2) k2^T + ..., would give
+      (0.7, 0.875).)"""
+    k1, k2o = (0.6, 0.8), (-0.8, 0.6)
+    v1, v2 = (2.0, -1.0), (1.0, 3.0)
+    o = _two_tokens(k1, k2o, v1, v2, (1.0, 2.0), (1.0, 1.0), 0.3, 0.5, 0.5, 0.25)
+    np.testing.assert_allclose(o[0], [2.2, -1.1], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(o[1], [0.65, -0.5], rtol=0, atol=1e-14)
+    o = _two_tokens(k1, k1, v1, v2, (1.0, 2.0), (1.0, 1.0), 0.9, 0.5, 0.5, 0.25)
+    np.testing.assert_allclose(o[0], [2.2, -1.1], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(o[1], [0.875, 0.7875], rtol=0, atol=1e-14)
 
 
 def test_branches_equal_flattened_paths():

@@ -1,13 +1,30 @@
-"""Pins of the RoPE oracle: agreement with the input generator's independent rotation,
-orthogonality and inversion, the relative-position property, identity at position 0,
-and central finite differences of the loss through the rotation."""
+"""Pins of the RoPE oracle: hand-derived rotations of a 4-dimensional head at base 10000
+(the frequency schedule and the rotate-half pairing, fixed by a golden file), agreement
+with the input generator's independent rotation, orthogonality and inversion, the
+relative-position property, identity at position 0, and central finite differences of
+the loss through the rotation."""
 
 import numpy as np
+
+from conftest import read_golden
 
 import synth
 from oracle import attention as A
 from oracle import dag as D
 from oracle import rope as R
+
+
+def test_rotate_hand_derived_golden():
+    """Unit vectors of a D = 4 head at positions 1, 7 and 100: frequencies 1 and 1/100,
+    pairs (x0, x2) and (x1, x3).  A wrong frequency exponent, an interleaved pairing or
+    a flipped sine fails here."""
+    vals = np.array(read_golden("rope_d4_base10000.txt"), dtype=np.float64).reshape(-1, 9)
+    pos = vals[:, 0].astype(np.int64)
+    x = vals[:, 1:5].reshape(-1, 1, 4)
+    want = vals[:, 5:9].reshape(-1, 1, 4)
+    np.testing.assert_allclose(R.rotate(x, pos, base=10000.0), want, rtol=0, atol=1e-15)
+    back = R.rotate(want, pos, base=10000.0, inverse=True)
+    np.testing.assert_allclose(back, x, rtol=0, atol=1e-15)
 
 
 def test_rotate_matches_generator_rotation():
