@@ -125,7 +125,9 @@ def test_bwd_full_size_sampled(name):
     """The full tree through the benchmark's launches.  The oracle computes dQ on
     sampled query rows, and dK/dV of sampled keys from every query that sees them
     (so mounted keys include their readers' gradients); whole-tensor identities
-    check every row: sum_j dV_j = sum of dO over the group's heads, sum_j dK_j = 0."""
+    check every row: sum_j dV_j = sum of dO over the group's heads, sum_j dK_j = 0.
+    For the single trees, KV head 0 is also checked over every key and row (the shared
+    prefix included)."""
     say(f"case bwd {name} sampled")
     dag, x = workload(name, 16, 4, 128, "bf16", 0.5, with_dout=True)
     o, lse, dq, dk, dv = _run(dag, x, "bf16")
@@ -153,6 +155,34 @@ def test_bwd_full_size_sampled(name):
     dk_mag = np.abs(dk).sum(axis=0).max()
     say(f"  |sum dK| / sum |dK| = {dk_sum / dk_mag:.3e}")
     assert dk_sum <= GRAD_TOL * dk_mag
+    if name != "forest1m":
+        _check_head_group0(dag, x, dq, dk, dv)
+
+
+def _check_head_group0(dag, x, dq, dk, dv):
+    """Whole-tensor parity for KV head 0 at full size.  Heads are independent, so the
+    oracle over every query row of the first group (query heads 0..G-1, KV head 0) gives
+    dK/dV of every key of KV head 0 from all its readers, and dQ of every row of those
+    query heads.  The shared prefix (owned once, summing every branch's queries) and the
+    mounted spans (their readers' gradients routed into the producer's tokens) are also
+    reported on their own."""
+    G = x["q"].shape[1] // x["k"].shape[1]
+    say(f"  oracle: KV head 0 over all {dag.T} rows")
+    gq, gk, gv = A.attn_bwd(x["q"][:, :G], x["k"][:, :1], x["v"][:, :1], x["do"][:, :G],
+                            dag.branches, dag.mounts)
+    check_grad(dq[:, :G], gq, "dQ (heads of KV head 0, all rows)")
+    check_grad(dk[:, :1], gk, "dK (KV head 0, all keys)")
+    check_grad(dv[:, :1], gv, "dV (KV head 0, all keys)")
+    roots = [(int(s), int(s + L)) for (p, f, s, L) in dag.branches if p < 0]
+    pk = np.concatenate([np.arange(lo, hi) for lo, hi in roots])
+    check_grad(dk[pk, :1], gk[pk], "dK (shared prefix, KV head 0)")
+    check_grad(dv[pk, :1], gv[pk], "dV (shared prefix, KV head 0)")
+    spans = [(int(dag.branches[p_, 2]) + int(s_), int(dag.branches[p_, 2]) + int(e_))
+             for (r_, rp_, p_, s_, e_) in dag.mounts]
+    if spans:
+        mk = np.concatenate([np.arange(lo, hi) for lo, hi in _merge(spans)])
+        check_grad(dk[mk, :1], gk[mk], "dK (mounted spans, KV head 0)")
+        check_grad(dv[mk, :1], gv[mk], "dV (mounted spans, KV head 0)")
 
 
 def test_bwd_workspace_error():
@@ -166,3 +196,29 @@ def test_bwd_workspace_error():
     with pytest.raises(tpb.OctopusError) as ei:
         tpb.attn_bwd(plan, t["q"], t["k"], t["v"], o, lse, t["do"], ws=small)
     assert ei.value.name == "EWORKSPACE"
+
+
+def test_fwd_bwd_on_a_side_stream():
+    """Work enqueued on a stream other than the current one, with outputs and workspaces
+    allocated by the binding: equal to the same calls on the current stream."""
+    import torch
+    import tree_packed_block_amd as tpb
+    say("case fwd+bwd on a side stream")
+    dag, x = workload("episode_small", 16, 4, 128, "bf16", 0.5, with_dout=True)
+    plan = tpb.Plan(dag.branches, dag.mounts, dag.T).upload()
+    t = {k: dev(v, "bf16") for k, v in x.items()}
+    o0, l0 = tpb.attn_fwd(plan, t["q"], t["k"], t["v"])
+    g0 = tpb.attn_bwd(plan, t["q"], t["k"], t["v"], o0, l0, t["do"])
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    o1, l1 = tpb.attn_fwd(plan, t["q"], t["k"], t["v"], stream=side)
+    g1 = tpb.attn_bwd(plan, t["q"], t["k"], t["v"], o1, l1, t["do"], stream=side)
+    # the current stream allocates and writes while the side stream still runs
+    junk = [torch.full((1 << 20,), 7.0, device="cuda") for _ in range(8)]
+    side.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    assert torch.equal(o1, o0) and torch.equal(l1, l0)
+    for a, b in zip(g1, g0):
+        assert torch.equal(a, b)

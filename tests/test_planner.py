@@ -380,7 +380,10 @@ def test_new_entry_points_reject_bad_arguments_before_any_launch():
     # both children fork from the root at offset 256: one checkpoint slot
     assert tpb.gdn_workspace_bytes(p, 2) == 1 * 2 * 128 * 128 * 4
     # extend
-    assert _code(L.octopus_paged_mount_extend(tpb.BF16, 1, 16, 4, 64, 64, 0.0, fake, fake, fake,
+    assert _code(L.octopus_paged_mount_extend(tpb.BF16, 1, 16, 4, 96, 64, 0.0, fake, fake, fake,
+                                              4, fake, 1, fake, fake, fake, fake, fake, fake,
+                                              fake, fake, fake, None)) == "EUNSUPPORTED"
+    assert _code(L.octopus_paged_mount_extend(5, 1, 16, 4, 64, 64, 0.0, fake, fake, fake,
                                               4, fake, 1, fake, fake, fake, fake, fake, fake,
                                               fake, fake, fake, None)) == "EUNSUPPORTED"
     assert _code(L.octopus_paged_mount_extend(tpb.BF16, 1, 16, 4, 128, 64, 0.0, fake, fake, fake,
@@ -437,3 +440,49 @@ def test_plan_at_the_token_limit():
     with pytest.raises(tpb.OctopusError):
         tpb.Plan(np.array([[-1, 0, 0, n * L + 1]], np.int32), np.zeros((0, 5), np.int32),
                  n * L + 1)
+
+
+def _nnz_closed_form(br, mt):
+    """Visible pairs of an episode-shaped tree (or a forest of them) where no mounted key
+    is otherwise visible to its reader: every branch's rows see their inherited context
+    (the parent's first `fork` tokens, the parent's own context there, and mounts the
+    parent had read by then), their own tokens causally, and every span mounted at or
+    before their offset.  Every non-root branch of these trees forks from its tree's root,
+    which has no mounts, so the inherited context is `fork` keys."""
+    total = 0
+    for b, (parent, fork, start, L) in enumerate(br):
+        L = int(L)
+        inherited = 0 if parent < 0 else int(fork)
+        total += L * inherited + L * (L + 1) // 2
+        for (reader, rpos, producer, s, e) in mt:
+            if int(reader) == b:
+                total += (L - int(rpos)) * (int(e) - int(s))
+    return total
+
+
+@pytest.mark.parametrize("name,want", [("episode131k", 1_514_769_199),
+                                       ("episode262k", 6_058_939_877),
+                                       ("forest1m", 24_310_578_842)])
+def test_plan_nnz_full_size_closed_form(name, want):
+    """The numerator of the headline FLOP count: the planner's visible-pair count at
+    full size equals the closed form over the tables, and the stated figure."""
+    dag, _ = synth.build(name)
+    br, mt = dag.branches, dag.mounts
+    for (parent, fork, start, L) in br:  # the closed form's premise
+        assert parent < 0 or br[parent][0] < 0
+    for (reader, rpos, producer, s, e) in mt:
+        assert br[reader][0] >= 0 and br[producer][0] >= 0 and reader != producer
+    assert _nnz_closed_form(br, mt) == want
+    p = tpb.Plan(br, mt, dag.T)
+    assert p.stats()["nnz"] == want
+
+
+def test_gpu_fuzz_any_producer_draws_descendants():
+    """The any-producer GPU fuzz cases (tests/test_edge_gpu.py) do mount spans of the
+    reader's own descendants, so the kernels are known to consume that layout."""
+    import test_edge_gpu as E
+    n = 0
+    for seed in range(8):
+        dag, _ = E._any_producer_dag(1000 + seed)
+        n += sum(E._descends(dag.branches, int(p), int(r)) for (r, rp, p, s, e) in dag.mounts)
+    assert n >= 3
