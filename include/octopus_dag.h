@@ -103,7 +103,10 @@ typedef struct {
 
 /* ---------------------------------------------------------------- planning (host) */
 
-/* Validate the tables, compute positions, and build the tile plan: for every
+/* Plans one packed tree (Octopus project page, card "03 · Training": every branch of a
+ * tree packed into one unpadded 1-D pass, compiled once per tree; the branch and mount
+ * rows are the `fork` and `read_thread` rows of the primitives table).
+ * Validate the tables, compute positions, and build the tile plan: for every
  * 128-row query tile the ordered list of KV tiles holding a key some row of the
  * tile sees, each FULL (every row sees every key) or PARTIAL (a per-row bit mask),
  * the transposed lists (for every KV tile, the query tiles that see it), and
@@ -158,7 +161,9 @@ void octopus_plan_destroy(octopus_plan* plan);
 size_t octopus_fwd_workspace_bytes(const octopus_plan* plan, octopus_dtype dtype,
                                    int32_t Hq, int32_t Hkv, int32_t D);
 
-/* Forward of packed-DAG attention over the uploaded plan.
+/* Forward of packed-DAG attention over the uploaded plan: the block-sparse pass
+ * structured as a prefix tree (ia.com.br article, section "Crédito contrafactual ...";
+ * project page, card "03 · Training"), row i attending to Ctx(i) above.
  *   q   THD [T][Hq][D], k, v THD [T][Hkv][D]  (dtype; rotated at the plan's positions)
  *   o   THD [T][Hq][D] (dtype), lse float32 [Hq][T] (natural log) -- both written
  * Supported: bf16 with D in {64, 128}; fp32 with D in {64, 128}; Hq % Hkv == 0,
@@ -174,7 +179,10 @@ int octopus_dag_attn_fwd(const octopus_plan* plan, octopus_dtype dtype, int32_t 
 size_t octopus_bwd_workspace_bytes(const octopus_plan* plan, octopus_dtype dtype,
                                    int32_t Hq, int32_t Hkv, int32_t D);
 
-/* Backward of L = sum <dO, O> given the forward's o and lse:
+/* Backward of L = sum <dO, O> given the forward's o and lse (project page, card
+ * "03 · Training": a shared prefix owned once, reader gradients routed into the
+ * producer's KV; ia.com.br article, section "Crédito contrafactual ...": mount edges
+ * differentiable end to end):
  *   dq THD [T][Hq][D]; dk, dv THD [T][Hkv][D]  (dtype) -- written, not accumulated.
  * Every dK/dV row is produced by exactly one work unit (the owner of its KV tile),
  * summing the queries of every branch that sees it (descendants through the shared
@@ -312,15 +320,17 @@ int octopus_decode_segments(const octopus_branch* branches, int32_t n_branches,
 size_t octopus_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t n_split);
 
 /* One-token attention of B cursors over their segments, read in place from the
- * pools.  q [B][Hq][D]; k_pool, v_pool [n_pages][Hkv][page_size][D] (dtype);
+ * pools (project page, primitives table, rows "fork" and "read_thread": shared radix
+ * pages and mounted spans read zero-copy; card "01 · Runtime": paged serving of the
+ * branch cursors).  q [B][Hq][D]; k_pool, v_pool [n_pages][Hkv][page_size][D] (dtype);
  * seg_* and, with n_groups > 0, grp_ptr / grp_cur as produced by
  * octopus_decode_segments (n_groups = 0: share = 0 lists, group arrays ignored), on
  * the device.  Every list is split into n_split contiguous chunks (1 <= n_split <=
  * 256); the partial softmax states of a cursor's own chunks and of its group's shared
  * chunks are merged by LSE.  Writes o [B][Hq][D] (dtype) and, if lse is not NULL,
  * float32 [B][Hq].  Segments naming a page outside [0, n_pages) are skipped; group
- * entries naming no cursor in [0, B) are ignored.  Supported: bf16, D = 128,
- * page_size = 64, Hq / Hkv <= 8.
+ * entries naming no cursor in [0, B) are ignored.  Supported: bf16 (matrix cores) and
+ * fp32 (exact float32 arithmetic), D in {64, 128}, page_size = 64, Hq / Hkv <= 8.
  * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP. */
 int octopus_paged_mount_decode(octopus_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
                                int32_t D, int32_t page_size, float scale, const void* q,
@@ -363,7 +373,8 @@ int octopus_extend_segments(const octopus_branch* branches, int32_t n_branches,
  * float32 [n_rows][Hq].  Needs no workspace.  Index arrays that do not come from
  * octopus_extend_segments give undefined values (never a read outside the pools: a
  * segment naming a page outside [0, n_pages) reads page 0 and is masked).
- * Supported: bf16, D = 128, page_size = 64, Hq / Hkv <= 16.
+ * Supported: bf16 (matrix cores) and fp32 (exact float32 arithmetic), D in {64, 128},
+ * page_size = 64, Hq / Hkv <= 16.
  * Errors: EINVAL, EUNSUPPORTED, EHIP. */
 int octopus_paged_mount_extend(octopus_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
                                int32_t D, int32_t page_size, float scale, const void* q,

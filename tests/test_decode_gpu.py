@@ -13,13 +13,13 @@ from parity import TOL, check_close, dev, host, say
 pytestmark = pytest.mark.gpu
 
 
-def _decode_inputs(wl, Hq=16, Hkv=4, Dh=128, seed=55):
+def _decode_inputs(wl, Hq=16, Hkv=4, Dh=128, seed=55, dtype="bf16"):
     rng = np.random.default_rng(seed)
     return synth.draw_decode_inputs(rng, len(wl.cursors), Hq, Hkv, Dh, wl.n_pages,
-                                    wl.page_size)
+                                    wl.page_size, dtype=dtype)
 
 
-def _gpu_decode(wl, x, n_split, segs=None, share=False):
+def _gpu_decode(wl, x, n_split, segs=None, share=False, dtype="bf16"):
     """Through the C ABI; with ``share``, the inherited context of every group of cursors
     is a list of its own, read once per block of cursors."""
     import torch
@@ -28,7 +28,7 @@ def _gpu_decode(wl, x, n_split, segs=None, share=False):
         segs = tpb.decode_segments(wl.dag.branches, wl.dag.mounts, wl.page_ptr, wl.pages,
                                    wl.page_size, wl.n_pages, wl.cursors, share=share)
     sd = [torch.from_numpy(np.ascontiguousarray(s, dtype=np.int32)).cuda() for s in segs]
-    q, kp, vp = dev(x["q"], "bf16"), dev(x["k_pool"], "bf16"), dev(x["v_pool"], "bf16")
+    q, kp, vp = dev(x["q"], dtype), dev(x["k_pool"], dtype), dev(x["v_pool"], dtype)
     o, lse = tpb.paged_mount_decode(q, kp, vp, *sd, n_split=n_split)
     torch.cuda.synchronize()
     return host(o), host(lse)
@@ -47,6 +47,33 @@ def test_decode_small(n_split, share):
                                page_size=64)
     x = _decode_inputs(wl)
     o, lse = _gpu_decode(wl, x, n_split, share=share)
+    ro, rl = _oracle(wl, x)
+    check_close(o, ro, TOL["bf16"], "O")
+    check_close(lse, rl, TOL["bf16"], "LSE")
+
+
+@pytest.mark.parametrize("share", [False, True])
+@pytest.mark.parametrize("n_split", [1, 3])
+@pytest.mark.parametrize("Dh,dtype", [(64, "bf16"), (64, "fp32"), (128, "fp32")])
+def test_decode_small_head_dims_and_fp32(Dh, dtype, n_split, share):
+    """head_dim 64 (bf16 MFMA kernel) and float32 pools (exact float32 kernel) with the
+    same segment lists, shared or not."""
+    say(f"case decode small D={Dh} {dtype} n_split={n_split} share={share}")
+    wl = synth.decode_workload(seed=6, n_cursors=7, prefix=200, own_max=260, span_max=90,
+                               page_size=64)
+    x = _decode_inputs(wl, Hq=8, Hkv=2, Dh=Dh, dtype=dtype)
+    o, lse = _gpu_decode(wl, x, n_split, share=share, dtype=dtype)
+    ro, rl = _oracle(wl, x)
+    check_close(o, ro, TOL[dtype], "O")
+    check_close(lse, rl, TOL[dtype], "LSE")
+
+
+def test_decode_full_batch_head_dim_64():
+    """The 64-cursor batch at head_dim 64: every cursor against the oracle."""
+    say("case decode 64 cursors D=64")
+    wl = synth.decode_workload()
+    x = _decode_inputs(wl, Dh=64)
+    o, lse = _gpu_decode(wl, x, 32, share=True)
     ro, rl = _oracle(wl, x)
     check_close(o, ro, TOL["bf16"], "O")
     check_close(lse, rl, TOL["bf16"], "LSE")
@@ -137,8 +164,8 @@ def test_decode_argument_errors():
     with pytest.raises(tpb.OctopusError) as ei:
         tpb.paged_mount_decode(q, kp, kp, seg, seg, seg, seg, n_split=0)
     assert ei.value.name == "EINVAL"
-    q64 = torch.zeros((2, 16, 64), dtype=torch.bfloat16, device="cuda")
-    kp64 = torch.zeros((4, 4, 64, 64), dtype=torch.bfloat16, device="cuda")
+    q96 = torch.zeros((2, 16, 96), dtype=torch.bfloat16, device="cuda")
+    kp96 = torch.zeros((4, 4, 64, 96), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(tpb.OctopusError) as ei:
-        tpb.paged_mount_decode(q64, kp64, kp64, seg, seg, seg, seg, n_split=2)
+        tpb.paged_mount_decode(q96, kp96, kp96, seg, seg, seg, seg, n_split=2)
     assert ei.value.name == "EUNSUPPORTED"

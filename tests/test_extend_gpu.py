@@ -22,13 +22,13 @@ def _q_ptr(n_new):
     return np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)
 
 
-def _gpu_extend(wl, n_new, x):
+def _gpu_extend(wl, n_new, x, dtype="bf16"):
     import torch
     import tree_packed_block_amd as tpb
     segs = tpb.extend_segments(wl.dag.branches, wl.dag.mounts, wl.page_ptr, wl.pages,
                                wl.page_size, wl.n_pages, wl.cursors, n_new)
     sp, pg, lo, hi, thr, causal, first = segs
-    q, kp, vp = dev(x["q"], "bf16"), dev(x["k_pool"], "bf16"), dev(x["v_pool"], "bf16")
+    q, kp, vp = dev(x["q"], dtype), dev(x["k_pool"], dtype), dev(x["v_pool"], dtype)
     o, lse = tpb.paged_mount_extend(q, kp, vp, _i32(_q_ptr(n_new)), int(max(n_new)),
                                     _i32(first), _i32(sp), _i32(pg), _i32(lo), _i32(hi),
                                     _i32(thr), _i32(causal))
@@ -42,9 +42,9 @@ def _oracle(wl, n_new, x, only=None):
                       only=only)
 
 
-def _inputs(wl, n_new, Hq, Hkv, seed=77):
+def _inputs(wl, n_new, Hq, Hkv, seed=77, Dh=128, dtype="bf16"):
     return synth.draw_extend_inputs(np.random.default_rng(seed), int(np.sum(n_new)), Hq, Hkv,
-                                    128, wl.n_pages, wl.page_size)
+                                    Dh, wl.n_pages, wl.page_size, dtype=dtype)
 
 
 def test_extend_small():
@@ -56,6 +56,36 @@ def test_extend_small():
     L = wl.dag.branches[wl.cursors, 3]
     n_new = np.minimum(L, np.random.default_rng(9).integers(1, 300, size=len(L)))
     x = _inputs(wl, n_new, 16, 4)
+    o, lse = _gpu_extend(wl, n_new, x)
+    ro, rl = _oracle(wl, n_new, x)
+    check_close(o, ro, TOL["bf16"], "O")
+    check_close(lse, rl, TOL["bf16"], "LSE")
+
+
+@pytest.mark.parametrize("Dh,dtype", [(64, "bf16"), (64, "fp32"), (128, "fp32")])
+def test_extend_small_head_dims_and_fp32(Dh, dtype):
+    """head_dim 64 (bf16 MFMA kernel) and float32 pools (exact float32 kernel)."""
+    say(f"case extend small D={Dh} {dtype}")
+    wl = synth.decode_workload(seed=5, n_cursors=6, prefix=256, own_max=300, span_max=100,
+                               page_size=64)
+    L = wl.dag.branches[wl.cursors, 3]
+    n_new = np.minimum(L, np.random.default_rng(9).integers(1, 300, size=len(L)))
+    x = _inputs(wl, n_new, 8, 2, Dh=Dh, dtype=dtype)
+    o, lse = _gpu_extend(wl, n_new, x, dtype=dtype)
+    ro, rl = _oracle(wl, n_new, x)
+    check_close(o, ro, TOL[dtype], "O")
+    check_close(lse, rl, TOL[dtype], "LSE")
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_extend_fuzz_head_dim_64(seed):
+    say(f"case extend fuzz D=64 seed={seed}")
+    rng = np.random.default_rng(400 + seed)
+    dag = synth.fuzz_dag(rng, max_len=300, max_branches=7, max_mounts=6)
+    n_pages, ptr, pages = synth.dags.assign_pages(dag, 64, rng)
+    wl = synth.DecodeWorkload(dag, 64, n_pages, ptr, pages, np.arange(dag.nb, dtype=np.int32))
+    n_new = np.array([int(rng.integers(1, L + 1)) for L in dag.branches[:, 3]])
+    x = _inputs(wl, n_new, 6, 2, seed=500 + seed, Dh=64)
     o, lse = _gpu_extend(wl, n_new, x)
     ro, rl = _oracle(wl, n_new, x)
     check_close(o, ro, TOL["bf16"], "O")
@@ -132,8 +162,8 @@ def test_extend_argument_errors():
     import torch
     import tree_packed_block_amd as tpb
     z = torch.zeros(4, dtype=torch.int32, device="cuda")
-    q = torch.zeros((2, 16, 64), dtype=torch.bfloat16, device="cuda")
-    kp = torch.zeros((4, 4, 64, 64), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((2, 16, 96), dtype=torch.bfloat16, device="cuda")
+    kp = torch.zeros((4, 4, 64, 96), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(tpb.OctopusError) as ei:
         tpb.paged_mount_extend(q, kp, kp, z[:2], 2, z[:1], z[:2], z, z, z, z, z)
     assert ei.value.name == "EUNSUPPORTED"

@@ -221,11 +221,14 @@ class Plan:
         finished with it."""
         import torch
         n = self.device_bytes()
+        mine = buffer is None
         if buffer is None:
             buffer = torch.empty(n, dtype=torch.uint8, device=device)
         if buffer.dtype != torch.uint8 or not buffer.is_cuda or not buffer.is_contiguous():
             raise OctopusError(EINVAL, "plan buffer must be a contiguous uint8 device tensor")
-        stream = stream or torch.cuda.current_stream(buffer.device)
+        stream = _stream(stream, buffer.device)
+        if mine:
+            _owned(stream, buffer)
         _check(lib().octopus_plan_upload(self._h, _vp(buffer.data_ptr()), buffer.numel(),
                                          _vp(stream.cuda_stream)))
         if sync:
@@ -243,6 +246,22 @@ def _dtype_code(t):
     if t.dtype == torch.float32:
         return FP32
     raise OctopusError(EUNSUPPORTED, f"dtype {t.dtype} not supported")
+
+
+def _stream(stream, device):
+    """The stream to enqueue on (the current one if ``stream`` is None)."""
+    import torch
+    return stream or torch.cuda.current_stream(device)
+
+
+def _owned(s, *tensors):
+    """Tensors this module allocated for work enqueued on ``s``: when ``s`` is not the
+    current stream, tell the caching allocator they are in use there, so their memory
+    is not handed to other work before ``s`` has finished with it."""
+    import torch
+    for t in tensors:
+        if t is not None and s != torch.cuda.current_stream(t.device):
+            t.record_stream(s)
 
 
 def _need(t, shape, dtype, name):
@@ -269,17 +288,22 @@ def attn_fwd(plan: Plan, q, k, v, scale=None, o=None, lse=None, ws=None, stream=
     _need(q, (plan.T, Hq, D), q.dtype, "q")
     _need(k, (plan.T, Hkv, D), q.dtype, "k")
     _need(v, (plan.T, Hkv, D), q.dtype, "v")
+    s = _stream(stream, q.device)
+    mine = []
     if o is None:
         o = torch.empty_like(q)
+        mine.append(o)
     if lse is None:
         lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+        mine.append(lse)
     _need(o, q.shape, q.dtype, "o")
     _need(lse, (Hq, T), torch.float32, "lse")
     code = _dtype_code(q)
     if ws is None:
         need = fwd_workspace_bytes(plan, code, Hq, Hkv, D)
         ws = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
-    s = stream or torch.cuda.current_stream(q.device)
+        mine.append(ws)
+    _owned(s, *mine)
     _check(lib().octopus_dag_attn_fwd(plan.handle, code, Hq, Hkv, D, float(scale or 0.0),
                                       q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                       lse.data_ptr(), None if ws is None else ws.data_ptr(),
@@ -302,14 +326,23 @@ def attn_bwd(plan: Plan, q, k, v, o, lse, dout, scale=None, dq=None, dk=None, dv
                        (dout, (plan.T, Hq, D), "dout")):
         _need(t, shp, q.dtype, nm)
     _need(lse, (Hq, T), torch.float32, "lse")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    s = _stream(stream, q.device)
+    mine = []
+    if dq is None:
+        dq = torch.empty_like(q)
+        mine.append(dq)
+    if dk is None:
+        dk = torch.empty_like(k)
+        mine.append(dk)
+    if dv is None:
+        dv = torch.empty_like(v)
+        mine.append(dv)
     code = _dtype_code(q)
     need = bwd_workspace_bytes(plan, code, Hq, Hkv, D)
     if ws is None:
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    s = stream or torch.cuda.current_stream(q.device)
+        mine.append(ws)
+    _owned(s, *mine)
     _check(lib().octopus_dag_attn_bwd(plan.handle, code, Hq, Hkv, D, float(scale or 0.0),
                                       q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                       lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
@@ -367,9 +400,11 @@ def rope(x, pos, base=10000.0, inverse=False, out=None, stream=None):
         raise OctopusError(EINVAL, "x must be a contiguous device tensor")
     if pos.dtype != torch.int32 or not pos.is_cuda or pos.numel() != rows:
         raise OctopusError(EINVAL, "pos must be a device int32 tensor with one entry per row")
-    out = torch.empty_like(x) if out is None else out
+    s = _stream(stream, x.device)
+    if out is None:
+        out = torch.empty_like(x)
+        _owned(s, out)
     _need(out, x.shape, x.dtype, "out")
-    s = stream or torch.cuda.current_stream(x.device)
     _check(lib().octopus_rope(_dtype_code(x), rows, H, D, float(base), 1 if inverse else 0,
                               pos.data_ptr(), x.data_ptr(), out.data_ptr(), _vp(s.cuda_stream)))
     return out
@@ -388,14 +423,21 @@ def attn_fwd_rope(plan: Plan, q, k, v, base=10000.0, scale=None, o=None, lse=Non
     _need(q, (plan.T, Hq, D), q.dtype, "q")
     _need(k, (plan.T, Hkv, D), q.dtype, "k")
     _need(v, (plan.T, Hkv, D), q.dtype, "v")
-    o = torch.empty_like(q) if o is None else o
-    lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device) if lse is None else lse
+    s = _stream(stream, q.device)
+    mine = []
+    if o is None:
+        o = torch.empty_like(q)
+        mine.append(o)
+    if lse is None:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+        mine.append(lse)
     code = _dtype_code(q)
     if ws is None:
         need = rope_workspace_bytes(plan, code, Hq, Hkv, D) + fwd_workspace_bytes(plan, code,
                                                                                 Hq, Hkv, D)
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
-    s = stream or torch.cuda.current_stream(q.device)
+        mine.append(ws)
+    _owned(s, *mine)
     _check(lib().octopus_dag_attn_fwd_rope(plan.handle, code, Hq, Hkv, D, float(scale or 0.0),
                                            float(base), q.data_ptr(), k.data_ptr(),
                                            v.data_ptr(), o.data_ptr(), lse.data_ptr(),
@@ -413,15 +455,24 @@ def attn_bwd_rope(plan: Plan, q, k, v, o, lse, dout, base=10000.0, scale=None, d
                        (v, (plan.T, Hkv, D), "v"), (o, (plan.T, Hq, D), "o"),
                        (dout, (plan.T, Hq, D), "dout")):
         _need(t, shp, q.dtype, nm)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    s = _stream(stream, q.device)
+    mine = []
+    if dq is None:
+        dq = torch.empty_like(q)
+        mine.append(dq)
+    if dk is None:
+        dk = torch.empty_like(k)
+        mine.append(dk)
+    if dv is None:
+        dv = torch.empty_like(v)
+        mine.append(dv)
     code = _dtype_code(q)
     if ws is None:
         need = rope_workspace_bytes(plan, code, Hq, Hkv, D) + bwd_workspace_bytes(plan, code,
                                                                                 Hq, Hkv, D)
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
-    s = stream or torch.cuda.current_stream(q.device)
+        mine.append(ws)
+    _owned(s, *mine)
     _check(lib().octopus_dag_attn_bwd_rope(plan.handle, code, Hq, Hkv, D, float(scale or 0.0),
                                            float(base), q.data_ptr(), k.data_ptr(),
                                            v.data_ptr(), o.data_ptr(), lse.data_ptr(),
@@ -448,11 +499,16 @@ def gated_delta_scan(plan: Plan, q, k, v, alpha, beta, o=None, ws=None, stream=N
     _need(v, (plan.T, H, Dv), q.dtype, "v")
     _need(alpha, (plan.T, H), torch.float32, "alpha")
     _need(beta, (plan.T, H), torch.float32, "beta")
-    o = torch.empty_like(v) if o is None else o
+    s = _stream(stream, q.device)
+    mine = []
+    if o is None:
+        o = torch.empty_like(v)
+        mine.append(o)
     if ws is None:
         ws = torch.empty(max(gdn_workspace_bytes(plan, H, Dk, Dv), 16), dtype=torch.uint8,
                          device=q.device)
-    s = stream or torch.cuda.current_stream(q.device)
+        mine.append(ws)
+    _owned(s, *mine)
     _check(lib().octopus_gated_delta_scan(plan.handle, _dtype_code(q), H, Dk, Dv, q.data_ptr(),
                                           k.data_ptr(), v.data_ptr(), alpha.data_ptr(),
                                           beta.data_ptr(), o.data_ptr(), ws.data_ptr(),
@@ -528,12 +584,19 @@ def paged_mount_decode(q, k_pool, v_pool, seg_ptr, seg_page, seg_lo, seg_hi, grp
             raise OctopusError(EINVAL, f"{nm} must be a contiguous int32 device tensor")
     if seg_ptr.numel() != B + n_groups + 1:
         raise OctopusError(EINVAL, "seg_ptr must have B + n_groups + 1 entries")
-    o = torch.empty_like(q) if o is None else o
-    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    s = _stream(stream, q.device)
+    mine = []
+    if o is None:
+        o = torch.empty_like(q)
+        mine.append(o)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        mine.append(lse)
     need = decode_workspace_bytes(B, Hq, D, n_split)
     if ws is None:
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    s = stream or torch.cuda.current_stream(q.device)
+        mine.append(ws)
+    _owned(s, *mine)
     gp = grp_ptr.data_ptr() if grp_ptr is not None else None
     gc = grp_cur.data_ptr() if grp_cur is not None else None
     _check(lib().octopus_paged_mount_decode(
@@ -595,9 +658,15 @@ def paged_mount_extend(q, k_pool, v_pool, q_ptr, max_new, first_off, seg_ptr, se
     B = q_ptr.numel() - 1
     if first_off.numel() != B or seg_ptr.numel() != B + 1:
         raise OctopusError(EINVAL, "first_off and seg_ptr must match q_ptr's cursor count")
-    o = torch.empty_like(q) if o is None else o
-    lse = torch.empty((n_rows, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
-    s = stream or torch.cuda.current_stream(q.device)
+    s = _stream(stream, q.device)
+    mine = []
+    if o is None:
+        o = torch.empty_like(q)
+        mine.append(o)
+    if lse is None:
+        lse = torch.empty((n_rows, Hq), dtype=torch.float32, device=q.device)
+        mine.append(lse)
+    _owned(s, *mine)
     _check(lib().octopus_paged_mount_extend(
         _dtype_code(q), B, Hq, Hkv, D, page_size, float(scale or 0.0), q.data_ptr(),
         k_pool.data_ptr(), v_pool.data_ptr(), n_pages, q_ptr.data_ptr(), int(max_new),

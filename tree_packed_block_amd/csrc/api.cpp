@@ -552,8 +552,9 @@ int octopus_paged_mount_extend(octopus_dtype dtype, int32_t B, int32_t Hq, int32
                                const int32_t* seg_lo, const int32_t* seg_hi,
                                const int32_t* seg_thr, const int32_t* seg_causal, void* o,
                                float* lse, void* stream) {
-    if (dtype != OCTOPUS_BF16) return fail(OCTOPUS_EUNSUPPORTED, "extend supports bf16 only");
-    if (D != 128) return fail(OCTOPUS_EUNSUPPORTED, "extend supports head_dim 128 only");
+    if (dtype != OCTOPUS_BF16 && dtype != OCTOPUS_FP32)
+        return fail(OCTOPUS_EUNSUPPORTED, "dtype must be bf16 or fp32");
+    if (D != 64 && D != 128) return fail(OCTOPUS_EUNSUPPORTED, "head_dim must be 64 or 128");
     if (page_size != 64) return fail(OCTOPUS_EUNSUPPORTED, "extend supports page_size 64 only");
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
         return fail(OCTOPUS_EINVAL, "B, Hq, Hkv must be positive with Hq % Hkv == 0");
@@ -568,10 +569,10 @@ int octopus_paged_mount_extend(octopus_dtype dtype, int32_t B, int32_t Hq, int32
         !seg_causal)
         return fail(OCTOPUS_EINVAL, "index arrays must not be NULL");
     if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
-    hipError_t e = octo::launch_extend_bf16(B, Hq, Hkv, D, scale, q, k_pool, v_pool, n_pages,
-                                            q_ptr, max_new, first_off, seg_ptr, seg_page, seg_lo,
-                                            seg_hi, seg_thr, seg_causal, o, lse,
-                                            (hipStream_t)stream);
+    hipError_t e = octo::launch_extend(dtype == OCTOPUS_BF16, B, Hq, Hkv, D, scale, q, k_pool,
+                                       v_pool, n_pages, q_ptr, max_new, first_off, seg_ptr,
+                                       seg_page, seg_lo, seg_hi, seg_thr, seg_causal, o, lse,
+                                       (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "extend launch");
     return ok();
 }
@@ -588,8 +589,9 @@ int octopus_paged_mount_decode(octopus_dtype dtype, int32_t B, int32_t Hq, int32
                                const int32_t* seg_lo, const int32_t* seg_hi, int32_t n_groups,
                                const int32_t* grp_ptr, const int32_t* grp_cur, int32_t n_split,
                                void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
-    if (dtype != OCTOPUS_BF16) return fail(OCTOPUS_EUNSUPPORTED, "decode supports bf16 only");
-    if (D != 128) return fail(OCTOPUS_EUNSUPPORTED, "decode supports head_dim 128 only");
+    if (dtype != OCTOPUS_BF16 && dtype != OCTOPUS_FP32)
+        return fail(OCTOPUS_EUNSUPPORTED, "dtype must be bf16 or fp32");
+    if (D != 64 && D != 128) return fail(OCTOPUS_EUNSUPPORTED, "head_dim must be 64 or 128");
     if (page_size != 64) return fail(OCTOPUS_EUNSUPPORTED, "decode supports page_size 64 only");
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
         return fail(OCTOPUS_EINVAL, "B, Hq, Hkv must be positive with Hq % Hkv == 0");
@@ -610,10 +612,10 @@ int octopus_paged_mount_decode(octopus_dtype dtype, int32_t B, int32_t Hq, int32
         return fail(OCTOPUS_EWORKSPACE, "decode workspace needs " + std::to_string(need) +
                                             " bytes, 16-byte aligned");
     if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
-    hipError_t e = octo::launch_decode_bf16(B, Hq, Hkv, D, page_size, scale, q, k_pool, v_pool,
-                                            n_pages, seg_ptr, seg_page, seg_lo, seg_hi,
-                                            n_groups, grp_ptr, grp_cur, n_split, o, lse,
-                                            static_cast<float*>(ws), (hipStream_t)stream);
+    hipError_t e = octo::launch_decode(dtype == OCTOPUS_BF16, B, Hq, Hkv, D, page_size, scale,
+                                       q, k_pool, v_pool, n_pages, seg_ptr, seg_page, seg_lo,
+                                       seg_hi, n_groups, grp_ptr, grp_cur, n_split, o, lse,
+                                       static_cast<float*>(ws), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return ok();
 }

@@ -273,10 +273,10 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(
 // sum, and 2 floats of padding so every state starts 16-byte aligned.  Every slot is
 // written by the split pass (an empty one as max -inf, sum 0, zero accumulator), so
 // the lanes read 64 slots' maxima at once and the accumulation needs no branch.
-template <int D>
+template <int D, typename OT>
 __global__ __launch_bounds__(64) void decode_combine_kernel(int B, int Hq, int n_slots,
                                                             const float* __restrict__ partial,
-                                                            bf16* __restrict__ O,
+                                                            OT* __restrict__ O,
                                                             float* __restrict__ LSE) {
     const int c = blockIdx.x / Hq, h = blockIdx.x % Hq;
     const int lane = threadIdx.x;
@@ -321,26 +321,172 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(int B, int Hq, int n
     const float inv = 1.f / L;
 #pragma unroll
     for (int e = 0; e < D / 64; ++e)
-        O[((size_t)c * Hq + h) * D + lane + 64 * e] = (bf16)(acc[e] * inv);
+        O[((size_t)c * Hq + h) * D + lane + 64 * e] = (OT)(acc[e] * inv);
     if (LSE != nullptr && lane == 0) LSE[(size_t)c * Hq + h] = (M + log2f(L)) * kLn2;
 }
 
-hipError_t launch_decode_bf16(int B, int Hq, int Hkv, int D, int page_size, float scale,
-                              const void* q, const void* k_pool, const void* v_pool,
-                              int n_pages, const int32_t* seg_ptr, const int32_t* seg_page,
-                              const int32_t* seg_lo, const int32_t* seg_hi, int n_groups,
-                              const int32_t* grp_ptr, const int32_t* grp_cur, int n_split,
-                              void* o, float* lse, float* partial, hipStream_t s) {
-    (void)page_size;
-    (void)D;  // checked by the caller: D == 128, page_size == 64
+// ------------------------------------------------------------------ float32
+//
+// Exact float32 decode (for float32 pools): one wave64 per work item as above, each lane
+// owning one slot of the page.  Per page the K and V blocks are staged in LDS (rows padded
+// by one float so the per-slot row reads spread over the banks), every lane scores its
+// slot for the G query heads, the running max and sum per head are wave-uniform, and the
+// accumulator is split across the lanes by feature (lane l holds features l + 64e).  A
+// group item serves one cursor of its group (the inherited context is read once per
+// cursor: this variant is for exactness, not bandwidth).  It writes the same partial
+// states as the bf16 kernel, which the combine kernel merges.
+template <int D>
+__global__ __launch_bounds__(64) void decode_split_fp32_kernel(
+    int B, int Hq, int Hkv, int n_split, int n_slots, float scale_log2,
+    const float* __restrict__ Qd, const float* __restrict__ Kp, const float* __restrict__ Vp,
+    int n_pages, const int32_t* __restrict__ seg_ptr, const int32_t* __restrict__ seg_page,
+    const int32_t* __restrict__ seg_lo, const int32_t* __restrict__ seg_hi, int n_groups,
+    const int32_t* __restrict__ grp_ptr, const int32_t* __restrict__ grp_cur,
+    float* __restrict__ partial) {
+    constexpr int E = D / 64;   // features per lane
+    constexpr int GMAX = 8;     // query heads per KV head
+    __shared__ float ks[kPage][D + 1];
+    __shared__ float vs[kPage][D + 1];
+    __shared__ float qs[GMAX][D];
+    __shared__ float ps[GMAX][kPage];
+    const int lane = threadIdx.x;
+    const int per = B * Hkv * n_split;
+    int item = blockIdx.x;
+    const bool grp = n_groups > 0 && item >= per;
+    if (grp) item -= per;
+    const int split = item % n_split;
+    const int kvh = (item / n_split) % Hkv;
+    const int c = item / (n_split * Hkv);
+    const int G = Hq / Hkv;
+    int list = c, cursor = c;
+    if (grp) {
+        int lo_g = 0, hi_g = n_groups;
+        while (hi_g - lo_g > 1) {
+            const int mid = (lo_g + hi_g) >> 1;
+            if (grp_ptr[mid] <= c) lo_g = mid; else hi_g = mid;
+        }
+        if (c < grp_ptr[lo_g] || c >= grp_ptr[lo_g + 1]) return;
+        list = B + lo_g;
+        cursor = grp_cur[c];
+        if (cursor < 0 || cursor >= B) return;  // not a cursor: nothing to write
+    }
+    for (int i = lane; i < G * D; i += 64)
+        qs[i / D][i % D] = Qd[((size_t)cursor * Hq + kvh * G) * D + i];
+
+    const int s0 = seg_ptr[list], s1 = seg_ptr[list + 1];
+    const long long ns = s1 - s0;
+    const int a = s0 + (int)((ns * split) / n_split);
+    const int b = s0 + (int)((ns * (split + 1)) / n_split);
+
+    float m[GMAX], l[GMAX], o[GMAX][E];
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[h][e] = 0.f;
+    }
+    for (int sg = a; sg < b; ++sg) {
+        const int page = seg_page[sg], lo = seg_lo[sg], hi = seg_hi[sg];
+        if (!seg_ok(page, lo, hi, n_pages)) continue;  // wave-uniform
+        const size_t blk = ((size_t)page * Hkv + kvh) * kPage * D;
+        __syncthreads();  // the previous page's LDS reads are done
+        for (int i = lane; i < kPage * D; i += 64) {
+            const int r = i / D, d = i % D;
+            const bool in = r >= lo && r < hi;
+            ks[r][d] = in ? Kp[blk + i] : 0.f;
+            vs[r][d] = in ? Vp[blk + i] : 0.f;
+        }
+        __syncthreads();
+        const bool vis = lane >= lo && lane < hi;
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h) {
+            if (h >= G) break;
+            float sc = 0.f;
+            for (int d = 0; d < D; ++d) sc = fmaf(qs[h][d], ks[lane][d], sc);
+            const float t = vis ? sc * scale_log2 : -INFINITY;
+            float mx = t;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+            const float mnew = fmaxf(m[h], mx);
+            const float alpha = m[h] == -INFINITY ? 0.f : exp2f(m[h] - mnew);
+            const float pv = t == -INFINITY ? 0.f : exp2f(t - mnew);
+            float ps_sum = pv;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) ps_sum += __shfl_xor(ps_sum, off);
+            l[h] = l[h] * alpha + ps_sum;
+            m[h] = mnew;
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[h][e] *= alpha;
+            ps[h][lane] = pv;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h) {
+            if (h >= G) break;
+            for (int j = lo; j < hi; ++j) {
+                const float pj = ps[h][j];
+#pragma unroll
+                for (int e = 0; e < E; ++e) o[h][e] = fmaf(pj, vs[j][lane + 64 * e], o[h][e]);
+            }
+        }
+    }
+    const int slot = grp ? n_split + split : split;
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) {
+        if (h >= G) break;
+        float* out = partial + (((size_t)cursor * n_slots + slot) * Hq + kvh * G + h) * (D + 4);
+#pragma unroll
+        for (int e = 0; e < E; ++e) out[lane + 64 * e] = o[h][e];
+        if (lane == 0) {
+            out[D] = (a < b && l[h] > 0.f) ? m[h] : -INFINITY;
+            out[D + 1] = l[h];
+        }
+    }
+}
+
+template <int D>
+static void decode_launch(bool b16, int B, int Hq, int Hkv, float scale, const void* q,
+                          const void* k_pool, const void* v_pool, int n_pages,
+                          const int32_t* seg_ptr, const int32_t* seg_page, const int32_t* seg_lo,
+                          const int32_t* seg_hi, int n_groups, const int32_t* grp_ptr,
+                          const int32_t* grp_cur, int n_split, void* o, float* lse,
+                          float* partial, hipStream_t s) {
     const int n_slots = n_groups > 0 ? 2 * n_split : n_split;
     const int items = (n_groups > 0 ? 2 : 1) * B * Hkv * n_split;
-    hipLaunchKernelGGL(decode_split_kernel<128>, dim3((items + kWaves - 1) / kWaves),
-                       dim3(64 * kWaves), 0, s, B, Hq, Hkv, n_split, n_slots, scale * kLog2e,
-                       (const bf16*)q, (const bf16*)k_pool, (const bf16*)v_pool, n_pages, seg_ptr,
-                       seg_page, seg_lo, seg_hi, n_groups, grp_ptr, grp_cur, partial);
-    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(B * Hq), dim3(64), 0, s, B, Hq, n_slots,
-                       partial, (bf16*)o, lse);
+    if (b16) {
+        hipLaunchKernelGGL(decode_split_kernel<D>, dim3((items + kWaves - 1) / kWaves),
+                           dim3(64 * kWaves), 0, s, B, Hq, Hkv, n_split, n_slots,
+                           scale * kLog2e, (const bf16*)q, (const bf16*)k_pool,
+                           (const bf16*)v_pool, n_pages, seg_ptr, seg_page, seg_lo, seg_hi,
+                           n_groups, grp_ptr, grp_cur, partial);
+        hipLaunchKernelGGL((decode_combine_kernel<D, bf16>), dim3(B * Hq), dim3(64), 0, s, B,
+                           Hq, n_slots, partial, (bf16*)o, lse);
+    } else {
+        hipLaunchKernelGGL(decode_split_fp32_kernel<D>, dim3(items), dim3(64), 0, s, B, Hq,
+                           Hkv, n_split, n_slots, scale * kLog2e, (const float*)q,
+                           (const float*)k_pool, (const float*)v_pool, n_pages, seg_ptr,
+                           seg_page, seg_lo, seg_hi, n_groups, grp_ptr, grp_cur, partial);
+        hipLaunchKernelGGL((decode_combine_kernel<D, float>), dim3(B * Hq), dim3(64), 0, s, B,
+                           Hq, n_slots, partial, (float*)o, lse);
+    }
+}
+
+hipError_t launch_decode(bool b16, int B, int Hq, int Hkv, int D, int page_size, float scale,
+                         const void* q, const void* k_pool, const void* v_pool, int n_pages,
+                         const int32_t* seg_ptr, const int32_t* seg_page,
+                         const int32_t* seg_lo, const int32_t* seg_hi, int n_groups,
+                         const int32_t* grp_ptr, const int32_t* grp_cur, int n_split, void* o,
+                         float* lse, float* partial, hipStream_t s) {
+    (void)page_size;  // checked by the caller: page_size == 64
+    if (D == 128)
+        decode_launch<128>(b16, B, Hq, Hkv, scale, q, k_pool, v_pool, n_pages, seg_ptr,
+                           seg_page, seg_lo, seg_hi, n_groups, grp_ptr, grp_cur, n_split, o,
+                           lse, partial, s);
+    else
+        decode_launch<64>(b16, B, Hq, Hkv, scale, q, k_pool, v_pool, n_pages, seg_ptr,
+                          seg_page, seg_lo, seg_hi, n_groups, grp_ptr, grp_cur, n_split, o,
+                          lse, partial, s);
     return hipGetLastError();
 }
 

@@ -257,7 +257,108 @@ __global__ __launch_bounds__(256 * HPW, 1) void extend_bf16_kernel(
     }
 }
 
-template <int HPW>
+// ------------------------------------------------------------------ float32
+//
+// Exact float32 extend (for float32 pools): one wave64 per (cursor, new token j <
+// max_new, KV head), tokens past the cursor's count leaving at once; each
+// lane owning one slot of a page.  Per segment the wave stages the page-head blocks of K
+// and V in LDS, scores its slot for the G query heads with the visibility rule of the
+// thresholds, and keeps a running max and sum per head (wave-uniform) and the
+// accumulator split across the lanes by feature.  Segments are sorted by threshold, so
+// the walk stops at the first one the token's offset does not reach.
+template <int D>
+__global__ __launch_bounds__(64) void extend_fp32_kernel(
+    int Hq, int Hkv, int max_new, float scale_log2, const float* __restrict__ Q,
+    const float* __restrict__ Kp, const float* __restrict__ Vp, int n_pages,
+    const int32_t* __restrict__ q_ptr, const int32_t* __restrict__ first_off,
+    const int32_t* __restrict__ seg_ptr, const int32_t* __restrict__ seg_page,
+    const int32_t* __restrict__ seg_lo, const int32_t* __restrict__ seg_hi,
+    const int32_t* __restrict__ seg_thr, const int32_t* __restrict__ seg_causal,
+    float* __restrict__ O, float* __restrict__ LSE) {
+    constexpr int E = D / 64;
+    constexpr int GMAX = 16;
+    __shared__ float ks[kSlots][D + 1];
+    __shared__ float vs[kSlots][D + 1];
+    __shared__ float qs[GMAX][D];
+    __shared__ float ps[GMAX][kSlots];
+    const int lane = threadIdx.x;
+    const int kvh = blockIdx.x % Hkv;
+    const int j = (blockIdx.x / Hkv) % max_new;  // new token j of cursor c
+    const int c = blockIdx.x / (Hkv * max_new);
+    const int G = Hq / Hkv;
+    if (j >= q_ptr[c + 1] - q_ptr[c]) return;
+    const int row = q_ptr[c] + j;
+    const int r_own = first_off[c] + j;
+    const size_t qrow = ((size_t)row * Hq + kvh * G) * D;
+    for (int i = lane; i < G * D; i += 64) qs[i / D][i % D] = Q[qrow + i];
+
+    float m[GMAX], l[GMAX], o[GMAX][E];
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[h][e] = 0.f;
+    }
+    for (int sg = seg_ptr[c]; sg < seg_ptr[c + 1]; ++sg) {
+        const int thr = seg_thr[sg];
+        if (thr > r_own) break;  // sorted by threshold: no later segment is seen
+        const int pg = seg_page[sg], lo = seg_lo[sg], hi = seg_hi[sg];
+        const bool causal = seg_causal[sg] != 0;
+        if (!(pg >= 0 && pg < n_pages && lo >= 0 && lo < hi && hi <= kSlots)) continue;
+        const size_t blk = ((size_t)pg * Hkv + kvh) * kSlots * D;
+        __syncthreads();
+        for (int i = lane; i < kSlots * D; i += 64) {
+            const int r = i / D, d = i % D;
+            const bool in = r >= lo && r < hi;
+            ks[r][d] = in ? Kp[blk + i] : 0.f;
+            vs[r][d] = in ? Vp[blk + i] : 0.f;
+        }
+        __syncthreads();
+        const bool vis = lane >= lo && lane < hi && r_own >= thr + (causal ? lane - lo : 0);
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h) {
+            if (h >= G) break;
+            float sc = 0.f;
+            for (int d = 0; d < D; ++d) sc = fmaf(qs[h][d], ks[lane][d], sc);
+            const float t = vis ? sc * scale_log2 : -INFINITY;
+            float mx = t;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+            const float mnew = fmaxf(m[h], mx);
+            const float alpha = m[h] == -INFINITY ? 0.f : exp2f(m[h] - mnew);
+            const float pv = t == -INFINITY ? 0.f : exp2f(t - mnew);
+            float sum = pv;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+            l[h] = l[h] * alpha + sum;
+            m[h] = mnew;
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[h][e] *= alpha;
+            ps[h][lane] = pv;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h) {
+            if (h >= G) break;
+            for (int j = lo; j < hi; ++j) {
+                const float pj = ps[h][j];
+#pragma unroll
+                for (int e = 0; e < E; ++e) o[h][e] = fmaf(pj, vs[j][lane + 64 * e], o[h][e]);
+            }
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) {
+        if (h >= G) break;
+        const float inv = 1.f / l[h];
+#pragma unroll
+        for (int e = 0; e < E; ++e) O[qrow + (size_t)h * D + lane + 64 * e] = o[h][e] * inv;
+        if (lane == 0) LSE[(size_t)row * Hq + kvh * G + h] = (m[h] + log2f(l[h])) * kLn2;
+    }
+}
+
+template <int D, int HPW>
 static void extend_launch(int B, int Hq, int Hkv, int n_qt, float sl2, const void* q,
                           const void* k_pool, const void* v_pool, int n_pages,
                           const int32_t* q_ptr, const int32_t* first_off, const int32_t* seg_ptr,
@@ -265,28 +366,50 @@ static void extend_launch(int B, int Hq, int Hkv, int n_qt, float sl2, const voi
                           const int32_t* seg_thr, const int32_t* seg_causal, void* o, float* lse,
                           hipStream_t s) {
     const int G = Hq / Hkv;
-    hipLaunchKernelGGL((extend_bf16_kernel<128, HPW>), dim3(xcd_grid(B * n_qt * Hkv, G / HPW)),
+    hipLaunchKernelGGL((extend_bf16_kernel<D, HPW>), dim3(xcd_grid(B * n_qt * Hkv, G / HPW)),
                        dim3(256 * HPW), 0, s, B, Hq, Hkv, n_qt, sl2, (const bf16*)q,
                        (const bf16*)k_pool, (const bf16*)v_pool, n_pages, q_ptr, first_off,
                        seg_ptr, seg_page, seg_lo, seg_hi, seg_thr, seg_causal, (bf16*)o, lse);
 }
 
-hipError_t launch_extend_bf16(int B, int Hq, int Hkv, int D, float scale, const void* q,
-                              const void* k_pool, const void* v_pool, int n_pages,
-                              const int32_t* q_ptr, int max_new, const int32_t* first_off,
-                              const int32_t* seg_ptr, const int32_t* seg_page,
-                              const int32_t* seg_lo, const int32_t* seg_hi,
-                              const int32_t* seg_thr, const int32_t* seg_causal, void* o,
-                              float* lse, hipStream_t s) {
-    (void)D;  // checked by the caller: D == 128
+template <int D>
+static void extend_dispatch(bool b16, int B, int Hq, int Hkv, int max_new, int n_qt, float sl2,
+                            const void* q, const void* k_pool, const void* v_pool, int n_pages,
+                            const int32_t* q_ptr, const int32_t* first_off,
+                            const int32_t* seg_ptr, const int32_t* seg_page,
+                            const int32_t* seg_lo, const int32_t* seg_hi, const int32_t* seg_thr,
+                            const int32_t* seg_causal, void* o, float* lse, hipStream_t s) {
+    if (!b16) {
+        hipLaunchKernelGGL(extend_fp32_kernel<D>, dim3(B * max_new * Hkv), dim3(64), 0, s, Hq,
+                           Hkv, max_new, sl2, (const float*)q, (const float*)k_pool,
+                           (const float*)v_pool, n_pages, q_ptr, first_off, seg_ptr, seg_page,
+                           seg_lo, seg_hi, seg_thr, seg_causal, (float*)o, lse);
+    } else if ((Hq / Hkv) % 2 == 0) {
+        extend_launch<D, 2>(B, Hq, Hkv, n_qt, sl2, q, k_pool, v_pool, n_pages, q_ptr, first_off,
+                            seg_ptr, seg_page, seg_lo, seg_hi, seg_thr, seg_causal, o, lse, s);
+    } else {
+        extend_launch<D, 1>(B, Hq, Hkv, n_qt, sl2, q, k_pool, v_pool, n_pages, q_ptr, first_off,
+                            seg_ptr, seg_page, seg_lo, seg_hi, seg_thr, seg_causal, o, lse, s);
+    }
+}
+
+hipError_t launch_extend(bool b16, int B, int Hq, int Hkv, int D, float scale, const void* q,
+                         const void* k_pool, const void* v_pool, int n_pages,
+                         const int32_t* q_ptr, int max_new, const int32_t* first_off,
+                         const int32_t* seg_ptr, const int32_t* seg_page,
+                         const int32_t* seg_lo, const int32_t* seg_hi,
+                         const int32_t* seg_thr, const int32_t* seg_causal, void* o,
+                         float* lse, hipStream_t s) {
     const int n_qt = (max_new + kBq - 1) / kBq;
     const float sl2 = scale * kLog2e;
-    if ((Hq / Hkv) % 2 == 0)
-        extend_launch<2>(B, Hq, Hkv, n_qt, sl2, q, k_pool, v_pool, n_pages, q_ptr, first_off,
-                         seg_ptr, seg_page, seg_lo, seg_hi, seg_thr, seg_causal, o, lse, s);
+    if (D == 128)
+        extend_dispatch<128>(b16, B, Hq, Hkv, max_new, n_qt, sl2, q, k_pool, v_pool, n_pages,
+                             q_ptr, first_off, seg_ptr, seg_page, seg_lo, seg_hi, seg_thr,
+                             seg_causal, o, lse, s);
     else
-        extend_launch<1>(B, Hq, Hkv, n_qt, sl2, q, k_pool, v_pool, n_pages, q_ptr, first_off,
-                         seg_ptr, seg_page, seg_lo, seg_hi, seg_thr, seg_causal, o, lse, s);
+        extend_dispatch<64>(b16, B, Hq, Hkv, max_new, n_qt, sl2, q, k_pool, v_pool, n_pages,
+                            q_ptr, first_off, seg_ptr, seg_page, seg_lo, seg_hi, seg_thr,
+                            seg_causal, o, lse, s);
     return hipGetLastError();
 }
 

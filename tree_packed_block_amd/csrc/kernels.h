@@ -66,13 +66,14 @@ hipError_t launch_bwd_dq(bool bf16, const DevPlan& p, int Hq, int Hkv, int D, fl
                          const void* q, const void* k, const void* v, const void* dout,
                          float* ws, void* dq, hipStream_t s);
 // Decode: per-cursor segment lists 0..B-1, then (n_groups > 0) one shared list per group
-// of cursors (grp_ptr / grp_cur).  partial: float32 [B][2 n_split][Hq][D + 4].
-hipError_t launch_decode_bf16(int B, int Hq, int Hkv, int D, int page_size, float scale,
-                              const void* q, const void* k_pool, const void* v_pool,
-                              int n_pages, const int32_t* seg_ptr, const int32_t* seg_page,
-                              const int32_t* seg_lo, const int32_t* seg_hi, int n_groups,
-                              const int32_t* grp_ptr, const int32_t* grp_cur, int n_split,
-                              void* o, float* lse, float* partial, hipStream_t s);
+// of cursors (grp_ptr / grp_cur).  partial: float32 [B][2 n_split][Hq][D + 4].  `bf16`
+// selects the MFMA kernel, otherwise float32 pools and outputs.  D in {64, 128}.
+hipError_t launch_decode(bool bf16, int B, int Hq, int Hkv, int D, int page_size, float scale,
+                         const void* q, const void* k_pool, const void* v_pool, int n_pages,
+                         const int32_t* seg_ptr, const int32_t* seg_page,
+                         const int32_t* seg_lo, const int32_t* seg_hi, int n_groups,
+                         const int32_t* grp_ptr, const int32_t* grp_cur, int n_split, void* o,
+                         float* lse, float* partial, hipStream_t s);
 
 // Rotary embedding in place or out of place: x is [rows][H][D] (bf16 if `bf16`, else
 // float32); row r turns by pos[r] * base^(-2i/D) on pairs (i, i + D/2), by the opposite
@@ -94,12 +95,13 @@ hipError_t launch_gdn_scan(const DevPlan& p, int l0, int n_br, int H, const void
 
 // Extend: rows q_ptr[c] .. q_ptr[c+1]-1 of q are cursor c's new tokens (own offsets
 // first_off[c] + j); segments as built by build_extend_segments.  max_new >= every m_c.
-hipError_t launch_extend_bf16(int B, int Hq, int Hkv, int D, float scale, const void* q,
-                              const void* k_pool, const void* v_pool, int n_pages,
-                              const int32_t* q_ptr, int max_new, const int32_t* first_off,
-                              const int32_t* seg_ptr, const int32_t* seg_page,
-                              const int32_t* seg_lo, const int32_t* seg_hi,
-                              const int32_t* seg_thr, const int32_t* seg_causal, void* o,
-                              float* lse, hipStream_t s);
+// `bf16` selects the MFMA kernel, otherwise float32.  D in {64, 128}.
+hipError_t launch_extend(bool bf16, int B, int Hq, int Hkv, int D, float scale, const void* q,
+                         const void* k_pool, const void* v_pool, int n_pages,
+                         const int32_t* q_ptr, int max_new, const int32_t* first_off,
+                         const int32_t* seg_ptr, const int32_t* seg_page,
+                         const int32_t* seg_lo, const int32_t* seg_hi,
+                         const int32_t* seg_thr, const int32_t* seg_causal, void* o,
+                         float* lse, hipStream_t s);
 
 }  // namespace octo
