@@ -502,30 +502,50 @@ def main():
                     "once per block of 8 cursors); not an HBM figure"}
         del kc, vc
 
-    # The RoPE pass of the RoPE entry points, on its own clock: Q and K turned at the
-    # plan's positions in one launch (the forward runs it once, the backward once more
-    # and once in reverse on dQ, dK).
+    # RoPE at the plan's positions, on its own clock.  The forward with unrotated Q and K
+    # turns K in one pass and each query row in the forward kernel's registers; the
+    # backward turns Q and K in one pass and dQ, dK back in the registers of the kernels
+    # that produce them.  The pass is also timed alone (on K, as the forward runs it, and
+    # on Q) against the HBM roofline.
     wsr = torch.empty(tpb.rope_workspace_bytes(probe, tpb.BF16, HQ, HKV, HD)
-                      + tpb.fwd_workspace_bytes(probe, tpb.BF16, HQ, HKV, HD),
+                      + max(tpb.fwd_workspace_bytes(probe, tpb.BF16, HQ, HKV, HD),
+                            tpb.bwd_workspace_bytes(probe, tpb.BF16, HQ, HKV, HD)),
                       dtype=torch.uint8, device=dev)
     plan_r = tpb.Plan(dag.branches, dag.mounts, dag.T).upload()
+    pos_d = torch.from_numpy(pos.astype(np.int32)).to(dev)
     o_r, lse_r = torch.empty_like(q), torch.empty_like(lse)
+    kr_, qr_ = torch.empty_like(k), torch.empty_like(q)
 
-    def run_rope():
-        tpb.attn_fwd_rope(plan_r, q, k, v, o=o_r, lse=lse_r, ws=wsr)
+    def clock(fn, n=3):
+        fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        ev[0].record(stream)
+        for j in range(n):
+            fn()
+            ev[j + 1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([ev[j].elapsed_time(ev[j + 1]) for j in range(n)]))
 
-    run_rope()
-    ev_r = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    ev_r[0].record(stream)
-    for j in range(3):
-        run_rope()
-        ev_r[j + 1].record(stream)
-    torch.cuda.synchronize()
-    ms_r = float(np.median([ev_r[j].elapsed_time(ev_r[j + 1]) for j in range(3)]))
-    out["breakdown"]["fwd_rope"] = {
-        "ms": round(ms_r, 3), "rope_overhead_ms": round(ms_r - per["fwd"], 3),
-        "note": "forward with unrotated Q, K: the RoPE pass (Q and K turned at the plan's "
-                "positions, one launch) plus the same forward"}
+    ms_r = clock(lambda: tpb.attn_fwd_rope(plan_r, q, k, v, o=o_r, lse=lse_r, ws=wsr))
+    ms_rb = clock(lambda: tpb.attn_bwd_rope(plan_r, q, k, v, o_r, lse_r, do, dq=dq, dk=dk,
+                                            dv=dv, ws=wsr))
+    ms_pk = clock(lambda: tpb.rope(k, pos_d, out=kr_), n=10)
+    ms_pq = clock(lambda: tpb.rope(q, pos_d, out=qr_), n=10)
+    bwd_ms = per["bwd_preprocess"] + per["bwd_dkdv"] + per["bwd_dq"]
+    pass_bytes_k = 2.0 * k.numel() * 2 + dag.T * 4
+    pass_bytes_q = 2.0 * q.numel() * 2 + dag.T * 4
+    out["breakdown"]["rope"] = {
+        "fwd_ms": round(ms_r, 3), "fwd_overhead_ms": round(ms_r - per["fwd"], 3),
+        "bwd_ms": round(ms_rb, 3), "bwd_overhead_ms": round(ms_rb - bwd_ms, 3),
+        "pass_k_ms": round(ms_pk, 3),
+        "pass_k_GB/s": round(pass_bytes_k / (ms_pk * 1e-3) / 1e9, 1),
+        "pass_q_ms": round(ms_pq, 3),
+        "pass_q_GB/s": round(pass_bytes_q / (ms_pq * 1e-3) / 1e9, 1),
+        "pass_q_frac_of_peak": round(pass_bytes_q / (ms_pq * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "note": "unrotated Q and K: forward = K pass + forward turning each query row in "
+                "registers; backward = one Q+K pass + the three backward phases turning dQ "
+                "and dK back in registers; overheads against the step's own fwd and bwd "
+                "event times; pass bytes = read + write of the tensor + positions"}
 
     # Recurrent-layer scan over the same tree, on its own clock: 16 heads of 128 x 128
     # gated delta-rule state, each branch from its parent's fork checkpoint.

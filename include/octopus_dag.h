@@ -227,29 +227,36 @@ int octopus_dag_positions(const octopus_branch* branches, int32_t n_branches,
  * (x_i, x_{i+D/2}) turned by pos[r] * rope_base^(-2i/D) (by the opposite angle if
  * inverse), written to out (may equal x).  pos: device int32[rows].  Mounted keys keep
  * the position they were written at, so paged keys are stored rotated once, at their
- * producer's positions (card "02 · Memory": rotation-free mounts).
+ * producer's positions (card "02 · Memory": rotation-free mounts).  Angles are reduced in
+ * float64 (pos * theta reaches 2^24 radians).
  * Supported: bf16 and fp32, D in {64, 128}.  Errors: EINVAL, EUNSUPPORTED, EHIP. */
 int octopus_rope(octopus_dtype dtype, int32_t rows, int32_t H, int32_t D, float rope_base,
                  int32_t inverse, const int32_t* pos, const void* x, void* out, void* stream);
 
-/* Extra workspace bytes of the RoPE variants below: rotated copies of Q and K. */
+/* Extra workspace bytes of the RoPE variants below: rotated copies of Q and K (the bf16
+ * forward uses only the part for K). */
 size_t octopus_rope_workspace_bytes(const octopus_plan* plan, octopus_dtype dtype,
                                     int32_t Hq, int32_t Hkv, int32_t D);
 
-/* octopus_dag_attn_fwd with Q and K given unrotated: both are turned at the plan's
- * positions (rope_base > 1) into the front of the workspace, then the forward runs on
- * them.  ws: 256-byte aligned, octopus_rope_workspace_bytes + octopus_fwd_workspace_bytes
- * bytes, the rotated copies first.  Errors as octopus_dag_attn_fwd. */
+/* octopus_dag_attn_fwd with Q and K given unrotated, turned at the plan's positions
+ * (card "02 · Memory": keys keep the rotation of the position they were written at; a
+ * reader's positions jump after a mount).  bf16: K is turned by one pass into the front
+ * of the workspace and every query row is turned in the forward kernel's registers; fp32:
+ * Q and K are turned into copies first.  ws: 256-byte aligned, octopus_rope_workspace_bytes
+ * + octopus_fwd_workspace_bytes bytes suffice (the rotated copies first).  Errors as
+ * octopus_dag_attn_fwd. */
 int octopus_dag_attn_fwd_rope(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
                               int32_t Hkv, int32_t D, float scale, float rope_base,
                               const void* q, const void* k, const void* v, void* o, float* lse,
                               void* ws, size_t ws_bytes, void* stream);
 
-/* octopus_dag_attn_bwd with Q and K given unrotated: gradients are taken with respect to
- * the rotated copies and dQ, dK are then turned back in place (the rotation is
- * orthogonal), so they are the gradients with respect to the unrotated inputs.  ws as
- * for the forward, with octopus_bwd_workspace_bytes after the rotated copies.
- * Errors as octopus_dag_attn_bwd. */
+/* octopus_dag_attn_bwd with Q and K given unrotated: Q and K are turned by one pass into
+ * the front of the workspace, gradients are taken with respect to the rotated copies and
+ * dQ, dK are turned back (the rotation is orthogonal), so they are the gradients with
+ * respect to the unrotated inputs.  bf16: the dQ and dK/dV kernels turn their results back
+ * in registers before storing them; fp32: a pass turns them back in place.  ws: 256-byte
+ * aligned, octopus_rope_workspace_bytes + octopus_bwd_workspace_bytes bytes, the rotated
+ * copies first.  Errors as octopus_dag_attn_bwd. */
 int octopus_dag_attn_bwd_rope(const octopus_plan* plan, octopus_dtype dtype, int32_t Hq,
                               int32_t Hkv, int32_t D, float scale, float rope_base,
                               const void* q, const void* k, const void* v, const void* o,

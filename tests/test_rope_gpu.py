@@ -122,3 +122,39 @@ def test_rope_decode_and_extend_queries():
                           wl.dag.mounts, wl.page_ptr, wl.pages, 64, wl.cursors, q_ptr)
     check_close(host(oe), reo, TOL["bf16"], "extend O")
     check_close(host(le), rel, TOL["bf16"], "extend LSE")
+
+
+@pytest.mark.timeout(900)
+def test_rope_fwd_bwd_full_size_sampled():
+    """The 131,072-token tree with unrotated Q and K (query rows and gradients turned in
+    the kernels' registers, positions up to ~2*10^4): O and LSE on sampled rows, dQ on
+    sampled rows, dK/dV on keys whose every reader the oracle enumerates."""
+    import torch
+    import tree_packed_block_amd as tpb
+    from parity import sample_rows
+    from test_bwd_gpu import _key_samples, _merge
+    say("case rope fwd+bwd episode131k sampled")
+    dag, _ = synth.build("episode131k")
+    rng = np.random.default_rng(31)
+    x = synth.draw_attention_inputs(rng, dag.T, 16, 4, 128, np.zeros(dag.T, dtype=np.int64),
+                                    dtype="bf16", std=0.5, with_dout=True)
+    plan = tpb.Plan(dag.branches, dag.mounts, dag.T).upload()
+    assert int(plan.positions().max()) > 16384
+    t = {k: dev(v, "bf16") for k, v in x.items()}
+    o, lse = tpb.attn_fwd_rope(plan, t["q"], t["k"], t["v"])
+    dq, dk, dv = tpb.attn_bwd_rope(plan, t["q"], t["k"], t["v"], o, lse, t["do"])
+    torch.cuda.synchronize()
+    o, lse, dq, dk, dv = host(o), host(lse), host(dq), host(dk), host(dv)
+    qrows = sample_rows(dag)
+    ro, rl = R.attn_fwd(x["q"], x["k"], x["v"], dag.branches, dag.mounts, rows=qrows)
+    qi = np.concatenate([np.arange(lo, hi) for lo, hi in qrows])
+    check_close(o[qi], ro[qi], TOL["bf16"], "O (sampled rows)")
+    check_close(lse[:, qi], rl[:, qi], TOL["bf16"], "LSE (sampled rows)")
+    keys, krows = _key_samples(dag)
+    rows = _merge(qrows + krows)
+    gq, gk, gv = R.attn_bwd(x["q"], x["k"], x["v"], x["do"], dag.branches, dag.mounts,
+                            rows=rows)
+    ki = np.concatenate([np.arange(lo, hi) for lo, hi in keys])
+    check_grad(dq[qi], gq[qi], "dQ (sampled rows)")
+    check_grad(dk[ki], gk[ki], "dK (sampled keys)")
+    check_grad(dv[ki], gv[ki], "dV (sampled keys)")

@@ -214,7 +214,7 @@ int octopus_dag_attn_fwd(const octopus_plan* plan, octopus_dtype dtype, int32_t 
     if (dtype == OCTOPUS_BF16) {
         e = octo::launch_tiles_t(dp.T, dp.nKT, Hkv, D, v, ws, (hipStream_t)stream);
         if (e == hipSuccess)
-            e = octo::launch_fwd_bf16(dp, Hq, Hkv, D, scale, q, k, ws, o, lse,
+            e = octo::launch_fwd_bf16(dp, Hq, Hkv, D, scale, q, k, ws, o, lse, nullptr,
                                       (hipStream_t)stream);
     } else {
         e = octo::launch_fwd_fp32(dp, Hq, Hkv, D, scale, q, k, v, o, lse, (hipStream_t)stream);
@@ -252,19 +252,35 @@ int octopus_dag_attn_fwd_rope(const octopus_plan* plan, octopus_dtype dtype, int
     int rc = check_attn(plan, dtype, Hq, Hkv, D, {q, k, v, o, lse});
     if (rc != OCTOPUS_OK) return rc;
     if (!(rope_base > 1.f)) return fail(OCTOPUS_EINVAL, "rope_base must be > 1");
-    const size_t head = rope_part(plan, dtype, Hq, Hkv, D);
+    const bool b16 = dtype == OCTOPUS_BF16;
+    const size_t es = b16 ? 2 : 4;
+    const size_t T = (size_t)plan->p.T;
+    // bf16: only K is rotated by a pass (the forward turns each query row in registers);
+    // fp32: rotated copies of Q and K.
+    const size_t head = b16 ? round256(T * Hkv * D * es) : rope_part(plan, dtype, Hq, Hkv, D);
     const size_t need = head + octopus_fwd_workspace_bytes(plan, dtype, Hq, Hkv, D);
     if (ws == nullptr || ws_bytes < need || !aligned(ws, 256))
         return fail(OCTOPUS_EWORKSPACE, "forward (rope) workspace needs " +
                                             std::to_string(need) + " bytes, 256-byte aligned");
     unsigned char* w = static_cast<unsigned char*>(ws);
-    const size_t es = dtype == OCTOPUS_BF16 ? 2 : 4;
-    void* qr = w;
-    void* kr = w + round256((size_t)plan->p.T * Hq * D * es);
     const octo::DevPlan dp = dev_view(plan->p);
-    const bool b16 = dtype == OCTOPUS_BF16;
-    const hipError_t e = octo::launch_rope2(b16, dp.T, D, rope_base, false, dp.pos, Hq, q, qr,
-                                            Hkv, k, kr, (hipStream_t)stream);
+    hipStream_t st = (hipStream_t)stream;
+    if (b16) {
+        void* kr = w;
+        hipError_t e = octo::launch_rope(true, dp.T, Hkv, D, rope_base, false, dp.pos, k, kr, st);
+        if (e == hipSuccess) e = octo::launch_tiles_t(dp.T, dp.nKT, Hkv, D, v, w + head, st);
+        if (e == hipSuccess) {
+            if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
+            const octo::RopeFreq rt = octo::rope_freq(D, rope_base);
+            e = octo::launch_fwd_bf16(dp, Hq, Hkv, D, scale, q, kr, w + head, o, lse, &rt, st);
+        }
+        if (e != hipSuccess) return hip_fail(e, "forward (rope) launch");
+        return ok();
+    }
+    void* qr = w;
+    void* kr = w + round256(T * Hq * D * es);
+    const hipError_t e = octo::launch_rope2(false, dp.T, D, rope_base, false, dp.pos, Hq, q, qr,
+                                            Hkv, k, kr, st);
     if (e != hipSuccess) return hip_fail(e, "rope launch");
     return octopus_dag_attn_fwd(plan, dtype, Hq, Hkv, D, scale, qr, kr, v, o, lse, w + head,
                                 ws_bytes - head, stream);
@@ -313,7 +329,7 @@ int octopus_dag_attn_bwd_dkdv(const octopus_plan* plan, octopus_dtype dtype, int
     if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
     const hipError_t e = octo::launch_bwd_dkdv(dtype == OCTOPUS_BF16, dev_view(plan->p), Hq, Hkv,
                                                D, scale, q, k, v, dout,
-                                               static_cast<const float*>(ws), dk, dv,
+                                               static_cast<const float*>(ws), dk, dv, nullptr,
                                                (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "backward dK/dV launch");
     return ok();
@@ -331,7 +347,7 @@ int octopus_dag_attn_bwd_dq(const octopus_plan* plan, octopus_dtype dtype, int32
     const hipError_t e = octo::launch_bwd_dq(dtype == OCTOPUS_BF16, dev_view(plan->p), Hq, Hkv, D,
                                              scale, q, k, v, dout,
                                              static_cast<float*>(const_cast<void*>(ws)), dq,
-                                             (hipStream_t)stream);
+                                             nullptr, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "backward dQ launch");
     return ok();
 }
@@ -378,7 +394,25 @@ int octopus_dag_attn_bwd_rope(const octopus_plan* plan, octopus_dtype dtype, int
     hipError_t e = octo::launch_rope2(b16, dp.T, D, rope_base, false, dp.pos, Hq, q, qr, Hkv, k,
                                       kr, st);
     if (e != hipSuccess) return hip_fail(e, "rope launch");
-    // Gradients with respect to the rotated Q and K, then turned back in place.
+    if (b16) {
+        // Gradients with respect to the rotated Q and K, each turned back in registers by
+        // the kernel that produces it (the rotation is orthogonal).
+        void* bws = w + head;
+        const size_t bws_bytes = ws_bytes - head;
+        if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
+        const octo::RopeFreq rt = octo::rope_freq(D, rope_base);
+        rc = octopus_dag_attn_bwd_preprocess(plan, dtype, Hq, Hkv, D, o, lse, dout, bws,
+                                             bws_bytes, stream);
+        if (rc != OCTOPUS_OK) return rc;
+        e = octo::launch_bwd_dkdv(true, dp, Hq, Hkv, D, scale, qr, kr, v, dout,
+                                  static_cast<const float*>(bws), dk, dv, &rt, st);
+        if (e == hipSuccess)
+            e = octo::launch_bwd_dq(true, dp, Hq, Hkv, D, scale, qr, kr, v, dout,
+                                    static_cast<float*>(bws), dq, &rt, st);
+        if (e != hipSuccess) return hip_fail(e, "backward (rope) launch");
+        return ok();
+    }
+    // fp32: gradients with respect to the rotated Q and K, then turned back in place.
     rc = octopus_dag_attn_bwd(plan, dtype, Hq, Hkv, D, scale, qr, kr, v, o, lse, dout, dq, dk,
                               dv, w + head, ws_bytes - head, stream);
     if (rc != OCTOPUS_OK) return rc;

@@ -134,13 +134,16 @@ __device__ __forceinline__ bf16x8 split3(float x, bool on) {
 // One wave of a dK/dV workgroup.  ROLE 0 accumulates dK (and hands P to its partner),
 // ROLE 1 accumulates dV (and hands dS over).  Both roles run the same sequence of
 // barriers.
-template <int D, int ROLE>
+// With ROPE, Q and K come rotated at the plan's positions and the dK wave turns its
+// result back at the keys' positions before storing it (the gradient with respect to the
+// unrotated K; the rotation is orthogonal).
+template <int D, int ROLE, bool ROPE>
 __device__ __forceinline__ void dkdv_wave(const DevPlan& P, int Hq, int Hkv, int kb, int kvh,
                                           float scale, float scale_log2,
                                           const bf16* __restrict__ Q, const bf16* __restrict__ K,
                                           const bf16* __restrict__ V, const bf16* __restrict__ dO,
                                           const float* __restrict__ ws, bf16* __restrict__ out,
-                                          unsigned char* smem) {
+                                          unsigned char* smem, const RopeFreq& rt) {
     using C = DkdvLayout<D>;
     constexpr int KS = D / 16, DB = D / 32, CPR = D / 8;
     const int T = P.T, G = Hq / Hkv, Tp = padded_rows(T);
@@ -388,6 +391,7 @@ __device__ __forceinline__ void dkdv_wave(const DevPlan& P, int Hq, int Hkv, int
     for (int kk = 0; kk < 2; ++kk) {
         const int key = key0 + 32 * kk;
         if (key >= T) continue;
+        if constexpr (ROPE && ROLE == 0) rope_accum(acc[kk], P.pos[key], rt, g, -1.f);
         bf16* row = out + (size_t)key * kvstride + (size_t)kvh * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -401,11 +405,11 @@ __device__ __forceinline__ void dkdv_wave(const DevPlan& P, int Hq, int Hkv, int
     }
 }
 
-template <int D>
+template <int D, bool ROPE>
 __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
     DevPlan P, int Hq, int Hkv, float scale, float scale_log2, const bf16* __restrict__ Q,
     const bf16* __restrict__ K, const bf16* __restrict__ V, const bf16* __restrict__ dO,
-    const float* __restrict__ ws, bf16* __restrict__ dK, bf16* __restrict__ dV) {
+    const float* __restrict__ ws, bf16* __restrict__ dK, bf16* __restrict__ dV, RopeFreq rt) {
     constexpr int M = 4;  // consecutive blocks of one KV head dealt to one XCD
     __shared__ __attribute__((aligned(1024))) unsigned char smem[DkdvLayout<D>::BYTES];
     int grp, mm;
@@ -415,16 +419,20 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
     const int kvh = grp % Hkv;
     const int kb = ld_const(P.blk_order + rank);
     if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1)
-        dkdv_wave<D, 1>(P, Hq, Hkv, kb, kvh, scale, scale_log2, Q, K, V, dO, ws, dV, smem);
+        dkdv_wave<D, 1, ROPE>(P, Hq, Hkv, kb, kvh, scale, scale_log2, Q, K, V, dO, ws, dV, smem,
+                              rt);
     else
-        dkdv_wave<D, 0>(P, Hq, Hkv, kb, kvh, scale, scale_log2, Q, K, V, dO, ws, dK, smem);
+        dkdv_wave<D, 0, ROPE>(P, Hq, Hkv, kb, kvh, scale, scale_log2, Q, K, V, dO, ws, dK, smem,
+                              rt);
 }
 
-template <int D, int HPW>
+// With ROPE, Q and K come rotated and dQ is turned back at the row's position before it
+// is stored.
+template <int D, int HPW, bool ROPE>
 __global__ __launch_bounds__(256 * HPW, 1) void dq_bf16_kernel(
     DevPlan P, int Hq, int Hkv, float scale, float scale_log2, const bf16* __restrict__ Q,
     const bf16* __restrict__ K, const bf16* __restrict__ V, const bf16* __restrict__ dO,
-    const float* __restrict__ ws, bf16* __restrict__ dQ) {
+    const float* __restrict__ ws, bf16* __restrict__ dQ, RopeFreq rt) {
     using L = KvLayout<D>;
     constexpr int NTHR = 256 * HPW;
     constexpr int KS = D / 16, DB = D / 32;
@@ -551,6 +559,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void dq_bf16_kernel(
     }
 
     if (row < T) {
+        if constexpr (ROPE) rope_accum(dq, P.pos[row], rt, g, -1.f);
         bf16* out = dQ + (size_t)row * qstride + (size_t)h * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -730,12 +739,18 @@ hipError_t launch_bwd_preprocess(bool bf16_, const DevPlan& p, int Hq, int D, co
 template <int D>
 static void dkdv_launch(bool bf16_, const DevPlan& p, int Hq, int Hkv, float scale,
                         const void* q, const void* k, const void* v, const void* dout,
-                        const float* ws, void* dk, void* dv, hipStream_t s) {
-    if (bf16_)
-        hipLaunchKernelGGL(dkdv_bf16_kernel<D>, dim3(xcd_grid((p.nKB + 3) / 4 * Hkv, 4)),
-                           dim3(256), 0, s, p, Hq, Hkv, scale, scale * kLog2e, (const bf16*)q,
-                           (const bf16*)k, (const bf16*)v, (const bf16*)dout, ws, (bf16*)dk,
-                           (bf16*)dv);
+                        const float* ws, void* dk, void* dv, const RopeFreq* rope,
+                        hipStream_t s) {
+    const dim3 grid(xcd_grid((p.nKB + 3) / 4 * Hkv, 4));
+    const RopeFreq rt = rope ? *rope : RopeFreq{};
+    if (bf16_ && rope)
+        hipLaunchKernelGGL((dkdv_bf16_kernel<D, true>), grid, dim3(256), 0, s, p, Hq, Hkv, scale,
+                           scale * kLog2e, (const bf16*)q, (const bf16*)k, (const bf16*)v,
+                           (const bf16*)dout, ws, (bf16*)dk, (bf16*)dv, rt);
+    else if (bf16_)
+        hipLaunchKernelGGL((dkdv_bf16_kernel<D, false>), grid, dim3(256), 0, s, p, Hq, Hkv, scale,
+                           scale * kLog2e, (const bf16*)q, (const bf16*)k, (const bf16*)v,
+                           (const bf16*)dout, ws, (bf16*)dk, (bf16*)dv, rt);
     else
         hipLaunchKernelGGL(dkdv_fp32_kernel<D>, dim3(p.nKT * Hkv), dim3(64), 0, s, p, Hq, Hkv,
                            scale, (const float*)q, (const float*)k, (const float*)v,
@@ -744,30 +759,38 @@ static void dkdv_launch(bool bf16_, const DevPlan& p, int Hq, int Hkv, float sca
 
 hipError_t launch_bwd_dkdv(bool bf16_, const DevPlan& p, int Hq, int Hkv, int D, float scale,
                            const void* q, const void* k, const void* v, const void* dout,
-                           const float* ws, void* dk, void* dv, hipStream_t s) {
-    if (D == 128) dkdv_launch<128>(bf16_, p, Hq, Hkv, scale, q, k, v, dout, ws, dk, dv, s);
-    else dkdv_launch<64>(bf16_, p, Hq, Hkv, scale, q, k, v, dout, ws, dk, dv, s);
+                           const float* ws, void* dk, void* dv, const RopeFreq* rope,
+                           hipStream_t s) {
+    if (D == 128) dkdv_launch<128>(bf16_, p, Hq, Hkv, scale, q, k, v, dout, ws, dk, dv, rope, s);
+    else dkdv_launch<64>(bf16_, p, Hq, Hkv, scale, q, k, v, dout, ws, dk, dv, rope, s);
     return hipGetLastError();
 }
 
 template <int D, int HPW>
 static hipError_t dq_bf16_launch(const DevPlan& p, int Hq, int Hkv, float scale, const void* q,
                                  const void* k, const void* v, const void* dout, float* ws,
-                                 void* dq, hipStream_t s) {
-    hipLaunchKernelGGL((dq_bf16_kernel<D, HPW>), dim3(xcd_grid(p.nQT * Hkv, Hq / Hkv / HPW)),
-                       dim3(256 * HPW), 0, s, p, Hq, Hkv, scale, scale * kLog2e, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)dout, ws, (bf16*)dq);
+                                 void* dq, const RopeFreq* rope, hipStream_t s) {
+    const dim3 grid(xcd_grid(p.nQT * Hkv, Hq / Hkv / HPW)), block(256 * HPW);
+    const RopeFreq rt = rope ? *rope : RopeFreq{};
+    if (rope)
+        hipLaunchKernelGGL((dq_bf16_kernel<D, HPW, true>), grid, block, 0, s, p, Hq, Hkv, scale,
+                           scale * kLog2e, (const bf16*)q, (const bf16*)k, (const bf16*)v,
+                           (const bf16*)dout, ws, (bf16*)dq, rt);
+    else
+        hipLaunchKernelGGL((dq_bf16_kernel<D, HPW, false>), grid, block, 0, s, p, Hq, Hkv, scale,
+                           scale * kLog2e, (const bf16*)q, (const bf16*)k, (const bf16*)v,
+                           (const bf16*)dout, ws, (bf16*)dq, rt);
     return hipGetLastError();
 }
 
 template <int D>
 static hipError_t dq_launch(bool bf16_, const DevPlan& p, int Hq, int Hkv, float scale,
                             const void* q, const void* k, const void* v, const void* dout,
-                            float* ws, void* dq, hipStream_t s) {
+                            float* ws, void* dq, const RopeFreq* rope, hipStream_t s) {
     if (bf16_) {
         if ((Hq / Hkv) % 2 == 0)
-            return dq_bf16_launch<D, 2>(p, Hq, Hkv, scale, q, k, v, dout, ws, dq, s);
-        return dq_bf16_launch<D, 1>(p, Hq, Hkv, scale, q, k, v, dout, ws, dq, s);
+            return dq_bf16_launch<D, 2>(p, Hq, Hkv, scale, q, k, v, dout, ws, dq, rope, s);
+        return dq_bf16_launch<D, 1>(p, Hq, Hkv, scale, q, k, v, dout, ws, dq, rope, s);
     }
     hipLaunchKernelGGL(dq_fp32_kernel<D>, dim3(p.nQT * Hq), dim3(kBq), 0, s, p, Hq, Hkv, scale,
                        (const float*)q, (const float*)k, (const float*)v, (const float*)dout,
@@ -777,9 +800,9 @@ static hipError_t dq_launch(bool bf16_, const DevPlan& p, int Hq, int Hkv, float
 
 hipError_t launch_bwd_dq(bool bf16_, const DevPlan& p, int Hq, int Hkv, int D, float scale,
                          const void* q, const void* k, const void* v, const void* dout,
-                         float* ws, void* dq, hipStream_t s) {
-    if (D == 128) return dq_launch<128>(bf16_, p, Hq, Hkv, scale, q, k, v, dout, ws, dq, s);
-    return dq_launch<64>(bf16_, p, Hq, Hkv, scale, q, k, v, dout, ws, dq, s);
+                         float* ws, void* dq, const RopeFreq* rope, hipStream_t s) {
+    if (D == 128) return dq_launch<128>(bf16_, p, Hq, Hkv, scale, q, k, v, dout, ws, dq, rope, s);
+    return dq_launch<64>(bf16_, p, Hq, Hkv, scale, q, k, v, dout, ws, dq, rope, s);
 }
 
 }  // namespace octo

@@ -5,6 +5,8 @@
 
 #include <cstdint>
 
+#include "kernels.h"
+
 namespace octo {
 
 typedef __bf16 bf16;
@@ -91,6 +93,82 @@ __device__ __forceinline__ float row_sum8(bf16x8 v, float acc) {
     acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), ones, acc, false);
     acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), ones, acc, false);
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), ones, acc, false);
+}
+
+// ---------------------------------------------------------------- rotary embedding
+//
+// Rotate-half rotary embedding at a token's position (RopeFreq, kernels.h): feature
+// pairs (x_i, x_{i+D/2}) turn by pos * theta_i.
+
+// r^n for 0 <= n < 64 (binary powers; n is a compile-time constant plus a lane bit).
+__device__ __forceinline__ double ipow64(double r, int n) {
+    double out = 1.0, p = r;
+#pragma unroll
+    for (int b = 0; b < 6; ++b) {
+        if ((n >> b) & 1) out *= p;
+        p *= p;
+    }
+    return out;
+}
+
+// cos and sin of pair i's angle at position pos.  The angle in turns, pos * turn0 *
+// ratio^i, is reduced in float64 to a fraction f of a turn in [-1/2, 1/2]; then f = q/4 +
+// y/(2 pi) with q the nearest quarter turn and |y| <= pi/4, where the Taylor polynomials
+// of sin y (to y^9/9!) and cos y (to y^10/10!) are within 2e-9; the quarter turns are
+// applied exactly.  Straight-line code: no tables, no private memory.
+__device__ __forceinline__ void rope_angle(int pos, const RopeFreq& f, int i, float& c,
+                                           float& s) {
+    const double t = (double)pos * (f.turn0 * ipow64(f.ratio, i));
+    const float fr = (float)(t - rint(t));
+    const float q = rintf(4.f * fr);
+    const float y = (fr - 0.25f * q) * 6.283185307179586f;
+    const float y2 = y * y;
+    const float sy =
+        y * (1.f + y2 * (-1.f / 6 + y2 * (1.f / 120 + y2 * (-1.f / 5040 + y2 * (1.f / 362880)))));
+    const float cy =
+        1.f + y2 * (-0.5f + y2 * (1.f / 24 + y2 * (-1.f / 720 + y2 * (1.f / 40320 +
+                                                                       y2 * (-1.f / 3628800)))));
+    const int qi = (int)q & 3;
+    c = qi == 0 ? cy : qi == 1 ? -sy : qi == 2 ? -cy : sy;
+    s = qi == 0 ? sy : qi == 1 ? cy : qi == 2 ? -sy : -cy;
+}
+
+// Turn the query operand of one lane in place: qf[ks][e] holds feature 16 ks + 8 g + e
+// (the MFMA B-operand layout of one row), so the pair partner of ks < KS/2 is ks + KS/2
+// in the same lane.  sign = +1 turns forward, -1 back.
+template <int KS>
+__device__ __forceinline__ void rope_operand(bf16x8 (&qf)[KS], int pos, const RopeFreq& rf,
+                                             int g, float sign) {
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float c, s;
+            rope_angle(pos, rf, 16 * ks + 8 * g + e, c, s);
+            s *= sign;
+            const float a = (float)qf[ks][e], b = (float)qf[ks + KS / 2][e];
+            qf[ks][e] = (bf16)(a * c - b * s);
+            qf[ks + KS / 2][e] = (bf16)(b * c + a * s);
+        }
+}
+
+// Turn an accumulator tile in place: acc[db][j] holds feature 32 db + 8 (j / 4) + 4 g +
+// j % 4 of the lane's column (the MFMA result layout of a D x 32 transposed tile), so
+// the pair partner of db < DB/2 is db + DB/2 in the same lane.
+template <int DB>
+__device__ __forceinline__ void rope_accum(f32x16 (&acc)[DB], int pos, const RopeFreq& rf,
+                                           int g, float sign) {
+#pragma unroll
+    for (int db = 0; db < DB / 2; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            float c, s;
+            rope_angle(pos, rf, 32 * db + 8 * (j >> 2) + 4 * g + (j & 3), c, s);
+            s *= sign;
+            const float a = acc[db][j], b = acc[db + DB / 2][j];
+            acc[db][j] = a * c - b * s;
+            acc[db + DB / 2][j] = b * c + a * s;
+        }
 }
 
 constexpr float kLog2e = 1.4426950408889634f;

@@ -65,11 +65,13 @@ hipError_t launch_tiles_t(int T, int nKT, int Hkv, int D, const void* src, void*
     return hipGetLastError();
 }
 
-template <int D, int HPW>
+// With ROPE, Q is given unrotated and each lane turns its query row's operand in
+// registers at the row's plan position (K comes rotated).
+template <int D, int HPW, bool ROPE>
 __global__ __launch_bounds__(256 * HPW, 1) void fwd_bf16_kernel(
     DevPlan P, int Hq, int Hkv, float scale_log2, const bf16* __restrict__ Q,
     const bf16* __restrict__ K, const bf16* __restrict__ VX, bf16* __restrict__ O,
-    float* __restrict__ LSE) {
+    float* __restrict__ LSE, RopeFreq rt) {
     using L = KvLayout<D>;
     constexpr int NTHR = 256 * HPW;
     constexpr int KS = D / 16, DB = D / 32;
@@ -100,6 +102,9 @@ __global__ __launch_bounds__(256 * HPW, 1) void fwd_bf16_kernel(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
         qf[ks] = row < T ? ld16(Q + row * qstride + (size_t)h * D + 16 * ks + 8 * g) : zero8();
+    if constexpr (ROPE) {
+        if (row < T) rope_operand(qf, P.pos[row], rt, g, 1.f);
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) settle(qf[ks]);
 
@@ -274,24 +279,30 @@ __global__ __launch_bounds__(128) void fwd_fp32_kernel(DevPlan P, int Hq, int Hk
 
 template <int D, int HPW>
 static void fwd_bf16_launch(const DevPlan& p, int Hq, int Hkv, float sl2, const void* q,
-                            const void* k, const void* vx, void* o, float* lse, hipStream_t s) {
+                            const void* k, const void* vx, void* o, float* lse,
+                            const RopeFreq* rope, hipStream_t s) {
     const int G = Hq / Hkv;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, HPW>), dim3(xcd_grid(p.nQT * Hkv, G / HPW)),
-                       dim3(256 * HPW), 0, s, p, Hq, Hkv, sl2, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)vx, (bf16*)o, lse);
+    const dim3 grid(xcd_grid(p.nQT * Hkv, G / HPW)), block(256 * HPW);
+    const RopeFreq rt = rope ? *rope : RopeFreq{};
+    if (rope)
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, HPW, true>), grid, block, 0, s, p, Hq, Hkv, sl2,
+                           (const bf16*)q, (const bf16*)k, (const bf16*)vx, (bf16*)o, lse, rt);
+    else
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, HPW, false>), grid, block, 0, s, p, Hq, Hkv, sl2,
+                           (const bf16*)q, (const bf16*)k, (const bf16*)vx, (bf16*)o, lse, rt);
 }
 
 hipError_t launch_fwd_bf16(const DevPlan& p, int Hq, int Hkv, int D, float scale,
                            const void* q, const void* k, const void* vx, void* o, float* lse,
-                           hipStream_t s) {
+                           const RopeFreq* rope, hipStream_t s) {
     const float sl2 = scale * kLog2e;
     const bool pair = (Hq / Hkv) % 2 == 0;
     if (D == 128) {
-        if (pair) fwd_bf16_launch<128, 2>(p, Hq, Hkv, sl2, q, k, vx, o, lse, s);
-        else fwd_bf16_launch<128, 1>(p, Hq, Hkv, sl2, q, k, vx, o, lse, s);
+        if (pair) fwd_bf16_launch<128, 2>(p, Hq, Hkv, sl2, q, k, vx, o, lse, rope, s);
+        else fwd_bf16_launch<128, 1>(p, Hq, Hkv, sl2, q, k, vx, o, lse, rope, s);
     } else {
-        if (pair) fwd_bf16_launch<64, 2>(p, Hq, Hkv, sl2, q, k, vx, o, lse, s);
-        else fwd_bf16_launch<64, 1>(p, Hq, Hkv, sl2, q, k, vx, o, lse, s);
+        if (pair) fwd_bf16_launch<64, 2>(p, Hq, Hkv, sl2, q, k, vx, o, lse, rope, s);
+        else fwd_bf16_launch<64, 1>(p, Hq, Hkv, sl2, q, k, vx, o, lse, rope, s);
     }
     return hipGetLastError();
 }

@@ -33,6 +33,15 @@ struct DevPlan {
         *sc_level_br;
 };
 
+// Rotary-embedding frequencies of rotate-half pairs (x_i, x_{i+D/2}): pair i turns by
+// pos * theta_i radians, theta_i = base^(-2i/D), i.e. pos * turn0 * ratio^i full turns with
+// turn0 = 1 / (2 pi) and ratio = base^(-2/D).  Float64: pos * theta_0 reaches 2^24
+// radians, which only float64 reduces to a fraction of a turn without losing the angle.
+struct RopeFreq {
+    double turn0, ratio;
+};
+RopeFreq rope_freq(int D, float base);
+
 constexpr int kBq = 128;  // query rows per tile
 constexpr int kBk = 64;   // keys per KV tile
 
@@ -47,9 +56,11 @@ hipError_t launch_tiles_t(int T, int nKT, int Hkv, int D, const void* src, void*
                           hipStream_t s);
 
 // The bf16 forward reads V through `vx` (tiles_t layout, filled by the caller).
+// With `rope` (not NULL), q is unrotated and turned in registers at the plan positions;
+// k must come rotated.
 hipError_t launch_fwd_bf16(const DevPlan& p, int Hq, int Hkv, int D, float scale,
                            const void* q, const void* k, const void* vx, void* o, float* lse,
-                           hipStream_t s);
+                           const RopeFreq* rope, hipStream_t s);
 hipError_t launch_fwd_fp32(const DevPlan& p, int Hq, int Hkv, int D, float scale,
                            const void* q, const void* k, const void* v, void* o, float* lse,
                            hipStream_t s);
@@ -59,12 +70,15 @@ hipError_t launch_fwd_fp32(const DevPlan& p, int Hq, int Hkv, int D, float scale
 size_t bwd_workspace_floats(int T, int Hq);
 hipError_t launch_bwd_preprocess(bool bf16, const DevPlan& p, int Hq, int D, const void* o,
                                  const void* dout, const float* lse, float* ws, hipStream_t s);
+// With `rope` (bf16 only), q and k come rotated at the plan positions and dk (dq) is
+// turned back in registers before it is stored.
 hipError_t launch_bwd_dkdv(bool bf16, const DevPlan& p, int Hq, int Hkv, int D, float scale,
                            const void* q, const void* k, const void* v, const void* dout,
-                           const float* ws, void* dk, void* dv, hipStream_t s);
+                           const float* ws, void* dk, void* dv, const RopeFreq* rope,
+                           hipStream_t s);
 hipError_t launch_bwd_dq(bool bf16, const DevPlan& p, int Hq, int Hkv, int D, float scale,
                          const void* q, const void* k, const void* v, const void* dout,
-                         float* ws, void* dq, hipStream_t s);
+                         float* ws, void* dq, const RopeFreq* rope, hipStream_t s);
 // Decode: per-cursor segment lists 0..B-1, then (n_groups > 0) one shared list per group
 // of cursors (grp_ptr / grp_cur).  partial: float32 [B][2 n_split][Hq][D + 4].  `bf16`
 // selects the MFMA kernel, otherwise float32 pools and outputs.  D in {64, 128}.
