@@ -348,6 +348,32 @@ int octopus_paged_mount_decode(octopus_dtype dtype, int32_t B, int32_t Hq, int32
                                const int32_t* grp_cur, int32_t n_split, void* o, float* lse,
                                void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of device scratch octopus_paged_mount_decode_noalloc holds per GPU (48 MiB). */
+#define OCTOPUS_DECODE_SCRATCH_BYTES (48u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): octopus_paged_mount_decode with the
+ * partial softmax states kept in a device array of OCTOPUS_DECODE_SCRATCH_BYTES bytes
+ * that the library holds on every GPU it runs on until the process ends, instead of a
+ * caller workspace.  The array of the current device is used (the stream must belong to
+ * it); its address is looked up on the first call on each device.  The call allocates
+ * and frees nothing.  Calls on one GPU share its array: calls whose work overlaps on
+ * that GPU (several streams, or several host threads) race and give undefined results.
+ * The array keeps the last call's contents; nothing in it needs clearing, since every
+ * partial state a call reads was written by the same call.  Arguments, support and
+ * results as octopus_paged_mount_decode.
+ * Errors: as octopus_paged_mount_decode, EWORKSPACE when the partial states
+ * (octopus_decode_workspace_bytes) exceed OCTOPUS_DECODE_SCRATCH_BYTES (nothing is
+ * enqueued), EHIP if the array's address cannot be looked up. */
+int octopus_paged_mount_decode_noalloc(octopus_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                       int32_t D, int32_t page_size, float scale, const void* q,
+                                       const void* k_pool, const void* v_pool, int32_t n_pages,
+                                       const int32_t* seg_ptr, const int32_t* seg_page,
+                                       const int32_t* seg_lo, const int32_t* seg_hi,
+                                       int32_t n_groups, const int32_t* grp_ptr,
+                                       const int32_t* grp_cur, int32_t n_split, void* o,
+                                       float* lse, void* stream);
+
 /* ---------------------------------------------------------------- paged extend */
 
 /* Host helper for extend (prefill of several new tokens per cursor: a continuation

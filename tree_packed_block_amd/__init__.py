@@ -10,6 +10,7 @@ ancestor, own and mounted pages, as described on the Octopus project page (secti
 
 from ._lib import (  # noqa: F401
     BF16,
+    DECODE_SCRATCH_BYTES,
     FP32,
     EXPORTS,
     LIB_PATH,
@@ -33,5 +34,6 @@ from ._lib import (  # noqa: F401
     fwd_workspace_bytes,
     lib,
     paged_mount_decode,
+    paged_mount_decode_noalloc,
     paged_mount_extend,
 )

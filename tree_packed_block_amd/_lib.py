@@ -21,6 +21,7 @@ OK, EINVAL, ECYCLE, EUNSUPPORTED, ENOMEM, EWORKSPACE, EHIP, ESTATE = 0, -1, -2, 
 _NAMES = {EINVAL: "EINVAL", ECYCLE: "ECYCLE", EUNSUPPORTED: "EUNSUPPORTED",
           ENOMEM: "ENOMEM", EWORKSPACE: "EWORKSPACE", EHIP: "EHIP", ESTATE: "ESTATE"}
 BF16, FP32 = 0, 1
+DECODE_SCRATCH_BYTES = 48 << 20  # OCTOPUS_DECODE_SCRATCH_BYTES
 
 # Every symbol include/octopus_dag.h declares.
 EXPORTS = [
@@ -29,7 +30,8 @@ EXPORTS = [
     "octopus_plan_export_tiles", "octopus_plan_destroy", "octopus_fwd_workspace_bytes", "octopus_dag_attn_fwd",
     "octopus_bwd_workspace_bytes", "octopus_dag_attn_bwd", "octopus_dag_attn_bwd_preprocess",
     "octopus_dag_attn_bwd_dkdv", "octopus_dag_attn_bwd_dq", "octopus_decode_segments",
-    "octopus_decode_workspace_bytes", "octopus_paged_mount_decode", "octopus_extend_segments",
+    "octopus_decode_workspace_bytes", "octopus_paged_mount_decode",
+    "octopus_paged_mount_decode_noalloc", "octopus_extend_segments",
     "octopus_paged_mount_extend", "octopus_dag_positions", "octopus_rope",
     "octopus_rope_workspace_bytes", "octopus_dag_attn_fwd_rope", "octopus_dag_attn_bwd_rope",
     "octopus_gdn_workspace_bytes", "octopus_gated_delta_scan", "octopus_last_error",
@@ -109,6 +111,7 @@ def lib():
                                              _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp,
                                              ctypes.c_int32, _vp, _vp, _vp, ctypes.c_size_t,
                                              _vp]
+    L.octopus_paged_mount_decode_noalloc.argtypes = L.octopus_paged_mount_decode.argtypes[:-3] + [_vp]
     L.octopus_extend_segments.argtypes = [_vp, ctypes.c_int32, _vp, ctypes.c_int32, _vp, _vp,
                                           ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int32,
                                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
@@ -604,6 +607,55 @@ def paged_mount_decode(q, k_pool, v_pool, seg_ptr, seg_page, seg_lo, seg_hi, grp
         k_pool.data_ptr(), v_pool.data_ptr(), n_pages, seg_ptr.data_ptr(), seg_page.data_ptr(),
         seg_lo.data_ptr(), seg_hi.data_ptr(), n_groups, gp, gc, int(n_split), o.data_ptr(),
         lse.data_ptr(), ws.data_ptr(), ws.numel(), _vp(s.cuda_stream)))
+    return o, lse
+
+
+def paged_mount_decode_noalloc(q, k_pool, v_pool, seg_ptr, seg_page, seg_lo, seg_hi,
+                               grp_ptr=None, grp_cur=None, n_split=16, scale=None, o=None,
+                               lse=None, stream=None):
+    """``paged_mount_decode`` through the entry point that allocates no device memory:
+    the partial states live in the library's per-GPU scratch array (at most
+    ``DECODE_SCRATCH_BYTES``; calls that overlap on one GPU race).  Pass ``o`` and
+    ``lse`` to allocate nothing here either."""
+    import torch
+    B, Hq, D = q.shape
+    n_pages, Hkv, page_size, _ = k_pool.shape
+    _need(q, (B, Hq, D), q.dtype, "q")
+    _need(k_pool, (n_pages, Hkv, page_size, D), q.dtype, "k_pool")
+    _need(v_pool, (n_pages, Hkv, page_size, D), q.dtype, "v_pool")
+    arrays = [(seg_ptr, "seg_ptr"), (seg_page, "seg_page"), (seg_lo, "seg_lo"),
+              (seg_hi, "seg_hi")]
+    if (grp_ptr is None) != (grp_cur is None):
+        raise OctopusError(EINVAL, "grp_ptr and grp_cur go together")
+    n_groups = 0
+    if grp_ptr is not None:
+        arrays += [(grp_ptr, "grp_ptr"), (grp_cur, "grp_cur")]
+        n_groups = grp_ptr.numel() - 1
+        if grp_cur.numel() != B:
+            raise OctopusError(EINVAL, "grp_cur must have B entries")
+    for t, nm in arrays:
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise OctopusError(EINVAL, f"{nm} must be a contiguous int32 device tensor")
+    if seg_ptr.numel() != B + n_groups + 1:
+        raise OctopusError(EINVAL, "seg_ptr must have B + n_groups + 1 entries")
+    s = _stream(stream, q.device)
+    mine = []
+    if o is None:
+        o = torch.empty_like(q)
+        mine.append(o)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        mine.append(lse)
+    _need(o, q.shape, q.dtype, "o")
+    _need(lse, (B, Hq), torch.float32, "lse")
+    _owned(s, *mine)
+    gp = grp_ptr.data_ptr() if grp_ptr is not None else None
+    gc = grp_cur.data_ptr() if grp_cur is not None else None
+    _check(lib().octopus_paged_mount_decode_noalloc(
+        _dtype_code(q), B, Hq, Hkv, D, page_size, float(scale or 0.0), q.data_ptr(),
+        k_pool.data_ptr(), v_pool.data_ptr(), n_pages, seg_ptr.data_ptr(), seg_page.data_ptr(),
+        seg_lo.data_ptr(), seg_hi.data_ptr(), n_groups, gp, gc, int(n_split), o.data_ptr(),
+        lse.data_ptr(), _vp(s.cuda_stream)))
     return o, lse
 
 

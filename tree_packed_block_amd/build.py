@@ -22,7 +22,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liboctopus_dag.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-HIP_SOURCES = ["fwd.hip", "bwd.hip", "decode.hip", "extend.hip", "rope.hip", "scan.hip"]
+HIP_SOURCES = ["fwd.hip", "bwd.hip", "decode.hip", "extend.hip", "rope.hip", "scan.hip",
+               "noalloc.hip"]
 CXX_SOURCES = ["plan.cpp", "api.cpp"]
 
 HIPCC_FLAGS = [

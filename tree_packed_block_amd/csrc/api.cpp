@@ -616,13 +616,14 @@ size_t octopus_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t 
     return (size_t)B * 2 * n_split * Hq * (D + 4) * sizeof(float);
 }
 
-int octopus_paged_mount_decode(octopus_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
-                               int32_t D, int32_t page_size, float scale, const void* q,
-                               const void* k_pool, const void* v_pool, int32_t n_pages,
-                               const int32_t* seg_ptr, const int32_t* seg_page,
-                               const int32_t* seg_lo, const int32_t* seg_hi, int32_t n_groups,
-                               const int32_t* grp_ptr, const int32_t* grp_cur, int32_t n_split,
-                               void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+// Argument checks shared by the two decode entry points (nothing is enqueued on error).
+int check_decode(octopus_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                 int32_t page_size, const void* q, const void* k_pool, const void* v_pool,
+                 int32_t n_pages, const int32_t* seg_ptr, const int32_t* seg_page,
+                 const int32_t* seg_lo, const int32_t* seg_hi, int32_t n_groups,
+                 const int32_t* grp_ptr, const int32_t* grp_cur, int32_t n_split, void* o) {
     if (dtype != OCTOPUS_BF16 && dtype != OCTOPUS_FP32)
         return fail(OCTOPUS_EUNSUPPORTED, "dtype must be bf16 or fp32");
     if (D != 64 && D != 128) return fail(OCTOPUS_EUNSUPPORTED, "head_dim must be 64 or 128");
@@ -641,6 +642,22 @@ int octopus_paged_mount_decode(octopus_dtype dtype, int32_t B, int32_t Hq, int32
     if (n_groups < 0 || n_groups > B) return fail(OCTOPUS_EINVAL, "n_groups must be in [0, B]");
     if (n_groups > 0 && (!grp_ptr || !grp_cur))
         return fail(OCTOPUS_EINVAL, "group arrays must not be NULL");
+    return OCTOPUS_OK;
+}
+
+}  // namespace
+
+int octopus_paged_mount_decode(octopus_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                               int32_t D, int32_t page_size, float scale, const void* q,
+                               const void* k_pool, const void* v_pool, int32_t n_pages,
+                               const int32_t* seg_ptr, const int32_t* seg_page,
+                               const int32_t* seg_lo, const int32_t* seg_hi, int32_t n_groups,
+                               const int32_t* grp_ptr, const int32_t* grp_cur, int32_t n_split,
+                               void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+    const int rc = check_decode(dtype, B, Hq, Hkv, D, page_size, q, k_pool, v_pool, n_pages,
+                                seg_ptr, seg_page, seg_lo, seg_hi, n_groups, grp_ptr, grp_cur,
+                                n_split, o);
+    if (rc != OCTOPUS_OK) return rc;
     const size_t need = octopus_decode_workspace_bytes(B, Hq, D, n_split);
     if (ws == nullptr || ws_bytes < need || !aligned(ws, 16))
         return fail(OCTOPUS_EWORKSPACE, "decode workspace needs " + std::to_string(need) +
@@ -650,6 +667,37 @@ int octopus_paged_mount_decode(octopus_dtype dtype, int32_t B, int32_t Hq, int32
                                        q, k_pool, v_pool, n_pages, seg_ptr, seg_page, seg_lo,
                                        seg_hi, n_groups, grp_ptr, grp_cur, n_split, o, lse,
                                        static_cast<float*>(ws), (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return ok();
+}
+
+int octopus_paged_mount_decode_noalloc(octopus_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                       int32_t D, int32_t page_size, float scale, const void* q,
+                                       const void* k_pool, const void* v_pool, int32_t n_pages,
+                                       const int32_t* seg_ptr, const int32_t* seg_page,
+                                       const int32_t* seg_lo, const int32_t* seg_hi,
+                                       int32_t n_groups, const int32_t* grp_ptr,
+                                       const int32_t* grp_cur, int32_t n_split, void* o,
+                                       float* lse, void* stream) {
+    const int rc = check_decode(dtype, B, Hq, Hkv, D, page_size, q, k_pool, v_pool, n_pages,
+                                seg_ptr, seg_page, seg_lo, seg_hi, n_groups, grp_ptr, grp_cur,
+                                n_split, o);
+    if (rc != OCTOPUS_OK) return rc;
+    const size_t need = octopus_decode_workspace_bytes(B, Hq, D, n_split);
+    if (need > (size_t)OCTOPUS_DECODE_SCRATCH_BYTES)
+        return fail(OCTOPUS_EWORKSPACE,
+                    "decode partial states need " + std::to_string(need) +
+                        " bytes; the no-allocation entry point holds at most " +
+                        std::to_string((size_t)OCTOPUS_DECODE_SCRATCH_BYTES) +
+                        " (fewer splits or cursors per call)");
+    void* scratch = nullptr;
+    hipError_t e = octo::decode_scratch(&scratch);
+    if (e != hipSuccess) return hip_fail(e, "decode scratch lookup");
+    if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
+    e = octo::launch_decode(dtype == OCTOPUS_BF16, B, Hq, Hkv, D, page_size, scale, q, k_pool,
+                            v_pool, n_pages, seg_ptr, seg_page, seg_lo, seg_hi, n_groups, grp_ptr,
+                            grp_cur, n_split, o, lse, static_cast<float*>(scratch),
+                            (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return ok();
 }

@@ -89,6 +89,11 @@ hipError_t launch_decode(bool bf16, int B, int Hq, int Hkv, int D, int page_size
                          const int32_t* grp_ptr, const int32_t* grp_cur, int n_split, void* o,
                          float* lse, float* partial, hipStream_t s);
 
+// Address of this device's scratch array of OCTOPUS_DECODE_SCRATCH_BYTES bytes (the
+// current device; looked up once per device and kept).  Used by the decode entry point
+// that allocates nothing.
+hipError_t decode_scratch(void** ptr);
+
 // Rotary embedding in place or out of place: x is [rows][H][D] (bf16 if `bf16`, else
 // float32); row r turns by pos[r] * base^(-2i/D) on pairs (i, i + D/2), by the opposite
 // angle if `inverse`.  out may equal x.
