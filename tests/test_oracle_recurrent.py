@@ -122,3 +122,92 @@ def test_beta_zero_keeps_state_and_alpha_gates():
     o, final = RC.scan(q, k, v, a, b, branches)
     np.testing.assert_allclose(final[1], 0.125 * final[0], atol=1e-12)
     np.testing.assert_allclose(o[7, 0], final[1][0] @ q[7, 0], atol=1e-12)
+
+
+# ---------------------------------------------------------------------------- backward
+
+def test_backward_one_token_hand_derived():
+    """From S_0 = 0 one token gives o = b (k.q) v, so with upstream g:
+    dq = b (g.v) k, dk = b (g.v) q, dv = b (k.q) g, db = (k.q)(g.v), da = 0."""
+    k = np.array([[[0.6, 0.8]]]); q = np.array([[[1.0, 2.0]]]); v = np.array([[[2.0, -1.0]]])
+    g = np.array([[[0.5, 3.0]]])
+    a = np.array([[0.3]]); b = np.array([[0.5]])
+    dq, dk, dv, da, db = RC.scan_bwd(q, k, v, a, b, g, np.array([[-1, 0, 0, 1]]))
+    gv, kq = -2.0, 2.2  # g.v = 1 - 3, k.q = 0.6 + 1.6
+    np.testing.assert_allclose(dq[0, 0], 0.5 * gv * np.array([0.6, 0.8]), atol=1e-14)
+    np.testing.assert_allclose(dk[0, 0], 0.5 * gv * np.array([1.0, 2.0]), atol=1e-14)
+    np.testing.assert_allclose(dv[0, 0], 0.5 * kq * np.array([0.5, 3.0]), atol=1e-14)
+    np.testing.assert_allclose(db[0, 0], kq * gv, atol=1e-14)
+    np.testing.assert_allclose(da[0, 0], 0.0, atol=1e-14)
+
+
+def _loss(q, k, v, a, b, do, branches):
+    o, _ = RC.scan(q, k, v, a, b, branches)
+    return float(np.sum(o * do))
+
+
+def test_backward_finite_differences():
+    """Central differences of L = sum <dO, o> through forks (children forked at 0, inside
+    and at the end of their parents) for every input."""
+    for seed in range(3):
+        rng = np.random.default_rng(40 + seed)
+        dag = synth.fuzz_dag(rng, max_len=7, max_branches=5, max_mounts=2)
+        q, k, v, a, b = _inputs(rng, dag.T, 2, 3, 4)
+        do = rng.standard_normal(v.shape)
+        grads = RC.scan_bwd(q, k, v, a, b, do, dag.branches, segment=3)
+        eps = 1e-6
+        for which, arr in enumerate((q, k, v, a, b)):
+            for _ in range(4):
+                idx = tuple(int(rng.integers(0, n)) for n in arr.shape)
+                xs = [x.copy() for x in (q, k, v, a, b)]
+                xs[which][idx] += eps
+                lp = _loss(*xs, do, dag.branches)
+                xs[which][idx] -= 2 * eps
+                lm = _loss(*xs, do, dag.branches)
+                fd = (lp - lm) / (2 * eps)
+                assert abs(fd - grads[which][idx]) < 1e-6 * max(1.0, abs(fd)), (which, idx)
+
+
+def test_backward_equals_autograd_over_flattened_paths():
+    """An independent formulation: every branch runs the plain recurrence over its whole
+    flattened root-to-branch path in torch (float64, CPU) and contributes the outputs of its
+    own tokens; torch.autograd of the summed loss must equal the packed backward (shared
+    prefix tokens collect the gradients of every branch that passes through them)."""
+    import torch
+    for seed in range(3):
+        rng = np.random.default_rng(60 + seed)
+        dag = synth.fuzz_dag(rng, max_len=10, max_branches=6, max_mounts=2)
+        q, k, v, a, b = _inputs(rng, dag.T, 2, 4, 3)
+        do = rng.standard_normal(v.shape)
+        tq, tk, tv, ta, tb = (torch.tensor(x, dtype=torch.float64, requires_grad=True)
+                              for x in (q, k, v, a, b))
+        tdo = torch.tensor(do, dtype=torch.float64)
+        loss = torch.zeros((), dtype=torch.float64)
+        for br in range(dag.nb):
+            idx = RC.path_tokens(dag.branches, br)
+            L = int(dag.branches[br, 3])
+            S = torch.zeros((2, 3, 4), dtype=torch.float64)
+            for j, t in enumerate(idx):
+                Sk = torch.einsum("hij,hj->hi", S, tk[t])
+                S = ta[t][:, None, None] * (S - tb[t][:, None, None] * Sk[:, :, None]
+                                            * tk[t][:, None, :]) \
+                    + tb[t][:, None, None] * tv[t][:, :, None] * tk[t][:, None, :]
+                if j >= len(idx) - L:
+                    loss = loss + torch.sum(torch.einsum("hij,hj->hi", S, tq[t]) * tdo[t])
+        loss.backward()
+        ours = RC.scan_bwd(q, k, v, a, b, do, dag.branches, segment=4)
+        for got, ref in zip(ours, (tq.grad, tk.grad, tv.grad, ta.grad, tb.grad)):
+            np.testing.assert_allclose(got, ref.numpy(), rtol=1e-10, atol=1e-11)
+
+
+def test_backward_segment_size_does_not_matter():
+    rng = np.random.default_rng(80)
+    dag = synth.fuzz_dag(rng, max_len=40, max_branches=6, max_mounts=2)
+    q, k, v, a, b = _inputs(rng, dag.T, 1, 4, 4)
+    do = rng.standard_normal(v.shape)
+    g1 = RC.scan_bwd(q, k, v, a, b, do, dag.branches, segment=1)
+    g2 = RC.scan_bwd(q, k, v, a, b, do, dag.branches, segment=7)
+    g3 = RC.scan_bwd(q, k, v, a, b, do, dag.branches)
+    for x, y, z in zip(g1, g2, g3):
+        np.testing.assert_array_equal(x, y)
+        np.testing.assert_array_equal(x, z)
