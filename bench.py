@@ -140,7 +140,8 @@ KERNEL_KEYS = (("fwd_bf16_kernel", "fwd"), ("tiles_t_kernel", "fwd"),
                ("preprocess_bf16_kernel", "bwd_preprocess"),
                ("dkdv_bf16_kernel", "bwd_dkdv"), ("dq_bf16_kernel", "bwd_dq"),
                ("decode_split_kernel", "decode"), ("decode_combine_kernel", "decode"),
-               ("rope_kernel", "rope"), ("gdn_scan_kernel", "gdn_scan"))
+               ("rope_kernel", "rope"), ("gdn_chunk_fwd_kernel", "gdn_scan"),
+               ("gdn_chunk_bwd_kernel", "gdn_scan_bwd"))
 CALIBRATION_BYTES = 1 << 30  # the --calibrate-copy transfer
 
 
@@ -555,27 +556,28 @@ def main():
     for n in ("q", "k", "v"):
         ts[n] = ts[n].to(torch.bfloat16)
     os_ = torch.empty_like(ts["v"])
+    dos = (torch.randn(ts["v"].shape, generator=torch.Generator(device=dev).manual_seed(23),
+                       device=dev) * 0.5).to(torch.bfloat16)
+    grads = [torch.empty_like(ts[n]) for n in ("q", "k", "v", "alpha", "beta")]
     wss = torch.empty(max(tpb.gdn_workspace_bytes(probe, H_s), 16), dtype=torch.uint8,
                       device=dev)
+    wsb = torch.empty(max(tpb.gdn_bwd_workspace_bytes(probe, H_s), 16), dtype=torch.uint8,
+                      device=dev)
     plan_s = tpb.Plan(dag.branches, dag.mounts, dag.T).upload()
-
-    def run_scan():
-        tpb.gated_delta_scan(plan_s, ts["q"], ts["k"], ts["v"], ts["alpha"], ts["beta"],
-                             o=os_, ws=wss)
-
-    run_scan()
-    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    ev_s[0].record(stream)
-    for j in range(3):
-        run_scan()
-        ev_s[j + 1].record(stream)
-    torch.cuda.synchronize()
-    ms_s = float(np.median([ev_s[j].elapsed_time(ev_s[j + 1]) for j in range(3)]))
+    ms_s = clock(lambda: tpb.gated_delta_scan(plan_s, ts["q"], ts["k"], ts["v"], ts["alpha"],
+                                              ts["beta"], o=os_, ws=wss))
+    ms_sb = clock(lambda: tpb.gated_delta_scan_bwd(plan_s, ts["q"], ts["k"], ts["v"],
+                                                   ts["alpha"], ts["beta"], dos, *grads,
+                                                   ws=wsb))
     flops_s = 6.0 * 128 * 128 * H_s * dag.T
     out["breakdown"]["gdn_scan"] = {
-        "ms": round(ms_s, 3), "GFLOP/s": round(flops_s / (ms_s * 1e-3) / 1e9, 1),
-        "note": "16 heads, 128x128 state, 6*Dk*Dv FLOP per token-head; sequential along "
-                "each branch (critical path: root + longest worker)"}
+        "fwd_ms": round(ms_s, 3), "fwd_GFLOP/s": round(flops_s / (ms_s * 1e-3) / 1e9, 1),
+        "bwd_ms": round(ms_sb, 3),
+        "note": "16 heads, 128x128 state, 32-token chunks on the matrix cores; rate on "
+                "6*Dk*Dv FLOP per token-head of the recurrence; the backward recomputes the "
+                "forward (states at chunk starts) and is timed whole; sequential along each "
+                "branch (critical path: root + longest worker)"}
+    del wsb
 
     if not args.no_cpu_baseline:
         log("cpu baseline (float64 oracle on a sample) ...")

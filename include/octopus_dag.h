@@ -278,13 +278,35 @@ size_t octopus_gdn_workspace_bytes(const octopus_plan* plan, int32_t H, int32_t 
  * over each branch's own tokens in order, a root from S = 0, a child from its parent's
  * state just before the parent's own token `fork`; mounts are ignored.
  * q, k [T][H][Dk], v, o [T][H][Dv] (dtype); alpha, beta float32 [T][H] (device).
- * The plan must be uploaded.  Levels of the tree run one launch each, in order.
+ * alpha in (0, 1] (values below 2^-100 act as 2^-100), beta in [0, 1].
+ * The plan must be uploaded.  Levels of the tree run one launch each, in order; every
+ * branch is taken 32 tokens at a time on the matrix cores (chunks also end at every fork
+ * offset), one workgroup per (branch, head).
  * Supported: bf16, Dk = Dv = 128.  Errors: EINVAL, ESTATE, EUNSUPPORTED, EWORKSPACE,
  * EHIP. */
 int octopus_gated_delta_scan(const octopus_plan* plan, octopus_dtype dtype, int32_t H,
                              int32_t Dk, int32_t Dv, const void* q, const void* k,
                              const void* v, const float* alpha, const float* beta, void* o,
                              void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of octopus_gated_delta_scan_bwd: float32 checkpoint slots, the state at
+ * the start of every chunk of the plan (32-token chunks, split at fork offsets), and
+ * gradient slots, each H x Dv x Dk. */
+size_t octopus_gdn_bwd_workspace_bytes(const octopus_plan* plan, int32_t H, int32_t Dk,
+                                       int32_t Dv);
+
+/* Backward of octopus_gated_delta_scan: gradients of L = sum_t <dout_t, o_t> with respect
+ * to q, k, v (written, [T][H][D] bf16) and to alpha, beta (written, [T][H] float32).  The
+ * gradient of a child's initial state (its parent's state at the fork) flows into the
+ * parent's earlier tokens; mounted spans receive nothing (the recurrent layers skip them;
+ * project page, primitives table).  Recomputes the forward chunk by chunk (the states at
+ * chunk starts go to the workspace), then walks every branch's chunks in reverse, deepest
+ * branches first.  Same support and errors as octopus_gated_delta_scan. */
+int octopus_gated_delta_scan_bwd(const octopus_plan* plan, octopus_dtype dtype, int32_t H,
+                                 int32_t Dk, int32_t Dv, const void* q, const void* k,
+                                 const void* v, const float* alpha, const float* beta,
+                                 const void* dout, void* dq, void* dk, void* dv, float* dalpha,
+                                 float* dbeta, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- paged decode */
 

@@ -29,6 +29,8 @@ from ._lib import (  # noqa: F401
     decode_workspace_bytes,
     extend_segments,
     gated_delta_scan,
+    gated_delta_scan_bwd,
+    gdn_bwd_workspace_bytes,
     gdn_workspace_bytes,
     default_scale,
     fwd_workspace_bytes,

@@ -34,7 +34,8 @@ EXPORTS = [
     "octopus_paged_mount_decode_noalloc", "octopus_extend_segments",
     "octopus_paged_mount_extend", "octopus_dag_positions", "octopus_rope",
     "octopus_rope_workspace_bytes", "octopus_dag_attn_fwd_rope", "octopus_dag_attn_bwd_rope",
-    "octopus_gdn_workspace_bytes", "octopus_gated_delta_scan", "octopus_last_error",
+    "octopus_gdn_workspace_bytes", "octopus_gated_delta_scan",
+    "octopus_gdn_bwd_workspace_bytes", "octopus_gated_delta_scan_bwd", "octopus_last_error",
     "octopus_version",
 ]
 
@@ -141,6 +142,11 @@ def lib():
     L.octopus_gated_delta_scan.argtypes = [_vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                            ctypes.c_size_t, _vp]
+    L.octopus_gdn_bwd_workspace_bytes.argtypes = L.octopus_gdn_workspace_bytes.argtypes
+    L.octopus_gdn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.octopus_gated_delta_scan_bwd.argtypes = [_vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int32] + [_vp] * 11 + [_vp,
+                                                                                ctypes.c_size_t, _vp]
     L.octopus_last_error.restype = ctypes.c_char_p
     L.octopus_version.restype = ctypes.c_char_p
     _lib = L
@@ -517,6 +523,52 @@ def gated_delta_scan(plan: Plan, q, k, v, alpha, beta, o=None, ws=None, stream=N
                                           beta.data_ptr(), o.data_ptr(), ws.data_ptr(),
                                           ws.numel(), _vp(s.cuda_stream)))
     return o
+
+
+def gdn_bwd_workspace_bytes(plan: Plan, H, Dk=128, Dv=128) -> int:
+    return int(lib().octopus_gdn_bwd_workspace_bytes(plan.handle, H, Dk, Dv))
+
+
+def gated_delta_scan_bwd(plan: Plan, q, k, v, alpha, beta, dout, dq=None, dk=None, dv=None,
+                         dalpha=None, dbeta=None, ws=None, stream=None):
+    """Backward of ``gated_delta_scan``: returns ``(dq, dk, dv, dalpha, dbeta)``."""
+    import torch
+    T, H, Dk = q.shape
+    Dv = v.shape[2]
+    _need(q, (plan.T, H, Dk), q.dtype, "q")
+    _need(k, (plan.T, H, Dk), q.dtype, "k")
+    _need(v, (plan.T, H, Dv), q.dtype, "v")
+    _need(dout, (plan.T, H, Dv), q.dtype, "dout")
+    _need(alpha, (plan.T, H), torch.float32, "alpha")
+    _need(beta, (plan.T, H), torch.float32, "beta")
+    s = _stream(stream, q.device)
+    mine = []
+    if dq is None:
+        dq = torch.empty_like(q)
+        mine.append(dq)
+    if dk is None:
+        dk = torch.empty_like(k)
+        mine.append(dk)
+    if dv is None:
+        dv = torch.empty_like(v)
+        mine.append(dv)
+    if dalpha is None:
+        dalpha = torch.empty_like(alpha)
+        mine.append(dalpha)
+    if dbeta is None:
+        dbeta = torch.empty_like(beta)
+        mine.append(dbeta)
+    if ws is None:
+        ws = torch.empty(max(gdn_bwd_workspace_bytes(plan, H, Dk, Dv), 16), dtype=torch.uint8,
+                         device=q.device)
+        mine.append(ws)
+    _owned(s, *mine)
+    _check(lib().octopus_gated_delta_scan_bwd(
+        plan.handle, _dtype_code(q), H, Dk, Dv, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+        alpha.data_ptr(), beta.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+        dv.data_ptr(), dalpha.data_ptr(), dbeta.data_ptr(), ws.data_ptr(), ws.numel(),
+        _vp(s.cuda_stream)))
+    return dq, dk, dv, dalpha, dbeta
 
 
 # ----------------------------------------------------------------------------- decode

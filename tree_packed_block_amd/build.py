@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liboctopus_dag.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-HIP_SOURCES = ["fwd.hip", "bwd.hip", "decode.hip", "extend.hip", "rope.hip", "scan.hip",
+HIP_SOURCES = ["fwd.hip", "bwd.hip", "decode.hip", "extend.hip", "rope.hip", "scan_chunk.hip",
                "noalloc.hip"]
 CXX_SOURCES = ["plan.cpp", "api.cpp"]
 

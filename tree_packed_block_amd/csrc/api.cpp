@@ -66,6 +66,7 @@ octo::DevPlan dev_view(const octo::Plan& p) {
     d.sc_ck_off = reinterpret_cast<const int32_t*>(base + p.layout.sc_ck_off);
     d.sc_ck_slot = reinterpret_cast<const int32_t*>(base + p.layout.sc_ck_slot);
     d.sc_level_br = reinterpret_cast<const int32_t*>(base + p.layout.sc_level_br);
+    d.sc_chunk_base = reinterpret_cast<const int32_t*>(base + p.layout.sc_chunk_base);
     return d;
 }
 
@@ -526,10 +527,61 @@ int octopus_gated_delta_scan(const octopus_plan* plan, octopus_dtype dtype, int3
     const octo::DevPlan dp = dev_view(plan->p);
     const std::vector<int32_t>& lp = plan->p.level_ptr;
     for (size_t l = 0; l + 1 < lp.size(); ++l) {
-        const hipError_t e = octo::launch_gdn_scan(dp, lp[l], lp[l + 1] - lp[l], H, q, k, v,
-                                                   alpha, beta, o, static_cast<float*>(ws),
-                                                   (hipStream_t)stream);
+        const hipError_t e = octo::launch_gdn_chunk_fwd(dp, lp[l], lp[l + 1] - lp[l], H, q, k, v,
+                                                        alpha, beta, o, static_cast<float*>(ws),
+                                                        nullptr, (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail(e, "scan launch");
+    }
+    return ok();
+}
+
+size_t octopus_gdn_bwd_workspace_bytes(const octopus_plan* plan, int32_t H, int32_t Dk,
+                                       int32_t Dv) {
+    if (plan == nullptr || H < 1 || Dk != 128 || Dv != 128) return 0;
+    const size_t per = (size_t)H * Dv * Dk * sizeof(float);
+    return per * ((size_t)2 * std::max(plan->p.n_slots, 1) + (size_t)plan->p.n_chunks);
+}
+
+int octopus_gated_delta_scan_bwd(const octopus_plan* plan, octopus_dtype dtype, int32_t H,
+                                 int32_t Dk, int32_t Dv, const void* q, const void* k,
+                                 const void* v, const float* alpha, const float* beta,
+                                 const void* dout, void* dq, void* dk, void* dv, float* dalpha,
+                                 float* dbeta, void* ws, size_t ws_bytes, void* stream) {
+    if (plan == nullptr) return fail(OCTOPUS_EINVAL, "plan is NULL");
+    if (plan->p.dev == nullptr) return fail(OCTOPUS_ESTATE, "plan not uploaded");
+    if (dtype != OCTOPUS_BF16) return fail(OCTOPUS_EUNSUPPORTED, "the scan supports bf16 only");
+    if (Dk != 128 || Dv != 128) return fail(OCTOPUS_EUNSUPPORTED, "the scan supports Dk = Dv = 128");
+    if (H < 1) return fail(OCTOPUS_EINVAL, "H must be >= 1");
+    for (const void* p : {q, k, v, (const void*)alpha, (const void*)beta, dout,
+                          (const void*)dq, (const void*)dk, (const void*)dv,
+                          (const void*)dalpha, (const void*)dbeta}) {
+        if (p == nullptr) return fail(OCTOPUS_EINVAL, "a tensor pointer is NULL");
+        if (!aligned(p, 16)) return fail(OCTOPUS_EINVAL, "tensors must be 16-byte aligned");
+    }
+    const size_t need = octopus_gdn_bwd_workspace_bytes(plan, H, Dk, Dv);
+    if (ws == nullptr || ws_bytes < need || !aligned(ws, 16))
+        return fail(OCTOPUS_EWORKSPACE, "scan backward workspace needs " + std::to_string(need) +
+                                            " bytes, 16-byte aligned");
+    const octo::DevPlan dp = dev_view(plan->p);
+    const std::vector<int32_t>& lp = plan->p.level_ptr;
+    hipStream_t st = (hipStream_t)stream;
+    const size_t per = (size_t)H * Dv * Dk;  // floats per slot or chunk state
+    float* slots = static_cast<float*>(ws);
+    float* chunks = slots + per * std::max(plan->p.n_slots, 1);
+    float* dslots = chunks + per * (size_t)plan->p.n_chunks;
+    // the forward again, keeping the state at the start of every chunk
+    for (size_t l = 0; l + 1 < lp.size(); ++l) {
+        const hipError_t e = octo::launch_gdn_chunk_fwd(dp, lp[l], lp[l + 1] - lp[l], H, q, k, v,
+                                                        alpha, beta, nullptr, slots, chunks, st);
+        if (e != hipSuccess) return hip_fail(e, "scan backward (forward pass) launch");
+    }
+    hipError_t e = octo::launch_fill_zero(dslots, per * std::max(plan->p.n_slots, 1), st);
+    if (e != hipSuccess) return hip_fail(e, "scan backward (clear) launch");
+    // deepest level first: a child's initial-state gradient reaches its parent's slot
+    for (size_t l = lp.size() - 1; l-- > 0;) {
+        e = octo::launch_gdn_chunk_bwd(dp, lp[l], lp[l + 1] - lp[l], H, q, k, v, alpha, beta,
+                                       dout, chunks, dslots, dq, dk, dv, dalpha, dbeta, st);
+        if (e != hipSuccess) return hip_fail(e, "scan backward launch");
     }
     return ok();
 }

@@ -550,6 +550,24 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
             }
             p.sc_ck_ptr.push_back((int32_t)p.sc_ck_off.size());
         }
+        // Chunks of the chunked scan: boundaries every kScanChunk own tokens and at every
+        // checkpoint offset inside the branch (the kernel walks the same rule).
+        p.sc_chunk_base.assign(nb + 1, 0);
+        for (int32_t b = 0; b < nb; ++b) {
+            const int32_t len = d.br[b].len;
+            int32_t c = p.sc_ck_ptr[b];
+            int32_t r = 0, count = 0;
+            while (c < p.sc_ck_ptr[b + 1] && p.sc_ck_off[c] <= r) ++c;
+            while (r < len) {
+                int32_t e = std::min(len, (r / kScanChunk + 1) * kScanChunk);
+                if (c < p.sc_ck_ptr[b + 1]) e = std::min(e, p.sc_ck_off[c]);
+                r = e;
+                ++count;
+                while (c < p.sc_ck_ptr[b + 1] && p.sc_ck_off[c] <= r) ++c;
+            }
+            p.sc_chunk_base[b + 1] = p.sc_chunk_base[b] + count;
+        }
+        p.n_chunks = p.sc_chunk_base[nb];
         std::vector<int32_t> depth(nb, 0);
         int32_t max_depth = 0;
         for (int32_t b = 0; b < nb; ++b) {
@@ -591,6 +609,7 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     L.sc_ck_off = place(std::max<size_t>(p.sc_ck_off.size(), 1) * 4);
     L.sc_ck_slot = place(std::max<size_t>(p.sc_ck_slot.size(), 1) * 4);
     L.sc_level_br = place((size_t)nb * 4);
+    L.sc_chunk_base = place((size_t)(nb + 1) * 4);
     L.total = std::max<size_t>(at, 256);
     p.blob.assign(L.total, 0);
     auto put = [&](size_t off, const void* src, size_t bytes) {
@@ -622,6 +641,7 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     put(L.sc_ck_off, p.sc_ck_off.data(), p.sc_ck_off.size() * 4);
     put(L.sc_ck_slot, p.sc_ck_slot.data(), p.sc_ck_slot.size() * 4);
     put(L.sc_level_br, p.level_br.data(), p.level_br.size() * 4);
+    put(L.sc_chunk_base, p.sc_chunk_base.data(), p.sc_chunk_base.size() * 4);
     return OCTOPUS_OK;
 }
 

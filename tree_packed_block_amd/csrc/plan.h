@@ -66,7 +66,7 @@ struct DevLayout {
     size_t fwd_order = 0, qt_ptr = 0, q_pairs = 0, bwd_order = 0, kt_ptr = 0,
            k_pairs = 0, mask_rows = 0, mask_cols = 0, blk_order = 0, blk_ptr = 0,
            blk_entries = 0, pos = 0, sc_start = 0, sc_len = 0, sc_init = 0, sc_ck_ptr = 0,
-           sc_ck_off = 0, sc_ck_slot = 0, sc_level_br = 0, total = 0;
+           sc_ck_off = 0, sc_ck_slot = 0, sc_level_br = 0, sc_chunk_base = 0, total = 0;
 };
 
 struct Plan {
@@ -90,11 +90,18 @@ struct Plan {
     // token sc_ck_off[j] into slot sc_ck_slot[j] (its children's fork points).
     std::vector<int32_t> sc_init, sc_ck_ptr, sc_ck_off, sc_ck_slot, level_ptr, level_br;
     int32_t n_slots = 0;
+    // Chunked scan: branch b's chunks (own tokens split every kScanChunk tokens and at
+    // every checkpoint offset) are numbered sc_chunk_base[b] .. sc_chunk_base[b+1]-1.
+    std::vector<int32_t> sc_chunk_base;
+    int64_t n_chunks = 0;
     DevLayout layout;
     std::vector<unsigned char> blob;  // host image of the device copy
     void* dev = nullptr;              // caller-owned device copy after upload
     void* pinned = nullptr;           // page-locked copy of `blob` used by uploads
 };
+
+// Tokens per chunk of the chunked recurrent scan.
+constexpr int32_t kScanChunk = 32;
 
 int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, int32_t nm,
                int32_t T, int32_t kv_tile, Plan& out, std::string& err);
