@@ -266,7 +266,10 @@ int octopus_dag_attn_bwd_rope(const octopus_plan* plan, octopus_dtype dtype, int
 /* ---------------------------------------------------------------- recurrent scan */
 
 /* Workspace bytes of octopus_gated_delta_scan: float32 fork checkpoints
- * [n_slots][H][Dv][Dk], one slot per distinct (parent, fork offset) of the plan. */
+ * [n_slots][H][Dv][Dk], one slot per distinct (parent, fork offset) of the plan, then one
+ * 33,024-byte record per (chunk, head) (the chunk's gated score matrices, the inverse of
+ * its triangular system and the state-independent part of its W): 4.3 GB at 262,144
+ * tokens and H = 16. */
 size_t octopus_gdn_workspace_bytes(const octopus_plan* plan, int32_t H, int32_t Dk,
                                    int32_t Dv);
 
@@ -279,9 +282,10 @@ size_t octopus_gdn_workspace_bytes(const octopus_plan* plan, int32_t H, int32_t 
  * state just before the parent's own token `fork`; mounts are ignored.
  * q, k [T][H][Dk], v, o [T][H][Dv] (dtype); alpha, beta float32 [T][H] (device).
  * alpha in (0, 1] (values below 2^-100 act as 2^-100), beta in [0, 1].
- * The plan must be uploaded.  Levels of the tree run one launch each, in order; every
- * branch is taken 32 tokens at a time on the matrix cores (chunks also end at every fork
- * offset), one workgroup per (branch, head).
+ * The plan must be uploaded.  Every branch is taken 32 tokens at a time on the matrix
+ * cores (chunks also end at every fork offset): one launch prepares every (chunk, head)
+ * in parallel, then the levels of the tree run one launch each, in order, one workgroup
+ * per (branch, head).
  * Supported: bf16, Dk = Dv = 128.  Errors: EINVAL, ESTATE, EUNSUPPORTED, EWORKSPACE,
  * EHIP. */
 int octopus_gated_delta_scan(const octopus_plan* plan, octopus_dtype dtype, int32_t H,
@@ -289,9 +293,10 @@ int octopus_gated_delta_scan(const octopus_plan* plan, octopus_dtype dtype, int3
                              const void* v, const float* alpha, const float* beta, void* o,
                              void* ws, size_t ws_bytes, void* stream);
 
-/* Workspace bytes of octopus_gated_delta_scan_bwd: float32 checkpoint slots, the state at
- * the start of every chunk of the plan (32-token chunks, split at fork offsets), and
- * gradient slots, each H x Dv x Dk. */
+/* Workspace bytes of octopus_gated_delta_scan_bwd: float32 checkpoint slots and gradient
+ * slots, the state at the start and the state gradient at the end of every chunk of the
+ * plan (32-token chunks, split at fork offsets), each H x Dv x Dk, and the per-chunk
+ * records of the forward (21.5 GB at 262,144 tokens and H = 16). */
 size_t octopus_gdn_bwd_workspace_bytes(const octopus_plan* plan, int32_t H, int32_t Dk,
                                        int32_t Dv);
 
@@ -299,9 +304,10 @@ size_t octopus_gdn_bwd_workspace_bytes(const octopus_plan* plan, int32_t H, int3
  * to q, k, v (written, [T][H][D] bf16) and to alpha, beta (written, [T][H] float32).  The
  * gradient of a child's initial state (its parent's state at the fork) flows into the
  * parent's earlier tokens; mounted spans receive nothing (the recurrent layers skip them;
- * project page, primitives table).  Recomputes the forward chunk by chunk (the states at
- * chunk starts go to the workspace), then walks every branch's chunks in reverse, deepest
- * branches first.  Same support and errors as octopus_gated_delta_scan. */
+ * project page, primitives table).  Recomputes the forward (the states at chunk starts go
+ * to the workspace), walks every branch's chunks in reverse carrying only the state
+ * gradient (deepest branches first), then computes every chunk's gradients in parallel.
+ * Same support and errors as octopus_gated_delta_scan. */
 int octopus_gated_delta_scan_bwd(const octopus_plan* plan, octopus_dtype dtype, int32_t H,
                                  int32_t Dk, int32_t Dv, const void* q, const void* k,
                                  const void* v, const float* alpha, const float* beta,

@@ -377,8 +377,18 @@ def test_new_entry_points_reject_bad_arguments_before_any_launch():
     assert _code(L.octopus_gated_delta_scan(p.handle, tpb.BF16, 2, 128, 128, fake, fake, fake,
                                             fake, fake, fake, fake, 1 << 30, None)) == "ESTATE"
     assert tpb.lib().octopus_gdn_workspace_bytes(p.handle, 2, 64, 128) == 0
-    # both children fork from the root at offset 256: one checkpoint slot
-    assert tpb.gdn_workspace_bytes(p, 2) == 1 * 2 * 128 * 128 * 4
+    # both children fork from the root at offset 256: one checkpoint slot; chunks end every
+    # 32 own tokens and at every fork offset; one 8,256-float record per (chunk, head)
+    br = np.asarray(dag.branches).reshape(-1, 4)
+    n_chunks = 0
+    for b, (_, _, _, ln) in enumerate(br):
+        cuts = set(range(32, int(ln), 32)) | {int(f) for par, f, _, _ in br
+                                              if par == b and 0 < f < ln}
+        n_chunks += len(cuts) + 1 if ln > 0 else 0
+    state = 2 * 128 * 128 * 4
+    assert tpb.gdn_workspace_bytes(p, 2) == 1 * state + n_chunks * 2 * 8256 * 4
+    assert tpb.gdn_bwd_workspace_bytes(p, 2) == (2 * 1 + 2 * n_chunks) * state + \
+        n_chunks * 2 * 8256 * 4
     # extend
     assert _code(L.octopus_paged_mount_extend(tpb.BF16, 1, 16, 4, 96, 64, 0.0, fake, fake, fake,
                                               4, fake, 1, fake, fake, fake, fake, fake, fake,

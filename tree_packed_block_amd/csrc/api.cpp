@@ -2,9 +2,11 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <initializer_list>
 #include <memory>
 #include <new>
 #include <string>
@@ -67,6 +69,8 @@ octo::DevPlan dev_view(const octo::Plan& p) {
     d.sc_ck_slot = reinterpret_cast<const int32_t*>(base + p.layout.sc_ck_slot);
     d.sc_level_br = reinterpret_cast<const int32_t*>(base + p.layout.sc_level_br);
     d.sc_chunk_base = reinterpret_cast<const int32_t*>(base + p.layout.sc_chunk_base);
+    d.sc_chunk_tok = reinterpret_cast<const int32_t*>(base + p.layout.sc_chunk_tok);
+    d.sc_chunk_nt = reinterpret_cast<const int32_t*>(base + p.layout.sc_chunk_nt);
     return d;
 }
 
@@ -501,35 +505,60 @@ int octopus_rope(octopus_dtype dtype, int32_t rows, int32_t H, int32_t D, float 
     return ok();
 }
 
+namespace {
+// Bytes of one float32 H x 128 x 128 state set (a checkpoint slot, or one chunk's).
+size_t gdn_state_bytes(int32_t H) { return (size_t)H * 128 * 128 * sizeof(float); }
+size_t gdn_prep_bytes(const octopus_plan* plan, int32_t H) {
+    return octo::gdn_prep_floats(plan->p.n_chunks, H) * sizeof(float);
+}
+// Arguments shared by the scan's forward and backward.
+int check_gdn(const octopus_plan* plan, octopus_dtype dtype, int32_t H, int32_t Dk, int32_t Dv,
+              std::initializer_list<const void*> tensors) {
+    if (plan == nullptr) return fail(OCTOPUS_EINVAL, "plan is NULL");
+    if (plan->p.dev == nullptr) return fail(OCTOPUS_ESTATE, "plan not uploaded");
+    if (dtype != OCTOPUS_BF16) return fail(OCTOPUS_EUNSUPPORTED, "the scan supports bf16 only");
+    if (Dk != 128 || Dv != 128) return fail(OCTOPUS_EUNSUPPORTED, "the scan supports Dk = Dv = 128");
+    if (H < 1) return fail(OCTOPUS_EINVAL, "H must be >= 1");
+    if ((int64_t)plan->p.n_chunks * H > INT32_MAX)
+        return fail(OCTOPUS_EUNSUPPORTED, "too many (chunk, head) pairs for one launch");
+    for (const void* p : tensors) {
+        if (p == nullptr) return fail(OCTOPUS_EINVAL, "a tensor pointer is NULL");
+        if (!aligned(p, 16)) return fail(OCTOPUS_EINVAL, "tensors must be 16-byte aligned");
+    }
+    return OCTOPUS_OK;
+}
+}  // namespace
+
 size_t octopus_gdn_workspace_bytes(const octopus_plan* plan, int32_t H, int32_t Dk,
                                    int32_t Dv) {
     if (plan == nullptr || H < 1 || Dk != 128 || Dv != 128) return 0;
-    return (size_t)std::max(plan->p.n_slots, 1) * H * Dv * Dk * sizeof(float);
+    return (size_t)std::max(plan->p.n_slots, 1) * gdn_state_bytes(H) + gdn_prep_bytes(plan, H);
 }
 
 int octopus_gated_delta_scan(const octopus_plan* plan, octopus_dtype dtype, int32_t H,
                              int32_t Dk, int32_t Dv, const void* q, const void* k,
                              const void* v, const float* alpha, const float* beta, void* o,
                              void* ws, size_t ws_bytes, void* stream) {
-    if (plan == nullptr) return fail(OCTOPUS_EINVAL, "plan is NULL");
-    if (plan->p.dev == nullptr) return fail(OCTOPUS_ESTATE, "plan not uploaded");
-    if (dtype != OCTOPUS_BF16) return fail(OCTOPUS_EUNSUPPORTED, "the scan supports bf16 only");
-    if (Dk != 128 || Dv != 128) return fail(OCTOPUS_EUNSUPPORTED, "the scan supports Dk = Dv = 128");
-    if (H < 1) return fail(OCTOPUS_EINVAL, "H must be >= 1");
-    for (const void* p : {q, k, v, (const void*)alpha, (const void*)beta, (const void*)o}) {
-        if (p == nullptr) return fail(OCTOPUS_EINVAL, "a tensor pointer is NULL");
-        if (!aligned(p, 16)) return fail(OCTOPUS_EINVAL, "tensors must be 16-byte aligned");
-    }
+    const int rc = check_gdn(plan, dtype, H, Dk, Dv,
+                             {q, k, v, (const void*)alpha, (const void*)beta, (const void*)o});
+    if (rc != OCTOPUS_OK) return rc;
     const size_t need = octopus_gdn_workspace_bytes(plan, H, Dk, Dv);
     if (ws == nullptr || ws_bytes < need || !aligned(ws, 16))
         return fail(OCTOPUS_EWORKSPACE, "scan workspace needs " + std::to_string(need) +
                                             " bytes, 16-byte aligned");
     const octo::DevPlan dp = dev_view(plan->p);
     const std::vector<int32_t>& lp = plan->p.level_ptr;
+    hipStream_t st = (hipStream_t)stream;
+    float* slots = static_cast<float*>(ws);
+    float* prep = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                           (size_t)std::max(plan->p.n_slots, 1) *
+                                               gdn_state_bytes(H));
+    hipError_t e = octo::launch_gdn_chunk_prep(dp, plan->p.n_chunks, H, q, k, v, alpha, beta,
+                                               prep, st);
+    if (e != hipSuccess) return hip_fail(e, "scan prep launch");
     for (size_t l = 0; l + 1 < lp.size(); ++l) {
-        const hipError_t e = octo::launch_gdn_chunk_fwd(dp, lp[l], lp[l + 1] - lp[l], H, q, k, v,
-                                                        alpha, beta, o, static_cast<float*>(ws),
-                                                        nullptr, (hipStream_t)stream);
+        e = octo::launch_gdn_chunk_fwd(dp, lp[l], lp[l + 1] - lp[l], H, q, k, prep, o, slots,
+                                       nullptr, st);
         if (e != hipSuccess) return hip_fail(e, "scan launch");
     }
     return ok();
@@ -538,8 +567,8 @@ int octopus_gated_delta_scan(const octopus_plan* plan, octopus_dtype dtype, int3
 size_t octopus_gdn_bwd_workspace_bytes(const octopus_plan* plan, int32_t H, int32_t Dk,
                                        int32_t Dv) {
     if (plan == nullptr || H < 1 || Dk != 128 || Dv != 128) return 0;
-    const size_t per = (size_t)H * Dv * Dk * sizeof(float);
-    return per * ((size_t)2 * std::max(plan->p.n_slots, 1) + (size_t)plan->p.n_chunks);
+    return (size_t)2 * std::max(plan->p.n_slots, 1) * gdn_state_bytes(H) +
+           gdn_prep_bytes(plan, H) + (size_t)2 * plan->p.n_chunks * gdn_state_bytes(H);
 }
 
 int octopus_gated_delta_scan_bwd(const octopus_plan* plan, octopus_dtype dtype, int32_t H,
@@ -547,17 +576,11 @@ int octopus_gated_delta_scan_bwd(const octopus_plan* plan, octopus_dtype dtype, 
                                  const void* v, const float* alpha, const float* beta,
                                  const void* dout, void* dq, void* dk, void* dv, float* dalpha,
                                  float* dbeta, void* ws, size_t ws_bytes, void* stream) {
-    if (plan == nullptr) return fail(OCTOPUS_EINVAL, "plan is NULL");
-    if (plan->p.dev == nullptr) return fail(OCTOPUS_ESTATE, "plan not uploaded");
-    if (dtype != OCTOPUS_BF16) return fail(OCTOPUS_EUNSUPPORTED, "the scan supports bf16 only");
-    if (Dk != 128 || Dv != 128) return fail(OCTOPUS_EUNSUPPORTED, "the scan supports Dk = Dv = 128");
-    if (H < 1) return fail(OCTOPUS_EINVAL, "H must be >= 1");
-    for (const void* p : {q, k, v, (const void*)alpha, (const void*)beta, dout,
-                          (const void*)dq, (const void*)dk, (const void*)dv,
-                          (const void*)dalpha, (const void*)dbeta}) {
-        if (p == nullptr) return fail(OCTOPUS_EINVAL, "a tensor pointer is NULL");
-        if (!aligned(p, 16)) return fail(OCTOPUS_EINVAL, "tensors must be 16-byte aligned");
-    }
+    const int rc = check_gdn(plan, dtype, H, Dk, Dv,
+                             {q, k, v, (const void*)alpha, (const void*)beta, dout,
+                              (const void*)dq, (const void*)dk, (const void*)dv,
+                              (const void*)dalpha, (const void*)dbeta});
+    if (rc != OCTOPUS_OK) return rc;
     const size_t need = octopus_gdn_bwd_workspace_bytes(plan, H, Dk, Dv);
     if (ws == nullptr || ws_bytes < need || !aligned(ws, 16))
         return fail(OCTOPUS_EWORKSPACE, "scan backward workspace needs " + std::to_string(need) +
@@ -565,24 +588,34 @@ int octopus_gated_delta_scan_bwd(const octopus_plan* plan, octopus_dtype dtype, 
     const octo::DevPlan dp = dev_view(plan->p);
     const std::vector<int32_t>& lp = plan->p.level_ptr;
     hipStream_t st = (hipStream_t)stream;
-    const size_t per = (size_t)H * Dv * Dk;  // floats per slot or chunk state
+    const size_t n_slots = (size_t)std::max(plan->p.n_slots, 1);
+    const size_t per = gdn_state_bytes(H) / sizeof(float);  // floats per state set
+    const int64_t nc = plan->p.n_chunks;
     float* slots = static_cast<float*>(ws);
-    float* chunks = slots + per * std::max(plan->p.n_slots, 1);
-    float* dslots = chunks + per * (size_t)plan->p.n_chunks;
+    float* dslots = slots + per * n_slots;
+    float* chunks = dslots + per * n_slots;
+    float* dsc = chunks + per * (size_t)nc;
+    float* prep = dsc + per * (size_t)nc;
     // the forward again, keeping the state at the start of every chunk
+    hipError_t e = octo::launch_gdn_chunk_prep(dp, nc, H, q, k, v, alpha, beta, prep, st);
+    if (e != hipSuccess) return hip_fail(e, "scan backward (prep) launch");
     for (size_t l = 0; l + 1 < lp.size(); ++l) {
-        const hipError_t e = octo::launch_gdn_chunk_fwd(dp, lp[l], lp[l + 1] - lp[l], H, q, k, v,
-                                                        alpha, beta, nullptr, slots, chunks, st);
+        e = octo::launch_gdn_chunk_fwd(dp, lp[l], lp[l + 1] - lp[l], H, q, k, prep, nullptr,
+                                       slots, chunks, st);
         if (e != hipSuccess) return hip_fail(e, "scan backward (forward pass) launch");
     }
-    hipError_t e = octo::launch_fill_zero(dslots, per * std::max(plan->p.n_slots, 1), st);
+    e = octo::launch_fill_zero(dslots, per * n_slots, st);
     if (e != hipSuccess) return hip_fail(e, "scan backward (clear) launch");
-    // deepest level first: a child's initial-state gradient reaches its parent's slot
+    // state gradients, deepest level first: a child's initial-state gradient reaches its
+    // parent's slot before the parent runs
     for (size_t l = lp.size() - 1; l-- > 0;) {
-        e = octo::launch_gdn_chunk_bwd(dp, lp[l], lp[l + 1] - lp[l], H, q, k, v, alpha, beta,
-                                       dout, chunks, dslots, dq, dk, dv, dalpha, dbeta, st);
-        if (e != hipSuccess) return hip_fail(e, "scan backward launch");
+        e = octo::launch_gdn_chunk_dstate(dp, lp[l], lp[l + 1] - lp[l], H, q, k, dout, prep, dsc,
+                                          dslots, st);
+        if (e != hipSuccess) return hip_fail(e, "scan backward (state gradient) launch");
     }
+    e = octo::launch_gdn_chunk_grad(dp, nc, H, q, k, v, alpha, beta, dout, prep, chunks, dsc, dq,
+                                    dk, dv, dalpha, dbeta, st);
+    if (e != hipSuccess) return hip_fail(e, "scan backward launch");
     return ok();
 }
 

@@ -31,7 +31,9 @@ struct DevPlan {
     // branches grouped by depth.
     const int32_t *sc_start, *sc_len, *sc_init, *sc_ck_ptr, *sc_ck_off, *sc_ck_slot,
         *sc_level_br;
-    const int32_t* sc_chunk_base;  // [nb+1]: first chunk of every branch (chunked scan)
+    // Chunked scan: first chunk of every branch [nb+1]; first packed token and length of
+    // every chunk [n_chunks].
+    const int32_t *sc_chunk_base, *sc_chunk_tok, *sc_chunk_nt;
 };
 
 // Rotary-embedding frequencies of rotate-half pairs (x_i, x_{i+D/2}): pair i turns by
@@ -106,27 +108,34 @@ hipError_t launch_rope2(bool bf16, int rows, int D, float base, bool inverse,
                         const int32_t* pos, int H, const void* x, void* out, int H2,
                         const void* x2, void* out2, hipStream_t s);
 
-// Gated delta-rule scan of the branches level_br[l0 .. l0 + n_br) (matrix cores,
-// 32-token chunks), one workgroup per (branch, head): q, k, v [T][H][128] bf16, alpha,
-// beta float32 [T][H]; o [T][H][128] bf16 (may be NULL); states: float32 checkpoint slots
-// [n_slots][H][128][128] (row = value index).  With chunk_states (may be NULL), also
-// the state at the start of every chunk, float32 [sc_chunk_base[b] + c][H][128][128],
-// for the backward.
+// Chunked gated delta-rule scan (matrix cores, 32-token chunks as listed by the plan):
+// q, k, v, dout [T][H][128] bf16, alpha, beta float32 [T][H].  The prep kernel writes a
+// record of gdn_prep_floats / (n_chunks H) floats per (chunk, head) into `prep`
+// (one launch over every chunk); the forward walks the branches level_br[l0 .. l0 + n_br)
+// (one workgroup per (branch, head)) from their checkpoint slots `states`
+// [n_slots][H][128][128] float32 (row = value index), writing o [T][H][128] bf16 (may be
+// NULL) and, with chunk_states (may be NULL), the state at the start of every chunk
+// [c][H][128][128].
+size_t gdn_prep_floats(int64_t n_chunks, int H);
+hipError_t launch_gdn_chunk_prep(const DevPlan& p, int64_t n_chunks, int H, const void* q,
+                                 const void* k, const void* v, const float* alpha,
+                                 const float* beta, float* prep, hipStream_t s);
 hipError_t launch_gdn_chunk_fwd(const DevPlan& p, int l0, int n_br, int H, const void* q,
-                                const void* k, const void* v, const float* alpha,
-                                const float* beta, void* o, float* states, float* chunk_states,
-                                hipStream_t s);
-
-// Backward of the chunked scan for the branches level_br[l0 .. l0 + n_br) (levels in
-// reverse order): chunk_states from launch_gdn_chunk_fwd; dstates [n_slots][H][128][128]
-// float32 gradient slots, zero before the first level, which children add their
-// initial-state gradients to; dq, dk, dv [T][H][128] bf16 and dalpha, dbeta [T][H] float32
-// are written.
-hipError_t launch_gdn_chunk_bwd(const DevPlan& p, int l0, int n_br, int H, const void* q,
-                                const void* k, const void* v, const float* alpha,
-                                const float* beta, const void* dout, const float* chunk_states,
-                                float* dstates, void* dq, void* dk, void* dv, float* dalpha,
-                                float* dbeta, hipStream_t s);
+                                const void* k, const float* prep, void* o, float* states,
+                                float* chunk_states, hipStream_t s);
+// Backward: the state gradient of the branches level_br[l0 .. l0 + n_br) in reverse
+// (levels deepest first), written at every chunk's end into dsc [c][H][128][128];
+// dstates [n_slots][H][128][128] float32 gradient slots, zero before the first level,
+// which children add their initial-state gradients to.  Then, over every chunk,
+// dq, dk, dv [T][H][128] bf16 and dalpha, dbeta [T][H] float32.
+hipError_t launch_gdn_chunk_dstate(const DevPlan& p, int l0, int n_br, int H, const void* q,
+                                   const void* k, const void* dout, const float* prep,
+                                   float* dsc, float* dstates, hipStream_t s);
+hipError_t launch_gdn_chunk_grad(const DevPlan& p, int64_t n_chunks, int H, const void* q,
+                                 const void* k, const void* v, const float* alpha,
+                                 const float* beta, const void* dout, const float* prep,
+                                 const float* chunk_states, const float* dsc, void* dq, void* dk,
+                                 void* dv, float* dalpha, float* dbeta, hipStream_t s);
 hipError_t launch_fill_zero(float* p, size_t n_floats, hipStream_t s);
 
 // Extend: rows q_ptr[c] .. q_ptr[c+1]-1 of q are cursor c's new tokens (own offsets

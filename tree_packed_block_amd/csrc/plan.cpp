@@ -553,19 +553,22 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
         // Chunks of the chunked scan: boundaries every kScanChunk own tokens and at every
         // checkpoint offset inside the branch (the kernel walks the same rule).
         p.sc_chunk_base.assign(nb + 1, 0);
+        p.sc_chunk_tok.clear();
+        p.sc_chunk_nt.clear();
         for (int32_t b = 0; b < nb; ++b) {
             const int32_t len = d.br[b].len;
             int32_t c = p.sc_ck_ptr[b];
-            int32_t r = 0, count = 0;
+            int32_t r = 0;
             while (c < p.sc_ck_ptr[b + 1] && p.sc_ck_off[c] <= r) ++c;
             while (r < len) {
                 int32_t e = std::min(len, (r / kScanChunk + 1) * kScanChunk);
                 if (c < p.sc_ck_ptr[b + 1]) e = std::min(e, p.sc_ck_off[c]);
+                p.sc_chunk_tok.push_back(d.br[b].start + r);
+                p.sc_chunk_nt.push_back(e - r);
                 r = e;
-                ++count;
                 while (c < p.sc_ck_ptr[b + 1] && p.sc_ck_off[c] <= r) ++c;
             }
-            p.sc_chunk_base[b + 1] = p.sc_chunk_base[b] + count;
+            p.sc_chunk_base[b + 1] = (int32_t)p.sc_chunk_tok.size();
         }
         p.n_chunks = p.sc_chunk_base[nb];
         std::vector<int32_t> depth(nb, 0);
@@ -610,6 +613,8 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     L.sc_ck_slot = place(std::max<size_t>(p.sc_ck_slot.size(), 1) * 4);
     L.sc_level_br = place((size_t)nb * 4);
     L.sc_chunk_base = place((size_t)(nb + 1) * 4);
+    L.sc_chunk_tok = place(std::max<size_t>(p.sc_chunk_tok.size(), 1) * 4);
+    L.sc_chunk_nt = place(std::max<size_t>(p.sc_chunk_nt.size(), 1) * 4);
     L.total = std::max<size_t>(at, 256);
     p.blob.assign(L.total, 0);
     auto put = [&](size_t off, const void* src, size_t bytes) {
@@ -642,6 +647,8 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     put(L.sc_ck_slot, p.sc_ck_slot.data(), p.sc_ck_slot.size() * 4);
     put(L.sc_level_br, p.level_br.data(), p.level_br.size() * 4);
     put(L.sc_chunk_base, p.sc_chunk_base.data(), p.sc_chunk_base.size() * 4);
+    put(L.sc_chunk_tok, p.sc_chunk_tok.data(), p.sc_chunk_tok.size() * 4);
+    put(L.sc_chunk_nt, p.sc_chunk_nt.data(), p.sc_chunk_nt.size() * 4);
     return OCTOPUS_OK;
 }
 

@@ -66,7 +66,8 @@ struct DevLayout {
     size_t fwd_order = 0, qt_ptr = 0, q_pairs = 0, bwd_order = 0, kt_ptr = 0,
            k_pairs = 0, mask_rows = 0, mask_cols = 0, blk_order = 0, blk_ptr = 0,
            blk_entries = 0, pos = 0, sc_start = 0, sc_len = 0, sc_init = 0, sc_ck_ptr = 0,
-           sc_ck_off = 0, sc_ck_slot = 0, sc_level_br = 0, sc_chunk_base = 0, total = 0;
+           sc_ck_off = 0, sc_ck_slot = 0, sc_level_br = 0, sc_chunk_base = 0, sc_chunk_tok = 0,
+           sc_chunk_nt = 0, total = 0;
 };
 
 struct Plan {
@@ -91,8 +92,9 @@ struct Plan {
     std::vector<int32_t> sc_init, sc_ck_ptr, sc_ck_off, sc_ck_slot, level_ptr, level_br;
     int32_t n_slots = 0;
     // Chunked scan: branch b's chunks (own tokens split every kScanChunk tokens and at
-    // every checkpoint offset) are numbered sc_chunk_base[b] .. sc_chunk_base[b+1]-1.
-    std::vector<int32_t> sc_chunk_base;
+    // every checkpoint offset) are numbered sc_chunk_base[b] .. sc_chunk_base[b+1]-1;
+    // chunk c covers packed tokens sc_chunk_tok[c] .. sc_chunk_tok[c] + sc_chunk_nt[c] - 1.
+    std::vector<int32_t> sc_chunk_base, sc_chunk_tok, sc_chunk_nt;
     int64_t n_chunks = 0;
     DevLayout layout;
     std::vector<unsigned char> blob;  // host image of the device copy

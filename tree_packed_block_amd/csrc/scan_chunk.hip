@@ -5,29 +5,37 @@
 // bypass the recurrent layers), per head with state S (Dv x Dk):
 //     S_t = alpha_t (S_{t-1} - beta_t (S_{t-1} k_t) k_t^T) + beta_t v_t k_t^T,  o_t = S_t q_t,
 // is applied 32 tokens at a time.  Within a chunk starting from S_0, with
-// gamma_t = alpha_1 ... alpha_t, the state is
-//     S_t = gamma_t S_0 + sum_{i<=t} (gamma_t / gamma_i) w_i k_i^T
+// gamma_t = alpha_1 ... alpha_t and Gamma[t][i] = gamma_t / gamma_i (<= 1), the state is
+//     S_t = gamma_t S_0 + sum_{i<=t} Gamma[t][i] w_i k_i^T
 // where the rows w_t solve the unit lower-triangular system
-//     w_t + beta_t sum_{i<t} (gamma_t / gamma_i) (k_t . k_i) w_i = beta_t (v_t - gamma_t S_0 k_t),
-// so that, as matrices over the chunk (rows = tokens),
-//     W = solve(I + diag(beta) (K K^T o Gamma_strict), diag(beta) (V - diag(gamma) K S_0^T))
-//     O = diag(gamma) Q S_0^T + (Q K^T o Gamma_incl) W
+//     N W = diag(beta) (V - diag(gamma) K S_0^T),  N = I + diag(beta) (K K^T o Gamma_strict).
+// With T = N^{-1} and U = T diag(beta) V, which do not depend on the state,
+//     W   = U - T diag(beta gamma) X,        X = K S_0^T
+//     O   = diag(gamma) Q S_0^T + M W,        M = Q K^T o Gamma_incl
 //     S_C = gamma_C S_0 + W^T diag(gamma_C / gamma) K.
-// (Gamma[t][i] = gamma_t / gamma_i <= 1: every factor is bounded.)  These are the
-// chunk-wise products of the published gated delta rule (Yang, Kautz and Hatamizadeh,
-// 2024), restated for this kernel's layout.
+// These are the chunk-wise products of the published gated delta rule (Yang, Kautz and
+// Hatamizadeh, 2024), restated for this layout.
 //
-// One workgroup per (branch, head) walks the branch's chunks in order; chunk boundaries
-// fall every 32 own tokens and at every offset where a child forks (its checkpoint is the
-// state there).  Value rows evolve independently, so wave w owns value rows
-// [32 w, 32 w + 32) of the state, held transposed in MFMA accumulators (S^T: 4 tiles of
-// 32 keys x 32 values, lane = value row), and needs no other wave's data: the chunk's
-// K, Q, V, alpha, beta are staged once in LDS for all four waves.  Products whose operands
-// are bf16 inputs (K K^T, Q K^T) are exact on v_mfma_f32_32x32x16_bf16; operands held in
-// float32 (the state, W, the gated score matrix) enter as a bf16 high part plus a bf16
-// low part (relative error below 2^-16 per operand).  The 32-row triangular solve runs
-// on the vector unit, each lane holding 16 rows of one value column and exchanging
-// partial sums with its partner lane.
+// Work split (chunk boundaries every 32 own tokens and at every offset where a child
+// forks, listed by the plan):
+//   prep   every (chunk, head) in parallel: the gated score matrices, T (a 32-row
+//          triangular solve), U; written to a per-chunk record.
+//   fwd    one workgroup per (branch, head), chunks in order, levels of the tree one
+//          launch each: only the state-dependent products above (no solve).
+//   dstate backward, one workgroup per (branch, head), chunks in reverse, deepest level
+//          first: the state gradient alone,
+//              dW = M^T dO + diag(gamma_C / gamma) K dS_C^T,   dR = T^T dW,
+//              dS_0 = gamma_C dS_C - K^T diag(beta gamma) dR + Q^T diag(gamma) dO,
+//          with a child's initial-state gradient added at its fork offset.
+//   grad   every (chunk, head) in parallel, from the state at the chunk's start and the
+//          state gradient at its end: dQ, dK, dV, d alpha, d beta.
+//
+// In the sequential kernels wave w owns value rows [32 w, 32 w + 32) of the state, held
+// transposed in MFMA accumulators (S^T: 4 tiles of 32 keys x 32 values, lane = value
+// row); value rows evolve independently, so no wave needs another's data.  Products of
+// bf16 inputs (K K^T, Q K^T, K and Q against anything) are exact on
+// v_mfma_f32_32x32x16_bf16; float32 operands (state, W, T, M, gradients) enter as a bf16
+// high part plus a bf16 low part (relative error below 2^-16 per operand).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -37,15 +45,30 @@ namespace {
 
 constexpr int kD = 128;         // Dk = Dv
 constexpr int kC = 32;          // tokens per chunk
-constexpr int kWaves = kD / 32; // one wave per 32 value rows
+constexpr int kWaves = kD / 32; // one wave per 32 value rows (or key columns)
 constexpr int kThr = 64 * kWaves;
 constexpr int kRowB = kD * 2;   // bytes of one bf16 row
+
+// Per (chunk, head) record written by the prep kernel, float32:
+//   U   [4 waves][4][64 lanes][4]  U[acc_row(4q + r, g)][32 w + n] (accumulator order)
+//   T   [64 lanes][16]             T[n][acc_row(j, g)]   (A operand, k in row order)
+//   TT  [64 lanes][16]             T[acc_row(j, g)][n]   (A operand of T^T)
+//   M   [64 lanes][16]             M[n][acc_row(j, g)]
+//   MT  [64 lanes][16]             M[acc_row(j, g)][n]
+//   gam [32], bg [32]              gamma_t and beta_t gamma_t
+constexpr int kRecU = 0, kRecT = 4096, kRecTT = 5120, kRecM = 6144, kRecMT = 7168,
+              kRecGam = 8192, kRecBG = 8224, kRec = 8256;
 
 // Element e of hi and lo take x as hi + lo, both bf16 (|x - hi - lo| <= 2^-16 |x|).
 __device__ __forceinline__ void split2(float x, bf16x8& hi, bf16x8& lo, int e) {
     const bf16 h = (bf16)x;
     hi[e] = h;
     lo[e] = (bf16)(x - (float)h);
+}
+// Elements 8 kk .. 8 kk + 7 of v, split.
+__device__ __forceinline__ void split8(const float (&v)[16], int kk, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) split2(v[8 * kk + e], hi, lo, e);
 }
 
 // x plus the value of the lane 32 away (the other half of the wave).
@@ -55,13 +78,30 @@ __device__ __forceinline__ float pair_sum(float x) { return x + __shfl_xor(x, 32
 // 8 (j / 4) + 4 g + j % 4.
 __device__ __forceinline__ constexpr int acc_row(int j, int g) { return 8 * (j >> 2) + 4 * g + (j & 3); }
 
-// Forward substitution w_t -= sum_{i<t} c_t L[t][i] w_i over the 32 rows of this lane's
-// value column (rows acc_row(j, g); the other 16 rows are in the lane 32 away).  L is
-// [t][i] row-major with zeros on and above the diagonal; c_t = beta[t] if beta is given,
-// else 1.  Rows go in 8 blocks of 4 consecutive rows, each held by one half of the wave:
-// both halves sum their finished rows for the block's rows, exchanges (independent of
-// one another, so their latencies overlap) add the halves, and the owner finishes the
-// block's rows in order.
+// 16 floats from 4 float4 at p, p + s, p + 2 s, p + 3 s.
+__device__ __forceinline__ void ld16f(const float* p, int s, float (&v)[16]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float4 x = *reinterpret_cast<const float4*>(p + q * s);
+        v[4 * q] = x.x;
+        v[4 * q + 1] = x.y;
+        v[4 * q + 2] = x.z;
+        v[4 * q + 3] = x.w;
+    }
+}
+__device__ __forceinline__ void st16f(float* p, int s, const float (&v)[16]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(p + q * s) =
+            make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+}
+
+// Forward substitution w_t -= c_t sum_{i<t} L[t][i] w_i over the 32 rows of this lane's
+// column (rows acc_row(j, g); the other 16 rows are in the lane 32 away).  L is [t][i]
+// row-major with zeros on and above the diagonal; c_t = beta[t].  Rows go in 8 blocks of
+// 4 consecutive rows, each held by one half of the wave: both halves sum their finished
+// rows for the block's rows, exchanges (independent of one another, so their latencies
+// overlap) add the halves, and the owner finishes the block's rows in order.
 __device__ __forceinline__ void fwd_solve(float (&wv)[16], const float* L, const float* beta,
                                           int g) {
 #pragma unroll
@@ -74,8 +114,7 @@ __device__ __forceinline__ void fwd_solve(float (&wv)[16], const float* L, const
             float part = 0.f;
 #pragma unroll
             for (int q4 = 0; q4 <= q; ++q4) {
-                // the owner's own run q is the block itself (done below)
-                if (q4 == q && g == gb) continue;
+                if (q4 == q && g == gb) continue;  // the block itself (done below)
                 const float4 l4 = *reinterpret_cast<const float4*>(L + t * 32 + 8 * q4 + 4 * g);
                 part = fmaf(l4.x, wv[4 * q4], part);
                 part = fmaf(l4.y, wv[4 * q4 + 1], part);
@@ -90,102 +129,250 @@ __device__ __forceinline__ void fwd_solve(float (&wv)[16], const float* L, const
                 const int t = 8 * q + 4 * gb + r;
                 float acc = tot[r];
 #pragma unroll
-                for (int r2 = 0; r2 < r; ++r2) acc = fmaf(L[t * 32 + 8 * q + 4 * gb + r2], wv[4 * q + r2], acc);
-                wv[4 * q + r] -= beta ? beta[t] * acc : acc;
+                for (int r2 = 0; r2 < r; ++r2)
+                    acc = fmaf(L[t * 32 + 8 * q + 4 * gb + r2], wv[4 * q + r2], acc);
+                wv[4 * q + r] -= beta[t] * acc;
             }
         }
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// Back substitution d_t -= sum_{s>t} beta_s LT[t][s] d_s (LT[t][s] = L[s][t], zero for
-// s <= t), the transposed system of fwd_solve, blocks in reverse order.
-__device__ __forceinline__ void bwd_solve(float (&dr)[16], const float* LT, const float* beta,
-                                          int g) {
+// Per-lane LDS offsets of the transposed reads of a swizzled chunk tile: the A operand
+// K^T (rows: keys 32 db + n; k: tokens) or the B operand V (columns 32 db + n; k:
+// tokens), tokens in the accumulator's row order (rows 4g + r/4 (+8) of each 16-row
+// k-step).
+__device__ __forceinline__ void tr_offsets(int lane, int (&tr)[4][2]) {
+    const int r_in = lane & 15, dh = (lane >> 4) & 1, g = lane >> 5;
 #pragma unroll
-    for (int blk = 7; blk >= 0; --blk) {
-        const int q = blk >> 1, gb = blk & 1;
-        float tot[4];
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 8 * q + 4 * gb + r;
-            float part = 0.f;
-#pragma unroll
-            for (int q4 = q; q4 < 4; ++q4) {
-                if (q4 == q && g == gb) continue;
-                const float4 l4 = *reinterpret_cast<const float4*>(LT + t * 32 + 8 * q4 + 4 * g);
-                const float4 b4 = *reinterpret_cast<const float4*>(beta + 8 * q4 + 4 * g);
-                part = fmaf(l4.x * b4.x, dr[4 * q4], part);
-                part = fmaf(l4.y * b4.y, dr[4 * q4 + 1], part);
-                part = fmaf(l4.z * b4.z, dr[4 * q4 + 2], part);
-                part = fmaf(l4.w * b4.w, dr[4 * q4 + 3], part);
-            }
-            tot[r] = pair_sum(part);
+        for (int hf = 0; hf < 2; ++hf) {
+            const int row = 4 * g + (r_in >> 2) + 8 * hf;
+            const int chunk = 4 * db + 2 * dh + ((r_in & 3) >> 1);
+            tr[db][hf] = row * kRowB + swz<kD>(row, chunk) * 16 + 8 * (r_in & 1);
         }
-        if (g == gb) {
+}
+__device__ __forceinline__ bf16x8 rd_tr(const unsigned char* base, const int (&tr)[4][2], int db,
+                                        int kk) {
+    return cat(lds8_tr(base, tr[db][0], 16 * kk * kRowB), lds8_tr(base, tr[db][1], 16 * kk * kRowB));
+}
+// Row reads of a swizzled tile: 8 bytes (k values k0 .. k0 + 3) or 16 bytes.
+__device__ __forceinline__ bf16x4 rd4(const unsigned char* base, int row, int k0) {
+    return *reinterpret_cast<const bf16x4*>(base + row * kRowB + swz<kD>(row, k0 >> 3) * 16 +
+                                            (k0 & 7) * 2);
+}
+__device__ __forceinline__ bf16x8 rd8(const unsigned char* base, int row, int k0) {
+    return *reinterpret_cast<const bf16x8*>(base + row * kRowB + swz<kD>(row, k0 >> 3) * 16);
+}
+// A operand of row n with k values in the accumulator's row order: k0 .. k0 + 3 and
+// k0 + 8 .. k0 + 11 (k0 = 32 bk + 16 kh + 4 g).
+__device__ __forceinline__ bf16x8 rd_perm(const unsigned char* base, int n, int k0) {
+    return cat(rd4(base, n, k0), rd4(base, n, k0 + 8));
+}
+
+// One bf16 element (token row t, column col) of a swizzled tile.
+__device__ __forceinline__ float tile_at(const unsigned char* base, int t, int col) {
+    return (float)*reinterpret_cast<const bf16*>(base + t * kRowB + swz<kD>(t, col >> 3) * 16 +
+                                                 (col & 7) * 2);
+}
+
+// Rows t < nt of a chunk of x [T][H][128] (bf16, head h, first token tok0), zeros past
+// nt: thread tid loads 16-byte pieces tid and tid + 256 (row p / 16, columns 8 (p % 16)).
+__device__ __forceinline__ void fetch_rows(const bf16* __restrict__ x, size_t tok0, int nt,
+                                           int H, int h, int tid, bf16x8 (&r)[2]) {
 #pragma unroll
-            for (int r = 3; r >= 0; --r) {
-                const int t = 8 * q + 4 * gb + r;
-                float acc = tot[r];
+    for (int u = 0; u < 2; ++u) {
+        const int p = u * kThr + tid, t = p >> 4;
+        r[u] = t < nt ? ld16(x + ((tok0 + t) * H + h) * kD + 8 * (p & 15)) : zero8();
+    }
+}
+// ... and into a swizzled LDS tile.
+__device__ __forceinline__ void put_rows(unsigned char* tile, int tid, const bf16x8 (&r)[2]) {
 #pragma unroll
-                for (int r2 = r + 1; r2 < 4; ++r2) {
-                    const int s2 = 8 * q + 4 * gb + r2;
-                    acc = fmaf(LT[t * 32 + s2] * beta[s2], dr[4 * q + r2], acc);
-                }
-                dr[4 * q + r] -= acc;
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
+    for (int u = 0; u < 2; ++u) {
+        const int p = u * kThr + tid;
+        *reinterpret_cast<bf16x8*>(tile + tile_off<kD>(p >> 4, p & 15)) = r[u];
     }
 }
 
-struct ChunkSmem {
-    unsigned char K[kC * kRowB];   // swizzled rows (tile_off)
+// Sum of v[j] over the 32 lanes of this lane's half (lanes with the same g).
+__device__ __forceinline__ void half_sum16(float (&v)[16]) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) v[j] += __shfl_xor(v[j], off);
+}
+
+// log2 gamma_t for lanes t < 32 (inclusive prefix sums of log2 alpha over the chunk;
+// alpha is clamped at 2^-100: a zero gate still empties the state, and every ratio of
+// gammas stays a finite difference of logarithms).
+__device__ __forceinline__ float log2_gamma(const float* alpha, int lane) {
+    float la = lane < kC ? __log2f(fmaxf(alpha[lane], 7.8886e-31f)) : 0.f;
+#pragma unroll
+    for (int d = 1; d < kC; d <<= 1) {
+        const float y = __shfl_up(la, d, 64);
+        if ((lane & (kC - 1)) >= d) la += y;
+    }
+    return la;
+}
+
+struct PrepSmem {
+    unsigned char K[kC * kRowB];
     unsigned char Q[kC * kRowB];
     unsigned char V[kC * kRowB];
     float alpha[kC], beta[kC];
-    // per wave: beta-scaled gated K K^T (strict lower, [t][i]) and gated Q K^T
-    // (lower with diagonal, [t][i]), gamma and log2 gamma of the chunk's tokens
-    float L[kWaves][kC * kC];
-    float M[kWaves][kC * kC];
-    float gam[kWaves][kC], lg[kWaves][kC];
+    float lg[2][kC];    // log2 gamma (one copy per wave that needs it)
+    float LG[kC * kC];  // gated K K^T, strict lower, [t][i]
+    float T[kC * kC];   // N^{-1}, [t][s]
+    float M[kC * kC];   // gated Q K^T, lower with diagonal, [t][i]
 };
 
 }  // namespace
 
+// ---------------------------------------------------------------- prep (parallel)
+
+__global__ __launch_bounds__(kThr) void gdn_chunk_prep_kernel(
+    DevPlan P, int H, const bf16* __restrict__ Qg, const bf16* __restrict__ Kg,
+    const bf16* __restrict__ Vg, const float* __restrict__ Ag, const float* __restrict__ Bg,
+    float* __restrict__ prep) {
+    __shared__ __attribute__((aligned(1024))) PrepSmem S;
+    const int c = blockIdx.x / H, h = blockIdx.x % H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, g = lane >> 5;
+    const size_t tok0 = ld_const(P.sc_chunk_tok + c);
+    const int nt = ld_const(P.sc_chunk_nt + c);
+    float* rec = prep + ((size_t)c * H + h) * kRec;
+
+    {
+        bf16x8 rk[2], rq[2], rv[2];
+        fetch_rows(Kg, tok0, nt, H, h, tid, rk);
+        fetch_rows(Qg, tok0, nt, H, h, tid, rq);
+        fetch_rows(Vg, tok0, nt, H, h, tid, rv);
+        if (tid < 2 * kC) {
+            const int t = tid & (kC - 1);
+            (tid < kC ? S.alpha : S.beta)[t] =
+                t < nt ? (tid < kC ? Ag : Bg)[(tok0 + t) * H + h] : (tid < kC ? 1.f : 0.f);
+        }
+        put_rows(S.K, tid, rk);
+        put_rows(S.Q, tid, rq);
+        put_rows(S.V, tid, rv);
+    }
+    wait_lds();
+    barrier();
+
+    if (w < 2) {
+        // wave 0: gated K K^T and T; wave 1: gated Q K^T
+        const float la = log2_gamma(S.alpha, lane);
+        if (lane < kC) S.lg[w][lane] = la;
+        f32x16 acc = zero16();
+        const unsigned char* A = w == 0 ? S.K : S.Q;
+#pragma unroll
+        for (int ks = 0; ks < kD / 16; ++ks)
+            acc = mfma_32x32x16(rd8(A, n, 16 * ks + 8 * g), rd8(S.K, n, 16 * ks + 8 * g), acc);
+        wait_lds();
+        __builtin_amdgcn_wave_barrier();
+        // accumulator: column i = n, rows t = acc_row(j, g)
+        const float lgi = S.lg[w][n];
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int t = acc_row(j, g);
+            const float gt = exp2f(S.lg[w][t] - lgi);
+            v[j] = (w == 0 ? n < t : n <= t) ? acc[j] * gt : 0.f;
+        }
+        if (w == 0) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) S.LG[acc_row(j, g) * kC + n] = v[j];
+            wait_lds();
+            __builtin_amdgcn_wave_barrier();
+            // T = N^{-1}: column n of the identity through the forward substitution
+            float tv[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) tv[j] = acc_row(j, g) == n ? 1.f : 0.f;
+            fwd_solve(tv, S.LG, S.beta, g);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) S.T[acc_row(j, g) * kC + n] = tv[j];
+            st16f(rec + kRecTT + lane * 16, 4, tv);  // T^T rows n: T[acc_row(j, g)][n]
+            if (lane < kC) {
+                const float gm = exp2f(la);
+                rec[kRecGam + lane] = gm;
+                rec[kRecBG + lane] = S.beta[lane] * gm;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) S.M[acc_row(j, g) * kC + n] = v[j];
+            st16f(rec + kRecMT + lane * 16, 4, v);  // M^T rows n: M[acc_row(j, g)][n]
+        }
+    }
+    wait_lds();
+    barrier();
+
+    // U = (T diag(beta)) V for value columns 32 w + n: A = T rows n with the k values in
+    // the accumulator's row order, B = V read transposed (exact).
+    int tr[4][2];
+    tr_offsets(lane, tr);
+    float trow[16], brow[16];
+    ld16f(S.T + n * kC + 4 * g, 8, trow);  // T[n][acc_row(j, g)]
+    ld16f(S.beta + 4 * g, 8, brow);
+    f32x16 u = zero16();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 ah, al;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) split2(trow[8 * kk + e] * brow[8 * kk + e], ah, al, e);
+        const bf16x8 bv = rd_tr(S.V, tr, w, kk);
+        u = mfma_32x32x16(ah, bv, u);
+        u = mfma_32x32x16(al, bv, u);
+    }
+    {
+        float uv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) uv[j] = u[j];
+        st16f(rec + kRecU + (w * 4 * 64 + lane) * 4, 64 * 4, uv);
+    }
+    if (w == 2) st16f(rec + kRecT + lane * 16, 4, trow);
+    if (w == 3) {
+        float mrow[16];
+        ld16f(S.M + n * kC + 4 * g, 8, mrow);
+        st16f(rec + kRecM + lane * 16, 4, mrow);
+    }
+}
+
+// ---------------------------------------------------------------- forward (sequential)
+
 // states: checkpoint slots [n_slots][H][Dv][Dk] float32 (row = value index).
-// chunk_states (may be NULL): the state at the start of every chunk of every branch,
-// [P.sc_chunk_base[b] + c][H][Dv][Dk] float32, for the backward.  Og may be NULL (the
-// backward's recomputation needs the states only).
+// chunk_states (may be NULL): the state at the start of every chunk, [c][H][Dv][Dk].
+// Og may be NULL (the backward needs the states only).
 __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
     DevPlan P, int l0, int H, const bf16* __restrict__ Qg, const bf16* __restrict__ Kg,
-    const bf16* __restrict__ Vg, const float* __restrict__ Ag, const float* __restrict__ Bg,
-    bf16* __restrict__ Og, float* __restrict__ states, float* __restrict__ chunk_states) {
-    __shared__ __attribute__((aligned(1024))) ChunkSmem S;
+    const float* __restrict__ prep, bf16* __restrict__ Og, float* __restrict__ states,
+    float* __restrict__ chunk_states) {
+    __shared__ __attribute__((aligned(1024))) unsigned char SK[2][kC * kRowB];
+    __shared__ __attribute__((aligned(1024))) unsigned char SQ[2][kC * kRowB];
     const int b = ld_const(P.sc_level_br + l0 + blockIdx.x / H);
     const int h = blockIdx.x % H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, g = lane >> 5;
     const int dv = 32 * w + n;  // this lane's value row (accumulator column)
-    const int start = ld_const(P.sc_start + b), len = ld_const(P.sc_len + b);
+    const int start = ld_const(P.sc_start + b);
     const int init = ld_const(P.sc_init + b);
-    const size_t rs = (size_t)H * kD;  // elements per token in q, k, v, o
+    const int cbase = ld_const(P.sc_chunk_base + b);
+    const int nch = ld_const(P.sc_chunk_base + b + 1) - cbase;
 
     // S^T tiles: St[bk][j] = S[dv][32 bk + acc_row(j, g)].
     f32x16 St[4];
     if (init >= 0) {
         const float* src = states + (((size_t)init * H + h) * kD + dv) * kD;
 #pragma unroll
-        for (int bk = 0; bk < 4; ++bk)
+        for (int bk = 0; bk < 4; ++bk) {
+            float v[16];
+            ld16f(src + 32 * bk + 4 * g, 8, v);
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const float4 x = *reinterpret_cast<const float4*>(src + 32 * bk + 8 * q4 + 4 * g);
-                St[bk][4 * q4] = x.x;
-                St[bk][4 * q4 + 1] = x.y;
-                St[bk][4 * q4 + 2] = x.z;
-                St[bk][4 * q4 + 3] = x.w;
-            }
+            for (int j = 0; j < 16; ++j) St[bk][j] = v[j];
+        }
     } else {
 #pragma unroll
         for (int bk = 0; bk < 4; ++bk) St[bk] = zero16();
@@ -193,12 +380,12 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
     auto store_state = [&](float* dst_base) {
         float* dst = dst_base + ((size_t)h * kD + dv) * kD;
 #pragma unroll
-        for (int bk = 0; bk < 4; ++bk)
+        for (int bk = 0; bk < 4; ++bk) {
+            float v[16];
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-                *reinterpret_cast<float4*>(dst + 32 * bk + 8 * q4 + 4 * g) =
-                    make_float4(St[bk][4 * q4], St[bk][4 * q4 + 1], St[bk][4 * q4 + 2],
-                                St[bk][4 * q4 + 3]);
+            for (int j = 0; j < 16; ++j) v[j] = St[bk][j];
+            st16f(dst + 32 * bk + 4 * g, 8, v);
+        }
     };
     int ck = ld_const(P.sc_ck_ptr + b);
     const int ck_end = ld_const(P.sc_ck_ptr + b + 1);
@@ -208,145 +395,68 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
             ++ck;
         }
     };
-    const int cbase = chunk_states ? ld_const(P.sc_chunk_base + b) : 0;
+    int tr[4][2];
+    tr_offsets(lane, tr);
 
-    // Per-lane LDS offsets of the operands.  Row reads (A operand: row n, k values
-    // 16 ks + 8 g .. + 8) and the permuted pairs of 4 (k values 16 kh + 4 g .. + 4 and
-    // 16 kh + 8 + 4 g .. + 4, matching the accumulator rows a lane holds); transposed
-    // reads of K for the A operand of the state update (rows 4g + r/4 (+8) of each 16-row
-    // k-step, as the forward kernel's V^T reads).
-    int tr_[4][2];
-    {
-        const int r_in = lane & 15, dh = (lane >> 4) & 1;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int row = 4 * g + (r_in >> 2) + 8 * hf;
-                const int chunk = 4 * db + 2 * dh + ((r_in & 3) >> 1);
-                tr_[db][hf] = row * kRowB + swz<kD>(row, chunk) * 16 + 8 * (r_in & 1);
-            }
-    }
-    // 8-byte read of k values [k0, k0 + 4) of row `row` of a swizzled tile.
-    auto rd4 = [&](const unsigned char* base, int row, int k0) {
-        return *reinterpret_cast<const bf16x4*>(base + row * kRowB + swz<kD>(row, k0 >> 3) * 16 +
-                                                (k0 & 7) * 2);
-    };
-    auto rd8 = [&](const unsigned char* base, int row, int k0) {
-        return *reinterpret_cast<const bf16x8*>(base + row * kRowB + swz<kD>(row, k0 >> 3) * 16);
-    };
-
-    // Chunk loads: thread tid copies 16-byte pieces p = tid and tid + 256 of K, Q and V
-    // (row p / 16, columns 8 (p % 16) ..), zeros past the chunk's length; lanes below 64
-    // of wave 0 fetch alpha (t < 32) or beta.  Loaded into registers one chunk ahead.
-    bf16x8 pk[2], pq[2], pv[2];
-    float pab = 0.f;
-    auto fetch = [&](int r0, int nt) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int p = u * kThr + tid, t = p >> 4;
-            const size_t off = (size_t)(start + r0 + t) * rs + (size_t)h * kD + 8 * (p & 15);
-            const bool in = t < nt;
-            pk[u] = in ? ld16(Kg + off) : zero8();
-            pq[u] = in ? ld16(Qg + off) : zero8();
-            pv[u] = in ? ld16(Vg + off) : zero8();
-        }
-        if (tid < 2 * kC) {
-            const int t = tid & (kC - 1);
-            const size_t off = (size_t)(start + r0 + t) * H + h;
-            pab = t < nt ? (tid < kC ? Ag : Bg)[off] : (tid < kC ? 1.f : 0.f);
-        }
-    };
-    auto put = [&]() {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int p = u * kThr + tid;
-            const int off = tile_off<kD>(p >> 4, p & 15);
-            *reinterpret_cast<bf16x8*>(S.K + off) = pk[u];
-            *reinterpret_cast<bf16x8*>(S.Q + off) = pq[u];
-            *reinterpret_cast<bf16x8*>(S.V + off) = pv[u];
-        }
-        if (tid < 2 * kC) (tid < kC ? S.alpha : S.beta)[tid & (kC - 1)] = pab;
-    };
-    // next chunk end after own offset r: every 32 tokens and at every checkpoint offset
-    auto chunk_end = [&](int r, int ckp) {
-        int e = min(len, (r / kC + 1) * kC);
-        if (ckp < ck_end) e = min(e, max(ld_const(P.sc_ck_off + ckp), r + 1));
-        return e;
+    // The next chunk's operands, loaded into registers one chunk ahead.
+    bf16x8 pk[2], pq[2];
+    float pu[16], pt[16], pm[16], pgam[16], pbg[16], pgc = 1.f;
+    auto fetch = [&](int c) {
+        const size_t tok0 = ld_const(P.sc_chunk_tok + c);
+        const int nt = ld_const(P.sc_chunk_nt + c);
+        fetch_rows(Kg, tok0, nt, H, h, tid, pk);
+        fetch_rows(Qg, tok0, nt, H, h, tid, pq);
+        const float* rec = prep + ((size_t)c * H + h) * kRec;
+        ld16f(rec + kRecU + (w * 4 * 64 + lane) * 4, 64 * 4, pu);
+        ld16f(rec + kRecT + lane * 16, 4, pt);
+        ld16f(rec + kRecM + lane * 16, 4, pm);
+        ld16f(rec + kRecGam + 4 * g, 8, pgam);
+        ld16f(rec + kRecBG + 4 * g, 8, pbg);
+        pgc = rec[kRecGam + nt - 1];
     };
 
     save_due(0);
-    int r0 = 0;
-    int e0 = chunk_end(0, ck);
+    if (nch > 0) fetch(cbase);
     bf16 ostash[16];
-    int o_row0 = 0, o_nt = 0;
-    fetch(0, e0);
-    float* Lw = S.L[w];
-    float* Mw = S.M[w];
-    float* gam = S.gam[w];
-    float* lg = S.lg[w];
-    for (int ci = 0; r0 < len; ++ci) {
-        const int nt = e0 - r0;  // tokens in this chunk (1..32)
-        barrier();               // every wave is done with the previous chunk's LDS
-        put();
+    size_t o_tok = 0;
+    int o_nt = 0;
+    for (int ci = 0; ci < nch; ++ci) {
+        const int c = cbase + ci, buf = ci & 1;
+        const size_t tok0 = ld_const(P.sc_chunk_tok + c);
+        const int nt = ld_const(P.sc_chunk_nt + c);
+        const unsigned char* K = SK[buf];
+        const unsigned char* Q = SQ[buf];
+        put_rows(SK[buf], tid, pk);
+        put_rows(SQ[buf], tid, pq);
+        float cu[16], ct[16], cm[16], cgam[16], cbg[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            cu[j] = pu[j];
+            ct[j] = pt[j];
+            cm[j] = pm[j];
+            cgam[j] = pgam[j];
+            cbg[j] = pbg[j];
+        }
+        const float gC = pgc;
         wait_lds();
+        // (one barrier per chunk: the buffer written here was last read two chunks ago,
+        // before every wave passed the previous chunk's barrier)
         barrier();
-        // The previous chunk's outputs, stored now: issued before this chunk's loads, they
+        // The previous chunk's outputs, stored now: issued before the next loads, they
         // have a whole chunk to complete before the next wait on those loads.
         if (Og != nullptr && o_nt > 0) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const int t = acc_row(j, g);
-                if (t < o_nt) Og[(size_t)(start + o_row0 + t) * rs + (size_t)h * kD + dv] = ostash[j];
+                if (t < o_nt) Og[((o_tok + t) * H + h) * kD + dv] = ostash[j];
             }
         }
-        if (chunk_states) store_state(chunk_states + (size_t)(cbase + ci) * H * kD * kD);
-        const int r1 = e0;
-        int ck_next = ck;
-        while (ck_next < ck_end && ld_const(P.sc_ck_off + ck_next) <= r1) ++ck_next;
-        const int e1 = r1 < len ? chunk_end(r1, ck_next) : r1;
-        if (r1 < len) fetch(r1, e1 - r1);  // in flight while this chunk is computed
+        if (chunk_states) store_state(chunk_states + (size_t)c * H * kD * kD);
+        if (ci + 1 < nch) fetch(c + 1);  // in flight while this chunk is computed
 
-        // gamma_t (inclusive products of alpha over the chunk), in log2 and linear form
-        {
-            // (alpha is clamped at 2^-100: a zero gate still empties the state, and every
-            // ratio of gammas stays a finite difference of logarithms)
-            float la = lane < kC ? __log2f(fmaxf(S.alpha[lane], 7.8886e-31f)) : 0.f;
-#pragma unroll
-            for (int d = 1; d < kC; d <<= 1) {
-                const float y = __shfl_up(la, d, 64);
-                if ((lane & (kC - 1)) >= d) la += y;
-            }
-            if (lane < kC) {
-                lg[lane] = la;
-                gam[lane] = exp2f(la);
-            }
-        }
-        // K K^T and Q K^T (exact bf16 products), gated and masked into L and M.
-        f32x16 akk = zero16(), aqk = zero16();
-#pragma unroll
-        for (int ks = 0; ks < kD / 16; ++ks) {
-            const bf16x8 kb = rd8(S.K, n, 16 * ks + 8 * g);  // B: K row n (= key i)
-            akk = mfma_32x32x16(rd8(S.K, n, 16 * ks + 8 * g), kb, akk);
-            aqk = mfma_32x32x16(rd8(S.Q, n, 16 * ks + 8 * g), kb, aqk);
-        }
-        wait_lds();  // gam, lg written by this wave's lanes
-        __builtin_amdgcn_wave_barrier();
-        {
-            // accumulator: column i = n, rows t = acc_row(j, g)
-            const int i = n;
-            const float lgi = lg[i];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int t = acc_row(j, g);
-                const float gt = exp2f(lg[t] - lgi);
-                Lw[t * kC + i] = i < t ? S.beta[t] * akk[j] * gt : 0.f;
-                Mw[t * kC + i] = i <= t ? aqk[j] * gt : 0.f;
-            }
-        }
-        // X = K S_0^T and Y = Q S_0^T for this wave's value rows: A = K (Q) rows with the
-        // k values in the accumulator's row order, B = the state's hi and lo parts.
-        // (high and low parts into separate accumulators: four independent MFMA chains)
+        // X = K S_0^T and Y = Q S_0^T for this wave's value rows (A = K, Q rows with the
+        // k values in the accumulator's row order; B = the state's hi and lo parts, in
+        // separate accumulators: four independent chains).
         f32x16 X = zero16(), Y = zero16(), X2 = zero16(), Y2 = zero16();
 #pragma unroll
         for (int bk = 0; bk < 4; ++bk)
@@ -356,123 +466,267 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
 #pragma unroll
                 for (int e = 0; e < 8; ++e) split2(St[bk][8 * kh + e], shi, slo, e);
                 const int k0 = 32 * bk + 16 * kh + 4 * g;
-                const bf16x8 ak = cat(rd4(S.K, n, k0), rd4(S.K, n, k0 + 8));
-                const bf16x8 aq = cat(rd4(S.Q, n, k0), rd4(S.Q, n, k0 + 8));
+                const bf16x8 ak = rd_perm(K, n, k0);
+                const bf16x8 aq = rd_perm(Q, n, k0);
                 X = mfma_32x32x16(ak, shi, X);
                 X2 = mfma_32x32x16(ak, slo, X2);
                 Y = mfma_32x32x16(aq, shi, Y);
                 Y2 = mfma_32x32x16(aq, slo, Y2);
             }
+        // W = U - T diag(beta gamma) X
+        float xs[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            X[j] += X2[j];
-            Y[j] += Y2[j];
+        for (int j = 0; j < 16; ++j) xs[j] = (X[j] + X2[j]) * cbg[j];
+        f32x16 Wa = zero16();
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            bf16x8 th, tl, xh, xl;
+            split8(ct, kk, th, tl);
+            split8(xs, kk, xh, xl);
+            Wa = mfma_32x32x16(th, xh, Wa);
+            Wa = mfma_32x32x16(th, xl, Wa);
+            Wa = mfma_32x32x16(tl, xh, Wa);
         }
-        wait_lds();
-        __builtin_amdgcn_wave_barrier();
-        // R = diag(beta) (V - diag(gamma) X), then the triangular solve for W in place.
         float wv[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int t = acc_row(j, g);
-            const float vt = (float)*reinterpret_cast<const bf16*>(
-                S.V + t * kRowB + swz<kD>(t, dv >> 3) * 16 + (dv & 7) * 2);
-            wv[j] = S.beta[t] * (vt - gam[t] * X[j]);
-        }
-        fwd_solve(wv, Lw, nullptr, g);
-        // O = diag(gamma) Y + M W (M: A operand in the accumulator's row order).
-        bf16x8 whi[2], wlo[2];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) split2(wv[8 * kk + e], whi[kk], wlo[kk], e);
+        for (int j = 0; j < 16; ++j) wv[j] = cu[j] - Wa[j];
+        // O = diag(gamma) Y + M W
         f32x16 MW = zero16();
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            const float4 m0 = *reinterpret_cast<const float4*>(Mw + n * kC + 16 * kk + 4 * g);
-            const float4 m1 = *reinterpret_cast<const float4*>(Mw + n * kC + 16 * kk + 8 + 4 * g);
-            const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-            bf16x8 mhi, mlo;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) split2(mv[e], mhi, mlo, e);
-            MW = mfma_32x32x16(mhi, whi[kk], MW);
-            MW = mfma_32x32x16(mhi, wlo[kk], MW);
-            MW = mfma_32x32x16(mlo, whi[kk], MW);
+            bf16x8 mh, ml, wh, wl;
+            split8(cm, kk, mh, ml);
+            split8(wv, kk, wh, wl);
+            MW = mfma_32x32x16(mh, wh, MW);
+            MW = mfma_32x32x16(mh, wl, MW);
+            MW = mfma_32x32x16(ml, wh, MW);
         }
-        // (stored at the start of the next chunk)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) ostash[j] = (bf16)(gam[acc_row(j, g)] * Y[j] + MW[j]);
-        o_row0 = r0;
+        for (int j = 0; j < 16; ++j) ostash[j] = (bf16)(cgam[j] * (Y[j] + Y2[j]) + MW[j]);
+        o_tok = tok0;
         o_nt = nt;
         // S^T <- gamma_C S^T + K^T (diag(gamma_C / gamma) W): A = K^T (transposed reads),
         // B = the scaled W rows of this lane's value column.
-        const float gC = gam[nt - 1];
+        float us[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) us[j] = wv[j] * (gC / cgam[j]);
         bf16x8 uhi[2], ulo[2];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int t = acc_row(8 * kk + e, g);
-                split2(wv[8 * kk + e] * (gC / gam[t]), uhi[kk], ulo[kk], e);
-            }
+        split8(us, 0, uhi[0], ulo[0]);
+        split8(us, 1, uhi[1], ulo[1]);
 #pragma unroll
         for (int bk = 0; bk < 4; ++bk) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) St[bk][j] *= gC;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 ak = cat(lds8_tr(S.K, tr_[bk][0], 16 * kk * kRowB),
-                                      lds8_tr(S.K, tr_[bk][1], 16 * kk * kRowB));
+                const bf16x8 ak = rd_tr(K, tr, bk, kk);
                 St[bk] = mfma_32x32x16(ak, uhi[kk], St[bk]);
                 St[bk] = mfma_32x32x16(ak, ulo[kk], St[bk]);
             }
         }
-        r0 = r1;
-        e0 = e1;
-        save_due(r0);
+        save_due((int)(tok0 - start) + nt);
     }
     if (Og != nullptr) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const int t = acc_row(j, g);
-            if (t < o_nt) Og[(size_t)(start + o_row0 + t) * rs + (size_t)h * kD + dv] = ostash[j];
+            if (t < o_nt) Og[((o_tok + t) * H + h) * kD + dv] = ostash[j];
         }
     }
 }
 
-// ---------------------------------------------------------------- backward
+// ---------------------------------------------------------------- backward: dS (sequential)
+
+// Walks each branch's chunks in reverse carrying dS (the gradient of L = sum_t <dO_t, o_t>
+// with respect to the state at the current boundary), storing it at every chunk's end
+// into dsc [c][H][Dv][Dk] for the gradient kernel.  dstates [n_slots][H][Dv][Dk]: slots
+// that children (deeper levels, launched earlier) added their initial-state gradients to;
+// this branch's own initial-state gradient is added to its parent's slot.
+__global__ __launch_bounds__(kThr, 1) void gdn_chunk_dstate_kernel(
+    DevPlan P, int l0, int H, const bf16* __restrict__ Qg, const bf16* __restrict__ Kg,
+    const bf16* __restrict__ dOg, const float* __restrict__ prep, float* __restrict__ dsc,
+    float* __restrict__ dstates) {
+    __shared__ __attribute__((aligned(1024))) unsigned char SK[2][kC * kRowB];
+    __shared__ __attribute__((aligned(1024))) unsigned char SQ[2][kC * kRowB];
+    __shared__ __attribute__((aligned(1024))) unsigned char SO[2][kC * kRowB];
+    const int b = ld_const(P.sc_level_br + l0 + blockIdx.x / H);
+    const int h = blockIdx.x % H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, g = lane >> 5;
+    const int dv = 32 * w + n;
+    const int start = ld_const(P.sc_start + b), len = ld_const(P.sc_len + b);
+    const int init = ld_const(P.sc_init + b);
+    const int cbase = ld_const(P.sc_chunk_base + b);
+    const int nch = ld_const(P.sc_chunk_base + b + 1) - cbase;
+    const int ck_lo = ld_const(P.sc_ck_ptr + b);
+    int ckr = ld_const(P.sc_ck_ptr + b + 1) - 1;
+
+    // dS^T tiles (rows: keys, lane: value row)
+    f32x16 dSt[4];
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk) dSt[bk] = zero16();
+    auto add_handed = [&](int r) {
+        while (ckr >= ck_lo && ld_const(P.sc_ck_off + ckr) == r) {
+            const float* src =
+                dstates + (((size_t)ld_const(P.sc_ck_slot + ckr) * H + h) * kD + dv) * kD;
+#pragma unroll
+            for (int bk = 0; bk < 4; ++bk) {
+                float v[16];
+                ld16f(src + 32 * bk + 4 * g, 8, v);
+#pragma unroll
+                for (int j = 0; j < 16; ++j) dSt[bk][j] += v[j];
+            }
+            --ckr;
+        }
+    };
+    add_handed(len);
+    int tr[4][2];
+    tr_offsets(lane, tr);
+
+    bf16x8 pk[2], pq[2], po[2];
+    float pmt[16], ptt[16], pgam[16], pbg[16], pgc = 1.f;
+    auto fetch = [&](int c) {
+        const size_t tok0 = ld_const(P.sc_chunk_tok + c);
+        const int nt = ld_const(P.sc_chunk_nt + c);
+        fetch_rows(Kg, tok0, nt, H, h, tid, pk);
+        fetch_rows(Qg, tok0, nt, H, h, tid, pq);
+        fetch_rows(dOg, tok0, nt, H, h, tid, po);
+        const float* rec = prep + ((size_t)c * H + h) * kRec;
+        ld16f(rec + kRecMT + lane * 16, 4, pmt);
+        ld16f(rec + kRecTT + lane * 16, 4, ptt);
+        ld16f(rec + kRecGam + 4 * g, 8, pgam);
+        ld16f(rec + kRecBG + 4 * g, 8, pbg);
+        pgc = rec[kRecGam + nt - 1];
+    };
+    if (nch > 0) fetch(cbase + nch - 1);
+    for (int ci = nch - 1; ci >= 0; --ci) {
+        const int c = cbase + ci, buf = ci & 1;
+        const int r0 = ld_const(P.sc_chunk_tok + c) - start;
+        const unsigned char* K = SK[buf];
+        const unsigned char* Q = SQ[buf];
+        const unsigned char* dO = SO[buf];
+        put_rows(SK[buf], tid, pk);
+        put_rows(SQ[buf], tid, pq);
+        put_rows(SO[buf], tid, po);
+        float cmt[16], ctt[16], cgam[16], cbg[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            cmt[j] = pmt[j];
+            ctt[j] = ptt[j];
+            cgam[j] = pgam[j];
+            cbg[j] = pbg[j];
+        }
+        const float gC = pgc;
+        wait_lds();
+        barrier();
+        {
+            float* dst = dsc + (((size_t)c * H + h) * kD + dv) * kD;
+#pragma unroll
+            for (int bk = 0; bk < 4; ++bk) {
+                float v[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) v[j] = dSt[bk][j];
+                st16f(dst + 32 * bk + 4 * g, 8, v);
+            }
+        }
+        if (ci > 0) fetch(c - 1);
+
+        // dW = M^T dO + diag(gamma_C / gamma) K dS_C^T
+        f32x16 tA = zero16(), tB = zero16(), tB2 = zero16();
+        bf16x8 o8[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            bf16x8 mh, ml;
+            split8(cmt, kk, mh, ml);
+            o8[kk] = rd_tr(dO, tr, w, kk);
+            tA = mfma_32x32x16(mh, o8[kk], tA);
+            tA = mfma_32x32x16(ml, o8[kk], tA);
+        }
+#pragma unroll
+        for (int bk = 0; bk < 4; ++bk)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                bf16x8 shi, slo;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) split2(dSt[bk][8 * kh + e], shi, slo, e);
+                const bf16x8 ak = rd_perm(K, n, 32 * bk + 16 * kh + 4 * g);
+                tB = mfma_32x32x16(ak, shi, tB);
+                tB2 = mfma_32x32x16(ak, slo, tB2);
+            }
+        float dw[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dw[j] = tA[j] + (gC / cgam[j]) * (tB[j] + tB2[j]);
+        // dR = T^T dW; dX = -diag(beta gamma) dR, dY = diag(gamma) dO
+        f32x16 dR = zero16();
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            bf16x8 th, tl, wh, wl;
+            split8(ctt, kk, th, tl);
+            split8(dw, kk, wh, wl);
+            dR = mfma_32x32x16(th, wh, dR);
+            dR = mfma_32x32x16(th, wl, dR);
+            dR = mfma_32x32x16(tl, wh, dR);
+        }
+        bf16x8 xh[2], xl[2], yh[2], yl[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int j = 8 * kk + e;
+                split2(-cbg[j] * dR[j], xh[kk], xl[kk], e);
+                split2(cgam[j] * (float)o8[kk][e], yh[kk], yl[kk], e);
+            }
+        // dS_0^T = gamma_C dS_C^T + K^T dX + Q^T dY
+#pragma unroll
+        for (int bk = 0; bk < 4; ++bk) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) dSt[bk][j] *= gC;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 ak = rd_tr(K, tr, bk, kk);
+                const bf16x8 aq = rd_tr(Q, tr, bk, kk);
+                dSt[bk] = mfma_32x32x16(ak, xh[kk], dSt[bk]);
+                dSt[bk] = mfma_32x32x16(ak, xl[kk], dSt[bk]);
+                dSt[bk] = mfma_32x32x16(aq, yh[kk], dSt[bk]);
+                dSt[bk] = mfma_32x32x16(aq, yl[kk], dSt[bk]);
+            }
+        }
+        add_handed(r0);
+    }
+    // the gradient of this branch's initial state goes to its parent's fork slot
+    if (init >= 0) {
+        float* dst = dstates + (((size_t)init * H + h) * kD + dv) * kD;
+#pragma unroll
+        for (int bk = 0; bk < 4; ++bk)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) atomicAdd(dst + 32 * bk + acc_row(j, g), dSt[bk][j]);
+    }
+}
+
+// ---------------------------------------------------------------- backward: gradients (parallel)
 //
-// Gradients of L = sum_t <dO_t, o_t> chunk by chunk in reverse, from the state at the
-// start of every chunk (saved by a forward pass) and the gradient dS_C of the state at
-// the chunk's end (carried from the chunk after it).  With R = diag(beta) (V - diag(gamma)
-// X), X = K S_0^T, Y = Q S_0^T, N = I + diag(beta) LG (LG = K K^T o Gamma_strict),
-// M = Q K^T o Gamma_incl, W = N^{-1} R:
-//     dW   = M^T dO + diag(gamma_C / gamma) K dS_C^T
-//     dR   = N^{-T} dW                 (back substitution)
-//     d(diag(beta) LG) = -dR W^T       (strict lower part)
+// Per (chunk, head), from S_0 (the state at the chunk's start) and dS_C (the state
+// gradient at its end), with R = diag(beta) (V - diag(gamma) X), W = N^{-1} R:
+//     dW   = M^T dO + diag(gamma_C / gamma) K dS_C^T,  dR = N^{-T} dW
+//     d(diag(beta) LG) = -dR W^T (strict lower),  dM = dO W^T (lower with diagonal)
 //     dV   = diag(beta) dR,  dX = -diag(beta gamma) dR,  dY = diag(gamma) dO
-//     dM   = dO W^T                    (lower part with diagonal)
 //     dQ   = dY S_0 + (dM o Gamma) K
 //     dK   = dX S_0 + diag(gamma_C / gamma) W dS_C + (dA + dA^T) K + (dM o Gamma)^T Q,
 //            dA = diag(beta) d(diag(beta) LG) o Gamma
-//     dS_0 = gamma_C dS_C + K^T dX + Q^T dY
 // and the gates through log gamma (natural log; every factor gamma_t / gamma_i and every
 // gamma_t, gamma_C contributes its own term), summed from the end of the chunk to give
-// d log alpha.  A child's initial-state gradient is added to its parent's at the fork
-// offset (atomically: siblings forked at one offset share a slot).
-//
-// Wave w owns value rows [32 w, 32 w + 32) for everything that evolves row by row (the
-// state, dS, W, dR, dV) and key columns [32 w, 32 w + 32) of the chunk's dQ and dK; the
-// sums over value rows (dQ, dK partials, dR W^T, dO W^T, the gate and beta terms) are
+// d log alpha.  Wave w owns value rows [32 w, 32 w + 32) for what runs per value row (W,
+// dR, dV) and key columns [32 w, 32 w + 32) of dQ and dK; sums over value rows are
 // gathered in LDS.
-struct ChunkBwdSmem {
+namespace {
+struct GradSmem {
     unsigned char K[kC * kRowB];
     unsigned char Q[kC * kRowB];
     unsigned char V[kC * kRowB];
     unsigned char dO[kC * kRowB];
     float alpha[kC], beta[kC], gam[kC], lg[kC];
     float LG[kC * kC];   // gated K K^T, strict lower, [t][i]
-    float LGT[kC * kC];  // its transpose
     float M[kC * kC];    // gated Q K^T, lower with diagonal, [t][i]
     float MT[kC * kC];   // its transpose
     float P[kC * kC];    // sum over value rows of dR_t . W_i, then dA
@@ -486,334 +740,280 @@ struct ChunkBwdSmem {
     float S0[kWaves][32 * 32];  // one key tile of S_0: [key][value row]
     float dS[kWaves][32 * 32];  // the same tile of dS_C
 };
+}  // namespace
 
-// Sum of v[j] over the 32 lanes of this lane's half (lanes with the same g).
-__device__ __forceinline__ void half_sum16(float (&v)[16]) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) v[j] += __shfl_xor(v[j], off);
-}
-
-__global__ __launch_bounds__(kThr, 1) void gdn_chunk_bwd_kernel(
-    DevPlan P, int l0, int H, const bf16* __restrict__ Qg, const bf16* __restrict__ Kg,
+__global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
+    DevPlan P, int H, const bf16* __restrict__ Qg, const bf16* __restrict__ Kg,
     const bf16* __restrict__ Vg, const float* __restrict__ Ag, const float* __restrict__ Bg,
-    const bf16* __restrict__ dOg, const float* __restrict__ chunk_states,
-    float* __restrict__ dstates, bf16* __restrict__ dQg, bf16* __restrict__ dKg,
-    bf16* __restrict__ dVg, float* __restrict__ dAg, float* __restrict__ dBg) {
-    __shared__ __attribute__((aligned(1024))) ChunkBwdSmem S;
-    const int b = ld_const(P.sc_level_br + l0 + blockIdx.x / H);
-    const int h = blockIdx.x % H;
+    const bf16* __restrict__ dOg, const float* __restrict__ prep,
+    const float* __restrict__ chunk_states, const float* __restrict__ dsc,
+    bf16* __restrict__ dQg, bf16* __restrict__ dKg, bf16* __restrict__ dVg,
+    float* __restrict__ dAg, float* __restrict__ dBg) {
+    __shared__ __attribute__((aligned(1024))) GradSmem S;
+    const int c = blockIdx.x / H, h = blockIdx.x % H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, g = lane >> 5;
     const int dv = 32 * w + n;
-    const int start = ld_const(P.sc_start + b), len = ld_const(P.sc_len + b);
-    const int init = ld_const(P.sc_init + b);
-    const size_t rs = (size_t)H * kD;
-    const int ck_lo = ld_const(P.sc_ck_ptr + b);
-    int ckr = ld_const(P.sc_ck_ptr + b + 1) - 1;
-    const int cbase = ld_const(P.sc_chunk_base + b);
-    const int nch = ld_const(P.sc_chunk_base + b + 1) - cbase;
+    const size_t tok0 = ld_const(P.sc_chunk_tok + c);
+    const int nt = ld_const(P.sc_chunk_nt + c);
+    const float* rec = prep + ((size_t)c * H + h) * kRec;
+    const float* S0g = chunk_states + (((size_t)c * H + h) * kD + dv) * kD;
+    const float* dSg = dsc + (((size_t)c * H + h) * kD + dv) * kD;
     float* Wl = S.W[w];
     float* dRl = S.dR[w];
     float* S0l = S.S0[w];
     float* dSl = S.dS[w];
-
-    int tr_[4][2];
-    {
-        const int r_in = lane & 15, dh = (lane >> 4) & 1;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int row = 4 * g + (r_in >> 2) + 8 * hf;
-                const int chunk = 4 * db + 2 * dh + ((r_in & 3) >> 1);
-                tr_[db][hf] = row * kRowB + swz<kD>(row, chunk) * 16 + 8 * (r_in & 1);
-            }
-    }
-    auto rd4 = [&](const unsigned char* base, int row, int k0) {
-        return *reinterpret_cast<const bf16x4*>(base + row * kRowB + swz<kD>(row, k0 >> 3) * 16 +
-                                                (k0 & 7) * 2);
-    };
-    auto rd8 = [&](const unsigned char* base, int row, int k0) {
-        return *reinterpret_cast<const bf16x8*>(base + row * kRowB + swz<kD>(row, k0 >> 3) * 16);
-    };
+    int tr[4][2];
+    tr_offsets(lane, tr);
     // 8 floats at p[0..3] and p[off..off+3], split into bf16 high and low parts
     auto ld_split = [&](const float* p, int off, bf16x8& hi, bf16x8& lo, float scale) {
         const float4 a = *reinterpret_cast<const float4*>(p);
-        const float4 c = *reinterpret_cast<const float4*>(p + off);
-        const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+        const float4 cc = *reinterpret_cast<const float4*>(p + off);
+        const float v[8] = {a.x, a.y, a.z, a.w, cc.x, cc.y, cc.z, cc.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) split2(v[e] * scale, hi, lo, e);
     };
 
-    // dS^T tiles (rows: keys, lane: value row), the gradient of the state at the current
-    // boundary; starts with what children forked at the branch's end handed over.
-    f32x16 dSt[4];
+    // ---- loads: chunk inputs (zeros past nt; alpha 1, beta 0), cleared sums
+    {
+        bf16x8 rk[2], rq[2], rv[2], ro[2];
+        fetch_rows(Kg, tok0, nt, H, h, tid, rk);
+        fetch_rows(Qg, tok0, nt, H, h, tid, rq);
+        fetch_rows(Vg, tok0, nt, H, h, tid, rv);
+        fetch_rows(dOg, tok0, nt, H, h, tid, ro);
+        put_rows(S.K, tid, rk);
+        put_rows(S.Q, tid, rq);
+        put_rows(S.V, tid, rv);
+        put_rows(S.dO, tid, ro);
+    }
+    if (tid < 2 * kC) {
+        const int t = tid & (kC - 1);
+        (tid < kC ? S.alpha : S.beta)[t] =
+            t < nt ? (tid < kC ? Ag : Bg)[(tok0 + t) * H + h] : (tid < kC ? 1.f : 0.f);
+        (tid < kC ? S.dg : S.db)[t] = 0.f;
+    }
+    {
+        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int bk = 0; bk < 4; ++bk) dSt[bk] = zero16();
-    auto add_handed = [&](int r) {
-        while (ckr >= ck_lo && ld_const(P.sc_ck_off + ckr) == r) {
-            const float* src =
-                dstates + (((size_t)ld_const(P.sc_ck_slot + ckr) * H + h) * kD + dv) * kD;
-#pragma unroll
-            for (int bk = 0; bk < 4; ++bk)
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const float4 x = *reinterpret_cast<const float4*>(src + 32 * bk + 8 * q4 + 4 * g);
-                    dSt[bk][4 * q4] += x.x;
-                    dSt[bk][4 * q4 + 1] += x.y;
-                    dSt[bk][4 * q4 + 2] += x.z;
-                    dSt[bk][4 * q4 + 3] += x.w;
-                }
-            --ckr;
+        for (int u = 0; u < kC * kD / 4 / kThr; ++u) {
+            reinterpret_cast<float4*>(S.dQa)[u * kThr + tid] = z;
+            reinterpret_cast<float4*>(S.dKa)[u * kThr + tid] = z;
         }
-    };
-    add_handed(len);
+        reinterpret_cast<float4*>(S.P)[tid] = z;
+        reinterpret_cast<float4*>(S.dM)[tid] = z;
+    }
+    wait_lds();
+    barrier();
 
-    int r1 = len;
-    for (int j = nch - 1; j >= 0; --j) {
-        int r0 = ((r1 - 1) / kC) * kC;
-        if (ckr >= ck_lo) r0 = max(r0, ld_const(P.sc_ck_off + ckr));
-        const int nt = r1 - r0;
-
-        barrier();  // the previous chunk is done with every shared array
-        // ---- loads: chunk inputs (zeros past nt; alpha 1, beta 0), cleared sums, S_0
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int p = u * kThr + tid, t = p >> 4;
-            const size_t off = (size_t)(start + r0 + t) * rs + (size_t)h * kD + 8 * (p & 15);
-            const bool in = t < nt;
-            const int lo = tile_off<kD>(t, p & 15);
-            *reinterpret_cast<bf16x8*>(S.K + lo) = in ? ld16(Kg + off) : zero8();
-            *reinterpret_cast<bf16x8*>(S.Q + lo) = in ? ld16(Qg + off) : zero8();
-            *reinterpret_cast<bf16x8*>(S.V + lo) = in ? ld16(Vg + off) : zero8();
-            *reinterpret_cast<bf16x8*>(S.dO + lo) = in ? ld16(dOg + off) : zero8();
+    // ---- gammas and the gated score matrices (wave 0); X, Y (every wave)
+    if (w == 0) {
+        const float la = log2_gamma(S.alpha, lane);
+        if (lane < kC) {
+            S.lg[lane] = la;
+            S.gam[lane] = exp2f(la);
         }
-        if (tid < 2 * kC) {
-            const int t = tid & (kC - 1);
-            const size_t off = (size_t)(start + r0 + t) * H + h;
-            (tid < kC ? S.alpha : S.beta)[t] = t < nt ? (tid < kC ? Ag : Bg)[off] : (tid < kC ? 1.f : 0.f);
-            (tid < kC ? S.dg : S.db)[t] = 0.f;
-        }
-        {
-            const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+        f32x16 akk = zero16(), aqk = zero16();
 #pragma unroll
-            for (int u = 0; u < kC * kD / 4 / kThr; ++u) {
-                reinterpret_cast<float4*>(S.dQa)[u * kThr + tid] = z;
-                reinterpret_cast<float4*>(S.dKa)[u * kThr + tid] = z;
-            }
-            reinterpret_cast<float4*>(S.P)[tid] = z;
-            reinterpret_cast<float4*>(S.dM)[tid] = z;
-        }
-        f32x16 St[4];
-        {
-            const float* src = chunk_states + (((size_t)(cbase + j) * H + h) * kD + dv) * kD;
-#pragma unroll
-            for (int bk = 0; bk < 4; ++bk)
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const float4 x = *reinterpret_cast<const float4*>(src + 32 * bk + 8 * q4 + 4 * g);
-                    St[bk][4 * q4] = x.x;
-                    St[bk][4 * q4 + 1] = x.y;
-                    St[bk][4 * q4 + 2] = x.z;
-                    St[bk][4 * q4 + 3] = x.w;
-                }
+        for (int ks = 0; ks < kD / 16; ++ks) {
+            const bf16x8 kb = rd8(S.K, n, 16 * ks + 8 * g);
+            akk = mfma_32x32x16(rd8(S.K, n, 16 * ks + 8 * g), kb, akk);
+            aqk = mfma_32x32x16(rd8(S.Q, n, 16 * ks + 8 * g), kb, aqk);
         }
         wait_lds();
-        barrier();
-
-        // ---- gammas and the gated score matrices (wave 0); X, Y (every wave)
-        if (w == 0) {
-            float la = lane < kC ? __log2f(fmaxf(S.alpha[lane], 7.8886e-31f)) : 0.f;
-#pragma unroll
-            for (int d = 1; d < kC; d <<= 1) {
-                const float y = __shfl_up(la, d, 64);
-                if ((lane & (kC - 1)) >= d) la += y;
-            }
-            if (lane < kC) {
-                S.lg[lane] = la;
-                S.gam[lane] = exp2f(la);
-            }
-            f32x16 akk = zero16(), aqk = zero16();
-#pragma unroll
-            for (int ks = 0; ks < kD / 16; ++ks) {
-                const bf16x8 kb = rd8(S.K, n, 16 * ks + 8 * g);
-                akk = mfma_32x32x16(rd8(S.K, n, 16 * ks + 8 * g), kb, akk);
-                aqk = mfma_32x32x16(rd8(S.Q, n, 16 * ks + 8 * g), kb, aqk);
-            }
-            wait_lds();
-            __builtin_amdgcn_wave_barrier();
-            const int i = n;
-            const float lgi = S.lg[i];
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj) {
-                const int t = acc_row(jj, g);
-                const float gt = exp2f(S.lg[t] - lgi);
-                const float lgv = i < t ? akk[jj] * gt : 0.f;
-                const float mv = i <= t ? aqk[jj] * gt : 0.f;
-                S.LG[t * kC + i] = lgv;
-                S.LGT[i * kC + t] = lgv;
-                S.M[t * kC + i] = mv;
-                S.MT[i * kC + t] = mv;
-            }
-        }
-        f32x16 X = zero16(), Y = zero16();
-#pragma unroll
-        for (int bk = 0; bk < 4; ++bk)
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
-                bf16x8 shi, slo;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) split2(St[bk][8 * kh + e], shi, slo, e);
-                const int k0 = 32 * bk + 16 * kh + 4 * g;
-                const bf16x8 ak = cat(rd4(S.K, n, k0), rd4(S.K, n, k0 + 8));
-                const bf16x8 aq = cat(rd4(S.Q, n, k0), rd4(S.Q, n, k0 + 8));
-                X = mfma_32x32x16(ak, shi, X);
-                X = mfma_32x32x16(ak, slo, X);
-                Y = mfma_32x32x16(aq, shi, Y);
-                Y = mfma_32x32x16(aq, slo, Y);
-            }
-        wait_lds();
-        barrier();
-
-        const float gC = S.gam[nt - 1];
-        // per row t of this lane (accumulator order): V and dO of this lane's value column
-        auto vat = [&](const unsigned char* base, int t) {
-            return (float)*reinterpret_cast<const bf16*>(base + t * kRowB +
-                                                         swz<kD>(t, dv >> 3) * 16 + (dv & 7) * 2);
-        };
-        // gate term of O = diag(gamma) Y + ...: gamma_t <dO_t, Y_t>, summed over value rows
-        {
-            float r[16];
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj) {
-                const int t = acc_row(jj, g);
-                r[jj] = S.gam[t] * vat(S.dO, t) * Y[jj];
-            }
-            half_sum16(r);
-            if (n == 0) {
-#pragma unroll
-                for (int jj = 0; jj < 16; ++jj) atomicAdd(&S.dg[acc_row(jj, g)], r[jj]);
-            }
-        }
-        // ---- forward: R and the solve for W (as in the forward kernel); vx = V - gamma X
-        float wv[16], vx[16];
+        __builtin_amdgcn_wave_barrier();
+        const int i = n;
+        const float lgi = S.lg[i];
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
             const int t = acc_row(jj, g);
-            vx[jj] = vat(S.V, t) - S.gam[t] * X[jj];
-            wv[jj] = S.beta[t] * vx[jj];
+            const float gt = exp2f(S.lg[t] - lgi);
+            const float mv = i <= t ? aqk[jj] * gt : 0.f;
+            S.LG[t * kC + i] = i < t ? akk[jj] * gt : 0.f;
+            S.M[t * kC + i] = mv;
+            S.MT[i * kC + t] = mv;
         }
-        fwd_solve(wv, S.LG, S.beta, g);
-        // ---- dW = M^T dO + diag(gamma_C / gamma) K dS_C^T
-        f32x16 tA = zero16(), tB = zero16();
+    }
+    f32x16 X = zero16(), Y = zero16(), X2 = zero16(), Y2 = zero16();
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk) {
+        float sv[16];
+        ld16f(S0g + 32 * bk + 4 * g, 8, sv);
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+            bf16x8 shi, slo;
+            split8(sv, kh, shi, slo);
+            const int k0 = 32 * bk + 16 * kh + 4 * g;
+            const bf16x8 ak = rd_perm(S.K, n, k0);
+            const bf16x8 aq = rd_perm(S.Q, n, k0);
+            X = mfma_32x32x16(ak, shi, X);
+            X2 = mfma_32x32x16(ak, slo, X2);
+            Y = mfma_32x32x16(aq, shi, Y);
+            Y2 = mfma_32x32x16(aq, slo, Y2);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        X[j] += X2[j];
+        Y[j] += Y2[j];
+    }
+    float gam[16], bg[16];
+    ld16f(rec + kRecGam + 4 * g, 8, gam);
+    ld16f(rec + kRecBG + 4 * g, 8, bg);
+    const float gC = rec[kRecGam + nt - 1];
+    wait_lds();
+    barrier();
+
+    // gate term of O = diag(gamma) Y + ...: gamma_t <dO_t, Y_t>, summed over value rows
+    {
+        float r[16];
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) r[jj] = gam[jj] * tile_at(S.dO, acc_row(jj, g), dv) * Y[jj];
+        half_sum16(r);
+        if (n == 0) {
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) atomicAdd(&S.dg[acc_row(jj, g)], r[jj]);
+        }
+    }
+    // ---- W = U - T diag(beta gamma) X; vx = V - gamma X
+    float wv[16], vx[16];
+    {
+        float tv[16], xs[16];
+        ld16f(rec + kRecT + lane * 16, 4, tv);
+        ld16f(rec + kRecU + (w * 4 * 64 + lane) * 4, 64 * 4, wv);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            xs[j] = X[j] * bg[j];
+            vx[j] = tile_at(S.V, acc_row(j, g), dv) - gam[j] * X[j];
+        }
+        f32x16 Wa = zero16();
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            bf16x8 th, tl, xh, xl;
+            split8(tv, kk, th, tl);
+            split8(xs, kk, xh, xl);
+            Wa = mfma_32x32x16(th, xh, Wa);
+            Wa = mfma_32x32x16(th, xl, Wa);
+            Wa = mfma_32x32x16(tl, xh, Wa);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) wv[j] -= Wa[j];
+    }
+    // ---- dW = M^T dO + diag(gamma_C / gamma) K dS_C^T; dR = T^T dW
+    float dr[16], tb[16];
+    {
+        f32x16 tA = zero16(), tB = zero16(), tB2 = zero16();
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             bf16x8 mhi, mlo;
             ld_split(S.MT + n * kC + 16 * kk + 4 * g, 8, mhi, mlo, 1.f);
-            const bf16x8 bo = cat(lds8_tr(S.dO, tr_[w][0], 16 * kk * kRowB),
-                                  lds8_tr(S.dO, tr_[w][1], 16 * kk * kRowB));
+            const bf16x8 bo = rd_tr(S.dO, tr, w, kk);
             tA = mfma_32x32x16(mhi, bo, tA);
             tA = mfma_32x32x16(mlo, bo, tA);
         }
 #pragma unroll
-        for (int bk = 0; bk < 4; ++bk)
+        for (int bk = 0; bk < 4; ++bk) {
+            float sv[16];
+            ld16f(dSg + 32 * bk + 4 * g, 8, sv);
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
                 bf16x8 shi, slo;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) split2(dSt[bk][8 * kh + e], shi, slo, e);
-                const int k0 = 32 * bk + 16 * kh + 4 * g;
-                const bf16x8 ak = cat(rd4(S.K, n, k0), rd4(S.K, n, k0 + 8));
+                split8(sv, kh, shi, slo);
+                const bf16x8 ak = rd_perm(S.K, n, 32 * bk + 16 * kh + 4 * g);
                 tB = mfma_32x32x16(ak, shi, tB);
-                tB = mfma_32x32x16(ak, slo, tB);
+                tB2 = mfma_32x32x16(ak, slo, tB2);
             }
-        float dr[16], tb[16];
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-            tb[jj] = tB[jj] * (gC / S.gam[acc_row(jj, g)]);
-            dr[jj] = tA[jj] + tb[jj];
         }
-        // ---- dR = N^{-T} dW: back substitution, N^T[t][s] = beta_s LG[s][t] (s > t)
-        bwd_solve(dr, S.LGT, S.beta, g);
-        // ---- W and dR to LDS ([t][value row]); dV; the beta and gate terms per row
+        float dw[16], ttv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            tb[j] = (tB[j] + tB2[j]) * (gC / gam[j]);
+            dw[j] = tA[j] + tb[j];
+        }
+        ld16f(rec + kRecTT + lane * 16, 4, ttv);
+        f32x16 dRa = zero16();
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            bf16x8 th, tl, wh, wl;
+            split8(ttv, kk, th, tl);
+            split8(dw, kk, wh, wl);
+            dRa = mfma_32x32x16(th, wh, dRa);
+            dRa = mfma_32x32x16(th, wl, dRa);
+            dRa = mfma_32x32x16(tl, wh, dRa);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dr[j] = dRa[j];
+    }
+    // ---- W and dR to LDS ([t][value row]); dV; the beta and gate terms per row
+    float sx = 0.f;  // terms of d L / d log gamma_C: this lane's part
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+        const int t = acc_row(jj, g);
+        Wl[t * 32 + n] = wv[jj];
+        dRl[t * 32 + n] = dr[jj];
+        if (t < nt) dVg[((tok0 + t) * H + h) * kD + dv] = (bf16)(S.beta[t] * dr[jj]);
+    }
+    {
+        float rdb[16], rdg[16];
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
             const int t = acc_row(jj, g);
-            Wl[t * 32 + n] = wv[jj];
-            dRl[t * 32 + n] = dr[jj];
-            if (t < nt)
-                dVg[(size_t)(start + r0 + t) * rs + (size_t)h * kD + dv] =
-                    (bf16)(S.beta[t] * dr[jj]);
+            rdb[jj] = dr[jj] * vx[jj];
+            const float x = wv[jj] * tb[jj];
+            sx += x;
+            // -beta_t gamma_t <dR_t, X_t> - x_t, with gamma_t X_t = V_t - vx_t
+            rdg[jj] = -S.beta[t] * dr[jj] * (tile_at(S.V, t, dv) - vx[jj]) - x;
         }
-        {
-            float rdb[16], rdg[16];
-            float sx = 0.f;
+        half_sum16(rdb);
+        half_sum16(rdg);
+        if (n == 0) {
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj) {
                 const int t = acc_row(jj, g);
-                rdb[jj] = dr[jj] * vx[jj];
-                const float x = wv[jj] * tb[jj];
-                sx += x;
-                // -beta_t gamma_t <dR_t, X_t> - x_t, with gamma_t X_t = V_t - vx_t
-                rdg[jj] = -S.beta[t] * dr[jj] * (vat(S.V, t) - vx[jj]) - x;
-            }
-            // gamma_C <dS_C, S_0> over this lane's elements
-#pragma unroll
-            for (int bk = 0; bk < 4; ++bk)
-#pragma unroll
-                for (int jj = 0; jj < 16; ++jj) sx += gC * dSt[bk][jj] * St[bk][jj];
-            half_sum16(rdb);
-            half_sum16(rdg);
-            sx += __shfl_xor(sx, 32);
-#pragma unroll
-            for (int off = 16; off >= 1; off >>= 1) sx += __shfl_xor(sx, off);
-            if (n == 0) {
-#pragma unroll
-                for (int jj = 0; jj < 16; ++jj) {
-                    const int t = acc_row(jj, g);
-                    atomicAdd(&S.db[t], rdb[jj]);
-                    atomicAdd(&S.dg[t], rdg[jj]);
-                }
-            }
-            if (lane == 0) atomicAdd(&S.dg[nt - 1], sx);
-        }
-        wait_lds();
-        __builtin_amdgcn_wave_barrier();
-        // ---- sums over this wave's value rows: dR W^T and dO W^T (C x C)
-        {
-            f32x16 pp = zero16(), pm = zero16();
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                bf16x8 ah, al, bh, bl;
-                ld_split(dRl + n * 32 + 16 * ks + 8 * g, 4, ah, al, 1.f);
-                ld_split(Wl + n * 32 + 16 * ks + 8 * g, 4, bh, bl, 1.f);
-                pp = mfma_32x32x16(ah, bh, pp);
-                pp = mfma_32x32x16(ah, bl, pp);
-                pp = mfma_32x32x16(al, bh, pp);
-                const bf16x8 ao = rd8(S.dO, n, 32 * w + 16 * ks + 8 * g);
-                pm = mfma_32x32x16(ao, bh, pm);
-                pm = mfma_32x32x16(ao, bl, pm);
-            }
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj) {
-                const int t = acc_row(jj, g);
-                atomicAdd(&S.P[t * kC + n], pp[jj]);
-                atomicAdd(&S.dM[t * kC + n], pm[jj]);
+                atomicAdd(&S.db[t], rdb[jj]);
+                atomicAdd(&S.dg[t], rdg[jj]);
             }
         }
-        // ---- dQ, dK partials over this wave's value rows, one key tile at a time
-        float gmn = S.gam[n], btn = S.beta[n];  // the A operands' rows are t = n
-        const float xs = -btn * gmn, ws_ = gC / gmn;
+    }
+    wait_lds();
+    __builtin_amdgcn_wave_barrier();
+    // ---- sums over this wave's value rows: dR W^T and dO W^T (C x C)
+    {
+        f32x16 pp = zero16(), pm = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 ah, al, bh, bl;
+            ld_split(dRl + n * 32 + 16 * ks + 8 * g, 4, ah, al, 1.f);
+            ld_split(Wl + n * 32 + 16 * ks + 8 * g, 4, bh, bl, 1.f);
+            pp = mfma_32x32x16(ah, bh, pp);
+            pp = mfma_32x32x16(ah, bl, pp);
+            pp = mfma_32x32x16(al, bh, pp);
+            const bf16x8 ao = rd8(S.dO, n, 32 * w + 16 * ks + 8 * g);
+            pm = mfma_32x32x16(ao, bh, pm);
+            pm = mfma_32x32x16(ao, bl, pm);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+            const int t = acc_row(jj, g);
+            atomicAdd(&S.P[t * kC + n], pp[jj]);
+            atomicAdd(&S.dM[t * kC + n], pm[jj]);
+        }
+    }
+    // ---- dQ, dK partials over this wave's value rows, one key tile at a time
+    {
+        const float gmn = S.gam[n], btn = S.beta[n];  // the A operands' rows are t = n
+        const float xsc = -btn * gmn, wsc = gC / gmn;
 #pragma unroll
         for (int bk = 0; bk < 4; ++bk) {
+            float sv[16], dsv[16];
+            ld16f(S0g + 32 * bk + 4 * g, 8, sv);
+            ld16f(dSg + 32 * bk + 4 * g, 8, dsv);
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj) {
                 const int kr = acc_row(jj, g);
-                S0l[kr * 32 + n] = St[bk][jj];
-                dSl[kr * 32 + n] = dSt[bk][jj];
+                S0l[kr * 32 + n] = sv[jj];
+                dSl[kr * 32 + n] = dsv[jj];
+                sx += gC * sv[jj] * dsv[jj];  // gamma_C <dS_C, S_0>
             }
             wait_lds();
             __builtin_amdgcn_wave_barrier();
@@ -821,8 +1021,8 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_bwd_kernel(
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 bf16x8 xh, xl, wh, wl, sh, sl, dh, dl, yh, yl;
-                ld_split(dRl + n * 32 + 16 * ks + 8 * g, 4, xh, xl, xs);
-                ld_split(Wl + n * 32 + 16 * ks + 8 * g, 4, wh, wl, ws_);
+                ld_split(dRl + n * 32 + 16 * ks + 8 * g, 4, xh, xl, xsc);
+                ld_split(Wl + n * 32 + 16 * ks + 8 * g, 4, wh, wl, wsc);
                 ld_split(S0l + n * 32 + 16 * ks + 8 * g, 4, sh, sl, 1.f);
                 ld_split(dSl + n * 32 + 16 * ks + 8 * g, 4, dh, dl, 1.f);
                 {
@@ -849,140 +1049,99 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_bwd_kernel(
             wait_lds();
             __builtin_amdgcn_wave_barrier();
         }
-        // ---- dS_0 = gamma_C dS_C + K^T dX + Q^T dY (the new carry)
-        {
-            bf16x8 xh[2], xl[2], yh[2], yl[2];
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 o8 = cat(lds8_tr(S.dO, tr_[w][0], 16 * kk * kRowB),
-                                      lds8_tr(S.dO, tr_[w][1], 16 * kk * kRowB));
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int jj = 8 * kk + e, t = acc_row(jj, g);
-                    const float gt = S.gam[t];
-                    split2(-S.beta[t] * gt * dr[jj], xh[kk], xl[kk], e);
-                    split2(gt * (float)o8[e], yh[kk], yl[kk], e);
-                }
-            }
-#pragma unroll
-            for (int bk = 0; bk < 4; ++bk) {
-#pragma unroll
-                for (int jj = 0; jj < 16; ++jj) dSt[bk][jj] *= gC;
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const bf16x8 ak = cat(lds8_tr(S.K, tr_[bk][0], 16 * kk * kRowB),
-                                          lds8_tr(S.K, tr_[bk][1], 16 * kk * kRowB));
-                    const bf16x8 aq = cat(lds8_tr(S.Q, tr_[bk][0], 16 * kk * kRowB),
-                                          lds8_tr(S.Q, tr_[bk][1], 16 * kk * kRowB));
-                    dSt[bk] = mfma_32x32x16(ak, xh[kk], dSt[bk]);
-                    dSt[bk] = mfma_32x32x16(ak, xl[kk], dSt[bk]);
-                    dSt[bk] = mfma_32x32x16(aq, yh[kk], dSt[bk]);
-                    dSt[bk] = mfma_32x32x16(aq, yl[kk], dSt[bk]);
-                }
-            }
-        }
-        wait_lds();
-        barrier();
-
-        // ---- C x C terms (every thread: row t, columns 4q .. 4q + 3)
-        {
-            const int t = tid >> 3, q = tid & 7;
-            const float lgt = S.lg[t], btt = S.beta[t];
-            float erow = 0.f, brow = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 4 * q + e;
-                const float gt = i <= t ? exp2f(lgt - S.lg[i]) : 0.f;
-                const float dbl = i < t ? -S.P[t * kC + i] : 0.f;  // d(diag(beta) LG)
-                const float lgv = S.LG[t * kC + i];
-                const float dmv = i <= t ? S.dM[t * kC + i] : 0.f;
-                // (the diagonal ratio gamma_t / gamma_t is 1: no gate term)
-                const float ek = btt * dbl * lgv, eq = i < t ? dmv * S.M[t * kC + i] : 0.f;
-                brow += dbl * lgv;
-                erow += ek + eq;
-                if (i < t) atomicAdd(&S.dg[i], -(ek + eq));
-                S.P[t * kC + i] = btt * dbl * gt;  // dA (strict lower)
-                S.dM[t * kC + i] = dmv * gt;       // dM o Gamma (lower with diagonal)
-            }
-#pragma unroll
-            for (int off = 4; off >= 1; off >>= 1) {
-                erow += __shfl_xor(erow, off);
-                brow += __shfl_xor(brow, off);
-            }
-            if (q == 0) {
-                atomicAdd(&S.dg[t], erow);
-                atomicAdd(&S.db[t], brow);
-            }
-        }
-        wait_lds();
-        barrier();
-
-        // ---- dQ and dK of key columns [32 w, 32 w + 32)
-        {
-            f32x16 fq, fk;
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj) {
-                const int t = acc_row(jj, g);
-                fq[jj] = S.dQa[t * kD + dv];
-                fk[jj] = S.dKa[t * kD + dv];
-            }
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 bkv = cat(lds8_tr(S.K, tr_[w][0], 16 * kk * kRowB),
-                                       lds8_tr(S.K, tr_[w][1], 16 * kk * kRowB));
-                const bf16x8 bqv = cat(lds8_tr(S.Q, tr_[w][0], 16 * kk * kRowB),
-                                       lds8_tr(S.Q, tr_[w][1], 16 * kk * kRowB));
-                // rows i of this k-step in the accumulator order
-                bf16x8 qh, ql, ah, al, th, tl;
-                ld_split(S.dM + n * kC + 16 * kk + 4 * g, 8, qh, ql, 1.f);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int i = 16 * kk + 8 * (e >> 2) + 4 * g + (e & 3);
-                    split2(S.P[n * kC + i] + S.P[i * kC + n], ah, al, e);
-                    split2(S.dM[i * kC + n], th, tl, e);
-                }
-                fq = mfma_32x32x16(qh, bkv, fq);
-                fq = mfma_32x32x16(ql, bkv, fq);
-                fk = mfma_32x32x16(ah, bkv, fk);
-                fk = mfma_32x32x16(al, bkv, fk);
-                fk = mfma_32x32x16(th, bqv, fk);
-                fk = mfma_32x32x16(tl, bqv, fk);
-            }
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj) {
-                const int t = acc_row(jj, g);
-                if (t < nt) {
-                    const size_t o = (size_t)(start + r0 + t) * rs + (size_t)h * kD + dv;
-                    dQg[o] = (bf16)fq[jj];
-                    dKg[o] = (bf16)fk[jj];
-                }
-            }
-        }
-        // ---- d alpha (suffix sums of d log gamma) and d beta
-        if (w == 0 && lane < kC) {
-            float v = lane < nt ? S.dg[lane] : 0.f;
-#pragma unroll
-            for (int d = 1; d < kC; d <<= 1) {
-                const float y = __shfl_down(v, d, 64);
-                if (lane + d < kC) v += y;
-            }
-            if (lane < nt) {
-                const size_t o = (size_t)(start + r0 + lane) * H + h;
-                dAg[o] = v / S.alpha[lane];
-                dBg[o] = S.db[lane];
-            }
-        }
-        add_handed(r0);
-        r1 = r0;
     }
-    // the gradient of this branch's initial state goes to its parent's fork slot
-    if (init >= 0) {
-        float* dst = dstates + (((size_t)init * H + h) * kD + dv) * kD;
+    sx += __shfl_xor(sx, 32);
 #pragma unroll
-        for (int bk = 0; bk < 4; ++bk)
+    for (int off = 16; off >= 1; off >>= 1) sx += __shfl_xor(sx, off);
+    if (lane == 0) atomicAdd(&S.dg[nt - 1], sx);
+    wait_lds();
+    barrier();
+
+    // ---- C x C terms (every thread: row t, columns 4q .. 4q + 3)
+    {
+        const int t = tid >> 3, q = tid & 7;
+        const float lgt = S.lg[t], btt = S.beta[t];
+        float erow = 0.f, brow = 0.f;
 #pragma unroll
-            for (int jj = 0; jj < 16; ++jj)
-                atomicAdd(dst + 32 * bk + acc_row(jj, g), dSt[bk][jj]);
+        for (int e = 0; e < 4; ++e) {
+            const int i = 4 * q + e;
+            const float gt = i <= t ? exp2f(lgt - S.lg[i]) : 0.f;
+            const float dbl = i < t ? -S.P[t * kC + i] : 0.f;  // d(diag(beta) LG)
+            const float lgv = S.LG[t * kC + i];
+            const float dmv = i <= t ? S.dM[t * kC + i] : 0.f;
+            // (the diagonal ratio gamma_t / gamma_t is 1: no gate term)
+            const float ek = btt * dbl * lgv, eq = i < t ? dmv * S.M[t * kC + i] : 0.f;
+            brow += dbl * lgv;
+            erow += ek + eq;
+            if (i < t) atomicAdd(&S.dg[i], -(ek + eq));
+            S.P[t * kC + i] = btt * dbl * gt;  // dA (strict lower)
+            S.dM[t * kC + i] = dmv * gt;       // dM o Gamma (lower with diagonal)
+        }
+#pragma unroll
+        for (int off = 4; off >= 1; off >>= 1) {
+            erow += __shfl_xor(erow, off);
+            brow += __shfl_xor(brow, off);
+        }
+        if (q == 0) {
+            atomicAdd(&S.dg[t], erow);
+            atomicAdd(&S.db[t], brow);
+        }
+    }
+    wait_lds();
+    barrier();
+
+    // ---- dQ and dK of key columns [32 w, 32 w + 32)
+    {
+        f32x16 fq, fk;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+            const int t = acc_row(jj, g);
+            fq[jj] = S.dQa[t * kD + dv];
+            fk[jj] = S.dKa[t * kD + dv];
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const bf16x8 bkv = rd_tr(S.K, tr, w, kk);
+            const bf16x8 bqv = rd_tr(S.Q, tr, w, kk);
+            // rows i of this k-step in the accumulator order
+            bf16x8 qh, ql, ah, al, th, tl;
+            ld_split(S.dM + n * kC + 16 * kk + 4 * g, 8, qh, ql, 1.f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int i = 16 * kk + 8 * (e >> 2) + 4 * g + (e & 3);
+                split2(S.P[n * kC + i] + S.P[i * kC + n], ah, al, e);
+                split2(S.dM[i * kC + n], th, tl, e);
+            }
+            fq = mfma_32x32x16(qh, bkv, fq);
+            fq = mfma_32x32x16(ql, bkv, fq);
+            fk = mfma_32x32x16(ah, bkv, fk);
+            fk = mfma_32x32x16(al, bkv, fk);
+            fk = mfma_32x32x16(th, bqv, fk);
+            fk = mfma_32x32x16(tl, bqv, fk);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+            const int t = acc_row(jj, g);
+            if (t < nt) {
+                const size_t o = ((tok0 + t) * H + h) * kD + dv;
+                dQg[o] = (bf16)fq[jj];
+                dKg[o] = (bf16)fk[jj];
+            }
+        }
+    }
+    // ---- d alpha (suffix sums of d log gamma) and d beta
+    if (w == 0 && lane < kC) {
+        float v = lane < nt ? S.dg[lane] : 0.f;
+#pragma unroll
+        for (int d = 1; d < kC; d <<= 1) {
+            const float y = __shfl_down(v, d, 64);
+            if (lane + d < kC) v += y;
+        }
+        if (lane < nt) {
+            const size_t o = (tok0 + lane) * H + h;
+            dAg[o] = v / S.alpha[lane];
+            dBg[o] = S.db[lane];
+        }
     }
 }
 
@@ -991,16 +1150,45 @@ __global__ void fill_zero_kernel(float4* p, size_t n4) {
     if (i < n4) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-hipError_t launch_gdn_chunk_bwd(const DevPlan& p, int l0, int n_br, int H, const void* q,
-                                const void* k, const void* v, const float* alpha,
-                                const float* beta, const void* dout, const float* chunk_states,
-                                float* dstates, void* dq, void* dk, void* dv, float* dalpha,
-                                float* dbeta, hipStream_t s) {
+size_t gdn_prep_floats(int64_t n_chunks, int H) { return (size_t)n_chunks * H * kRec; }
+
+hipError_t launch_gdn_chunk_prep(const DevPlan& p, int64_t n_chunks, int H, const void* q,
+                                 const void* k, const void* v, const float* alpha,
+                                 const float* beta, float* prep, hipStream_t s) {
+    if (n_chunks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(gdn_chunk_prep_kernel, dim3((unsigned)(n_chunks * H)), dim3(kThr), 0, s,
+                       p, H, (const bf16*)q, (const bf16*)k, (const bf16*)v, alpha, beta, prep);
+    return hipGetLastError();
+}
+
+hipError_t launch_gdn_chunk_fwd(const DevPlan& p, int l0, int n_br, int H, const void* q,
+                                const void* k, const float* prep, void* o, float* states,
+                                float* chunk_states, hipStream_t s) {
     if (n_br <= 0) return hipSuccess;
-    hipLaunchKernelGGL(gdn_chunk_bwd_kernel, dim3(n_br * H), dim3(kThr), 0, s, p, l0, H,
-                       (const bf16*)q, (const bf16*)k, (const bf16*)v, alpha, beta,
-                       (const bf16*)dout, chunk_states, dstates, (bf16*)dq, (bf16*)dk, (bf16*)dv,
-                       dalpha, dbeta);
+    hipLaunchKernelGGL(gdn_chunk_fwd_kernel, dim3(n_br * H), dim3(kThr), 0, s, p, l0, H,
+                       (const bf16*)q, (const bf16*)k, prep, (bf16*)o, states, chunk_states);
+    return hipGetLastError();
+}
+
+hipError_t launch_gdn_chunk_dstate(const DevPlan& p, int l0, int n_br, int H, const void* q,
+                                   const void* k, const void* dout, const float* prep,
+                                   float* dsc, float* dstates, hipStream_t s) {
+    if (n_br <= 0) return hipSuccess;
+    hipLaunchKernelGGL(gdn_chunk_dstate_kernel, dim3(n_br * H), dim3(kThr), 0, s, p, l0, H,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)dout, prep, dsc, dstates);
+    return hipGetLastError();
+}
+
+hipError_t launch_gdn_chunk_grad(const DevPlan& p, int64_t n_chunks, int H, const void* q,
+                                 const void* k, const void* v, const float* alpha,
+                                 const float* beta, const void* dout, const float* prep,
+                                 const float* chunk_states, const float* dsc, void* dq, void* dk,
+                                 void* dv, float* dalpha, float* dbeta, hipStream_t s) {
+    if (n_chunks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(gdn_chunk_grad_kernel, dim3((unsigned)(n_chunks * H)), dim3(kThr), 0, s,
+                       p, H, (const bf16*)q, (const bf16*)k, (const bf16*)v, alpha, beta,
+                       (const bf16*)dout, prep, chunk_states, dsc, (bf16*)dq, (bf16*)dk,
+                       (bf16*)dv, dalpha, dbeta);
     return hipGetLastError();
 }
 
@@ -1009,17 +1197,6 @@ hipError_t launch_fill_zero(float* p, size_t n_floats, hipStream_t s) {
     if (n4 == 0) return hipSuccess;
     hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
                        reinterpret_cast<float4*>(p), n4);
-    return hipGetLastError();
-}
-
-hipError_t launch_gdn_chunk_fwd(const DevPlan& p, int l0, int n_br, int H, const void* q,
-                                const void* k, const void* v, const float* alpha,
-                                const float* beta, void* o, float* states, float* chunk_states,
-                                hipStream_t s) {
-    if (n_br <= 0) return hipSuccess;
-    hipLaunchKernelGGL(gdn_chunk_fwd_kernel, dim3(n_br * H), dim3(kThr), 0, s, p, l0, H,
-                       (const bf16*)q, (const bf16*)k, (const bf16*)v, alpha, beta, (bf16*)o,
-                       states, chunk_states);
     return hipGetLastError();
 }
 
