@@ -267,7 +267,7 @@ int octopus_dag_attn_bwd_rope(const octopus_plan* plan, octopus_dtype dtype, int
 
 /* Workspace bytes of octopus_gated_delta_scan: float32 fork checkpoints
  * [n_slots][H][Dv][Dk], one slot per distinct (parent, fork offset) of the plan, then one
- * 33,024-byte record per (chunk, head) (the chunk's gated score matrices, the inverse of
+ * 33,792-byte record per (chunk, head) (the chunk's gated score matrices, the inverse of
  * its triangular system and the state-independent part of its W): 4.3 GB at 262,144
  * tokens and H = 16. */
 size_t octopus_gdn_workspace_bytes(const octopus_plan* plan, int32_t H, int32_t Dk,

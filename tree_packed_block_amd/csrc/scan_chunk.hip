@@ -36,6 +36,8 @@
 // bf16 inputs (K K^T, Q K^T, K and Q against anything) are exact on
 // v_mfma_f32_32x32x16_bf16; float32 operands (state, W, T, M, gradients) enter as a bf16
 // high part plus a bf16 low part (relative error below 2^-16 per operand).
+#include <cstddef>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -49,15 +51,19 @@ constexpr int kWaves = kD / 32; // one wave per 32 value rows (or key columns)
 constexpr int kThr = 64 * kWaves;
 constexpr int kRowB = kD * 2;   // bytes of one bf16 row
 
-// Per (chunk, head) record written by the prep kernel, float32:
-//   U   [4 waves][4][64 lanes][4]  U[acc_row(4q + r, g)][32 w + n] (accumulator order)
-//   T   [64 lanes][16]             T[n][acc_row(j, g)]   (A operand, k in row order)
-//   TT  [64 lanes][16]             T[acc_row(j, g)][n]   (A operand of T^T)
-//   M   [64 lanes][16]             M[n][acc_row(j, g)]
-//   MT  [64 lanes][16]             M[acc_row(j, g)][n]
-//   gam [32], bg [32]              gamma_t and beta_t gamma_t
-constexpr int kRecU = 0, kRecT = 4096, kRecTT = 5120, kRecM = 6144, kRecMT = 7168,
-              kRecGam = 8192, kRecBG = 8224, kRec = 8256;
+// Per (chunk, head) record written by the prep kernel, float32.  Matrices in "lane
+// order" [4][64 lanes][4]: element j = 4 q + r of lane l sits at (64 q + l) * 4 + r, so
+// that 64 lanes reading one float4 each touch 1 KiB of consecutive bytes.
+//   U    [4 waves] lane order: U[acc_row(j, g)][32 w + n]      (accumulator order)
+//   T    lane order: T[n][acc_row(j, g)]     (A operand with k in the accumulator's order)
+//   M    lane order: M[n][acc_row(j, g)]
+//   G    gamma_t [32], beta_t gamma_t [32], gamma_C / gamma_t [32], unused [160]
+//   TT   lane order: T[acc_row(j, g)][n]     (A operand of T^T)
+//   MT   lane order: M[acc_row(j, g)][n]
+// The forward reads T, M, G and the backward G, TT, MT as one contiguous block each.
+constexpr int kRecU = 0, kRecT = 4096, kRecM = 5120, kRecG = 6144, kRecTT = 6400,
+              kRecMT = 7424, kRec = 8448;
+constexpr int kGam = 0, kBG = 32, kIG = 64;  // offsets inside G
 
 // Element e of hi and lo take x as hi + lo, both bf16 (|x - hi - lo| <= 2^-16 |x|).
 __device__ __forceinline__ void split2(float x, bf16x8& hi, bf16x8& lo, int e) {
@@ -88,6 +94,10 @@ __device__ __forceinline__ void ld16f(const float* p, int s, float (&v)[16]) {
         v[4 * q + 2] = x.z;
         v[4 * q + 3] = x.w;
     }
+}
+// A matrix in lane order (see the record) at p: this lane's 16 elements.
+__device__ __forceinline__ void ld_lane(const float* p, int lane, float (&v)[16]) {
+    ld16f(p + 4 * lane, 256, v);
 }
 __device__ __forceinline__ void st16f(float* p, int s, const float (&v)[16]) {
 #pragma unroll
@@ -196,6 +206,29 @@ __device__ __forceinline__ void put_rows(unsigned char* tile, int tid, const bf1
     }
 }
 
+// The same rows copied by DMA (global_load_lds) into a swizzled tile at LDS byte address
+// `lds`: piece li = 256 i + tid (row li / 16, slot li % 16) receives column chunk
+// swz(row, slot) of row min(row, nt - 1); rows past nt repeat the last row (every use
+// multiplies them by zero or discards them).
+__device__ __forceinline__ void dma_rows(unsigned lds, const bf16* x, size_t tok0, int nt, int H,
+                                         int h, int tid, int w) {
+    const bf16* base = x + (tok0 * H + h) * kD;
+    const unsigned rstride = (unsigned)H * kD * 2;  // bytes per token row
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int li = i * kThr + tid, row = li >> 4, slot = li & 15;
+        const unsigned off = (unsigned)min(row, nt - 1) * rstride + (unsigned)swz<kD>(row, slot) * 16;
+        dma16_s(base, off, lds + (i * kThr + w * 64) * 16);
+    }
+}
+// n_inst x 1 KiB of a record block (16-byte pieces, wave instruction k copies pieces
+// 64 k .. 64 k + 63), shared round robin by the waves.
+__device__ __forceinline__ void dma_block(unsigned lds, const float* src, int n_inst, int w,
+                                          int lane) {
+    for (int k = w; k < n_inst; k += kWaves)
+        dma16_s(src, (unsigned)(k * 64 + lane) * 16, lds + k * 64 * 16);
+}
+
 // Sum of v[j] over the 32 lanes of this lane's half (lanes with the same g).
 __device__ __forceinline__ void half_sum16(float (&v)[16]) {
 #pragma unroll
@@ -294,16 +327,19 @@ __global__ __launch_bounds__(kThr) void gdn_chunk_prep_kernel(
             fwd_solve(tv, S.LG, S.beta, g);
 #pragma unroll
             for (int j = 0; j < 16; ++j) S.T[acc_row(j, g) * kC + n] = tv[j];
-            st16f(rec + kRecTT + lane * 16, 4, tv);  // T^T rows n: T[acc_row(j, g)][n]
+            st16f(rec + kRecTT + 4 * lane, 256, tv);  // T^T rows n: T[acc_row(j, g)][n]
+            // gamma_C / gamma_t as one difference of logarithms (1 past nt)
+            const float lgC = __shfl(la, nt - 1, 64);
             if (lane < kC) {
                 const float gm = exp2f(la);
-                rec[kRecGam + lane] = gm;
-                rec[kRecBG + lane] = S.beta[lane] * gm;
+                rec[kRecG + kGam + lane] = gm;
+                rec[kRecG + kBG + lane] = S.beta[lane] * gm;
+                rec[kRecG + kIG + lane] = exp2f(lgC - la);
             }
         } else {
 #pragma unroll
             for (int j = 0; j < 16; ++j) S.M[acc_row(j, g) * kC + n] = v[j];
-            st16f(rec + kRecMT + lane * 16, 4, v);  // M^T rows n: M[acc_row(j, g)][n]
+            st16f(rec + kRecMT + 4 * lane, 256, v);  // M^T rows n: M[acc_row(j, g)][n]
         }
     }
     wait_lds();
@@ -332,15 +368,25 @@ __global__ __launch_bounds__(kThr) void gdn_chunk_prep_kernel(
         for (int j = 0; j < 16; ++j) uv[j] = u[j];
         st16f(rec + kRecU + (w * 4 * 64 + lane) * 4, 64 * 4, uv);
     }
-    if (w == 2) st16f(rec + kRecT + lane * 16, 4, trow);
+    if (w == 2) st16f(rec + kRecT + 4 * lane, 256, trow);
     if (w == 3) {
         float mrow[16];
         ld16f(S.M + n * kC + 4 * g, 8, mrow);
-        st16f(rec + kRecM + lane * 16, 4, mrow);
+        st16f(rec + kRecM + 4 * lane, 256, mrow);
     }
 }
 
 // ---------------------------------------------------------------- forward (sequential)
+
+// LDS of the sequential forward, per buffer: the chunk's K and Q (swizzled tiles), each
+// wave's part of U, and the shared T, M, G block of the record.
+struct FwdBuf {
+    unsigned char K[kC * kRowB];
+    unsigned char Q[kC * kRowB];
+    float U[kWaves][1024];
+    float TMG[kRecG + 256 - kRecT];  // T, M, G as in the record
+};
+constexpr int kTMGInst = (kRecG + 256 - kRecT) * 4 / 1024;  // 1 KiB DMA instructions
 
 // states: checkpoint slots [n_slots][H][Dv][Dk] float32 (row = value index).
 // chunk_states (may be NULL): the state at the start of every chunk, [c][H][Dv][Dk].
@@ -349,8 +395,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
     DevPlan P, int l0, int H, const bf16* __restrict__ Qg, const bf16* __restrict__ Kg,
     const float* __restrict__ prep, bf16* __restrict__ Og, float* __restrict__ states,
     float* __restrict__ chunk_states) {
-    __shared__ __attribute__((aligned(1024))) unsigned char SK[2][kC * kRowB];
-    __shared__ __attribute__((aligned(1024))) unsigned char SQ[2][kC * kRowB];
+    __shared__ __attribute__((aligned(1024))) FwdBuf SB[2];
     const int b = ld_const(P.sc_level_br + l0 + blockIdx.x / H);
     const int h = blockIdx.x % H;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -361,6 +406,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
     const int init = ld_const(P.sc_init + b);
     const int cbase = ld_const(P.sc_chunk_base + b);
     const int nch = ld_const(P.sc_chunk_base + b + 1) - cbase;
+    const size_t rs = (size_t)H * kD;  // elements per token row of q, k, o
 
     // S^T tiles: St[bk][j] = S[dv][32 bk + acc_row(j, g)].
     f32x16 St[4];
@@ -397,62 +443,57 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
     };
     int tr[4][2];
     tr_offsets(lane, tr);
-
-    // The next chunk's operands, loaded into registers one chunk ahead.
-    bf16x8 pk[2], pq[2];
-    float pu[16], pt[16], pm[16], pgam[16], pbg[16], pgc = 1.f;
-    auto fetch = [&](int c) {
+    const unsigned sb0 = __builtin_amdgcn_readfirstlane(lds_addr(&SB[0]));
+    constexpr unsigned kBufB = sizeof(FwdBuf);
+    // chunk c's operands into buffer `buf` (asynchronous; waited for at the next barrier)
+    auto issue = [&](int c, int buf) {
         const size_t tok0 = ld_const(P.sc_chunk_tok + c);
         const int nt = ld_const(P.sc_chunk_nt + c);
-        fetch_rows(Kg, tok0, nt, H, h, tid, pk);
-        fetch_rows(Qg, tok0, nt, H, h, tid, pq);
+        const unsigned base = sb0 + buf * kBufB;
+        dma_rows(base + offsetof(FwdBuf, K), Kg, tok0, nt, H, h, tid, w);
+        dma_rows(base + offsetof(FwdBuf, Q), Qg, tok0, nt, H, h, tid, w);
         const float* rec = prep + ((size_t)c * H + h) * kRec;
-        ld16f(rec + kRecU + (w * 4 * 64 + lane) * 4, 64 * 4, pu);
-        ld16f(rec + kRecT + lane * 16, 4, pt);
-        ld16f(rec + kRecM + lane * 16, 4, pm);
-        ld16f(rec + kRecGam + 4 * g, 8, pgam);
-        ld16f(rec + kRecBG + 4 * g, 8, pbg);
-        pgc = rec[kRecGam + nt - 1];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            dma16_s(rec + kRecU + w * 1024, (unsigned)(q * 64 + lane) * 16,
+                    base + offsetof(FwdBuf, U) + w * 4096 + q * 1024);
+        dma_block(base + offsetof(FwdBuf, TMG), rec + kRecT, kTMGInst, w, lane);
     };
 
     save_due(0);
-    if (nch > 0) fetch(cbase);
+    if (nch > 0) issue(cbase, 0);
     bf16 ostash[16];
-    size_t o_tok = 0;
+    bf16* o_ptr = nullptr;
     int o_nt = 0;
     for (int ci = 0; ci < nch; ++ci) {
         const int c = cbase + ci, buf = ci & 1;
         const size_t tok0 = ld_const(P.sc_chunk_tok + c);
         const int nt = ld_const(P.sc_chunk_nt + c);
-        const unsigned char* K = SK[buf];
-        const unsigned char* Q = SQ[buf];
-        put_rows(SK[buf], tid, pk);
-        put_rows(SQ[buf], tid, pq);
-        float cu[16], ct[16], cm[16], cgam[16], cbg[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            cu[j] = pu[j];
-            ct[j] = pt[j];
-            cm[j] = pm[j];
-            cgam[j] = pgam[j];
-            cbg[j] = pbg[j];
-        }
-        const float gC = pgc;
-        wait_lds();
-        // (one barrier per chunk: the buffer written here was last read two chunks ago,
-        // before every wave passed the previous chunk's barrier)
+        const FwdBuf& B = SB[buf];
+        // (one barrier per chunk: the other buffer, filled next, was last read in the
+        // previous chunk, which every wave has finished once this barrier passes)
+        wait_vmem<0>();
         barrier();
-        // The previous chunk's outputs, stored now: issued before the next loads, they
-        // have a whole chunk to complete before the next wait on those loads.
-        if (Og != nullptr && o_nt > 0) {
+        // The previous chunk's outputs, stored now: they complete while this chunk runs.
+        if (o_nt > 0) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const int t = acc_row(j, g);
-                if (t < o_nt) Og[((o_tok + t) * H + h) * kD + dv] = ostash[j];
+                if (t < o_nt) o_ptr[t * rs] = ostash[j];
             }
         }
         if (chunk_states) store_state(chunk_states + (size_t)c * H * kD * kD);
-        if (ci + 1 < nch) fetch(c + 1);  // in flight while this chunk is computed
+        if (ci + 1 < nch) issue(c + 1, buf ^ 1);
+
+        const float* TMG = B.TMG;
+        float cu[16], ct[16], cm[16], cgam[16], cbg[16], cig[16];
+        ld_lane(B.U[w], lane, cu);
+        ld_lane(TMG, lane, ct);
+        ld_lane(TMG + (kRecM - kRecT), lane, cm);
+        ld16f(TMG + (kRecG - kRecT) + kGam + 4 * g, 8, cgam);
+        ld16f(TMG + (kRecG - kRecT) + kBG + 4 * g, 8, cbg);
+        ld16f(TMG + (kRecG - kRecT) + kIG + 4 * g, 8, cig);
+        const float gC = TMG[(kRecG - kRecT) + kGam + nt - 1];
 
         // X = K S_0^T and Y = Q S_0^T for this wave's value rows (A = K, Q rows with the
         // k values in the accumulator's row order; B = the state's hi and lo parts, in
@@ -466,8 +507,8 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
 #pragma unroll
                 for (int e = 0; e < 8; ++e) split2(St[bk][8 * kh + e], shi, slo, e);
                 const int k0 = 32 * bk + 16 * kh + 4 * g;
-                const bf16x8 ak = rd_perm(K, n, k0);
-                const bf16x8 aq = rd_perm(Q, n, k0);
+                const bf16x8 ak = rd_perm(B.K, n, k0);
+                const bf16x8 aq = rd_perm(B.Q, n, k0);
                 X = mfma_32x32x16(ak, shi, X);
                 X2 = mfma_32x32x16(ak, slo, X2);
                 Y = mfma_32x32x16(aq, shi, Y);
@@ -501,15 +542,17 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
             MW = mfma_32x32x16(mh, wl, MW);
             MW = mfma_32x32x16(ml, wh, MW);
         }
+        if (Og != nullptr) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) ostash[j] = (bf16)(cgam[j] * (Y[j] + Y2[j]) + MW[j]);
-        o_tok = tok0;
-        o_nt = nt;
+            for (int j = 0; j < 16; ++j) ostash[j] = (bf16)(cgam[j] * (Y[j] + Y2[j]) + MW[j]);
+            o_ptr = Og + (tok0 * H + h) * kD + dv;
+            o_nt = nt;
+        }
         // S^T <- gamma_C S^T + K^T (diag(gamma_C / gamma) W): A = K^T (transposed reads),
         // B = the scaled W rows of this lane's value column.
         float us[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) us[j] = wv[j] * (gC / cgam[j]);
+        for (int j = 0; j < 16; ++j) us[j] = wv[j] * cig[j];
         bf16x8 uhi[2], ulo[2];
         split8(us, 0, uhi[0], ulo[0]);
         split8(us, 1, uhi[1], ulo[1]);
@@ -519,23 +562,33 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
             for (int j = 0; j < 16; ++j) St[bk][j] *= gC;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 ak = rd_tr(K, tr, bk, kk);
+                const bf16x8 ak = rd_tr(B.K, tr, bk, kk);
                 St[bk] = mfma_32x32x16(ak, uhi[kk], St[bk]);
                 St[bk] = mfma_32x32x16(ak, ulo[kk], St[bk]);
             }
         }
         save_due((int)(tok0 - start) + nt);
     }
-    if (Og != nullptr) {
+    if (o_nt > 0) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const int t = acc_row(j, g);
-            if (t < o_nt) Og[((o_tok + t) * H + h) * kD + dv] = ostash[j];
+            if (t < o_nt) o_ptr[t * rs] = ostash[j];
         }
     }
 }
 
 // ---------------------------------------------------------------- backward: dS (sequential)
+
+// LDS of the state-gradient pass, per buffer: the chunk's K, Q and dO (swizzled tiles)
+// and the record's G, TT, MT block.
+struct DstateBuf {
+    unsigned char K[kC * kRowB];
+    unsigned char Q[kC * kRowB];
+    unsigned char dO[kC * kRowB];
+    float GTM[kRec - kRecG];  // G, TT, MT as in the record
+};
+constexpr int kGTMInst = (kRec - kRecG) * 4 / 1024;
 
 // Walks each branch's chunks in reverse carrying dS (the gradient of L = sum_t <dO_t, o_t>
 // with respect to the state at the current boundary), storing it at every chunk's end
@@ -546,9 +599,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_dstate_kernel(
     DevPlan P, int l0, int H, const bf16* __restrict__ Qg, const bf16* __restrict__ Kg,
     const bf16* __restrict__ dOg, const float* __restrict__ prep, float* __restrict__ dsc,
     float* __restrict__ dstates) {
-    __shared__ __attribute__((aligned(1024))) unsigned char SK[2][kC * kRowB];
-    __shared__ __attribute__((aligned(1024))) unsigned char SQ[2][kC * kRowB];
-    __shared__ __attribute__((aligned(1024))) unsigned char SO[2][kC * kRowB];
+    __shared__ __attribute__((aligned(1024))) DstateBuf SB[2];
     const int b = ld_const(P.sc_level_br + l0 + blockIdx.x / H);
     const int h = blockIdx.x % H;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -583,42 +634,27 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_dstate_kernel(
     add_handed(len);
     int tr[4][2];
     tr_offsets(lane, tr);
-
-    bf16x8 pk[2], pq[2], po[2];
-    float pmt[16], ptt[16], pgam[16], pbg[16], pgc = 1.f;
-    auto fetch = [&](int c) {
+    const unsigned sb0 = __builtin_amdgcn_readfirstlane(lds_addr(&SB[0]));
+    constexpr unsigned kBufB = sizeof(DstateBuf);
+    auto issue = [&](int c, int buf) {
         const size_t tok0 = ld_const(P.sc_chunk_tok + c);
         const int nt = ld_const(P.sc_chunk_nt + c);
-        fetch_rows(Kg, tok0, nt, H, h, tid, pk);
-        fetch_rows(Qg, tok0, nt, H, h, tid, pq);
-        fetch_rows(dOg, tok0, nt, H, h, tid, po);
-        const float* rec = prep + ((size_t)c * H + h) * kRec;
-        ld16f(rec + kRecMT + lane * 16, 4, pmt);
-        ld16f(rec + kRecTT + lane * 16, 4, ptt);
-        ld16f(rec + kRecGam + 4 * g, 8, pgam);
-        ld16f(rec + kRecBG + 4 * g, 8, pbg);
-        pgc = rec[kRecGam + nt - 1];
+        const unsigned base = sb0 + buf * kBufB;
+        dma_rows(base + offsetof(DstateBuf, K), Kg, tok0, nt, H, h, tid, w);
+        dma_rows(base + offsetof(DstateBuf, Q), Qg, tok0, nt, H, h, tid, w);
+        dma_rows(base + offsetof(DstateBuf, dO), dOg, tok0, nt, H, h, tid, w);
+        dma_block(base + offsetof(DstateBuf, GTM), prep + ((size_t)c * H + h) * kRec + kRecG,
+                  kGTMInst, w, lane);
     };
-    if (nch > 0) fetch(cbase + nch - 1);
+    // (the loads above, of the handed gradients, are waited for before the first chunk's
+    // barrier along with the first DMA)
+    if (nch > 0) issue(cbase + nch - 1, (nch - 1) & 1);
     for (int ci = nch - 1; ci >= 0; --ci) {
         const int c = cbase + ci, buf = ci & 1;
+        const int nt = ld_const(P.sc_chunk_nt + c);
         const int r0 = ld_const(P.sc_chunk_tok + c) - start;
-        const unsigned char* K = SK[buf];
-        const unsigned char* Q = SQ[buf];
-        const unsigned char* dO = SO[buf];
-        put_rows(SK[buf], tid, pk);
-        put_rows(SQ[buf], tid, pq);
-        put_rows(SO[buf], tid, po);
-        float cmt[16], ctt[16], cgam[16], cbg[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            cmt[j] = pmt[j];
-            ctt[j] = ptt[j];
-            cgam[j] = pgam[j];
-            cbg[j] = pbg[j];
-        }
-        const float gC = pgc;
-        wait_lds();
+        const DstateBuf& B = SB[buf];
+        wait_vmem<0>();
         barrier();
         {
             float* dst = dsc + (((size_t)c * H + h) * kD + dv) * kD;
@@ -630,7 +666,16 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_dstate_kernel(
                 st16f(dst + 32 * bk + 4 * g, 8, v);
             }
         }
-        if (ci > 0) fetch(c - 1);
+        if (ci > 0) issue(c - 1, buf ^ 1);
+
+        const float* G = B.GTM;
+        float cmt[16], ctt[16], cgam[16], cbg[16], cig[16];
+        ld_lane(G + (kRecMT - kRecG), lane, cmt);
+        ld_lane(G + (kRecTT - kRecG), lane, ctt);
+        ld16f(G + kGam + 4 * g, 8, cgam);
+        ld16f(G + kBG + 4 * g, 8, cbg);
+        ld16f(G + kIG + 4 * g, 8, cig);
+        const float gC = G[kGam + nt - 1];
 
         // dW = M^T dO + diag(gamma_C / gamma) K dS_C^T
         f32x16 tA = zero16(), tB = zero16(), tB2 = zero16();
@@ -639,7 +684,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_dstate_kernel(
         for (int kk = 0; kk < 2; ++kk) {
             bf16x8 mh, ml;
             split8(cmt, kk, mh, ml);
-            o8[kk] = rd_tr(dO, tr, w, kk);
+            o8[kk] = rd_tr(B.dO, tr, w, kk);
             tA = mfma_32x32x16(mh, o8[kk], tA);
             tA = mfma_32x32x16(ml, o8[kk], tA);
         }
@@ -650,14 +695,15 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_dstate_kernel(
                 bf16x8 shi, slo;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) split2(dSt[bk][8 * kh + e], shi, slo, e);
-                const bf16x8 ak = rd_perm(K, n, 32 * bk + 16 * kh + 4 * g);
+                const bf16x8 ak = rd_perm(B.K, n, 32 * bk + 16 * kh + 4 * g);
                 tB = mfma_32x32x16(ak, shi, tB);
                 tB2 = mfma_32x32x16(ak, slo, tB2);
             }
         float dw[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) dw[j] = tA[j] + (gC / cgam[j]) * (tB[j] + tB2[j]);
-        // dR = T^T dW; dX = -diag(beta gamma) dR, dY = diag(gamma) dO
+        for (int j = 0; j < 16; ++j) dw[j] = tA[j] + cig[j] * (tB[j] + tB2[j]);
+        // dR = T^T dW; dX = -diag(beta gamma) dR, dY = diag(gamma) dO (rows past nt of the
+        // staged dO repeat the last row: masked here; dX vanishes there with beta)
         f32x16 dR = zero16();
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -675,7 +721,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_dstate_kernel(
             for (int e = 0; e < 8; ++e) {
                 const int j = 8 * kk + e;
                 split2(-cbg[j] * dR[j], xh[kk], xl[kk], e);
-                split2(cgam[j] * (float)o8[kk][e], yh[kk], yl[kk], e);
+                split2(acc_row(j, g) < nt ? cgam[j] * (float)o8[kk][e] : 0.f, yh[kk], yl[kk], e);
             }
         // dS_0^T = gamma_C dS_C^T + K^T dX + Q^T dY
 #pragma unroll
@@ -684,8 +730,8 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_dstate_kernel(
             for (int j = 0; j < 16; ++j) dSt[bk][j] *= gC;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 ak = rd_tr(K, tr, bk, kk);
-                const bf16x8 aq = rd_tr(Q, tr, bk, kk);
+                const bf16x8 ak = rd_tr(B.K, tr, bk, kk);
+                const bf16x8 aq = rd_tr(B.Q, tr, bk, kk);
                 dSt[bk] = mfma_32x32x16(ak, xh[kk], dSt[bk]);
                 dSt[bk] = mfma_32x32x16(ak, xl[kk], dSt[bk]);
                 dSt[bk] = mfma_32x32x16(aq, yh[kk], dSt[bk]);
@@ -857,10 +903,11 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
         X[j] += X2[j];
         Y[j] += Y2[j];
     }
-    float gam[16], bg[16];
-    ld16f(rec + kRecGam + 4 * g, 8, gam);
-    ld16f(rec + kRecBG + 4 * g, 8, bg);
-    const float gC = rec[kRecGam + nt - 1];
+    float gam[16], bg[16], ig[16];
+    ld16f(rec + kRecG + kGam + 4 * g, 8, gam);
+    ld16f(rec + kRecG + kBG + 4 * g, 8, bg);
+    ld16f(rec + kRecG + kIG + 4 * g, 8, ig);
+    const float gC = rec[kRecG + kGam + nt - 1];
     wait_lds();
     barrier();
 
@@ -879,8 +926,8 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
     float wv[16], vx[16];
     {
         float tv[16], xs[16];
-        ld16f(rec + kRecT + lane * 16, 4, tv);
-        ld16f(rec + kRecU + (w * 4 * 64 + lane) * 4, 64 * 4, wv);
+        ld_lane(rec + kRecT, lane, tv);
+        ld_lane(rec + kRecU + w * 1024, lane, wv);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             xs[j] = X[j] * bg[j];
@@ -927,10 +974,10 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
         float dw[16], ttv[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            tb[j] = (tB[j] + tB2[j]) * (gC / gam[j]);
+            tb[j] = (tB[j] + tB2[j]) * ig[j];
             dw[j] = tA[j] + tb[j];
         }
-        ld16f(rec + kRecTT + lane * 16, 4, ttv);
+        ld_lane(rec + kRecTT, lane, ttv);
         f32x16 dRa = zero16();
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -1001,8 +1048,9 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
     }
     // ---- dQ, dK partials over this wave's value rows, one key tile at a time
     {
-        const float gmn = S.gam[n], btn = S.beta[n];  // the A operands' rows are t = n
-        const float xsc = -btn * gmn, wsc = gC / gmn;
+        // the A operands' rows are t = n
+        const float gmn = S.gam[n], btn = S.beta[n];
+        const float xsc = -btn * gmn, wsc = rec[kRecG + kIG + n];
 #pragma unroll
         for (int bk = 0; bk < 4; ++bk) {
             float sv[16], dsv[16];
