@@ -229,12 +229,30 @@ __device__ __forceinline__ void dma_block(unsigned lds, const float* src, int n_
         dma16_s(src, (unsigned)(k * 64 + lane) * 16, lds + k * 64 * 16);
 }
 
-// Sum of v[j] over the 32 lanes of this lane's half (lanes with the same g).
+// v plus the value of the lane given by the DPP control CTRL (rows of 16 lanes enabled by
+// ROWS; disabled rows add 0).
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                             0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xF, false));
+}
+// Sum over each group of 8 lanes (xor 1, xor 2, then the mirror inside 8 lanes): every
+// lane of the group receives it.
+__device__ __forceinline__ float sum8(float v) {
+    v = dpp_add<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+    v = dpp_add<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+    return dpp_add<0x141>(v);  // row_half_mirror
+}
+// Sum over the 32 lanes of this lane's half of the wave, valid in lanes 31 and 63: sums
+// of 16 by the mirror inside each row, then row 0 (2) broadcast into row 1 (3).
+__device__ __forceinline__ float half_sum(float v) {
+    v = sum8(v);
+    v = dpp_add<0x140>(v);        // row_mirror
+    return dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+}
 __device__ __forceinline__ void half_sum16(float (&v)[16]) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) v[j] += __shfl_xor(v[j], off);
+    for (int j = 0; j < 16; ++j) v[j] = half_sum(v[j]);
 }
 
 // log2 gamma_t for lanes t < 32 (inclusive prefix sums of log2 alpha over the chunk;
@@ -917,7 +935,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) r[jj] = gam[jj] * tile_at(S.dO, acc_row(jj, g), dv) * Y[jj];
         half_sum16(r);
-        if (n == 0) {
+        if (n == 31) {
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj) atomicAdd(&S.dg[acc_row(jj, g)], r[jj]);
         }
@@ -1013,7 +1031,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
         }
         half_sum16(rdb);
         half_sum16(rdg);
-        if (n == 0) {
+        if (n == 31) {
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj) {
                 const int t = acc_row(jj, g);
@@ -1098,10 +1116,8 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
             __builtin_amdgcn_wave_barrier();
         }
     }
-    sx += __shfl_xor(sx, 32);
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) sx += __shfl_xor(sx, off);
-    if (lane == 0) atomicAdd(&S.dg[nt - 1], sx);
+    sx = half_sum(sx);
+    if (n == 31) atomicAdd(&S.dg[nt - 1], sx);
     wait_lds();
     barrier();
 
@@ -1125,11 +1141,8 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
             S.P[t * kC + i] = btt * dbl * gt;  // dA (strict lower)
             S.dM[t * kC + i] = dmv * gt;       // dM o Gamma (lower with diagonal)
         }
-#pragma unroll
-        for (int off = 4; off >= 1; off >>= 1) {
-            erow += __shfl_xor(erow, off);
-            brow += __shfl_xor(brow, off);
-        }
+        erow = sum8(erow);
+        brow = sum8(brow);
         if (q == 0) {
             atomicAdd(&S.dg[t], erow);
             atomicAdd(&S.db[t], brow);
