@@ -92,29 +92,90 @@ def traffic_record(kernel: str, workload: str):
     return k.get("fetch_bytes_per_launch", 0) + k.get("write_bytes_per_launch", 0)
 
 
-def cpu_baseline(dag, x, rows_per_part=768):
-    """The float64 oracle (as it stands) on a bounded sample: forward + backward of
-    the last rows of two workers and of the continuation (every row with its whole
-    context)."""
+def cpu_baseline(dag, x, dec, rows_per_part=768):
+    """The float64 oracle (as it stands) on bounded samples.  The headline sample: forward
+    + backward of the last rows of two workers and of the continuation of the benchmark's
+    tree (every row with its whole context).  Further rows, each a stated sample of another
+    workload: the ~20K-token forked DAG forward, the 131,072-token episode forward +
+    backward, and paged decode of a few cursors (GB/s of the K/V context they read)."""
     import numpy as np
+    import synth
     from oracle import attention as A
     from oracle import dag as D
+    from oracle import decode as Dec
+
+    def sample_parts(br, branches, n):
+        return [(int(br[b, 2]) + int(br[b, 3]) - n, int(br[b, 2]) + int(br[b, 3]))
+                for b in branches]
+
+    def pairs(dg, parts):
+        return sum(int(D.mask_rows(dg.branches, dg.mounts, dg.T, lo, hi).sum())
+                   for lo, hi in parts)
+
     br = dag.branches
-    parts = []
-    for b in (1, 2, dag.nb - 1):
-        start, L = int(br[b, 2]), int(br[b, 3])
-        parts.append((start + L - rows_per_part, start + L))
-    ctx = sum(int(D.mask_rows(br, dag.mounts, dag.T, lo, hi).sum()) for lo, hi in parts)
+    parts = sample_parts(br, (1, 2, dag.nb - 1), rows_per_part)
+    ctx = pairs(dag, parts)
     t0 = time.perf_counter()
     A.attn_fwd(x["q"], x["k"], x["v"], br, dag.mounts, rows=parts)
     A.attn_bwd(x["q"], x["k"], x["v"], x["do"], br, dag.mounts, rows=parts)
     dt = time.perf_counter() - t0
-    flops = 14.0 * HD * HQ * ctx
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
-            "cores": A.n_workers(), "kind": "oracle",
-            "sample": f"fwd+bwd of {len(parts)}x{rows_per_part} query rows (last rows of "
-                      f"workers 1, 2 and the continuation; {ctx} visible pairs), "
-                      f"float64, {dt:.1f} s"}
+    out = {"value": round(14.0 * HD * HQ * ctx / dt / 1e12, 6), "unit": "TFLOP/s",
+           "cores": A.n_workers(), "kind": "oracle",
+           "sample": f"fwd+bwd of {len(parts)}x{rows_per_part} query rows (last rows of "
+                     f"workers 1, 2 and the continuation; {ctx} visible pairs), "
+                     f"float64, {dt:.1f} s", "rows": []}
+
+    # ~20K-token forked DAG (4,096-token root, 4 children, 2 sibling mounts), forward
+    d2, rng2 = synth.build("forked")
+    x2 = synth.draw_attention_inputs(rng2, d2.T, HQ, HKV, HD,
+                                     D.positions(d2.branches, d2.mounts), dtype="bf16",
+                                     std=0.5)
+    p2 = sample_parts(d2.branches, (1, 2, 3, 4), 2048)
+    c2 = pairs(d2, p2)
+    t0 = time.perf_counter()
+    A.attn_fwd(x2["q"], x2["k"], x2["v"], d2.branches, d2.mounts, rows=p2)
+    dt = time.perf_counter() - t0
+    out["rows"].append({"workload": "forked DAG, ~20K tokens, forward",
+                        "value": round(4.0 * HD * HQ * c2 / dt / 1e12, 6), "unit": "TFLOP/s",
+                        "sample": f"fwd of 4x2048 query rows (last rows of the 4 children; "
+                                  f"{c2} visible pairs), {dt:.1f} s"})
+
+    # 131,072-token episode, forward + backward.  The oracle's work does not depend on
+    # the values: inputs tile one random 1,024-token block (drawing 131K tokens of inputs
+    # would take longer than the sample itself).
+    d4, rng4 = synth.build("episode131k")
+
+    def tiled(h):
+        blk = (0.5 * rng4.standard_normal((1024, h, HD))).astype(np.float32)
+        return np.tile(blk, (d4.T // 1024 + 1, 1, 1))[:d4.T]
+
+    q4, k4, v4, do4 = tiled(HQ), tiled(HKV), tiled(HKV), tiled(HQ)
+    p4 = sample_parts(d4.branches, (1, 2, d4.nb - 1), 768)
+    c4 = pairs(d4, p4)
+    t0 = time.perf_counter()
+    A.attn_fwd(q4, k4, v4, d4.branches, d4.mounts, rows=p4)
+    A.attn_bwd(q4, k4, v4, do4, d4.branches, d4.mounts, rows=p4)
+    dt = time.perf_counter() - t0
+    out["rows"].append({"workload": "episode tree of 131,072 tokens, forward + backward",
+                        "value": round(14.0 * HD * HQ * c4 / dt / 1e12, 6), "unit": "TFLOP/s",
+                        "sample": f"fwd+bwd of 3x768 query rows (last rows of workers 1, 2 "
+                                  f"and the continuation; {c4} visible pairs), inputs tiled from "
+                                  f"one random 1,024-token block, {dt:.1f} s"})
+
+    # paged decode: the first 16 cursors of the 64-cursor batch
+    wl, qd, kp, vp = dec
+    cur = wl.cursors[:16]
+    ntok = sum(int(Dec.cursor_tokens(wl.dag.branches, wl.dag.mounts, int(b)).size) for b in cur)
+    t0 = time.perf_counter()
+    Dec.decode(qd[:16], kp, vp, wl.dag.branches, wl.dag.mounts, wl.page_ptr, wl.pages,
+               wl.page_size, cur)
+    dt = time.perf_counter() - t0
+    byts = ntok * HKV * HD * 2 * 2
+    out["rows"].append({"workload": "paged mounted decode, 64-cursor batch",
+                        "value": round(byts / dt / 1e9, 3), "unit": "GB/s",
+                        "sample": f"16 cursors ({ntok} context tokens; bytes = their K and V "
+                                  f"in bf16, each cursor's context counted once), {dt:.1f} s"})
+    return out
 
 
 def extend_pairs(segs, n_new, branches, cursors) -> int:
@@ -140,8 +201,9 @@ KERNEL_KEYS = (("fwd_bf16_kernel", "fwd"), ("tiles_t_kernel", "fwd"),
                ("preprocess_bf16_kernel", "bwd_preprocess"),
                ("dkdv_bf16_kernel", "bwd_dkdv"), ("dq_bf16_kernel", "bwd_dq"),
                ("decode_split_kernel", "decode"), ("decode_combine_kernel", "decode"),
-               ("rope_kernel", "rope"), ("gdn_chunk_fwd_kernel", "gdn_scan"),
-               ("gdn_chunk_bwd_kernel", "gdn_scan_bwd"))
+               ("rope_kernel", "rope"), ("gdn_chunk_prep_kernel", "gdn_scan"),
+               ("gdn_chunk_fwd_kernel", "gdn_scan"), ("gdn_chunk_dstate_kernel", "gdn_scan_bwd"),
+               ("gdn_chunk_grad_kernel", "gdn_scan_bwd"))
 CALIBRATION_BYTES = 1 << 30  # the --calibrate-copy transfer
 
 
@@ -581,7 +643,7 @@ def main():
 
     if not args.no_cpu_baseline:
         log("cpu baseline (float64 oracle on a sample) ...")
-        out["cpu_baseline"] = cpu_baseline(dag, x)
+        out["cpu_baseline"] = cpu_baseline(dag, x, (wl, xd["q"], xd["k_pool"], xd["v_pool"]))
     print(json.dumps(out), flush=True)
 
 
