@@ -207,6 +207,19 @@ KERNEL_KEYS = (("fwd_bf16_kernel", "fwd"), ("tiles_t_kernel", "fwd"),
 CALIBRATION_BYTES = 1 << 30  # the --calibrate-copy transfer
 
 
+def kernel_key(name: str):
+    """The step phase a kernel's launches belong to (launches of several kernels in one
+    phase add up, e.g. decode = split + combine), or None.  The RoPE instances of the
+    attention kernels (template flag true: `Lb1E` in the mangled name) are the RoPE leg's,
+    not the step's: they get keys of their own."""
+    for sub, key in KERNEL_KEYS:
+        if sub in name:
+            if key in ("fwd", "bwd_dkdv", "bwd_dq") and sub != "tiles_t_kernel" and "Lb1E" in name:
+                return key + "_rope"
+            return key
+    return None
+
+
 def _counter_per_dispatch(csv_path: str, counter: str):
     """{kernel name: [value per dispatch]} for one counter of a rocprofv3 CSV."""
     import csv
@@ -237,10 +250,10 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str) -> dict:
         rec["calibration"][counter] = {"copy_kib": max(copies), "bytes_per_kib": factor}
         sums = {}
         for name, vals in per.items():
-            for sub, key in KERNEL_KEYS:
-                if sub in name:
-                    avg = sum(vals) / len(vals) * 1024.0 * factor
-                    sums[key] = sums.get(key, 0.0) + avg
+            key = kernel_key(name)
+            if key is not None:
+                avg = sum(vals) / len(vals) * 1024.0 * factor
+                sums[key] = sums.get(key, 0.0) + avg
         for key, v in sums.items():
             rec["kernels"].setdefault(key, {})[field] = round(v)
     path = os.path.join(ROOT, "profiles", "traffic.json")
