@@ -19,10 +19,40 @@ pytestmark = pytest.mark.gpu
 SCAN_TOL = 5e-3
 
 
-def _run(dag, H, seed):
+def _wide_gates(x, seed):
+    """Gates over their whole range instead of the recipe's: alpha exactly 1 (no decay),
+    U[0.3, 1) or U[0.02, 0.3) (fast decay), beta exactly 0 (no write), exactly 1 (full
+    replacement) or U[0, 1)."""
+    rng = np.random.default_rng(seed)
+    shape = x["alpha"].shape
+    a = rng.integers(0, 3, size=shape)
+    x["alpha"] = np.where(a == 0, 1.0, np.where(a == 1, rng.uniform(0.3, 1.0, shape),
+                                                rng.uniform(0.02, 0.3, shape))).astype(np.float32)
+    bsel = rng.integers(0, 4, size=shape)
+    x["beta"] = np.where(bsel == 0, 0.0, np.where(bsel == 1, 1.0, rng.uniform(0.0, 1.0, shape))
+                         ).astype(np.float32)
+    return x
+
+
+def _chain_dag():
+    """Five levels of nested forks: a 40-token root; a child forked at 17; a grandchild
+    forked at 33 of the child; a great-grandchild forked at 0 of the grandchild and another
+    at its end; one-token branches forked at the root's end and at 1; a mount that the
+    scan must ignore."""
+    rows_b = [[-1, 0, 0, 40], [0, 17, 40, 50], [1, 33, 90, 45], [2, 0, 135, 30],
+              [2, 45, 165, 31], [0, 40, 196, 1], [1, 1, 197, 1]]
+    rows_m = [[3, 5, 1, 10, 20]]
+    b = np.asarray(rows_b, dtype=np.int32)
+    m = np.asarray(rows_m, dtype=np.int32)
+    return synth.Dag("chain", b, m, 198)
+
+
+def _run(dag, H, seed, wide=False):
     import torch
     import tree_packed_block_amd as tpb
     x = synth.draw_scan_inputs(np.random.default_rng(seed), dag.T, H)
+    if wide:
+        x = _wide_gates(x, seed + 7)
     plan = tpb.Plan(dag.branches, dag.mounts, dag.T).upload()
     o = tpb.gated_delta_scan(plan, dev(x["q"], "bf16"), dev(x["k"], "bf16"),
                              dev(x["v"], "bf16"), torch.from_numpy(x["alpha"]).cuda(),
@@ -46,6 +76,23 @@ def test_scan_named(name):
     say(f"case scan {name}")
     dag, _ = synth.build(name)
     o, ro = _run(dag, 4, 11)
+    check_close(o, ro, SCAN_TOL, "o")
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_scan_wide_gates_and_short_branches(seed):
+    """Gates over their whole range on fuzzed DAGs of many short branches (one-token
+    branches, forks at 0 and at the end, chunks cut at every fork)."""
+    say(f"case scan wide gates seed={seed}")
+    dag = synth.fuzz_dag(np.random.default_rng(1300 + seed), max_len=70, max_branches=9,
+                         max_mounts=3)
+    o, ro = _run(dag, 2, 1400 + seed, wide=True)
+    check_close(o, ro, SCAN_TOL, "o")
+
+
+def test_scan_nested_forks():
+    say("case scan chain of nested forks")
+    o, ro = _run(_chain_dag(), 3, 1500, wide=True)
     check_close(o, ro, SCAN_TOL, "o")
 
 
@@ -86,10 +133,12 @@ def _check_grad_scan(got, ref, name, tol=SCAN_GRAD_TOL):
     assert np.all(err <= bound), f"{name}: {int(np.sum(err > bound))} elements outside tolerance"
 
 
-def _run_bwd(dag, H, seed):
+def _run_bwd(dag, H, seed, wide=False):
     import torch
     import tree_packed_block_amd as tpb
     x = synth.draw_scan_inputs(np.random.default_rng(seed), dag.T, H)
+    if wide:
+        x = _wide_gates(x, seed + 7)
     do = synth.round_bf16((0.5 * np.random.default_rng(seed + 1).standard_normal(
         x["v"].shape)).astype(np.float32))
     plan = tpb.Plan(dag.branches, dag.mounts, dag.T).upload()
@@ -125,3 +174,16 @@ def test_scan_bwd_full_episode():
     say("case scan bwd episode262k H=1")
     dag, _ = synth.build("episode262k")
     _run_bwd(dag, 1, 22)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_scan_bwd_wide_gates_and_short_branches(seed):
+    say(f"case scan bwd wide gates seed={seed}")
+    dag = synth.fuzz_dag(np.random.default_rng(1600 + seed), max_len=70, max_branches=9,
+                         max_mounts=3)
+    _run_bwd(dag, 2, 1700 + seed, wide=True)
+
+
+def test_scan_bwd_nested_forks():
+    say("case scan bwd chain of nested forks")
+    _run_bwd(_chain_dag(), 3, 1800, wide=True)
