@@ -229,6 +229,22 @@ __device__ __forceinline__ void dma_block(unsigned lds, const float* src, int n_
         dma16_s(src, (unsigned)(k * 64 + lane) * 16, lds + k * 64 * 16);
 }
 
+// The transposed tiles X[bk][j] = M[dv][32 bk + acc_row(j, g)] of a 128 x 128 matrix M held
+// by the four waves (lane = row dv), stored key-major: dst[k][dv] (lanes write consecutive
+// dv: 128 bytes per row k).
+__device__ __forceinline__ void store_key_major(float* dst, const f32x16 (&X)[4], int dv, int g) {
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dst[(32 * bk + acc_row(j, g)) * kD + dv] = X[bk][j];
+}
+// ... and read back into the same tiles.
+__device__ __forceinline__ void load_key_major(const float* src, int bk, int dv, int g,
+                                               float (&v)[16]) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = src[(32 * bk + acc_row(j, g)) * kD + dv];
+}
+
 // v plus the value of the lane given by the DPP control CTRL (rows of 16 lanes enabled by
 // ROWS; disabled rows add 0).
 template <int CTRL, int ROWS = 0xF>
@@ -407,7 +423,8 @@ struct FwdBuf {
 constexpr int kTMGInst = (kRecG + 256 - kRecT) * 4 / 1024;  // 1 KiB DMA instructions
 
 // states: checkpoint slots [n_slots][H][Dv][Dk] float32 (row = value index).
-// chunk_states (may be NULL): the state at the start of every chunk, [c][H][Dv][Dk].
+// chunk_states (may be NULL): the state at the start of every chunk, stored key-major
+// [c][H][Dk][Dv] (the layout the gradient pass reads its operands in).
 // Og may be NULL (the backward needs the states only).
 __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
     DevPlan P, int l0, int H, const bf16* __restrict__ Qg, const bf16* __restrict__ Kg,
@@ -500,7 +517,8 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
                 if (t < o_nt) o_ptr[t * rs] = ostash[j];
             }
         }
-        if (chunk_states) store_state(chunk_states + (size_t)c * H * kD * kD);
+        if (chunk_states)
+            store_key_major(chunk_states + ((size_t)c * H + h) * kD * kD, St, dv, g);
         if (ci + 1 < nch) issue(c + 1, buf ^ 1);
 
         const float* TMG = B.TMG;
@@ -610,7 +628,7 @@ constexpr int kGTMInst = (kRec - kRecG) * 4 / 1024;
 
 // Walks each branch's chunks in reverse carrying dS (the gradient of L = sum_t <dO_t, o_t>
 // with respect to the state at the current boundary), storing it at every chunk's end
-// into dsc [c][H][Dv][Dk] for the gradient kernel.  dstates [n_slots][H][Dv][Dk]: slots
+// into dsc [c][H][Dk][Dv] (key-major) for the gradient kernel.  dstates [n_slots][H][Dv][Dk]: slots
 // that children (deeper levels, launched earlier) added their initial-state gradients to;
 // this branch's own initial-state gradient is added to its parent's slot.
 __global__ __launch_bounds__(kThr, 1) void gdn_chunk_dstate_kernel(
@@ -674,16 +692,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_dstate_kernel(
         const DstateBuf& B = SB[buf];
         wait_vmem<0>();
         barrier();
-        {
-            float* dst = dsc + (((size_t)c * H + h) * kD + dv) * kD;
-#pragma unroll
-            for (int bk = 0; bk < 4; ++bk) {
-                float v[16];
-#pragma unroll
-                for (int j = 0; j < 16; ++j) v[j] = dSt[bk][j];
-                st16f(dst + 32 * bk + 4 * g, 8, v);
-            }
-        }
+        store_key_major(dsc + ((size_t)c * H + h) * kD * kD, dSt, dv, g);
         if (ci > 0) issue(c - 1, buf ^ 1);
 
         const float* G = B.GTM;
@@ -781,8 +790,9 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_dstate_kernel(
 // and the gates through log gamma (natural log; every factor gamma_t / gamma_i and every
 // gamma_t, gamma_C contributes its own term), summed from the end of the chunk to give
 // d log alpha.  Wave w owns value rows [32 w, 32 w + 32) for what runs per value row (W,
-// dR, dV) and key columns [32 w, 32 w + 32) of dQ and dK; sums over value rows are
-// gathered in LDS.
+// dR, dV) and key columns [32 w, 32 w + 32) of dQ and dK, which it sums over all value
+// rows itself: W and dR of every wave go through LDS, the states come key-major from
+// global memory as B operands.
 namespace {
 struct GradSmem {
     unsigned char K[kC * kRowB];
@@ -795,14 +805,10 @@ struct GradSmem {
     float MT[kC * kC];   // its transpose
     float P[kC * kC];    // sum over value rows of dR_t . W_i, then dA
     float dM[kC * kC];   // sum over value rows of dO_t . W_i, then dM o Gamma
-    float dQa[kC * kD];  // sums over value rows of the state products, [t][dk]
-    float dKa[kC * kD];
     float dg[kC];        // d L / d (natural log gamma_t)
     float db[kC];        // d L / d beta_t
     float W[kWaves][kC * 32];   // per wave: W [t][value row]
     float dR[kWaves][kC * 32];  // dR [t][value row]
-    float S0[kWaves][32 * 32];  // one key tile of S_0: [key][value row]
-    float dS[kWaves][32 * 32];  // the same tile of dS_C
 };
 }  // namespace
 
@@ -822,12 +828,11 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
     const size_t tok0 = ld_const(P.sc_chunk_tok + c);
     const int nt = ld_const(P.sc_chunk_nt + c);
     const float* rec = prep + ((size_t)c * H + h) * kRec;
-    const float* S0g = chunk_states + (((size_t)c * H + h) * kD + dv) * kD;
-    const float* dSg = dsc + (((size_t)c * H + h) * kD + dv) * kD;
+    // S_0 and dS_C of this (chunk, head), key-major [k][v]
+    const float* S0g = chunk_states + ((size_t)c * H + h) * kD * kD;
+    const float* dSg = dsc + ((size_t)c * H + h) * kD * kD;
     float* Wl = S.W[w];
     float* dRl = S.dR[w];
-    float* S0l = S.S0[w];
-    float* dSl = S.dS[w];
     int tr[4][2];
     tr_offsets(lane, tr);
     // 8 floats at p[0..3] and p[off..off+3], split into bf16 high and low parts
@@ -859,11 +864,6 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
     }
     {
         const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int u = 0; u < kC * kD / 4 / kThr; ++u) {
-            reinterpret_cast<float4*>(S.dQa)[u * kThr + tid] = z;
-            reinterpret_cast<float4*>(S.dKa)[u * kThr + tid] = z;
-        }
         reinterpret_cast<float4*>(S.P)[tid] = z;
         reinterpret_cast<float4*>(S.dM)[tid] = z;
     }
@@ -902,7 +902,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
 #pragma unroll
     for (int bk = 0; bk < 4; ++bk) {
         float sv[16];
-        ld16f(S0g + 32 * bk + 4 * g, 8, sv);
+        load_key_major(S0g, bk, dv, g, sv);
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
             bf16x8 shi, slo;
@@ -979,7 +979,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
 #pragma unroll
         for (int bk = 0; bk < 4; ++bk) {
             float sv[16];
-            ld16f(dSg + 32 * bk + 4 * g, 8, sv);
+            load_key_major(dSg, bk, dv, g, sv);
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
                 bf16x8 shi, slo;
@@ -1064,56 +1064,52 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
             atomicAdd(&S.dM[t * kC + n], pm[jj]);
         }
     }
-    // ---- dQ, dK partials over this wave's value rows, one key tile at a time
+    // ---- dQ = dY S_0 and dK = dX S_0 + diag(gamma_C / gamma) W dS_C for key columns
+    // kc = 32 w + n, summed over all 128 value rows: A operands (rows t) from every wave's
+    // W and dR in LDS and from dO; B operands S_0[v][kc], dS_C[v][kc] (8 consecutive v per
+    // lane and k-step, key-major in global memory).
+    wait_lds();
+    barrier();  // every wave's W and dR are in LDS
+    f32x16 fq = zero16(), fk = zero16();
     {
+        const int kc = 32 * w + n;
+        const float* s0r = S0g + (size_t)kc * kD + 8 * g;
+        const float* dsr = dSg + (size_t)kc * kD + 8 * g;
         // the A operands' rows are t = n
         const float gmn = S.gam[n], btn = S.beta[n];
         const float xsc = -btn * gmn, wsc = rec[kRecG + kIG + n];
 #pragma unroll
-        for (int bk = 0; bk < 4; ++bk) {
-            float sv[16], dsv[16];
-            ld16f(S0g + 32 * bk + 4 * g, 8, sv);
-            ld16f(dSg + 32 * bk + 4 * g, 8, dsv);
+        for (int ks = 0; ks < kD / 16; ++ks) {
+            const float4 sa = *reinterpret_cast<const float4*>(s0r + 16 * ks);
+            const float4 sb = *reinterpret_cast<const float4*>(s0r + 16 * ks + 4);
+            const float4 da = *reinterpret_cast<const float4*>(dsr + 16 * ks);
+            const float4 dbv = *reinterpret_cast<const float4*>(dsr + 16 * ks + 4);
+            const float s8[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+            const float d8[8] = {da.x, da.y, da.z, da.w, dbv.x, dbv.y, dbv.z, dbv.w};
+            bf16x8 sh, sl, dh, dl, xh, xl, wh, wl, yh, yl;
 #pragma unroll
-            for (int jj = 0; jj < 16; ++jj) {
-                const int kr = acc_row(jj, g);
-                S0l[kr * 32 + n] = sv[jj];
-                dSl[kr * 32 + n] = dsv[jj];
-                sx += gC * sv[jj] * dsv[jj];  // gamma_C <dS_C, S_0>
+            for (int e = 0; e < 8; ++e) {
+                split2(s8[e], sh, sl, e);
+                split2(d8[e], dh, dl, e);
+                sx += gC * s8[e] * d8[e];  // gamma_C <dS_C, S_0>: each element once
             }
-            wait_lds();
-            __builtin_amdgcn_wave_barrier();
-            f32x16 pk = zero16(), pq = zero16();
+            const int vw = ks >> 1, vl = 16 * (ks & 1) + 8 * g;
+            ld_split(S.dR[vw] + n * 32 + vl, 4, xh, xl, xsc);
+            ld_split(S.W[vw] + n * 32 + vl, 4, wh, wl, wsc);
+            {
+                const bf16x8 o8 = rd8(S.dO, n, 16 * ks + 8 * g);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                bf16x8 xh, xl, wh, wl, sh, sl, dh, dl, yh, yl;
-                ld_split(dRl + n * 32 + 16 * ks + 8 * g, 4, xh, xl, xsc);
-                ld_split(Wl + n * 32 + 16 * ks + 8 * g, 4, wh, wl, wsc);
-                ld_split(S0l + n * 32 + 16 * ks + 8 * g, 4, sh, sl, 1.f);
-                ld_split(dSl + n * 32 + 16 * ks + 8 * g, 4, dh, dl, 1.f);
-                {
-                    const bf16x8 o8 = rd8(S.dO, n, 32 * w + 16 * ks + 8 * g);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) split2((float)o8[e] * gmn, yh, yl, e);
-                }
-                pk = mfma_32x32x16(xh, sh, pk);
-                pk = mfma_32x32x16(xh, sl, pk);
-                pk = mfma_32x32x16(xl, sh, pk);
-                pk = mfma_32x32x16(wh, dh, pk);
-                pk = mfma_32x32x16(wh, dl, pk);
-                pk = mfma_32x32x16(wl, dh, pk);
-                pq = mfma_32x32x16(yh, sh, pq);
-                pq = mfma_32x32x16(yh, sl, pq);
-                pq = mfma_32x32x16(yl, sh, pq);
+                for (int e = 0; e < 8; ++e) split2((float)o8[e] * gmn, yh, yl, e);
             }
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj) {
-                const int t = acc_row(jj, g);
-                atomicAdd(&S.dKa[t * kD + 32 * bk + n], pk[jj]);
-                atomicAdd(&S.dQa[t * kD + 32 * bk + n], pq[jj]);
-            }
-            wait_lds();
-            __builtin_amdgcn_wave_barrier();
+            fk = mfma_32x32x16(xh, sh, fk);
+            fk = mfma_32x32x16(xh, sl, fk);
+            fk = mfma_32x32x16(xl, sh, fk);
+            fk = mfma_32x32x16(wh, dh, fk);
+            fk = mfma_32x32x16(wh, dl, fk);
+            fk = mfma_32x32x16(wl, dh, fk);
+            fq = mfma_32x32x16(yh, sh, fq);
+            fq = mfma_32x32x16(yh, sl, fq);
+            fq = mfma_32x32x16(yl, sh, fq);
         }
     }
     sx = half_sum(sx);
@@ -1151,15 +1147,8 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
     wait_lds();
     barrier();
 
-    // ---- dQ and dK of key columns [32 w, 32 w + 32)
+    // ---- the C x C terms of dQ and dK of key columns [32 w, 32 w + 32)
     {
-        f32x16 fq, fk;
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-            const int t = acc_row(jj, g);
-            fq[jj] = S.dQa[t * kD + dv];
-            fk[jj] = S.dKa[t * kD + dv];
-        }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const bf16x8 bkv = rd_tr(S.K, tr, w, kk);
