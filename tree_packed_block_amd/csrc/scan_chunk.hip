@@ -803,8 +803,10 @@ struct GradSmem {
     float LG[kC * kC];   // gated K K^T, strict lower, [t][i]
     float M[kC * kC];    // gated Q K^T, lower with diagonal, [t][i]
     float MT[kC * kC];   // its transpose
-    float P[kC * kC];    // sum over value rows of dR_t . W_i, then dA
-    float dM[kC * kC];   // sum over value rows of dO_t . W_i, then dM o Gamma
+    // per wave: its value rows' part of sum_v dR_t . W_i (of sum_v dO_t . W_i); slot 0
+    // then holds dA (dM o Gamma)
+    float P[kWaves][kC * kC];
+    float dM[kWaves][kC * kC];
     float dg[kC];        // d L / d (natural log gamma_t)
     float db[kC];        // d L / d beta_t
     float W[kWaves][kC * 32];   // per wave: W [t][value row]
@@ -863,9 +865,6 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
         (tid < kC ? S.dg : S.db)[t] = 0.f;
     }
     {
-        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-        reinterpret_cast<float4*>(S.P)[tid] = z;
-        reinterpret_cast<float4*>(S.dM)[tid] = z;
     }
     wait_lds();
     barrier();
@@ -1060,8 +1059,8 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
             const int t = acc_row(jj, g);
-            atomicAdd(&S.P[t * kC + n], pp[jj]);
-            atomicAdd(&S.dM[t * kC + n], pm[jj]);
+            S.P[w][t * kC + n] = pp[jj];
+            S.dM[w][t * kC + n] = pm[jj];
         }
     }
     // ---- dQ = dY S_0 and dK = dX S_0 + diag(gamma_C / gamma) W dS_C for key columns
@@ -1122,20 +1121,30 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
         const int t = tid >> 3, q = tid & 7;
         const float lgt = S.lg[t], btt = S.beta[t];
         float erow = 0.f, brow = 0.f;
+        float4 ps = *reinterpret_cast<const float4*>(S.P[0] + t * kC + 4 * q);
+        float4 ms = *reinterpret_cast<const float4*>(S.dM[0] + t * kC + 4 * q);
+#pragma unroll
+        for (int ww = 1; ww < kWaves; ++ww) {
+            const float4 a = *reinterpret_cast<const float4*>(S.P[ww] + t * kC + 4 * q);
+            const float4 b = *reinterpret_cast<const float4*>(S.dM[ww] + t * kC + 4 * q);
+            ps.x += a.x; ps.y += a.y; ps.z += a.z; ps.w += a.w;
+            ms.x += b.x; ms.y += b.y; ms.z += b.z; ms.w += b.w;
+        }
+        const float psum[4] = {ps.x, ps.y, ps.z, ps.w}, msum[4] = {ms.x, ms.y, ms.z, ms.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 4 * q + e;
             const float gt = i <= t ? exp2f(lgt - S.lg[i]) : 0.f;
-            const float dbl = i < t ? -S.P[t * kC + i] : 0.f;  // d(diag(beta) LG)
+            const float dbl = i < t ? -psum[e] : 0.f;  // d(diag(beta) LG)
             const float lgv = S.LG[t * kC + i];
-            const float dmv = i <= t ? S.dM[t * kC + i] : 0.f;
+            const float dmv = i <= t ? msum[e] : 0.f;
             // (the diagonal ratio gamma_t / gamma_t is 1: no gate term)
             const float ek = btt * dbl * lgv, eq = i < t ? dmv * S.M[t * kC + i] : 0.f;
             brow += dbl * lgv;
             erow += ek + eq;
             if (i < t) atomicAdd(&S.dg[i], -(ek + eq));
-            S.P[t * kC + i] = btt * dbl * gt;  // dA (strict lower)
-            S.dM[t * kC + i] = dmv * gt;       // dM o Gamma (lower with diagonal)
+            S.P[0][t * kC + i] = btt * dbl * gt;  // dA (strict lower)
+            S.dM[0][t * kC + i] = dmv * gt;       // dM o Gamma (lower with diagonal)
         }
         erow = sum8(erow);
         brow = sum8(brow);
@@ -1155,12 +1164,12 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
             const bf16x8 bqv = rd_tr(S.Q, tr, w, kk);
             // rows i of this k-step in the accumulator order
             bf16x8 qh, ql, ah, al, th, tl;
-            ld_split(S.dM + n * kC + 16 * kk + 4 * g, 8, qh, ql, 1.f);
+            ld_split(S.dM[0] + n * kC + 16 * kk + 4 * g, 8, qh, ql, 1.f);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int i = 16 * kk + 8 * (e >> 2) + 4 * g + (e & 3);
-                split2(S.P[n * kC + i] + S.P[i * kC + n], ah, al, e);
-                split2(S.dM[i * kC + n], th, tl, e);
+                split2(S.P[0][n * kC + i] + S.P[0][i * kC + n], ah, al, e);
+                split2(S.dM[0][i * kC + n], th, tl, e);
             }
             fq = mfma_32x32x16(qh, bkv, fq);
             fq = mfma_32x32x16(ql, bkv, fq);
