@@ -13,6 +13,7 @@ import pytest
 import synth
 from oracle import recurrent as RC
 from parity import check_close, dev, host, say
+from test_edge_gpu import EDGE_DAGS
 
 pytestmark = pytest.mark.gpu
 
@@ -187,3 +188,18 @@ def test_scan_bwd_wide_gates_and_short_branches(seed):
 def test_scan_bwd_nested_forks():
     say("case scan bwd chain of nested forks")
     _run_bwd(_chain_dag(), 3, 1800, wide=True)
+
+
+@pytest.mark.parametrize("name", sorted(EDGE_DAGS))
+def test_scan_edge_dags_fwd_bwd(name):
+    """The packing's degenerate cases (a single token, tile-aligned and one-past-aligned
+    streams, forks at 0 and at the end, a child packed before its parent, mounted spans of
+    any producer, which the scan ignores), gates over their whole range."""
+    say(f"case scan edge {name}")
+    rows_b, rows_m = EDGE_DAGS[name]
+    b = np.asarray(rows_b, dtype=np.int32).reshape(-1, 4)
+    m = np.asarray(rows_m, dtype=np.int32).reshape(-1, 5)
+    dag = synth.Dag(name, b, m, int(b[:, 3].sum()))
+    o, ro = _run(dag, 2, 1900, wide=True)
+    check_close(o, ro, SCAN_TOL, "o")
+    _run_bwd(dag, 2, 1950, wide=True)
