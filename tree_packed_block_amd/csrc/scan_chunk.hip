@@ -51,15 +51,18 @@ constexpr int kWaves = kD / 32; // one wave per 32 value rows (or key columns)
 constexpr int kThr = 64 * kWaves;
 constexpr int kRowB = kD * 2;   // bytes of one bf16 row
 
-// Per (chunk, head) record written by the prep kernel, float32.  Matrices in "lane
-// order" [4][64 lanes][4]: element j = 4 q + r of lane l sits at (64 q + l) * 4 + r, so
-// that 64 lanes reading one float4 each touch 1 KiB of consecutive bytes.
+// Per (chunk, head) record written by the prep kernel.  U in float32 "lane order"
+// [4][64 lanes][4] (element j = 4 q + r of lane l at (64 q + l) * 4 + r, so that 64 lanes
+// reading one float4 each touch 1 KiB of consecutive bytes); the matrices that only ever
+// enter MFMAs as A operands already split into bf16 high and low parts, "split order"
+// [k-step kk][part][64 lanes][8 bf16] (the 8 values of k-step kk of lane l at 16 l bytes of
+// its 1 KiB block), four blocks per matrix:
 //   U    [4 waves] lane order: U[acc_row(j, g)][32 w + n]      (accumulator order)
-//   T    lane order: T[n][acc_row(j, g)]     (A operand with k in the accumulator's order)
-//   M    lane order: M[n][acc_row(j, g)]
-//   G    gamma_t [32], beta_t gamma_t [32], gamma_C / gamma_t [32], unused [160]
-//   TT   lane order: T[acc_row(j, g)][n]     (A operand of T^T)
-//   MT   lane order: M[acc_row(j, g)][n]
+//   T    split order: T[n][acc_row(j, g)]    (A operand with k in the accumulator's order)
+//   M    split order: M[n][acc_row(j, g)]
+//   G    float32 gamma_t [32], beta_t gamma_t [32], gamma_C / gamma_t [32], unused [160]
+//   TT   split order: T[acc_row(j, g)][n]    (A operand of T^T)
+//   MT   split order: M[acc_row(j, g)][n]
 // The forward reads T, M, G and the backward G, TT, MT as one contiguous block each.
 constexpr int kRecU = 0, kRecT = 4096, kRecM = 5120, kRecG = 6144, kRecTT = 6400,
               kRecMT = 7424, kRec = 8448;
@@ -98,6 +101,25 @@ __device__ __forceinline__ void ld16f(const float* p, int s, float (&v)[16]) {
 // A matrix in lane order (see the record) at p: this lane's 16 elements.
 __device__ __forceinline__ void ld_lane(const float* p, int lane, float (&v)[16]) {
     ld16f(p + 4 * lane, 256, v);
+}
+// A matrix's 16 values of this lane (j = 8 kk + e) in split order at p, and back as the
+// bf16 parts of k-step kk.
+__device__ __forceinline__ void split8(const float (&v)[16], int kk, bf16x8& hi, bf16x8& lo);
+__device__ __forceinline__ void st_split(float* p, int lane, const float (&v)[16]) {
+    unsigned char* b = reinterpret_cast<unsigned char*>(p);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 hi, lo;
+        split8(v, kk, hi, lo);
+        *reinterpret_cast<bf16x8*>(b + ((2 * kk) * 64 + lane) * 16) = hi;
+        *reinterpret_cast<bf16x8*>(b + ((2 * kk + 1) * 64 + lane) * 16) = lo;
+    }
+}
+__device__ __forceinline__ void ld_split_rec(const float* p, int lane, int kk, bf16x8& hi,
+                                             bf16x8& lo) {
+    const unsigned char* b = reinterpret_cast<const unsigned char*>(p);
+    hi = *reinterpret_cast<const bf16x8*>(b + ((2 * kk) * 64 + lane) * 16);
+    lo = *reinterpret_cast<const bf16x8*>(b + ((2 * kk + 1) * 64 + lane) * 16);
 }
 __device__ __forceinline__ void st16f(float* p, int s, const float (&v)[16]) {
 #pragma unroll
@@ -361,7 +383,7 @@ __global__ __launch_bounds__(kThr) void gdn_chunk_prep_kernel(
             fwd_solve(tv, S.LG, S.beta, g);
 #pragma unroll
             for (int j = 0; j < 16; ++j) S.T[acc_row(j, g) * kC + n] = tv[j];
-            st16f(rec + kRecTT + 4 * lane, 256, tv);  // T^T rows n: T[acc_row(j, g)][n]
+            st_split(rec + kRecTT, lane, tv);  // T^T rows n: T[acc_row(j, g)][n]
             // gamma_C / gamma_t as one difference of logarithms (1 past nt)
             const float lgC = __shfl(la, nt - 1, 64);
             if (lane < kC) {
@@ -373,7 +395,7 @@ __global__ __launch_bounds__(kThr) void gdn_chunk_prep_kernel(
         } else {
 #pragma unroll
             for (int j = 0; j < 16; ++j) S.M[acc_row(j, g) * kC + n] = v[j];
-            st16f(rec + kRecMT + 4 * lane, 256, v);  // M^T rows n: M[acc_row(j, g)][n]
+            st_split(rec + kRecMT, lane, v);  // M^T rows n: M[acc_row(j, g)][n]
         }
     }
     wait_lds();
@@ -402,11 +424,11 @@ __global__ __launch_bounds__(kThr) void gdn_chunk_prep_kernel(
         for (int j = 0; j < 16; ++j) uv[j] = u[j];
         st16f(rec + kRecU + (w * 4 * 64 + lane) * 4, 64 * 4, uv);
     }
-    if (w == 2) st16f(rec + kRecT + 4 * lane, 256, trow);
+    if (w == 2) st_split(rec + kRecT, lane, trow);
     if (w == 3) {
         float mrow[16];
         ld16f(S.M + n * kC + 4 * g, 8, mrow);
-        st16f(rec + kRecM + 4 * lane, 256, mrow);
+        st_split(rec + kRecM, lane, mrow);
     }
 }
 
@@ -522,10 +544,8 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
         if (ci + 1 < nch) issue(c + 1, buf ^ 1);
 
         const float* TMG = B.TMG;
-        float cu[16], ct[16], cm[16], cgam[16], cbg[16], cig[16];
+        float cu[16], cgam[16], cbg[16], cig[16];
         ld_lane(B.U[w], lane, cu);
-        ld_lane(TMG, lane, ct);
-        ld_lane(TMG + (kRecM - kRecT), lane, cm);
         ld16f(TMG + (kRecG - kRecT) + kGam + 4 * g, 8, cgam);
         ld16f(TMG + (kRecG - kRecT) + kBG + 4 * g, 8, cbg);
         ld16f(TMG + (kRecG - kRecT) + kIG + 4 * g, 8, cig);
@@ -554,30 +574,33 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
         float xs[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) xs[j] = (X[j] + X2[j]) * cbg[j];
-        f32x16 Wa = zero16();
+        // (the three products of the split operands in separate accumulators: chains of 2)
+        f32x16 Wa = zero16(), Wb = zero16(), Wc = zero16();
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             bf16x8 th, tl, xh, xl;
-            split8(ct, kk, th, tl);
+            ld_split_rec(TMG, lane, kk, th, tl);
             split8(xs, kk, xh, xl);
             Wa = mfma_32x32x16(th, xh, Wa);
-            Wa = mfma_32x32x16(th, xl, Wa);
-            Wa = mfma_32x32x16(tl, xh, Wa);
+            Wb = mfma_32x32x16(th, xl, Wb);
+            Wc = mfma_32x32x16(tl, xh, Wc);
         }
         float wv[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) wv[j] = cu[j] - Wa[j];
+        for (int j = 0; j < 16; ++j) wv[j] = cu[j] - (Wa[j] + Wb[j] + Wc[j]);
         // O = diag(gamma) Y + M W
-        f32x16 MW = zero16();
+        f32x16 MW = zero16(), MWb = zero16(), MWc = zero16();
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             bf16x8 mh, ml, wh, wl;
-            split8(cm, kk, mh, ml);
+            ld_split_rec(TMG + (kRecM - kRecT), lane, kk, mh, ml);
             split8(wv, kk, wh, wl);
             MW = mfma_32x32x16(mh, wh, MW);
-            MW = mfma_32x32x16(mh, wl, MW);
-            MW = mfma_32x32x16(ml, wh, MW);
+            MWb = mfma_32x32x16(mh, wl, MWb);
+            MWc = mfma_32x32x16(ml, wh, MWc);
         }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) MW[j] += MWb[j] + MWc[j];
         if (Og != nullptr) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) ostash[j] = (bf16)(cgam[j] * (Y[j] + Y2[j]) + MW[j]);
@@ -696,9 +719,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_dstate_kernel(
         if (ci > 0) issue(c - 1, buf ^ 1);
 
         const float* G = B.GTM;
-        float cmt[16], ctt[16], cgam[16], cbg[16], cig[16];
-        ld_lane(G + (kRecMT - kRecG), lane, cmt);
-        ld_lane(G + (kRecTT - kRecG), lane, ctt);
+        float cgam[16], cbg[16], cig[16];
         ld16f(G + kGam + 4 * g, 8, cgam);
         ld16f(G + kBG + 4 * g, 8, cbg);
         ld16f(G + kIG + 4 * g, 8, cig);
@@ -710,7 +731,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_dstate_kernel(
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             bf16x8 mh, ml;
-            split8(cmt, kk, mh, ml);
+            ld_split_rec(G + (kRecMT - kRecG), lane, kk, mh, ml);
             o8[kk] = rd_tr(B.dO, tr, w, kk);
             tA = mfma_32x32x16(mh, o8[kk], tA);
             tA = mfma_32x32x16(ml, o8[kk], tA);
@@ -731,16 +752,18 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_dstate_kernel(
         for (int j = 0; j < 16; ++j) dw[j] = tA[j] + cig[j] * (tB[j] + tB2[j]);
         // dR = T^T dW; dX = -diag(beta gamma) dR, dY = diag(gamma) dO (rows past nt of the
         // staged dO repeat the last row: masked here; dX vanishes there with beta)
-        f32x16 dR = zero16();
+        f32x16 dR = zero16(), dRb = zero16(), dRc = zero16();
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             bf16x8 th, tl, wh, wl;
-            split8(ctt, kk, th, tl);
+            ld_split_rec(G + (kRecTT - kRecG), lane, kk, th, tl);
             split8(dw, kk, wh, wl);
             dR = mfma_32x32x16(th, wh, dR);
-            dR = mfma_32x32x16(th, wl, dR);
-            dR = mfma_32x32x16(tl, wh, dR);
+            dRb = mfma_32x32x16(th, wl, dRb);
+            dRc = mfma_32x32x16(tl, wh, dRc);
         }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dR[j] += dRb[j] + dRc[j];
         bf16x8 xh[2], xl[2], yh[2], yl[2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
@@ -942,8 +965,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
     // ---- W = U - T diag(beta gamma) X; vx = V - gamma X
     float wv[16], vx[16];
     {
-        float tv[16], xs[16];
-        ld_lane(rec + kRecT, lane, tv);
+        float xs[16];
         ld_lane(rec + kRecU + w * 1024, lane, wv);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -954,7 +976,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             bf16x8 th, tl, xh, xl;
-            split8(tv, kk, th, tl);
+            ld_split_rec(rec + kRecT, lane, kk, th, tl);
             split8(xs, kk, xh, xl);
             Wa = mfma_32x32x16(th, xh, Wa);
             Wa = mfma_32x32x16(th, xl, Wa);
@@ -988,18 +1010,17 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
                 tB2 = mfma_32x32x16(ak, slo, tB2);
             }
         }
-        float dw[16], ttv[16];
+        float dw[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             tb[j] = (tB[j] + tB2[j]) * ig[j];
             dw[j] = tA[j] + tb[j];
         }
-        ld_lane(rec + kRecTT, lane, ttv);
         f32x16 dRa = zero16();
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             bf16x8 th, tl, wh, wl;
-            split8(ttv, kk, th, tl);
+            ld_split_rec(rec + kRecTT, lane, kk, th, tl);
             split8(dw, kk, wh, wl);
             dRa = mfma_32x32x16(th, wh, dRa);
             dRa = mfma_32x32x16(th, wl, dRa);
