@@ -644,13 +644,21 @@ def main():
     ms_sb = clock(lambda: tpb.gated_delta_scan_bwd(plan_s, ts["q"], ts["k"], ts["v"],
                                                    ts["alpha"], ts["beta"], dos, *grads,
                                                    ws=wsb))
+    # the training pair: forward keeping its chunk states, backward without the replay
+    ms_ss = clock(lambda: tpb.gated_delta_scan_save(plan_s, ts["q"], ts["k"], ts["v"],
+                                                    ts["alpha"], ts["beta"], o=os_, ws=wsb))
+    ms_sbs = clock(lambda: tpb.gated_delta_scan_bwd_saved(plan_s, ts["q"], ts["k"], ts["v"],
+                                                          ts["alpha"], ts["beta"], dos, wsb,
+                                                          *grads))
     flops_s = 6.0 * 128 * 128 * H_s * dag.T
     out["breakdown"]["gdn_scan"] = {
         "fwd_ms": round(ms_s, 3), "fwd_GFLOP/s": round(flops_s / (ms_s * 1e-3) / 1e9, 1),
-        "bwd_ms": round(ms_sb, 3),
+        "bwd_ms": round(ms_sb, 3), "fwd_save_ms": round(ms_ss, 3),
+        "bwd_saved_ms": round(ms_sbs, 3),
         "note": "16 heads, 128x128 state, 32-token chunks on the matrix cores; rate on "
-                "6*Dk*Dv FLOP per token-head of the recurrence; the backward recomputes the "
-                "forward (states at chunk starts) and is timed whole; sequential along each "
+                "6*Dk*Dv FLOP per token-head of the recurrence; bwd recomputes the forward "
+                "(states at chunk starts) and is timed whole; fwd_save + bwd_saved is the "
+                "training pair that keeps those states instead; sequential along each "
                 "branch (critical path: root + longest worker)"}
     del wsb
 

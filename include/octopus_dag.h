@@ -293,10 +293,11 @@ int octopus_gated_delta_scan(const octopus_plan* plan, octopus_dtype dtype, int3
                              const void* v, const float* alpha, const float* beta, void* o,
                              void* ws, size_t ws_bytes, void* stream);
 
-/* Workspace bytes of octopus_gated_delta_scan_bwd: float32 checkpoint slots and gradient
- * slots, the state at the start and the state gradient at the end of every chunk of the
- * plan (32-token chunks, split at fork offsets), each H x Dv x Dk, and the per-chunk
- * records of the forward (21.5 GB at 262,144 tokens and H = 16). */
+/* Workspace bytes of octopus_gated_delta_scan_bwd: float32 checkpoint slots, one
+ * initial-state gradient per branch, the state at the start and the state gradient at the
+ * end of every chunk of the plan (32-token chunks, split at fork offsets), each
+ * H x Dv x Dk, and the per-chunk records of the forward (21.6 GB at 262,144 tokens and
+ * H = 16). */
 size_t octopus_gdn_bwd_workspace_bytes(const octopus_plan* plan, int32_t H, int32_t Dk,
                                        int32_t Dv);
 
@@ -307,12 +308,33 @@ size_t octopus_gdn_bwd_workspace_bytes(const octopus_plan* plan, int32_t H, int3
  * project page, primitives table).  Recomputes the forward (the states at chunk starts go
  * to the workspace), walks every branch's chunks in reverse carrying only the state
  * gradient (deepest branches first), then computes every chunk's gradients in parallel.
- * Same support and errors as octopus_gated_delta_scan. */
+ * Deterministic: the children forking at one offset hand their initial-state gradients
+ * to the parent in ascending branch order (no atomics), so repeated calls give the same
+ * bits.  Same support and errors as octopus_gated_delta_scan. */
 int octopus_gated_delta_scan_bwd(const octopus_plan* plan, octopus_dtype dtype, int32_t H,
                                  int32_t Dk, int32_t Dv, const void* q, const void* k,
                                  const void* v, const float* alpha, const float* beta,
                                  const void* dout, void* dq, void* dk, void* dv, float* dalpha,
                                  float* dbeta, void* ws, size_t ws_bytes, void* stream);
+
+/* Training pair: octopus_gated_delta_scan_save is octopus_gated_delta_scan (o written)
+ * that also leaves in ws (octopus_gdn_bwd_workspace_bytes bytes) the per-chunk records and
+ * the state at every chunk start; octopus_gated_delta_scan_bwd_saved is
+ * octopus_gated_delta_scan_bwd without its recomputation of the forward, reading them
+ * from that ws.  The caller passes the same plan and the same q, k, v, alpha, beta to both
+ * and leaves ws untouched in between (results are undefined otherwise: nothing checks
+ * it).  The backward leaves the saved part in place, so it may run again on the same ws
+ * (with another dout).  Same support and errors as octopus_gated_delta_scan_bwd. */
+int octopus_gated_delta_scan_save(const octopus_plan* plan, octopus_dtype dtype, int32_t H,
+                                  int32_t Dk, int32_t Dv, const void* q, const void* k,
+                                  const void* v, const float* alpha, const float* beta, void* o,
+                                  void* ws, size_t ws_bytes, void* stream);
+int octopus_gated_delta_scan_bwd_saved(const octopus_plan* plan, octopus_dtype dtype,
+                                       int32_t H, int32_t Dk, int32_t Dv, const void* q,
+                                       const void* k, const void* v, const float* alpha,
+                                       const float* beta, const void* dout, void* dq, void* dk,
+                                       void* dv, float* dalpha, float* dbeta, void* ws,
+                                       size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- paged decode */
 

@@ -387,7 +387,9 @@ def test_new_entry_points_reject_bad_arguments_before_any_launch():
         n_chunks += len(cuts) + 1 if ln > 0 else 0
     state = 2 * 128 * 128 * 4
     assert tpb.gdn_workspace_bytes(p, 2) == 1 * state + n_chunks * 2 * 8448 * 4
-    assert tpb.gdn_bwd_workspace_bytes(p, 2) == (2 * 1 + 2 * n_chunks) * state + \
+    # backward: checkpoint slots, one initial-state gradient per branch, two state sets
+    # per chunk, the records
+    assert tpb.gdn_bwd_workspace_bytes(p, 2) == (1 + len(br) + 2 * n_chunks) * state + \
         n_chunks * 2 * 8448 * 4
     # extend
     assert _code(L.octopus_paged_mount_extend(tpb.BF16, 1, 16, 4, 96, 64, 0.0, fake, fake, fake,

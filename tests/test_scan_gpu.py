@@ -203,3 +203,32 @@ def test_scan_edge_dags_fwd_bwd(name):
     o, ro = _run(dag, 2, 1900, wide=True)
     check_close(o, ro, SCAN_TOL, "o")
     _run_bwd(dag, 2, 1950, wide=True)
+
+
+@pytest.mark.parametrize("name", ["episode_small", "forest_small"])
+def test_scan_save_then_bwd_saved(name):
+    """The training pair (forward keeping its chunk states, backward without replaying the
+    forward) gives bit for bit the outputs and gradients of the plain forward and backward,
+    also when the backward runs a second time on the same workspace with another dO."""
+    import torch
+    import tree_packed_block_amd as tpb
+    say(f"case scan save + bwd_saved {name}")
+    dag, _ = synth.build(name)
+    H = 2
+    x = synth.draw_scan_inputs(np.random.default_rng(31), dag.T, H)
+    plan = tpb.Plan(dag.branches, dag.mounts, dag.T).upload()
+    t = [dev(x[n], "bf16") for n in ("q", "k", "v")]
+    a, b = torch.from_numpy(x["alpha"]).cuda(), torch.from_numpy(x["beta"]).cuda()
+    o_ref = tpb.gated_delta_scan(plan, *t, a, b)
+    o, ws = tpb.gated_delta_scan_save(plan, *t, a, b)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref), "forward outputs differ"
+    for seed in (32, 33):
+        do = dev(synth.round_bf16((0.5 * np.random.default_rng(seed).standard_normal(
+            x["v"].shape)).astype(np.float32)), "bf16")
+        ref = tpb.gated_delta_scan_bwd(plan, *t, a, b, do)
+        got = tpb.gated_delta_scan_bwd_saved(plan, *t, a, b, do, ws)
+        torch.cuda.synchronize()
+        for nm, g1, g2 in zip(("dq", "dk", "dv", "dalpha", "dbeta"), got, ref):
+            assert torch.equal(g1, g2), f"{nm} differs from the plain backward (dO seed {seed})"
+    say("  identical to the plain forward and backward")

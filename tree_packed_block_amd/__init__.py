@@ -30,6 +30,8 @@ from ._lib import (  # noqa: F401
     extend_segments,
     gated_delta_scan,
     gated_delta_scan_bwd,
+    gated_delta_scan_bwd_saved,
+    gated_delta_scan_save,
     gdn_bwd_workspace_bytes,
     gdn_workspace_bytes,
     default_scale,

@@ -35,7 +35,8 @@ EXPORTS = [
     "octopus_paged_mount_extend", "octopus_dag_positions", "octopus_rope",
     "octopus_rope_workspace_bytes", "octopus_dag_attn_fwd_rope", "octopus_dag_attn_bwd_rope",
     "octopus_gdn_workspace_bytes", "octopus_gated_delta_scan",
-    "octopus_gdn_bwd_workspace_bytes", "octopus_gated_delta_scan_bwd", "octopus_last_error",
+    "octopus_gdn_bwd_workspace_bytes", "octopus_gated_delta_scan_bwd",
+    "octopus_gated_delta_scan_save", "octopus_gated_delta_scan_bwd_saved", "octopus_last_error",
     "octopus_version",
 ]
 
@@ -147,6 +148,8 @@ def lib():
     L.octopus_gated_delta_scan_bwd.argtypes = [_vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
                                                ctypes.c_int32] + [_vp] * 11 + [_vp,
                                                                                 ctypes.c_size_t, _vp]
+    L.octopus_gated_delta_scan_save.argtypes = L.octopus_gated_delta_scan.argtypes
+    L.octopus_gated_delta_scan_bwd_saved.argtypes = L.octopus_gated_delta_scan_bwd.argtypes
     L.octopus_last_error.restype = ctypes.c_char_p
     L.octopus_version.restype = ctypes.c_char_p
     _lib = L
@@ -564,6 +567,62 @@ def gated_delta_scan_bwd(plan: Plan, q, k, v, alpha, beta, dout, dq=None, dk=Non
         mine.append(ws)
     _owned(s, *mine)
     _check(lib().octopus_gated_delta_scan_bwd(
+        plan.handle, _dtype_code(q), H, Dk, Dv, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+        alpha.data_ptr(), beta.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+        dv.data_ptr(), dalpha.data_ptr(), dbeta.data_ptr(), ws.data_ptr(), ws.numel(),
+        _vp(s.cuda_stream)))
+    return dq, dk, dv, dalpha, dbeta
+
+
+def gated_delta_scan_save(plan: Plan, q, k, v, alpha, beta, o=None, ws=None, stream=None):
+    """``gated_delta_scan`` that also keeps, in ``ws`` (``gdn_bwd_workspace_bytes``), what
+    ``gated_delta_scan_bwd_saved`` reads: returns ``(o, ws)``.  Keep ``ws`` and the inputs
+    unchanged until the backward has run."""
+    import torch
+    T, H, Dk = q.shape
+    Dv = v.shape[2]
+    _need(q, (plan.T, H, Dk), q.dtype, "q")
+    _need(k, (plan.T, H, Dk), q.dtype, "k")
+    _need(v, (plan.T, H, Dv), q.dtype, "v")
+    _need(alpha, (plan.T, H), torch.float32, "alpha")
+    _need(beta, (plan.T, H), torch.float32, "beta")
+    s = _stream(stream, q.device)
+    mine = []
+    if o is None:
+        o = torch.empty_like(v)
+        mine.append(o)
+    if ws is None:
+        ws = torch.empty(max(gdn_bwd_workspace_bytes(plan, H, Dk, Dv), 16), dtype=torch.uint8,
+                         device=q.device)
+        mine.append(ws)
+    _owned(s, *mine)
+    _check(lib().octopus_gated_delta_scan_save(plan.handle, _dtype_code(q), H, Dk, Dv,
+                                               q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                               alpha.data_ptr(), beta.data_ptr(), o.data_ptr(),
+                                               ws.data_ptr(), ws.numel(), _vp(s.cuda_stream)))
+    return o, ws
+
+
+def gated_delta_scan_bwd_saved(plan: Plan, q, k, v, alpha, beta, dout, ws, dq=None, dk=None,
+                               dv=None, dalpha=None, dbeta=None, stream=None):
+    """Backward of ``gated_delta_scan_save`` from the workspace it filled: returns
+    ``(dq, dk, dv, dalpha, dbeta)``."""
+    import torch
+    T, H, Dk = q.shape
+    Dv = v.shape[2]
+    _need(q, (plan.T, H, Dk), q.dtype, "q")
+    _need(k, (plan.T, H, Dk), q.dtype, "k")
+    _need(v, (plan.T, H, Dv), q.dtype, "v")
+    _need(dout, (plan.T, H, Dv), q.dtype, "dout")
+    _need(alpha, (plan.T, H), torch.float32, "alpha")
+    _need(beta, (plan.T, H), torch.float32, "beta")
+    s = _stream(stream, q.device)
+    outs = []
+    for t, like in ((dq, q), (dk, k), (dv, v), (dalpha, alpha), (dbeta, beta)):
+        outs.append(torch.empty_like(like) if t is None else t)
+    _owned(s, *[o for o, t in zip(outs, (dq, dk, dv, dalpha, dbeta)) if t is None])
+    dq, dk, dv, dalpha, dbeta = outs
+    _check(lib().octopus_gated_delta_scan_bwd_saved(
         plan.handle, _dtype_code(q), H, Dk, Dv, q.data_ptr(), k.data_ptr(), v.data_ptr(),
         alpha.data_ptr(), beta.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
         dv.data_ptr(), dalpha.data_ptr(), dbeta.data_ptr(), ws.data_ptr(), ws.numel(),

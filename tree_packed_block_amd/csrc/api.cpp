@@ -71,6 +71,8 @@ octo::DevPlan dev_view(const octo::Plan& p) {
     d.sc_chunk_base = reinterpret_cast<const int32_t*>(base + p.layout.sc_chunk_base);
     d.sc_chunk_tok = reinterpret_cast<const int32_t*>(base + p.layout.sc_chunk_tok);
     d.sc_chunk_nt = reinterpret_cast<const int32_t*>(base + p.layout.sc_chunk_nt);
+    d.sc_ck_kid_ptr = reinterpret_cast<const int32_t*>(base + p.layout.sc_ck_kid_ptr);
+    d.sc_ck_kid = reinterpret_cast<const int32_t*>(base + p.layout.sc_ck_kid);
     return d;
 }
 
@@ -567,56 +569,127 @@ int octopus_gated_delta_scan(const octopus_plan* plan, octopus_dtype dtype, int3
 size_t octopus_gdn_bwd_workspace_bytes(const octopus_plan* plan, int32_t H, int32_t Dk,
                                        int32_t Dv) {
     if (plan == nullptr || H < 1 || Dk != 128 || Dv != 128) return 0;
-    return (size_t)2 * std::max(plan->p.n_slots, 1) * gdn_state_bytes(H) +
-           gdn_prep_bytes(plan, H) + (size_t)2 * plan->p.n_chunks * gdn_state_bytes(H);
+    return ((size_t)std::max(plan->p.n_slots, 1) + plan->p.sc_init.size() +
+            (size_t)2 * plan->p.n_chunks) * gdn_state_bytes(H) +
+           gdn_prep_bytes(plan, H);
 }
+
+namespace {
+// The scan backward's workspace, in order: checkpoint slots [n_slots][H][128][128], every
+// branch's initial-state gradient [nb][H][128][128], the state at every chunk start and the
+// state gradient at every chunk end [n_chunks][H][128][128] (key-major), the per-chunk
+// records.
+struct GdnBwdWs {
+    float *slots, *dkids, *chunks, *dsc, *prep;
+};
+GdnBwdWs gdn_bwd_ws(const octopus_plan* plan, int32_t H, void* ws) {
+    const size_t n_slots = (size_t)std::max(plan->p.n_slots, 1);
+    const size_t per = gdn_state_bytes(H) / sizeof(float);  // floats per state set
+    const size_t nc = (size_t)plan->p.n_chunks;
+    GdnBwdWs w;
+    w.slots = static_cast<float*>(ws);
+    w.dkids = w.slots + per * n_slots;
+    w.chunks = w.dkids + per * plan->p.sc_init.size();
+    w.dsc = w.chunks + per * nc;
+    w.prep = w.dsc + per * nc;
+    return w;
+}
+int check_gdn_bwd_ws(const octopus_plan* plan, int32_t H, int32_t Dk, int32_t Dv, void* ws,
+                     size_t ws_bytes) {
+    const size_t need = octopus_gdn_bwd_workspace_bytes(plan, H, Dk, Dv);
+    if (ws == nullptr || ws_bytes < need || !aligned(ws, 16))
+        return fail(OCTOPUS_EWORKSPACE, "scan backward workspace needs " + std::to_string(need) +
+                                            " bytes, 16-byte aligned");
+    return OCTOPUS_OK;
+}
+// The forward, keeping in the backward's workspace what the backward reads: the records
+// and the state at every chunk start (o may be NULL).
+int gdn_forward_keep(const octopus_plan* plan, int32_t H, const void* q, const void* k,
+                     const void* v, const float* alpha, const float* beta, void* o, void* ws,
+                     hipStream_t st) {
+    const octo::DevPlan dp = dev_view(plan->p);
+    const std::vector<int32_t>& lp = plan->p.level_ptr;
+    const GdnBwdWs w = gdn_bwd_ws(plan, H, ws);
+    hipError_t e = octo::launch_gdn_chunk_prep(dp, plan->p.n_chunks, H, q, k, v, alpha, beta,
+                                               w.prep, st);
+    if (e != hipSuccess) return hip_fail(e, "scan prep launch");
+    for (size_t l = 0; l + 1 < lp.size(); ++l) {
+        e = octo::launch_gdn_chunk_fwd(dp, lp[l], lp[l + 1] - lp[l], H, q, k, w.prep, o, w.slots,
+                                       w.chunks, st);
+        if (e != hipSuccess) return hip_fail(e, "scan forward launch");
+    }
+    return OCTOPUS_OK;
+}
+// The backward proper, from what gdn_forward_keep left in the workspace.
+int gdn_backward_kept(const octopus_plan* plan, int32_t H, const void* q, const void* k,
+                      const void* v, const float* alpha, const float* beta, const void* dout,
+                      void* dq, void* dk, void* dv, float* dalpha, float* dbeta, void* ws,
+                      hipStream_t st) {
+    const octo::DevPlan dp = dev_view(plan->p);
+    const std::vector<int32_t>& lp = plan->p.level_ptr;
+    const GdnBwdWs w = gdn_bwd_ws(plan, H, ws);
+    hipError_t e = hipSuccess;
+    // state gradients, deepest level first: a child's initial-state gradient is written
+    // before its parent runs
+    for (size_t l = lp.size() - 1; l-- > 0;) {
+        e = octo::launch_gdn_chunk_dstate(dp, lp[l], lp[l + 1] - lp[l], H, q, k, dout, w.prep,
+                                          w.dsc, w.dkids, st);
+        if (e != hipSuccess) return hip_fail(e, "scan backward (state gradient) launch");
+    }
+    e = octo::launch_gdn_chunk_grad(dp, plan->p.n_chunks, H, q, k, v, alpha, beta, dout, w.prep,
+                                    w.chunks, w.dsc, dq, dk, dv, dalpha, dbeta, st);
+    if (e != hipSuccess) return hip_fail(e, "scan backward launch");
+    return OCTOPUS_OK;
+}
+}  // namespace
 
 int octopus_gated_delta_scan_bwd(const octopus_plan* plan, octopus_dtype dtype, int32_t H,
                                  int32_t Dk, int32_t Dv, const void* q, const void* k,
                                  const void* v, const float* alpha, const float* beta,
                                  const void* dout, void* dq, void* dk, void* dv, float* dalpha,
                                  float* dbeta, void* ws, size_t ws_bytes, void* stream) {
-    const int rc = check_gdn(plan, dtype, H, Dk, Dv,
-                             {q, k, v, (const void*)alpha, (const void*)beta, dout,
-                              (const void*)dq, (const void*)dk, (const void*)dv,
-                              (const void*)dalpha, (const void*)dbeta});
+    int rc = check_gdn(plan, dtype, H, Dk, Dv,
+                       {q, k, v, (const void*)alpha, (const void*)beta, dout, (const void*)dq,
+                        (const void*)dk, (const void*)dv, (const void*)dalpha,
+                        (const void*)dbeta});
+    if (rc == OCTOPUS_OK) rc = check_gdn_bwd_ws(plan, H, Dk, Dv, ws, ws_bytes);
     if (rc != OCTOPUS_OK) return rc;
-    const size_t need = octopus_gdn_bwd_workspace_bytes(plan, H, Dk, Dv);
-    if (ws == nullptr || ws_bytes < need || !aligned(ws, 16))
-        return fail(OCTOPUS_EWORKSPACE, "scan backward workspace needs " + std::to_string(need) +
-                                            " bytes, 16-byte aligned");
-    const octo::DevPlan dp = dev_view(plan->p);
-    const std::vector<int32_t>& lp = plan->p.level_ptr;
     hipStream_t st = (hipStream_t)stream;
-    const size_t n_slots = (size_t)std::max(plan->p.n_slots, 1);
-    const size_t per = gdn_state_bytes(H) / sizeof(float);  // floats per state set
-    const int64_t nc = plan->p.n_chunks;
-    float* slots = static_cast<float*>(ws);
-    float* dslots = slots + per * n_slots;
-    float* chunks = dslots + per * n_slots;
-    float* dsc = chunks + per * (size_t)nc;
-    float* prep = dsc + per * (size_t)nc;
     // the forward again, keeping the state at the start of every chunk
-    hipError_t e = octo::launch_gdn_chunk_prep(dp, nc, H, q, k, v, alpha, beta, prep, st);
-    if (e != hipSuccess) return hip_fail(e, "scan backward (prep) launch");
-    for (size_t l = 0; l + 1 < lp.size(); ++l) {
-        e = octo::launch_gdn_chunk_fwd(dp, lp[l], lp[l + 1] - lp[l], H, q, k, prep, nullptr,
-                                       slots, chunks, st);
-        if (e != hipSuccess) return hip_fail(e, "scan backward (forward pass) launch");
-    }
-    e = octo::launch_fill_zero(dslots, per * n_slots, st);
-    if (e != hipSuccess) return hip_fail(e, "scan backward (clear) launch");
-    // state gradients, deepest level first: a child's initial-state gradient reaches its
-    // parent's slot before the parent runs
-    for (size_t l = lp.size() - 1; l-- > 0;) {
-        e = octo::launch_gdn_chunk_dstate(dp, lp[l], lp[l + 1] - lp[l], H, q, k, dout, prep, dsc,
-                                          dslots, st);
-        if (e != hipSuccess) return hip_fail(e, "scan backward (state gradient) launch");
-    }
-    e = octo::launch_gdn_chunk_grad(dp, nc, H, q, k, v, alpha, beta, dout, prep, chunks, dsc, dq,
-                                    dk, dv, dalpha, dbeta, st);
-    if (e != hipSuccess) return hip_fail(e, "scan backward launch");
-    return ok();
+    rc = gdn_forward_keep(plan, H, q, k, v, alpha, beta, nullptr, ws, st);
+    if (rc == OCTOPUS_OK)
+        rc = gdn_backward_kept(plan, H, q, k, v, alpha, beta, dout, dq, dk, dv, dalpha, dbeta,
+                               ws, st);
+    return rc == OCTOPUS_OK ? ok() : rc;
+}
+
+int octopus_gated_delta_scan_save(const octopus_plan* plan, octopus_dtype dtype, int32_t H,
+                                  int32_t Dk, int32_t Dv, const void* q, const void* k,
+                                  const void* v, const float* alpha, const float* beta, void* o,
+                                  void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_gdn(plan, dtype, H, Dk, Dv,
+                       {q, k, v, (const void*)alpha, (const void*)beta, (const void*)o});
+    if (rc == OCTOPUS_OK) rc = check_gdn_bwd_ws(plan, H, Dk, Dv, ws, ws_bytes);
+    if (rc != OCTOPUS_OK) return rc;
+    rc = gdn_forward_keep(plan, H, q, k, v, alpha, beta, o, ws, (hipStream_t)stream);
+    return rc == OCTOPUS_OK ? ok() : rc;
+}
+
+int octopus_gated_delta_scan_bwd_saved(const octopus_plan* plan, octopus_dtype dtype,
+                                       int32_t H, int32_t Dk, int32_t Dv, const void* q,
+                                       const void* k, const void* v, const float* alpha,
+                                       const float* beta, const void* dout, void* dq, void* dk,
+                                       void* dv, float* dalpha, float* dbeta, void* ws,
+                                       size_t ws_bytes, void* stream) {
+    int rc = check_gdn(plan, dtype, H, Dk, Dv,
+                       {q, k, v, (const void*)alpha, (const void*)beta, dout, (const void*)dq,
+                        (const void*)dk, (const void*)dv, (const void*)dalpha,
+                        (const void*)dbeta});
+    if (rc == OCTOPUS_OK) rc = check_gdn_bwd_ws(plan, H, Dk, Dv, ws, ws_bytes);
+    if (rc != OCTOPUS_OK) return rc;
+    rc = gdn_backward_kept(plan, H, q, k, v, alpha, beta, dout, dq, dk, dv, dalpha, dbeta, ws,
+                           (hipStream_t)stream);
+    return rc == OCTOPUS_OK ? ok() : rc;
 }
 
 int octopus_extend_segments(const octopus_branch* branches, int32_t n_branches,

@@ -34,6 +34,8 @@ struct DevPlan {
     // Chunked scan: first chunk of every branch [nb+1]; first packed token and length of
     // every chunk [n_chunks].
     const int32_t *sc_chunk_base, *sc_chunk_tok, *sc_chunk_nt;
+    // The children forking at every checkpoint (CSR over the checkpoint entries, ascending).
+    const int32_t *sc_ck_kid_ptr, *sc_ck_kid;
 };
 
 // Rotary-embedding frequencies of rotate-half pairs (x_i, x_{i+D/2}): pair i turns by
@@ -124,19 +126,18 @@ hipError_t launch_gdn_chunk_fwd(const DevPlan& p, int l0, int n_br, int H, const
                                 const void* k, const float* prep, void* o, float* states,
                                 float* chunk_states, hipStream_t s);
 // Backward: the state gradient of the branches level_br[l0 .. l0 + n_br) in reverse
-// (levels deepest first), written at every chunk's end into dsc [c][H][128][128];
-// dstates [n_slots][H][128][128] float32 gradient slots, zero before the first level,
-// which children add their initial-state gradients to.  Then, over every chunk,
-// dq, dk, dv [T][H][128] bf16 and dalpha, dbeta [T][H] float32.
+// (levels deepest first), written at every chunk's end into dsc [c][H][128][128]
+// (key-major); dkids [nb][H][128][128] float32: every child's initial-state gradient,
+// written by the child and added by its parent.  Then, over every chunk, dq, dk, dv
+// [T][H][128] bf16 and dalpha, dbeta [T][H] float32.
 hipError_t launch_gdn_chunk_dstate(const DevPlan& p, int l0, int n_br, int H, const void* q,
                                    const void* k, const void* dout, const float* prep,
-                                   float* dsc, float* dstates, hipStream_t s);
+                                   float* dsc, float* dkids, hipStream_t s);
 hipError_t launch_gdn_chunk_grad(const DevPlan& p, int64_t n_chunks, int H, const void* q,
                                  const void* k, const void* v, const float* alpha,
                                  const float* beta, const void* dout, const float* prep,
                                  const float* chunk_states, const float* dsc, void* dq, void* dk,
                                  void* dv, float* dalpha, float* dbeta, hipStream_t s);
-hipError_t launch_fill_zero(float* p, size_t n_floats, hipStream_t s);
 
 // Extend: rows q_ptr[c] .. q_ptr[c+1]-1 of q are cursor c's new tokens (own offsets
 // first_off[c] + j); segments as built by build_extend_segments.  max_new >= every m_c.

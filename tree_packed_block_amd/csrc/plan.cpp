@@ -550,6 +550,22 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
             }
             p.sc_ck_ptr.push_back((int32_t)p.sc_ck_off.size());
         }
+        // The children forking at every checkpoint, in ascending branch order (the
+        // backward adds their initial-state gradients in this fixed order).
+        {
+            std::vector<int32_t> ck_of_slot(p.n_slots, -1);
+            for (size_t c = 0; c < p.sc_ck_slot.size(); ++c) ck_of_slot[p.sc_ck_slot[c]] = (int32_t)c;
+            std::vector<int32_t> count(p.sc_ck_slot.size() + 1, 0);
+            for (int32_t b = 0; b < nb; ++b)
+                if (p.sc_init[b] >= 0) ++count[ck_of_slot[p.sc_init[b]] + 1];
+            p.sc_ck_kid_ptr.assign(p.sc_ck_slot.size() + 1, 0);
+            for (size_t c = 0; c < p.sc_ck_slot.size(); ++c)
+                p.sc_ck_kid_ptr[c + 1] = p.sc_ck_kid_ptr[c] + count[c + 1];
+            p.sc_ck_kid.assign(p.sc_ck_kid_ptr.back(), 0);
+            std::vector<int32_t> fill(p.sc_ck_kid_ptr.begin(), p.sc_ck_kid_ptr.end() - 1);
+            for (int32_t b = 0; b < nb; ++b)  // ascending b: each list comes out sorted
+                if (p.sc_init[b] >= 0) p.sc_ck_kid[fill[ck_of_slot[p.sc_init[b]]]++] = b;
+        }
         // Chunks of the chunked scan: boundaries every kScanChunk own tokens and at every
         // checkpoint offset inside the branch (the kernel walks the same rule).
         p.sc_chunk_base.assign(nb + 1, 0);
@@ -611,6 +627,8 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     L.sc_ck_ptr = place(p.sc_ck_ptr.size() * 4);
     L.sc_ck_off = place(std::max<size_t>(p.sc_ck_off.size(), 1) * 4);
     L.sc_ck_slot = place(std::max<size_t>(p.sc_ck_slot.size(), 1) * 4);
+    L.sc_ck_kid_ptr = place(p.sc_ck_kid_ptr.size() * 4);
+    L.sc_ck_kid = place(std::max<size_t>(p.sc_ck_kid.size(), 1) * 4);
     L.sc_level_br = place((size_t)nb * 4);
     L.sc_chunk_base = place((size_t)(nb + 1) * 4);
     L.sc_chunk_tok = place(std::max<size_t>(p.sc_chunk_tok.size(), 1) * 4);
@@ -645,6 +663,8 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     put(L.sc_ck_ptr, p.sc_ck_ptr.data(), p.sc_ck_ptr.size() * 4);
     put(L.sc_ck_off, p.sc_ck_off.data(), p.sc_ck_off.size() * 4);
     put(L.sc_ck_slot, p.sc_ck_slot.data(), p.sc_ck_slot.size() * 4);
+    put(L.sc_ck_kid_ptr, p.sc_ck_kid_ptr.data(), p.sc_ck_kid_ptr.size() * 4);
+    put(L.sc_ck_kid, p.sc_ck_kid.data(), p.sc_ck_kid.size() * 4);
     put(L.sc_level_br, p.level_br.data(), p.level_br.size() * 4);
     put(L.sc_chunk_base, p.sc_chunk_base.data(), p.sc_chunk_base.size() * 4);
     put(L.sc_chunk_tok, p.sc_chunk_tok.data(), p.sc_chunk_tok.size() * 4);

@@ -67,7 +67,7 @@ struct DevLayout {
            k_pairs = 0, mask_rows = 0, mask_cols = 0, blk_order = 0, blk_ptr = 0,
            blk_entries = 0, pos = 0, sc_start = 0, sc_len = 0, sc_init = 0, sc_ck_ptr = 0,
            sc_ck_off = 0, sc_ck_slot = 0, sc_level_br = 0, sc_chunk_base = 0, sc_chunk_tok = 0,
-           sc_chunk_nt = 0, total = 0;
+           sc_chunk_nt = 0, sc_ck_kid_ptr = 0, sc_ck_kid = 0, total = 0;
 };
 
 struct Plan {
@@ -90,6 +90,8 @@ struct Plan {
     // starts from checkpoint slot sc_init (-1: zero state) and saves its state before own
     // token sc_ck_off[j] into slot sc_ck_slot[j] (its children's fork points).
     std::vector<int32_t> sc_init, sc_ck_ptr, sc_ck_off, sc_ck_slot, level_ptr, level_br;
+    // The children forking at checkpoint j: sc_ck_kid[sc_ck_kid_ptr[j] .. [j+1]), ascending.
+    std::vector<int32_t> sc_ck_kid_ptr, sc_ck_kid;
     int32_t n_slots = 0;
     // Chunked scan: branch b's chunks (own tokens split every kScanChunk tokens and at
     // every checkpoint offset) are numbered sc_chunk_base[b] .. sc_chunk_base[b+1]-1;

@@ -651,13 +651,14 @@ constexpr int kGTMInst = (kRec - kRecG) * 4 / 1024;
 
 // Walks each branch's chunks in reverse carrying dS (the gradient of L = sum_t <dO_t, o_t>
 // with respect to the state at the current boundary), storing it at every chunk's end
-// into dsc [c][H][Dk][Dv] (key-major) for the gradient kernel.  dstates [n_slots][H][Dv][Dk]: slots
-// that children (deeper levels, launched earlier) added their initial-state gradients to;
-// this branch's own initial-state gradient is added to its parent's slot.
+// into dsc [c][H][Dk][Dv] (key-major) for the gradient kernel.  dkids [nb][H][Dv][Dk]:
+// the gradient of every child branch's initial state, written by the child (deeper
+// levels run earlier) and added by its parent at the fork offset, the children of one
+// offset in ascending branch order (so the sums do not depend on scheduling).
 __global__ __launch_bounds__(kThr, 1) void gdn_chunk_dstate_kernel(
     DevPlan P, int l0, int H, const bf16* __restrict__ Qg, const bf16* __restrict__ Kg,
     const bf16* __restrict__ dOg, const float* __restrict__ prep, float* __restrict__ dsc,
-    float* __restrict__ dstates) {
+    float* __restrict__ dkids) {
     __shared__ __attribute__((aligned(1024))) DstateBuf SB[2];
     const int b = ld_const(P.sc_level_br + l0 + blockIdx.x / H);
     const int h = blockIdx.x % H;
@@ -678,14 +679,17 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_dstate_kernel(
     for (int bk = 0; bk < 4; ++bk) dSt[bk] = zero16();
     auto add_handed = [&](int r) {
         while (ckr >= ck_lo && ld_const(P.sc_ck_off + ckr) == r) {
-            const float* src =
-                dstates + (((size_t)ld_const(P.sc_ck_slot + ckr) * H + h) * kD + dv) * kD;
+            const int k1 = ld_const(P.sc_ck_kid_ptr + ckr + 1);
+            for (int i = ld_const(P.sc_ck_kid_ptr + ckr); i < k1; ++i) {
+                const int kid = ld_const(P.sc_ck_kid + i);
+                const float* src = dkids + (((size_t)kid * H + h) * kD + dv) * kD;
 #pragma unroll
-            for (int bk = 0; bk < 4; ++bk) {
-                float v[16];
-                ld16f(src + 32 * bk + 4 * g, 8, v);
+                for (int bk = 0; bk < 4; ++bk) {
+                    float v[16];
+                    ld16f(src + 32 * bk + 4 * g, 8, v);
 #pragma unroll
-                for (int j = 0; j < 16; ++j) dSt[bk][j] += v[j];
+                    for (int j = 0; j < 16; ++j) dSt[bk][j] += v[j];
+                }
             }
             --ckr;
         }
@@ -790,13 +794,16 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_dstate_kernel(
         }
         add_handed(r0);
     }
-    // the gradient of this branch's initial state goes to its parent's fork slot
+    // the gradient of this branch's initial state, for its parent
     if (init >= 0) {
-        float* dst = dstates + (((size_t)init * H + h) * kD + dv) * kD;
+        float* dst = dkids + (((size_t)b * H + h) * kD + dv) * kD;
 #pragma unroll
-        for (int bk = 0; bk < 4; ++bk)
+        for (int bk = 0; bk < 4; ++bk) {
+            float v[16];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) atomicAdd(dst + 32 * bk + acc_row(j, g), dSt[bk][j]);
+            for (int j = 0; j < 16; ++j) v[j] = dSt[bk][j];
+            st16f(dst + 32 * bk + 4 * g, 8, v);
+        }
     }
 }
 
@@ -830,8 +837,13 @@ struct GradSmem {
     // then holds dA (dM o Gamma)
     float P[kWaves][kC * kC];
     float dM[kWaves][kC * kC];
-    float dg[kC];        // d L / d (natural log gamma_t)
-    float db[kC];        // d L / d beta_t
+    // parts of d L / d (natural log gamma_t) and d L / d beta_t, each written by one lane
+    // and added in a fixed order at the end (no atomics: the result does not depend on
+    // scheduling): per wave, its value rows' part of every row's terms; the C x C stage's
+    // row sums; gamma_C's terms per wave and lane half
+    float dgw[kWaves][kC], dbw[kWaves][kC];
+    float erow[kC], brow[kC];
+    float sxw[kWaves][2];
     float W[kWaves][kC * 32];   // per wave: W [t][value row]
     float dR[kWaves][kC * 32];  // dR [t][value row]
 };
@@ -885,7 +897,6 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
         const int t = tid & (kC - 1);
         (tid < kC ? S.alpha : S.beta)[t] =
             t < nt ? (tid < kC ? Ag : Bg)[(tok0 + t) * H + h] : (tid < kC ? 1.f : 0.f);
-        (tid < kC ? S.dg : S.db)[t] = 0.f;
     }
     {
     }
@@ -959,7 +970,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
         half_sum16(r);
         if (n == 31) {
 #pragma unroll
-            for (int jj = 0; jj < 16; ++jj) atomicAdd(&S.dg[acc_row(jj, g)], r[jj]);
+            for (int jj = 0; jj < 16; ++jj) S.dgw[w][acc_row(jj, g)] = r[jj];
         }
     }
     // ---- W = U - T diag(beta gamma) X; vx = V - gamma X
@@ -1051,12 +1062,12 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
         }
         half_sum16(rdb);
         half_sum16(rdg);
-        if (n == 31) {
+        if (n == 31) {  // (the lane that wrote these rows' gate terms above)
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj) {
                 const int t = acc_row(jj, g);
-                atomicAdd(&S.db[t], rdb[jj]);
-                atomicAdd(&S.dg[t], rdg[jj]);
+                S.dbw[w][t] = rdb[jj];
+                S.dgw[w][t] += rdg[jj];
             }
         }
     }
@@ -1133,7 +1144,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
         }
     }
     sx = half_sum(sx);
-    if (n == 31) atomicAdd(&S.dg[nt - 1], sx);
+    if (n == 31) S.sxw[w][g] = sx;
     wait_lds();
     barrier();
 
@@ -1163,15 +1174,15 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
             const float ek = btt * dbl * lgv, eq = i < t ? dmv * S.M[t * kC + i] : 0.f;
             brow += dbl * lgv;
             erow += ek + eq;
-            if (i < t) atomicAdd(&S.dg[i], -(ek + eq));
+            S.LG[t * kC + i] = i < t ? ek + eq : 0.f;  // (taken from gamma_i's term)
             S.P[0][t * kC + i] = btt * dbl * gt;  // dA (strict lower)
             S.dM[0][t * kC + i] = dmv * gt;       // dM o Gamma (lower with diagonal)
         }
         erow = sum8(erow);
         brow = sum8(brow);
         if (q == 0) {
-            atomicAdd(&S.dg[t], erow);
-            atomicAdd(&S.db[t], brow);
+            S.erow[t] = erow;
+            S.brow[t] = brow;
         }
     }
     wait_lds();
@@ -1211,7 +1222,19 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
     }
     // ---- d alpha (suffix sums of d log gamma) and d beta
     if (w == 0 && lane < kC) {
-        float v = lane < nt ? S.dg[lane] : 0.f;
+        const int t = lane;
+        float dg = S.erow[t], db = S.brow[t];
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+            dg += S.dgw[ww][t];
+            db += S.dbw[ww][t];
+        }
+        for (int t2 = t + 1; t2 < kC; ++t2) dg -= S.LG[t2 * kC + t];
+        if (t == nt - 1) {
+#pragma unroll
+            for (int ww = 0; ww < kWaves; ++ww) dg += S.sxw[ww][0] + S.sxw[ww][1];
+        }
+        float v = t < nt ? dg : 0.f;
 #pragma unroll
         for (int d = 1; d < kC; d <<= 1) {
             const float y = __shfl_down(v, d, 64);
@@ -1220,14 +1243,9 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
         if (lane < nt) {
             const size_t o = (tok0 + lane) * H + h;
             dAg[o] = v / S.alpha[lane];
-            dBg[o] = S.db[lane];
+            dBg[o] = db;
         }
     }
-}
-
-__global__ void fill_zero_kernel(float4* p, size_t n4) {
-    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n4) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 size_t gdn_prep_floats(int64_t n_chunks, int H) { return (size_t)n_chunks * H * kRec; }
@@ -1252,10 +1270,10 @@ hipError_t launch_gdn_chunk_fwd(const DevPlan& p, int l0, int n_br, int H, const
 
 hipError_t launch_gdn_chunk_dstate(const DevPlan& p, int l0, int n_br, int H, const void* q,
                                    const void* k, const void* dout, const float* prep,
-                                   float* dsc, float* dstates, hipStream_t s) {
+                                   float* dsc, float* dkids, hipStream_t s) {
     if (n_br <= 0) return hipSuccess;
     hipLaunchKernelGGL(gdn_chunk_dstate_kernel, dim3(n_br * H), dim3(kThr), 0, s, p, l0, H,
-                       (const bf16*)q, (const bf16*)k, (const bf16*)dout, prep, dsc, dstates);
+                       (const bf16*)q, (const bf16*)k, (const bf16*)dout, prep, dsc, dkids);
     return hipGetLastError();
 }
 
@@ -1269,14 +1287,6 @@ hipError_t launch_gdn_chunk_grad(const DevPlan& p, int64_t n_chunks, int H, cons
                        p, H, (const bf16*)q, (const bf16*)k, (const bf16*)v, alpha, beta,
                        (const bf16*)dout, prep, chunk_states, dsc, (bf16*)dq, (bf16*)dk,
                        (bf16*)dv, dalpha, dbeta);
-    return hipGetLastError();
-}
-
-hipError_t launch_fill_zero(float* p, size_t n_floats, hipStream_t s) {
-    const size_t n4 = n_floats / 4;
-    if (n4 == 0) return hipSuccess;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
-                       reinterpret_cast<float4*>(p), n4);
     return hipGetLastError();
 }
 
