@@ -6,6 +6,7 @@ gradients (both are what the packed oracle computes)."""
 import numpy as np
 import pytest
 
+import synth
 from oracle import attention as A
 from parity import (GRAD_TOL, TOL, check_close, check_grad, dev, fuzz_workload, host,
                     sample_rows, say, workload)
@@ -222,3 +223,33 @@ def test_fwd_bwd_on_a_side_stream():
     assert torch.equal(o1, o0) and torch.equal(l1, l0)
     for a, b in zip(g1, g0):
         assert torch.equal(a, b)
+
+
+def test_fwd_bwd_and_decode_are_deterministic():
+    """No step sums with atomics (one writer per dK/dV row, dQ per query tile, decode
+    splits merged in a fixed order), so repeated calls give the same bits."""
+    import torch
+    import tree_packed_block_amd as tpb
+    say("case determinism: fwd, bwd and decode twice")
+    dag, x = workload("episode_mid", with_dout=True)
+    plan = tpb.Plan(dag.branches, dag.mounts, dag.T).upload()
+    t = {k: dev(v, "bf16") for k, v in x.items()}
+    runs = []
+    for _ in range(2):
+        o, lse = tpb.attn_fwd(plan, t["q"], t["k"], t["v"])
+        g = tpb.attn_bwd(plan, t["q"], t["k"], t["v"], o, lse, t["do"])
+        torch.cuda.synchronize()
+        runs.append((o, lse) + tuple(g))
+    for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), *runs):
+        assert torch.equal(a, b), f"{name} differs between two identical calls"
+    wl = synth.decode_workload(seed=7, n_cursors=9, prefix=300, own_max=700, span_max=200)
+    xd = synth.draw_decode_inputs(np.random.default_rng(3), len(wl.cursors), 16, 4, 128,
+                                  wl.n_pages, wl.page_size)
+    segs = tpb.decode_segments(wl.dag.branches, wl.dag.mounts, wl.page_ptr, wl.pages,
+                               wl.page_size, wl.n_pages, wl.cursors, share=True)
+    sd = [torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda() for a in segs]
+    qkv = [dev(xd[n], "bf16") for n in ("q", "k_pool", "v_pool")]
+    d1 = tpb.paged_mount_decode(*qkv, *sd, n_split=5)
+    d2 = tpb.paged_mount_decode(*qkv, *sd, n_split=5)
+    torch.cuda.synchronize()
+    assert torch.equal(d1[0], d2[0]) and torch.equal(d1[1], d2[1]), "decode differs"
