@@ -376,7 +376,16 @@ def test_new_entry_points_reject_bad_arguments_before_any_launch():
     # recurrent scan
     assert _code(L.octopus_gated_delta_scan(p.handle, tpb.BF16, 2, 128, 128, fake, fake, fake,
                                             fake, fake, fake, fake, 1 << 30, None)) == "ESTATE"
+    assert _code(L.octopus_gated_delta_scan_save(p.handle, tpb.BF16, 2, 128, 128, fake, fake,
+                                                 fake, fake, fake, fake, fake, 1 << 30,
+                                                 None)) == "ESTATE"
+    assert _code(L.octopus_gated_delta_scan_bwd(p.handle, tpb.BF16, 2, 128, 128, *[fake] * 11,
+                                                fake, 1 << 30, None)) == "ESTATE"
+    assert _code(L.octopus_gated_delta_scan_bwd_saved(p.handle, tpb.BF16, 2, 128, 128,
+                                                      *[fake] * 11, fake, 1 << 30,
+                                                      None)) == "ESTATE"
     assert tpb.lib().octopus_gdn_workspace_bytes(p.handle, 2, 64, 128) == 0
+    assert tpb.lib().octopus_gdn_bwd_workspace_bytes(p.handle, 0, 128, 128) == 0
     # both children fork from the root at offset 256: one checkpoint slot; chunks end every
     # 32 own tokens and at every fork offset; one 8,448-float record per (chunk, head)
     br = np.asarray(dag.branches).reshape(-1, 4)

@@ -232,3 +232,38 @@ def test_scan_save_then_bwd_saved(name):
         for nm, g1, g2 in zip(("dq", "dk", "dv", "dalpha", "dbeta"), got, ref):
             assert torch.equal(g1, g2), f"{nm} differs from the plain backward (dO seed {seed})"
     say("  identical to the plain forward and backward")
+
+
+def test_scan_entry_points_reject_bad_arguments():
+    """Errors found on the host with an uploaded plan, before any launch: unsupported
+    head sizes and dtypes, NULL tensors, a workspace that is too small."""
+    import ctypes
+    import torch
+    import tree_packed_block_amd as tpb
+    say("case scan error paths")
+    dag, _ = synth.build("episode_small")
+    plan = tpb.Plan(dag.branches, dag.mounts, dag.T).upload()
+    L = tpb.lib()
+    H = 2
+    buf = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    p = ctypes.c_void_p(buf.data_ptr())
+    big = tpb.gdn_bwd_workspace_bytes(plan, H)
+
+    def code(rc):
+        return tpb._lib._NAMES.get(rc, rc)
+
+    for fn, n_in in ((L.octopus_gated_delta_scan, 6), (L.octopus_gated_delta_scan_save, 6)):
+        args = [p] * n_in
+        assert code(fn(plan.handle, tpb.BF16, H, 64, 128, *args, p, big, None)) == "EUNSUPPORTED"
+        assert code(fn(plan.handle, tpb.FP32, H, 128, 128, *args, p, big, None)) == "EUNSUPPORTED"
+        assert code(fn(plan.handle, tpb.BF16, H, 128, 128, None, *args[1:], p, big,
+                       None)) == "EINVAL"
+        assert code(fn(plan.handle, tpb.BF16, H, 128, 128, *args, p, 16, None)) == "EWORKSPACE"
+    for fn in (L.octopus_gated_delta_scan_bwd, L.octopus_gated_delta_scan_bwd_saved):
+        args = [p] * 11
+        assert code(fn(plan.handle, tpb.BF16, H, 128, 64, *args, p, big, None)) == "EUNSUPPORTED"
+        assert code(fn(plan.handle, tpb.BF16, 0, 128, 128, *args, p, big, None)) == "EINVAL"
+        assert code(fn(plan.handle, tpb.BF16, H, 128, 128, *args[:5], None, *args[6:], p, big,
+                       None)) == "EINVAL"
+        assert code(fn(plan.handle, tpb.BF16, H, 128, 128, *args, p, big - 1,
+                       None)) == "EWORKSPACE"
