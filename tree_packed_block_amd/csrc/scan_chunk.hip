@@ -47,6 +47,11 @@ namespace {
 
 constexpr int kD = 128;         // Dk = Dv
 constexpr int kC = 32;          // tokens per chunk
+// Row stride (floats) of the C x C matrices in LDS whose rows the lanes of a wave read in
+// parallel (lane n reads row n): 36 floats = 9 pieces of 16 bytes, so the rows of 16
+// consecutive lanes start in different banks (a stride of 32 floats puts them all on the
+// same ones).
+constexpr int kCP = kC + 4;
 constexpr int kWaves = kD / 32; // one wave per 32 value rows (or key columns)
 constexpr int kThr = 64 * kWaves;
 constexpr int kRowB = kD * 2;   // bytes of one bf16 row
@@ -313,8 +318,8 @@ struct PrepSmem {
     float alpha[kC], beta[kC];
     float lg[2][kC];    // log2 gamma (one copy per wave that needs it)
     float LG[kC * kC];  // gated K K^T, strict lower, [t][i]
-    float T[kC * kC];   // N^{-1}, [t][s]
-    float M[kC * kC];   // gated Q K^T, lower with diagonal, [t][i]
+    float T[kC * kCP];  // N^{-1}, [t][s]
+    float M[kC * kCP];  // gated Q K^T, lower with diagonal, [t][i]
 };
 
 }  // namespace
@@ -382,7 +387,7 @@ __global__ __launch_bounds__(kThr) void gdn_chunk_prep_kernel(
             for (int j = 0; j < 16; ++j) tv[j] = acc_row(j, g) == n ? 1.f : 0.f;
             fwd_solve(tv, S.LG, S.beta, g);
 #pragma unroll
-            for (int j = 0; j < 16; ++j) S.T[acc_row(j, g) * kC + n] = tv[j];
+            for (int j = 0; j < 16; ++j) S.T[acc_row(j, g) * kCP + n] = tv[j];
             st_split(rec + kRecTT, lane, tv);  // T^T rows n: T[acc_row(j, g)][n]
             // gamma_C / gamma_t as one difference of logarithms (1 past nt)
             const float lgC = __shfl(la, nt - 1, 64);
@@ -394,7 +399,7 @@ __global__ __launch_bounds__(kThr) void gdn_chunk_prep_kernel(
             }
         } else {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) S.M[acc_row(j, g) * kC + n] = v[j];
+            for (int j = 0; j < 16; ++j) S.M[acc_row(j, g) * kCP + n] = v[j];
             st_split(rec + kRecMT, lane, v);  // M^T rows n: M[acc_row(j, g)][n]
         }
     }
@@ -406,7 +411,7 @@ __global__ __launch_bounds__(kThr) void gdn_chunk_prep_kernel(
     int tr[4][2];
     tr_offsets(lane, tr);
     float trow[16], brow[16];
-    ld16f(S.T + n * kC + 4 * g, 8, trow);  // T[n][acc_row(j, g)]
+    ld16f(S.T + n * kCP + 4 * g, 8, trow);  // T[n][acc_row(j, g)]
     ld16f(S.beta + 4 * g, 8, brow);
     f32x16 u = zero16();
 #pragma unroll
@@ -427,7 +432,7 @@ __global__ __launch_bounds__(kThr) void gdn_chunk_prep_kernel(
     if (w == 2) st_split(rec + kRecT, lane, trow);
     if (w == 3) {
         float mrow[16];
-        ld16f(S.M + n * kC + 4 * g, 8, mrow);
+        ld16f(S.M + n * kCP + 4 * g, 8, mrow);
         st_split(rec + kRecM, lane, mrow);
     }
 }
@@ -832,11 +837,11 @@ struct GradSmem {
     float alpha[kC], beta[kC], gam[kC], lg[kC];
     float LG[kC * kC];   // gated K K^T, strict lower, [t][i]
     float M[kC * kC];    // gated Q K^T, lower with diagonal, [t][i]
-    float MT[kC * kC];   // its transpose
+    float MT[kC * kCP];  // its transpose
     // per wave: its value rows' part of sum_v dR_t . W_i (of sum_v dO_t . W_i); slot 0
     // then holds dA (dM o Gamma)
-    float P[kWaves][kC * kC];
-    float dM[kWaves][kC * kC];
+    float P[kWaves][kC * kCP];
+    float dM[kWaves][kC * kCP];
     // parts of d L / d (natural log gamma_t) and d L / d beta_t, each written by one lane
     // and added in a fixed order at the end (no atomics: the result does not depend on
     // scheduling): per wave, its value rows' part of every row's terms; the C x C stage's
@@ -844,8 +849,8 @@ struct GradSmem {
     float dgw[kWaves][kC], dbw[kWaves][kC];
     float erow[kC], brow[kC];
     float sxw[kWaves][2];
-    float W[kWaves][kC * 32];   // per wave: W [t][value row]
-    float dR[kWaves][kC * 32];  // dR [t][value row]
+    float W[kWaves][kC * kCP];   // per wave: W [t][value row]
+    float dR[kWaves][kC * kCP];  // dR [t][value row]
 };
 }  // namespace
 
@@ -928,7 +933,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
             const float mv = i <= t ? aqk[jj] * gt : 0.f;
             S.LG[t * kC + i] = i < t ? akk[jj] * gt : 0.f;
             S.M[t * kC + i] = mv;
-            S.MT[i * kC + t] = mv;
+            S.MT[i * kCP + t] = mv;
         }
     }
     f32x16 X = zero16(), Y = zero16(), X2 = zero16(), Y2 = zero16();
@@ -1003,7 +1008,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             bf16x8 mhi, mlo;
-            ld_split(S.MT + n * kC + 16 * kk + 4 * g, 8, mhi, mlo, 1.f);
+            ld_split(S.MT + n * kCP + 16 * kk + 4 * g, 8, mhi, mlo, 1.f);
             const bf16x8 bo = rd_tr(S.dO, tr, w, kk);
             tA = mfma_32x32x16(mhi, bo, tA);
             tA = mfma_32x32x16(mlo, bo, tA);
@@ -1045,8 +1050,8 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
         const int t = acc_row(jj, g);
-        Wl[t * 32 + n] = wv[jj];
-        dRl[t * 32 + n] = dr[jj];
+        Wl[t * kCP + n] = wv[jj];
+        dRl[t * kCP + n] = dr[jj];
         if (t < nt) dVg[((tok0 + t) * H + h) * kD + dv] = (bf16)(S.beta[t] * dr[jj]);
     }
     {
@@ -1079,8 +1084,8 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             bf16x8 ah, al, bh, bl;
-            ld_split(dRl + n * 32 + 16 * ks + 8 * g, 4, ah, al, 1.f);
-            ld_split(Wl + n * 32 + 16 * ks + 8 * g, 4, bh, bl, 1.f);
+            ld_split(dRl + n * kCP + 16 * ks + 8 * g, 4, ah, al, 1.f);
+            ld_split(Wl + n * kCP + 16 * ks + 8 * g, 4, bh, bl, 1.f);
             pp = mfma_32x32x16(ah, bh, pp);
             pp = mfma_32x32x16(ah, bl, pp);
             pp = mfma_32x32x16(al, bh, pp);
@@ -1091,8 +1096,8 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
             const int t = acc_row(jj, g);
-            S.P[w][t * kC + n] = pp[jj];
-            S.dM[w][t * kC + n] = pm[jj];
+            S.P[w][t * kCP + n] = pp[jj];
+            S.dM[w][t * kCP + n] = pm[jj];
         }
     }
     // ---- dQ = dY S_0 and dK = dX S_0 + diag(gamma_C / gamma) W dS_C for key columns
@@ -1125,8 +1130,8 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
                 sx += gC * s8[e] * d8[e];  // gamma_C <dS_C, S_0>: each element once
             }
             const int vw = ks >> 1, vl = 16 * (ks & 1) + 8 * g;
-            ld_split(S.dR[vw] + n * 32 + vl, 4, xh, xl, xsc);
-            ld_split(S.W[vw] + n * 32 + vl, 4, wh, wl, wsc);
+            ld_split(S.dR[vw] + n * kCP + vl, 4, xh, xl, xsc);
+            ld_split(S.W[vw] + n * kCP + vl, 4, wh, wl, wsc);
             {
                 const bf16x8 o8 = rd8(S.dO, n, 16 * ks + 8 * g);
 #pragma unroll
@@ -1153,12 +1158,12 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
         const int t = tid >> 3, q = tid & 7;
         const float lgt = S.lg[t], btt = S.beta[t];
         float erow = 0.f, brow = 0.f;
-        float4 ps = *reinterpret_cast<const float4*>(S.P[0] + t * kC + 4 * q);
-        float4 ms = *reinterpret_cast<const float4*>(S.dM[0] + t * kC + 4 * q);
+        float4 ps = *reinterpret_cast<const float4*>(S.P[0] + t * kCP + 4 * q);
+        float4 ms = *reinterpret_cast<const float4*>(S.dM[0] + t * kCP + 4 * q);
 #pragma unroll
         for (int ww = 1; ww < kWaves; ++ww) {
-            const float4 a = *reinterpret_cast<const float4*>(S.P[ww] + t * kC + 4 * q);
-            const float4 b = *reinterpret_cast<const float4*>(S.dM[ww] + t * kC + 4 * q);
+            const float4 a = *reinterpret_cast<const float4*>(S.P[ww] + t * kCP + 4 * q);
+            const float4 b = *reinterpret_cast<const float4*>(S.dM[ww] + t * kCP + 4 * q);
             ps.x += a.x; ps.y += a.y; ps.z += a.z; ps.w += a.w;
             ms.x += b.x; ms.y += b.y; ms.z += b.z; ms.w += b.w;
         }
@@ -1175,8 +1180,8 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
             brow += dbl * lgv;
             erow += ek + eq;
             S.LG[t * kC + i] = i < t ? ek + eq : 0.f;  // (taken from gamma_i's term)
-            S.P[0][t * kC + i] = btt * dbl * gt;  // dA (strict lower)
-            S.dM[0][t * kC + i] = dmv * gt;       // dM o Gamma (lower with diagonal)
+            S.P[0][t * kCP + i] = btt * dbl * gt;  // dA (strict lower)
+            S.dM[0][t * kCP + i] = dmv * gt;       // dM o Gamma (lower with diagonal)
         }
         erow = sum8(erow);
         brow = sum8(brow);
@@ -1196,12 +1201,12 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
             const bf16x8 bqv = rd_tr(S.Q, tr, w, kk);
             // rows i of this k-step in the accumulator order
             bf16x8 qh, ql, ah, al, th, tl;
-            ld_split(S.dM[0] + n * kC + 16 * kk + 4 * g, 8, qh, ql, 1.f);
+            ld_split(S.dM[0] + n * kCP + 16 * kk + 4 * g, 8, qh, ql, 1.f);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int i = 16 * kk + 8 * (e >> 2) + 4 * g + (e & 3);
-                split2(S.P[0][n * kC + i] + S.P[0][i * kC + n], ah, al, e);
-                split2(S.dM[0][i * kC + n], th, tl, e);
+                split2(S.P[0][n * kCP + i] + S.P[0][i * kCP + n], ah, al, e);
+                split2(S.dM[0][i * kCP + n], th, tl, e);
             }
             fq = mfma_32x32x16(qh, bkv, fq);
             fq = mfma_32x32x16(ql, bkv, fq);
