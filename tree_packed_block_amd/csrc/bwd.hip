@@ -225,14 +225,37 @@ __device__ __forceinline__ void dkdv_wave(const DevPlan& P, int Hq, int Hkv, int
     // iterations it >= n_it, which repeat the last entry and so contribute nothing).
     // The entries are walked from the last query tile down: the key blocks of one branch
     // then start on the same query tiles together and share them in L2.
+    // The iterations are issued in order; (je, jh, jc) are the next one's entry, head and
+    // half, stepped without divisions.  Its entry is loaded at the end of the iteration
+    // before (`fetch_entry`), where the wait ahead of the barrier covers it: a scalar load
+    // in flight turns every LDS wait into a full one (scalar loads complete out of order),
+    // so none is left outstanding in the middle of an iteration.  `masked` keeps, per
+    // stage, whether the iteration using it needs its mask (PARTIAL, unseen or padding).
+    int je = e1 - 1, jh = 0, jc = 0;
+    int4 jent = ld_const(P.blk_entries + je);
+    bool masked[3];
+    auto fetch_entry = [&]() {
+        asm volatile("" ::: "memory");
+        jent = ld_const(P.blk_entries + je);
+    };
     auto issue = [&](auto st_c, int it) {
         constexpr int ST = decltype(st_c)::value;
         const bool pad = it >= n_it;
-        const int e = max(e1 - 1 - it / (2 * G), e0);
-        const int hh = (it >> 1) % G, c = it & 1;
-        const int h = kvh * G + hh;
-        const int4 ent = ld_const(P.blk_entries + e);
-        const int row0 = ent.x * kBq + c * 64;
+        const int h = kvh * G + jh;
+        const int4 ent = jent;
+        // all four loaded registers stay live until here (otherwise the unused fourth one
+        // is reused while the load is in flight, which forces an early wait)
+        asm volatile("" ::"s"(ent.x), "s"(ent.y), "s"(ent.z), "s"(ent.w));
+        const int row0 = ent.x * kBq + jc * 64;
+        if (++jc == 2) {
+            jc = 0;
+            if (++jh == G) {
+                jh = 0;
+                je = max(je - 1, e0);
+            }
+        }
+        const int mraw = pr ? ent.z : ent.y;
+        masked[ST] = mraw != -1 || pad;
         issue_rows<D, 256>(smem_base, C::Q0 + ST * C::MAT, Q, row0, T, h, qstride, dm, tid, w);
         issue_rows<D, 256>(smem_base, C::D0 + ST * C::MAT, dO, row0, T, h, qstride, dm, tid, w);
         if (lane < 8)  // 32 pieces of 16 bytes, 8 per wave: LSE2 (waves 0, 1), Delta (2, 3)
@@ -277,9 +300,6 @@ __device__ __forceinline__ void dkdv_wave(const DevPlan& P, int Hq, int Hkv, int
         wait_lds();
         barrier();
         issue(ic<(ST + 2) % 3>{}, it + 2);
-        const int4 ent = ld_const(P.blk_entries + max(e1 - 1 - it / (2 * G), e0));
-        const int mk = pr ? ent.z : ent.y;
-        const bool masked = mk != -1 || it >= n_it;  // PARTIAL, unseen or padding
         const int c = it & 1;
         const int xcur = (it & 1) * C::XB, xprev = C::XB - xcur;
 
@@ -334,7 +354,7 @@ __device__ __forceinline__ void dkdv_wave(const DevPlan& P, int Hq, int Hkv, int
                     give[kk][j >> 3][j & 7] = (bf16)dsv;
                 }
             }
-        if (__builtin_expect(masked, 0)) {  // wave-uniform and rare: clear P and dS where
+        if (__builtin_expect(masked[ST], 0)) {  // wave-uniform and rare: clear P and dS where
             asm volatile("");                  // the mask is 0 (a real branch, not selects)
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
@@ -372,10 +392,13 @@ __device__ __forceinline__ void dkdv_wave(const DevPlan& P, int Hq, int Hkv, int
                 for (int kk = 0; kk < 2; ++kk)
                     acc[kk][db] = mfma_32x32x16(a, keep[kk][ql], acc[kk][db]);
             }
+        fetch_entry();
     };
 
     issue(ic<0>{}, 0);
+    fetch_entry();
     issue(ic<1>{}, 1);
+    fetch_entry();
     for (int it = 0; it < n_run; it += 3) {
         step(ic<0>{}, it);
         step(ic<1>{}, it + 1);

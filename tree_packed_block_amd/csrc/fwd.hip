@@ -122,9 +122,24 @@ __global__ __launch_bounds__(256 * HPW, 1) void fwd_bf16_kernel(
 
     const int p0 = ld_const(P.qt_ptr + qt), p1 = ld_const(P.qt_ptr + qt + 1);
     const int n_it = p1 - p0;
+    // The tile pair of the next iteration to issue (index jn) is loaded at the end of the
+    // iteration before (`fetch_pair`), where it is not waited for until the next LDS wait:
+    // a scalar load waited for right after the barrier would stall every iteration.
+    // `partial` keeps, per stage, whether its tile is PARTIAL.
+    int jn = 0;
+    int2 jpr = n_it > 0 ? ld_const(P.q_pairs + p0) : make_int2(0, -1);
+    bool partial[3];
+    auto fetch_pair = [&]() {
+        __builtin_amdgcn_sched_barrier(0);  // after everything else of the iteration
+        asm volatile("" ::: "memory");
+        jpr = ld_const(P.q_pairs + p0 + min(jn, n_it - 1));
+    };
     auto issue = [&](auto st_c, int it) {
         constexpr int ST = decltype(st_c)::value;
-        const int2 pr = ld_const(P.q_pairs + p0 + it);
+        const int2 pr = jpr;
+        asm volatile("" ::"s"(pr.x), "s"(pr.y));
+        partial[ST] = pr.y >= 0;
+        ++jn;
         issue_kv_stage<D, NTHR, ST, false>(smem_base, K, nullptr, P.mask_rows, pr.x,
                                            pr.y >= 0 ? pr.y : P.n_partial, T, kvh, kvstride, dm,
                                            tid, w, lane);
@@ -137,7 +152,6 @@ __global__ __launch_bounds__(256 * HPW, 1) void fwd_bf16_kernel(
         else wait_vmem<0>();
         barrier();
         if (it + 2 < n_it) issue(ic<(ST + 2) % 3>{}, it + 2);
-        const bool partial = ld_const(P.q_pairs + p0 + it).y >= 0;
 
         // S^T (64 keys x 32 queries) = K Q^T, two 32-key blocks.
         f32x16 s[2];
@@ -149,7 +163,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void fwd_bf16_kernel(
             s[1] = mfma_32x32x16(lds16(smem, off.k[ks], ST * L::MAT + 32 * L::ROWB), qf[ks], s[1]);
         }
         lead_reads<2 * KS>();
-        if (partial) {
+        if (partial[ST]) {
             const uint64_t bits =
                 *reinterpret_cast<const uint64_t*>(smem + off_mask + ST * L::MASKB);
             const uint32_t b0 = (uint32_t)(bits >> (4 * g)), b1 = (uint32_t)(bits >> (32 + 4 * g));
@@ -192,10 +206,17 @@ __global__ __launch_bounds__(256 * HPW, 1) void fwd_bf16_kernel(
                 o[db] = mfma_32x32x16(lds16(smem, ovx, ST * L::MAT + tile_t_imm<D>(kk, db)),
                                       pf[kk], o[db]);
         lead_reads<4 * DB>();
+        fetch_pair();
     };
 
-    if (n_it > 0) issue(ic<0>{}, 0);
-    if (n_it > 1) issue(ic<1>{}, 1);
+    if (n_it > 0) {
+        issue(ic<0>{}, 0);
+        fetch_pair();
+    }
+    if (n_it > 1) {
+        issue(ic<1>{}, 1);
+        fetch_pair();
+    }
     for (int it = 0; it < n_it; it += 3) {
         step(ic<0>{}, it);
         if (it + 1 < n_it) step(ic<1>{}, it + 1);
