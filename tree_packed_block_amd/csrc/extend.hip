@@ -125,12 +125,34 @@ __global__ __launch_bounds__(256 * HPW, 1) void extend_bf16_kernel(
     // slot range copies page 0 and is masked out entirely.  For a partial page, rows
     // outside [lo, hi) are filled from row lo, so every V row the MFMAs read is finite
     // (those rows get probability 0).
+    // The segment of the next iteration to issue (jn) is loaded at the end of the iteration
+    // before (`fetch_seg`), so that no scalar load is waited for right after the barrier;
+    // the fields the step needs are kept per stage.
+    int jn = 0;
+    int jpg = 0, jlo = 0, jhi = 0, jthr = 0, jcau = 0;
+    auto fetch_seg = [&]() {
+        __builtin_amdgcn_sched_barrier(0);  // after everything else of the iteration
+        asm volatile("" ::: "memory");
+        const int sg = s0 + min(jn, n_it - 1);
+        jpg = ld_const(seg_page + sg);
+        jlo = ld_const(seg_lo + sg);
+        jhi = ld_const(seg_hi + sg);
+        jthr = ld_const(seg_thr + sg);
+        jcau = ld_const(seg_causal + sg);
+    };
+    int st_lo[3], st_hi[3], st_thr[3];
+    bool st_ok[3], st_cau[3];
     auto issue = [&](auto st_c, int it) {
         constexpr int ST = decltype(st_c)::value;
-        const int sg = s0 + it;
-        const int pg = ld_const(seg_page + sg), lo = ld_const(seg_lo + sg),
-                  hi = ld_const(seg_hi + sg);
+        const int pg = jpg, lo = jlo, hi = jhi;
+        asm volatile("" ::"s"(jpg), "s"(jlo), "s"(jhi), "s"(jthr), "s"(jcau));
         const bool ok = pg >= 0 && pg < n_pages && lo >= 0 && lo < hi && hi <= kSlots;
+        st_lo[ST] = lo;
+        st_hi[ST] = hi;
+        st_thr[ST] = jthr;
+        st_cau[ST] = jcau != 0;
+        st_ok[ST] = ok;
+        ++jn;
         const size_t blk = ((size_t)(ok ? pg : 0) * Hkv + kvh) * kSlots * D;
         const bf16* kb = Kp + blk;
         const bf16* vb = Vp + blk;
@@ -161,11 +183,8 @@ __global__ __launch_bounds__(256 * HPW, 1) void extend_bf16_kernel(
         else wait_vmem<0>();
         barrier();
         if (it + 2 < n_it) issue(ic<(ST + 2) % 3>{}, it + 2);
-        const int sg = s0 + it;
-        const int pg = ld_const(seg_page + sg), lo = ld_const(seg_lo + sg),
-                  hi = ld_const(seg_hi + sg), thr = ld_const(seg_thr + sg),
-                  causal = ld_const(seg_causal + sg);
-        const bool ok = pg >= 0 && pg < n_pages && lo >= 0 && lo < hi && hi <= kSlots;
+        const int lo = st_lo[ST], hi = st_hi[ST], thr = st_thr[ST];
+        const bool ok = st_ok[ST], causal = st_cau[ST];
 
         f32x16 s[2];
         s[0] = zero16();
@@ -230,10 +249,18 @@ __global__ __launch_bounds__(256 * HPW, 1) void extend_bf16_kernel(
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+        fetch_seg();
     };
 
-    if (n_it > 0) issue(ic<0>{}, 0);
-    if (n_it > 1) issue(ic<1>{}, 1);
+    if (n_it > 0) {
+        fetch_seg();
+        issue(ic<0>{}, 0);
+        fetch_seg();
+    }
+    if (n_it > 1) {
+        issue(ic<1>{}, 1);
+        fetch_seg();
+    }
     for (int it = 0; it < n_it; it += 3) {
         step(ic<0>{}, it);
         if (it + 1 < n_it) step(ic<1>{}, it + 1);
