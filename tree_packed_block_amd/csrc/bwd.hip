@@ -517,9 +517,22 @@ __global__ __launch_bounds__(256 * HPW, 1) void dq_bf16_kernel(
 
     const int p0 = ld_const(P.qt_ptr + qt), p1 = ld_const(P.qt_ptr + qt + 1);
     const int n_it = p1 - p0;
+    // The tile pair of the next iteration to issue (index jn) is loaded at the end of the
+    // iteration before (`fetch_pair`), so that no scalar load is waited for right after the
+    // barrier.  `partial` keeps, per stage, whether its tile is PARTIAL.
+    int jn = 0;
+    int2 jpr = n_it > 0 ? ld_const(P.q_pairs + p0) : make_int2(0, -1);
+    bool partial[3];
+    auto fetch_pair = [&]() {
+        asm volatile("" ::: "memory");
+        jpr = ld_const(P.q_pairs + p0 + min(jn, n_it - 1));
+    };
     auto issue = [&](auto st_c, int it) {
         constexpr int ST = decltype(st_c)::value;
-        const int2 pr = ld_const(P.q_pairs + p0 + it);
+        const int2 pr = jpr;
+        asm volatile("" ::"s"(pr.x), "s"(pr.y));
+        partial[ST] = pr.y >= 0;
+        ++jn;
         issue_kv_stage<D, NTHR, ST>(smem_base, K, V, P.mask_rows, pr.x,
                                     pr.y >= 0 ? pr.y : P.n_partial, T, kvh, kvstride, dm, tid,
                                     w, lane);
@@ -530,7 +543,6 @@ __global__ __launch_bounds__(256 * HPW, 1) void dq_bf16_kernel(
         else wait_vmem<0>();
         barrier();
         if (it + 2 < n_it) issue(ic<(ST + 2) % 3>{}, it + 2);
-        const bool partial = ld_const(P.q_pairs + p0 + it).y >= 0;
 
         // One 32-key block at a time: S and dP, dS, then its two k-steps of
         // dQ^T += K^T dS^T, whose MFMAs overlap the next block's softmax.
@@ -548,7 +560,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void dq_bf16_kernel(
 #pragma unroll
             for (int j = 0; j < 16; ++j)
                 sb[j >> 3][j & 7] = (bf16)(fast_exp2(sc[j]) * dp[j]);
-            if (__builtin_expect(partial, 0)) {  // wave-uniform and rare: clear dS where
+            if (__builtin_expect(partial[ST], 0)) {  // wave-uniform and rare: clear dS where
                 asm volatile("");                   // the mask is 0 (a real branch)
                 // The row's mask word, addressed from the lane id afresh (the opaque
                 // copy keeps the address from being hoisted and held across the loop).
@@ -571,10 +583,17 @@ __global__ __launch_bounds__(256 * HPW, 1) void dq_bf16_kernel(
                     dq[db] = mfma_32x32x16(a, sb[k2], dq[db]);
                 }
         }
+        fetch_pair();
     };
 
-    if (n_it > 0) issue(ic<0>{}, 0);
-    if (n_it > 1) issue(ic<1>{}, 1);
+    if (n_it > 0) {
+        issue(ic<0>{}, 0);
+        fetch_pair();
+    }
+    if (n_it > 1) {
+        issue(ic<1>{}, 1);
+        fetch_pair();
+    }
     for (int it = 0; it < n_it; it += 3) {
         step(ic<0>{}, it);
         if (it + 1 < n_it) step(ic<1>{}, it + 1);
