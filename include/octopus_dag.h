@@ -283,9 +283,14 @@ size_t octopus_gdn_workspace_bytes(const octopus_plan* plan, int32_t H, int32_t 
  * q, k [T][H][Dk], v, o [T][H][Dv] (dtype); alpha, beta float32 [T][H] (device).
  * alpha in (0, 1] (values below 2^-100 act as 2^-100), beta in [0, 1].
  * The plan must be uploaded.  Every branch is taken 32 tokens at a time on the matrix
- * cores (chunks also end at every fork offset): one launch prepares every (chunk, head)
- * in parallel, then the levels of the tree run one launch each, in order, one workgroup
- * per (branch, head).
+ * cores (chunks also end at every fork offset): the chunks' records are prepared in
+ * parallel, then the levels of the tree run one launch each, in order, one workgroup per
+ * (branch, head).  The deeper levels' records are prepared on a second stream of the
+ * current device while the first level runs (the scan entry points create that stream and
+ * two events per device on first use and keep them until the process ends); the second
+ * stream starts after the work already on `stream` and `stream` waits for it before the
+ * next level, so the call is ordered on `stream` like a plain launch sequence.  Calls from
+ * several host threads are serialised around the second stream.
  * Supported: bf16, Dk = Dv = 128.  Errors: EINVAL, ESTATE, EUNSUPPORTED, EWORKSPACE,
  * EHIP. */
 int octopus_gated_delta_scan(const octopus_plan* plan, octopus_dtype dtype, int32_t H,
@@ -307,7 +312,8 @@ size_t octopus_gdn_bwd_workspace_bytes(const octopus_plan* plan, int32_t H, int3
  * parent's earlier tokens; mounted spans receive nothing (the recurrent layers skip them;
  * project page, primitives table).  Recomputes the forward (the states at chunk starts go
  * to the workspace), walks every branch's chunks in reverse carrying only the state
- * gradient (deepest branches first), then computes every chunk's gradients in parallel.
+ * gradient (deepest branches first), then computes every chunk's gradients in parallel
+ * (the deeper levels' on the second stream while the first level's state gradient runs).
  * Deterministic: the children forking at one offset hand their initial-state gradients
  * to the parent in ascending branch order (no atomics), so repeated calls give the same
  * bits.  Same support and errors as octopus_gated_delta_scan. */

@@ -7,7 +7,9 @@
 #include <cstdint>
 #include <cstring>
 #include <initializer_list>
+#include <map>
 #include <memory>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -513,6 +515,116 @@ size_t gdn_state_bytes(int32_t H) { return (size_t)H * 128 * 128 * sizeof(float)
 size_t gdn_prep_bytes(const octopus_plan* plan, int32_t H) {
     return octo::gdn_prep_floats(plan->p.n_chunks, H) * sizeof(float);
 }
+
+// A second stream of the current device (default priority) with two events, created on
+// first use and kept for the life of the process.  The scan runs independent launches on
+// it next to the caller's stream: a fork event recorded on the caller's stream, work on
+// the side stream, a join event the caller's stream waits for.  g_side_mu is held from the
+// fork to the join so that concurrent calls do not re-record the events in between.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+std::map<int, SideStream> g_side;
+hipError_t side_stream(SideStream& out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    auto it = g_side.find(dev);
+    if (it == g_side.end()) {
+        SideStream sd;
+        e = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&sd.join, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            if (sd.join) (void)hipEventDestroy(sd.join);
+            if (sd.fork) (void)hipEventDestroy(sd.fork);
+            if (sd.s) (void)hipStreamDestroy(sd.s);
+            return e;
+        }
+        it = g_side.emplace(dev, sd).first;
+    }
+    out = it->second;
+    return hipSuccess;
+}
+// Forks work off `st` onto the side stream and joins it back: fork() records the fork
+// event and makes the side stream wait for it; join() (also run by the destructor, so
+// every return path joins) records the join event and makes `st` wait for it.
+class SideFork {
+  public:
+    explicit SideFork(hipStream_t st) : st_(st) {}
+    hipError_t fork(hipStream_t& side) {
+        lock_ = std::unique_lock<std::mutex>(g_side_mu);
+        hipError_t e = side_stream(sd_);
+        if (e == hipSuccess) e = hipEventRecord(sd_.fork, st_);
+        if (e == hipSuccess) e = hipStreamWaitEvent(sd_.s, sd_.fork, 0);
+        if (e != hipSuccess) {
+            lock_.unlock();
+            return e;
+        }
+        forked_ = true;
+        side = sd_.s;
+        return hipSuccess;
+    }
+    hipError_t join() {
+        if (!forked_) return hipSuccess;
+        forked_ = false;
+        hipError_t e = hipEventRecord(sd_.join, sd_.s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(st_, sd_.join, 0);
+        if (e != hipSuccess) (void)hipStreamSynchronize(sd_.s);  // cannot order st after it
+        lock_.unlock();
+        return e;
+    }
+    ~SideFork() { (void)join(); }
+
+  private:
+    hipStream_t st_;
+    SideStream sd_;
+    bool forked_ = false;
+    std::unique_lock<std::mutex> lock_;
+};
+
+// The scan forward: the records of every chunk, then the branches level by level.  The
+// first level's branches need only their own chunks' records, and one workgroup per
+// (branch, head) leaves most compute units idle, so the deeper levels' records are
+// prepared on the side stream while the first level runs.  chunk_states may be NULL.
+int gdn_forward_run(const octopus_plan* plan, int32_t H, const void* q, const void* k,
+                    const void* v, const float* alpha, const float* beta, void* o, float* slots,
+                    float* chunk_states, float* prep, hipStream_t st) {
+    const octo::DevPlan dp = dev_view(plan->p);
+    const std::vector<int32_t>& lp = plan->p.level_ptr;
+    const std::vector<int32_t>& lc = plan->p.level_chunk;
+    const int32_t first = lc[1];
+    const int64_t rest = plan->p.n_chunks - first;
+    // Order of the launches: the first level's records, then the fork, the first level's
+    // forward, and only then the side stream's records.  The forward's workgroups each need
+    // a whole compute unit, so they must be dispatched before the side stream's many small
+    // workgroups fill every unit (they become ready together when the first records land).
+    hipError_t e = octo::launch_gdn_chunk_prep(dp, 0, first, H, q, k, v, alpha, beta, prep, st);
+    if (e != hipSuccess) return hip_fail(e, "scan prep launch");
+    SideFork side(st);
+    hipStream_t s2 = nullptr;
+    if (rest > 0) {
+        e = side.fork(s2);
+        if (e != hipSuccess) return hip_fail(e, "scan side stream");
+    }
+    e = octo::launch_gdn_chunk_fwd(dp, lp[0], lp[1] - lp[0], H, q, k, prep, o, slots,
+                                   chunk_states, st);
+    if (e != hipSuccess) return hip_fail(e, "scan forward launch");
+    if (rest > 0) {
+        e = octo::launch_gdn_chunk_prep(dp, first, rest, H, q, k, v, alpha, beta, prep, s2);
+        if (e != hipSuccess) return hip_fail(e, "scan prep launch");
+    }
+    e = side.join();
+    if (e != hipSuccess) return hip_fail(e, "scan side stream");
+    for (size_t l = 1; l + 1 < lp.size(); ++l) {
+        e = octo::launch_gdn_chunk_fwd(dp, lp[l], lp[l + 1] - lp[l], H, q, k, prep, o, slots,
+                                       chunk_states, st);
+        if (e != hipSuccess) return hip_fail(e, "scan forward launch");
+    }
+    return OCTOPUS_OK;
+}
 // Arguments shared by the scan's forward and backward.
 int check_gdn(const octopus_plan* plan, octopus_dtype dtype, int32_t H, int32_t Dk, int32_t Dv,
               std::initializer_list<const void*> tensors) {
@@ -548,22 +660,13 @@ int octopus_gated_delta_scan(const octopus_plan* plan, octopus_dtype dtype, int3
     if (ws == nullptr || ws_bytes < need || !aligned(ws, 16))
         return fail(OCTOPUS_EWORKSPACE, "scan workspace needs " + std::to_string(need) +
                                             " bytes, 16-byte aligned");
-    const octo::DevPlan dp = dev_view(plan->p);
-    const std::vector<int32_t>& lp = plan->p.level_ptr;
-    hipStream_t st = (hipStream_t)stream;
     float* slots = static_cast<float*>(ws);
     float* prep = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                            (size_t)std::max(plan->p.n_slots, 1) *
                                                gdn_state_bytes(H));
-    hipError_t e = octo::launch_gdn_chunk_prep(dp, plan->p.n_chunks, H, q, k, v, alpha, beta,
-                                               prep, st);
-    if (e != hipSuccess) return hip_fail(e, "scan prep launch");
-    for (size_t l = 0; l + 1 < lp.size(); ++l) {
-        e = octo::launch_gdn_chunk_fwd(dp, lp[l], lp[l + 1] - lp[l], H, q, k, prep, o, slots,
-                                       nullptr, st);
-        if (e != hipSuccess) return hip_fail(e, "scan launch");
-    }
-    return ok();
+    const int r = gdn_forward_run(plan, H, q, k, v, alpha, beta, o, slots, nullptr, prep,
+                                  (hipStream_t)stream);
+    return r == OCTOPUS_OK ? ok() : r;
 }
 
 size_t octopus_gdn_bwd_workspace_bytes(const octopus_plan* plan, int32_t H, int32_t Dk,
@@ -607,18 +710,8 @@ int check_gdn_bwd_ws(const octopus_plan* plan, int32_t H, int32_t Dk, int32_t Dv
 int gdn_forward_keep(const octopus_plan* plan, int32_t H, const void* q, const void* k,
                      const void* v, const float* alpha, const float* beta, void* o, void* ws,
                      hipStream_t st) {
-    const octo::DevPlan dp = dev_view(plan->p);
-    const std::vector<int32_t>& lp = plan->p.level_ptr;
     const GdnBwdWs w = gdn_bwd_ws(plan, H, ws);
-    hipError_t e = octo::launch_gdn_chunk_prep(dp, plan->p.n_chunks, H, q, k, v, alpha, beta,
-                                               w.prep, st);
-    if (e != hipSuccess) return hip_fail(e, "scan prep launch");
-    for (size_t l = 0; l + 1 < lp.size(); ++l) {
-        e = octo::launch_gdn_chunk_fwd(dp, lp[l], lp[l + 1] - lp[l], H, q, k, w.prep, o, w.slots,
-                                       w.chunks, st);
-        if (e != hipSuccess) return hip_fail(e, "scan forward launch");
-    }
-    return OCTOPUS_OK;
+    return gdn_forward_run(plan, H, q, k, v, alpha, beta, o, w.slots, w.chunks, w.prep, st);
 }
 // The backward proper, from what gdn_forward_keep left in the workspace.
 int gdn_backward_kept(const octopus_plan* plan, int32_t H, const void* q, const void* k,
@@ -627,18 +720,41 @@ int gdn_backward_kept(const octopus_plan* plan, int32_t H, const void* q, const 
                       hipStream_t st) {
     const octo::DevPlan dp = dev_view(plan->p);
     const std::vector<int32_t>& lp = plan->p.level_ptr;
+    const std::vector<int32_t>& lc = plan->p.level_chunk;
     const GdnBwdWs w = gdn_bwd_ws(plan, H, ws);
     hipError_t e = hipSuccess;
     // state gradients, deepest level first: a child's initial-state gradient is written
     // before its parent runs
-    for (size_t l = lp.size() - 1; l-- > 0;) {
+    for (size_t l = lp.size() - 1; l-- > 1;) {
         e = octo::launch_gdn_chunk_dstate(dp, lp[l], lp[l + 1] - lp[l], H, q, k, dout, w.prep,
                                           w.dsc, w.dkids, st);
         if (e != hipSuccess) return hip_fail(e, "scan backward (state gradient) launch");
     }
-    e = octo::launch_gdn_chunk_grad(dp, plan->p.n_chunks, H, q, k, v, alpha, beta, dout, w.prep,
+    // The deeper levels' chunks have their state gradients now: their gradients run on the
+    // side stream while the first level's state gradient (few workgroups) runs here.
+    const int32_t first = lc[1];
+    const int64_t rest = plan->p.n_chunks - first;
+    // (the first level's state gradient is enqueued first, so that its workgroups, which
+    // each need a whole compute unit, are dispatched before the side stream's)
+    SideFork side(st);
+    hipStream_t s2 = nullptr;
+    if (rest > 0) {
+        e = side.fork(s2);
+        if (e != hipSuccess) return hip_fail(e, "scan side stream");
+    }
+    e = octo::launch_gdn_chunk_dstate(dp, lp[0], lp[1] - lp[0], H, q, k, dout, w.prep, w.dsc,
+                                      w.dkids, st);
+    if (e != hipSuccess) return hip_fail(e, "scan backward (state gradient) launch");
+    if (rest > 0) {
+        e = octo::launch_gdn_chunk_grad(dp, first, rest, H, q, k, v, alpha, beta, dout, w.prep,
+                                        w.chunks, w.dsc, dq, dk, dv, dalpha, dbeta, s2);
+        if (e != hipSuccess) return hip_fail(e, "scan backward launch");
+    }
+    e = octo::launch_gdn_chunk_grad(dp, 0, first, H, q, k, v, alpha, beta, dout, w.prep,
                                     w.chunks, w.dsc, dq, dk, dv, dalpha, dbeta, st);
     if (e != hipSuccess) return hip_fail(e, "scan backward launch");
+    e = side.join();
+    if (e != hipSuccess) return hip_fail(e, "scan side stream");
     return OCTOPUS_OK;
 }
 }  // namespace

@@ -112,15 +112,15 @@ hipError_t launch_rope2(bool bf16, int rows, int D, float base, bool inverse,
 
 // Chunked gated delta-rule scan (matrix cores, 32-token chunks as listed by the plan):
 // q, k, v, dout [T][H][128] bf16, alpha, beta float32 [T][H].  The prep kernel writes a
-// record of gdn_prep_floats / (n_chunks H) floats per (chunk, head) into `prep`
-// (one launch over every chunk); the forward walks the branches level_br[l0 .. l0 + n_br)
+// record of gdn_prep_floats / (n_chunks H) floats per (chunk, head) into `prep` for the
+// n_chunks chunks from chunk c0 on; the forward walks the branches level_br[l0 .. l0 + n_br)
 // (one workgroup per (branch, head)) from their checkpoint slots `states`
 // [n_slots][H][128][128] float32 (row = value index), writing o [T][H][128] bf16 (may be
 // NULL) and, with chunk_states (may be NULL), the state at the start of every chunk
 // [c][H][128][128].
 size_t gdn_prep_floats(int64_t n_chunks, int H);
-hipError_t launch_gdn_chunk_prep(const DevPlan& p, int64_t n_chunks, int H, const void* q,
-                                 const void* k, const void* v, const float* alpha,
+hipError_t launch_gdn_chunk_prep(const DevPlan& p, int c0, int64_t n_chunks, int H,
+                                 const void* q, const void* k, const void* v, const float* alpha,
                                  const float* beta, float* prep, hipStream_t s);
 hipError_t launch_gdn_chunk_fwd(const DevPlan& p, int l0, int n_br, int H, const void* q,
                                 const void* k, const float* prep, void* o, float* states,
@@ -128,13 +128,14 @@ hipError_t launch_gdn_chunk_fwd(const DevPlan& p, int l0, int n_br, int H, const
 // Backward: the state gradient of the branches level_br[l0 .. l0 + n_br) in reverse
 // (levels deepest first), written at every chunk's end into dsc [c][H][128][128]
 // (key-major); dkids [nb][H][128][128] float32: every child's initial-state gradient,
-// written by the child and added by its parent.  Then, over every chunk, dq, dk, dv
-// [T][H][128] bf16 and dalpha, dbeta [T][H] float32.
+// written by the child and added by its parent.  Then, over the n_chunks chunks from c0 on,
+// the gradients dq, dk, dv [T][H][128] bf16 and dalpha, dbeta [T][H] float32 of their
+// tokens.
 hipError_t launch_gdn_chunk_dstate(const DevPlan& p, int l0, int n_br, int H, const void* q,
                                    const void* k, const void* dout, const float* prep,
                                    float* dsc, float* dkids, hipStream_t s);
-hipError_t launch_gdn_chunk_grad(const DevPlan& p, int64_t n_chunks, int H, const void* q,
-                                 const void* k, const void* v, const float* alpha,
+hipError_t launch_gdn_chunk_grad(const DevPlan& p, int c0, int64_t n_chunks, int H,
+                                 const void* q, const void* k, const void* v, const float* alpha,
                                  const float* beta, const void* dout, const float* prep,
                                  const float* chunk_states, const float* dsc, void* dq, void* dk,
                                  void* dv, float* dalpha, float* dbeta, hipStream_t s);

@@ -566,27 +566,7 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
             for (int32_t b = 0; b < nb; ++b)  // ascending b: each list comes out sorted
                 if (p.sc_init[b] >= 0) p.sc_ck_kid[fill[ck_of_slot[p.sc_init[b]]]++] = b;
         }
-        // Chunks of the chunked scan: boundaries every kScanChunk own tokens and at every
-        // checkpoint offset inside the branch (the kernel walks the same rule).
-        p.sc_chunk_base.assign(nb + 1, 0);
-        p.sc_chunk_tok.clear();
-        p.sc_chunk_nt.clear();
-        for (int32_t b = 0; b < nb; ++b) {
-            const int32_t len = d.br[b].len;
-            int32_t c = p.sc_ck_ptr[b];
-            int32_t r = 0;
-            while (c < p.sc_ck_ptr[b + 1] && p.sc_ck_off[c] <= r) ++c;
-            while (r < len) {
-                int32_t e = std::min(len, (r / kScanChunk + 1) * kScanChunk);
-                if (c < p.sc_ck_ptr[b + 1]) e = std::min(e, p.sc_ck_off[c]);
-                p.sc_chunk_tok.push_back(d.br[b].start + r);
-                p.sc_chunk_nt.push_back(e - r);
-                r = e;
-                while (c < p.sc_ck_ptr[b + 1] && p.sc_ck_off[c] <= r) ++c;
-            }
-            p.sc_chunk_base[b + 1] = (int32_t)p.sc_chunk_tok.size();
-        }
-        p.n_chunks = p.sc_chunk_base[nb];
+        // Branches by depth (a branch's parent has a smaller index, so one pass suffices).
         std::vector<int32_t> depth(nb, 0);
         int32_t max_depth = 0;
         for (int32_t b = 0; b < nb; ++b) {
@@ -599,6 +579,34 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
         p.level_br.assign(nb, 0);
         std::vector<int32_t> fill(p.level_ptr.begin(), p.level_ptr.end() - 1);
         for (int32_t b = 0; b < nb; ++b) p.level_br[fill[depth[b]]++] = b;
+        // Chunks of the chunked scan: boundaries every kScanChunk own tokens and at every
+        // checkpoint offset inside the branch (the kernel walks the same rule), numbered
+        // level by level so that every level's chunks form one range.
+        p.sc_chunk_base.assign(2 * (size_t)nb, 0);
+        p.sc_chunk_tok.clear();
+        p.sc_chunk_nt.clear();
+        p.level_chunk.assign(1, 0);
+        for (int32_t l = 0; l <= max_depth; ++l) {
+            for (int32_t i = p.level_ptr[l]; i < p.level_ptr[l + 1]; ++i) {
+                const int32_t b = p.level_br[i];
+                const int32_t len = d.br[b].len;
+                p.sc_chunk_base[2 * b] = (int32_t)p.sc_chunk_tok.size();
+                int32_t c = p.sc_ck_ptr[b];
+                int32_t r = 0;
+                while (c < p.sc_ck_ptr[b + 1] && p.sc_ck_off[c] <= r) ++c;
+                while (r < len) {
+                    int32_t e = std::min(len, (r / kScanChunk + 1) * kScanChunk);
+                    if (c < p.sc_ck_ptr[b + 1]) e = std::min(e, p.sc_ck_off[c]);
+                    p.sc_chunk_tok.push_back(d.br[b].start + r);
+                    p.sc_chunk_nt.push_back(e - r);
+                    r = e;
+                    while (c < p.sc_ck_ptr[b + 1] && p.sc_ck_off[c] <= r) ++c;
+                }
+                p.sc_chunk_base[2 * b + 1] = (int32_t)p.sc_chunk_tok.size();
+            }
+            p.level_chunk.push_back((int32_t)p.sc_chunk_tok.size());
+        }
+        p.n_chunks = (int64_t)p.sc_chunk_tok.size();
     }
 
     // Device image: every array 256-byte aligned.
@@ -630,7 +638,7 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     L.sc_ck_kid_ptr = place(p.sc_ck_kid_ptr.size() * 4);
     L.sc_ck_kid = place(std::max<size_t>(p.sc_ck_kid.size(), 1) * 4);
     L.sc_level_br = place((size_t)nb * 4);
-    L.sc_chunk_base = place((size_t)(nb + 1) * 4);
+    L.sc_chunk_base = place(std::max<size_t>(p.sc_chunk_base.size(), 1) * 4);
     L.sc_chunk_tok = place(std::max<size_t>(p.sc_chunk_tok.size(), 1) * 4);
     L.sc_chunk_nt = place(std::max<size_t>(p.sc_chunk_nt.size(), 1) * 4);
     L.total = std::max<size_t>(at, 256);

@@ -94,9 +94,11 @@ struct Plan {
     std::vector<int32_t> sc_ck_kid_ptr, sc_ck_kid;
     int32_t n_slots = 0;
     // Chunked scan: branch b's chunks (own tokens split every kScanChunk tokens and at
-    // every checkpoint offset) are numbered sc_chunk_base[b] .. sc_chunk_base[b+1]-1;
+    // every checkpoint offset) are numbered sc_chunk_base[2b] .. sc_chunk_base[2b+1]-1;
     // chunk c covers packed tokens sc_chunk_tok[c] .. sc_chunk_tok[c] + sc_chunk_nt[c] - 1.
-    std::vector<int32_t> sc_chunk_base, sc_chunk_tok, sc_chunk_nt;
+    // Chunks are numbered level by level (in level_br order), so the chunks of level l are
+    // level_chunk[l] .. level_chunk[l+1]-1 (host only: launch ranges).
+    std::vector<int32_t> sc_chunk_base, sc_chunk_tok, sc_chunk_nt, level_chunk;
     int64_t n_chunks = 0;
     DevLayout layout;
     std::vector<unsigned char> blob;  // host image of the device copy

@@ -327,11 +327,11 @@ struct PrepSmem {
 // ---------------------------------------------------------------- prep (parallel)
 
 __global__ __launch_bounds__(kThr) void gdn_chunk_prep_kernel(
-    DevPlan P, int H, const bf16* __restrict__ Qg, const bf16* __restrict__ Kg,
+    DevPlan P, int c0, int H, const bf16* __restrict__ Qg, const bf16* __restrict__ Kg,
     const bf16* __restrict__ Vg, const float* __restrict__ Ag, const float* __restrict__ Bg,
     float* __restrict__ prep) {
     __shared__ __attribute__((aligned(1024))) PrepSmem S;
-    const int c = blockIdx.x / H, h = blockIdx.x % H;
+    const int c = c0 + (int)(blockIdx.x / H), h = blockIdx.x % H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, g = lane >> 5;
@@ -466,8 +466,8 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
     const int dv = 32 * w + n;  // this lane's value row (accumulator column)
     const int start = ld_const(P.sc_start + b);
     const int init = ld_const(P.sc_init + b);
-    const int cbase = ld_const(P.sc_chunk_base + b);
-    const int nch = ld_const(P.sc_chunk_base + b + 1) - cbase;
+    const int cbase = ld_const(P.sc_chunk_base + 2 * b);
+    const int nch = ld_const(P.sc_chunk_base + 2 * b + 1) - cbase;
     const size_t rs = (size_t)H * kD;  // elements per token row of q, k, o
 
     // S^T tiles: St[bk][j] = S[dv][32 bk + acc_row(j, g)].
@@ -673,8 +673,8 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_dstate_kernel(
     const int dv = 32 * w + n;
     const int start = ld_const(P.sc_start + b), len = ld_const(P.sc_len + b);
     const int init = ld_const(P.sc_init + b);
-    const int cbase = ld_const(P.sc_chunk_base + b);
-    const int nch = ld_const(P.sc_chunk_base + b + 1) - cbase;
+    const int cbase = ld_const(P.sc_chunk_base + 2 * b);
+    const int nch = ld_const(P.sc_chunk_base + 2 * b + 1) - cbase;
     const int ck_lo = ld_const(P.sc_ck_ptr + b);
     int ckr = ld_const(P.sc_ck_ptr + b + 1) - 1;
 
@@ -855,14 +855,14 @@ struct GradSmem {
 }  // namespace
 
 __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
-    DevPlan P, int H, const bf16* __restrict__ Qg, const bf16* __restrict__ Kg,
+    DevPlan P, int c0, int H, const bf16* __restrict__ Qg, const bf16* __restrict__ Kg,
     const bf16* __restrict__ Vg, const float* __restrict__ Ag, const float* __restrict__ Bg,
     const bf16* __restrict__ dOg, const float* __restrict__ prep,
     const float* __restrict__ chunk_states, const float* __restrict__ dsc,
     bf16* __restrict__ dQg, bf16* __restrict__ dKg, bf16* __restrict__ dVg,
     float* __restrict__ dAg, float* __restrict__ dBg) {
     __shared__ __attribute__((aligned(1024))) GradSmem S;
-    const int c = blockIdx.x / H, h = blockIdx.x % H;
+    const int c = c0 + (int)(blockIdx.x / H), h = blockIdx.x % H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, g = lane >> 5;
@@ -1255,12 +1255,13 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
 
 size_t gdn_prep_floats(int64_t n_chunks, int H) { return (size_t)n_chunks * H * kRec; }
 
-hipError_t launch_gdn_chunk_prep(const DevPlan& p, int64_t n_chunks, int H, const void* q,
-                                 const void* k, const void* v, const float* alpha,
+hipError_t launch_gdn_chunk_prep(const DevPlan& p, int c0, int64_t n_chunks, int H,
+                                 const void* q, const void* k, const void* v, const float* alpha,
                                  const float* beta, float* prep, hipStream_t s) {
     if (n_chunks <= 0) return hipSuccess;
     hipLaunchKernelGGL(gdn_chunk_prep_kernel, dim3((unsigned)(n_chunks * H)), dim3(kThr), 0, s,
-                       p, H, (const bf16*)q, (const bf16*)k, (const bf16*)v, alpha, beta, prep);
+                       p, c0, H, (const bf16*)q, (const bf16*)k, (const bf16*)v, alpha, beta,
+                       prep);
     return hipGetLastError();
 }
 
@@ -1282,14 +1283,14 @@ hipError_t launch_gdn_chunk_dstate(const DevPlan& p, int l0, int n_br, int H, co
     return hipGetLastError();
 }
 
-hipError_t launch_gdn_chunk_grad(const DevPlan& p, int64_t n_chunks, int H, const void* q,
-                                 const void* k, const void* v, const float* alpha,
+hipError_t launch_gdn_chunk_grad(const DevPlan& p, int c0, int64_t n_chunks, int H,
+                                 const void* q, const void* k, const void* v, const float* alpha,
                                  const float* beta, const void* dout, const float* prep,
                                  const float* chunk_states, const float* dsc, void* dq, void* dk,
                                  void* dv, float* dalpha, float* dbeta, hipStream_t s) {
     if (n_chunks <= 0) return hipSuccess;
     hipLaunchKernelGGL(gdn_chunk_grad_kernel, dim3((unsigned)(n_chunks * H)), dim3(kThr), 0, s,
-                       p, H, (const bf16*)q, (const bf16*)k, (const bf16*)v, alpha, beta,
+                       p, c0, H, (const bf16*)q, (const bf16*)k, (const bf16*)v, alpha, beta,
                        (const bf16*)dout, prep, chunk_states, dsc, (bf16*)dq, (bf16*)dk,
                        (bf16*)dv, dalpha, dbeta);
     return hipGetLastError();
