@@ -523,7 +523,7 @@ size_t gdn_prep_bytes(const octopus_plan* plan, int32_t H) {
 // fork to the join so that concurrent calls do not re-record the events in between.
 struct SideStream {
     hipStream_t s = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr, mid = nullptr;
 };
 std::mutex g_side_mu;
 std::map<int, SideStream> g_side;
@@ -537,7 +537,9 @@ hipError_t side_stream(SideStream& out) {
         e = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&sd.join, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&sd.mid, hipEventDisableTiming);
         if (e != hipSuccess) {
+            if (sd.mid) (void)hipEventDestroy(sd.mid);
             if (sd.join) (void)hipEventDestroy(sd.join);
             if (sd.fork) (void)hipEventDestroy(sd.fork);
             if (sd.s) (void)hipStreamDestroy(sd.s);
@@ -549,8 +551,9 @@ hipError_t side_stream(SideStream& out) {
     return hipSuccess;
 }
 // Forks work off `st` onto the side stream and joins it back: fork() records the fork
-// event and makes the side stream wait for it; join() (also run by the destructor, so
-// every return path joins) records the join event and makes `st` wait for it.
+// event and makes the side stream wait for it; mark() records a point of the side stream
+// that wait_mark() makes `st` wait for; join() (also run by the destructor, so every
+// return path joins) records the join event and makes `st` wait for it.
 class SideFork {
   public:
     explicit SideFork(hipStream_t st) : st_(st) {}
@@ -567,6 +570,8 @@ class SideFork {
         side = sd_.s;
         return hipSuccess;
     }
+    hipError_t mark() { return forked_ ? hipEventRecord(sd_.mid, sd_.s) : hipSuccess; }
+    hipError_t wait_mark() { return forked_ ? hipStreamWaitEvent(st_, sd_.mid, 0) : hipSuccess; }
     hipError_t join() {
         if (!forked_) return hipSuccess;
         forked_ = false;
@@ -759,6 +764,56 @@ int gdn_backward_kept(const octopus_plan* plan, int32_t H, const void* q, const 
 }
 }  // namespace
 
+namespace {
+// The backward with its forward replay.  The state gradient needs only q, k, dout and the
+// records, not the forward's states, so the whole state-gradient chain (deepest level first)
+// runs on the side stream while this stream replays the forward's levels; the gradients
+// follow once both are done.  (The first level's records come first, then the fork, the
+// first level's forward and the deeper levels' records on the side stream, as in the
+// forward.)
+int gdn_backward_full(const octopus_plan* plan, int32_t H, const void* q, const void* k,
+                      const void* v, const float* alpha, const float* beta, const void* dout,
+                      void* dq, void* dk, void* dv, float* dalpha, float* dbeta, void* ws,
+                      hipStream_t st) {
+    const octo::DevPlan dp = dev_view(plan->p);
+    const std::vector<int32_t>& lp = plan->p.level_ptr;
+    const std::vector<int32_t>& lc = plan->p.level_chunk;
+    const GdnBwdWs w = gdn_bwd_ws(plan, H, ws);
+    const int32_t first = lc[1];
+    const int64_t rest = plan->p.n_chunks - first;
+    hipError_t e = octo::launch_gdn_chunk_prep(dp, 0, first, H, q, k, v, alpha, beta, w.prep, st);
+    if (e != hipSuccess) return hip_fail(e, "scan prep launch");
+    SideFork side(st);
+    hipStream_t s2 = nullptr;
+    e = side.fork(s2);
+    if (e != hipSuccess) return hip_fail(e, "scan side stream");
+    e = octo::launch_gdn_chunk_fwd(dp, lp[0], lp[1] - lp[0], H, q, k, w.prep, nullptr, w.slots,
+                                   w.chunks, st);
+    if (e != hipSuccess) return hip_fail(e, "scan forward launch");
+    e = octo::launch_gdn_chunk_prep(dp, first, rest, H, q, k, v, alpha, beta, w.prep, s2);
+    if (e == hipSuccess) e = side.mark();
+    if (e != hipSuccess) return hip_fail(e, "scan prep launch");
+    for (size_t l = lp.size() - 1; l-- > 0;) {
+        e = octo::launch_gdn_chunk_dstate(dp, lp[l], lp[l + 1] - lp[l], H, q, k, dout, w.prep,
+                                          w.dsc, w.dkids, s2);
+        if (e != hipSuccess) return hip_fail(e, "scan backward (state gradient) launch");
+    }
+    e = side.wait_mark();
+    if (e != hipSuccess) return hip_fail(e, "scan side stream");
+    for (size_t l = 1; l + 1 < lp.size(); ++l) {
+        e = octo::launch_gdn_chunk_fwd(dp, lp[l], lp[l + 1] - lp[l], H, q, k, w.prep, nullptr,
+                                       w.slots, w.chunks, st);
+        if (e != hipSuccess) return hip_fail(e, "scan forward launch");
+    }
+    e = side.join();
+    if (e != hipSuccess) return hip_fail(e, "scan side stream");
+    e = octo::launch_gdn_chunk_grad(dp, 0, plan->p.n_chunks, H, q, k, v, alpha, beta, dout,
+                                    w.prep, w.chunks, w.dsc, dq, dk, dv, dalpha, dbeta, st);
+    if (e != hipSuccess) return hip_fail(e, "scan backward launch");
+    return OCTOPUS_OK;
+}
+}  // namespace
+
 int octopus_gated_delta_scan_bwd(const octopus_plan* plan, octopus_dtype dtype, int32_t H,
                                  int32_t Dk, int32_t Dv, const void* q, const void* k,
                                  const void* v, const float* alpha, const float* beta,
@@ -770,12 +825,10 @@ int octopus_gated_delta_scan_bwd(const octopus_plan* plan, octopus_dtype dtype, 
                         (const void*)dbeta});
     if (rc == OCTOPUS_OK) rc = check_gdn_bwd_ws(plan, H, Dk, Dv, ws, ws_bytes);
     if (rc != OCTOPUS_OK) return rc;
-    hipStream_t st = (hipStream_t)stream;
-    // the forward again, keeping the state at the start of every chunk
-    rc = gdn_forward_keep(plan, H, q, k, v, alpha, beta, nullptr, ws, st);
-    if (rc == OCTOPUS_OK)
-        rc = gdn_backward_kept(plan, H, q, k, v, alpha, beta, dout, dq, dk, dv, dalpha, dbeta,
-                               ws, st);
+    // the forward again (keeping the state at the start of every chunk) beside the state
+    // gradient, then the gradients
+    rc = gdn_backward_full(plan, H, q, k, v, alpha, beta, dout, dq, dk, dv, dalpha, dbeta, ws,
+                           (hipStream_t)stream);
     return rc == OCTOPUS_OK ? ok() : rc;
 }
 
