@@ -311,9 +311,9 @@ size_t octopus_gdn_bwd_workspace_bytes(const octopus_plan* plan, int32_t H, int3
  * gradient of a child's initial state (its parent's state at the fork) flows into the
  * parent's earlier tokens; mounted spans receive nothing (the recurrent layers skip them;
  * project page, primitives table).  Recomputes the forward (the states at chunk starts go
- * to the workspace), walks every branch's chunks in reverse carrying only the state
- * gradient (deepest branches first), then computes every chunk's gradients in parallel
- * (the deeper levels' on the second stream while the first level's state gradient runs).
+ * to the workspace) and, beside it on the second stream (see octopus_gated_delta_scan),
+ * walks every branch's chunks in reverse carrying only the state gradient (deepest
+ * branches first); then computes every chunk's gradients in parallel.
  * Deterministic: the children forking at one offset hand their initial-state gradients
  * to the parent in ascending branch order (no atomics), so repeated calls give the same
  * bits.  Same support and errors as octopus_gated_delta_scan. */
@@ -330,7 +330,9 @@ int octopus_gated_delta_scan_bwd(const octopus_plan* plan, octopus_dtype dtype, 
  * from that ws.  The caller passes the same plan and the same q, k, v, alpha, beta to both
  * and leaves ws untouched in between (results are undefined otherwise: nothing checks
  * it).  The backward leaves the saved part in place, so it may run again on the same ws
- * (with another dout).  Same support and errors as octopus_gated_delta_scan_bwd. */
+ * (with another dout); it runs the deeper levels' gradients on the second stream while the
+ * first level's state gradient runs.  Same support and errors as
+ * octopus_gated_delta_scan_bwd. */
 int octopus_gated_delta_scan_save(const octopus_plan* plan, octopus_dtype dtype, int32_t H,
                                   int32_t Dk, int32_t Dv, const void* q, const void* k,
                                   const void* v, const float* alpha, const float* beta, void* o,
