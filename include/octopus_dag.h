@@ -34,13 +34,17 @@
  *   - Device tensors are row-major and contiguous.  "THD" means [T][H][D].
  *   - bf16 is IEEE bfloat16 storage with float32 accumulation; outputs are rounded to
  *     nearest even.  fp32 tensors are float32 throughout.
- *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Device
- *     work is enqueued asynchronously on it; no entry point synchronises it.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream) of the current
+ *     device.  Device work is enqueued asynchronously on it; no entry point synchronises
+ *     it.  (The gated delta-rule scan also runs part of its work on a second stream of
+ *     the device, ordered into `stream`; see there.)
  *   - The caller owns every device buffer (tensors, plan buffer, workspaces).  The
  *     library never allocates or frees device memory.  A plan owns host memory only.
- *   - Return value: OCTOPUS_OK (0) or a negative error code.  On error nothing has
- *     been enqueued and outputs are untouched; octopus_last_error() returns a
- *     thread-local message naming the offending row or argument.
+ *   - Return value: OCTOPUS_OK (0) or a negative error code.  On an argument error
+ *     (EINVAL, ESTATE, EUNSUPPORTED, EWORKSPACE, ECYCLE) nothing has been enqueued and
+ *     outputs are untouched; EHIP (a failed launch) may follow launches of the same call
+ *     that were enqueued.  octopus_last_error() returns a thread-local message naming the
+ *     offending row or argument.
  */
 #ifndef OCTOPUS_DAG_H
 #define OCTOPUS_DAG_H
