@@ -52,6 +52,9 @@ constexpr int kC = 32;          // tokens per chunk
 // consecutive lanes start in different banks (a stride of 32 floats puts them all on the
 // same ones).
 constexpr int kCP = kC + 4;
+// Row stride (bf16) of the split W and dR rows of the gradient pass: 40 bf16 = 5 pieces
+// of 16 bytes.
+constexpr int kSP = 40;
 constexpr int kWaves = kD / 32; // one wave per 32 value rows (or key columns)
 constexpr int kThr = 64 * kWaves;
 constexpr int kRowB = kD * 2;   // bytes of one bf16 row
@@ -851,6 +854,11 @@ struct GradSmem {
     float sxw[kWaves][2];
     float W[kWaves][kC * kCP];   // per wave: W [t][value row]
     float dR[kWaves][kC * kCP];  // dR [t][value row]
+    // the same as bf16 high and low parts, split once by the owning wave and read as A
+    // operands by every wave: rows of kSP bf16 (80 bytes, so the rows of 16 consecutive
+    // lanes start in different banks)
+    bf16 WH[kWaves][kC * kSP], WL[kWaves][kC * kSP];
+    bf16 RH[kWaves][kC * kSP], RL[kWaves][kC * kSP];
 };
 }  // namespace
 
@@ -1086,6 +1094,11 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
             bf16x8 ah, al, bh, bl;
             ld_split(dRl + n * kCP + 16 * ks + 8 * g, 4, ah, al, 1.f);
             ld_split(Wl + n * kCP + 16 * ks + 8 * g, 4, bh, bl, 1.f);
+            const int so = n * kSP + 16 * ks + 8 * g;  // row t = n, this lane's 8 value rows
+            *reinterpret_cast<bf16x8*>(S.RH[w] + so) = ah;
+            *reinterpret_cast<bf16x8*>(S.RL[w] + so) = al;
+            *reinterpret_cast<bf16x8*>(S.WH[w] + so) = bh;
+            *reinterpret_cast<bf16x8*>(S.WL[w] + so) = bl;
             pp = mfma_32x32x16(ah, bh, pp);
             pp = mfma_32x32x16(ah, bl, pp);
             pp = mfma_32x32x16(al, bh, pp);
@@ -1102,18 +1115,19 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
     }
     // ---- dQ = dY S_0 and dK = dX S_0 + diag(gamma_C / gamma) W dS_C for key columns
     // kc = 32 w + n, summed over all 128 value rows: A operands (rows t) from every wave's
-    // W and dR in LDS and from dO; B operands S_0[v][kc], dS_C[v][kc] (8 consecutive v per
-    // lane and k-step, key-major in global memory).
+    // split W and dR in LDS and from dO; B operands S_0[v][kc], dS_C[v][kc] (8 consecutive
+    // v per lane and k-step, key-major in global memory).  The row factors of dY = diag(gamma)
+    // dO and dX = -diag(beta gamma) dR and the gamma_C / gamma of the W term scale the
+    // products' rows afterwards (fx, fw, fq), so the A operands need no scaling or splitting
+    // here (dO is bf16 already).
     wait_lds();
     barrier();  // every wave's W and dR are in LDS
-    f32x16 fq = zero16(), fk = zero16();
+    f32x16 fq = zero16(), fk;
     {
+        f32x16 fx = zero16(), fw = zero16();
         const int kc = 32 * w + n;
         const float* s0r = S0g + (size_t)kc * kD + 8 * g;
         const float* dsr = dSg + (size_t)kc * kD + 8 * g;
-        // the A operands' rows are t = n
-        const float gmn = S.gam[n], btn = S.beta[n];
-        const float xsc = -btn * gmn, wsc = rec[kRecG + kIG + n];
 #pragma unroll
         for (int ks = 0; ks < kD / 16; ++ks) {
             const float4 sa = *reinterpret_cast<const float4*>(s0r + 16 * ks);
@@ -1122,30 +1136,37 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
             const float4 dbv = *reinterpret_cast<const float4*>(dsr + 16 * ks + 4);
             const float s8[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
             const float d8[8] = {da.x, da.y, da.z, da.w, dbv.x, dbv.y, dbv.z, dbv.w};
-            bf16x8 sh, sl, dh, dl, xh, xl, wh, wl, yh, yl;
+            bf16x8 sh, sl, dh, dl;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 split2(s8[e], sh, sl, e);
                 split2(d8[e], dh, dl, e);
                 sx += gC * s8[e] * d8[e];  // gamma_C <dS_C, S_0>: each element once
             }
-            const int vw = ks >> 1, vl = 16 * (ks & 1) + 8 * g;
-            ld_split(S.dR[vw] + n * kCP + vl, 4, xh, xl, xsc);
-            ld_split(S.W[vw] + n * kCP + vl, 4, wh, wl, wsc);
-            {
-                const bf16x8 o8 = rd8(S.dO, n, 16 * ks + 8 * g);
+            const int so = n * kSP + 16 * (ks & 1) + 8 * g;  // wave ks / 2's value rows
+            const bf16x8 xh = *reinterpret_cast<const bf16x8*>(S.RH[ks >> 1] + so);
+            const bf16x8 xl = *reinterpret_cast<const bf16x8*>(S.RL[ks >> 1] + so);
+            const bf16x8 wh = *reinterpret_cast<const bf16x8*>(S.WH[ks >> 1] + so);
+            const bf16x8 wl = *reinterpret_cast<const bf16x8*>(S.WL[ks >> 1] + so);
+            const bf16x8 o8 = rd8(S.dO, n, 16 * ks + 8 * g);
+            fx = mfma_32x32x16(xh, sh, fx);
+            fx = mfma_32x32x16(xh, sl, fx);
+            fx = mfma_32x32x16(xl, sh, fx);
+            fw = mfma_32x32x16(wh, dh, fw);
+            fw = mfma_32x32x16(wh, dl, fw);
+            fw = mfma_32x32x16(wl, dh, fw);
+            fq = mfma_32x32x16(o8, sh, fq);
+            fq = mfma_32x32x16(o8, sl, fq);
+        }
+        // the row factors at the accumulator's rows t = acc_row(j, g)
+        float rg[16], rbg[16], rig[16];
+        ld16f(rec + kRecG + kGam + 4 * g, 8, rg);
+        ld16f(rec + kRecG + kBG + 4 * g, 8, rbg);
+        ld16f(rec + kRecG + kIG + 4 * g, 8, rig);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) split2((float)o8[e] * gmn, yh, yl, e);
-            }
-            fk = mfma_32x32x16(xh, sh, fk);
-            fk = mfma_32x32x16(xh, sl, fk);
-            fk = mfma_32x32x16(xl, sh, fk);
-            fk = mfma_32x32x16(wh, dh, fk);
-            fk = mfma_32x32x16(wh, dl, fk);
-            fk = mfma_32x32x16(wl, dh, fk);
-            fq = mfma_32x32x16(yh, sh, fq);
-            fq = mfma_32x32x16(yh, sl, fq);
-            fq = mfma_32x32x16(yl, sh, fq);
+        for (int j = 0; j < 16; ++j) {
+            fk[j] = rig[j] * fw[j] - rbg[j] * fx[j];
+            fq[j] *= rg[j];
         }
     }
     sx = half_sum(sx);
