@@ -219,12 +219,15 @@ __device__ __forceinline__ float tile_at(const unsigned char* base, int t, int c
 
 // Rows t < nt of a chunk of x [T][H][128] (bf16, head h, first token tok0), zeros past
 // nt: thread tid loads 16-byte pieces tid and tid + 256 (row p / 16, columns 8 (p % 16)).
+// The loads are unconditional (a row past nt reads row nt - 1 and is then replaced by
+// zeros), so they issue back to back with no branch between them.
 __device__ __forceinline__ void fetch_rows(const bf16* __restrict__ x, size_t tok0, int nt,
                                            int H, int h, int tid, bf16x8 (&r)[2]) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int p = u * kThr + tid, t = p >> 4;
-        r[u] = t < nt ? ld16(x + ((tok0 + t) * H + h) * kD + 8 * (p & 15)) : zero8();
+        const bf16x8 v = ld16(x + ((tok0 + min(t, nt - 1)) * H + h) * kD + 8 * (p & 15));
+        r[u] = t < nt ? v : zero8();
     }
 }
 // ... and into a swizzled LDS tile.
@@ -894,24 +897,27 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
         for (int e = 0; e < 8; ++e) split2(v[e] * scale, hi, lo, e);
     };
 
-    // ---- loads: chunk inputs (zeros past nt; alpha 1, beta 0), cleared sums
+    // ---- loads: chunk inputs (zeros past nt; alpha 1, beta 0), cleared sums; S_0 as the B
+    // operands of X and Y (issued now, with the rows, so that their latencies overlap)
+    float s0v[4][16];
     {
         bf16x8 rk[2], rq[2], rv[2], ro[2];
         fetch_rows(Kg, tok0, nt, H, h, tid, rk);
         fetch_rows(Qg, tok0, nt, H, h, tid, rq);
         fetch_rows(Vg, tok0, nt, H, h, tid, rv);
         fetch_rows(dOg, tok0, nt, H, h, tid, ro);
+        // the gates: every thread loads one (in bounds, so the load is not in a branch and
+        // is issued before the states; threads 0 .. 63 keep theirs)
+        const int ta = tid & (kC - 1);
+        const float gate = (tid < kC ? Ag : Bg)[(tok0 + min(ta, nt - 1)) * H + h];
+#pragma unroll
+        for (int bk = 0; bk < 4; ++bk) load_key_major(S0g, bk, dv, g, s0v[bk]);
         put_rows(S.K, tid, rk);
         put_rows(S.Q, tid, rq);
         put_rows(S.V, tid, rv);
         put_rows(S.dO, tid, ro);
-    }
-    if (tid < 2 * kC) {
-        const int t = tid & (kC - 1);
-        (tid < kC ? S.alpha : S.beta)[t] =
-            t < nt ? (tid < kC ? Ag : Bg)[(tok0 + t) * H + h] : (tid < kC ? 1.f : 0.f);
-    }
-    {
+        if (tid < 2 * kC)
+            (tid < kC ? S.alpha : S.beta)[ta] = ta < nt ? gate : (tid < kC ? 1.f : 0.f);
     }
     wait_lds();
     barrier();
@@ -947,12 +953,10 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
     f32x16 X = zero16(), Y = zero16(), X2 = zero16(), Y2 = zero16();
 #pragma unroll
     for (int bk = 0; bk < 4; ++bk) {
-        float sv[16];
-        load_key_major(S0g, bk, dv, g, sv);
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
             bf16x8 shi, slo;
-            split8(sv, kh, shi, slo);
+            split8(s0v[bk], kh, shi, slo);
             const int k0 = 32 * bk + 16 * kh + 4 * g;
             const bf16x8 ak = rd_perm(S.K, n, k0);
             const bf16x8 aq = rd_perm(S.Q, n, k0);
@@ -962,6 +966,10 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
             Y2 = mfma_32x32x16(aq, slo, Y2);
         }
     }
+    // dS_C as the B operands of dW (issued here, used two phases later)
+    float dsv[4][16];
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk) load_key_major(dSg, bk, dv, g, dsv[bk]);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         X[j] += X2[j];
@@ -1023,12 +1031,10 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
         }
 #pragma unroll
         for (int bk = 0; bk < 4; ++bk) {
-            float sv[16];
-            load_key_major(dSg, bk, dv, g, sv);
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
                 bf16x8 shi, slo;
-                split8(sv, kh, shi, slo);
+                split8(dsv[bk], kh, shi, slo);
                 const bf16x8 ak = rd_perm(S.K, n, 32 * bk + 16 * kh + 4 * g);
                 tB = mfma_32x32x16(ak, shi, tB);
                 tB2 = mfma_32x32x16(ak, slo, tB2);
