@@ -606,7 +606,10 @@ int gdn_forward_run(const octopus_plan* plan, int32_t H, const void* q, const vo
     // forward, and only then the side stream's records.  The forward's workgroups each need
     // a whole compute unit, so they must be dispatched before the side stream's many small
     // workgroups fill every unit (they become ready together when the first records land).
-    hipError_t e = octo::launch_gdn_chunk_prep(dp, 0, first, H, q, k, v, alpha, beta, prep, st);
+    // (the transposed record blocks only when a backward follows: chunk_states kept)
+    const bool with_t = chunk_states != nullptr;
+    hipError_t e = octo::launch_gdn_chunk_prep(dp, 0, first, H, with_t, q, k, v, alpha, beta,
+                                               prep, st);
     if (e != hipSuccess) return hip_fail(e, "scan prep launch");
     SideFork side(st);
     hipStream_t s2 = nullptr;
@@ -618,7 +621,8 @@ int gdn_forward_run(const octopus_plan* plan, int32_t H, const void* q, const vo
                                    chunk_states, st);
     if (e != hipSuccess) return hip_fail(e, "scan forward launch");
     if (rest > 0) {
-        e = octo::launch_gdn_chunk_prep(dp, first, rest, H, q, k, v, alpha, beta, prep, s2);
+        e = octo::launch_gdn_chunk_prep(dp, first, rest, H, with_t, q, k, v, alpha, beta, prep,
+                                        s2);
         if (e != hipSuccess) return hip_fail(e, "scan prep launch");
     }
     e = side.join();
@@ -781,7 +785,8 @@ int gdn_backward_full(const octopus_plan* plan, int32_t H, const void* q, const 
     const GdnBwdWs w = gdn_bwd_ws(plan, H, ws);
     const int32_t first = lc[1];
     const int64_t rest = plan->p.n_chunks - first;
-    hipError_t e = octo::launch_gdn_chunk_prep(dp, 0, first, H, q, k, v, alpha, beta, w.prep, st);
+    hipError_t e = octo::launch_gdn_chunk_prep(dp, 0, first, H, true, q, k, v, alpha, beta,
+                                               w.prep, st);
     if (e != hipSuccess) return hip_fail(e, "scan prep launch");
     SideFork side(st);
     hipStream_t s2 = nullptr;
@@ -790,7 +795,7 @@ int gdn_backward_full(const octopus_plan* plan, int32_t H, const void* q, const 
     e = octo::launch_gdn_chunk_fwd(dp, lp[0], lp[1] - lp[0], H, q, k, w.prep, nullptr, w.slots,
                                    w.chunks, st);
     if (e != hipSuccess) return hip_fail(e, "scan forward launch");
-    e = octo::launch_gdn_chunk_prep(dp, first, rest, H, q, k, v, alpha, beta, w.prep, s2);
+    e = octo::launch_gdn_chunk_prep(dp, first, rest, H, true, q, k, v, alpha, beta, w.prep, s2);
     if (e == hipSuccess) e = side.mark();
     if (e != hipSuccess) return hip_fail(e, "scan prep launch");
     for (size_t l = lp.size() - 1; l-- > 0;) {

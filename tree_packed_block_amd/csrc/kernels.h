@@ -113,13 +113,14 @@ hipError_t launch_rope2(bool bf16, int rows, int D, float base, bool inverse,
 // Chunked gated delta-rule scan (matrix cores, 32-token chunks as listed by the plan):
 // q, k, v, dout [T][H][128] bf16, alpha, beta float32 [T][H].  The prep kernel writes a
 // record of gdn_prep_floats / (n_chunks H) floats per (chunk, head) into `prep` for the
-// n_chunks chunks from chunk c0 on; the forward walks the branches level_br[l0 .. l0 + n_br)
+// n_chunks chunks from chunk c0 on (with_t: also the transposed blocks that only the backward
+// reads); the forward walks the branches level_br[l0 .. l0 + n_br)
 // (one workgroup per (branch, head)) from their checkpoint slots `states`
 // [n_slots][H][128][128] float32 (row = value index), writing o [T][H][128] bf16 (may be
 // NULL) and, with chunk_states (may be NULL), the state at the start of every chunk
 // [c][H][128][128].
 size_t gdn_prep_floats(int64_t n_chunks, int H);
-hipError_t launch_gdn_chunk_prep(const DevPlan& p, int c0, int64_t n_chunks, int H,
+hipError_t launch_gdn_chunk_prep(const DevPlan& p, int c0, int64_t n_chunks, int H, bool with_t,
                                  const void* q, const void* k, const void* v, const float* alpha,
                                  const float* beta, float* prep, hipStream_t s);
 hipError_t launch_gdn_chunk_fwd(const DevPlan& p, int l0, int n_br, int H, const void* q,

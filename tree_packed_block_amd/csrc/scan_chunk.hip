@@ -332,8 +332,9 @@ struct PrepSmem {
 
 // ---------------------------------------------------------------- prep (parallel)
 
+// with_t: also the transposes T^T and M^T, which only the backward reads.
 __global__ __launch_bounds__(kThr) void gdn_chunk_prep_kernel(
-    DevPlan P, int c0, int H, const bf16* __restrict__ Qg, const bf16* __restrict__ Kg,
+    DevPlan P, int c0, int H, bool with_t, const bf16* __restrict__ Qg, const bf16* __restrict__ Kg,
     const bf16* __restrict__ Vg, const float* __restrict__ Ag, const float* __restrict__ Bg,
     float* __restrict__ prep) {
     __shared__ __attribute__((aligned(1024))) PrepSmem S;
@@ -394,7 +395,7 @@ __global__ __launch_bounds__(kThr) void gdn_chunk_prep_kernel(
             fwd_solve(tv, S.LG, S.beta, g);
 #pragma unroll
             for (int j = 0; j < 16; ++j) S.T[acc_row(j, g) * kCP + n] = tv[j];
-            st_split(rec + kRecTT, lane, tv);  // T^T rows n: T[acc_row(j, g)][n]
+            if (with_t) st_split(rec + kRecTT, lane, tv);  // T^T rows n: T[acc_row(j, g)][n]
             // gamma_C / gamma_t as one difference of logarithms (1 past nt)
             const float lgC = __shfl(la, nt - 1, 64);
             if (lane < kC) {
@@ -406,7 +407,7 @@ __global__ __launch_bounds__(kThr) void gdn_chunk_prep_kernel(
         } else {
 #pragma unroll
             for (int j = 0; j < 16; ++j) S.M[acc_row(j, g) * kCP + n] = v[j];
-            st_split(rec + kRecMT, lane, v);  // M^T rows n: M[acc_row(j, g)][n]
+            if (with_t) st_split(rec + kRecMT, lane, v);  // M^T rows n: M[acc_row(j, g)][n]
         }
     }
     wait_lds();
@@ -1282,12 +1283,12 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
 
 size_t gdn_prep_floats(int64_t n_chunks, int H) { return (size_t)n_chunks * H * kRec; }
 
-hipError_t launch_gdn_chunk_prep(const DevPlan& p, int c0, int64_t n_chunks, int H,
+hipError_t launch_gdn_chunk_prep(const DevPlan& p, int c0, int64_t n_chunks, int H, bool with_t,
                                  const void* q, const void* k, const void* v, const float* alpha,
                                  const float* beta, float* prep, hipStream_t s) {
     if (n_chunks <= 0) return hipSuccess;
     hipLaunchKernelGGL(gdn_chunk_prep_kernel, dim3((unsigned)(n_chunks * H)), dim3(kThr), 0, s,
-                       p, c0, H, (const bf16*)q, (const bf16*)k, (const bf16*)v, alpha, beta,
+                       p, c0, H, with_t, (const bf16*)q, (const bf16*)k, (const bf16*)v, alpha, beta,
                        prep);
     return hipGetLastError();
 }
