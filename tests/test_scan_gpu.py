@@ -234,6 +234,47 @@ def test_scan_save_then_bwd_saved(name):
     say("  identical to the plain forward and backward")
 
 
+def test_scan_on_a_side_stream():
+    """The scan runs part of its work on a second stream of its own, forked from and joined
+    back into the caller's stream.  On a caller's side stream, with the inputs written on that
+    stream just before the call and the outputs read on it right after, forward, backward and
+    the training pair give the same bits as on the current stream."""
+    import torch
+    import tree_packed_block_amd as tpb
+    say("case scan on a side stream")
+    dag, _ = synth.build("episode_small")
+    H = 2
+    x = synth.draw_scan_inputs(np.random.default_rng(41), dag.T, H)
+    plan = tpb.Plan(dag.branches, dag.mounts, dag.T).upload()
+    t = [dev(x[n], "bf16") for n in ("q", "k", "v")]
+    a, b = torch.from_numpy(x["alpha"]).cuda(), torch.from_numpy(x["beta"]).cuda()
+    do = dev(synth.round_bf16((0.5 * np.random.default_rng(42).standard_normal(
+        x["v"].shape)).astype(np.float32)), "bf16")
+    o_ref = tpb.gated_delta_scan(plan, *t, a, b)
+    g_ref = tpb.gated_delta_scan_bwd(plan, *t, a, b, do)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        # inputs produced on the side stream right before the calls: the scan's own second
+        # stream must start after them
+        t2 = [torch.empty_like(z) for z in t]
+        for dst, src in zip(t2, t):
+            dst.copy_(src)
+        a2, b2, do2 = a.clone(), b.clone(), do.clone()
+        o = tpb.gated_delta_scan(plan, *t2, a2, b2, stream=side)
+        g = tpb.gated_delta_scan_bwd(plan, *t2, a2, b2, do2, stream=side)
+        o_s, ws = tpb.gated_delta_scan_save(plan, *t2, a2, b2, stream=side)
+        g_s = tpb.gated_delta_scan_bwd_saved(plan, *t2, a2, b2, do2, ws, stream=side)
+        # outputs consumed on the side stream right after: the joins must come first
+        outs = [z.clone() for z in (o, *g, o_s, *g_s)]
+    side.synchronize()
+    refs = (o_ref, *g_ref, o_ref, *g_ref)
+    names = ("o", "dq", "dk", "dv", "dalpha", "dbeta") * 2
+    for nm, got, ref in zip(names, outs, refs):
+        assert torch.equal(got, ref), f"{nm} differs on a side stream"
+    say("  identical on a side stream")
+
+
 def test_scan_entry_points_reject_bad_arguments():
     """Errors found on the host with an uploaded plan, before any launch: unsupported
     head sizes and dtypes, NULL tensors, a workspace that is too small."""
