@@ -516,11 +516,12 @@ size_t gdn_prep_bytes(const octopus_plan* plan, int32_t H) {
     return octo::gdn_prep_floats(plan->p.n_chunks, H) * sizeof(float);
 }
 
-// A second stream of the current device (default priority) with two events, created on
+// A second stream of the current device (default priority) with three events, created on
 // first use and kept for the life of the process.  The scan runs independent launches on
 // it next to the caller's stream: a fork event recorded on the caller's stream, work on
-// the side stream, a join event the caller's stream waits for.  g_side_mu is held from the
-// fork to the join so that concurrent calls do not re-record the events in between.
+// the side stream (with an optional mark the caller's stream may wait for), a join event
+// the caller's stream waits for.  g_side_mu is held from the fork to the join so that
+// concurrent calls do not re-record the events in between.
 struct SideStream {
     hipStream_t s = nullptr;
     hipEvent_t fork = nullptr, join = nullptr, mid = nullptr;
