@@ -32,9 +32,13 @@ HIPCC_FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 # Per-source code-generation options.  The kernels never produce NaN on purpose, so
-# fmaxf need not quiet NaN operands (that costs one extra instruction per maximum).
+# fmaxf need not quiet NaN operands (that costs one extra instruction per maximum).  The
+# scan kernels fit in the 256 architectural registers with their MFMA accumulators there
+# too; in the default form the compiler puts those in AGPRs and copies them back and
+# forth for every VALU operation on the state.
 HIP_FILE_FLAGS: dict = {"fwd.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"],
-                        "extend.hip": ["-fno-honor-nans"]}
+                        "extend.hip": ["-fno-honor-nans"],
+                        "scan_chunk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
              "-D__HIP_PLATFORM_AMD__"]
 

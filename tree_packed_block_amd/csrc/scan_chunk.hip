@@ -76,16 +76,37 @@ constexpr int kRecU = 0, kRecT = 4096, kRecM = 5120, kRecG = 6144, kRecTT = 6400
               kRecMT = 7424, kRec = 8448;
 constexpr int kGam = 0, kBG = 32, kIG = 64;  // offsets inside G
 
-// Element e of hi and lo take x as hi + lo, both bf16 (|x - hi - lo| <= 2^-16 |x|).
-__device__ __forceinline__ void split2(float x, bf16x8& hi, bf16x8& lo, int e) {
-    const bf16 h = (bf16)x;
-    hi[e] = h;
-    lo[e] = (bf16)(x - (float)h);
+// x0 and x1 as hi + lo, each part a pair of bf16 (element 0 in the low half): hi rounded
+// to nearest, lo the rounded remainder (|x - hi - lo| <= 2^-16 |x|).  A pair takes one
+// conversion instruction per part.
+__device__ __forceinline__ void split_pair(float x0, float x1, unsigned& hi, unsigned& lo) {
+    typedef __attribute__((ext_vector_type(2))) float f32x2;
+    const unsigned h = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x0, x1}, bf16x2));
+    const float h0 = __builtin_bit_cast(float, h << 16);
+    const float h1 = __builtin_bit_cast(float, h & 0xffff0000u);
+    hi = h;
+    lo = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x0 - h0, x1 - h1}, bf16x2));
+}
+// Element e of hi and lo take x[e] as hi + lo.
+__device__ __forceinline__ void split8p(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+    typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+    u32x4 h, l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        unsigned a, b;
+        split_pair(x[2 * i], x[2 * i + 1], a, b);
+        h[i] = a;
+        l[i] = b;
+    }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
 }
 // Elements 8 kk .. 8 kk + 7 of v, split.
 __device__ __forceinline__ void split8(const float (&v)[16], int kk, bf16x8& hi, bf16x8& lo) {
+    float x[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) split2(v[8 * kk + e], hi, lo, e);
+    for (int e = 0; e < 8; ++e) x[e] = v[8 * kk + e];
+    split8p(x, hi, lo);
 }
 
 // x plus the value of the lane 32 away (the other half of the wave).
@@ -262,20 +283,58 @@ __device__ __forceinline__ void dma_block(unsigned lds, const float* src, int n_
         dma16_s(src, (unsigned)(k * 64 + lane) * 16, lds + k * 64 * 16);
 }
 
+// Word 3 of a raw buffer resource on gfx9-family chips (32-bit data format, no swizzle).
+constexpr int kBufferWord3 = 0x00020000;
+
 // The transposed tiles X[bk][j] = M[dv][32 bk + acc_row(j, g)] of a 128 x 128 matrix M held
 // by the four waves (lane = row dv), stored key-major: dst[k][dv] (lanes write consecutive
-// dv: 128 bytes per row k).
+// dv: 128 bytes per row k).  dst is the same for the whole workgroup: the stores go through
+// one buffer resource over its 64 KiB, with the lane's part of the offset computed once and
+// the rest a constant of each store.
 __device__ __forceinline__ void store_key_major(float* dst, const f32x16 (&X)[4], int dv, int g) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(dst, 0, kD * kD * 4, kBufferWord3);
+    const int lane_off = (4 * g * kD + dv) * 4;
 #pragma unroll
     for (int bk = 0; bk < 4; ++bk)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) dst[(32 * bk + acc_row(j, g)) * kD + dv] = X[bk][j];
+        for (int j = 0; j < 16; ++j) {
+            // (the element is copied out first: this compiler's bit_cast of a vector
+            // element reads the vector's first element instead)
+            const float x = X[bk][j];
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), r, lane_off,
+                                                  (32 * bk + 8 * (j >> 2) + (j & 3)) * kD * 4, 0);
+        }
 }
-// ... and read back into the same tiles.
+// ... and read back into the same tiles (src the same for the whole workgroup, read
+// through one buffer resource like the stores).
 __device__ __forceinline__ void load_key_major(const float* src, int bk, int dv, int g,
                                                float (&v)[16]) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(src), 0, kD * kD * 4, kBufferWord3);
+    const int lane_off = (4 * g * kD + dv) * 4;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = src[(32 * bk + acc_row(j, g)) * kD + dv];
+    for (int j = 0; j < 16; ++j)
+        v[j] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(
+                       r, lane_off, (32 * bk + 8 * (j >> 2) + (j & 3)) * kD * 4, 0));
+}
+
+// A buffer resource over rows 0 .. nt - 1 of a chunk of a [T][H][128] bf16 tensor, from
+// `row0` (the chunk's first token, the head's 128 columns); rs = H * 128 elements per token.
+// A store to row t >= nt lies outside it (the column is below the row stride) and the
+// hardware drops it, so the stores of a chunk need no test of their row.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rows(bf16* row0, int nt, int rs) {
+    return __builtin_amdgcn_make_buffer_rsrc(row0, 0, nt * rs * 2, kBufferWord3);
+}
+__device__ __forceinline__ void st_row(__amdgpu_buffer_rsrc_t r, int t, int col, int rs, bf16 v) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r,
+                                          (t * rs + col) * 2, 0, 0);
+}
+// Elements 2 i and 2 i + 1 of v as a pair of bf16.
+__device__ __forceinline__ bf16x2 cvt_pair(const float (&v)[16], int i) {
+    typedef __attribute__((ext_vector_type(2))) float f32x2;
+    return __builtin_convertvector(((f32x2){v[2 * i], v[2 * i + 1]}), bf16x2);
 }
 
 // v plus the value of the lane given by the DPP control CTRL (rows of 16 lanes enabled by
@@ -424,8 +483,10 @@ __global__ __launch_bounds__(kThr) void gdn_chunk_prep_kernel(
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
         bf16x8 ah, al;
+        float x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) split2(trow[8 * kk + e] * brow[8 * kk + e], ah, al, e);
+        for (int e = 0; e < 8; ++e) x[e] = trow[8 * kk + e] * brow[8 * kk + e];
+        split8p(x, ah, al);
         const bf16x8 bv = rd_tr(S.V, tr, w, kk);
         u = mfma_32x32x16(ah, bv, u);
         u = mfma_32x32x16(al, bv, u);
@@ -531,9 +592,16 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
 
     save_due(0);
     if (nch > 0) issue(cbase, 0);
-    bf16 ostash[16];
-    bf16* o_ptr = nullptr;
+    bf16x2 ostash[8];  // rows acc_row(2 i, g), acc_row(2 i + 1, g)
+    bf16* o_ptr = nullptr;  // row 0 of the stashed chunk, this head (uniform)
     int o_nt = 0;
+    // Through a buffer resource over the chunk's o_nt rows: a row past o_nt is outside it,
+    // and the hardware drops that store (the lane's column dv is below the row stride).
+    auto store_o = [&]() {
+        const __amdgpu_buffer_rsrc_t r = chunk_rows(o_ptr, o_nt, (int)rs);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) st_row(r, acc_row(j, g), dv, (int)rs, ostash[j >> 1][j & 1]);
+    };
     for (int ci = 0; ci < nch; ++ci) {
         const int c = cbase + ci, buf = ci & 1;
         const size_t tok0 = ld_const(P.sc_chunk_tok + c);
@@ -544,13 +612,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
         wait_vmem<0>();
         barrier();
         // The previous chunk's outputs, stored now: they complete while this chunk runs.
-        if (o_nt > 0) {
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int t = acc_row(j, g);
-                if (t < o_nt) o_ptr[t * rs] = ostash[j];
-            }
-        }
+        if (o_nt > 0) store_o();
         if (chunk_states)
             store_key_major(chunk_states + ((size_t)c * H + h) * kD * kD, St, dv, g);
         if (ci + 1 < nch) issue(c + 1, buf ^ 1);
@@ -572,8 +634,10 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
                 bf16x8 shi, slo;
+                float x[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) split2(St[bk][8 * kh + e], shi, slo, e);
+                for (int e = 0; e < 8; ++e) x[e] = St[bk][8 * kh + e];
+                split8p(x, shi, slo);
                 const int k0 = 32 * bk + 16 * kh + 4 * g;
                 const bf16x8 ak = rd_perm(B.K, n, k0);
                 const bf16x8 aq = rd_perm(B.Q, n, k0);
@@ -615,8 +679,15 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
         for (int j = 0; j < 16; ++j) MW[j] += MWb[j] + MWc[j];
         if (Og != nullptr) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) ostash[j] = (bf16)(cgam[j] * (Y[j] + Y2[j]) + MW[j]);
-            o_ptr = Og + (tok0 * H + h) * kD + dv;
+            for (int i = 0; i < 8; ++i) {
+                typedef __attribute__((ext_vector_type(2))) float f32x2;
+                const int j = 2 * i;
+                ostash[i] = __builtin_convertvector(
+                    ((f32x2){cgam[j] * (Y[j] + Y2[j]) + MW[j],
+                             cgam[j + 1] * (Y[j + 1] + Y2[j + 1]) + MW[j + 1]}),
+                    bf16x2);
+            }
+            o_ptr = Og + (tok0 * H + h) * kD;
             o_nt = nt;
         }
         // S^T <- gamma_C S^T + K^T (diag(gamma_C / gamma) W): A = K^T (transposed reads),
@@ -640,13 +711,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
         }
         save_due((int)(tok0 - start) + nt);
     }
-    if (o_nt > 0) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int t = acc_row(j, g);
-            if (t < o_nt) o_ptr[t * rs] = ostash[j];
-        }
-    }
+    if (o_nt > 0) store_o();
 }
 
 // ---------------------------------------------------------------- backward: dS (sequential)
@@ -757,8 +822,10 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_dstate_kernel(
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
                 bf16x8 shi, slo;
+                float x[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) split2(dSt[bk][8 * kh + e], shi, slo, e);
+                for (int e = 0; e < 8; ++e) x[e] = dSt[bk][8 * kh + e];
+                split8p(x, shi, slo);
                 const bf16x8 ak = rd_perm(B.K, n, 32 * bk + 16 * kh + 4 * g);
                 tB = mfma_32x32x16(ak, shi, tB);
                 tB2 = mfma_32x32x16(ak, slo, tB2);
@@ -782,13 +849,17 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_dstate_kernel(
         for (int j = 0; j < 16; ++j) dR[j] += dRb[j] + dRc[j];
         bf16x8 xh[2], xl[2], yh[2], yl[2];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int kk = 0; kk < 2; ++kk) {
+            float x[8], y[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int j = 8 * kk + e;
-                split2(-cbg[j] * dR[j], xh[kk], xl[kk], e);
-                split2(acc_row(j, g) < nt ? cgam[j] * (float)o8[kk][e] : 0.f, yh[kk], yl[kk], e);
+                x[e] = -cbg[j] * dR[j];
+                y[e] = acc_row(j, g) < nt ? cgam[j] * (float)o8[kk][e] : 0.f;
             }
+            split8p(x, xh[kk], xl[kk]);
+            split8p(y, yh[kk], yl[kk]);
+        }
         // dS_0^T = gamma_C dS_C^T + K^T dX + Q^T dY
 #pragma unroll
         for (int bk = 0; bk < 4; ++bk) {
@@ -893,9 +964,9 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
     auto ld_split = [&](const float* p, int off, bf16x8& hi, bf16x8& lo, float scale) {
         const float4 a = *reinterpret_cast<const float4*>(p);
         const float4 cc = *reinterpret_cast<const float4*>(p + off);
-        const float v[8] = {a.x, a.y, a.z, a.w, cc.x, cc.y, cc.z, cc.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) split2(v[e] * scale, hi, lo, e);
+        const float v[8] = {a.x * scale, a.y * scale, a.z * scale, a.w * scale,
+                            cc.x * scale, cc.y * scale, cc.z * scale, cc.w * scale};
+        split8p(v, hi, lo);
     };
 
     // ---- loads: chunk inputs (zeros past nt; alpha 1, beta 0), cleared sums; S_0 as the B
@@ -1062,12 +1133,23 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
     }
     // ---- W and dR to LDS ([t][value row]); dV; the beta and gate terms per row
     float sx = 0.f;  // terms of d L / d log gamma_C: this lane's part
+    const int rs = H * kD;
+    {
+        float dvv[16];
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-        const int t = acc_row(jj, g);
-        Wl[t * kCP + n] = wv[jj];
-        dRl[t * kCP + n] = dr[jj];
-        if (t < nt) dVg[((tok0 + t) * H + h) * kD + dv] = (bf16)(S.beta[t] * dr[jj]);
+        for (int jj = 0; jj < 16; ++jj) {
+            const int t = acc_row(jj, g);
+            Wl[t * kCP + n] = wv[jj];
+            dRl[t * kCP + n] = dr[jj];
+            dvv[jj] = S.beta[t] * dr[jj];
+        }
+        const __amdgpu_buffer_rsrc_t r = chunk_rows(dVg + (tok0 * H + h) * kD, nt, rs);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const bf16x2 pr = cvt_pair(dvv, i);
+            st_row(r, acc_row(2 * i, g), dv, rs, pr[0]);
+            st_row(r, acc_row(2 * i + 1, g), dv, rs, pr[1]);
+        }
     }
     {
         float rdb[16], rdg[16];
@@ -1144,12 +1226,10 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
             const float s8[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
             const float d8[8] = {da.x, da.y, da.z, da.w, dbv.x, dbv.y, dbv.z, dbv.w};
             bf16x8 sh, sl, dh, dl;
+            split8p(s8, sh, sl);
+            split8p(d8, dh, dl);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                split2(s8[e], sh, sl, e);
-                split2(d8[e], dh, dl, e);
-                sx += gC * s8[e] * d8[e];  // gamma_C <dS_C, S_0>: each element once
-            }
+            for (int e = 0; e < 8; ++e) sx += gC * s8[e] * d8[e];  // gamma_C <dS_C, S_0>: each element once
             const int so = n * kSP + 16 * (ks & 1) + 8 * g;  // wave ks / 2's value rows
             const bf16x8 xh = *reinterpret_cast<const bf16x8*>(S.RH[ks >> 1] + so);
             const bf16x8 xl = *reinterpret_cast<const bf16x8*>(S.RL[ks >> 1] + so);
@@ -1230,12 +1310,15 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
             // rows i of this k-step in the accumulator order
             bf16x8 qh, ql, ah, al, th, tl;
             ld_split(S.dM[0] + n * kCP + 16 * kk + 4 * g, 8, qh, ql, 1.f);
+            float a8[8], t8[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int i = 16 * kk + 8 * (e >> 2) + 4 * g + (e & 3);
-                split2(S.P[0][n * kCP + i] + S.P[0][i * kCP + n], ah, al, e);
-                split2(S.dM[0][i * kCP + n], th, tl, e);
+                a8[e] = S.P[0][n * kCP + i] + S.P[0][i * kCP + n];
+                t8[e] = S.dM[0][i * kCP + n];
             }
+            split8p(a8, ah, al);
+            split8p(t8, th, tl);
             fq = mfma_32x32x16(qh, bkv, fq);
             fq = mfma_32x32x16(ql, bkv, fq);
             fk = mfma_32x32x16(ah, bkv, fk);
@@ -1243,13 +1326,22 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
             fk = mfma_32x32x16(th, bqv, fk);
             fk = mfma_32x32x16(tl, bqv, fk);
         }
+        {
+            const __amdgpu_buffer_rsrc_t rq = chunk_rows(dQg + (tok0 * H + h) * kD, nt, rs);
+            const __amdgpu_buffer_rsrc_t rk = chunk_rows(dKg + (tok0 * H + h) * kD, nt, rs);
+            float q16[16], k16[16];
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-            const int t = acc_row(jj, g);
-            if (t < nt) {
-                const size_t o = ((tok0 + t) * H + h) * kD + dv;
-                dQg[o] = (bf16)fq[jj];
-                dKg[o] = (bf16)fk[jj];
+            for (int jj = 0; jj < 16; ++jj) {
+                q16[jj] = fq[jj];
+                k16[jj] = fk[jj];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const bf16x2 pq = cvt_pair(q16, i), pk = cvt_pair(k16, i);
+                st_row(rq, acc_row(2 * i, g), dv, rs, pq[0]);
+                st_row(rq, acc_row(2 * i + 1, g), dv, rs, pq[1]);
+                st_row(rk, acc_row(2 * i, g), dv, rs, pk[0]);
+                st_row(rk, acc_row(2 * i + 1, g), dv, rs, pk[1]);
             }
         }
     }
