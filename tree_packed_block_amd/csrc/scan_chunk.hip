@@ -52,9 +52,6 @@ constexpr int kC = 32;          // tokens per chunk
 // consecutive lanes start in different banks (a stride of 32 floats puts them all on the
 // same ones).
 constexpr int kCP = kC + 4;
-// Row stride (bf16) of the split W and dR rows of the gradient pass: 40 bf16 = 5 pieces
-// of 16 bytes.
-constexpr int kSP = 40;
 constexpr int kWaves = kD / 32; // one wave per 32 value rows (or key columns)
 constexpr int kThr = 64 * kWaves;
 constexpr int kRowB = kD * 2;   // bytes of one bf16 row
@@ -905,21 +902,17 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_dstate_kernel(
 // d log alpha.  Wave w owns value rows [32 w, 32 w + 32) for what runs per value row (W,
 // dR, dV) and key columns [32 w, 32 w + 32) of dQ and dK, which it sums over all value
 // rows itself: W and dR of every wave go through LDS, the states come key-major from
-// global memory as B operands.
+// global memory as B operands.  The two C x C sums over value rows (dR W^T, dO W^T) are
+// one product each over all 128 value rows (waves 0 and 1).  The LDS fits in half a
+// compute unit, so two workgroups share one and overlap each other's loads and barriers.
 namespace {
 struct GradSmem {
     unsigned char K[kC * kRowB];
     unsigned char Q[kC * kRowB];
-    unsigned char V[kC * kRowB];
     unsigned char dO[kC * kRowB];
     float alpha[kC], beta[kC], gam[kC], lg[kC];
     float LG[kC * kC];   // gated K K^T, strict lower, [t][i]
     float M[kC * kC];    // gated Q K^T, lower with diagonal, [t][i]
-    float MT[kC * kCP];  // its transpose
-    // per wave: its value rows' part of sum_v dR_t . W_i (of sum_v dO_t . W_i); slot 0
-    // then holds dA (dM o Gamma)
-    float P[kWaves][kC * kCP];
-    float dM[kWaves][kC * kCP];
     // parts of d L / d (natural log gamma_t) and d L / d beta_t, each written by one lane
     // and added in a fixed order at the end (no atomics: the result does not depend on
     // scheduling): per wave, its value rows' part of every row's terms; the C x C stage's
@@ -927,17 +920,29 @@ struct GradSmem {
     float dgw[kWaves][kC], dbw[kWaves][kC];
     float erow[kC], brow[kC];
     float sxw[kWaves][2];
-    float W[kWaves][kC * kCP];   // per wave: W [t][value row]
-    float dR[kWaves][kC * kCP];  // dR [t][value row]
-    // the same as bf16 high and low parts, split once by the owning wave and read as A
-    // operands by every wave: rows of kSP bf16 (80 bytes, so the rows of 16 consecutive
-    // lanes start in different banks)
-    bf16 WH[kWaves][kC * kSP], WL[kWaves][kC * kSP];
-    bf16 RH[kWaves][kC * kSP], RL[kWaves][kC * kSP];
+    // W and dR of all 128 value rows as bf16 high and low parts, [t][value row]: each wave
+    // writes its value rows' columns, every wave reads rows as A (and B) operands.  The
+    // 16-byte pieces of row t are XOR-swizzled by t % 16 (gr_off), so the rows that 16
+    // consecutive lanes read start in different banks.
+    bf16 WH[kC * kD], WL[kC * kD], RH[kC * kD], RL[kC * kD];
+    union {
+        struct {  // up to the W and dR phase
+            unsigned char V[kC * kRowB];
+            float MT[kC * kCP];  // M transposed
+        } a;
+        struct {  // from the C x C sums on
+            float P[kC * kCP];   // sum_v dR_t . W_i, then dA
+            float dM[kC * kCP];  // sum_v dO_t . W_i, then dM o Gamma
+        } b;
+    } u;
 };
+// Byte offset of value row v in row t of the [t][value row] bf16 arrays above.
+__device__ __forceinline__ int gr_off(int t, int v) {
+    return t * kRowB + (((v >> 3) ^ (t & 15)) << 4) + (v & 7) * 2;
+}
 }  // namespace
 
-__global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
+__global__ __launch_bounds__(kThr, 2) void gdn_chunk_grad_kernel(
     DevPlan P, int c0, int H, const bf16* __restrict__ Qg, const bf16* __restrict__ Kg,
     const bf16* __restrict__ Vg, const float* __restrict__ Ag, const float* __restrict__ Bg,
     const bf16* __restrict__ dOg, const float* __restrict__ prep,
@@ -956,8 +961,6 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
     // S_0 and dS_C of this (chunk, head), key-major [k][v]
     const float* S0g = chunk_states + ((size_t)c * H + h) * kD * kD;
     const float* dSg = dsc + ((size_t)c * H + h) * kD * kD;
-    float* Wl = S.W[w];
-    float* dRl = S.dR[w];
     int tr[4][2];
     tr_offsets(lane, tr);
     // 8 floats at p[0..3] and p[off..off+3], split into bf16 high and low parts
@@ -986,7 +989,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
         for (int bk = 0; bk < 4; ++bk) load_key_major(S0g, bk, dv, g, s0v[bk]);
         put_rows(S.K, tid, rk);
         put_rows(S.Q, tid, rq);
-        put_rows(S.V, tid, rv);
+        put_rows(S.u.a.V, tid, rv);
         put_rows(S.dO, tid, ro);
         if (tid < 2 * kC)
             (tid < kC ? S.alpha : S.beta)[ta] = ta < nt ? gate : (tid < kC ? 1.f : 0.f);
@@ -1019,7 +1022,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
             const float mv = i <= t ? aqk[jj] * gt : 0.f;
             S.LG[t * kC + i] = i < t ? akk[jj] * gt : 0.f;
             S.M[t * kC + i] = mv;
-            S.MT[i * kCP + t] = mv;
+            S.u.a.MT[i * kCP + t] = mv;
         }
     }
     f32x16 X = zero16(), Y = zero16(), X2 = zero16(), Y2 = zero16();
@@ -1074,7 +1077,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             xs[j] = X[j] * bg[j];
-            vx[j] = tile_at(S.V, acc_row(j, g), dv) - gam[j] * X[j];
+            vx[j] = tile_at(S.u.a.V, acc_row(j, g), dv) - gam[j] * X[j];
         }
         f32x16 Wa = zero16();
 #pragma unroll
@@ -1096,7 +1099,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             bf16x8 mhi, mlo;
-            ld_split(S.MT + n * kCP + 16 * kk + 4 * g, 8, mhi, mlo, 1.f);
+            ld_split(S.u.a.MT + n * kCP + 16 * kk + 4 * g, 8, mhi, mlo, 1.f);
             const bf16x8 bo = rd_tr(S.dO, tr, w, kk);
             tA = mfma_32x32x16(mhi, bo, tA);
             tA = mfma_32x32x16(mlo, bo, tA);
@@ -1131,18 +1134,13 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
 #pragma unroll
         for (int j = 0; j < 16; ++j) dr[j] = dRa[j];
     }
-    // ---- W and dR to LDS ([t][value row]); dV; the beta and gate terms per row
+    // ---- dV; the beta and gate terms per row; W and dR to LDS
     float sx = 0.f;  // terms of d L / d log gamma_C: this lane's part
     const int rs = H * kD;
     {
         float dvv[16];
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-            const int t = acc_row(jj, g);
-            Wl[t * kCP + n] = wv[jj];
-            dRl[t * kCP + n] = dr[jj];
-            dvv[jj] = S.beta[t] * dr[jj];
-        }
+        for (int jj = 0; jj < 16; ++jj) dvv[jj] = S.beta[acc_row(jj, g)] * dr[jj];
         const __amdgpu_buffer_rsrc_t r = chunk_rows(dVg + (tok0 * H + h) * kD, nt, rs);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -1160,7 +1158,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
             const float x = wv[jj] * tb[jj];
             sx += x;
             // -beta_t gamma_t <dR_t, X_t> - x_t, with gamma_t X_t = V_t - vx_t
-            rdg[jj] = -S.beta[t] * dr[jj] * (tile_at(S.V, t, dv) - vx[jj]) - x;
+            rdg[jj] = -S.beta[t] * dr[jj] * (tile_at(S.u.a.V, t, dv) - vx[jj]) - x;
         }
         half_sum16(rdb);
         half_sum16(rdg);
@@ -1173,34 +1171,61 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
             }
         }
     }
-    wait_lds();
-    __builtin_amdgcn_wave_barrier();
-    // ---- sums over this wave's value rows: dR W^T and dO W^T (C x C)
+    // W and dR of this wave's value rows (column dv) split into bf16 parts and written into
+    // rows t = acc_row(j, g) of the shared arrays (the pairs of a lane's rows converted
+    // together)
     {
-        f32x16 pp = zero16(), pm = zero16();
+        unsigned char* const wh = reinterpret_cast<unsigned char*>(S.WH);
+        unsigned char* const wl = reinterpret_cast<unsigned char*>(S.WL);
+        unsigned char* const rh = reinterpret_cast<unsigned char*>(S.RH);
+        unsigned char* const rl = reinterpret_cast<unsigned char*>(S.RL);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 ah, al, bh, bl;
-            ld_split(dRl + n * kCP + 16 * ks + 8 * g, 4, ah, al, 1.f);
-            ld_split(Wl + n * kCP + 16 * ks + 8 * g, 4, bh, bl, 1.f);
-            const int so = n * kSP + 16 * ks + 8 * g;  // row t = n, this lane's 8 value rows
-            *reinterpret_cast<bf16x8*>(S.RH[w] + so) = ah;
-            *reinterpret_cast<bf16x8*>(S.RL[w] + so) = al;
-            *reinterpret_cast<bf16x8*>(S.WH[w] + so) = bh;
-            *reinterpret_cast<bf16x8*>(S.WL[w] + so) = bl;
-            pp = mfma_32x32x16(ah, bh, pp);
-            pp = mfma_32x32x16(ah, bl, pp);
-            pp = mfma_32x32x16(al, bh, pp);
-            const bf16x8 ao = rd8(S.dO, n, 32 * w + 16 * ks + 8 * g);
-            pm = mfma_32x32x16(ao, bh, pm);
-            pm = mfma_32x32x16(ao, bl, pm);
+        for (int i = 0; i < 8; ++i) {
+            const int o0 = gr_off(acc_row(2 * i, g), dv), o1 = gr_off(acc_row(2 * i + 1, g), dv);
+            unsigned a, b;
+            split_pair(wv[2 * i], wv[2 * i + 1], a, b);
+            *reinterpret_cast<unsigned short*>(wh + o0) = (unsigned short)a;
+            *reinterpret_cast<unsigned short*>(wh + o1) = (unsigned short)(a >> 16);
+            *reinterpret_cast<unsigned short*>(wl + o0) = (unsigned short)b;
+            *reinterpret_cast<unsigned short*>(wl + o1) = (unsigned short)(b >> 16);
+            split_pair(dr[2 * i], dr[2 * i + 1], a, b);
+            *reinterpret_cast<unsigned short*>(rh + o0) = (unsigned short)a;
+            *reinterpret_cast<unsigned short*>(rh + o1) = (unsigned short)(a >> 16);
+            *reinterpret_cast<unsigned short*>(rl + o0) = (unsigned short)b;
+            *reinterpret_cast<unsigned short*>(rl + o1) = (unsigned short)(b >> 16);
         }
+    }
+    wait_lds();
+    barrier();  // every wave's W and dR are in LDS; V and M^T are no longer read
+    // ---- the C x C sums over all value rows: P = dR W^T (wave 0), dM = dO W^T (wave 1).
+    // A operand: rows t = n with 8 value rows per k-step half; B operand: W^T, column i = n
+    // (the same reads of W's row i).
+    if (w < 2) {
+        f32x16 acc = zero16();
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-            const int t = acc_row(jj, g);
-            S.P[w][t * kCP + n] = pp[jj];
-            S.dM[w][t * kCP + n] = pm[jj];
+        for (int ks = 0; ks < kD / 16; ++ks) {
+            const int off = gr_off(n, 16 * ks + 8 * g);
+            const bf16x8 bh = *reinterpret_cast<const bf16x8*>(
+                reinterpret_cast<const unsigned char*>(S.WH) + off);
+            const bf16x8 bl = *reinterpret_cast<const bf16x8*>(
+                reinterpret_cast<const unsigned char*>(S.WL) + off);
+            if (w == 0) {
+                const bf16x8 ah = *reinterpret_cast<const bf16x8*>(
+                    reinterpret_cast<const unsigned char*>(S.RH) + off);
+                const bf16x8 al = *reinterpret_cast<const bf16x8*>(
+                    reinterpret_cast<const unsigned char*>(S.RL) + off);
+                acc = mfma_32x32x16(ah, bh, acc);
+                acc = mfma_32x32x16(ah, bl, acc);
+                acc = mfma_32x32x16(al, bh, acc);
+            } else {
+                const bf16x8 ao = rd8(S.dO, n, 16 * ks + 8 * g);
+                acc = mfma_32x32x16(ao, bh, acc);
+                acc = mfma_32x32x16(ao, bl, acc);
+            }
         }
+        float* const dst = w == 0 ? S.u.b.P : S.u.b.dM;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) dst[acc_row(jj, g) * kCP + n] = acc[jj];
     }
     // ---- dQ = dY S_0 and dK = dX S_0 + diag(gamma_C / gamma) W dS_C for key columns
     // kc = 32 w + n, summed over all 128 value rows: A operands (rows t) from every wave's
@@ -1209,8 +1234,6 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
     // dO and dX = -diag(beta gamma) dR and the gamma_C / gamma of the W term scale the
     // products' rows afterwards (fx, fw, fq), so the A operands need no scaling or splitting
     // here (dO is bf16 already).
-    wait_lds();
-    barrier();  // every wave's W and dR are in LDS
     f32x16 fq = zero16(), fk;
     {
         f32x16 fx = zero16(), fw = zero16();
@@ -1230,11 +1253,15 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
             split8p(d8, dh, dl);
 #pragma unroll
             for (int e = 0; e < 8; ++e) sx += gC * s8[e] * d8[e];  // gamma_C <dS_C, S_0>: each element once
-            const int so = n * kSP + 16 * (ks & 1) + 8 * g;  // wave ks / 2's value rows
-            const bf16x8 xh = *reinterpret_cast<const bf16x8*>(S.RH[ks >> 1] + so);
-            const bf16x8 xl = *reinterpret_cast<const bf16x8*>(S.RL[ks >> 1] + so);
-            const bf16x8 wh = *reinterpret_cast<const bf16x8*>(S.WH[ks >> 1] + so);
-            const bf16x8 wl = *reinterpret_cast<const bf16x8*>(S.WL[ks >> 1] + so);
+            const int so = gr_off(n, 16 * ks + 8 * g);  // row t = n, 8 value rows
+            const bf16x8 xh = *reinterpret_cast<const bf16x8*>(
+                reinterpret_cast<const unsigned char*>(S.RH) + so);
+            const bf16x8 xl = *reinterpret_cast<const bf16x8*>(
+                reinterpret_cast<const unsigned char*>(S.RL) + so);
+            const bf16x8 wh = *reinterpret_cast<const bf16x8*>(
+                reinterpret_cast<const unsigned char*>(S.WH) + so);
+            const bf16x8 wl = *reinterpret_cast<const bf16x8*>(
+                reinterpret_cast<const unsigned char*>(S.WL) + so);
             const bf16x8 o8 = rd8(S.dO, n, 16 * ks + 8 * g);
             fx = mfma_32x32x16(xh, sh, fx);
             fx = mfma_32x32x16(xh, sl, fx);
@@ -1266,15 +1293,8 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
         const int t = tid >> 3, q = tid & 7;
         const float lgt = S.lg[t], btt = S.beta[t];
         float erow = 0.f, brow = 0.f;
-        float4 ps = *reinterpret_cast<const float4*>(S.P[0] + t * kCP + 4 * q);
-        float4 ms = *reinterpret_cast<const float4*>(S.dM[0] + t * kCP + 4 * q);
-#pragma unroll
-        for (int ww = 1; ww < kWaves; ++ww) {
-            const float4 a = *reinterpret_cast<const float4*>(S.P[ww] + t * kCP + 4 * q);
-            const float4 b = *reinterpret_cast<const float4*>(S.dM[ww] + t * kCP + 4 * q);
-            ps.x += a.x; ps.y += a.y; ps.z += a.z; ps.w += a.w;
-            ms.x += b.x; ms.y += b.y; ms.z += b.z; ms.w += b.w;
-        }
+        const float4 ps = *reinterpret_cast<const float4*>(S.u.b.P + t * kCP + 4 * q);
+        const float4 ms = *reinterpret_cast<const float4*>(S.u.b.dM + t * kCP + 4 * q);
         const float psum[4] = {ps.x, ps.y, ps.z, ps.w}, msum[4] = {ms.x, ms.y, ms.z, ms.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1288,8 +1308,8 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
             brow += dbl * lgv;
             erow += ek + eq;
             S.LG[t * kC + i] = i < t ? ek + eq : 0.f;  // (taken from gamma_i's term)
-            S.P[0][t * kCP + i] = btt * dbl * gt;  // dA (strict lower)
-            S.dM[0][t * kCP + i] = dmv * gt;       // dM o Gamma (lower with diagonal)
+            S.u.b.P[t * kCP + i] = btt * dbl * gt;  // dA (strict lower)
+            S.u.b.dM[t * kCP + i] = dmv * gt;       // dM o Gamma (lower with diagonal)
         }
         erow = sum8(erow);
         brow = sum8(brow);
@@ -1309,13 +1329,13 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_grad_kernel(
             const bf16x8 bqv = rd_tr(S.Q, tr, w, kk);
             // rows i of this k-step in the accumulator order
             bf16x8 qh, ql, ah, al, th, tl;
-            ld_split(S.dM[0] + n * kCP + 16 * kk + 4 * g, 8, qh, ql, 1.f);
+            ld_split(S.u.b.dM + n * kCP + 16 * kk + 4 * g, 8, qh, ql, 1.f);
             float a8[8], t8[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int i = 16 * kk + 8 * (e >> 2) + 4 * g + (e & 3);
-                a8[e] = S.P[0][n * kCP + i] + S.P[0][i * kCP + n];
-                t8[e] = S.dM[0][i * kCP + n];
+                a8[e] = S.u.b.P[n * kCP + i] + S.u.b.P[i * kCP + n];
+                t8[e] = S.u.b.dM[i * kCP + n];
             }
             split8p(a8, ah, al);
             split8p(t8, th, tl);
