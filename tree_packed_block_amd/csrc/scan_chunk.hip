@@ -625,7 +625,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
         // X = K S_0^T and Y = Q S_0^T for this wave's value rows (A = K, Q rows with the
         // k values in the accumulator's row order; B = the state's hi and lo parts, in
         // separate accumulators: four independent chains).
-        f32x16 X = zero16(), Y = zero16(), X2 = zero16(), Y2 = zero16();
+        f32x16 X = zero16(), Y = zero16();
 #pragma unroll
         for (int bk = 0; bk < 4; ++bk)
 #pragma unroll
@@ -639,49 +639,45 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
                 const bf16x8 ak = rd_perm(B.K, n, k0);
                 const bf16x8 aq = rd_perm(B.Q, n, k0);
                 X = mfma_32x32x16(ak, shi, X);
-                X2 = mfma_32x32x16(ak, slo, X2);
                 Y = mfma_32x32x16(aq, shi, Y);
-                Y2 = mfma_32x32x16(aq, slo, Y2);
+                X = mfma_32x32x16(ak, slo, X);
+                Y = mfma_32x32x16(aq, slo, Y);
             }
         // W = U - T diag(beta gamma) X
         float xs[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) xs[j] = (X[j] + X2[j]) * cbg[j];
-        // (the three products of the split operands in separate accumulators: chains of 2)
-        f32x16 Wa = zero16(), Wb = zero16(), Wc = zero16();
+        for (int j = 0; j < 16; ++j) xs[j] = X[j] * cbg[j];
+        f32x16 Wa = zero16();
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             bf16x8 th, tl, xh, xl;
             ld_split_rec(TMG, lane, kk, th, tl);
             split8(xs, kk, xh, xl);
             Wa = mfma_32x32x16(th, xh, Wa);
-            Wb = mfma_32x32x16(th, xl, Wb);
-            Wc = mfma_32x32x16(tl, xh, Wc);
+            Wa = mfma_32x32x16(th, xl, Wa);
+            Wa = mfma_32x32x16(tl, xh, Wa);
         }
         float wv[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) wv[j] = cu[j] - (Wa[j] + Wb[j] + Wc[j]);
+        for (int j = 0; j < 16; ++j) wv[j] = cu[j] - Wa[j];
         // O = diag(gamma) Y + M W
-        f32x16 MW = zero16(), MWb = zero16(), MWc = zero16();
+        f32x16 MW = zero16();
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             bf16x8 mh, ml, wh, wl;
             ld_split_rec(TMG + (kRecM - kRecT), lane, kk, mh, ml);
             split8(wv, kk, wh, wl);
             MW = mfma_32x32x16(mh, wh, MW);
-            MWb = mfma_32x32x16(mh, wl, MWb);
-            MWc = mfma_32x32x16(ml, wh, MWc);
+            MW = mfma_32x32x16(mh, wl, MW);
+            MW = mfma_32x32x16(ml, wh, MW);
         }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) MW[j] += MWb[j] + MWc[j];
         if (Og != nullptr) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 typedef __attribute__((ext_vector_type(2))) float f32x2;
                 const int j = 2 * i;
                 ostash[i] = __builtin_convertvector(
-                    ((f32x2){cgam[j] * (Y[j] + Y2[j]) + MW[j],
-                             cgam[j + 1] * (Y[j + 1] + Y2[j + 1]) + MW[j + 1]}),
+                    ((f32x2){cgam[j] * Y[j] + MW[j], cgam[j + 1] * Y[j + 1] + MW[j + 1]}),
                     bf16x2);
             }
             o_ptr = Og + (tok0 * H + h) * kD;
@@ -804,7 +800,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_dstate_kernel(
         const float gC = G[kGam + nt - 1];
 
         // dW = M^T dO + diag(gamma_C / gamma) K dS_C^T
-        f32x16 tA = zero16(), tB = zero16(), tB2 = zero16();
+        f32x16 tA = zero16(), tB = zero16();
         bf16x8 o8[2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -825,25 +821,23 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_dstate_kernel(
                 split8p(x, shi, slo);
                 const bf16x8 ak = rd_perm(B.K, n, 32 * bk + 16 * kh + 4 * g);
                 tB = mfma_32x32x16(ak, shi, tB);
-                tB2 = mfma_32x32x16(ak, slo, tB2);
+                tB = mfma_32x32x16(ak, slo, tB);
             }
         float dw[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) dw[j] = tA[j] + cig[j] * (tB[j] + tB2[j]);
+        for (int j = 0; j < 16; ++j) dw[j] = tA[j] + cig[j] * tB[j];
         // dR = T^T dW; dX = -diag(beta gamma) dR, dY = diag(gamma) dO (rows past nt of the
         // staged dO repeat the last row: masked here; dX vanishes there with beta)
-        f32x16 dR = zero16(), dRb = zero16(), dRc = zero16();
+        f32x16 dR = zero16();
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             bf16x8 th, tl, wh, wl;
             ld_split_rec(G + (kRecTT - kRecG), lane, kk, th, tl);
             split8(dw, kk, wh, wl);
             dR = mfma_32x32x16(th, wh, dR);
-            dRb = mfma_32x32x16(th, wl, dRb);
-            dRc = mfma_32x32x16(tl, wh, dRc);
+            dR = mfma_32x32x16(th, wl, dR);
+            dR = mfma_32x32x16(tl, wh, dR);
         }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) dR[j] += dRb[j] + dRc[j];
         bf16x8 xh[2], xl[2], yh[2], yl[2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -1025,7 +1019,7 @@ __global__ __launch_bounds__(kThr, 2) void gdn_chunk_grad_kernel(
             S.u.a.MT[i * kCP + t] = mv;
         }
     }
-    f32x16 X = zero16(), Y = zero16(), X2 = zero16(), Y2 = zero16();
+    f32x16 X = zero16(), Y = zero16();
 #pragma unroll
     for (int bk = 0; bk < 4; ++bk) {
 #pragma unroll
@@ -1036,20 +1030,15 @@ __global__ __launch_bounds__(kThr, 2) void gdn_chunk_grad_kernel(
             const bf16x8 ak = rd_perm(S.K, n, k0);
             const bf16x8 aq = rd_perm(S.Q, n, k0);
             X = mfma_32x32x16(ak, shi, X);
-            X2 = mfma_32x32x16(ak, slo, X2);
             Y = mfma_32x32x16(aq, shi, Y);
-            Y2 = mfma_32x32x16(aq, slo, Y2);
+            X = mfma_32x32x16(ak, slo, X);
+            Y = mfma_32x32x16(aq, slo, Y);
         }
     }
     // dS_C as the B operands of dW (issued here, used two phases later)
     float dsv[4][16];
 #pragma unroll
     for (int bk = 0; bk < 4; ++bk) load_key_major(dSg, bk, dv, g, dsv[bk]);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        X[j] += X2[j];
-        Y[j] += Y2[j];
-    }
     float gam[16], bg[16], ig[16];
     ld16f(rec + kRecG + kGam + 4 * g, 8, gam);
     ld16f(rec + kRecG + kBG + 4 * g, 8, bg);
@@ -1095,7 +1084,7 @@ __global__ __launch_bounds__(kThr, 2) void gdn_chunk_grad_kernel(
     // ---- dW = M^T dO + diag(gamma_C / gamma) K dS_C^T; dR = T^T dW
     float dr[16], tb[16];
     {
-        f32x16 tA = zero16(), tB = zero16(), tB2 = zero16();
+        f32x16 tA = zero16(), tB = zero16();
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             bf16x8 mhi, mlo;
@@ -1112,13 +1101,13 @@ __global__ __launch_bounds__(kThr, 2) void gdn_chunk_grad_kernel(
                 split8(dsv[bk], kh, shi, slo);
                 const bf16x8 ak = rd_perm(S.K, n, 32 * bk + 16 * kh + 4 * g);
                 tB = mfma_32x32x16(ak, shi, tB);
-                tB2 = mfma_32x32x16(ak, slo, tB2);
+                tB = mfma_32x32x16(ak, slo, tB);
             }
         }
         float dw[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            tb[j] = (tB[j] + tB2[j]) * ig[j];
+            tb[j] = tB[j] * ig[j];
             dw[j] = tA[j] + tb[j];
         }
         f32x16 dRa = zero16();
