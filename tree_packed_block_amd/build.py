@@ -22,8 +22,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liboctopus_dag.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-HIP_SOURCES = ["fwd.hip", "bwd.hip", "decode.hip", "extend.hip", "rope.hip", "scan_chunk.hip",
-               "noalloc.hip"]
+HIP_SOURCES = ["fwd.hip", "bwd.hip", "dq.hip", "decode.hip", "extend.hip", "rope.hip",
+               "scan_chunk.hip", "noalloc.hip"]
 CXX_SOURCES = ["plan.cpp", "api.cpp"]
 
 HIPCC_FLAGS = [
@@ -32,13 +32,19 @@ HIPCC_FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 # Per-source code-generation options.  The kernels never produce NaN on purpose, so
-# fmaxf need not quiet NaN operands (that costs one extra instruction per maximum).  The
-# scan kernels fit in the 256 architectural registers with their MFMA accumulators there
-# too; in the default form the compiler puts those in AGPRs and copies them back and
-# forth for every VALU operation on the state.
-HIP_FILE_FLAGS: dict = {"fwd.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"],
-                        "extend.hip": ["-fno-honor-nans"],
-                        "scan_chunk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# fmaxf need not quiet NaN operands (that costs one extra instruction per maximum).
+# VGPR-form MFMAs keep the accumulators in the architectural registers: in the default
+# form the compiler puts them in AGPRs wherever a kernel needs more than 256 registers or
+# runs one head per workgroup, and copies them back and forth around every VALU operation
+# on them (the two-head attention kernels compile to the same code either way).  The
+# dK/dV pass (bwd.hip) is the exception: it needs more than 256 registers and is faster
+# with its accumulators in AGPRs.
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+HIP_FILE_FLAGS: dict = {"fwd.hip": ["-fno-honor-nans", *_VGPR_FORM],
+                        "dq.hip": _VGPR_FORM,
+                        "decode.hip": ["-fno-honor-nans", *_VGPR_FORM],
+                        "extend.hip": ["-fno-honor-nans", *_VGPR_FORM],
+                        "scan_chunk.hip": _VGPR_FORM}
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
              "-D__HIP_PLATFORM_AMD__"]
 

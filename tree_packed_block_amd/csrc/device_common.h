@@ -42,6 +42,21 @@ __device__ __forceinline__ bf16x8 zero8() {
 __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+// x as the sum of three bf16 values (the error is below 2^-24 |x|), in slots 0..2 of
+// an MFMA operand; lanes of the upper half (k values 8..15) carry zeros.  The backward
+// passes add a row's -LSE2 and -Delta to its scores through this one extra k-step.
+__device__ __forceinline__ bf16x8 split3(float x, bool on) {
+    x = on ? fmaxf(x, -1e30f) : 0.f;  // a padded row's -inf becomes a finite -1e30
+    const bf16 h = (bf16)x;
+    const float r1 = x - (float)h;
+    const bf16 m = (bf16)r1;
+    const bf16 l = (bf16)(r1 - (float)m);
+    bf16x8 v = zero8();
+    v[0] = h;
+    v[1] = m;
+    v[2] = l;
+    return v;
+}
 __device__ __forceinline__ f32x16 zero16() {
     f32x16 z;
 #pragma unroll

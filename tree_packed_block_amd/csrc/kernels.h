@@ -48,6 +48,9 @@ struct RopeFreq {
 RopeFreq rope_freq(int D, float base);
 
 constexpr int kBq = 128;  // query rows per tile
+// Rows of the backward's LSE2 and Delta workspace per head: T rounded up to whole query
+// tiles (the padded rows hold LSE2 = +inf and Delta = 0).
+__host__ __device__ inline int padded_rows(int T) { return (T + kBq - 1) / kBq * kBq; }
 constexpr int kBk = 64;   // keys per KV tile
 
 // V re-laid per 64-key tile so that the forward's MFMA operands which contract over
