@@ -387,7 +387,7 @@ def test_new_entry_points_reject_bad_arguments_before_any_launch():
     assert tpb.lib().octopus_gdn_workspace_bytes(p.handle, 2, 64, 128) == 0
     assert tpb.lib().octopus_gdn_bwd_workspace_bytes(p.handle, 0, 128, 128) == 0
     # both children fork from the root at offset 256: one checkpoint slot; chunks end every
-    # 32 own tokens and at every fork offset; one 8,448-float record per (chunk, head)
+    # 32 own tokens and at every fork offset; one 5,376-float record per (chunk, head)
     br = np.asarray(dag.branches).reshape(-1, 4)
     n_chunks = 0
     for b, (_, _, _, ln) in enumerate(br):
@@ -395,11 +395,11 @@ def test_new_entry_points_reject_bad_arguments_before_any_launch():
                                               if par == b and 0 < f < ln}
         n_chunks += len(cuts) + 1 if ln > 0 else 0
     state = 2 * 128 * 128 * 4
-    assert tpb.gdn_workspace_bytes(p, 2) == 1 * state + n_chunks * 2 * 8448 * 4
+    assert tpb.gdn_workspace_bytes(p, 2) == 1 * state + n_chunks * 2 * 5376 * 4
     # backward: checkpoint slots, one initial-state gradient per branch, two state sets
     # per chunk, the records
     assert tpb.gdn_bwd_workspace_bytes(p, 2) == (1 + len(br) + 2 * n_chunks) * state + \
-        n_chunks * 2 * 8448 * 4
+        n_chunks * 2 * 5376 * 4
     # extend
     assert _code(L.octopus_paged_mount_extend(tpb.BF16, 1, 16, 4, 96, 64, 0.0, fake, fake, fake,
                                               4, fake, 1, fake, fake, fake, fake, fake, fake,

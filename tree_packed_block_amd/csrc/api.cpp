@@ -609,7 +609,7 @@ int gdn_forward_run(const octopus_plan* plan, int32_t H, const void* q, const vo
     // workgroups fill every unit (they become ready together when the first records land).
     // (the transposed record blocks only when a backward follows: chunk_states kept)
     const bool with_t = chunk_states != nullptr;
-    hipError_t e = octo::launch_gdn_chunk_prep(dp, 0, first, H, with_t, q, k, v, alpha, beta,
+    hipError_t e = octo::launch_gdn_chunk_prep(dp, 0, first, H, with_t, q, k, alpha, beta,
                                                prep, st);
     if (e != hipSuccess) return hip_fail(e, "scan prep launch");
     SideFork side(st);
@@ -618,19 +618,19 @@ int gdn_forward_run(const octopus_plan* plan, int32_t H, const void* q, const vo
         e = side.fork(s2);
         if (e != hipSuccess) return hip_fail(e, "scan side stream");
     }
-    e = octo::launch_gdn_chunk_fwd(dp, lp[0], lp[1] - lp[0], H, q, k, prep, o, slots,
+    e = octo::launch_gdn_chunk_fwd(dp, lp[0], lp[1] - lp[0], H, q, k, v, prep, o, slots,
                                    chunk_states, st);
     if (e != hipSuccess) return hip_fail(e, "scan forward launch");
     if (rest > 0) {
-        e = octo::launch_gdn_chunk_prep(dp, first, rest, H, with_t, q, k, v, alpha, beta, prep,
+        e = octo::launch_gdn_chunk_prep(dp, first, rest, H, with_t, q, k, alpha, beta, prep,
                                         s2);
         if (e != hipSuccess) return hip_fail(e, "scan prep launch");
     }
     e = side.join();
     if (e != hipSuccess) return hip_fail(e, "scan side stream");
     for (size_t l = 1; l + 1 < lp.size(); ++l) {
-        e = octo::launch_gdn_chunk_fwd(dp, lp[l], lp[l + 1] - lp[l], H, q, k, prep, o, slots,
-                                       chunk_states, st);
+        e = octo::launch_gdn_chunk_fwd(dp, lp[l], lp[l + 1] - lp[l], H, q, k, v, prep, o,
+                                       slots, chunk_states, st);
         if (e != hipSuccess) return hip_fail(e, "scan forward launch");
     }
     return OCTOPUS_OK;
@@ -786,17 +786,17 @@ int gdn_backward_full(const octopus_plan* plan, int32_t H, const void* q, const 
     const GdnBwdWs w = gdn_bwd_ws(plan, H, ws);
     const int32_t first = lc[1];
     const int64_t rest = plan->p.n_chunks - first;
-    hipError_t e = octo::launch_gdn_chunk_prep(dp, 0, first, H, true, q, k, v, alpha, beta,
+    hipError_t e = octo::launch_gdn_chunk_prep(dp, 0, first, H, true, q, k, alpha, beta,
                                                w.prep, st);
     if (e != hipSuccess) return hip_fail(e, "scan prep launch");
     SideFork side(st);
     hipStream_t s2 = nullptr;
     e = side.fork(s2);
     if (e != hipSuccess) return hip_fail(e, "scan side stream");
-    e = octo::launch_gdn_chunk_fwd(dp, lp[0], lp[1] - lp[0], H, q, k, w.prep, nullptr, w.slots,
-                                   w.chunks, st);
+    e = octo::launch_gdn_chunk_fwd(dp, lp[0], lp[1] - lp[0], H, q, k, v, w.prep, nullptr,
+                                   w.slots, w.chunks, st);
     if (e != hipSuccess) return hip_fail(e, "scan forward launch");
-    e = octo::launch_gdn_chunk_prep(dp, first, rest, H, true, q, k, v, alpha, beta, w.prep, s2);
+    e = octo::launch_gdn_chunk_prep(dp, first, rest, H, true, q, k, alpha, beta, w.prep, s2);
     if (e == hipSuccess) e = side.mark();
     if (e != hipSuccess) return hip_fail(e, "scan prep launch");
     for (size_t l = lp.size() - 1; l-- > 0;) {
@@ -807,7 +807,7 @@ int gdn_backward_full(const octopus_plan* plan, int32_t H, const void* q, const 
     e = side.wait_mark();
     if (e != hipSuccess) return hip_fail(e, "scan side stream");
     for (size_t l = 1; l + 1 < lp.size(); ++l) {
-        e = octo::launch_gdn_chunk_fwd(dp, lp[l], lp[l + 1] - lp[l], H, q, k, w.prep, nullptr,
+        e = octo::launch_gdn_chunk_fwd(dp, lp[l], lp[l + 1] - lp[l], H, q, k, v, w.prep, nullptr,
                                        w.slots, w.chunks, st);
         if (e != hipSuccess) return hip_fail(e, "scan forward launch");
     }

@@ -124,11 +124,11 @@ hipError_t launch_rope2(bool bf16, int rows, int D, float base, bool inverse,
 // [c][H][128][128].
 size_t gdn_prep_floats(int64_t n_chunks, int H);
 hipError_t launch_gdn_chunk_prep(const DevPlan& p, int c0, int64_t n_chunks, int H, bool with_t,
-                                 const void* q, const void* k, const void* v, const float* alpha,
+                                 const void* q, const void* k, const float* alpha,
                                  const float* beta, float* prep, hipStream_t s);
 hipError_t launch_gdn_chunk_fwd(const DevPlan& p, int l0, int n_br, int H, const void* q,
-                                const void* k, const float* prep, void* o, float* states,
-                                float* chunk_states, hipStream_t s);
+                                const void* k, const void* v, const float* prep, void* o,
+                                float* states, float* chunk_states, hipStream_t s);
 // Backward: the state gradient of the branches level_br[l0 .. l0 + n_br) in reverse
 // (levels deepest first), written at every chunk's end into dsc [c][H][128][128]
 // (key-major); dkids [nb][H][128][128] float32: every child's initial-state gradient,

@@ -56,21 +56,20 @@ constexpr int kWaves = kD / 32; // one wave per 32 value rows (or key columns)
 constexpr int kThr = 64 * kWaves;
 constexpr int kRowB = kD * 2;   // bytes of one bf16 row
 
-// Per (chunk, head) record written by the prep kernel.  U in float32 "lane order"
-// [4][64 lanes][4] (element j = 4 q + r of lane l at (64 q + l) * 4 + r, so that 64 lanes
-// reading one float4 each touch 1 KiB of consecutive bytes); the matrices that only ever
-// enter MFMAs as A operands already split into bf16 high and low parts, "split order"
+// Per (chunk, head) record written by the prep kernel.  The matrices that only ever enter
+// MFMAs as A operands, already split into bf16 high and low parts, "split order"
 // [k-step kk][part][64 lanes][8 bf16] (the 8 values of k-step kk of lane l at 16 l bytes of
-// its 1 KiB block), four blocks per matrix:
-//   U    [4 waves] lane order: U[acc_row(j, g)][32 w + n]      (accumulator order)
+// its 1 KiB block), four blocks per matrix; then float32 vectors:
+//   TB   split order: (T diag(beta))[n][acc_row(j, g)]  (A operand of U = T diag(beta) V,
+//        which the passes that need U form themselves from the chunk's V)
 //   T    split order: T[n][acc_row(j, g)]    (A operand with k in the accumulator's order)
 //   M    split order: M[n][acc_row(j, g)]
 //   G    float32 gamma_t [32], beta_t gamma_t [32], gamma_C / gamma_t [32], unused [160]
 //   TT   split order: T[acc_row(j, g)][n]    (A operand of T^T)
 //   MT   split order: M[acc_row(j, g)][n]
-// The forward reads T, M, G and the backward G, TT, MT as one contiguous block each.
-constexpr int kRecU = 0, kRecT = 4096, kRecM = 5120, kRecG = 6144, kRecTT = 6400,
-              kRecMT = 7424, kRec = 8448;
+// The forward reads TB, T, M, G and the backward G, TT, MT as one contiguous block each.
+constexpr int kRecTB = 0, kRecT = 1024, kRecM = 2048, kRecG = 3072, kRecTT = 3328,
+              kRecMT = 4352, kRec = 5376;
 constexpr int kGam = 0, kBG = 32, kIG = 64;  // offsets inside G
 
 // x0 and x1 as hi + lo, each part a pair of bf16 (element 0 in the low half): hi rounded
@@ -78,7 +77,8 @@ constexpr int kGam = 0, kBG = 32, kIG = 64;  // offsets inside G
 // conversion instruction per part.
 __device__ __forceinline__ void split_pair(float x0, float x1, unsigned& hi, unsigned& lo) {
     typedef __attribute__((ext_vector_type(2))) float f32x2;
-    const unsigned h = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x0, x1}, bf16x2));
+    const unsigned h =
+        __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x0, x1}, bf16x2));
     const float h0 = __builtin_bit_cast(float, h << 16);
     const float h1 = __builtin_bit_cast(float, h & 0xffff0000u);
     hi = h;
@@ -376,7 +376,6 @@ __device__ __forceinline__ float log2_gamma(const float* alpha, int lane) {
 struct PrepSmem {
     unsigned char K[kC * kRowB];
     unsigned char Q[kC * kRowB];
-    unsigned char V[kC * kRowB];
     float alpha[kC], beta[kC];
     float lg[2][kC];    // log2 gamma (one copy per wave that needs it)
     float LG[kC * kC];  // gated K K^T, strict lower, [t][i]
@@ -391,8 +390,7 @@ struct PrepSmem {
 // with_t: also the transposes T^T and M^T, which only the backward reads.
 __global__ __launch_bounds__(kThr) void gdn_chunk_prep_kernel(
     DevPlan P, int c0, int H, bool with_t, const bf16* __restrict__ Qg, const bf16* __restrict__ Kg,
-    const bf16* __restrict__ Vg, const float* __restrict__ Ag, const float* __restrict__ Bg,
-    float* __restrict__ prep) {
+    const float* __restrict__ Ag, const float* __restrict__ Bg, float* __restrict__ prep) {
     __shared__ __attribute__((aligned(1024))) PrepSmem S;
     const int c = c0 + (int)(blockIdx.x / H), h = blockIdx.x % H;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -403,10 +401,9 @@ __global__ __launch_bounds__(kThr) void gdn_chunk_prep_kernel(
     float* rec = prep + ((size_t)c * H + h) * kRec;
 
     {
-        bf16x8 rk[2], rq[2], rv[2];
+        bf16x8 rk[2], rq[2];
         fetch_rows(Kg, tok0, nt, H, h, tid, rk);
         fetch_rows(Qg, tok0, nt, H, h, tid, rq);
-        fetch_rows(Vg, tok0, nt, H, h, tid, rv);
         if (tid < 2 * kC) {
             const int t = tid & (kC - 1);
             (tid < kC ? S.alpha : S.beta)[t] =
@@ -414,7 +411,6 @@ __global__ __launch_bounds__(kThr) void gdn_chunk_prep_kernel(
         }
         put_rows(S.K, tid, rk);
         put_rows(S.Q, tid, rq);
-        put_rows(S.V, tid, rv);
     }
     wait_lds();
     barrier();
@@ -469,32 +465,21 @@ __global__ __launch_bounds__(kThr) void gdn_chunk_prep_kernel(
     wait_lds();
     barrier();
 
-    // U = (T diag(beta)) V for value columns 32 w + n: A = T rows n with the k values in
-    // the accumulator's row order, B = V read transposed (exact).
-    int tr[4][2];
-    tr_offsets(lane, tr);
-    float trow[16], brow[16];
-    ld16f(S.T + n * kCP + 4 * g, 8, trow);  // T[n][acc_row(j, g)]
-    ld16f(S.beta + 4 * g, 8, brow);
-    f32x16 u = zero16();
+    // The split blocks of T diag(beta) (wave 0), T (wave 2) and M (wave 3): rows n with the
+    // k values in the accumulator's row order.
+    if (w == 0 || w == 2) {
+        float trow[16];
+        ld16f(S.T + n * kCP + 4 * g, 8, trow);  // T[n][acc_row(j, g)]
+        if (w == 0) {
+            float brow[16];
+            ld16f(S.beta + 4 * g, 8, brow);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 ah, al;
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = trow[8 * kk + e] * brow[8 * kk + e];
-        split8p(x, ah, al);
-        const bf16x8 bv = rd_tr(S.V, tr, w, kk);
-        u = mfma_32x32x16(ah, bv, u);
-        u = mfma_32x32x16(al, bv, u);
+            for (int j = 0; j < 16; ++j) trow[j] *= brow[j];
+            st_split(rec + kRecTB, lane, trow);
+        } else {
+            st_split(rec + kRecT, lane, trow);
+        }
     }
-    {
-        float uv[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) uv[j] = u[j];
-        st16f(rec + kRecU + (w * 4 * 64 + lane) * 4, 64 * 4, uv);
-    }
-    if (w == 2) st_split(rec + kRecT, lane, trow);
     if (w == 3) {
         float mrow[16];
         ld16f(S.M + n * kCP + 4 * g, 8, mrow);
@@ -502,17 +487,35 @@ __global__ __launch_bounds__(kThr) void gdn_chunk_prep_kernel(
     }
 }
 
+// U = T diag(beta) V for this wave's value columns 32 w + n, in the accumulator's layout
+// (element j: row acc_row(j, g)): A = the record's split T diag(beta) block at tb, B = the
+// chunk's V tile read transposed (exact; the block's columns past the chunk's end are zero).
+__device__ __forceinline__ void form_u(const float* tb, const unsigned char* Vt,
+                                       const int (&tr)[4][2], int w, int lane, float (&u)[16]) {
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 ah, al;
+        ld_split_rec(tb, lane, kk, ah, al);
+        const bf16x8 bv = rd_tr(Vt, tr, w, kk);
+        acc = mfma_32x32x16(ah, bv, acc);
+        acc = mfma_32x32x16(al, bv, acc);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) u[j] = acc[j];
+}
+
 // ---------------------------------------------------------------- forward (sequential)
 
-// LDS of the sequential forward, per buffer: the chunk's K and Q (swizzled tiles), each
-// wave's part of U, and the shared T, M, G block of the record.
+// LDS of the sequential forward, per buffer: the chunk's K, Q and V (swizzled tiles) and
+// the TB, T, M, G block of the record.
 struct FwdBuf {
     unsigned char K[kC * kRowB];
     unsigned char Q[kC * kRowB];
-    float U[kWaves][1024];
-    float TMG[kRecG + 256 - kRecT];  // T, M, G as in the record
+    unsigned char V[kC * kRowB];
+    float TMG[kRecG + 256 - kRecTB];  // TB, T, M, G as in the record
 };
-constexpr int kTMGInst = (kRecG + 256 - kRecT) * 4 / 1024;  // 1 KiB DMA instructions
+constexpr int kTMGInst = (kRecG + 256 - kRecTB) * 4 / 1024;  // 1 KiB DMA instructions
 
 // states: checkpoint slots [n_slots][H][Dv][Dk] float32 (row = value index).
 // chunk_states (may be NULL): the state at the start of every chunk, stored key-major
@@ -520,8 +523,8 @@ constexpr int kTMGInst = (kRecG + 256 - kRecT) * 4 / 1024;  // 1 KiB DMA instruc
 // Og may be NULL (the backward needs the states only).
 __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
     DevPlan P, int l0, int H, const bf16* __restrict__ Qg, const bf16* __restrict__ Kg,
-    const float* __restrict__ prep, bf16* __restrict__ Og, float* __restrict__ states,
-    float* __restrict__ chunk_states) {
+    const bf16* __restrict__ Vg, const float* __restrict__ prep, bf16* __restrict__ Og,
+    float* __restrict__ states, float* __restrict__ chunk_states) {
     __shared__ __attribute__((aligned(1024))) FwdBuf SB[2];
     const int b = ld_const(P.sc_level_br + l0 + blockIdx.x / H);
     const int h = blockIdx.x % H;
@@ -579,12 +582,9 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
         const unsigned base = sb0 + buf * kBufB;
         dma_rows(base + offsetof(FwdBuf, K), Kg, tok0, nt, H, h, tid, w);
         dma_rows(base + offsetof(FwdBuf, Q), Qg, tok0, nt, H, h, tid, w);
+        dma_rows(base + offsetof(FwdBuf, V), Vg, tok0, nt, H, h, tid, w);
         const float* rec = prep + ((size_t)c * H + h) * kRec;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            dma16_s(rec + kRecU + w * 1024, (unsigned)(q * 64 + lane) * 16,
-                    base + offsetof(FwdBuf, U) + w * 4096 + q * 1024);
-        dma_block(base + offsetof(FwdBuf, TMG), rec + kRecT, kTMGInst, w, lane);
+        dma_block(base + offsetof(FwdBuf, TMG), rec + kRecTB, kTMGInst, w, lane);
     };
 
     save_due(0);
@@ -616,11 +616,11 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
 
         const float* TMG = B.TMG;
         float cu[16], cgam[16], cbg[16], cig[16];
-        ld_lane(B.U[w], lane, cu);
-        ld16f(TMG + (kRecG - kRecT) + kGam + 4 * g, 8, cgam);
-        ld16f(TMG + (kRecG - kRecT) + kBG + 4 * g, 8, cbg);
-        ld16f(TMG + (kRecG - kRecT) + kIG + 4 * g, 8, cig);
-        const float gC = TMG[(kRecG - kRecT) + kGam + nt - 1];
+        form_u(TMG, B.V, tr, w, lane, cu);  // (independent of the state)
+        ld16f(TMG + (kRecG - kRecTB) + kGam + 4 * g, 8, cgam);
+        ld16f(TMG + (kRecG - kRecTB) + kBG + 4 * g, 8, cbg);
+        ld16f(TMG + (kRecG - kRecTB) + kIG + 4 * g, 8, cig);
+        const float gC = TMG[(kRecG - kRecTB) + kGam + nt - 1];
 
         // X = K S_0^T and Y = Q S_0^T for this wave's value rows (A = K, Q rows with the
         // k values in the accumulator's row order; B = the state's hi and lo parts, in
@@ -651,7 +651,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             bf16x8 th, tl, xh, xl;
-            ld_split_rec(TMG, lane, kk, th, tl);
+            ld_split_rec(TMG + (kRecT - kRecTB), lane, kk, th, tl);
             split8(xs, kk, xh, xl);
             Wa = mfma_32x32x16(th, xh, Wa);
             Wa = mfma_32x32x16(th, xl, Wa);
@@ -665,7 +665,7 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             bf16x8 mh, ml, wh, wl;
-            ld_split_rec(TMG + (kRecM - kRecT), lane, kk, mh, ml);
+            ld_split_rec(TMG + (kRecM - kRecTB), lane, kk, mh, ml);
             split8(wv, kk, wh, wl);
             MW = mfma_32x32x16(mh, wh, MW);
             MW = mfma_32x32x16(mh, wl, MW);
@@ -1062,7 +1062,7 @@ __global__ __launch_bounds__(kThr, 2) void gdn_chunk_grad_kernel(
     float wv[16], vx[16];
     {
         float xs[16];
-        ld_lane(rec + kRecU + w * 1024, lane, wv);
+        form_u(rec + kRecTB, S.u.a.V, tr, w, lane, wv);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             xs[j] = X[j] * bg[j];
@@ -1240,8 +1240,9 @@ __global__ __launch_bounds__(kThr, 2) void gdn_chunk_grad_kernel(
             bf16x8 sh, sl, dh, dl;
             split8p(s8, sh, sl);
             split8p(d8, dh, dl);
+            // gamma_C <dS_C, S_0>: each element once
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sx += gC * s8[e] * d8[e];  // gamma_C <dS_C, S_0>: each element once
+            for (int e = 0; e < 8; ++e) sx += gC * s8[e] * d8[e];
             const int so = gr_off(n, 16 * ks + 8 * g);  // row t = n, 8 value rows
             const bf16x8 xh = *reinterpret_cast<const bf16x8*>(
                 reinterpret_cast<const unsigned char*>(S.RH) + so);
@@ -1385,21 +1386,21 @@ __global__ __launch_bounds__(kThr, 2) void gdn_chunk_grad_kernel(
 size_t gdn_prep_floats(int64_t n_chunks, int H) { return (size_t)n_chunks * H * kRec; }
 
 hipError_t launch_gdn_chunk_prep(const DevPlan& p, int c0, int64_t n_chunks, int H, bool with_t,
-                                 const void* q, const void* k, const void* v, const float* alpha,
+                                 const void* q, const void* k, const float* alpha,
                                  const float* beta, float* prep, hipStream_t s) {
     if (n_chunks <= 0) return hipSuccess;
     hipLaunchKernelGGL(gdn_chunk_prep_kernel, dim3((unsigned)(n_chunks * H)), dim3(kThr), 0, s,
-                       p, c0, H, with_t, (const bf16*)q, (const bf16*)k, (const bf16*)v, alpha, beta,
-                       prep);
+                       p, c0, H, with_t, (const bf16*)q, (const bf16*)k, alpha, beta, prep);
     return hipGetLastError();
 }
 
 hipError_t launch_gdn_chunk_fwd(const DevPlan& p, int l0, int n_br, int H, const void* q,
-                                const void* k, const float* prep, void* o, float* states,
-                                float* chunk_states, hipStream_t s) {
+                                const void* k, const void* v, const float* prep, void* o,
+                                float* states, float* chunk_states, hipStream_t s) {
     if (n_br <= 0) return hipSuccess;
     hipLaunchKernelGGL(gdn_chunk_fwd_kernel, dim3(n_br * H), dim3(kThr), 0, s, p, l0, H,
-                       (const bf16*)q, (const bf16*)k, prep, (bf16*)o, states, chunk_states);
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, prep, (bf16*)o, states,
+                       chunk_states);
     return hipGetLastError();
 }
 
