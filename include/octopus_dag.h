@@ -271,9 +271,8 @@ int octopus_dag_attn_bwd_rope(const octopus_plan* plan, octopus_dtype dtype, int
 
 /* Workspace bytes of octopus_gated_delta_scan: float32 fork checkpoints
  * [n_slots][H][Dv][Dk], one slot per distinct (parent, fork offset) of the plan, then one
- * 33,792-byte record per (chunk, head) (the chunk's gated score matrices, the inverse of
- * its triangular system and the state-independent part of its W): 4.3 GB at 262,144
- * tokens and H = 16. */
+ * 21,504-byte record per (chunk, head) (the chunk's gated score matrices, the inverse of
+ * its triangular system and its gates): 2.8 GB at 262,144 tokens and H = 16. */
 size_t octopus_gdn_workspace_bytes(const octopus_plan* plan, int32_t H, int32_t Dk,
                                    int32_t Dv);
 
@@ -305,7 +304,7 @@ int octopus_gated_delta_scan(const octopus_plan* plan, octopus_dtype dtype, int3
 /* Workspace bytes of octopus_gated_delta_scan_bwd: float32 checkpoint slots, one
  * initial-state gradient per branch, the state at the start and the state gradient at the
  * end of every chunk of the plan (32-token chunks, split at fork offsets), each
- * H x Dv x Dk, and the per-chunk records of the forward (21.6 GB at 262,144 tokens and
+ * H x Dv x Dk, and the per-chunk records of the forward (20.0 GB at 262,144 tokens and
  * H = 16). */
 size_t octopus_gdn_bwd_workspace_bytes(const octopus_plan* plan, int32_t H, int32_t Dk,
                                        int32_t Dv);
