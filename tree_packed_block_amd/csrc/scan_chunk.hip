@@ -623,8 +623,8 @@ __global__ __launch_bounds__(kThr, 1) void gdn_chunk_fwd_kernel(
         const float gC = TMG[(kRecG - kRecTB) + kGam + nt - 1];
 
         // X = K S_0^T and Y = Q S_0^T for this wave's value rows (A = K, Q rows with the
-        // k values in the accumulator's row order; B = the state's hi and lo parts, in
-        // separate accumulators: four independent chains).
+        // k values in the accumulator's row order; B = the state's hi and lo parts, the two
+        // products of each chained in one accumulator).
         f32x16 X = zero16(), Y = zero16();
 #pragma unroll
         for (int bk = 0; bk < 4; ++bk)
