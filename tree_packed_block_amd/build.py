@@ -36,12 +36,12 @@ HIPCC_FLAGS = [
 # VGPR-form MFMAs keep the accumulators in the architectural registers: in the default
 # form the compiler puts them in AGPRs wherever a kernel needs more than 256 registers or
 # runs one head per workgroup, and copies them back and forth around every VALU operation
-# on them (the two-head attention kernels compile to the same code either way).  The
-# dK/dV pass (bwd.hip) is the exception: it needs more than 256 registers and is faster
-# with its accumulators in AGPRs.
+# on them (the two-head attention kernels compile to the same code either way).  Measured
+# per file: the forward, extend, decode and scan kernels are faster in VGPR form; the dK/dV
+# pass (bwd.hip, more than 256 registers) and the one-head dQ pass (dq.hip) are faster in
+# the default form.
 _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 HIP_FILE_FLAGS: dict = {"fwd.hip": ["-fno-honor-nans", *_VGPR_FORM],
-                        "dq.hip": _VGPR_FORM,
                         "decode.hip": ["-fno-honor-nans", *_VGPR_FORM],
                         "extend.hip": ["-fno-honor-nans", *_VGPR_FORM],
                         "scan_chunk.hip": _VGPR_FORM}

@@ -4,8 +4,8 @@
 // mounted spans alike).  dQ = scale dS K with dS = P (dO V^T - Delta) and P = exp(S - LSE),
 // the scores recomputed from the workspace's LSE2 and Delta rows: one workgroup per
 // (query tile, one or two query heads of one KV group), walking the forward's tile lists.
-// Kept in its own file: it compiles with MFMA accumulators in the architectural registers,
-// which the dK/dV pass does not want.
+// Kept in a file of its own, so that its code-generation options can differ from the dK/dV
+// pass's.
 #include "device_common.h"
 #include "kernels.h"
 #include "kvstage.h"
