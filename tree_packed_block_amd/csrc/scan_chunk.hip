@@ -124,13 +124,8 @@ __device__ __forceinline__ void ld16f(const float* p, int s, float (&v)[16]) {
         v[4 * q + 3] = x.w;
     }
 }
-// A matrix in lane order (see the record) at p: this lane's 16 elements.
-__device__ __forceinline__ void ld_lane(const float* p, int lane, float (&v)[16]) {
-    ld16f(p + 4 * lane, 256, v);
-}
 // A matrix's 16 values of this lane (j = 8 kk + e) in split order at p, and back as the
 // bf16 parts of k-step kk.
-__device__ __forceinline__ void split8(const float (&v)[16], int kk, bf16x8& hi, bf16x8& lo);
 __device__ __forceinline__ void st_split(float* p, int lane, const float (&v)[16]) {
     unsigned char* b = reinterpret_cast<unsigned char*>(p);
 #pragma unroll
