@@ -19,6 +19,7 @@
 // codes); the sanitizers abort the process on any memory or undefined-behaviour error.
 #include <cstdint>
 #include <cstdio>
+#include <cstring>
 #include <string>
 #include <vector>
 
@@ -80,8 +81,21 @@ int main() {
                                              cur.data(), n_cur, nnew.data(), sp, spg, slo, shi,
                                              thr, causal, first, err);
         }
-        std::printf("case %d rc %d nnz %lld pop %lld seg %d %d ext %d\n", n_case, rc,
-                    (long long)plan.nnz, pop, rs0, rs1, rx);
+        // The device image, written into a buffer of exactly its size: its tile lists and
+        // positions must equal the plan's own.
+        int img = 0;
+        if (rc == OCTOPUS_OK) {
+            std::vector<unsigned char> im(plan.layout.total);
+            octo::write_device_image(plan, im.data());
+            const size_t qb = plan.q_pairs.size() * sizeof(octo::TilePair);
+            bool same = qb == 0 || std::memcmp(im.data() + plan.layout.q_pairs,
+                                               plan.q_pairs.data(), qb) == 0;
+            const int32_t* pos = reinterpret_cast<const int32_t*>(im.data() + plan.layout.pos);
+            for (int i = 0; i < T && same; ++i) same = pos[i] == (int32_t)plan.dag.pos[i];
+            img = same ? 1 : 2;
+        }
+        std::printf("case %d rc %d nnz %lld pop %lld seg %d %d ext %d img %d\n", n_case, rc,
+                    (long long)plan.nnz, pop, rs0, rs1, rx, img);
         ++n_case;
     }
     return 0;

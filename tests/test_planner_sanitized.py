@@ -75,7 +75,7 @@ def _run(driver, text):
     for line in r.stdout.splitlines():
         f = line.split()
         out.append({"rc": int(f[3]), "nnz": int(f[5]), "pop": int(f[7]),
-                    "seg": (int(f[9]), int(f[10])), "ext": int(f[12])})
+                    "seg": (int(f[9]), int(f[10])), "ext": int(f[12]), "img": int(f[14])})
     return out
 
 
@@ -102,6 +102,7 @@ def test_sanitized_planner_valid_tables(driver):
         want = _oracle_nnz(dag)
         assert r["rc"] == 0 and r["nnz"] == want and r["pop"] == want, (r, want)
         assert r["seg"] == (0, 0) and r["ext"] == 0
+        assert r["img"] == 1, r  # the device image holds the plan's own lists
 
 
 def test_sanitized_planner_invalid_tables(driver):

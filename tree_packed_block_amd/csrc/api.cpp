@@ -160,7 +160,7 @@ int octopus_plan_upload(octopus_plan* plan, void* dev_buf, size_t bytes, void* s
         void* h = nullptr;
         const hipError_t ea = hipHostMalloc(&h, plan->p.layout.total, hipHostMallocDefault);
         if (ea != hipSuccess) return hip_fail(ea, "plan upload (page-locked staging)");
-        std::memcpy(h, plan->p.blob.data(), plan->p.layout.total);
+        octo::write_device_image(plan->p, static_cast<unsigned char*>(h));
         plan->p.pinned = h;
     }
     const hipError_t e = hipMemcpyAsync(dev_buf, plan->p.pinned, plan->p.layout.total,

@@ -496,6 +496,7 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     p.nKB = (nKT + 1) / 2;
     p.blk_ptr.assign(p.nKB + 1, 0);
     p.blk_entries.clear();
+    p.blk_entries.reserve(p.k_pairs.size());  // at most one entry per listed pair
     for (int32_t b = 0; b < p.nKB; ++b) {
         const int32_t t0 = 2 * b, t1 = 2 * b + 1;
         int32_t i0 = p.kt_ptr[t0], e0 = p.kt_ptr[t0 + 1];
@@ -642,9 +643,18 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     L.sc_chunk_tok = place(std::max<size_t>(p.sc_chunk_tok.size(), 1) * 4);
     L.sc_chunk_nt = place(std::max<size_t>(p.sc_chunk_nt.size(), 1) * 4);
     L.total = std::max<size_t>(at, 256);
-    p.blob.assign(L.total, 0);
+    return OCTOPUS_OK;
+}
+
+void write_device_image(const Plan& p, unsigned char* dst) {
+    const DevLayout& L = p.layout;
+    const DagInfo& d = p.dag;
+    const int32_t nb = (int32_t)d.br.size();
+    size_t end = 0;  // end of the last array written; the gaps before each are zeroed
     auto put = [&](size_t off, const void* src, size_t bytes) {
-        if (bytes) std::memcpy(p.blob.data() + off, src, bytes);
+        std::memset(dst + end, 0, off - end);
+        if (bytes) std::memcpy(dst + off, src, bytes);
+        end = off + bytes;
     };
     put(L.fwd_order, p.fwd_order.data(), p.fwd_order.size() * 4);
     put(L.qt_ptr, p.qt_ptr.data(), p.qt_ptr.size() * 4);
@@ -658,14 +668,18 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     put(L.blk_ptr, p.blk_ptr.data(), p.blk_ptr.size() * 4);
     put(L.blk_entries, p.blk_entries.data(), p.blk_entries.size() * sizeof(BlockEntry));
     {
-        int32_t* pos = reinterpret_cast<int32_t*>(p.blob.data() + L.pos);
-        for (int32_t i = 0; i < T; ++i) pos[i] = (int32_t)d.pos[i];
-        int32_t* st = reinterpret_cast<int32_t*>(p.blob.data() + L.sc_start);
-        int32_t* ln = reinterpret_cast<int32_t*>(p.blob.data() + L.sc_len);
-        for (int32_t b = 0; b < nb; ++b) {
-            st[b] = d.br[b].start;
-            ln[b] = d.br[b].len;
-        }
+        put(L.pos, nullptr, 0);
+        int32_t* pos = reinterpret_cast<int32_t*>(dst + L.pos);
+        for (int32_t i = 0; i < p.T; ++i) pos[i] = (int32_t)d.pos[i];
+        end = L.pos + (size_t)p.T * 4;
+        put(L.sc_start, nullptr, 0);
+        int32_t* st = reinterpret_cast<int32_t*>(dst + L.sc_start);
+        for (int32_t b = 0; b < nb; ++b) st[b] = d.br[b].start;
+        end = L.sc_start + (size_t)nb * 4;
+        put(L.sc_len, nullptr, 0);
+        int32_t* ln = reinterpret_cast<int32_t*>(dst + L.sc_len);
+        for (int32_t b = 0; b < nb; ++b) ln[b] = d.br[b].len;
+        end = L.sc_len + (size_t)nb * 4;
     }
     put(L.sc_init, p.sc_init.data(), p.sc_init.size() * 4);
     put(L.sc_ck_ptr, p.sc_ck_ptr.data(), p.sc_ck_ptr.size() * 4);
@@ -677,7 +691,7 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     put(L.sc_chunk_base, p.sc_chunk_base.data(), p.sc_chunk_base.size() * 4);
     put(L.sc_chunk_tok, p.sc_chunk_tok.data(), p.sc_chunk_tok.size() * 4);
     put(L.sc_chunk_nt, p.sc_chunk_nt.data(), p.sc_chunk_nt.size() * 4);
-    return OCTOPUS_OK;
+    std::memset(dst + end, 0, L.total - end);
 }
 
 void export_mask(const Plan& p, int32_t lo, int32_t hi, uint8_t* bits) {

@@ -101,9 +101,8 @@ struct Plan {
     std::vector<int32_t> sc_chunk_base, sc_chunk_tok, sc_chunk_nt, level_chunk;
     int64_t n_chunks = 0;
     DevLayout layout;
-    std::vector<unsigned char> blob;  // host image of the device copy
-    void* dev = nullptr;              // caller-owned device copy after upload
-    void* pinned = nullptr;           // page-locked copy of `blob` used by uploads
+    void* dev = nullptr;     // caller-owned device copy after upload
+    void* pinned = nullptr;  // page-locked image of the device copy (write_device_image)
 };
 
 // Tokens per chunk of the chunked recurrent scan.
@@ -111,6 +110,9 @@ constexpr int32_t kScanChunk = 32;
 
 int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, int32_t nm,
                int32_t T, int32_t kv_tile, Plan& out, std::string& err);
+// The device image of a plan (layout.total bytes, every array at its layout offset, the
+// padding between them zero) written into dst, e.g. page-locked staging for an upload.
+void write_device_image(const Plan& p, unsigned char* dst);
 
 // Dense bits of rows [lo, hi) from the tile lists only (see octopus_plan_export_mask).
 void export_mask(const Plan& p, int32_t lo, int32_t hi, uint8_t* bits);
