@@ -2,6 +2,9 @@
 #include "plan.h"
 
 #include <algorithm>
+#include <atomic>
+#include <exception>
+#include <thread>
 #include <map>
 #include <climits>
 #include <cstring>
@@ -53,6 +56,40 @@ void merge(std::vector<Interval>& v) {
         }
     }
     v.resize(w + 1);
+}
+
+// fn(i) for every i in [0, n), spread over up to `threads` host threads that take the
+// items in turn (the caller's results must not depend on which thread runs an item).  An
+// exception thrown by fn is rethrown here after every thread has stopped.
+template <class F>
+void parallel_for(int32_t n, int32_t threads, const F& fn) {
+    threads = std::max<int32_t>(1, std::min(threads, n));
+    if (threads == 1) {
+        for (int32_t i = 0; i < n; ++i) fn(i);
+        return;
+    }
+    std::atomic<int32_t> next{0};
+    std::vector<std::exception_ptr> fault(threads);
+    std::vector<std::thread> pool;
+    pool.reserve(threads);
+    for (int32_t w = 0; w < threads; ++w)
+        pool.emplace_back([&, w]() {
+            try {
+                for (int32_t i = next++; i < n; i = next++) fn(i);
+            } catch (...) {
+                fault[w] = std::current_exception();
+                next = n;
+            }
+        });
+    for (std::thread& t : pool) t.join();
+    for (const std::exception_ptr& e : fault)
+        if (e) std::rethrow_exception(e);
+}
+
+// Host threads for the planner's parallel phases.
+int32_t plan_threads() {
+    const int32_t hw = (int32_t)std::thread::hardware_concurrency();
+    return std::max<int32_t>(1, std::min<int32_t>(hw, 16));
 }
 
 int validate(const octopus_branch* br, int32_t nb, const octopus_mount* mt, int32_t nm,
@@ -316,123 +353,166 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     for (int32_t b = 0; b < nb; ++b)
         for (int32_t r = 0; r < d.br[b].len; ++r) row_branch[d.br[b].start + r] = b;
 
-    std::vector<std::vector<Interval>> rows(Bq);
-    std::vector<Interval> scratch;
-    // Difference arrays over KV tiles, cleared entry by entry after each query tile; only
-    // the tile ranges some row touches are swept, so planning costs O(rows x intervals +
-    // listed pairs) rather than O(query tiles x KV tiles) (a forest of many trees would
-    // otherwise sweep every tile of every tree for every query tile).
-    std::vector<int32_t> full_diff(nKT + 1, 0), touch_diff(nKT + 1, 0);
-    std::vector<std::pair<int64_t, int64_t>> spans;  // touched tile ranges [t0, t1)
-    std::vector<std::pair<int64_t, int64_t>> row_sp, prev_sp;  // one row's ranges
-    std::vector<size_t> cursor(Bq);
+    // The query tiles' lists, planned in blocks of consecutive tiles that host threads take
+    // in turn; the blocks are joined in tile order (mask indices offset by the masks of the
+    // blocks before), so the plan does not depend on the threads.
+    struct TileBlock {
+        std::vector<TilePair> pairs;   // mask: index among this block's partial masks
+        std::vector<uint64_t> masks;
+        std::vector<int32_t> count;    // pairs per query tile
+        int64_t nnz = 0;
+    };
+    auto plan_tiles = [&](int32_t qt_lo, int32_t qt_hi, TileBlock& out) {
+        std::vector<std::vector<Interval>> rows(Bq);
+        std::vector<Interval> scratch;
+        // Difference arrays over KV tiles, cleared entry by entry after each query tile;
+        // only the tile ranges some row touches are swept, so planning costs O(rows x
+        // intervals + listed pairs) rather than O(query tiles x KV tiles) (a forest of many
+        // trees would otherwise sweep every tile of every tree for every query tile).
+        std::vector<int32_t> full_diff(nKT + 1, 0), touch_diff(nKT + 1, 0);
+        std::vector<std::pair<int64_t, int64_t>> spans;  // touched tile ranges [t0, t1)
+        std::vector<std::pair<int64_t, int64_t>> row_sp, prev_sp;  // one row's ranges
+        std::vector<size_t> cursor(Bq);
+        std::vector<uint64_t> words(Bq * p.row_words);
+        out.count.assign(qt_hi - qt_lo, 0);
+        for (int32_t qt = qt_lo; qt < qt_hi; ++qt) {
+            const size_t n_before = out.pairs.size();
+            const int32_t r0 = qt * Bq;
+            const int32_t nv = std::min(Bq, T - r0);
+            spans.clear();
+            prev_sp.clear();
+            for (int32_t rr = 0; rr < nv; ++rr) {
+                const int32_t i = r0 + rr;
+                const int32_t b = row_branch[i];
+                const int32_t r = i - d.br[b].start;
+                // Ctx(b, r) = Ctx(b, r - 1) + the own token i (never already in it: a branch
+                // does not mount itself) + the spans mounted at rpos = r.  Without such a
+                // mount the previous row's intervals are copied and the one ending at i
+                // grows by one key (joining the next interval if that starts at i + 1).
+                bool inc = rr > 0 && r > 0 && row_branch[i - 1] == b;
+                if (inc)
+                    for (int32_t id : d.mounts_of[b])
+                        if (d.mt[id].rpos == r) { inc = false; break; }
+                if (inc) {
+                    std::vector<Interval>& cur = rows[rr];
+                    cur = rows[rr - 1];
+                    for (size_t j = 0; j < cur.size(); ++j) {
+                        if (cur[j].hi != i) continue;
+                        cur[j].hi = (int64_t)i + 1;
+                        if (j + 1 < cur.size() && cur[j + 1].lo == (int64_t)i + 1) {
+                            cur[j].hi = cur[j + 1].hi;
+                            cur.erase(cur.begin() + (j + 1));
+                        }
+                        break;
+                    }
+                } else {
+                    d.row_context(b, r, rows[rr], scratch);
+                }
+                row_sp.clear();
+                for (const Interval& iv : rows[rr]) {
+                    out.nnz += iv.hi - iv.lo;
+                    const int64_t t0 = iv.lo / Bk, t1 = (iv.hi + Bk - 1) / Bk;
+                    touch_diff[t0] += 1;
+                    touch_diff[t1] -= 1;
+                    // Neighbouring rows mostly repeat their ranges; keep each range once.
+                    row_sp.push_back({t0, t1});
+                    if (std::find(prev_sp.begin(), prev_sp.end(), row_sp.back()) == prev_sp.end())
+                        spans.push_back({t0, t1});
+                    const int64_t f0 = (iv.lo + Bk - 1) / Bk, f1 = iv.hi / Bk;
+                    if (f0 < f1) {
+                        full_diff[f0] += 1;
+                        full_diff[f1] -= 1;
+                    }
+                }
+                cursor[rr] = 0;
+                prev_sp.swap(row_sp);
+            }
+            // Merge the touched ranges; every interval starts and ends inside one merged
+            // range, so the running sums are 0 at the start of each.
+            std::sort(spans.begin(), spans.end());
+            size_t n_sp = 0;
+            for (size_t j = 0; j < spans.size(); ++j) {
+                if (n_sp > 0 && spans[j].first <= spans[n_sp - 1].second)
+                    spans[n_sp - 1].second = std::max(spans[n_sp - 1].second, spans[j].second);
+                else
+                    spans[n_sp++] = spans[j];
+            }
+            for (size_t sp = 0; sp < n_sp; ++sp) {
+                int32_t touch = 0, full = 0;
+                for (int32_t t = (int32_t)spans[sp].first; t < (int32_t)spans[sp].second; ++t) {
+                    touch += touch_diff[t];
+                    full += full_diff[t];
+                    if (touch == 0) continue;
+                    if (full == nv) {
+                        out.pairs.push_back({t, -1});
+                        continue;
+                    }
+                    // PARTIAL: per-row bits of keys [t*Bk, t*Bk + Bk) that the row sees.
+                    const int64_t k0 = (int64_t)t * Bk, k1 = k0 + Bk;
+                    std::fill(words.begin(), words.end(), 0);
+                    for (int32_t rr = 0; rr < nv; ++rr) {
+                        const auto& iv = rows[rr];
+                        size_t c = cursor[rr];
+                        while (c < iv.size() && iv[c].hi <= k0) ++c;
+                        cursor[rr] = c;
+                        for (size_t j = c; j < iv.size() && iv[j].lo < k1; ++j) {
+                            const int64_t a = std::max(iv[j].lo, k0) - k0;
+                            const int64_t e = std::min(iv[j].hi, k1) - k0;
+                            set_bits(&words[rr * p.row_words], a, e);
+                        }
+                    }
+                    const int32_t idx = (int32_t)(out.masks.size() / (Bq * p.row_words));
+                    out.masks.insert(out.masks.end(), words.begin(), words.end());
+                    out.pairs.push_back({t, idx});
+                }
+            }
+            // Clear the entries this query tile set.
+            for (int32_t rr = 0; rr < nv; ++rr) {
+                for (const Interval& iv : rows[rr]) {
+                    touch_diff[iv.lo / Bk] = 0;
+                    touch_diff[(iv.hi + Bk - 1) / Bk] = 0;
+                    full_diff[(iv.lo + Bk - 1) / Bk] = 0;
+                    full_diff[iv.hi / Bk] = 0;
+                }
+            }
+            out.count[qt - qt_lo] = (int32_t)(out.pairs.size() - n_before);
+        }
+    };
+    const int32_t n_blocks = std::max<int32_t>(1, std::min<int32_t>(nQT / 8, 256));
+    std::vector<TileBlock> blocks(n_blocks);
+    auto block_lo = [&](int32_t i) { return (int32_t)((int64_t)nQT * i / n_blocks); };
+    const int32_t n_threads = std::min(plan_threads(), std::max<int32_t>(1, n_blocks / 2));
+    parallel_for(n_blocks, n_threads,
+                 [&](int32_t i) { plan_tiles(block_lo(i), block_lo(i + 1), blocks[i]); });
+    // Join the blocks in tile order: each block's pairs and masks go to their offsets (mask
+    // indices shifted by the masks of the blocks before).
+    const size_t mask_words = (size_t)Bq * p.row_words;
+    std::vector<size_t> pair_at(n_blocks + 1, 0), mask_at(n_blocks + 1, 0);
     p.qt_ptr.assign(nQT + 1, 0);
-    p.q_pairs.clear();
-    p.mask_rows.clear();
     p.nnz = 0;
-    std::vector<uint64_t> words(Bq * p.row_words);
-
-    for (int32_t qt = 0; qt < nQT; ++qt) {
-        const int32_t r0 = qt * Bq;
-        const int32_t nv = std::min(Bq, T - r0);
-        spans.clear();
-        prev_sp.clear();
-        for (int32_t rr = 0; rr < nv; ++rr) {
-            const int32_t i = r0 + rr;
-            const int32_t b = row_branch[i];
-            const int32_t r = i - d.br[b].start;
-            // Ctx(b, r) = Ctx(b, r - 1) + the own token i (never already in it: a branch
-            // does not mount itself) + the spans mounted at rpos = r.  Without such a
-            // mount the previous row's intervals are copied and the one ending at i
-            // grows by one key (joining the next interval if that starts at i + 1).
-            bool inc = rr > 0 && r > 0 && row_branch[i - 1] == b;
-            if (inc)
-                for (int32_t id : d.mounts_of[b])
-                    if (d.mt[id].rpos == r) { inc = false; break; }
-            if (inc) {
-                std::vector<Interval>& cur = rows[rr];
-                cur = rows[rr - 1];
-                for (size_t j = 0; j < cur.size(); ++j) {
-                    if (cur[j].hi != i) continue;
-                    cur[j].hi = (int64_t)i + 1;
-                    if (j + 1 < cur.size() && cur[j + 1].lo == (int64_t)i + 1) {
-                        cur[j].hi = cur[j + 1].hi;
-                        cur.erase(cur.begin() + (j + 1));
-                    }
-                    break;
-                }
-            } else {
-                d.row_context(b, r, rows[rr], scratch);
-            }
-            row_sp.clear();
-            for (const Interval& iv : rows[rr]) {
-                p.nnz += iv.hi - iv.lo;
-                const int64_t t0 = iv.lo / Bk, t1 = (iv.hi + Bk - 1) / Bk;
-                touch_diff[t0] += 1;
-                touch_diff[t1] -= 1;
-                // Neighbouring rows mostly repeat their ranges; keep each range once.
-                row_sp.push_back({t0, t1});
-                if (std::find(prev_sp.begin(), prev_sp.end(), row_sp.back()) == prev_sp.end())
-                    spans.push_back({t0, t1});
-                const int64_t f0 = (iv.lo + Bk - 1) / Bk, f1 = iv.hi / Bk;
-                if (f0 < f1) {
-                    full_diff[f0] += 1;
-                    full_diff[f1] -= 1;
-                }
-            }
-            cursor[rr] = 0;
-            prev_sp.swap(row_sp);
-        }
-        // Merge the touched ranges; every interval starts and ends inside one merged
-        // range, so the running sums are 0 at the start of each.
-        std::sort(spans.begin(), spans.end());
-        size_t n_sp = 0;
-        for (size_t j = 0; j < spans.size(); ++j) {
-            if (n_sp > 0 && spans[j].first <= spans[n_sp - 1].second)
-                spans[n_sp - 1].second = std::max(spans[n_sp - 1].second, spans[j].second);
-            else
-                spans[n_sp++] = spans[j];
-        }
-        for (size_t sp = 0; sp < n_sp; ++sp) {
-            int32_t touch = 0, full = 0;
-            for (int32_t t = (int32_t)spans[sp].first; t < (int32_t)spans[sp].second; ++t) {
-                touch += touch_diff[t];
-                full += full_diff[t];
-                if (touch == 0) continue;
-                if (full == nv) {
-                    p.q_pairs.push_back({t, -1});
-                    continue;
-                }
-                // PARTIAL: per-row bits of keys [t*Bk, t*Bk + Bk) that the row sees.
-                const int64_t k0 = (int64_t)t * Bk, k1 = k0 + Bk;
-                std::fill(words.begin(), words.end(), 0);
-                for (int32_t rr = 0; rr < nv; ++rr) {
-                    const auto& iv = rows[rr];
-                    size_t c = cursor[rr];
-                    while (c < iv.size() && iv[c].hi <= k0) ++c;
-                    cursor[rr] = c;
-                    for (size_t j = c; j < iv.size() && iv[j].lo < k1; ++j) {
-                        const int64_t a = std::max(iv[j].lo, k0) - k0;
-                        const int64_t e = std::min(iv[j].hi, k1) - k0;
-                        set_bits(&words[rr * p.row_words], a, e);
-                    }
-                }
-                const int32_t idx = (int32_t)(p.mask_rows.size() / (Bq * p.row_words));
-                p.mask_rows.insert(p.mask_rows.end(), words.begin(), words.end());
-                p.q_pairs.push_back({t, idx});
-            }
-        }
-        // Clear the entries this query tile set.
-        for (int32_t rr = 0; rr < nv; ++rr) {
-            for (const Interval& iv : rows[rr]) {
-                touch_diff[iv.lo / Bk] = 0;
-                touch_diff[(iv.hi + Bk - 1) / Bk] = 0;
-                full_diff[(iv.lo + Bk - 1) / Bk] = 0;
-                full_diff[iv.hi / Bk] = 0;
-            }
-        }
-        p.qt_ptr[qt + 1] = (int32_t)p.q_pairs.size();
+    for (int32_t i = 0; i < n_blocks; ++i) {
+        pair_at[i + 1] = pair_at[i] + blocks[i].pairs.size();
+        mask_at[i + 1] = mask_at[i] + blocks[i].masks.size() / mask_words;
+        for (int32_t qt = block_lo(i); qt < block_lo(i + 1); ++qt)
+            p.qt_ptr[qt + 1] = p.qt_ptr[qt] + blocks[i].count[qt - block_lo(i)];
+        p.nnz += blocks[i].nnz;
     }
+    p.q_pairs.resize(pair_at[n_blocks]);
+    // (room for the all-ones mask appended below)
+    p.mask_rows.reserve((mask_at[n_blocks] + 1) * mask_words);
+    p.mask_rows.resize(mask_at[n_blocks] * mask_words);
+    parallel_for(n_blocks, n_threads, [&](int32_t i) {
+        TileBlock& b = blocks[i];
+        const int32_t base = (int32_t)mask_at[i];
+        TilePair* dst = p.q_pairs.data() + pair_at[i];
+        for (size_t j = 0; j < b.pairs.size(); ++j) {
+            const TilePair& tp = b.pairs[j];
+            dst[j] = {tp.tile, tp.mask < 0 ? tp.mask : base + tp.mask};
+        }
+        std::copy(b.masks.begin(), b.masks.end(), p.mask_rows.begin() + mask_at[i] * mask_words);
+        TileBlock().pairs.swap(b.pairs);  // free as we go
+        TileBlock().masks.swap(b.masks);
+    });
     p.n_partial = (int64_t)(p.mask_rows.size() / (Bq * p.row_words));
 
     // One extra all-ones mask (index n_partial) that kernels may use for FULL tiles.
@@ -444,23 +524,27 @@ int build_plan(const octopus_branch* br, int32_t nb, const octopus_mount* mt, in
     p.mask_cols.assign((p.n_partial + 2) * Bk * p.col_words, 0);
     std::fill(p.mask_cols.begin() + p.n_partial * Bk * p.col_words,
               p.mask_cols.begin() + (p.n_partial + 1) * Bk * p.col_words, ~0ull);
-    for (int64_t m = 0; m < p.n_partial; ++m) {
-        const uint64_t* wr = &p.mask_rows[m * Bq * p.row_words];
-        uint64_t* wc = &p.mask_cols[m * Bk * p.col_words];
-        if (Bk == 64) {  // one word per row: transpose 64-row blocks as bit matrices
-            for (int32_t hf = 0; hf < Bq / 64; ++hf) {
-                uint64_t blk[64];
-                std::copy(wr + 64 * hf, wr + 64 * hf + 64, blk);
-                transpose64(blk);
-                for (int32_t kk = 0; kk < 64; ++kk) wc[kk * p.col_words + hf] = blk[kk];
+    const int32_t n_mc = (int32_t)std::min<int64_t>(p.n_partial, 256);  // mask groups
+    parallel_for(n_mc, p.n_partial >= 512 ? plan_threads() : 1, [&](int32_t grp) {
+        const int64_t m0 = p.n_partial * grp / n_mc, m1 = p.n_partial * (grp + 1) / n_mc;
+        for (int64_t m = m0; m < m1; ++m) {
+            const uint64_t* wr = &p.mask_rows[m * Bq * p.row_words];
+            uint64_t* wc = &p.mask_cols[m * Bk * p.col_words];
+            if (Bk == 64) {  // one word per row: transpose 64-row blocks as bit matrices
+                for (int32_t hf = 0; hf < Bq / 64; ++hf) {
+                    uint64_t blk[64];
+                    std::copy(wr + 64 * hf, wr + 64 * hf + 64, blk);
+                    transpose64(blk);
+                    for (int32_t kk = 0; kk < 64; ++kk) wc[kk * p.col_words + hf] = blk[kk];
+                }
+                continue;
             }
-            continue;
+            for (int32_t rr = 0; rr < Bq; ++rr)
+                for (int32_t kk = 0; kk < Bk; ++kk)
+                    if ((wr[rr * p.row_words + (kk >> 6)] >> (kk & 63)) & 1)
+                        wc[kk * p.col_words + (rr >> 6)] |= 1ull << (rr & 63);
         }
-        for (int32_t rr = 0; rr < Bq; ++rr)
-            for (int32_t kk = 0; kk < Bk; ++kk)
-                if ((wr[rr * p.row_words + (kk >> 6)] >> (kk & 63)) & 1)
-                    wc[kk * p.col_words + (rr >> 6)] |= 1ull << (rr & 63);
-    }
+    });
 
     // Transposed lists: for every KV tile, the query tiles that see it, ascending.
     p.kt_ptr.assign(nKT + 1, 0);
