@@ -1,4 +1,5 @@
-"""The host planner under AddressSanitizer and UndefinedBehaviorSanitizer (CPU).
+"""The host planner under AddressSanitizer and UndefinedBehaviorSanitizer, and under
+ThreadSanitizer (its query tiles are planned on host threads) (CPU).
 
 ``tests/sanitize/plan_driver.cpp`` is compiled with g++ together with the planner's
 source and the two sanitizers (any memory or undefined-behaviour error aborts it), then
@@ -24,12 +25,11 @@ CSRC = os.path.join(ROOT, "tree_packed_block_amd", "csrc")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 
-@pytest.fixture(scope="module")
-def driver():
+def _build_driver(sanitize, tag):
     if shutil.which("g++") is None:
         pytest.skip("g++ is not available")
-    out = os.path.join(tempfile.mkdtemp(prefix="plan_san_"), "plan_driver")
-    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+    out = os.path.join(tempfile.mkdtemp(prefix="plan_san_"), "plan_driver_" + tag)
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=" + sanitize,
            "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-D__HIP_PLATFORM_AMD__",
            "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
            "-I" + os.path.join(ROCM, "include"),
@@ -37,10 +37,20 @@ def driver():
            os.path.join(CSRC, "plan.cpp"), "-o", out]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
-        if "asan" in r.stdout.lower() or "ubsan" in r.stdout.lower():
+        if "san" in r.stdout.lower():
             pytest.skip("sanitizer runtime not available: " + r.stdout[-300:])
         raise AssertionError("driver build failed:\n" + r.stdout)
     return out
+
+
+@pytest.fixture(scope="module")
+def driver():
+    return _build_driver("address,undefined", "asan")
+
+
+@pytest.fixture(scope="module")
+def tsan_driver():
+    return _build_driver("thread", "tsan")
 
 
 def _case_text(branches, mounts, T, page_size=16, pages=None, n_new=None):
@@ -142,3 +152,29 @@ def test_sanitized_planner_invalid_tables(driver):
     text = "".join(_case_text(b, m, T) for b, m, T in bad)
     res = _run(driver, text)
     assert [r["rc"] for r in res] == want
+
+
+def test_threaded_planner_under_thread_sanitizer(tsan_driver):
+    # Trees of 16K-60K tokens: enough query tiles that the planner splits them over host
+    # threads (blocks of consecutive tiles, joined in order) and transposes the masks on
+    # them; ThreadSanitizer must report no race and the plans must stay exact.
+    rng = np.random.default_rng(5)
+    dags = [synth.build("forked")[0]]
+    for seed in range(3):
+        r = np.random.default_rng(70 + seed)
+        dags.append(synth.fuzz_dag(r, max_branches=10, max_len=6000, max_mounts=8))
+    text = ""
+    for dag in dags:
+        pages = synth.dags.assign_pages(dag, 16, rng)
+        text += _case_text(dag.branches, dag.mounts, dag.T, 16, pages, None)
+    env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1")
+    r = subprocess.run([tsan_driver], input=text, stdout=subprocess.PIPE,
+                       stderr=subprocess.PIPE, text=True, timeout=900, env=env)
+    assert r.returncode == 0, "thread sanitizer report:\n" + r.stderr[-4000:]
+    assert "ThreadSanitizer" not in r.stderr, r.stderr[-4000:]
+    lines = r.stdout.splitlines()
+    assert len(lines) == len(dags)
+    for dag, line in zip(dags, lines):
+        f = line.split()
+        assert int(f[3]) == 0 and int(f[7]) == int(f[5]) == _oracle_nnz(dag), (line, dag.T)
+        assert int(f[14]) == 1, line
