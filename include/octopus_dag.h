@@ -115,7 +115,9 @@ typedef struct {
  * tile sees, each FULL (every row sees every key) or PARTIAL (a per-row bit mask),
  * the transposed lists (for every KV tile, the query tiles that see it), and
  * longest-first launch orders.  kv_tile must be 64.  total_tokens must be in
- * [1, 2^24].  Synchronous and re-entrant; touches no device.
+ * [1, 2^24].  Synchronous and re-entrant; touches no device.  The per-tile lists and
+ * the mask transposes of plans with many query tiles run on up to 16 host threads that the
+ * call starts and joins; the plan does not depend on how many.
  * Errors: EINVAL (table rules above), ECYCLE, EUNSUPPORTED, ENOMEM.
  * On success *out owns the plan; free it with octopus_plan_destroy. */
 int octopus_dag_plan(const octopus_branch* branches, int32_t n_branches,
